@@ -1,0 +1,206 @@
+#!/usr/bin/env python3
+"""Benchmark of the streaming LM-head + cross-entropy step (forward + backward).
+
+One step = lmhead_loss_fwd + lmhead_loss_bwd of the mean loss over the whole
+batch at the Llama-3.1-8B shape (N = 32768 tokens of one 32k sequence,
+H = 4096, V = 128256, bf16 inputs, fp32 accumulation), inputs resident in HBM.
+Prints one JSON line with tokens/s, the MFMA fractions, peak HBM, the
+roofline of the dominant kernel and the fp64 CPU oracle timed on a sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="ce_bf16_8b")
+    ap.add_argument("--chunk", type=int, default=8192, help="max rows per chunk")
+    ap.add_argument("--cpu-sample-rows", type=int, default=64)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import synthetic
+    import lm_head_vocab_amd as L
+    from lm_head_vocab_amd.runner import LossRun
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    L.load_library()
+    dev = torch.device("cuda", 0)
+
+    t0 = time.time()
+    prob = synthetic.make_problem(args.workload)
+    gen_s = time.time() - t0
+    N, H, V = prob.n_rows, prob.hidden_dim, prob.vocab
+
+    def up(x):
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    h = up(prob.hidden)
+    W = up(prob.W)
+    labels = torch.from_numpy(prob.labels).to(dev)
+    mask = None if prob.mask is None else torch.from_numpy(prob.mask).to(dev)
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats()
+    base_alloc = torch.cuda.memory_allocated()
+
+    run = LossRun(h, W, prob.weights, labels=labels, mask=mask, max_chunk_rows=args.chunk,
+                  want_terms=False)
+    dh = torch.empty((N, H), dtype=torch.float32, device=dev)
+    dW = torch.empty((V, H), dtype=torch.float32, device=dev)
+    gmean = torch.ones(1, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        run.forward(stream)
+        run.backward(grad_mean=gmean, dhidden=dh, dW=dW, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    trace = L.binding.Trace(capacity=128 * args.steps)
+    trace.attach(run.problem)
+    torch.cuda.synchronize()
+    wall0 = time.time()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.time() - wall0
+    kernels = summarize_trace(trace.read(), args.steps)
+    run.problem.trace = None
+    trace.close()
+    per_step = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
+    ms_total = sum(per_step)
+    ms_med = per_step[len(per_step) // 2]
+    ms_mean = ms_total / args.steps
+    peak_bytes = torch.cuda.max_memory_allocated()
+
+    # executed MFMA flops per step (schedule): fwd 2NHV, recompute 2NHV, dh 2NHV, dW 2NHV
+    nhv = float(N) * H * V
+    exec_flops = 8.0 * nhv
+    model_flops = 6.0 * nhv
+    tflops = exec_flops / (ms_mean * 1e-3) / 1e12
+    model_tflops = model_flops / (ms_mean * 1e-3) / 1e12
+
+    dom = max(kernels, key=lambda k: kernels[k]["ms_total"])
+    d = kernels[dom]
+    achieved = d["work_per_launch"] / (d["ms_avg"] * 1e-3) / 1e12
+    kern = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 1),
+            "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
+            "traffic": None, "flops_per_launch": d["work_per_launch"],
+            "avg_launch_ms": round(d["ms_avg"], 4), "launches_per_step": d["launches_per_step"]}
+
+    result = {
+        "metric": "fused LM-head+loss fwd+bwd tokens/s, % bf16 MFMA peak, peak HBM GiB @8B shape",
+        "value": round(N / (ms_mean * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_mean, 3),
+        "ms_per_step_median": round(ms_med, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; h ~ N(0,1), W ~ N(0,0.02), labels uniform)",
+        "config": {"workload": args.workload, "tokens": N, "hidden": H, "vocab": V,
+                   "loss": "ce_label", "chunk_rows": int(run.workspace.numel() and args.chunk),
+                   "parallelism": "none (1 GPU)"},
+        "mfma_frac_executed": round(tflops / BF16_PEAK_TFLOPS, 4),
+        "mfma_frac_model": round(model_tflops / BF16_PEAK_TFLOPS, 4),
+        "executed_tflops": round(tflops, 1),
+        "peak_hbm_gib": round(peak_bytes / 2**30, 3),
+        "peak_hbm_gib_above_inputs": round((peak_bytes - base_alloc) / 2**30, 3),
+        "logits_sized_limit_gib": round(N * V * 2 / 2**30, 3),
+        "workspace_gib": round(run.workspace.numel() / 2**30, 3),
+        "roofline": kern,
+        "kernels": {k: {"ms_per_step": round(v["ms_total"] / args.steps, 3),
+                        "launches_per_step": v["launches_per_step"],
+                        "tflops": round(v["work_per_launch"] / (v["ms_avg"] * 1e-3) / 1e12, 1)
+                        if v["is_flops"] else None}
+                    for k, v in sorted(kernels.items(), key=lambda kv: -kv[1]["ms_total"])},
+        "wall_s_timed": round(wall, 3),
+        "input_gen_s": round(gen_s, 1),
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(prob, args.cpu_sample_rows)
+    print(json.dumps(result), flush=True)
+
+
+FLOP_KERNELS = ("stats_q", "stats_p", "div", "dz", "gemm_dh", "gemm_dW")
+
+
+def summarize_trace(entries, steps):
+    """Per-kernel totals from the library's HIP-event trace of the timed steps."""
+    out = {}
+    for name, ms, work in entries:
+        e = out.setdefault(name, {"ms_total": 0.0, "n": 0, "work": 0.0})
+        e["ms_total"] += ms
+        e["n"] += 1
+        e["work"] += work
+    for name, e in out.items():
+        e["ms_avg"] = e["ms_total"] / e["n"]
+        e["work_per_launch"] = e["work"] / e["n"]
+        e["launches_per_step"] = e["n"] / steps
+        e["is_flops"] = name in FLOP_KERNELS
+    return out
+
+
+def cpu_baseline(prob, rows):
+    """The fp64 oracle, as it stands, on the first `rows` rows of the same workload."""
+    import numpy as np
+    from oracle import specloss_oracle as O
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count()
+    sel = np.arange(rows)
+    t0 = time.time()
+    w64 = O._weights64(O.OracleProblem.of(prob))
+    widen_s = time.time() - t0
+    t0 = time.time()
+    seed = O.mean_seed(prob)
+    O.forward(prob, rows=sel, weights64=w64)
+    O.backward(prob, seed=seed, rows=sel, weights64=w64)
+    dt = time.time() - t0
+    return {"value": round(rows / dt, 2), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"fwd+bwd (fp64, dense logits per 64-row block) of the first {rows} of "
+                      f"{prob.n_rows} rows, full vocab and dW; {dt:.1f} s, plus {widen_s:.1f} s "
+                      f"widening W to fp64 once"}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,201 @@
+/*
+ * libspecloss: streaming LM-head + loss for speculative draft-head training
+ * on one AMD Instinct MI355X (gfx950).
+ *
+ * The operation (Nebius blog "Training speculative decoders: removing the
+ * logits and attention bottlenecks", sections "The logits bottleneck..." and
+ * "Streaming Cross Entropy"): hidden states -> LM head -> vocabulary logits ->
+ * a per-token loss, computed tile by tile so that the [tokens, vocab] logits
+ * tensor never exists in memory.  The losses are the language-model
+ * cross-entropy against token labels and the target-vs-draft losses of the
+ * vLLM speculators "Loss Functions" page ("Available Losses" table), alone or
+ * as an unnormalised weighted sum ("Weighted Combinations").  The backward
+ * ("Backward pass" section of the blog) recomputes logits tiles and returns
+ * the gradients with respect to the hidden states and the LM-head weight.
+ *
+ * Notation: N aligned rows (tokens, or (head, position) pairs), hidden size
+ * H, vocabulary V.  Draft logits z = W h with q = softmax(z); target logits
+ * u = W_t g with p = softmax(u).  W and W_t are [V, H] row-major (one row
+ * per vocabulary entry, the layout of a linear layer's weight), no bias.
+ *
+ * Conventions for every call:
+ *  - All tensor pointers are DEVICE pointers owned by the caller; the
+ *    library never allocates device memory.  Tensors are dense row-major.
+ *    Floating tensors (hidden, W, target_hidden, W_t) must be 16-byte
+ *    aligned; every other pointer 4-byte aligned (8 for counts).
+ *  - Work is enqueued on `stream` (NULL = the null stream) and is
+ *    asynchronous: outputs are valid once the stream has synchronised.
+ *  - Every argument is checked on the host before anything is enqueued.
+ *    Return value 0 = success, else a negative SPECLOSS_E_* code and
+ *    nothing was enqueued.  An unsupported case is an error; there is no
+ *    fallback to another implementation.  SPECLOSS_E_HIP is returned when
+ *    a HIP launch fails (work enqueued before it may have run).
+ *  - Labels, masks and row maps live on the device and are not inspected
+ *    by the host: an unmasked row whose label (or target row) is out of
+ *    range is treated as masked and counted in counts[1].
+ *  - Results are deterministic: two calls with the same inputs, the same
+ *    workspace size and the same device give bitwise-identical outputs.
+ *  - Calls that share a workspace must not overlap in time.
+ */
+#ifndef SPECLOSS_H
+#define SPECLOSS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Loss kinds.  Names (specloss_kind_name) follow the speculators page. */
+typedef enum {
+  SPECLOSS_CE_LABEL = 0,    /* "ce_label": -log q_y, y = given label (blog, "Streaming Cross Entropy") */
+  SPECLOSS_CE_ARGMAX_P = 1, /* "ce": -log q_y, y = argmax p, lowest index on ties ("Available Losses", ce) */
+  SPECLOSS_KL = 2,          /* "kl_div": KL(p || q) ("Available Losses", kl_div) */
+  SPECLOSS_RKL = 3,         /* "rkl": KL(q || p) ("Available Losses", rkl) */
+  SPECLOSS_JSD = 4,         /* "jsd": (KL(p||m) + KL(q||m)) / 2, m = (p+q)/2 ("Available Losses", jsd) */
+  SPECLOSS_TV = 5,          /* "tv": 1 - alpha, alpha = sum_v min(p_v, q_v) ("Available Losses", tv) */
+  SPECLOSS_NLA = 6,         /* "nla": -log alpha ("Available Losses", nla) */
+  SPECLOSS_LK_HYBRID = 7,   /* "lk_hybrid": lam KL(p||q) + (1-lam)(1-alpha), lam = exp(-3 alpha)
+                               held constant in the backward ("Available Losses", lk_hybrid) */
+  SPECLOSS_NUM_KINDS = 8
+} specloss_kind;
+
+typedef enum { SPECLOSS_F32 = 0, SPECLOSS_BF16 = 1 } specloss_dtype;
+
+enum {
+  SPECLOSS_OK = 0,
+  SPECLOSS_E_INVAL = -1,       /* null/inconsistent argument, bad size, no nonzero weight */
+  SPECLOSS_E_UNSUPPORTED = -2, /* H not a multiple of 64, misaligned pointer, unknown dtype */
+  SPECLOSS_E_WORKSPACE = -3,   /* workspace missing or smaller than the minimum */
+  SPECLOSS_E_HIP = -4          /* a HIP launch failed */
+};
+
+#define SPECLOSS_IGNORE_INDEX (-100)
+
+/* Per-row statistics the forward saves for the backward (opaque layout). */
+#define SPECLOSS_SAVED_FIELDS 9
+
+/* Opaque kernel trace (see specloss_trace_create). */
+typedef struct specloss_trace specloss_trace;
+
+/*
+ * One loss problem.  Rows must already be aligned (blog, "Correctness:
+ * alignment before chunking"): row r pairs hidden_states[r] with its label
+ * and/or its target row; masks are per aligned row.
+ *
+ * A row is valid iff mask == NULL or mask[r] != 0, and, when the
+ * SPECLOSS_CE_LABEL weight is nonzero, labels[r] != SPECLOSS_IGNORE_INDEX.
+ * Invalid rows contribute exactly 0 to every loss and gradient.  The
+ * number of valid rows is the loss denominator (blog, "Backward pass":
+ * normalise by valid tokens, not by chunks).
+ */
+typedef struct {
+  int64_t n_rows;              /* N > 0 */
+  int64_t hidden;              /* H > 0, multiple of 64 */
+  int64_t vocab;               /* V > 0, < 2^31 */
+  int32_t in_dtype;            /* specloss_dtype of hidden_states, W, target_hidden, W_t */
+  int32_t reserved;            /* must be 0 */
+  const void* hidden_states;   /* [N, H] draft hidden states */
+  const void* W;               /* [V, H] draft LM-head weight */
+  const int32_t* labels;       /* [N] token labels, or NULL when no label kind is on */
+  const void* target_hidden;   /* [n_target_rows, H] target hidden states, or NULL */
+  int64_t n_target_rows;       /* rows of target_hidden */
+  const void* W_t;             /* [V, H] target LM-head weight (may equal W), or NULL */
+  const int32_t* target_row;   /* [N] row of target_hidden for each row, or NULL = identity */
+  const uint8_t* mask;         /* [N] 0 = masked, or NULL = no mask */
+  float weights[SPECLOSS_NUM_KINDS]; /* per-kind weight, used as given (not normalised); 0 = off */
+  specloss_trace* trace;       /* NULL, or a trace that records every launch of the call */
+} specloss_problem;
+
+/*
+ * Bytes of device workspace needed when at most `max_chunk_rows` rows are
+ * processed per chunk (rounded up to a multiple of 256; <= 0 selects 8192).
+ * The backward stages a bf16 (fp32 for fp32 inputs) logit-gradient chunk of
+ * about 2 * chunk * V elements; no buffer of N x V elements is ever needed.
+ * The calls pick the largest chunk that fits the workspace they are given.
+ */
+int lmhead_loss_workspace_size(const specloss_problem* p, int64_t max_chunk_rows, size_t* bytes);
+
+/* Bytes of the `saved` buffer for n_rows rows (256-byte aligned arrays). */
+size_t specloss_saved_bytes(int64_t n_rows);
+
+/*
+ * Forward.  Outputs (device):
+ *   loss      [N]    fp32, required: sum_k weights[k] * L_k(row), 0 on invalid rows.
+ *   term_loss [K][N] fp32 or NULL: unweighted L_k(row) for every kind k
+ *                    (rows of kinds that are off are left untouched); the
+ *                    speculators page logs each term before its weight.
+ *   lse_q     [N]    fp32 or NULL: logsumexp of the draft logits.
+ *   saved            specloss_saved_bytes(N) bytes or NULL: state for the backward.
+ *   counts    [2]    int64, required: n_valid, n_bad (unmasked rows with an
+ *                    out-of-range label or target row; treated as masked).
+ *   reduced   [1+K]  fp32 or NULL: sum(loss)/n_valid, then sum(L_k)/n_valid
+ *                    for each kind (0 when n_valid == 0).
+ */
+int lmhead_loss_fwd(const specloss_problem* p, void* workspace, size_t ws_bytes, float* loss,
+                    float* term_loss, float* lse_q, void* saved, int64_t* counts, float* reduced,
+                    hipStream_t stream);
+
+/*
+ * Backward of sum_r seed_r * loss_r, with
+ *   seed_r = (grad_loss ? grad_loss[r] : 0) + (grad_mean ? grad_mean[0] / n_valid : 0)
+ * on valid rows and 0 elsewhere (grad_mean is the gradient of the mean
+ * loss; counts and saved come from lmhead_loss_fwd on the same problem).
+ * At least one of grad_loss, grad_mean is non-NULL.
+ *   dhidden [N, H] in dh_dtype (fp32 or bf16), or NULL to skip.
+ *   dW      [V, H] fp32, or NULL to skip.  accumulate_dW != 0 adds to its
+ *           contents, else it is overwritten.  Gradients flow to the draft
+ *           side only (no gradient for target_hidden or W_t).
+ */
+int lmhead_loss_bwd(const specloss_problem* p, const float* grad_loss, const float* grad_mean,
+                    const int64_t* counts, const void* saved, void* workspace, size_t ws_bytes,
+                    void* dhidden, int32_t dh_dtype, float* dW, int accumulate_dW,
+                    hipStream_t stream);
+
+/*
+ * Alignment before chunking for draft heads (blog, "Correctness: alignment
+ * before chunking"): head k predicts `shifts[k]` tokens ahead.  Rows are
+ * head-major, row = (k * batch + b) * seq_len + t, and its target row is
+ * b * seq_len + t + shifts[k] when that position is inside the sequence
+ * and (if loss_mask != NULL) loss_mask of that position is nonzero; then
+ * mask_out = 1, else mask_out = 0 and target_row_out = -1.
+ *   shifts         host [n_heads], each >= 0
+ *   loss_mask      device [batch * seq_len] or NULL
+ *   target_row_out device int32 [n_heads * batch * seq_len]
+ *   mask_out       device uint8 [n_heads * batch * seq_len]
+ */
+int specloss_align_heads(int64_t seq_len, int64_t batch, int32_t n_heads, const int32_t* shifts,
+                         const uint8_t* loss_mask, int32_t* target_row_out, uint8_t* mask_out,
+                         hipStream_t stream);
+
+/*
+ * Kernel trace for measurement.  specloss_trace_create makes `capacity`
+ * pairs of HIP events on the current device (the only HIP objects the
+ * library ever creates; NULL on failure).  While a problem's `trace` field
+ * points at it, each kernel launch of lmhead_loss_fwd / lmhead_loss_bwd is
+ * bracketed by an event pair recorded on the call's stream, together with
+ * a kernel id (specloss_kernel_name) and its algorithmic work (flops for
+ * the contractions, bytes moved for the row kernels).  Launches beyond the
+ * capacity are counted but not recorded.  specloss_trace_read waits for the
+ * recorded events and returns up to `max` entries (milliseconds per
+ * launch); specloss_trace_reset forgets them.  A trace must not be used by
+ * two calls at the same time.
+ */
+specloss_trace* specloss_trace_create(int32_t capacity);
+void specloss_trace_destroy(specloss_trace* t);
+void specloss_trace_reset(specloss_trace* t);
+int specloss_trace_read(specloss_trace* t, int32_t max, int32_t* kernel_id, float* ms,
+                        double* work, int32_t* count);
+const char* specloss_kernel_name(int32_t id);
+
+const char* specloss_strerror(int code);
+const char* specloss_kind_name(int kind); /* "ce_label","ce","kl_div","rkl","jsd","tv","nla","lk_hybrid" */
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPECLOSS_H */

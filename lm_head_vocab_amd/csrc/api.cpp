@@ -1,0 +1,636 @@
+// C-ABI of libspecloss: argument checks, workspace plan and launch sequence.
+//
+// Forward, per chunk of rows (blog "Streaming Cross Entropy": tokens are
+// independent, so rows are processed in chunks and only per-row statistics
+// survive a chunk):
+//   pass 1   k_stats on (W, hidden)        -> per (vocab tile, row) max / sum-exp
+//            k_stats on (W_t, target rows) -> same plus argmax (target kinds)
+//   merge    k_combine1 -> logsumexp of q and p, argmax p
+//   gather   k_rowdot   -> label logit z_y (ce_label) and z at argmax p (ce)
+//   pass 2   k_div      -> alpha, S, KL, rKL, JSD, E_q[g] partials (divergences)
+//   losses   k_combine2 -> per-row weighted loss, unweighted terms, saved stats
+// then k_reduce -> sum / n_valid (blog "Backward pass": one denominator).
+// Backward, per chunk (blog "Backward pass": per-chunk logits, gradients for
+// the chunk's hidden states, LM-head gradient accumulated over chunks):
+//   k_dz (recompute + logit gradient) -> staged dz chunk, both layouts
+//   k_gemm dh = dz W^T^T  and  k_gemm dW (+)= dz^T h, chunks in order.
+#include <math.h>
+#include <string.h>
+
+#include <new>
+
+#include "launch.hpp"
+#include "specloss.h"
+
+using namespace specloss;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr int64_t kDefaultChunk = 8192;
+constexpr int64_t kChunkQuantum = 256;
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+int64_t cdiv(int64_t x, int64_t m) { return (x + m - 1) / m; }
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+struct KindSet {
+  uint32_t active = 0;  // bit k = weight k nonzero
+  bool label = false;   // ce_label on
+  bool target = false;  // any kind needing the target side
+  bool pass2 = false;   // any divergence needing a second sweep
+  bool dual_bwd = false;
+  uint32_t need = 0;    // SUM_* bits
+};
+
+KindSet kinds_of(const float* w) {
+  KindSet k;
+  for (int i = 0; i < kNumKinds; ++i)
+    if (w[i] != 0.0f) k.active |= 1u << i;
+  auto on = [&](int i) { return (k.active >> i) & 1u; };
+  k.label = on(SPECLOSS_CE_LABEL);
+  k.target = (k.active & ~(1u << SPECLOSS_CE_LABEL)) != 0;
+  if (on(SPECLOSS_KL)) k.need |= SUM_KL;
+  if (on(SPECLOSS_RKL)) k.need |= SUM_RKL;
+  if (on(SPECLOSS_JSD)) k.need |= SUM_JSD | SUM_EQG;
+  if (on(SPECLOSS_TV) || on(SPECLOSS_NLA)) k.need |= SUM_ALPHA | SUM_S;
+  if (on(SPECLOSS_LK_HYBRID)) k.need |= SUM_ALPHA | SUM_S | SUM_KL;
+  if (k.need) k.need |= SUM_ALPHA;  // alpha is reported whenever a second sweep runs
+  k.pass2 = k.need != 0;
+  k.dual_bwd = (k.active & ~((1u << SPECLOSS_CE_LABEL) | (1u << SPECLOSS_CE_ARGMAX_P))) != 0;
+  return k;
+}
+
+size_t elem_size(const specloss_problem* p) { return p->in_dtype == SPECLOSS_BF16 ? 2 : 4; }
+
+int check_problem(const specloss_problem* p, KindSet* ks) {
+  if (!p) return SPECLOSS_E_INVAL;
+  if (p->n_rows <= 0 || p->hidden <= 0 || p->vocab <= 0) return SPECLOSS_E_INVAL;
+  if (p->n_rows > INT32_MAX / 2 || p->vocab > INT32_MAX / 2 || p->hidden > INT32_MAX / 2)
+    return SPECLOSS_E_UNSUPPORTED;
+  if (p->reserved != 0) return SPECLOSS_E_INVAL;
+  if (p->in_dtype != SPECLOSS_F32 && p->in_dtype != SPECLOSS_BF16) return SPECLOSS_E_UNSUPPORTED;
+  if (p->hidden % 64 != 0) return SPECLOSS_E_UNSUPPORTED;
+  if (!p->hidden_states || !p->W) return SPECLOSS_E_INVAL;
+  if (!aligned(p->hidden_states, 16) || !aligned(p->W, 16)) return SPECLOSS_E_UNSUPPORTED;
+  for (int i = 0; i < kNumKinds; ++i)
+    if (!isfinite(p->weights[i])) return SPECLOSS_E_INVAL;
+  KindSet k = kinds_of(p->weights);
+  if (!k.active) return SPECLOSS_E_INVAL;
+  if (k.label) {
+    if (!p->labels) return SPECLOSS_E_INVAL;
+    if (!aligned(p->labels, 4)) return SPECLOSS_E_UNSUPPORTED;
+  }
+  if (k.target) {
+    if (!p->target_hidden || !p->W_t || p->n_target_rows <= 0) return SPECLOSS_E_INVAL;
+    if (p->n_target_rows > INT32_MAX / 2) return SPECLOSS_E_UNSUPPORTED;
+    if (!aligned(p->target_hidden, 16) || !aligned(p->W_t, 16)) return SPECLOSS_E_UNSUPPORTED;
+    if (p->target_row) {
+      if (!aligned(p->target_row, 4)) return SPECLOSS_E_UNSUPPORTED;
+    } else if (p->n_target_rows < p->n_rows) {
+      return SPECLOSS_E_INVAL;  // identity map needs a target row per row
+    }
+  }
+  *ks = k;
+  return SPECLOSS_OK;
+}
+
+// Workspace: a head used by both directions, then the forward and backward
+// regions, which overlap (the two directions never run at the same time on
+// one workspace).
+struct Layout {
+  int64_t N, H, V, Vp, Tv, Nc;
+  size_t es;
+  // head
+  size_t terms, saved, seed, head_end;
+  // forward
+  size_t pz, pu, p2, zy, fwd_end;
+  // backward
+  size_t wt, ht, dz, dzt, bwd_end;
+};
+
+Layout plan(const specloss_problem* p, const KindSet& k, int64_t Nc) {
+  Layout L;
+  L.N = p->n_rows;
+  L.H = p->hidden;
+  L.V = p->vocab;
+  L.Vp = round_up(L.V, kVocabTile);
+  L.Tv = L.Vp / kVocabTile;
+  L.Nc = Nc;
+  L.es = elem_size(p);
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o = align_up(o + bytes, kAlign);
+    return at;
+  };
+  L.terms = take((size_t)kNumKinds * L.N * 4);
+  L.saved = take(specloss_saved_bytes(L.N));
+  L.seed = take((size_t)L.N * 4);
+  L.head_end = o;
+  const size_t tile_cols = (size_t)L.Tv * Nc * 4;
+  L.pz = take(2 * tile_cols);
+  L.pu = take(k.target ? 3 * tile_cols : 0);
+  L.p2 = take(k.pass2 ? (size_t)kNumSums * tile_cols : 0);
+  L.zy = take(2 * (size_t)Nc * 4);
+  L.fwd_end = o;
+  o = L.head_end;
+  L.wt = take((size_t)L.H * L.Vp * L.es);
+  L.ht = take((size_t)L.H * Nc * L.es);
+  L.dz = take((size_t)Nc * L.Vp * L.es);
+  L.dzt = take((size_t)L.Vp * Nc * L.es);
+  L.bwd_end = o;
+  return L;
+}
+
+// largest chunk (multiple of 256, at most the padded row count) whose region fits
+int64_t pick_chunk(const specloss_problem* p, const KindSet& k, size_t ws_bytes, bool bwd) {
+  const int64_t top = round_up(p->n_rows, kChunkQuantum);
+  int64_t lo = 1, hi = top / kChunkQuantum, best = 0;
+  while (lo <= hi) {  // the requirement grows with the chunk
+    const int64_t mid = (lo + hi) / 2;
+    const Layout L = plan(p, k, mid * kChunkQuantum);
+    if ((bwd ? L.bwd_end : L.fwd_end) <= ws_bytes) {
+      best = mid;
+      lo = mid + 1;
+    } else {
+      hi = mid - 1;
+    }
+  }
+  return best * kChunkQuantum;
+}
+
+SavedView saved_view(void* base, int64_t n) {
+  const size_t stride = align_up((size_t)n * 4, kAlign);
+  char* b = static_cast<char*>(base);
+  SavedView v;
+  v.lse_q = reinterpret_cast<float*>(b + 0 * stride);
+  v.lse_p = reinterpret_cast<float*>(b + 1 * stride);
+  v.y_label = reinterpret_cast<int32_t*>(b + 2 * stride);
+  v.y_arg = reinterpret_cast<int32_t*>(b + 3 * stride);
+  v.alpha = reinterpret_cast<float*>(b + 4 * stride);
+  v.S = reinterpret_cast<float*>(b + 5 * stride);
+  v.rkl = reinterpret_cast<float*>(b + 6 * stride);
+  v.eqg = reinterpret_cast<float*>(b + 7 * stride);
+  v.flags = reinterpret_cast<int32_t*>(b + 8 * stride);
+  return v;
+}
+
+GemmOperand op(const void* base, int64_t ld, int64_t n_rows, const int32_t* map = nullptr,
+               int64_t map_len = 0) {
+  GemmOperand g;
+  g.base = base;
+  g.ld = ld;
+  g.n_rows = (int32_t)n_rows;
+  g.map = map;
+  g.map_len = (int32_t)map_len;
+  return g;
+}
+
+const void* offset_rows(const void* base, int64_t rows, int64_t H, size_t es) {
+  return static_cast<const char*>(base) + (size_t)rows * H * es;
+}
+
+// target-side B operand for chunk rows [r0, r0 + rows)
+GemmOperand target_operand(const specloss_problem* p, int64_t r0, int64_t rows, size_t es) {
+  if (p->target_row) return op(p->target_hidden, p->hidden, p->n_target_rows, p->target_row + r0, rows);
+  return op(offset_rows(p->target_hidden, r0, p->hidden, es), p->hidden, rows);
+}
+
+#define HIP_TRY(expr)                                   \
+  do {                                                  \
+    if ((expr) != hipSuccess) return SPECLOSS_E_HIP;    \
+  } while (0)
+
+enum KernelId : int32_t {
+  K_VALIDITY, K_STATS_Q, K_STATS_P, K_COMBINE1, K_ROWDOT, K_DIV, K_COMBINE2, K_REDUCE, K_COPY,
+  K_SEED, K_TRANSPOSE_W, K_TRANSPOSE_H, K_DZ, K_GEMM_DH, K_GEMM_DW, K_NUM_IDS
+};
+const char* const kKernelNames[K_NUM_IDS] = {
+    "validity", "stats_q", "stats_p", "combine1", "rowdot", "div", "combine2", "reduce",
+    "copy_lse", "seed", "transpose_W", "transpose_h", "dz", "gemm_dh", "gemm_dW"};
+
+// Brackets launches with the trace's events when the problem carries one.
+struct Tracer {
+  specloss_trace* t;
+  hipStream_t s;
+  int begin(int32_t id, double work);
+  void end(int i);
+};
+
+#define TRACED(tr, id, work, expr)                       \
+  do {                                                   \
+    const int ti_ = (tr).begin((id), (work));            \
+    const hipError_t e_ = (expr);                        \
+    (tr).end(ti_);                                       \
+    if (e_ != hipSuccess) return SPECLOSS_E_HIP;         \
+  } while (0)
+
+}  // namespace
+
+struct specloss_trace {
+  int32_t capacity;
+  int32_t count;
+  hipEvent_t* ev;  // 2 * capacity: begin, end
+  int32_t* ids;
+  double* work;
+};
+
+namespace {
+int Tracer::begin(int32_t id, double w) {
+  if (!t) return -1;
+  const int i = t->count++;
+  if (i >= t->capacity) return -1;
+  t->ids[i] = id;
+  t->work[i] = w;
+  hipEventRecord(t->ev[2 * i], s);
+  return i;
+}
+void Tracer::end(int i) {
+  if (t && i >= 0) hipEventRecord(t->ev[2 * i + 1], s);
+}
+}  // namespace
+
+extern "C" {
+
+size_t specloss_saved_bytes(int64_t n_rows) {
+  if (n_rows <= 0) return 0;
+  return (size_t)SPECLOSS_SAVED_FIELDS * align_up((size_t)n_rows * 4, kAlign);
+}
+
+int lmhead_loss_workspace_size(const specloss_problem* p, int64_t max_chunk_rows, size_t* bytes) {
+  KindSet k;
+  const int rc = check_problem(p, &k);
+  if (rc) return rc;
+  if (!bytes) return SPECLOSS_E_INVAL;
+  int64_t nc = max_chunk_rows <= 0 ? kDefaultChunk : max_chunk_rows;
+  nc = round_up(nc, kChunkQuantum);
+  nc = nc < round_up(p->n_rows, kChunkQuantum) ? nc : round_up(p->n_rows, kChunkQuantum);
+  const Layout L = plan(p, k, nc);
+  *bytes = L.fwd_end > L.bwd_end ? L.fwd_end : L.bwd_end;
+  return SPECLOSS_OK;
+}
+
+int lmhead_loss_fwd(const specloss_problem* p, void* workspace, size_t ws_bytes, float* loss,
+                    float* term_loss, float* lse_q, void* saved, int64_t* counts, float* reduced,
+                    hipStream_t stream) {
+  KindSet k;
+  int rc = check_problem(p, &k);
+  if (rc) return rc;
+  if (!loss || !counts) return SPECLOSS_E_INVAL;
+  if (!aligned(loss, 4) || !aligned(term_loss, 4) || !aligned(lse_q, 4) || !aligned(saved, 4) ||
+      !aligned(counts, 8) || !aligned(reduced, 4))
+    return SPECLOSS_E_UNSUPPORTED;
+  if (!workspace || !aligned(workspace, kAlign)) return SPECLOSS_E_WORKSPACE;
+  const int64_t Nc = pick_chunk(p, k, ws_bytes, false);
+  if (Nc <= 0) return SPECLOSS_E_WORKSPACE;
+  const Layout L = plan(p, k, Nc);
+  char* ws = static_cast<char*>(workspace);
+  const bool bf16 = p->in_dtype == SPECLOSS_BF16;
+  const int64_t N = L.N, H = L.H;
+  const SavedView sv = saved_view(saved ? saved : ws + L.saved, N);
+  float* terms = term_loss ? term_loss : reinterpret_cast<float*>(ws + L.terms);
+  float* pz = reinterpret_cast<float*>(ws + L.pz);
+  float* pu = reinterpret_cast<float*>(ws + L.pu);
+  float* p2 = reinterpret_cast<float*>(ws + L.p2);
+  float* zy = reinterpret_cast<float*>(ws + L.zy);
+  const int64_t tile_cols = L.Tv * Nc;
+  Tracer tr{p->trace, stream};
+
+  ValidityLaunch va;
+  va.n = N;
+  va.mask = p->mask;
+  va.labels = p->labels;
+  va.use_labels = k.label;
+  va.target_row = p->target_row;
+  va.n_target = p->n_target_rows;
+  va.use_target = k.target;
+  va.vocab = (int32_t)p->vocab;
+  va.flags = sv.flags;
+  va.y_label = sv.y_label;
+  va.counts = counts;
+  TRACED(tr, K_VALIDITY, (double)N * 10, launch_validity(va, stream));
+
+  for (int64_t r0 = 0; r0 < N; r0 += Nc) {
+    const int64_t rows = (N - r0) < Nc ? (N - r0) : Nc;
+    const GemmOperand Bh = op(offset_rows(p->hidden_states, r0, H, L.es), H, rows);
+
+    StatsLaunch sz;
+    sz.A = op(p->W, H, p->vocab);
+    sz.B = Bh;
+    sz.k_len = (int32_t)H;
+    sz.vocab = (int32_t)p->vocab;
+    sz.tiles_m = (int32_t)L.Tv;
+    sz.tiles_n = (int32_t)cdiv(rows, 256);
+    sz.ncols = (int32_t)rows;
+    sz.ldp = (int32_t)Nc;
+    sz.pm = pz;
+    sz.ps = pz + tile_cols;
+    sz.pi = nullptr;
+    TRACED(tr, K_STATS_Q, 2.0 * rows * H * p->vocab, launch_stats(bf16, false, sz, stream));
+
+    if (k.target) {
+      StatsLaunch su = sz;
+      su.A = op(p->W_t, H, p->vocab);
+      su.B = target_operand(p, r0, rows, L.es);
+      su.pm = pu;
+      su.ps = pu + tile_cols;
+      su.pi = reinterpret_cast<int32_t*>(pu + 2 * tile_cols);
+      TRACED(tr, K_STATS_P, 2.0 * rows * H * p->vocab, launch_stats(bf16, true, su, stream));
+    }
+
+    Combine1Launch c1;
+    c1.tiles_m = (int32_t)L.Tv;
+    c1.ncols = (int32_t)rows;
+    c1.ldp = (int32_t)Nc;
+    c1.pm_z = pz;
+    c1.ps_z = pz + tile_cols;
+    c1.pm_u = k.target ? pu : nullptr;
+    c1.ps_u = k.target ? pu + tile_cols : nullptr;
+    c1.pi_u = k.target ? reinterpret_cast<const int32_t*>(pu + 2 * tile_cols) : nullptr;
+    c1.lse_q = sv.lse_q + r0;
+    c1.lse_p = sv.lse_p + r0;
+    c1.y_arg = sv.y_arg + r0;
+    TRACED(tr, K_COMBINE1, (k.target ? 5.0 : 2.0) * L.Tv * rows * 4, launch_combine1(c1, stream));
+
+    const bool ce_lab = (k.active >> SPECLOSS_CE_LABEL) & 1u;
+    const bool ce_arg = (k.active >> SPECLOSS_CE_ARGMAX_P) & 1u;
+    if (ce_lab || ce_arg) {
+      RowdotLaunch rd;
+      rd.W = p->W;
+      rd.h = offset_rows(p->hidden_states, r0, H, L.es);
+      rd.H = H;
+      rd.ncols = (int32_t)rows;
+      rd.vocab = (int32_t)p->vocab;
+      rd.y1 = ce_lab ? sv.y_label + r0 : nullptr;
+      rd.y2 = ce_arg ? sv.y_arg + r0 : nullptr;
+      rd.out1 = zy;
+      rd.out2 = zy + Nc;
+      TRACED(tr, K_ROWDOT, 2.0 * rows * H * L.es * ((ce_lab ? 1 : 0) + (ce_arg ? 1 : 0)), launch_rowdot(bf16, rd, stream));
+    }
+
+    if (k.pass2) {
+      DivLaunch dv;
+      dv.Az = op(p->W, H, p->vocab);
+      dv.Bz = Bh;
+      dv.Au = op(p->W_t, H, p->vocab);
+      dv.Bu = target_operand(p, r0, rows, L.es);
+      dv.k_len = (int32_t)H;
+      dv.vocab = (int32_t)p->vocab;
+      dv.tiles_m = (int32_t)L.Tv;
+      dv.tiles_n = (int32_t)cdiv(rows, 128);
+      dv.ncols = (int32_t)rows;
+      dv.ldp = (int32_t)Nc;
+      dv.lse_q = sv.lse_q + r0;
+      dv.lse_p = sv.lse_p + r0;
+      dv.need = k.need;
+      dv.part = p2;
+      dv.part_stride = tile_cols;
+      TRACED(tr, K_DIV, 4.0 * rows * H * p->vocab, launch_div(bf16, dv, stream));
+    }
+
+    Combine2Launch c2;
+    c2.tiles_m = (int32_t)L.Tv;
+    c2.ncols = (int32_t)rows;
+    c2.ldp = (int32_t)Nc;
+    c2.part = p2;
+    c2.part_stride = tile_cols;
+    c2.need = k.need;
+    memcpy(c2.w, p->weights, sizeof(c2.w));
+    c2.flags = sv.flags + r0;
+    c2.lse_q = sv.lse_q + r0;
+    c2.zy_lab = ce_lab ? zy : nullptr;
+    c2.zy_arg = ce_arg ? zy + Nc : nullptr;
+    c2.loss = loss + r0;
+    c2.term = terms + r0;
+    c2.term_stride = N;
+    c2.alpha = sv.alpha + r0;
+    c2.S = sv.S + r0;
+    c2.rkl = sv.rkl + r0;
+    c2.eqg = sv.eqg + r0;
+    TRACED(tr, K_COMBINE2, (double)rows * 4 * (2 + __builtin_popcount(k.need) * L.Tv), launch_combine2(c2, stream));
+  }
+
+  if (reduced) {
+    ReduceLaunch rl;
+    rl.n = N;
+    rl.loss = loss;
+    rl.term = terms;
+    rl.term_stride = N;
+    rl.active = k.active;
+    rl.counts = counts;
+    rl.reduced = reduced;
+    TRACED(tr, K_REDUCE, (double)N * 4 * (1 + __builtin_popcount(k.active)), launch_reduce(rl, stream));
+  }
+  if (lse_q) TRACED(tr, K_COPY, (double)N * 8, hipMemcpyAsync(lse_q, sv.lse_q, (size_t)N * 4, hipMemcpyDeviceToDevice, stream));
+  return SPECLOSS_OK;
+}
+
+int lmhead_loss_bwd(const specloss_problem* p, const float* grad_loss, const float* grad_mean,
+                    const int64_t* counts, const void* saved, void* workspace, size_t ws_bytes,
+                    void* dhidden, int32_t dh_dtype, float* dW, int accumulate_dW,
+                    hipStream_t stream) {
+  KindSet k;
+  int rc = check_problem(p, &k);
+  if (rc) return rc;
+  if (!saved || !counts) return SPECLOSS_E_INVAL;
+  if (!grad_loss && !grad_mean) return SPECLOSS_E_INVAL;
+  if (!dhidden && !dW) return SPECLOSS_E_INVAL;
+  if (dh_dtype != SPECLOSS_F32 && dh_dtype != SPECLOSS_BF16) return SPECLOSS_E_UNSUPPORTED;
+  if (!aligned(grad_loss, 4) || !aligned(grad_mean, 4) || !aligned(counts, 8) ||
+      !aligned(saved, 4) || !aligned(dW, 4) ||
+      !aligned(dhidden, dh_dtype == SPECLOSS_F32 ? 4 : 2))
+    return SPECLOSS_E_UNSUPPORTED;
+  if (!workspace || !aligned(workspace, kAlign)) return SPECLOSS_E_WORKSPACE;
+  const int64_t Nc = pick_chunk(p, k, ws_bytes, true);
+  if (Nc <= 0) return SPECLOSS_E_WORKSPACE;
+  const Layout L = plan(p, k, Nc);
+  char* ws = static_cast<char*>(workspace);
+  const bool bf16 = p->in_dtype == SPECLOSS_BF16;
+  const int64_t N = L.N, H = L.H, V = L.V, Vp = L.Vp;
+  const SavedView sv = saved_view(const_cast<void*>(saved), N);
+  float* seed = reinterpret_cast<float*>(ws + L.seed);
+  void* wt = ws + L.wt;
+  void* ht = ws + L.ht;
+  void* dz = ws + L.dz;
+  void* dzt = ws + L.dzt;
+  const size_t dh_es = dh_dtype == SPECLOSS_BF16 ? 2 : 4;
+  Tracer tr{p->trace, stream};
+
+  SeedLaunch sd;
+  sd.n = N;
+  sd.flags = sv.flags;
+  sd.grad_loss = grad_loss;
+  sd.grad_mean = grad_mean;
+  sd.counts = counts;
+  sd.seed = seed;
+  TRACED(tr, K_SEED, (double)N * 12, launch_seed(sd, stream));
+  if (dhidden) TRACED(tr, K_TRANSPOSE_W, 2.0 * Vp * H * L.es, launch_transpose(bf16, p->W, V, H, wt, Vp, stream));
+
+  int chunk = 0;
+  for (int64_t r0 = 0; r0 < N; r0 += Nc, ++chunk) {
+    const int64_t rows = (N - r0) < Nc ? (N - r0) : Nc;
+    const void* hc = offset_rows(p->hidden_states, r0, H, L.es);
+    if (dW) TRACED(tr, K_TRANSPOSE_H, 2.0 * Nc * H * L.es, launch_transpose(bf16, hc, rows, H, ht, Nc, stream));
+
+    DzLaunch dl;
+    dl.Az = op(p->W, H, V);
+    dl.Bz = op(hc, H, rows);
+    if (k.dual_bwd) {
+      dl.Au = op(p->W_t, H, V);
+      dl.Bu = target_operand(p, r0, rows, L.es);
+    } else {
+      dl.Au = dl.Az;
+      dl.Bu = dl.Bz;
+    }
+    dl.k_len = (int32_t)H;
+    dl.vocab = (int32_t)V;
+    dl.tiles_m = (int32_t)L.Tv;
+    dl.tiles_n = (int32_t)cdiv(rows, k.dual_bwd ? 128 : 256);
+    dl.ncols = (int32_t)rows;
+    dl.r0 = r0;
+    dl.seed = seed;
+    dl.sv = sv;
+    memcpy(dl.w, p->weights, sizeof(dl.w));
+    dl.dz = dz;
+    dl.ld_dz = Vp;
+    dl.dzt = dzt;
+    dl.ld_dzt = Nc;
+    TRACED(tr, K_DZ, (k.dual_bwd ? 4.0 : 2.0) * rows * H * V, launch_dz(bf16, k.dual_bwd, dl, stream));
+
+    if (dhidden) {
+      GemmLaunch g;
+      g.A = op(dz, Vp, Nc);
+      g.B = op(wt, Vp, H);
+      g.k_len = (int32_t)Vp;
+      g.tiles_m = (int32_t)cdiv(rows, 256);
+      g.tiles_n = (int32_t)cdiv(H, 256);
+      g.m_valid = (int32_t)rows;
+      g.n_valid = (int32_t)H;
+      g.C = static_cast<char*>(dhidden) + (size_t)r0 * H * dh_es;
+      g.ldc = H;
+      g.accumulate = 0;
+      g.out_bf16 = dh_dtype == SPECLOSS_BF16;
+      TRACED(tr, K_GEMM_DH, 2.0 * rows * H * V, launch_gemm(bf16, g, stream));
+    }
+    if (dW) {
+      GemmLaunch g;
+      g.A = op(dzt, Nc, Vp);
+      g.B = op(ht, Nc, H);
+      g.k_len = (int32_t)round_up(rows, 64);
+      g.tiles_m = (int32_t)L.Tv;
+      g.tiles_n = (int32_t)cdiv(H, 256);
+      g.m_valid = (int32_t)V;
+      g.n_valid = (int32_t)H;
+      g.C = dW;
+      g.ldc = H;
+      g.accumulate = (chunk > 0 || accumulate_dW) ? 1 : 0;
+      g.out_bf16 = 0;
+      TRACED(tr, K_GEMM_DW, 2.0 * rows * H * V, launch_gemm(bf16, g, stream));
+    }
+  }
+  return SPECLOSS_OK;
+}
+
+int specloss_align_heads(int64_t seq_len, int64_t batch, int32_t n_heads, const int32_t* shifts,
+                         const uint8_t* loss_mask, int32_t* target_row_out, uint8_t* mask_out,
+                         hipStream_t stream) {
+  if (seq_len <= 0 || batch <= 0 || n_heads <= 0 || !shifts || !target_row_out || !mask_out)
+    return SPECLOSS_E_INVAL;
+  if (n_heads > 64 || seq_len * batch > INT32_MAX / 2 ||
+      (int64_t)n_heads * batch * seq_len > INT32_MAX / 2)
+    return SPECLOSS_E_UNSUPPORTED;
+  if (!aligned(target_row_out, 4)) return SPECLOSS_E_UNSUPPORTED;
+  AlignLaunch a;
+  a.seq_len = seq_len;
+  a.batch = batch;
+  a.n_heads = n_heads;
+  for (int i = 0; i < 64; ++i) a.shifts[i] = 0;
+  for (int i = 0; i < n_heads; ++i) {
+    if (shifts[i] < 0) return SPECLOSS_E_INVAL;
+    a.shifts[i] = shifts[i];
+  }
+  a.loss_mask = loss_mask;
+  a.target_row = target_row_out;
+  a.mask = mask_out;
+  HIP_TRY(launch_align(a, stream));
+  return SPECLOSS_OK;
+}
+
+specloss_trace* specloss_trace_create(int32_t capacity) {
+  if (capacity <= 0 || capacity > (1 << 20)) return nullptr;
+  specloss_trace* t = new (std::nothrow) specloss_trace;
+  if (!t) return nullptr;
+  t->capacity = capacity;
+  t->count = 0;
+  t->ev = new (std::nothrow) hipEvent_t[2 * (size_t)capacity];
+  t->ids = new (std::nothrow) int32_t[capacity];
+  t->work = new (std::nothrow) double[capacity];
+  int made = 0;
+  bool ok = t->ev && t->ids && t->work;
+  for (; ok && made < 2 * capacity; ++made)
+    if (hipEventCreate(&t->ev[made]) != hipSuccess) ok = false;
+  if (!ok) {
+    for (int i = 0; i + 1 < made; ++i) hipEventDestroy(t->ev[i]);
+    t->capacity = 0;
+    specloss_trace_destroy(t);
+    return nullptr;
+  }
+  return t;
+}
+
+void specloss_trace_destroy(specloss_trace* t) {
+  if (!t) return;
+  if (t->ev)
+    for (int i = 0; i < 2 * t->capacity; ++i) hipEventDestroy(t->ev[i]);
+  delete[] t->ev;
+  delete[] t->ids;
+  delete[] t->work;
+  delete t;
+}
+
+void specloss_trace_reset(specloss_trace* t) {
+  if (t) t->count = 0;
+}
+
+int specloss_trace_read(specloss_trace* t, int32_t max, int32_t* kernel_id, float* ms,
+                        double* work, int32_t* count) {
+  if (!t || !count || max < 0) return SPECLOSS_E_INVAL;
+  *count = t->count;
+  const int n = t->count < t->capacity ? t->count : t->capacity;
+  for (int i = 0; i < n && i < max; ++i) {
+    if (hipEventSynchronize(t->ev[2 * i + 1]) != hipSuccess) return SPECLOSS_E_HIP;
+    float e = 0.0f;
+    if (hipEventElapsedTime(&e, t->ev[2 * i], t->ev[2 * i + 1]) != hipSuccess) return SPECLOSS_E_HIP;
+    if (kernel_id) kernel_id[i] = t->ids[i];
+    if (ms) ms[i] = e;
+    if (work) work[i] = t->work[i];
+  }
+  return SPECLOSS_OK;
+}
+
+const char* specloss_kernel_name(int32_t id) {
+  if (id < 0 || id >= K_NUM_IDS) return nullptr;
+  return kKernelNames[id];
+}
+
+const char* specloss_strerror(int code) {
+  switch (code) {
+    case SPECLOSS_OK: return "success";
+    case SPECLOSS_E_INVAL: return "invalid argument";
+    case SPECLOSS_E_UNSUPPORTED: return "unsupported shape, dtype or alignment";
+    case SPECLOSS_E_WORKSPACE: return "workspace missing or too small";
+    case SPECLOSS_E_HIP: return "HIP launch failed";
+    default: return "unknown error";
+  }
+}
+
+const char* specloss_kind_name(int kind) {
+  static const char* names[kNumKinds] = {"ce_label", "ce", "kl_div", "rkl",
+                                         "jsd",      "tv", "nla",    "lk_hybrid"};
+  if (kind < 0 || kind >= kNumKinds) return nullptr;
+  return names[kind];
+}
+
+}  // extern "C"

@@ -1,0 +1,725 @@
+// HIP kernels of the streaming LM-head loss for gfx950.
+//
+// Vocab-tiled passes (one workgroup per 256-row vocabulary tile x token tile;
+// the logits tile lives only in accumulator registers):
+//   k_stats  pass 1: per (vocab tile, token) running max and sum of exp of the
+//            logits (and the argmax for the target side): blog "Streaming Cross
+//            Entropy", the logsumexp of every token without its logits row.
+//   k_div    pass 2: recomputes draft and target tiles and sums, per token,
+//            min(p,q), q*1[q<p], p log(p/q), q log(q/p) and the JSD terms with
+//            the final logsumexps (speculators "Available Losses" table).
+//   k_dz     backward recompute: forms the logit gradient of the weighted loss
+//            in registers and stages it (bf16 for bf16 inputs) for the two
+//            contractions (blog "Backward pass").
+// Plain contraction k_gemm: dh = dz W and dW (+)= dz^T h.
+// Row kernels: validity/counts, label-logit gather, partial merges, means,
+// gradient seeds, transposes and head alignment.
+//
+// Every reduction runs in a fixed order (no floating-point atomics), so
+// results are bitwise repeatable.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "launch.hpp"
+#include "tile_gemm.hpp"
+
+namespace specloss {
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+template <typename T>
+__device__ __forceinline__ Operand<T> as_op(const GemmOperand& g) {
+  return Operand<T>{static_cast<const T*>(g.base), g.ld, g.n_rows, g.map, g.map_len};
+}
+
+// Merge two (max, sum of exp(x - max)) pairs; `a` is the lower-index side.
+__device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2) {
+  const float mn = fmaxf(m, m2);
+  if (mn == -INFINITY) return;
+  s = s * fast_exp2((m - mn) * kLog2e) + s2 * fast_exp2((m2 - mn) * kLog2e);
+  m = mn;
+}
+
+// ============================================================================
+// pass 1: per-tile softmax statistics
+// ============================================================================
+template <typename T, bool ARGMAX>
+__global__ __launch_bounds__(kThreads, 1) void k_stats(StatsLaunch a) {
+  using Cfg = TileCfg<T, 256, 256>;
+  __shared__ __attribute__((aligned(16))) char smem[Cfg::LDS_BYTES];
+  int tm, tn;
+  if (!tile_of(a.tiles_m, a.tiles_n, 4, tm, tn)) return;
+
+  f32x16_t acc[Cfg::FM][Cfg::FN];
+  zero_acc<Cfg>(acc);
+  tile_mainloop<T, Cfg>(acc, as_op<T>(a.A), tm * Cfg::BM, as_op<T>(a.B), tn * Cfg::BN, a.k_len,
+                        smem);
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int v_base = tm * Cfg::BM + wm * Cfg::WM;
+  const bool tail = tm * Cfg::BM + Cfg::BM > a.vocab;
+
+  float mj[Cfg::FN], sj[Cfg::FN];
+  int ij[Cfg::FN];
+#pragma unroll
+  for (int j = 0; j < Cfg::FN; ++j) {
+    float mx = -INFINITY;
+    int idx = 0x7fffffff;
+#pragma unroll
+    for (int i = 0; i < Cfg::FM; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int v = v_base + i * 32 + frag_row(r, lane);
+        float x = acc[i][j][r];
+        if (tail && v >= a.vocab) x = -INFINITY;
+        if (ARGMAX) {
+          if (x > mx) { mx = x; idx = v; }  // strict: keeps the lowest index
+        } else {
+          mx = fmaxf(mx, x);
+        }
+      }
+    float s = 0.0f;
+    if (mx != -INFINITY) {
+      const float mb = mx * kLog2e;
+#pragma unroll
+      for (int i = 0; i < Cfg::FM; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int v = v_base + i * 32 + frag_row(r, lane);
+          float x = acc[i][j][r];
+          if (tail && v >= a.vocab) x = -INFINITY;
+          s += fast_exp2(fmaf(x, kLog2e, -mb));
+        }
+    }
+    // the two half-waves hold the same token column, rows 4 apart
+    const float mo = __shfl_xor(mx, 32);
+    const float so = __shfl_xor(s, 32);
+    const int io = ARGMAX ? __shfl_xor(idx, 32) : 0;
+    const bool lo = lane < 32;
+    float m1 = lo ? mx : mo, s1 = lo ? s : so;
+    const float m2 = lo ? mo : mx, s2 = lo ? so : s;
+    int i1 = lo ? idx : io;
+    const int i2 = lo ? io : idx;
+    if (ARGMAX) i1 = (m2 > m1) ? i2 : ((m2 == m1) ? min(i1, i2) : i1);
+    lse_merge(m1, s1, m2, s2);
+    mj[j] = m1;
+    sj[j] = s1;
+    ij[j] = i1;
+  }
+
+  // the two wave rows (wm) share token columns: wm = 1 hands its values over
+  float* red = reinterpret_cast<float*>(smem);
+  if (wm == 1 && lane < 32) {
+#pragma unroll
+    for (int j = 0; j < Cfg::FN; ++j) {
+      const int c = wn * Cfg::WN + j * 32 + lane;
+      red[c * 3 + 0] = mj[j];
+      red[c * 3 + 1] = sj[j];
+      red[c * 3 + 2] = __int_as_float(ij[j]);
+    }
+  }
+  __syncthreads();
+  if (wm == 0 && lane < 32) {
+#pragma unroll
+    for (int j = 0; j < Cfg::FN; ++j) {
+      const int c = wn * Cfg::WN + j * 32 + lane;
+      float m = mj[j], s = sj[j];
+      int id = ij[j];
+      const float m2 = red[c * 3 + 0], s2 = red[c * 3 + 1];
+      const int i2 = __float_as_int(red[c * 3 + 2]);
+      if (ARGMAX) id = (m2 > m) ? i2 : ((m2 == m) ? min(id, i2) : id);
+      lse_merge(m, s, m2, s2);
+      const int col = tn * Cfg::BN + c;
+      if (col < a.ncols) {
+        const int64_t o = (int64_t)tm * a.ldp + col;
+        a.pm[o] = m;
+        a.ps[o] = s;
+        if (ARGMAX) a.pi[o] = id;
+      }
+    }
+  }
+}
+
+// ============================================================================
+// pass 2: divergence sums with the final logsumexps
+// ============================================================================
+template <typename T>
+__global__ __launch_bounds__(kThreads, 1) void k_div(DivLaunch a) {
+  using Cfg = TileCfg<T, 256, 128>;
+  __shared__ __attribute__((aligned(16))) char smem[Cfg::LDS_BYTES];
+  int tm, tn;
+  if (!tile_of(a.tiles_m, a.tiles_n, 4, tm, tn)) return;
+
+  f32x16_t az[Cfg::FM][Cfg::FN], au[Cfg::FM][Cfg::FN];
+  zero_acc<Cfg>(az);
+  zero_acc<Cfg>(au);
+  tile_mainloop<T, Cfg>(az, as_op<T>(a.Az), tm * Cfg::BM, as_op<T>(a.Bz), tn * Cfg::BN, a.k_len,
+                        smem);
+  tile_mainloop<T, Cfg>(au, as_op<T>(a.Au), tm * Cfg::BM, as_op<T>(a.Bu), tn * Cfg::BN, a.k_len,
+                        smem);
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int v_base = tm * Cfg::BM + wm * Cfg::WM;
+  const bool tail = tm * Cfg::BM + Cfg::BM > a.vocab;
+  const uint32_t need = a.need;
+
+  float sums[Cfg::FN][kNumSums];
+#pragma unroll
+  for (int j = 0; j < Cfg::FN; ++j) {
+    const int col = min(tn * Cfg::BN + wn * Cfg::WN + j * 32 + (lane & 31), a.ncols - 1);
+    const float lq0 = a.lse_q[col], lp0 = a.lse_p[col];
+    float s_alpha = 0.f, s_s = 0.f, s_kl = 0.f, s_rkl = 0.f, s_jsd = 0.f, s_eqg = 0.f;
+#pragma unroll
+    for (int i = 0; i < Cfg::FM; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int v = v_base + i * 32 + frag_row(r, lane);
+        if (tail && v >= a.vocab) continue;
+        const float lq = az[i][j][r] - lq0;
+        const float lp = au[i][j][r] - lp0;
+        const float q = fast_exp2(lq * kLog2e);
+        const float p = fast_exp2(lp * kLog2e);
+        if (need & SUM_ALPHA) s_alpha += fminf(p, q);
+        if (need & SUM_S) s_s += (q < p) ? q : ((q == p) ? 0.5f * q : 0.0f);
+        if (need & SUM_KL) s_kl += p * (lp - lq);
+        if (need & SUM_RKL) s_rkl += q * (lq - lp);
+        if (need & (SUM_JSD | SUM_EQG)) {
+          const float lm = fast_log2(0.5f * (p + q)) * kLn2;
+          if (need & SUM_JSD) s_jsd += 0.5f * (p * (lp - lm) + q * (lq - lm));
+          if (need & SUM_EQG) s_eqg += 0.5f * q * (lq - lm);
+        }
+      }
+    float v6[kNumSums] = {s_alpha, s_s, s_kl, s_rkl, s_jsd, s_eqg};
+    const bool lo = lane < 32;
+#pragma unroll
+    for (int f = 0; f < kNumSums; ++f) {
+      const float o = __shfl_xor(v6[f], 32);
+      sums[j][f] = lo ? (v6[f] + o) : (o + v6[f]);
+    }
+  }
+
+  float* red = reinterpret_cast<float*>(smem);  // [BN][kNumSums]
+  if (wm == 1 && lane < 32) {
+#pragma unroll
+    for (int j = 0; j < Cfg::FN; ++j) {
+      const int c = wn * Cfg::WN + j * 32 + lane;
+#pragma unroll
+      for (int f = 0; f < kNumSums; ++f) red[c * kNumSums + f] = sums[j][f];
+    }
+  }
+  __syncthreads();
+  if (wm == 0 && lane < 32) {
+#pragma unroll
+    for (int j = 0; j < Cfg::FN; ++j) {
+      const int c = wn * Cfg::WN + j * 32 + lane;
+      const int col = tn * Cfg::BN + c;
+      if (col >= a.ncols) continue;
+#pragma unroll
+      for (int f = 0; f < kNumSums; ++f)
+        if (need & (1u << f))
+          a.part[f * a.part_stride + (int64_t)tm * a.ldp + col] = sums[j][f] + red[c * kNumSums + f];
+    }
+  }
+}
+
+// ============================================================================
+// backward recompute: logit gradient tile -> staged chunk (two layouts)
+// ============================================================================
+template <typename T>
+__device__ __forceinline__ void store4(T* dst, float a0, float a1, float a2, float a3);
+template <>
+__device__ __forceinline__ void store4<bf16_bits>(bf16_bits* dst, float a0, float a1, float a2,
+                                                  float a3) {
+  bf16x4_t v = {(__bf16)a0, (__bf16)a1, (__bf16)a2, (__bf16)a3};
+  *reinterpret_cast<bf16x4_t*>(dst) = v;
+}
+template <>
+__device__ __forceinline__ void store4<float>(float* dst, float a0, float a1, float a2, float a3) {
+  f32x4_t v = {a0, a1, a2, a3};
+  *reinterpret_cast<f32x4_t*>(dst) = v;
+}
+template <typename T>
+__device__ __forceinline__ void store1(T* dst, float x);
+template <>
+__device__ __forceinline__ void store1<bf16_bits>(bf16_bits* dst, float x) {
+  *reinterpret_cast<__bf16*>(dst) = (__bf16)x;
+}
+template <>
+__device__ __forceinline__ void store1<float>(float* dst, float x) {
+  *dst = x;
+}
+
+struct RowCoef {
+  float seed, lse_q, lse_p, alpha, S, rkl, eqg, lam;
+  int y_lab, y_arg;
+};
+
+template <bool DUAL>
+__device__ __forceinline__ float dz_elem(const RowCoef& c, const float* w, float z, float u,
+                                         int v) {
+  const float lq = z - c.lse_q;
+  const float q = fast_exp2(lq * kLog2e);
+  float g = 0.0f;
+  if (w[0] != 0.0f) g += w[0] * (q - (v == c.y_lab ? 1.0f : 0.0f));
+  if (w[1] != 0.0f) g += w[1] * (q - (v == c.y_arg ? 1.0f : 0.0f));
+  if (DUAL) {
+    const float lp = u - c.lse_p;
+    const float p = fast_exp2(lp * kLog2e);
+    if (w[2] != 0.0f) g += w[2] * (q - p);
+    if (w[3] != 0.0f) g += w[3] * q * (lq - lp - c.rkl);
+    if (w[4] != 0.0f) {
+      const float lm = fast_log2(0.5f * (p + q)) * kLn2;
+      g += w[4] * q * (0.5f * (lq - lm) - c.eqg);
+    }
+    if (w[5] != 0.0f || w[6] != 0.0f || w[7] != 0.0f) {
+      const float cc = (q < p) ? 1.0f : ((q == p) ? 0.5f : 0.0f);
+      const float tv = -q * (cc - c.S);
+      if (w[5] != 0.0f) g += w[5] * tv;
+      if (w[6] != 0.0f) g += w[6] * tv / c.alpha;
+      if (w[7] != 0.0f) g += w[7] * (c.lam * (q - p) + (1.0f - c.lam) * tv);
+    }
+  }
+  return g;
+}
+
+template <typename T, bool DUAL>
+__global__ __launch_bounds__(kThreads, 1) void k_dz(DzLaunch a) {
+  using Cfg = TileCfg<T, 256, (DUAL ? 128 : 256)>;
+  __shared__ __attribute__((aligned(16))) char smem[Cfg::LDS_BYTES];
+  int tm, tn;
+  if (!tile_of(a.tiles_m, a.tiles_n, 4, tm, tn)) return;
+
+  f32x16_t az[Cfg::FM][Cfg::FN];
+  f32x16_t au[DUAL ? Cfg::FM : 1][DUAL ? Cfg::FN : 1];
+  zero_acc<Cfg>(az);
+  tile_mainloop<T, Cfg>(az, as_op<T>(a.Az), tm * Cfg::BM, as_op<T>(a.Bz), tn * Cfg::BN, a.k_len,
+                        smem);
+  if constexpr (DUAL) {
+    zero_acc<Cfg>(au);
+    tile_mainloop<T, Cfg>(au, as_op<T>(a.Au), tm * Cfg::BM, as_op<T>(a.Bu), tn * Cfg::BN,
+                          a.k_len, smem);
+  }
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int v_base = tm * Cfg::BM + wm * Cfg::WM;
+  T* dz = static_cast<T*>(a.dz);
+  T* dzt = static_cast<T*>(a.dzt);
+
+#pragma unroll
+  for (int j = 0; j < Cfg::FN; ++j) {
+    const int c = tn * Cfg::BN + wn * Cfg::WN + j * 32 + (lane & 31);  // chunk row
+    const int64_t gr = a.r0 + min(c, a.ncols - 1);
+    RowCoef rc;
+    rc.seed = (c < a.ncols) ? a.seed[gr] : 0.0f;
+    rc.lse_q = a.sv.lse_q[gr];
+    rc.y_lab = a.sv.y_label[gr];
+    rc.y_arg = a.sv.y_arg[gr];
+    if (DUAL) {
+      rc.lse_p = a.sv.lse_p[gr];
+      rc.alpha = a.sv.alpha[gr];
+      rc.S = a.sv.S[gr];
+      rc.rkl = a.sv.rkl[gr];
+      rc.eqg = a.sv.eqg[gr];
+      rc.lam = __expf(-3.0f * rc.alpha);
+    }
+    const bool live = rc.seed != 0.0f;
+#pragma unroll
+    for (int i = 0; i < Cfg::FM; ++i)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        float o[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = g4 * 4 + e;
+          const int v = v_base + i * 32 + frag_row(r, lane);
+          float d = 0.0f;
+          if (live && v < a.vocab) {
+            const float u = DUAL ? au[DUAL ? i : 0][DUAL ? j : 0][r] : 0.0f;
+            d = rc.seed * dz_elem<DUAL>(rc, a.w, az[i][j][r], u, v);
+          }
+          o[e] = d;
+        }
+        const int v0 = v_base + i * 32 + frag_row(g4 * 4, lane);
+        store4<T>(dz + (int64_t)c * a.ld_dz + v0, o[0], o[1], o[2], o[3]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) store1<T>(dzt + (int64_t)(v0 + e) * a.ld_dzt + c, o[e]);
+      }
+  }
+}
+
+// ============================================================================
+// plain contraction with store / accumulate epilogue
+// ============================================================================
+template <typename T, typename OutT>
+__global__ __launch_bounds__(kThreads, 1) void k_gemm(GemmLaunch a) {
+  using Cfg = TileCfg<T, 256, 256>;
+  __shared__ __attribute__((aligned(16))) char smem[Cfg::LDS_BYTES];
+  int tm, tn;
+  if (!tile_of(a.tiles_m, a.tiles_n, 4, tm, tn)) return;
+  f32x16_t acc[Cfg::FM][Cfg::FN];
+  zero_acc<Cfg>(acc);
+  tile_mainloop<T, Cfg>(acc, as_op<T>(a.A), tm * Cfg::BM, as_op<T>(a.B), tn * Cfg::BN, a.k_len,
+                        smem);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  OutT* C = static_cast<OutT*>(a.C);
+#pragma unroll
+  for (int i = 0; i < Cfg::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < Cfg::FN; ++j) {
+      const int col = tn * Cfg::BN + wn * Cfg::WN + j * 32 + (lane & 31);
+      if (col >= a.n_valid) continue;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = tm * Cfg::BM + wm * Cfg::WM + i * 32 + frag_row(r, lane);
+        if (row >= a.m_valid) continue;
+        OutT* p = C + (int64_t)row * a.ldc + col;
+        float x = acc[i][j][r];
+        if constexpr (sizeof(OutT) == 4) {
+          if (a.accumulate) x += *reinterpret_cast<float*>(p);
+          *reinterpret_cast<float*>(p) = x;
+        } else {
+          if (a.accumulate) x += (float)*reinterpret_cast<__bf16*>(p);
+          *reinterpret_cast<__bf16*>(p) = (__bf16)x;
+        }
+      }
+    }
+}
+
+// ============================================================================
+// row kernels
+// ============================================================================
+__global__ __launch_bounds__(1024) void k_validity(ValidityLaunch a) {
+  __shared__ int64_t red[2][1024];
+  int64_t nv = 0, nb = 0;
+  for (int64_t r = threadIdx.x; r < a.n; r += 1024) {
+    int valid = a.mask ? (a.mask[r] != 0) : 1;
+    int bad = 0;
+    int lab = -1;
+    if (a.use_labels) {
+      lab = a.labels[r];
+      if (lab == -100) {
+        valid = 0;
+      } else if (lab < 0 || lab >= a.vocab) {
+        bad = valid;
+        valid = 0;
+      }
+    }
+    if (a.use_target && a.target_row) {
+      const int tr = a.target_row[r];
+      if (tr < 0 || tr >= a.n_target) {
+        bad |= valid;
+        valid = 0;
+      }
+    }
+    a.flags[r] = valid;
+    a.y_label[r] = (a.use_labels && valid) ? lab : -1;
+    nv += valid;
+    nb += bad;
+  }
+  red[0][threadIdx.x] = nv;
+  red[1][threadIdx.x] = nb;
+  __syncthreads();
+  for (int o = 512; o > 0; o >>= 1) {
+    if ((int)threadIdx.x < o) {
+      red[0][threadIdx.x] += red[0][threadIdx.x + o];
+      red[1][threadIdx.x] += red[1][threadIdx.x + o];
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    a.counts[0] = red[0][0];
+    a.counts[1] = red[1][0];
+  }
+}
+
+// one wave per row: z_y = W[y] . h[row] in fp32, fixed lane/tree order
+template <typename T>
+__global__ __launch_bounds__(256) void k_rowdot(RowdotLaunch a) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= a.ncols) return;
+  const T* h = static_cast<const T*>(a.h) + (int64_t)row * a.H;
+  const T* W = static_cast<const T*>(a.W);
+  constexpr int KC = ElemTraits<T>::kPerChunk;
+  for (int which = 0; which < 2; ++which) {
+    const int32_t* y = which ? a.y2 : a.y1;
+    float* out = which ? a.out2 : a.out1;
+    if (!y) continue;
+    const int lab = y[row];
+    const bool ok = lab >= 0 && lab < a.vocab;
+    float acc = 0.0f;
+    if (ok) {
+      const T* wr = W + (int64_t)lab * a.H;
+      for (int64_t k = (int64_t)lane * KC; k < a.H; k += 64 * KC) {
+        const i32x4_t hv = *reinterpret_cast<const i32x4_t*>(h + k);
+        const i32x4_t wv = *reinterpret_cast<const i32x4_t*>(wr + k);
+        if constexpr (sizeof(T) == 2) {
+          const bf16x8_t hb = __builtin_bit_cast(bf16x8_t, hv);
+          const bf16x8_t wb = __builtin_bit_cast(bf16x8_t, wv);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc = fmaf((float)hb[e], (float)wb[e], acc);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc = fmaf(__int_as_float(hv[e]), __int_as_float(wv[e]), acc);
+        }
+      }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o);
+    if (lane == 0) out[row] = ok ? acc : 0.0f;
+  }
+}
+
+__global__ __launch_bounds__(256) void k_combine1(Combine1Launch a) {
+  const int c = blockIdx.x * 256 + threadIdx.x;
+  if (c >= a.ncols) return;
+  {
+    float m = -INFINITY;
+    for (int t = 0; t < a.tiles_m; ++t) m = fmaxf(m, a.pm_z[(int64_t)t * a.ldp + c]);
+    float s = 0.0f;
+    for (int t = 0; t < a.tiles_m; ++t) {
+      const int64_t o = (int64_t)t * a.ldp + c;
+      s += a.ps_z[o] * expf(a.pm_z[o] - m);
+    }
+    a.lse_q[c] = m + logf(s);
+  }
+  if (a.pm_u) {
+    float m = -INFINITY;
+    int best = 0;
+    for (int t = 0; t < a.tiles_m; ++t) {
+      const float x = a.pm_u[(int64_t)t * a.ldp + c];
+      if (x > m) { m = x; best = t; }  // first tile holding the max: lowest index
+    }
+    float s = 0.0f;
+    for (int t = 0; t < a.tiles_m; ++t) {
+      const int64_t o = (int64_t)t * a.ldp + c;
+      s += a.ps_u[o] * expf(a.pm_u[o] - m);
+    }
+    a.lse_p[c] = m + logf(s);
+    a.y_arg[c] = a.pi_u[(int64_t)best * a.ldp + c];
+  } else {
+    a.lse_p[c] = 0.0f;
+    a.y_arg[c] = -1;
+  }
+}
+
+__global__ __launch_bounds__(256) void k_combine2(Combine2Launch a) {
+  const int c = blockIdx.x * 256 + threadIdx.x;
+  if (c >= a.ncols) return;
+  float sum[kNumSums];
+#pragma unroll
+  for (int f = 0; f < kNumSums; ++f) {
+    sum[f] = 0.0f;
+    if (a.need & (1u << f))
+      for (int t = 0; t < a.tiles_m; ++t) sum[f] += a.part[f * a.part_stride + (int64_t)t * a.ldp + c];
+  }
+  const float alpha = sum[0], S = sum[1], kl = sum[2], rkl = sum[3], jsd = sum[4], eqg = sum[5];
+  const bool valid = a.flags[c] != 0;
+  float L[kNumKinds];
+  L[0] = a.zy_lab ? a.lse_q[c] - a.zy_lab[c] : 0.0f;
+  L[1] = a.zy_arg ? a.lse_q[c] - a.zy_arg[c] : 0.0f;
+  L[2] = kl;
+  L[3] = rkl;
+  L[4] = jsd;
+  L[5] = 1.0f - alpha;
+  L[6] = -logf(alpha);
+  const float lam = expf(-3.0f * alpha);
+  L[7] = lam * kl + (1.0f - lam) * (1.0f - alpha);
+  float total = 0.0f;
+#pragma unroll
+  for (int k = 0; k < kNumKinds; ++k) {
+    if (a.w[k] == 0.0f) continue;
+    const float lk = valid ? L[k] : 0.0f;
+    total += a.w[k] * lk;
+    a.term[k * a.term_stride + c] = lk;
+  }
+  a.loss[c] = valid ? total : 0.0f;
+  a.alpha[c] = (a.need & SUM_ALPHA) ? alpha : 1.0f;
+  a.S[c] = S;
+  a.rkl[c] = rkl;
+  a.eqg[c] = eqg;
+}
+
+__global__ __launch_bounds__(1024) void k_reduce(ReduceLaunch a) {
+  __shared__ double red[1024];
+  const int64_t nv = a.counts[0];
+  for (int q = 0; q <= kNumKinds; ++q) {
+    const float* src;
+    if (q == 0) {
+      src = a.loss;
+    } else {
+      if (!(a.active & (1u << (q - 1)))) {
+        if (threadIdx.x == 0) a.reduced[q] = 0.0f;
+        continue;
+      }
+      src = a.term + (int64_t)(q - 1) * a.term_stride;
+    }
+    double s = 0.0;
+    for (int64_t r = threadIdx.x; r < a.n; r += 1024) s += (double)src[r];
+    red[threadIdx.x] = s;
+    __syncthreads();
+    for (int o = 512; o > 0; o >>= 1) {
+      if ((int)threadIdx.x < o) red[threadIdx.x] += red[threadIdx.x + o];
+      __syncthreads();
+    }
+    if (threadIdx.x == 0) a.reduced[q] = nv > 0 ? (float)(red[0] / (double)nv) : 0.0f;
+    __syncthreads();
+  }
+}
+
+__global__ __launch_bounds__(256) void k_seed(SeedLaunch a) {
+  const int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (r >= a.n) return;
+  const int64_t nv = a.counts[0];
+  float s = 0.0f;
+  if (a.flags[r]) {
+    if (a.grad_loss) s += a.grad_loss[r];
+    if (a.grad_mean && nv > 0) s += a.grad_mean[0] / (float)nv;
+  }
+  a.seed[r] = s;
+}
+
+// 64 x 64 tile transpose through LDS; pads columns [rows, ld_out) with zeros
+template <typename T>
+__global__ __launch_bounds__(256) void k_transpose(const T* in, int64_t rows, int64_t cols, T* out,
+                                                   int64_t ld_out) {
+  __shared__ T tile[64][65];
+  const int64_t c0 = (int64_t)blockIdx.x * 64;  // source row block (becomes out column)
+  const int64_t j0 = (int64_t)blockIdx.y * 64;  // source column block (becomes out row)
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  for (int y = ty; y < 64; y += 4) {
+    const int64_t r = c0 + y, j = j0 + tx;
+    tile[y][tx] = (r < rows && j < cols) ? in[r * cols + j] : T(0);
+  }
+  __syncthreads();
+  for (int y = ty; y < 64; y += 4) {
+    const int64_t j = j0 + y, c = c0 + tx;
+    if (j < cols && c < ld_out) out[j * ld_out + c] = tile[tx][y];
+  }
+}
+
+__global__ __launch_bounds__(256) void k_align(AlignLaunch a) {
+  const int64_t n = (int64_t)a.n_heads * a.batch * a.seq_len;
+  const int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (r >= n) return;
+  const int64_t t = r % a.seq_len;
+  const int64_t kb = r / a.seq_len;
+  const int64_t b = kb % a.batch;
+  const int k = (int)(kb / a.batch);
+  const int64_t tt = t + a.shifts[k];
+  int32_t tr = -1;
+  uint8_t m = 0;
+  if (tt < a.seq_len) {
+    const int64_t src = b * a.seq_len + tt;
+    if (!a.loss_mask || a.loss_mask[src]) {
+      tr = (int32_t)src;
+      m = 1;
+    }
+  }
+  a.target_row[r] = tr;
+  a.mask[r] = m;
+}
+
+// ============================================================================
+// launchers
+// ============================================================================
+hipError_t launch_stats(bool bf16, bool argmax, const StatsLaunch& a, hipStream_t s) {
+  const dim3 grid(grid_for_tiles(a.tiles_m * a.tiles_n)), block(kThreads);
+  if (bf16) {
+    if (argmax) hipLaunchKernelGGL((k_stats<bf16_bits, true>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((k_stats<bf16_bits, false>), grid, block, 0, s, a);
+  } else {
+    if (argmax) hipLaunchKernelGGL((k_stats<float, true>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((k_stats<float, false>), grid, block, 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_div(bool bf16, const DivLaunch& a, hipStream_t s) {
+  const dim3 grid(grid_for_tiles(a.tiles_m * a.tiles_n)), block(kThreads);
+  if (bf16) hipLaunchKernelGGL(k_div<bf16_bits>, grid, block, 0, s, a);
+  else hipLaunchKernelGGL(k_div<float>, grid, block, 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_dz(bool bf16, bool dual, const DzLaunch& a, hipStream_t s) {
+  const dim3 grid(grid_for_tiles(a.tiles_m * a.tiles_n)), block(kThreads);
+  if (bf16) {
+    if (dual) hipLaunchKernelGGL((k_dz<bf16_bits, true>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((k_dz<bf16_bits, false>), grid, block, 0, s, a);
+  } else {
+    if (dual) hipLaunchKernelGGL((k_dz<float, true>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((k_dz<float, false>), grid, block, 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm(bool bf16, const GemmLaunch& a, hipStream_t s) {
+  const dim3 grid(grid_for_tiles(a.tiles_m * a.tiles_n)), block(kThreads);
+  if (bf16) {
+    if (a.out_bf16) hipLaunchKernelGGL((k_gemm<bf16_bits, bf16_bits>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((k_gemm<bf16_bits, float>), grid, block, 0, s, a);
+  } else {
+    if (a.out_bf16) hipLaunchKernelGGL((k_gemm<float, bf16_bits>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((k_gemm<float, float>), grid, block, 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_validity(const ValidityLaunch& a, hipStream_t s) {
+  hipLaunchKernelGGL(k_validity, dim3(1), dim3(1024), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_rowdot(bool bf16, const RowdotLaunch& a, hipStream_t s) {
+  const dim3 grid((a.ncols + 3) / 4), block(256);
+  if (bf16) hipLaunchKernelGGL(k_rowdot<bf16_bits>, grid, block, 0, s, a);
+  else hipLaunchKernelGGL(k_rowdot<float>, grid, block, 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine1(const Combine1Launch& a, hipStream_t s) {
+  hipLaunchKernelGGL(k_combine1, dim3((a.ncols + 255) / 256), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine2(const Combine2Launch& a, hipStream_t s) {
+  hipLaunchKernelGGL(k_combine2, dim3((a.ncols + 255) / 256), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_reduce(const ReduceLaunch& a, hipStream_t s) {
+  hipLaunchKernelGGL(k_reduce, dim3(1), dim3(1024), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_seed(const SeedLaunch& a, hipStream_t s) {
+  hipLaunchKernelGGL(k_seed, dim3((unsigned)((a.n + 255) / 256)), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_transpose(bool bf16, const void* in, int64_t rows, int64_t cols, void* out,
+                            int64_t ld_out, hipStream_t s) {
+  const dim3 grid((unsigned)((ld_out + 63) / 64), (unsigned)((cols + 63) / 64)), block(256);
+  if (bf16)
+    hipLaunchKernelGGL(k_transpose<bf16_bits>, grid, block, 0, s,
+                       static_cast<const bf16_bits*>(in), rows, cols, static_cast<bf16_bits*>(out),
+                       ld_out);
+  else
+    hipLaunchKernelGGL(k_transpose<float>, grid, block, 0, s, static_cast<const float*>(in), rows,
+                       cols, static_cast<float*>(out), ld_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_align(const AlignLaunch& a, hipStream_t s) {
+  const int64_t n = (int64_t)a.n_heads * a.batch * a.seq_len;
+  hipLaunchKernelGGL(k_align, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace specloss

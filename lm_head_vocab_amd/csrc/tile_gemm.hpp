@@ -1,0 +1,232 @@
+// Tile machinery shared by every contraction of the streaming LM-head loss.
+//
+// One shape of contraction serves the whole path: C[m][n] = sum_k A[m][k] B[n][k]
+// with both operands K-contiguous ("NT").  The forward and the recompute take
+// A = W (vocabulary rows) and B = hidden rows; the backward contractions take
+// the staged logit gradient and transposed copies of W and of the hidden chunk,
+// so they are NT as well.
+//
+// gfx950 mapping:
+//  * 256 threads = 4 wave64s in a 2 x 2 grid; a wave owns a (BM/2) x (BN/2)
+//    sub-tile made of 32 x 32 MFMA fragments (v_mfma_f32_32x32x16_bf16 for
+//    bf16, v_mfma_f32_32x32x2_f32 for fp32), fp32 accumulators.
+//  * K advances in slabs of 128 bytes per row (64 bf16 / 32 fp32).  A slab of
+//    A and B sits in LDS as rows of eight 16-byte chunks, chunk c of row r
+//    stored at position c ^ (r & 7): eight consecutive rows read at the same
+//    logical chunk hit eight different bank groups (conflict-free ds_read_b128).
+//  * Two LDS stages; the next slab is fetched from HBM into registers while
+//    the MFMAs consume the current stage (one barrier per slab).
+//  * Workgroups are dealt round-robin to the 8 XCDs; `tile_of` renumbers them
+//    so each XCD walks a compact block of tiles and its private L2 sees the
+//    same A and B slabs from several tiles at once.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace specloss {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+typedef int i32x2_t __attribute__((ext_vector_type(2)));
+
+typedef uint16_t bf16_bits;  // storage type of bf16 tensors
+
+constexpr int kThreads = 256;
+constexpr int kRowBytes = 128;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+template <typename T>
+struct ElemTraits;
+template <>
+struct ElemTraits<bf16_bits> {
+  static constexpr int kPerChunk = 8;
+};
+template <>
+struct ElemTraits<float> {
+  static constexpr int kPerChunk = 4;
+};
+
+template <typename T, int BM_, int BN_>
+struct TileCfg {
+  static constexpr int BM = BM_, BN = BN_;
+  static constexpr int KC = ElemTraits<T>::kPerChunk;  // elements per 16-byte chunk
+  static constexpr int BK = 8 * KC;                    // elements per slab row (128 bytes)
+  static constexpr int WM = BM / 2, WN = BN / 2;       // wave sub-tile
+  static constexpr int FM = WM / 32, FN = WN / 32;     // 32x32 fragments per wave
+  static constexpr int LA = BM / 32, LB = BN / 32;     // 16-byte loads per thread per slab
+  static constexpr int STAGE = (BM + BN) * kRowBytes;  // bytes of one LDS stage
+  static constexpr int LDS_BYTES = 2 * STAGE;
+};
+
+// Rows of a K-contiguous operand.  Tile row r reads source row
+// map ? map[r] : r (relative to `base`), clamped into [0, n_rows): rows past
+// the end or unmapped rows still load valid memory and their results are
+// discarded by the epilogues.
+template <typename T>
+struct Operand {
+  const T* base;
+  int64_t ld;            // elements between rows
+  int32_t n_rows;        // valid source rows
+  const int32_t* map;    // optional gather map indexed by tile row (already offset)
+  int32_t map_len;       // entries readable in map
+};
+
+__device__ __forceinline__ int32_t clamp_row(int32_t r, int32_t n) {
+  return r < 0 ? 0 : (r >= n ? n - 1 : r);
+}
+
+template <typename T>
+__device__ __forceinline__ const T* row_ptr(const Operand<T>& op, int32_t r) {
+  int32_t src = r;
+  if (op.map != nullptr) src = op.map[r < op.map_len ? r : op.map_len - 1];
+  src = clamp_row(src, op.n_rows);
+  return op.base + (int64_t)src * op.ld;
+}
+
+// Accumulator fragment element -> tile coordinates (32x32 MFMA output layout):
+// register r of lane l holds row (r/4)*8 + (l/32)*4 + r%4 and column l%32.
+__device__ __forceinline__ int frag_row(int r, int lane) {
+  return ((r >> 2) << 3) + ((lane >> 5) << 2) + (r & 3);
+}
+
+template <typename T>
+__device__ __forceinline__ void mfma_slab_step(f32x16_t& acc, const i32x4_t& a, const i32x4_t& b);
+
+template <>
+__device__ __forceinline__ void mfma_slab_step<bf16_bits>(f32x16_t& acc, const i32x4_t& a,
+                                                          const i32x4_t& b) {
+  acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                __builtin_bit_cast(bf16x8_t, b), acc, 0, 0, 0);
+}
+
+// fp32: each lane holds four consecutive k of its row; instruction e pairs
+// element e of the low and high half-waves.  A and B use the same k
+// assignment, so the four instructions together sum over all eight k.
+template <>
+__device__ __forceinline__ void mfma_slab_step<float>(f32x16_t& acc, const i32x4_t& a,
+                                                      const i32x4_t& b) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__int_as_float(a[e]), __int_as_float(b[e]), acc,
+                                               0, 0, 0);
+}
+
+// C_tile = A[a_row0 : a_row0+BM, 0:k_len] * B[b_row0 : b_row0+BN, 0:k_len]^T,
+// accumulated into `acc` (which the caller zeroes).  k_len is a multiple of
+// Cfg::BK.  Ends with a barrier, so LDS is free for the epilogue.
+template <typename T, typename Cfg>
+__device__ __forceinline__ void tile_mainloop(f32x16_t (&acc)[Cfg::FM][Cfg::FN],
+                                              const Operand<T>& A, int32_t a_row0,
+                                              const Operand<T>& B, int32_t b_row0, int32_t k_len,
+                                              char* smem) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int lrow = tid >> 3;       // first slab row this thread loads
+  const int lchunk = tid & 7;      // 16-byte chunk this thread loads
+  const int swz = (lchunk ^ (lrow & 7)) << 4;
+
+  const T* pa[Cfg::LA];
+  const T* pb[Cfg::LB];
+#pragma unroll
+  for (int i = 0; i < Cfg::LA; ++i) pa[i] = row_ptr(A, a_row0 + lrow + 32 * i) + lchunk * Cfg::KC;
+#pragma unroll
+  for (int i = 0; i < Cfg::LB; ++i) pb[i] = row_ptr(B, b_row0 + lrow + 32 * i) + lchunk * Cfg::KC;
+
+  i32x4_t ra[Cfg::LA], rb[Cfg::LB];
+  auto gload = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < Cfg::LA; ++i) ra[i] = *reinterpret_cast<const i32x4_t*>(pa[i] + k0);
+#pragma unroll
+    for (int i = 0; i < Cfg::LB; ++i) rb[i] = *reinterpret_cast<const i32x4_t*>(pb[i] + k0);
+  };
+  auto lstore = [&](int stage) {
+    char* sa = smem + stage * Cfg::STAGE;
+    char* sb = sa + Cfg::BM * kRowBytes;
+#pragma unroll
+    for (int i = 0; i < Cfg::LA; ++i)
+      *reinterpret_cast<i32x4_t*>(sa + (lrow + 32 * i) * kRowBytes + swz) = ra[i];
+#pragma unroll
+    for (int i = 0; i < Cfg::LB; ++i)
+      *reinterpret_cast<i32x4_t*>(sb + (lrow + 32 * i) * kRowBytes + swz) = rb[i];
+  };
+
+  // per-lane LDS read offsets (row part); the chunk part depends on the step
+  const int frow = lane & 31;
+  const int half = lane >> 5;
+  const int nslab = k_len / Cfg::BK;
+
+  gload(0);
+  lstore(0);
+  __syncthreads();
+
+  for (int ks = 0; ks < nslab; ++ks) {
+    const int stage = ks & 1;
+    if (ks + 1 < nslab) gload((ks + 1) * Cfg::BK);
+    const char* sa = smem + stage * Cfg::STAGE;
+    const char* sb = sa + Cfg::BM * kRowBytes;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int chunk = 2 * s + half;
+      i32x4_t af[Cfg::FM], bfr[Cfg::FN];
+#pragma unroll
+      for (int i = 0; i < Cfg::FM; ++i) {
+        const int r = wm * Cfg::WM + i * 32 + frow;
+        af[i] = *reinterpret_cast<const i32x4_t*>(sa + r * kRowBytes + ((chunk ^ (r & 7)) << 4));
+      }
+#pragma unroll
+      for (int j = 0; j < Cfg::FN; ++j) {
+        const int r = wn * Cfg::WN + j * 32 + frow;
+        bfr[j] = *reinterpret_cast<const i32x4_t*>(sb + r * kRowBytes + ((chunk ^ (r & 7)) << 4));
+      }
+#pragma unroll
+      for (int i = 0; i < Cfg::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < Cfg::FN; ++j) mfma_slab_step<T>(acc[i][j], af[i], bfr[j]);
+    }
+    if (ks + 1 < nslab) lstore(stage ^ 1);
+    __syncthreads();
+  }
+}
+
+template <typename Cfg>
+__device__ __forceinline__ void zero_acc(f32x16_t (&acc)[Cfg::FM][Cfg::FN]) {
+#pragma unroll
+  for (int i = 0; i < Cfg::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < Cfg::FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+}
+
+// Workgroup -> tile.  Workgroups are dealt to the 8 XCDs round-robin
+// (workgroup b runs on XCD b % 8); renumber so XCD x owns the contiguous range
+// [x * per_xcd, (x+1) * per_xcd) of a grouped raster order in which
+// `group_m` consecutive tile-rows are walked column by column.  The grid must
+// have 8 * ceil(tiles / 8) workgroups; returns false for the padding ones.
+__device__ __forceinline__ bool tile_of(int tiles_m, int tiles_n, int group_m, int& tm, int& tn) {
+  const int total = tiles_m * tiles_n;
+  const int per_xcd = (total + 7) >> 3;
+  const int b = blockIdx.x;
+  const int logical = (b & 7) * per_xcd + (b >> 3);
+  if (logical >= total) return false;
+  const int group_size = group_m * tiles_n;
+  const int g = logical / group_size;
+  const int first_m = g * group_m;
+  const int gm = min(group_m, tiles_m - first_m);
+  const int idx = logical - g * group_size;
+  tm = first_m + idx % gm;
+  tn = idx / gm;
+  return true;
+}
+
+__host__ __device__ inline int grid_for_tiles(int tiles) { return ((tiles + 7) / 8) * 8; }
+
+}  // namespace specloss

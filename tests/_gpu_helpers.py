@@ -1,0 +1,115 @@
+"""Shared helpers of the GPU parity tests: upload a synthetic problem, run the
+HIP path through the C-ABI binding, and compare against the oracle."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+import lm_head_vocab_amd as L
+from lm_head_vocab_amd.runner import LossRun
+from oracle import specloss_oracle as O
+
+# acceptance bars (fixed by the benchmark spec of the path)
+LOSS_RTOL = 1e-3          # mean loss and per-term means, relative
+TOKEN_RTOL, TOKEN_ATOL = 1e-3, 1e-5   # per-token losses (derived: same bar per token)
+GRAD_FROB = 2e-2          # dh, dW relative Frobenius error
+ARGMAX_GAP = 1e-3         # argmax labels must match where the top-2 gap is at least this
+
+
+def say(msg: str) -> None:
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def to_device(prob, dev="cuda"):
+    def f(x):
+        if x is None:
+            return None
+        if prob.dtype == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(dev)
+
+    def i(x, dt):
+        return None if x is None else torch.from_numpy(np.ascontiguousarray(x).astype(dt)).to(dev)
+
+    return dict(hidden=f(prob.hidden), W=f(prob.W), labels=i(prob.labels, np.int32),
+                mask=i(prob.mask, np.uint8), target_hidden=f(prob.target_hidden), W_t=f(prob.W_t),
+                target_row=i(prob.target_row, np.int32))
+
+
+def make_run(prob, dev_inputs, **kw) -> LossRun:
+    return LossRun(dev_inputs["hidden"], dev_inputs["W"], prob.weights,
+                   labels=dev_inputs["labels"], mask=dev_inputs["mask"],
+                   target_hidden=dev_inputs["target_hidden"], W_t=dev_inputs["W_t"],
+                   target_row=dev_inputs["target_row"], **kw)
+
+
+def rel_frob(a: np.ndarray, b: np.ndarray) -> float:
+    nb = np.linalg.norm(b)
+    return float(np.linalg.norm(a - b) / (nb if nb > 0 else 1.0))
+
+
+def check_tokens(gpu: np.ndarray, ref: np.ndarray, what: str) -> None:
+    err = np.abs(gpu.astype(np.float64) - ref)
+    bad = err > TOKEN_RTOL * np.abs(ref) + TOKEN_ATOL
+    assert not bad.any(), (f"{what}: {int(bad.sum())} rows out of tolerance; worst row "
+                           f"{int(np.argmax(err))}: gpu {gpu[np.argmax(err)]} ref {ref[np.argmax(err)]}")
+
+
+def check_argmax(gpu_y: np.ndarray, prob, rows, valid) -> None:
+    """Hard labels equal the oracle's wherever its top-2 target logits differ by >= ARGMAX_GAP."""
+    Wt = O.widen(prob.W_t, prob.dtype)
+    tr = rows if prob.target_row is None else np.asarray(prob.target_row)[rows]
+    g = O.widen(prob.target_hidden[np.where(valid, tr, 0)], prob.dtype)
+    u = g @ Wt.T
+    top2 = np.sort(u, axis=1)[:, -2:]
+    decisive = (top2[:, 1] - top2[:, 0] >= ARGMAX_GAP) & valid
+    ref = O.argmax_lowest(u)
+    assert np.array_equal(gpu_y[decisive], ref[decisive])
+
+
+def full_parity(prob, *, max_chunk_rows=0, check_grads=True, tag=""):
+    """Run fwd (+bwd with the mean seed) on the GPU and compare every output with the oracle."""
+    say(f"[parity] {tag} {prob.name} N={prob.n_rows} H={prob.hidden_dim} V={prob.vocab} "
+        f"dtype={prob.dtype} weights={prob.weights} chunk={max_chunk_rows}")
+    dev = to_device(prob)
+    run = make_run(prob, dev, max_chunk_rows=max_chunk_rows)
+    run.forward()
+    torch.cuda.synchronize()
+    ref = O.forward(prob)
+    mean, term_means, n_valid = O.mean_loss(prob)
+    counts = run.counts.cpu().numpy()
+    assert counts[0] == ref.n_valid and counts[1] == ref.n_bad
+    loss = run.loss.cpu().numpy()
+    check_tokens(loss, ref.loss, "per-token loss")
+    assert np.all(loss[~ref.valid] == 0.0), "masked rows must contribute exactly 0"
+    red = run.reduced.cpu().numpy()
+    assert abs(red[0] - mean) <= LOSS_RTOL * abs(mean) + 1e-7, (red[0], mean)
+    for k, v in term_means.items():
+        got = red[1 + L.KINDS.index(k)]
+        assert abs(got - v) <= LOSS_RTOL * abs(v) + 1e-7, (k, got, v)
+        check_tokens(run.term[L.KINDS.index(k)].cpu().numpy(), ref.terms[k], f"term {k}")
+    lse = run.lse_q.cpu().numpy()
+    assert np.allclose(lse[ref.valid], ref.lse_q[ref.valid], rtol=1e-5, atol=1e-4)
+    if ref.alpha is not None and any(k in ("tv", "nla", "lk_hybrid", "kl_div", "rkl", "jsd")
+                                     for k in prob.weights):
+        alpha = run.saved_field(4).cpu().numpy()
+        assert np.allclose(alpha[ref.valid], ref.alpha[ref.valid], atol=1e-4)
+    if "ce" in prob.weights:
+        y = run.saved_field(3, torch.int32).cpu().numpy()
+        check_argmax(y, prob, np.arange(prob.n_rows), ref.valid)
+    out = dict(run=run, ref=ref, loss=loss)
+    if check_grads:
+        gm = torch.ones(1, dtype=torch.float32, device="cuda")
+        dh, dW = run.backward(grad_mean=gm)
+        torch.cuda.synchronize()
+        rdh, rdW = O.backward(prob)
+        dh_np, dW_np = dh.cpu().numpy(), dW.cpu().numpy()
+        e_dh, e_dW = rel_frob(dh_np, rdh), rel_frob(dW_np, rdW)
+        say(f"   rel frob dh {e_dh:.3e} dW {e_dW:.3e}")
+        assert e_dh <= GRAD_FROB and e_dW <= GRAD_FROB
+        assert np.all(dh_np[~ref.valid] == 0.0), "masked rows must get a zero gradient"
+        out.update(dh=dh_np, dW=dW_np, rdh=rdh, rdW=rdW)
+    return out

@@ -1,0 +1,226 @@
+"""GPU parity of the HIP path against the fp64 oracle (through the C-ABI).
+
+Small cases cover every loss kind, both dtypes, masks, ignore_index, bad
+labels, ragged tails in every dimension (several 256-row vocabulary tiles,
+several token tiles, chunks) and the degenerate cases.  Bars: loss and
+per-term means rel <= 1e-3, dh/dW rel Frobenius <= 2e-2, masked rows exactly
+0, argmax labels exact where the oracle's top-2 gap >= 1e-3, and bitwise
+repeatability.
+"""
+import numpy as np
+import pytest
+import torch
+
+import synthetic
+from oracle import specloss_oracle as O
+from tests._gpu_helpers import (GRAD_FROB, full_parity, make_run, rel_frob, say, to_device)
+
+pytestmark = pytest.mark.gpu
+
+KINDS = ("ce_label", "ce", "kl_div", "rkl", "jsd", "tv", "nla", "lk_hybrid")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import lm_head_vocab_amd as L
+    L.load_library()
+    yield
+
+
+def test_ce_fp32_small_full_size():
+    """The small fp32 cross-entropy workload at its full size: every output vs the oracle."""
+    p = synthetic.make_problem("ce_fp32_small")
+    full_parity(p, tag="c1-full")
+
+
+def test_ce_bf16_ragged():
+    p = synthetic.make_problem("ce_bf16_1b", n_rows=600, hidden_dim=192, vocab=1100)
+    full_parity(p, tag="ce-ragged")
+
+
+def test_ce_bf16_ragged_chunked():
+    """Chunks of 256 rows over 600 rows (3 chunks, ragged last)."""
+    p = synthetic.make_problem("ce_bf16_1b", n_rows=600, hidden_dim=192, vocab=1100)
+    full_parity(p, max_chunk_rows=256, tag="ce-chunked")
+
+
+def test_lk_hybrid_ragged():
+    p = synthetic.make_problem("lk_hybrid_bf16_8b", n_rows=300, hidden_dim=128, vocab=777)
+    full_parity(p, tag="lk-ragged")
+
+
+def test_multihead_ce_tv():
+    p = synthetic.make_problem("multihead_bf16_405b", seq_len=150, hidden_dim=256, vocab=1000)
+    full_parity(p, tag="multihead")
+
+
+@pytest.mark.parametrize("kind", KINDS)
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_each_kind(kind, dtype):
+    name = "lk_hybrid_bf16_8b"
+    p = synthetic.make_problem(name, n_rows=280, hidden_dim=128, vocab=600, weights={kind: 1.0})
+    if kind == "ce_label":
+        rng = np.random.default_rng(3)
+        p.labels = rng.integers(0, p.vocab, p.n_rows).astype(np.int32)
+    p.mask = (np.arange(p.n_rows) % 7 != 3).astype(np.uint8)
+    if dtype == "f32":
+        p.dtype = "f32"
+        for f in ("hidden", "W", "target_hidden", "W_t"):
+            setattr(p, f, synthetic.bf16_bits_to_f32(getattr(p, f)).copy())
+    full_parity(p, tag=f"kind-{kind}-{dtype}")
+
+
+def test_weighted_mix_all_kinds():
+    w = {"ce_label": 0.2, "ce": 0.1, "kl_div": 0.5, "rkl": 0.3, "jsd": 0.7, "tv": 0.9, "nla": 0.4,
+         "lk_hybrid": 1.3}
+    p = synthetic.make_problem("multihead_bf16_405b", seq_len=120, hidden_dim=128, vocab=700,
+                               weights=w)
+    rng = np.random.default_rng(5)
+    p.labels = rng.integers(0, p.vocab, p.n_rows).astype(np.int32)
+    p.labels[::11] = -100
+    full_parity(p, tag="mix")
+
+
+def test_determinism_bitwise():
+    p = synthetic.make_problem("multihead_bf16_405b", seq_len=100, hidden_dim=128, vocab=900)
+    dev = to_device(p)
+    outs = []
+    for rep in range(2):
+        say(f"[determinism] rep {rep}")
+        run = make_run(p, dev)
+        run.forward()
+        dh, dW = run.backward(grad_mean=torch.ones(1, device="cuda"))
+        torch.cuda.synchronize()
+        outs.append((run.loss.cpu(), run.term.cpu(), run.saved.cpu(), dh.cpu(), dW.cpu()))
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
+
+
+def test_chunk_size_invariance():
+    """Forward and dh do not depend on the chunking; dW only by rounding."""
+    p = synthetic.make_problem("ce_bf16_1b", n_rows=700, hidden_dim=128, vocab=900)
+    dev = to_device(p)
+    res = {}
+    for ch in (256, 512, 0):
+        say(f"[chunk] max_chunk_rows={ch}")
+        run = make_run(p, dev, max_chunk_rows=ch)
+        run.forward()
+        dh, dW = run.backward(grad_mean=torch.ones(1, device="cuda"))
+        torch.cuda.synchronize()
+        res[ch] = (run.loss.cpu(), dh.cpu(), dW.cpu().numpy())
+    for ch in (256, 512):
+        assert torch.equal(res[ch][0], res[0][0])
+        assert torch.equal(res[ch][1], res[0][1])
+        assert rel_frob(res[ch][2], res[0][2]) < 1e-5
+
+
+def test_masked_rows_perturbed():
+    """Finite garbage in masked rows changes no loss, no dW bit and no unmasked dh bit."""
+    p = synthetic.make_problem("ce_bf16_1b", n_rows=300, hidden_dim=128, vocab=800)
+    outs = []
+    for rep in range(2):
+        if rep:
+            p.hidden = p.hidden.copy()
+            p.hidden[p.mask == 0] = synthetic.f32_to_bf16_bits(
+                np.full((int((p.mask == 0).sum()), p.hidden_dim), 37.0, np.float32))
+        dev = to_device(p)
+        run = make_run(p, dev)
+        run.forward()
+        dh, dW = run.backward(grad_mean=torch.ones(1, device="cuda"))
+        torch.cuda.synchronize()
+        outs.append((run.loss.cpu(), dh.cpu(), dW.cpu()))
+    m = torch.from_numpy(p.mask != 0)
+    assert torch.equal(outs[0][0], outs[1][0])
+    assert torch.equal(outs[0][2], outs[1][2])
+    assert torch.equal(outs[0][1][m], outs[1][1][m])
+    assert torch.all(outs[1][1][~m] == 0)
+
+
+def test_bad_labels_counted_and_masked():
+    p = synthetic.make_problem("ce_bf16_1b", n_rows=260, hidden_dim=64, vocab=500)
+    p.labels = p.labels.copy()
+    p.labels[[3, 50, 200]] = [500, -7, 100000]
+    p.mask[[3, 200]] = 1
+    p.mask[[50]] = 0  # a masked bad label is not counted
+    out = full_parity(p, tag="bad-labels")
+    counts = out["run"].counts.cpu().numpy()
+    assert counts[1] == 2
+
+
+def test_all_rows_masked():
+    p = synthetic.make_problem("ce_bf16_1b", n_rows=100, hidden_dim=64, vocab=300)
+    p.mask = np.zeros(100, np.uint8)
+    dev = to_device(p)
+    run = make_run(p, dev)
+    run.forward()
+    dh, dW = run.backward(grad_mean=torch.ones(1, device="cuda"))
+    torch.cuda.synchronize()
+    assert run.counts.cpu().tolist() == [0, 0]
+    assert float(run.reduced[0]) == 0.0
+    assert torch.all(run.loss == 0) and torch.all(dh == 0) and torch.all(dW == 0)
+
+
+def test_single_row_and_tiny_vocab():
+    p = synthetic.make_problem("lk_hybrid_bf16_8b", n_rows=1, hidden_dim=64, vocab=3)
+    full_parity(p, tag="tiny")
+
+
+def test_per_token_seed_and_accumulate():
+    """grad_loss seeds per row; accumulate_dW adds onto existing contents."""
+    p = synthetic.make_problem("multihead_bf16_405b", seq_len=90, hidden_dim=128, vocab=520)
+    dev = to_device(p)
+    run = make_run(p, dev)
+    run.forward()
+    rng = np.random.default_rng(9)
+    seed = rng.uniform(-1, 1, p.n_rows)
+    g = torch.tensor(seed, dtype=torch.float32, device="cuda")
+    base = torch.full(tuple(dev["W"].shape), 0.25, dtype=torch.float32, device="cuda")
+    dh, dW = run.backward(grad_loss=g, dW=base.clone(), accumulate_dW=True)
+    torch.cuda.synchronize()
+    valid, _ = O.row_validity(O.OracleProblem.of(p))
+    rdh, rdW = O.backward(p, seed=np.where(valid, seed, 0.0))
+    assert rel_frob(dh.cpu().numpy(), rdh) <= GRAD_FROB
+    assert rel_frob(dW.cpu().numpy() - 0.25, rdW) <= GRAD_FROB
+
+
+def test_bf16_dhidden_output():
+    p = synthetic.make_problem("ce_bf16_1b", n_rows=300, hidden_dim=128, vocab=700)
+    dev = to_device(p)
+    run = make_run(p, dev)
+    run.forward()
+    dh = torch.empty(dev["hidden"].shape, dtype=torch.bfloat16, device="cuda")
+    dh, _ = run.backward(grad_mean=torch.ones(1, device="cuda"), dhidden=dh, want_dW=False)
+    torch.cuda.synchronize()
+    rdh, _ = O.backward(p, want_dW=False)
+    assert rel_frob(dh.float().cpu().numpy(), rdh) <= GRAD_FROB
+
+
+def test_align_heads_kernel():
+    import lm_head_vocab_amd as L
+    S, B, shifts = 37, 3, (1, 2, 5)
+    rng = np.random.default_rng(2)
+    lm = (rng.uniform(size=S * B) > 0.2).astype(np.uint8)
+    n = len(shifts) * B * S
+    tr = torch.empty(n, dtype=torch.int32, device="cuda")
+    mk = torch.empty(n, dtype=torch.uint8, device="cuda")
+    L.specloss_align_heads(S, B, shifts, torch.from_numpy(lm).cuda(), tr, mk)
+    torch.cuda.synchronize()
+    rtr, rmk = O.align_heads(S, shifts, batch=B, loss_mask=lm)
+    assert np.array_equal(tr.cpu().numpy(), rtr) and np.array_equal(mk.cpu().numpy(), rmk)
+
+
+def test_autograd_wrapper():
+    import lm_head_vocab_amd as L
+    p = synthetic.make_problem("ce_bf16_1b", n_rows=200, hidden_dim=64, vocab=500)
+    dev = to_device(p)
+    h = dev["hidden"].clone().requires_grad_(True)
+    W = dev["W"].clone().requires_grad_(True)
+    loss = L.lmhead_loss(h, W, {"ce_label": 1.0}, labels=dev["labels"], mask=dev["mask"])
+    loss.backward()
+    mean, _, _ = O.mean_loss(p)
+    rdh, rdW = O.backward(p)
+    assert abs(loss.item() - mean) <= 1e-3 * abs(mean)
+    assert rel_frob(h.grad.float().cpu().numpy(), rdh) <= GRAD_FROB
+    assert rel_frob(W.grad.float().cpu().numpy(), rdW) <= GRAD_FROB

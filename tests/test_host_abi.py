@@ -1,0 +1,180 @@
+"""CPU tests of the C-ABI library: exports, host-side validation, memory model.
+
+No compute call reaches the GPU here: every call below fails validation on
+the host before anything is enqueued (or is a pure host query).
+"""
+import ctypes
+import json
+import os
+import re
+
+import pytest
+import torch
+
+import lm_head_vocab_amd as L
+from lm_head_vocab_amd import binding as B
+from lm_head_vocab_amd import memory as M
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+GOLDEN = os.path.join(ROOT, "tests", "golden")
+
+E_INVAL, E_UNSUP, E_WS = -1, -2, -3
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return L.load_library()
+
+
+def test_library_exports_every_header_symbol(lib):
+    with open(os.path.join(ROOT, "include", "specloss.h")) as f:
+        text = f.read()
+    decl = re.findall(r"^(?:int|void|size_t|const char\*|specloss_trace\*)\s+(\w+)\s*\(", text, flags=re.M)
+    assert set(decl) == set(B.EXPORTS), decl
+    for name in decl:
+        assert hasattr(lib, name), name
+
+
+def test_struct_layout_matches_header():
+    assert ctypes.sizeof(B.Problem) == 136
+    assert B.Problem.weights.offset == 96
+
+
+def test_kind_names_and_errors(lib):
+    assert [L.kind_name(i) for i in range(8)] == list(B.KINDS)
+    assert L.kind_name(8) is None and L.kind_name(-1) is None
+    assert L.strerror(0) == "success"
+    assert "workspace" in L.strerror(E_WS)
+
+
+def _fake(addr):
+    return ctypes.c_void_p(addr)
+
+
+def _problem(**kw):
+    p = B.Problem()
+    p.n_rows, p.hidden, p.vocab = kw.get("N", 256), kw.get("H", 256), kw.get("V", 4096)
+    p.in_dtype = kw.get("dtype", B.BF16)
+    p.hidden_states = kw.get("h", 0x10000)
+    p.W = kw.get("W", 0x20000)
+    p.labels = kw.get("labels", 0x30000)
+    for k, w in kw.get("weights", {"ce_label": 1.0}).items():
+        p.weights[B.KINDS.index(k)] = w
+    if "target" in kw:
+        p.target_hidden, p.W_t, p.n_target_rows = 0x40000, 0x50000, kw["target"]
+    return p
+
+
+def _ws(lib, p):
+    out = ctypes.c_size_t()
+    return lib.lmhead_loss_workspace_size(ctypes.byref(p), 0, ctypes.byref(out)), out.value
+
+
+def _fwd(lib, p, ws=0x100000, ws_bytes=1 << 40, loss=0x200000, counts=0x300000):
+    return lib.lmhead_loss_fwd(ctypes.byref(p), ws, ws_bytes, loss, None, None, None, counts,
+                               None, None)
+
+
+@pytest.mark.parametrize("mut,code", [
+    (dict(H=100), E_UNSUP),
+    (dict(H=0), E_INVAL),
+    (dict(N=0), E_INVAL),
+    (dict(V=-1), E_INVAL),
+    (dict(dtype=7), E_UNSUP),
+    (dict(weights={}), E_INVAL),
+    (dict(weights={"ce_label": float("nan")}), E_INVAL),
+    (dict(labels=None), E_INVAL),
+    (dict(weights={"tv": 1.0}), E_INVAL),                 # target kind without target
+    (dict(weights={"kl_div": 1.0}, target=10), E_INVAL),  # identity map, too few target rows
+    (dict(h=0x10008), E_UNSUP),                           # misaligned hidden
+    (dict(W=None), E_INVAL),
+])
+def test_validation(lib, mut, code):
+    p = _problem(**mut)
+    assert _ws(lib, p)[0] == code
+    assert _fwd(lib, p) == code
+
+
+def test_reserved_field_and_null_problem(lib):
+    p = _problem()
+    p.reserved = 1
+    assert _fwd(lib, p) == E_INVAL
+    out = ctypes.c_size_t()
+    assert lib.lmhead_loss_workspace_size(None, 0, ctypes.byref(out)) == E_INVAL
+    assert lib.lmhead_loss_fwd(None, 0, 0, 0, None, None, None, 0, None, None) == E_INVAL
+
+
+def test_fwd_output_checks(lib):
+    p = _problem()
+    assert _fwd(lib, p, loss=0) == E_INVAL
+    assert _fwd(lib, p, counts=0) == E_INVAL
+    assert _fwd(lib, p, counts=0x300004) == E_UNSUP
+    assert _fwd(lib, p, ws=0) == E_WS
+    assert _fwd(lib, p, ws_bytes=1000) == E_WS
+    assert _fwd(lib, p, ws=0x100010) == E_WS  # workspace must be 256-byte aligned
+
+
+def test_bwd_checks(lib):
+    p = _problem()
+    bwd = lib.lmhead_loss_bwd
+    args = dict(gl=0x1000, gm=None, counts=0x2000, saved=0x3000, ws=0x100000, wsb=1 << 40,
+                dh=0x4000, dt=B.F32, dW=0x5000)
+
+    def call(**kw):
+        a = {**args, **kw}
+        return bwd(ctypes.byref(p), a["gl"], a["gm"], a["counts"], a["saved"], a["ws"], a["wsb"],
+                   a["dh"], a["dt"], a["dW"], 0, None)
+
+    assert call(gl=None) == E_INVAL
+    assert call(saved=None) == E_INVAL
+    assert call(counts=None) == E_INVAL
+    assert call(dh=None, dW=None) == E_INVAL
+    assert call(dt=5) == E_UNSUP
+    assert call(wsb=100) == E_WS
+
+
+def test_workspace_size_grows_with_chunk_and_stays_below_logits(lib):
+    p = _problem(N=32768, H=4096, V=128256)
+    sizes = []
+    for ch in (256, 1024, 8192):
+        out = ctypes.c_size_t()
+        assert lib.lmhead_loss_workspace_size(ctypes.byref(p), ch, ctypes.byref(out)) == 0
+        sizes.append(out.value)
+    assert sizes == sorted(sizes)
+    # no buffer reaches a bf16 [N, V] tensor at the 8B shape
+    assert sizes[-1] < M.logits_sized_limit_bytes(32768, 128256)
+
+
+def test_saved_bytes(lib):
+    assert L.specloss_saved_bytes(0) == 0
+    assert L.specloss_saved_bytes(1) == 9 * 256
+    assert L.specloss_saved_bytes(1000) == 9 * 4096
+
+
+def test_align_heads_validation(lib):
+    arr = (ctypes.c_int32 * 2)(1, -1)
+    assert lib.specloss_align_heads(10, 1, 2, arr, None, 0x1000, 0x2000, None) == E_INVAL
+    arr = (ctypes.c_int32 * 1)(1)
+    assert lib.specloss_align_heads(0, 1, 1, arr, None, 0x1000, 0x2000, None) == E_INVAL
+    assert lib.specloss_align_heads(10, 1, 65, arr, None, 0x1000, 0x2000, None) == E_UNSUP
+
+
+def test_memory_model_reproduces_page_figures():
+    with open(os.path.join(GOLDEN, "page_memory_figures.json")) as f:
+        g = json.load(f)["figures"]
+    gib = M.GIB
+    a, b, c, d = g
+    assert abs(M.dense_logits_bytes(a["batch"] * a["seq"], a["vocab"], 4) / gib - a["printed_GiB"]) < a["rounding"]
+    assert abs(M.hidden_bytes(b["batch"] * b["seq"], b["hidden"], 2) / gib - b["printed_GiB"]) < b["rounding"]
+    assert abs(M.dense_logits_bytes(c["batch"] * c["seq"], c["vocab"], 4, with_grad=True) / gib
+               - c["printed_GiB"]) < c["rounding"]
+    assert abs(M.streaming_bound_bytes(d["chunk"], d["vocab"], 4) / gib - d["printed_GiB"]) < d["rounding"]
+    # the literal 150_000 of the example line does not give the printed value
+    assert abs(M.streaming_bound_bytes(1024, 150_000, 4) / gib - 0.97) > 0.1
+
+
+def test_binding_rejects_bad_dtypes():
+    with pytest.raises(ValueError):
+        B.make_problem(torch.zeros(4, 64, dtype=torch.float16), torch.zeros(8, 64, dtype=torch.float16), {"ce_label": 1})
+    with pytest.raises(ValueError):
+        B.make_problem(torch.zeros(4, 64), torch.zeros(8, 64), {"bogus": 1})
