@@ -367,27 +367,41 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(GemmLaunch a) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   OutT* C = static_cast<OutT*>(a.C);
+  // Two fragments at a time: all their old values are loaded first (32 loads
+  // in flight), then added and stored.
+  constexpr int FB = 2;
 #pragma unroll
-  for (int i = 0; i < Cfg::FM; ++i)
+  for (int j = 0; j < Cfg::FN; ++j) {
+    const int col = tn * Cfg::BN + wn * Cfg::WN + j * 32 + (lane & 31);
+    const bool col_ok = col < a.n_valid;
 #pragma unroll
-    for (int j = 0; j < Cfg::FN; ++j) {
-      const int col = tn * Cfg::BN + wn * Cfg::WN + j * 32 + (lane & 31);
-      if (col >= a.n_valid) continue;
+    for (int i0 = 0; i0 < Cfg::FM; i0 += FB) {
+      float old[FB][16];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = tm * Cfg::BM + wm * Cfg::WM + i * 32 + frag_row(r, lane);
-        if (row >= a.m_valid) continue;
-        OutT* p = C + (int64_t)row * a.ldc + col;
-        float x = acc[i][j][r];
-        if constexpr (sizeof(OutT) == 4) {
-          if (a.accumulate) x += *reinterpret_cast<float*>(p);
-          *reinterpret_cast<float*>(p) = x;
-        } else {
-          if (a.accumulate) x += (float)*reinterpret_cast<__bf16*>(p);
-          *reinterpret_cast<__bf16*>(p) = (__bf16)x;
+      for (int ii = 0; ii < FB; ++ii)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = tm * Cfg::BM + wm * Cfg::WM + (i0 + ii) * 32 + frag_row(r, lane);
+          old[ii][r] = 0.0f;
+          if (a.accumulate && col_ok && row < a.m_valid) {
+            const OutT* p = C + (int64_t)row * a.ldc + col;
+            if constexpr (sizeof(OutT) == 4) old[ii][r] = *reinterpret_cast<const float*>(p);
+            else old[ii][r] = (float)*reinterpret_cast<const __bf16*>(p);
+          }
         }
-      }
+#pragma unroll
+      for (int ii = 0; ii < FB; ++ii)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = tm * Cfg::BM + wm * Cfg::WM + (i0 + ii) * 32 + frag_row(r, lane);
+          if (!col_ok || row >= a.m_valid) continue;
+          OutT* p = C + (int64_t)row * a.ldc + col;
+          const float x = acc[i0 + ii][j][r] + old[ii][r];
+          if constexpr (sizeof(OutT) == 4) *reinterpret_cast<float*>(p) = x;
+          else *reinterpret_cast<__bf16*>(p) = (__bf16)x;
+        }
     }
+  }
 }
 
 // ============================================================================

@@ -14,8 +14,8 @@
 //    A and B sits in LDS as rows of eight 16-byte chunks, chunk c of row r
 //    stored at position c ^ (r & 7): eight consecutive rows read at the same
 //    logical chunk hit eight different bank groups (conflict-free ds_read_b128).
-//  * Two LDS stages; the next slab is fetched from HBM into registers while
-//    the MFMAs consume the current stage (one barrier per slab).
+//  * Two LDS stages filled by direct-to-LDS loads: the next slab streams in
+//    while the MFMAs consume the current stage (one barrier per slab).
 //  * Workgroups are dealt round-robin to the 8 XCDs; `tile_of` renumbers them
 //    so each XCD walks a compact block of tiles and its private L2 sees the
 //    same A and B slabs from several tiles at once.
@@ -59,7 +59,6 @@ struct TileCfg {
   static constexpr int BK = 8 * KC;                    // elements per slab row (128 bytes)
   static constexpr int WM = BM / 2, WN = BN / 2;       // wave sub-tile
   static constexpr int FM = WM / 32, FN = WN / 32;     // 32x32 fragments per wave
-  static constexpr int LA = BM / 32, LB = BN / 32;     // 16-byte loads per thread per slab
   static constexpr int STAGE = (BM + BN) * kRowBytes;  // bytes of one LDS stage
   static constexpr int LDS_BYTES = 2 * STAGE;
 };
@@ -117,83 +116,163 @@ __device__ __forceinline__ void mfma_slab_step<float>(f32x16_t& acc, const i32x4
                                                0, 0, 0);
 }
 
+// MFMA instructions per (A fragment, B fragment) pair and k-step
+template <typename T>
+constexpr int kMfmaPerPair = sizeof(T) == 2 ? 1 : 4;
+
+// Wait until this wave's outstanding vector-memory operations (including
+// direct-to-LDS loads) have completed: s_waitcnt vmcnt(0), other counters
+// left alone (gfx9 encoding: expcnt 7, lgkmcnt 15).
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+__device__ __forceinline__ lds_void_t* to_lds(char* p) {
+  return (lds_void_t*)((__attribute__((address_space(3))) char*)(p));
+}
+
 // C_tile = A[a_row0 : a_row0+BM, 0:k_len] * B[b_row0 : b_row0+BN, 0:k_len]^T,
 // accumulated into `acc` (which the caller zeroes).  k_len is a multiple of
 // Cfg::BK.  Ends with a barrier, so LDS is free for the epilogue.
+//
+// Slab rows (A rows, then B rows) reach LDS by direct-to-LDS loads
+// (global_load_lds_dwordx4): one wave instruction fills 1 KB = 8 slab rows,
+// lane i landing at byte 16 i; lane i therefore fetches logical chunk
+// (i % 8) ^ (row % 8) of row i / 8, which realises the XOR swizzle.  Slab
+// k+1 is issued right after the barrier that frees its stage and lands while
+// the MFMAs consume slab k; the four k-steps of a slab read their fragments
+// one step ahead into a second register set.
+template <typename Cfg>
+__device__ __forceinline__ void read_frags(const char* sa, const char* sb, int s, int lane,
+                                           int wm, int wn, i32x4_t (&af)[Cfg::FM],
+                                           i32x4_t (&bf)[Cfg::FN]) {
+  const int frow = lane & 31;
+  const int chunk = 2 * s + (lane >> 5);
+#pragma unroll
+  for (int i = 0; i < Cfg::FM; ++i) {
+    const int r = wm * Cfg::WM + i * 32 + frow;
+    af[i] = *reinterpret_cast<const i32x4_t*>(sa + r * kRowBytes + ((chunk ^ (r & 7)) << 4));
+  }
+#pragma unroll
+  for (int j = 0; j < Cfg::FN; ++j) {
+    const int r = wn * Cfg::WN + j * 32 + frow;
+    bf[j] = *reinterpret_cast<const i32x4_t*>(sb + r * kRowBytes + ((chunk ^ (r & 7)) << 4));
+  }
+}
+
+// One direct-to-LDS load per 8-row group.  The builtin exists only for the
+// device pass of the single-source compile; the host pass never runs it.
+template <int PER_WAVE>
+__device__ __forceinline__ void issue_slab(const char* const (&src)[PER_WAVE], char* dst,
+                                           int64_t kbytes) {
+#if defined(__HIP_DEVICE_COMPILE__)
+#pragma unroll
+  for (int u = 0; u < PER_WAVE; ++u)
+    __builtin_amdgcn_global_load_lds(src[u] + kbytes, to_lds(dst + u * 1024), 16, 0, 0);
+#endif
+}
+
+// One slab = four k-steps of MFMAs.  Step s < 3 first issues step s+1's
+// fragment reads; step 3 (unless LAST) waits for slab k+1's loads, meets the
+// other waves at the barrier (all of them hold step 3's fragments, so this
+// stage is free), issues slab k+2 into it and reads slab k+1's step-0
+// fragments.  Inside a step, reads and loads are interleaved one per MFMA
+// so they land while the remaining MFMAs run.
+template <typename T, typename Cfg, int PER_WAVE, bool LAST>
+__device__ __forceinline__ void slab_steps(f32x16_t (&acc)[Cfg::FM][Cfg::FN],
+                                           i32x4_t (&fa)[2][Cfg::FM], i32x4_t (&fb)[2][Cfg::FN],
+                                           char* smem, int stage, int lane, int wm, int wn,
+                                           const char* const (&src)[PER_WAVE], char* wave_dst,
+                                           int64_t next_kbytes) {
+  constexpr int kR = Cfg::FM + Cfg::FN;
+  const char* sa = smem + stage * Cfg::STAGE;
+  const char* sb = sa + Cfg::BM * kRowBytes;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    if (s < 3) {
+      read_frags<Cfg>(sa, sb, s + 1, lane, wm, wn, fa[(s + 1) & 1], fb[(s + 1) & 1]);
+    } else if (!LAST) {
+      wait_vmem();
+      __syncthreads();
+      issue_slab<PER_WAVE>(src, wave_dst + stage * Cfg::STAGE, next_kbytes);
+      const char* na = smem + (stage ^ 1) * Cfg::STAGE;
+      read_frags<Cfg>(na, na + Cfg::BM * kRowBytes, 0, lane, wm, wn, fa[0], fb[0]);
+    }
+#pragma unroll
+    for (int i = 0; i < Cfg::FM; ++i)
+#pragma unroll
+      for (int j = 0; j < Cfg::FN; ++j) mfma_slab_step<T>(acc[i][j], fa[s & 1][i], fb[s & 1][j]);
+    if (s < 3 || !LAST) {
+#pragma unroll
+      for (int q = 0; q < kR; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, kMfmaPerPair<T>, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                 // LDS read
+      }
+      constexpr int kSlots = Cfg::FM * Cfg::FN - kR;  // MFMA slots left after the reads
+      if (s == 3) {
+        constexpr int kPerSlot = (PER_WAVE + kSlots - 1) / kSlots;
+#pragma unroll
+        for (int q = 0; q < kSlots; ++q) {
+          __builtin_amdgcn_sched_group_barrier(0x008, kMfmaPerPair<T>, 0);  // MFMA
+          __builtin_amdgcn_sched_group_barrier(0x020, kPerSlot, 0);          // slab loads
+        }
+      } else {
+        __builtin_amdgcn_sched_group_barrier(0x008, kSlots * kMfmaPerPair<T>, 0);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
 template <typename T, typename Cfg>
 __device__ __forceinline__ void tile_mainloop(f32x16_t (&acc)[Cfg::FM][Cfg::FN],
                                               const Operand<T>& A, int32_t a_row0,
                                               const Operand<T>& B, int32_t b_row0, int32_t k_len,
                                               char* smem) {
+  constexpr int ROWS = Cfg::BM + Cfg::BN;
+  constexpr int GROUPS = ROWS / 8;      // 1 KB load instructions per slab
+  constexpr int PER_WAVE = GROUPS / 4;  // per wave
+  static_assert(GROUPS % 4 == 0 && PER_WAVE % 2 == 0 && Cfg::BM % 8 == 0,
+                "slab must split into 8-row groups");
+  static_assert(Cfg::FM * Cfg::FN > Cfg::FM + Cfg::FN, "too few MFMAs per step");
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const int lrow = tid >> 3;       // first slab row this thread loads
-  const int lchunk = tid & 7;      // 16-byte chunk this thread loads
-  const int swz = (lchunk ^ (lrow & 7)) << 4;
+  const int prow = lane >> 3;
+  const int lchunk = (lane & 7) ^ prow;
 
-  const T* pa[Cfg::LA];
-  const T* pb[Cfg::LB];
+  const char* src[PER_WAVE];
 #pragma unroll
-  for (int i = 0; i < Cfg::LA; ++i) pa[i] = row_ptr(A, a_row0 + lrow + 32 * i) + lchunk * Cfg::KC;
-#pragma unroll
-  for (int i = 0; i < Cfg::LB; ++i) pb[i] = row_ptr(B, b_row0 + lrow + 32 * i) + lchunk * Cfg::KC;
-
-  i32x4_t ra[Cfg::LA], rb[Cfg::LB];
-  auto gload = [&](int k0) {
-#pragma unroll
-    for (int i = 0; i < Cfg::LA; ++i) ra[i] = *reinterpret_cast<const i32x4_t*>(pa[i] + k0);
-#pragma unroll
-    for (int i = 0; i < Cfg::LB; ++i) rb[i] = *reinterpret_cast<const i32x4_t*>(pb[i] + k0);
-  };
-  auto lstore = [&](int stage) {
-    char* sa = smem + stage * Cfg::STAGE;
-    char* sb = sa + Cfg::BM * kRowBytes;
-#pragma unroll
-    for (int i = 0; i < Cfg::LA; ++i)
-      *reinterpret_cast<i32x4_t*>(sa + (lrow + 32 * i) * kRowBytes + swz) = ra[i];
-#pragma unroll
-    for (int i = 0; i < Cfg::LB; ++i)
-      *reinterpret_cast<i32x4_t*>(sb + (lrow + 32 * i) * kRowBytes + swz) = rb[i];
-  };
-
-  // per-lane LDS read offsets (row part); the chunk part depends on the step
-  const int frow = lane & 31;
-  const int half = lane >> 5;
-  const int nslab = k_len / Cfg::BK;
-
-  gload(0);
-  lstore(0);
-  __syncthreads();
-
-  for (int ks = 0; ks < nslab; ++ks) {
-    const int stage = ks & 1;
-    if (ks + 1 < nslab) gload((ks + 1) * Cfg::BK);
-    const char* sa = smem + stage * Cfg::STAGE;
-    const char* sb = sa + Cfg::BM * kRowBytes;
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int chunk = 2 * s + half;
-      i32x4_t af[Cfg::FM], bfr[Cfg::FN];
-#pragma unroll
-      for (int i = 0; i < Cfg::FM; ++i) {
-        const int r = wm * Cfg::WM + i * 32 + frow;
-        af[i] = *reinterpret_cast<const i32x4_t*>(sa + r * kRowBytes + ((chunk ^ (r & 7)) << 4));
-      }
-#pragma unroll
-      for (int j = 0; j < Cfg::FN; ++j) {
-        const int r = wn * Cfg::WN + j * 32 + frow;
-        bfr[j] = *reinterpret_cast<const i32x4_t*>(sb + r * kRowBytes + ((chunk ^ (r & 7)) << 4));
-      }
-#pragma unroll
-      for (int i = 0; i < Cfg::FM; ++i)
-#pragma unroll
-        for (int j = 0; j < Cfg::FN; ++j) mfma_slab_step<T>(acc[i][j], af[i], bfr[j]);
-    }
-    if (ks + 1 < nslab) lstore(stage ^ 1);
-    __syncthreads();
+  for (int u = 0; u < PER_WAVE; ++u) {
+    const int row = (wave * PER_WAVE + u) * 8 + prow;
+    const T* p = row < Cfg::BM ? row_ptr(A, a_row0 + row) : row_ptr(B, b_row0 + row - Cfg::BM);
+    src[u] = reinterpret_cast<const char*>(p) + lchunk * 16;
   }
+  char* const wave_dst = smem + wave * PER_WAVE * 1024;
+
+  const int nslab = k_len / Cfg::BK;
+  const int64_t last_kbytes = (int64_t)(nslab - 1) * kRowBytes;
+  issue_slab<PER_WAVE>(src, wave_dst, 0);
+  wait_vmem();
+  __syncthreads();
+  // slab 1 (or, with a single slab, a harmless reload of slab 0 into the unused stage)
+  issue_slab<PER_WAVE>(src, wave_dst + Cfg::STAGE, nslab > 1 ? kRowBytes : 0);
+  i32x4_t fa[2][Cfg::FM], fb[2][Cfg::FN];
+  read_frags<Cfg>(smem, smem + Cfg::BM * kRowBytes, 0, lane, wm, wn, fa[0], fb[0]);
+  __builtin_amdgcn_sched_barrier(0);
+
+  for (int ks = 0; ks + 1 < nslab; ++ks) {
+    // slab k+2 when it exists, else a reload of the last slab into a stage
+    // that is never read again
+    const int64_t nk = (int64_t)(ks + 2) * kRowBytes;
+    slab_steps<T, Cfg, PER_WAVE, false>(acc, fa, fb, smem, ks & 1, lane, wm, wn, src, wave_dst,
+                                        nk < last_kbytes ? nk : last_kbytes);
+  }
+  slab_steps<T, Cfg, PER_WAVE, true>(acc, fa, fb, smem, (nslab - 1) & 1, lane, wm, wn, src,
+                                     wave_dst, 0);
+  wait_vmem();      // the last (reload) loads must land before LDS is reused
+  __syncthreads();  // LDS is handed to the epilogue
 }
 
 template <typename Cfg>

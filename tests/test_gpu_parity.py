@@ -93,7 +93,8 @@ def test_determinism_bitwise():
         run.forward()
         dh, dW = run.backward(grad_mean=torch.ones(1, device="cuda"))
         torch.cuda.synchronize()
-        outs.append((run.loss.cpu(), run.term.cpu(), run.saved.cpu(), dh.cpu(), dW.cpu()))
+        fields = [run.saved_field(i, torch.int32).cpu() for i in range(9)]  # bitwise; padding excluded
+        outs.append((run.loss.cpu(), run.term.cpu(), *fields, dh.cpu(), dW.cpu()))
     for a, b in zip(*outs):
         assert torch.equal(a, b)
 
