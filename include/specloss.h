@@ -104,7 +104,8 @@ typedef struct {
   const void* target_hidden;   /* [n_target_rows, H] target hidden states, or NULL */
   int64_t n_target_rows;       /* rows of target_hidden */
   const void* W_t;             /* [V, H] target LM-head weight (may equal W), or NULL */
-  const int32_t* target_row;   /* [N] row of target_hidden for each row, or NULL = identity */
+  const int32_t* target_row;   /* [N] row of target_hidden for each row, or NULL = identity;
+                                  with a map, target_hidden must be smaller than 4 GiB */
   const uint8_t* mask;         /* [N] 0 = masked, or NULL = no mask */
   float weights[SPECLOSS_NUM_KINDS]; /* per-kind weight, used as given (not normalised); 0 = off */
   specloss_trace* trace;       /* NULL, or a trace that records every launch of the call */

@@ -88,6 +88,9 @@ int check_problem(const specloss_problem* p, KindSet* ks) {
     if (!aligned(p->target_hidden, 16) || !aligned(p->W_t, 16)) return SPECLOSS_E_UNSUPPORTED;
     if (p->target_row) {
       if (!aligned(p->target_row, 4)) return SPECLOSS_E_UNSUPPORTED;
+      // gathered rows are addressed by 32-bit byte offsets from the tensor base
+      if ((uint64_t)p->n_target_rows * (uint64_t)p->hidden * elem_size(p) > 0xFFFFFFFFull)
+        return SPECLOSS_E_UNSUPPORTED;
     } else if (p->n_target_rows < p->n_rows) {
       return SPECLOSS_E_INVAL;  // identity map needs a target row per row
     }

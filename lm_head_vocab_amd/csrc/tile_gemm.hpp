@@ -131,17 +131,49 @@ __device__ __forceinline__ lds_void_t* to_lds(char* p) {
   return (lds_void_t*)((__attribute__((address_space(3))) char*)(p));
 }
 
-// C_tile = A[a_row0 : a_row0+BM, 0:k_len] * B[b_row0 : b_row0+BN, 0:k_len]^T,
-// accumulated into `acc` (which the caller zeroes).  k_len is a multiple of
-// Cfg::BK.  Ends with a barrier, so LDS is free for the epilogue.
-//
-// Slab rows (A rows, then B rows) reach LDS by direct-to-LDS loads
-// (global_load_lds_dwordx4): one wave instruction fills 1 KB = 8 slab rows,
-// lane i landing at byte 16 i; lane i therefore fetches logical chunk
-// (i % 8) ^ (row % 8) of row i / 8, which realises the XOR swizzle.  Slab
-// k+1 is issued right after the barrier that frees its stage and lands while
-// the MFMAs consume slab k; the four k-steps of a slab read their fragments
-// one step ahead into a second register set.
+// A wave's share of one slab: PER_WAVE groups of 8 rows, each group one
+// direct-to-LDS load of 1 KB.  Every group reads from a wave-uniform base
+// pointer (kept in SGPRs) plus a per-lane 32-bit byte offset, so a load costs
+// one scalar M0 write and the load itself, with no per-load vector address
+// arithmetic.
+template <int PER_WAVE>
+struct SlabLoads {
+  const char* base[PER_WAVE];  // uniform per group
+  uint32_t off[PER_WAVE];      // per lane: row offset + swizzled chunk
+  char* dst;                   // uniform: LDS address of group 0 in stage 0
+};
+
+// Issue groups [U0, U1) of a slab at byte offset kbytes along K into `stage`.
+// The builtin exists only for the device pass of the single-source compile.
+template <int PER_WAVE, int U0, int U1, typename Cfg>
+__device__ __forceinline__ void issue_groups(const SlabLoads<PER_WAVE>& L, int stage,
+                                             int64_t kbytes) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  char* dst = L.dst + stage * Cfg::STAGE;
+#pragma unroll
+  for (int u = U0; u < U1; ++u)
+    __builtin_amdgcn_global_load_lds(L.base[u] + kbytes + L.off[u], to_lds(dst + u * 1024), 16,
+                                     0, 0);
+#endif
+}
+
+template <typename T>
+__device__ __forceinline__ void group_source(const Operand<T>& op, int32_t row0, int r,
+                                             int lchunk, const char*& base, uint32_t& off) {
+  if (op.map != nullptr) {
+    // gathered rows: offsets from the operand base (host checks they fit 32 bits)
+    const int32_t idx = row0 + r;
+    const int32_t src = clamp_row(op.map[idx < op.map_len ? idx : op.map_len - 1], op.n_rows);
+    base = reinterpret_cast<const char*>(op.base);
+    off = (uint32_t)((int64_t)src * op.ld * (int64_t)sizeof(T)) + lchunk * 16;
+  } else {
+    // contiguous rows: offsets from the tile's first row
+    const int32_t src = clamp_row(row0 + r, op.n_rows);
+    base = reinterpret_cast<const char*>(op.base + (int64_t)row0 * op.ld);
+    off = (uint32_t)((int64_t)(src - row0) * op.ld * (int64_t)sizeof(T)) + lchunk * 16;
+  }
+}
+
 template <typename Cfg>
 __device__ __forceinline__ void read_frags(const char* sa, const char* sb, int s, int lane,
                                            int wm, int wn, i32x4_t (&af)[Cfg::FM],
@@ -160,41 +192,35 @@ __device__ __forceinline__ void read_frags(const char* sa, const char* sb, int s
   }
 }
 
-// One direct-to-LDS load per 8-row group.  The builtin exists only for the
-// device pass of the single-source compile; the host pass never runs it.
-template <int PER_WAVE>
-__device__ __forceinline__ void issue_slab(const char* const (&src)[PER_WAVE], char* dst,
-                                           int64_t kbytes) {
-#if defined(__HIP_DEVICE_COMPILE__)
-#pragma unroll
-  for (int u = 0; u < PER_WAVE; ++u)
-    __builtin_amdgcn_global_load_lds(src[u] + kbytes, to_lds(dst + u * 1024), 16, 0, 0);
-#endif
-}
-
-// One slab = four k-steps of MFMAs.  Step s < 3 first issues step s+1's
-// fragment reads; step 3 (unless LAST) waits for slab k+1's loads, meets the
-// other waves at the barrier (all of them hold step 3's fragments, so this
-// stage is free), issues slab k+2 into it and reads slab k+1's step-0
-// fragments.  Inside a step, reads and loads are interleaved one per MFMA
-// so they land while the remaining MFMAs run.
-template <typename T, typename Cfg, int PER_WAVE, bool LAST>
+// One slab = four k-steps of MFMAs.  Step 0 issues the second half of slab
+// k+1's loads (unless FIRST: the prologue loaded all of it); steps 0-2 read
+// the next step's fragments; step 3 (unless LAST) waits for slab k+1, meets
+// the other waves at the barrier (all of them now hold step 3's fragments,
+// so this stage is free), issues the first half of slab k+2 into it and
+// reads slab k+1's step-0 fragments.  Inside a step, fragment reads and
+// loads are interleaved with the MFMAs so they land while the rest run.
+template <typename T, typename Cfg, int PER_WAVE, bool FIRST, bool LAST>
 __device__ __forceinline__ void slab_steps(f32x16_t (&acc)[Cfg::FM][Cfg::FN],
                                            i32x4_t (&fa)[2][Cfg::FM], i32x4_t (&fb)[2][Cfg::FN],
                                            char* smem, int stage, int lane, int wm, int wn,
-                                           const char* const (&src)[PER_WAVE], char* wave_dst,
-                                           int64_t next_kbytes) {
+                                           const SlabLoads<PER_WAVE>& L, int64_t next_kbytes,
+                                           int64_t pend_kbytes) {
   constexpr int kR = Cfg::FM + Cfg::FN;
+  constexpr int kH = PER_WAVE / 2;
+  constexpr int kSlots = Cfg::FM * Cfg::FN - kR;  // MFMA slots left after the reads
+  constexpr int kPerSlot = (kH + kSlots - 1) / kSlots;
   const char* sa = smem + stage * Cfg::STAGE;
   const char* sb = sa + Cfg::BM * kRowBytes;
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
+    const bool loads = (s == 0 && !FIRST) || (s == 3 && !LAST);
+    if (s == 0 && !FIRST) issue_groups<PER_WAVE, kH, PER_WAVE, Cfg>(L, stage ^ 1, pend_kbytes);
     if (s < 3) {
       read_frags<Cfg>(sa, sb, s + 1, lane, wm, wn, fa[(s + 1) & 1], fb[(s + 1) & 1]);
     } else if (!LAST) {
       wait_vmem();
       __syncthreads();
-      issue_slab<PER_WAVE>(src, wave_dst + stage * Cfg::STAGE, next_kbytes);
+      issue_groups<PER_WAVE, 0, kH, Cfg>(L, stage, next_kbytes);
       const char* na = smem + (stage ^ 1) * Cfg::STAGE;
       read_frags<Cfg>(na, na + Cfg::BM * kRowBytes, 0, lane, wm, wn, fa[0], fb[0]);
     }
@@ -208,9 +234,7 @@ __device__ __forceinline__ void slab_steps(f32x16_t (&acc)[Cfg::FM][Cfg::FN],
         __builtin_amdgcn_sched_group_barrier(0x008, kMfmaPerPair<T>, 0);  // MFMA
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                 // LDS read
       }
-      constexpr int kSlots = Cfg::FM * Cfg::FN - kR;  // MFMA slots left after the reads
-      if (s == 3) {
-        constexpr int kPerSlot = (PER_WAVE + kSlots - 1) / kSlots;
+      if (loads) {
 #pragma unroll
         for (int q = 0; q < kSlots; ++q) {
           __builtin_amdgcn_sched_group_barrier(0x008, kMfmaPerPair<T>, 0);  // MFMA
@@ -224,6 +248,14 @@ __device__ __forceinline__ void slab_steps(f32x16_t (&acc)[Cfg::FM][Cfg::FN],
   }
 }
 
+// C_tile = A[a_row0 : a_row0+BM, 0:k_len] * B[b_row0 : b_row0+BN, 0:k_len]^T,
+// accumulated into `acc` (which the caller zeroes).  k_len is a multiple of
+// Cfg::BK.  Ends with a barrier, so LDS is free for the epilogue.
+//
+// Slab rows (A rows, then B rows) reach LDS by direct-to-LDS loads
+// (global_load_lds_dwordx4): one wave instruction fills 1 KB = 8 slab rows,
+// lane i landing at byte 16 i; lane i therefore fetches logical chunk
+// (i % 8) ^ (row % 8) of row i / 8, which realises the XOR swizzle.
 template <typename T, typename Cfg>
 __device__ __forceinline__ void tile_mainloop(f32x16_t (&acc)[Cfg::FM][Cfg::FN],
                                               const Operand<T>& A, int32_t a_row0,
@@ -235,43 +267,47 @@ __device__ __forceinline__ void tile_mainloop(f32x16_t (&acc)[Cfg::FM][Cfg::FN],
   static_assert(GROUPS % 4 == 0 && PER_WAVE % 2 == 0 && Cfg::BM % 8 == 0,
                 "slab must split into 8-row groups");
   static_assert(Cfg::FM * Cfg::FN > Cfg::FM + Cfg::FN, "too few MFMAs per step");
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave >> 1, wn = wave & 1;
   const int prow = lane >> 3;
   const int lchunk = (lane & 7) ^ prow;
 
-  const char* src[PER_WAVE];
+  SlabLoads<PER_WAVE> L;
 #pragma unroll
   for (int u = 0; u < PER_WAVE; ++u) {
-    const int row = (wave * PER_WAVE + u) * 8 + prow;
-    const T* p = row < Cfg::BM ? row_ptr(A, a_row0 + row) : row_ptr(B, b_row0 + row - Cfg::BM);
-    src[u] = reinterpret_cast<const char*>(p) + lchunk * 16;
+    const int g = wave * PER_WAVE + u;  // uniform: which 8-row group
+    if (g * 8 < Cfg::BM) group_source(A, a_row0, g * 8 + prow, lchunk, L.base[u], L.off[u]);
+    else group_source(B, b_row0, g * 8 - Cfg::BM + prow, lchunk, L.base[u], L.off[u]);
   }
-  char* const wave_dst = smem + wave * PER_WAVE * 1024;
+  L.dst = smem + wave * PER_WAVE * 1024;
 
   const int nslab = k_len / Cfg::BK;
   const int64_t last_kbytes = (int64_t)(nslab - 1) * kRowBytes;
-  issue_slab<PER_WAVE>(src, wave_dst, 0);
+  // slab 0 into stage 0; slab 1 (with a single slab, a harmless reload of
+  // slab 0) into stage 1
+  issue_groups<PER_WAVE, 0, PER_WAVE, Cfg>(L, 0, 0);
   wait_vmem();
   __syncthreads();
-  // slab 1 (or, with a single slab, a harmless reload of slab 0 into the unused stage)
-  issue_slab<PER_WAVE>(src, wave_dst + Cfg::STAGE, nslab > 1 ? kRowBytes : 0);
+  issue_groups<PER_WAVE, 0, PER_WAVE, Cfg>(L, 1, nslab > 1 ? kRowBytes : 0);
   i32x4_t fa[2][Cfg::FM], fb[2][Cfg::FN];
   read_frags<Cfg>(smem, smem + Cfg::BM * kRowBytes, 0, lane, wm, wn, fa[0], fb[0]);
   __builtin_amdgcn_sched_barrier(0);
 
-  for (int ks = 0; ks + 1 < nslab; ++ks) {
-    // slab k+2 when it exists, else a reload of the last slab into a stage
-    // that is never read again
-    const int64_t nk = (int64_t)(ks + 2) * kRowBytes;
-    slab_steps<T, Cfg, PER_WAVE, false>(acc, fa, fb, smem, ks & 1, lane, wm, wn, src, wave_dst,
-                                        nk < last_kbytes ? nk : last_kbytes);
+  // slab k+2's loads (clamped to the last slab: a reload into a stage that is
+  // never read again) start at slab k's step 3 and finish at slab k+1's step 0
+  auto clampk = [&](int k) { return k < nslab ? (int64_t)k * kRowBytes : last_kbytes; };
+  if (nslab > 1) {
+    slab_steps<T, Cfg, PER_WAVE, true, false>(acc, fa, fb, smem, 0, lane, wm, wn, L, clampk(2), 0);
+    for (int ks = 1; ks + 1 < nslab; ++ks)
+      slab_steps<T, Cfg, PER_WAVE, false, false>(acc, fa, fb, smem, ks & 1, lane, wm, wn, L,
+                                                 clampk(ks + 2), clampk(ks + 1));
+    slab_steps<T, Cfg, PER_WAVE, false, true>(acc, fa, fb, smem, (nslab - 1) & 1, lane, wm, wn, L,
+                                              0, clampk(nslab));
+  } else {
+    slab_steps<T, Cfg, PER_WAVE, true, true>(acc, fa, fb, smem, 0, lane, wm, wn, L, 0, 0);
   }
-  slab_steps<T, Cfg, PER_WAVE, true>(acc, fa, fb, smem, (nslab - 1) & 1, lane, wm, wn, src,
-                                     wave_dst, 0);
-  wait_vmem();      // the last (reload) loads must land before LDS is reused
+  wait_vmem();      // reloads must land before LDS is reused
   __syncthreads();  // LDS is handed to the epilogue
 }
 
