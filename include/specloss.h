@@ -112,8 +112,9 @@ typedef struct {
 } specloss_problem;
 
 /*
- * Bytes of device workspace needed when at most `max_chunk_rows` rows are
- * processed per chunk (rounded up to a multiple of 256; <= 0 selects 8192).
+ * Bytes of device workspace needed by any of the calls below when at most
+ * `max_chunk_rows` rows are processed per chunk (rounded up to a multiple of
+ * 256; <= 0 selects 8192).
  * The backward stages a bf16 (fp32 for fp32 inputs) logit-gradient chunk of
  * about 2 * chunk * V elements; no buffer of N x V elements is ever needed.
  * The calls pick the largest chunk that fits the workspace they are given.
@@ -155,6 +156,25 @@ int lmhead_loss_bwd(const specloss_problem* p, const float* grad_loss, const flo
                     const int64_t* counts, const void* saved, void* workspace, size_t ws_bytes,
                     void* dhidden, int32_t dh_dtype, float* dW, int accumulate_dW,
                     hipStream_t stream);
+
+/*
+ * Forward and backward in one call, for a loss that is the last node of the
+ * graph (its upstream gradient is known before the forward runs): all the
+ * outputs of lmhead_loss_fwd and of lmhead_loss_bwd for the seed
+ *   seed_r = (grad_loss ? grad_loss[r] : 0) + (grad_mean ? grad_mean[0] / n_valid : 0)
+ * on valid rows.  This is the per-chunk loop of the blog's "Backward pass"
+ * section (logits, loss and gradients of one token chunk, LM-head gradient
+ * accumulated over chunks): for the label and argmax-p cross-entropies the
+ * forward pass leaves exp(z - tile max) of the chunk (bf16 for bf16 inputs)
+ * in the workspace and the logit gradient is formed from it, so the logits
+ * are not recomputed.  Other kinds run the forward and backward sequences
+ * back to back.  `saved` may be NULL.  Errors as for the two calls.
+ */
+int lmhead_loss_fwd_bwd(const specloss_problem* p, void* workspace, size_t ws_bytes, float* loss,
+                        float* term_loss, float* lse_q, void* saved, int64_t* counts,
+                        float* reduced, const float* grad_loss, const float* grad_mean,
+                        void* dhidden, int32_t dh_dtype, float* dW, int accumulate_dW,
+                        hipStream_t stream);
 
 /*
  * Alignment before chunking for draft heads (blog, "Correctness: alignment

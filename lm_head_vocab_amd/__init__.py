@@ -6,6 +6,7 @@ tensors into its C-ABI.  There is no CPU or eager fallback.
 """
 from .binding import (  # noqa: F401
     IGNORE_INDEX, KINDS, SpecLossError, kind_name, lmhead_loss_bwd, lmhead_loss_fwd,
+    lmhead_loss_fwd_bwd,
     lmhead_loss_workspace_size, load_library, make_problem, specloss_align_heads,
     specloss_saved_bytes, strerror,
 )

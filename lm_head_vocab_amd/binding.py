@@ -59,6 +59,7 @@ EXPORTS = (
     "specloss_saved_bytes",
     "lmhead_loss_fwd",
     "lmhead_loss_bwd",
+    "lmhead_loss_fwd_bwd",
     "specloss_align_heads",
     "specloss_strerror",
     "specloss_kind_name",
@@ -90,6 +91,9 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.lmhead_loss_fwd.restype = ctypes.c_int
     lib.lmhead_loss_bwd.argtypes = [P, vp, vp, vp, vp, vp, sz, vp, i32, vp, ctypes.c_int, vp]
     lib.lmhead_loss_bwd.restype = ctypes.c_int
+    lib.lmhead_loss_fwd_bwd.argtypes = [P, vp, sz, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp,
+                                        ctypes.c_int, vp]
+    lib.lmhead_loss_fwd_bwd.restype = ctypes.c_int
     lib.specloss_align_heads.argtypes = [i64, i64, i32, ctypes.POINTER(i32), vp, vp, vp, vp]
     lib.specloss_align_heads.restype = ctypes.c_int
     lib.specloss_strerror.argtypes = [ctypes.c_int]
@@ -200,6 +204,20 @@ def lmhead_loss_bwd(problem: Problem, grad_loss: Optional[torch.Tensor],
         ctypes.byref(problem), _ptr(grad_loss), _ptr(grad_mean), _ptr(counts), _ptr(saved),
         _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(dhidden), dh_dtype,
         _ptr(dW), int(bool(accumulate_dW)), _stream(stream)), "lmhead_loss_bwd")
+
+
+def lmhead_loss_fwd_bwd(problem: Problem, workspace: torch.Tensor, loss: torch.Tensor,
+                        term_loss: Optional[torch.Tensor], lse_q: Optional[torch.Tensor],
+                        saved: Optional[torch.Tensor], counts: torch.Tensor,
+                        reduced: Optional[torch.Tensor], grad_loss: Optional[torch.Tensor],
+                        grad_mean: Optional[torch.Tensor], dhidden: Optional[torch.Tensor],
+                        dW: Optional[torch.Tensor], accumulate_dW: bool = False, stream=None) -> None:
+    dh_dtype = BF16 if (dhidden is not None and dhidden.dtype == torch.bfloat16) else F32
+    _check(load_library().lmhead_loss_fwd_bwd(
+        ctypes.byref(problem), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _ptr(loss), _ptr(term_loss), _ptr(lse_q), _ptr(saved), _ptr(counts), _ptr(reduced),
+        _ptr(grad_loss), _ptr(grad_mean), _ptr(dhidden), dh_dtype, _ptr(dW),
+        int(bool(accumulate_dW)), _stream(stream)), "lmhead_loss_fwd_bwd")
 
 
 def specloss_align_heads(seq_len: int, batch: int, shifts, loss_mask: Optional[torch.Tensor],

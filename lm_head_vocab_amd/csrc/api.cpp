@@ -111,6 +111,8 @@ struct Layout {
   size_t pz, pu, p2, zy, fwd_end;
   // backward
   size_t wt, ht, dz, dzt, bwd_end;
+  // single-call forward+backward: forward partials and backward buffers at once
+  size_t f_pz, f_pu, f_zy, f_wt, f_ht, f_dz, f_dzt, fused_end;
 };
 
 Layout plan(const specloss_problem* p, const KindSet& k, int64_t Nc) {
@@ -144,17 +146,32 @@ Layout plan(const specloss_problem* p, const KindSet& k, int64_t Nc) {
   L.dz = take((size_t)Nc * L.Vp * L.es);
   L.dzt = take((size_t)L.Vp * Nc * L.es);
   L.bwd_end = o;
+  o = L.head_end;
+  L.f_pz = take(2 * tile_cols);
+  L.f_pu = take(k.target ? 3 * tile_cols : 0);
+  L.f_zy = take(2 * (size_t)Nc * 4);
+  L.f_wt = take((size_t)L.H * L.Vp * L.es);
+  L.f_ht = take((size_t)L.H * Nc * L.es);
+  L.f_dz = take((size_t)Nc * L.Vp * L.es);
+  L.f_dzt = take((size_t)L.Vp * Nc * L.es);
+  L.fused_end = o;
   return L;
 }
 
 // largest chunk (multiple of 256, at most the padded row count) whose region fits
-int64_t pick_chunk(const specloss_problem* p, const KindSet& k, size_t ws_bytes, bool bwd) {
+enum Region { REGION_FWD, REGION_BWD, REGION_FUSED };
+
+size_t region_end(const Layout& L, Region r) {
+  return r == REGION_FWD ? L.fwd_end : (r == REGION_BWD ? L.bwd_end : L.fused_end);
+}
+
+int64_t pick_chunk(const specloss_problem* p, const KindSet& k, size_t ws_bytes, Region region) {
   const int64_t top = round_up(p->n_rows, kChunkQuantum);
   int64_t lo = 1, hi = top / kChunkQuantum, best = 0;
   while (lo <= hi) {  // the requirement grows with the chunk
     const int64_t mid = (lo + hi) / 2;
     const Layout L = plan(p, k, mid * kChunkQuantum);
-    if ((bwd ? L.bwd_end : L.fwd_end) <= ws_bytes) {
+    if (region_end(L, region) <= ws_bytes) {
       best = mid;
       lo = mid + 1;
     } else {
@@ -208,11 +225,13 @@ GemmOperand target_operand(const specloss_problem* p, int64_t r0, int64_t rows, 
 
 enum KernelId : int32_t {
   K_VALIDITY, K_STATS_Q, K_STATS_P, K_COMBINE1, K_ROWDOT, K_DIV, K_COMBINE2, K_REDUCE, K_COPY,
-  K_SEED, K_TRANSPOSE_W, K_TRANSPOSE_H, K_DZ, K_GEMM_DH, K_GEMM_DW, K_NUM_IDS
+  K_SEED, K_TRANSPOSE_W, K_TRANSPOSE_H, K_DZ, K_GEMM_DH, K_GEMM_DW, K_STATS_STAGE, K_DZ_STAGE,
+  K_NUM_IDS
 };
 const char* const kKernelNames[K_NUM_IDS] = {
     "validity", "stats_q", "stats_p", "combine1", "rowdot", "div", "combine2", "reduce",
-    "copy_lse", "seed", "transpose_W", "transpose_h", "dz", "gemm_dh", "gemm_dW"};
+    "copy_lse", "seed", "transpose_W", "transpose_h", "dz", "gemm_dh", "gemm_dW",
+    "stats_stage", "dz_stage"};
 
 // Brackets launches with the trace's events when the problem carries one.
 struct Tracer {
@@ -247,12 +266,260 @@ int Tracer::begin(int32_t id, double w) {
   if (i >= t->capacity) return -1;
   t->ids[i] = id;
   t->work[i] = w;
-  hipEventRecord(t->ev[2 * i], s);
+  (void)hipEventRecord(t->ev[2 * i], s);
   return i;
 }
 void Tracer::end(int i) {
-  if (t && i >= 0) hipEventRecord(t->ev[2 * i + 1], s);
+  if (t && i >= 0) (void)hipEventRecord(t->ev[2 * i + 1], s);
 }
+}  // namespace
+
+namespace {
+
+struct FwdBufs {
+  float* pz;   // q-side partials [2][Tv][Nc]
+  float* pu;   // p-side partials [3][Tv][Nc]
+  float* p2;   // pass-2 partials [kNumSums][Tv][Nc]
+  float* zy;   // gathered logits [2][Nc]
+  int64_t Nc;
+};
+
+int launch_validity_for(const specloss_problem* p, const KindSet& k, const SavedView& sv,
+                        int64_t* counts, Tracer& tr, hipStream_t stream) {
+  ValidityLaunch va;
+  va.n = p->n_rows;
+  va.mask = p->mask;
+  va.labels = p->labels;
+  va.use_labels = k.label;
+  va.target_row = p->target_row;
+  va.n_target = p->n_target_rows;
+  va.use_target = k.target;
+  va.vocab = (int32_t)p->vocab;
+  va.flags = sv.flags;
+  va.y_label = sv.y_label;
+  va.counts = counts;
+  TRACED(tr, K_VALIDITY, (double)p->n_rows * 10, launch_validity(va, stream));
+  return SPECLOSS_OK;
+}
+
+// Forward of chunk rows [r0, r0 + rows): pass 1 (q side, staged into `stage`
+// when given; p side with argmax), merge, label-logit gather, pass 2 and the
+// per-row losses.
+int fwd_chunk(const specloss_problem* p, const KindSet& k, const Layout& L, const FwdBufs& b,
+              const SavedView& sv, float* loss, float* terms, int64_t r0, int64_t rows,
+              void* stage, Tracer& tr, hipStream_t stream) {
+  const bool bf16 = p->in_dtype == SPECLOSS_BF16;
+  const int64_t H = L.H, Nc = b.Nc;
+  const int64_t tile_cols = L.Tv * Nc;
+  const GemmOperand Bh = op(offset_rows(p->hidden_states, r0, H, L.es), H, rows);
+
+  StatsLaunch sz;
+  sz.A = op(p->W, H, p->vocab);
+  sz.B = Bh;
+  sz.k_len = (int32_t)H;
+  sz.vocab = (int32_t)p->vocab;
+  sz.tiles_m = (int32_t)L.Tv;
+  sz.tiles_n = (int32_t)cdiv(rows, 256);
+  sz.ncols = (int32_t)rows;
+  sz.ldp = (int32_t)Nc;
+  sz.pm = b.pz;
+  sz.ps = b.pz + tile_cols;
+  sz.pi = nullptr;
+  if (stage) {
+    StatsStageLaunch ss;
+    ss.st = sz;
+    ss.stage = stage;
+    ss.ld_stage = L.Vp;
+    TRACED(tr, K_STATS_STAGE, 2.0 * rows * H * p->vocab, launch_stats_stage(bf16, ss, stream));
+  } else {
+    TRACED(tr, K_STATS_Q, 2.0 * rows * H * p->vocab, launch_stats(bf16, false, sz, stream));
+  }
+
+  if (k.target) {
+    StatsLaunch su = sz;
+    su.A = op(p->W_t, H, p->vocab);
+    su.B = target_operand(p, r0, rows, L.es);
+    su.pm = b.pu;
+    su.ps = b.pu + tile_cols;
+    su.pi = reinterpret_cast<int32_t*>(b.pu + 2 * tile_cols);
+    TRACED(tr, K_STATS_P, 2.0 * rows * H * p->vocab, launch_stats(bf16, true, su, stream));
+  }
+
+  Combine1Launch c1;
+  c1.tiles_m = (int32_t)L.Tv;
+  c1.ncols = (int32_t)rows;
+  c1.ldp = (int32_t)Nc;
+  c1.pm_z = b.pz;
+  c1.ps_z = b.pz + tile_cols;
+  c1.pm_u = k.target ? b.pu : nullptr;
+  c1.ps_u = k.target ? b.pu + tile_cols : nullptr;
+  c1.pi_u = k.target ? reinterpret_cast<const int32_t*>(b.pu + 2 * tile_cols) : nullptr;
+  c1.lse_q = sv.lse_q + r0;
+  c1.lse_p = sv.lse_p + r0;
+  c1.y_arg = sv.y_arg + r0;
+  TRACED(tr, K_COMBINE1, (k.target ? 5.0 : 2.0) * L.Tv * rows * 4, launch_combine1(c1, stream));
+
+  const bool ce_lab = (k.active >> SPECLOSS_CE_LABEL) & 1u;
+  const bool ce_arg = (k.active >> SPECLOSS_CE_ARGMAX_P) & 1u;
+  if (ce_lab || ce_arg) {
+    RowdotLaunch rd;
+    rd.W = p->W;
+    rd.h = offset_rows(p->hidden_states, r0, H, L.es);
+    rd.H = H;
+    rd.ncols = (int32_t)rows;
+    rd.vocab = (int32_t)p->vocab;
+    rd.y1 = ce_lab ? sv.y_label + r0 : nullptr;
+    rd.y2 = ce_arg ? sv.y_arg + r0 : nullptr;
+    rd.out1 = b.zy;
+    rd.out2 = b.zy + Nc;
+    TRACED(tr, K_ROWDOT, 2.0 * rows * H * L.es * ((ce_lab ? 1 : 0) + (ce_arg ? 1 : 0)),
+           launch_rowdot(bf16, rd, stream));
+  }
+
+  if (k.pass2) {
+    DivLaunch dv;
+    dv.Az = op(p->W, H, p->vocab);
+    dv.Bz = Bh;
+    dv.Au = op(p->W_t, H, p->vocab);
+    dv.Bu = target_operand(p, r0, rows, L.es);
+    dv.k_len = (int32_t)H;
+    dv.vocab = (int32_t)p->vocab;
+    dv.tiles_m = (int32_t)L.Tv;
+    dv.tiles_n = (int32_t)cdiv(rows, 128);
+    dv.ncols = (int32_t)rows;
+    dv.ldp = (int32_t)Nc;
+    dv.lse_q = sv.lse_q + r0;
+    dv.lse_p = sv.lse_p + r0;
+    dv.need = k.need;
+    dv.part = b.p2;
+    dv.part_stride = tile_cols;
+    TRACED(tr, K_DIV, 4.0 * rows * H * p->vocab, launch_div(bf16, dv, stream));
+  }
+
+  Combine2Launch c2;
+  c2.tiles_m = (int32_t)L.Tv;
+  c2.ncols = (int32_t)rows;
+  c2.ldp = (int32_t)Nc;
+  c2.part = b.p2;
+  c2.part_stride = tile_cols;
+  c2.need = k.need;
+  memcpy(c2.w, p->weights, sizeof(c2.w));
+  c2.flags = sv.flags + r0;
+  c2.lse_q = sv.lse_q + r0;
+  c2.zy_lab = ce_lab ? b.zy : nullptr;
+  c2.zy_arg = ce_arg ? b.zy + Nc : nullptr;
+  c2.loss = loss + r0;
+  c2.term = terms + r0;
+  c2.term_stride = p->n_rows;
+  c2.alpha = sv.alpha + r0;
+  c2.S = sv.S + r0;
+  c2.rkl = sv.rkl + r0;
+  c2.eqg = sv.eqg + r0;
+  TRACED(tr, K_COMBINE2, (double)rows * 4 * (2 + __builtin_popcount(k.need) * L.Tv),
+         launch_combine2(c2, stream));
+  return SPECLOSS_OK;
+}
+
+int launch_reduce_for(const specloss_problem* p, const KindSet& k, const float* loss,
+                      const float* terms, const int64_t* counts, float* reduced, Tracer& tr,
+                      hipStream_t stream) {
+  ReduceLaunch rl;
+  rl.n = p->n_rows;
+  rl.loss = loss;
+  rl.term = terms;
+  rl.term_stride = p->n_rows;
+  rl.active = k.active;
+  rl.counts = counts;
+  rl.reduced = reduced;
+  TRACED(tr, K_REDUCE, (double)p->n_rows * 4 * (1 + __builtin_popcount(k.active)),
+         launch_reduce(rl, stream));
+  return SPECLOSS_OK;
+}
+
+int launch_seed_for(const specloss_problem* p, const SavedView& sv, const float* grad_loss,
+                    const float* grad_mean, const int64_t* counts, float* seed, Tracer& tr,
+                    hipStream_t stream) {
+  SeedLaunch sd;
+  sd.n = p->n_rows;
+  sd.flags = sv.flags;
+  sd.grad_loss = grad_loss;
+  sd.grad_mean = grad_mean;
+  sd.counts = counts;
+  sd.seed = seed;
+  TRACED(tr, K_SEED, (double)p->n_rows * 12, launch_seed(sd, stream));
+  return SPECLOSS_OK;
+}
+
+// dh rows [r0, r0 + rows) = dz W and dW (+)= dz^T h for one chunk, from the
+// staged dz [Nc][Vp], dz^T [Vp][Nc], W^T [H][Vp] and h^T [H][Nc].
+int bwd_contract(const specloss_problem* p, const Layout& L, int64_t Nc, const void* dz,
+                 const void* dzt, const void* wt, const void* ht, int64_t r0, int64_t rows,
+                 bool accumulate, void* dhidden, int32_t dh_dtype, float* dW, Tracer& tr,
+                 hipStream_t stream) {
+  const bool bf16 = p->in_dtype == SPECLOSS_BF16;
+  const int64_t H = L.H, V = L.V, Vp = L.Vp;
+  const size_t dh_es = dh_dtype == SPECLOSS_BF16 ? 2 : 4;
+  if (dhidden) {
+    GemmLaunch g;
+    g.A = op(dz, Vp, Nc);
+    g.B = op(wt, Vp, H);
+    g.k_len = (int32_t)Vp;
+    g.tiles_m = (int32_t)cdiv(rows, 256);
+    g.tiles_n = (int32_t)cdiv(H, 256);
+    g.m_valid = (int32_t)rows;
+    g.n_valid = (int32_t)H;
+    g.C = static_cast<char*>(dhidden) + (size_t)r0 * H * dh_es;
+    g.ldc = H;
+    g.accumulate = 0;
+    g.out_bf16 = dh_dtype == SPECLOSS_BF16;
+    g.role = 0;
+    TRACED(tr, K_GEMM_DH, 2.0 * rows * H * V, launch_gemm(bf16, g, stream));
+  }
+  if (dW) {
+    GemmLaunch g;
+    g.A = op(dzt, Nc, Vp);
+    g.B = op(ht, Nc, H);
+    g.k_len = (int32_t)round_up(rows, 64);
+    g.tiles_m = (int32_t)L.Tv;
+    g.tiles_n = (int32_t)cdiv(H, 256);
+    g.m_valid = (int32_t)V;
+    g.n_valid = (int32_t)H;
+    g.C = dW;
+    g.ldc = H;
+    g.accumulate = accumulate ? 1 : 0;
+    g.out_bf16 = 0;
+    g.role = 1;
+    TRACED(tr, K_GEMM_DW, 2.0 * rows * H * V, launch_gemm(bf16, g, stream));
+  }
+  return SPECLOSS_OK;
+}
+
+#define TRY(expr)                   \
+  do {                              \
+    const int rc_ = (expr);         \
+    if (rc_) return rc_;            \
+  } while (0)
+
+int check_fwd_outputs(const float* loss, const float* term_loss, const float* lse_q,
+                      const void* saved, const int64_t* counts, const float* reduced) {
+  if (!loss || !counts) return SPECLOSS_E_INVAL;
+  if (!aligned(loss, 4) || !aligned(term_loss, 4) || !aligned(lse_q, 4) || !aligned(saved, 4) ||
+      !aligned(counts, 8) || !aligned(reduced, 4))
+    return SPECLOSS_E_UNSUPPORTED;
+  return SPECLOSS_OK;
+}
+
+int check_bwd_args(const float* grad_loss, const float* grad_mean, void* dhidden,
+                   int32_t dh_dtype, float* dW) {
+  if (!grad_loss && !grad_mean) return SPECLOSS_E_INVAL;
+  if (!dhidden && !dW) return SPECLOSS_E_INVAL;
+  if (dh_dtype != SPECLOSS_F32 && dh_dtype != SPECLOSS_BF16) return SPECLOSS_E_UNSUPPORTED;
+  if (!aligned(grad_loss, 4) || !aligned(grad_mean, 4) || !aligned(dW, 4) ||
+      !aligned(dhidden, dh_dtype == SPECLOSS_F32 ? 4 : 2))
+    return SPECLOSS_E_UNSUPPORTED;
+  return SPECLOSS_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -271,7 +538,9 @@ int lmhead_loss_workspace_size(const specloss_problem* p, int64_t max_chunk_rows
   nc = round_up(nc, kChunkQuantum);
   nc = nc < round_up(p->n_rows, kChunkQuantum) ? nc : round_up(p->n_rows, kChunkQuantum);
   const Layout L = plan(p, k, nc);
-  *bytes = L.fwd_end > L.bwd_end ? L.fwd_end : L.bwd_end;
+  size_t b = L.fwd_end > L.bwd_end ? L.fwd_end : L.bwd_end;
+  if (L.fused_end > b) b = L.fused_end;
+  *bytes = b;
   return SPECLOSS_OK;
 }
 
@@ -279,154 +548,29 @@ int lmhead_loss_fwd(const specloss_problem* p, void* workspace, size_t ws_bytes,
                     float* term_loss, float* lse_q, void* saved, int64_t* counts, float* reduced,
                     hipStream_t stream) {
   KindSet k;
-  int rc = check_problem(p, &k);
-  if (rc) return rc;
-  if (!loss || !counts) return SPECLOSS_E_INVAL;
-  if (!aligned(loss, 4) || !aligned(term_loss, 4) || !aligned(lse_q, 4) || !aligned(saved, 4) ||
-      !aligned(counts, 8) || !aligned(reduced, 4))
-    return SPECLOSS_E_UNSUPPORTED;
+  TRY(check_problem(p, &k));
+  TRY(check_fwd_outputs(loss, term_loss, lse_q, saved, counts, reduced));
   if (!workspace || !aligned(workspace, kAlign)) return SPECLOSS_E_WORKSPACE;
-  const int64_t Nc = pick_chunk(p, k, ws_bytes, false);
+  const int64_t Nc = pick_chunk(p, k, ws_bytes, REGION_FWD);
   if (Nc <= 0) return SPECLOSS_E_WORKSPACE;
   const Layout L = plan(p, k, Nc);
   char* ws = static_cast<char*>(workspace);
-  const bool bf16 = p->in_dtype == SPECLOSS_BF16;
-  const int64_t N = L.N, H = L.H;
+  const int64_t N = L.N;
   const SavedView sv = saved_view(saved ? saved : ws + L.saved, N);
   float* terms = term_loss ? term_loss : reinterpret_cast<float*>(ws + L.terms);
-  float* pz = reinterpret_cast<float*>(ws + L.pz);
-  float* pu = reinterpret_cast<float*>(ws + L.pu);
-  float* p2 = reinterpret_cast<float*>(ws + L.p2);
-  float* zy = reinterpret_cast<float*>(ws + L.zy);
-  const int64_t tile_cols = L.Tv * Nc;
+  const FwdBufs b{reinterpret_cast<float*>(ws + L.pz), reinterpret_cast<float*>(ws + L.pu),
+                  reinterpret_cast<float*>(ws + L.p2), reinterpret_cast<float*>(ws + L.zy), Nc};
   Tracer tr{p->trace, stream};
 
-  ValidityLaunch va;
-  va.n = N;
-  va.mask = p->mask;
-  va.labels = p->labels;
-  va.use_labels = k.label;
-  va.target_row = p->target_row;
-  va.n_target = p->n_target_rows;
-  va.use_target = k.target;
-  va.vocab = (int32_t)p->vocab;
-  va.flags = sv.flags;
-  va.y_label = sv.y_label;
-  va.counts = counts;
-  TRACED(tr, K_VALIDITY, (double)N * 10, launch_validity(va, stream));
-
+  TRY(launch_validity_for(p, k, sv, counts, tr, stream));
   for (int64_t r0 = 0; r0 < N; r0 += Nc) {
     const int64_t rows = (N - r0) < Nc ? (N - r0) : Nc;
-    const GemmOperand Bh = op(offset_rows(p->hidden_states, r0, H, L.es), H, rows);
-
-    StatsLaunch sz;
-    sz.A = op(p->W, H, p->vocab);
-    sz.B = Bh;
-    sz.k_len = (int32_t)H;
-    sz.vocab = (int32_t)p->vocab;
-    sz.tiles_m = (int32_t)L.Tv;
-    sz.tiles_n = (int32_t)cdiv(rows, 256);
-    sz.ncols = (int32_t)rows;
-    sz.ldp = (int32_t)Nc;
-    sz.pm = pz;
-    sz.ps = pz + tile_cols;
-    sz.pi = nullptr;
-    TRACED(tr, K_STATS_Q, 2.0 * rows * H * p->vocab, launch_stats(bf16, false, sz, stream));
-
-    if (k.target) {
-      StatsLaunch su = sz;
-      su.A = op(p->W_t, H, p->vocab);
-      su.B = target_operand(p, r0, rows, L.es);
-      su.pm = pu;
-      su.ps = pu + tile_cols;
-      su.pi = reinterpret_cast<int32_t*>(pu + 2 * tile_cols);
-      TRACED(tr, K_STATS_P, 2.0 * rows * H * p->vocab, launch_stats(bf16, true, su, stream));
-    }
-
-    Combine1Launch c1;
-    c1.tiles_m = (int32_t)L.Tv;
-    c1.ncols = (int32_t)rows;
-    c1.ldp = (int32_t)Nc;
-    c1.pm_z = pz;
-    c1.ps_z = pz + tile_cols;
-    c1.pm_u = k.target ? pu : nullptr;
-    c1.ps_u = k.target ? pu + tile_cols : nullptr;
-    c1.pi_u = k.target ? reinterpret_cast<const int32_t*>(pu + 2 * tile_cols) : nullptr;
-    c1.lse_q = sv.lse_q + r0;
-    c1.lse_p = sv.lse_p + r0;
-    c1.y_arg = sv.y_arg + r0;
-    TRACED(tr, K_COMBINE1, (k.target ? 5.0 : 2.0) * L.Tv * rows * 4, launch_combine1(c1, stream));
-
-    const bool ce_lab = (k.active >> SPECLOSS_CE_LABEL) & 1u;
-    const bool ce_arg = (k.active >> SPECLOSS_CE_ARGMAX_P) & 1u;
-    if (ce_lab || ce_arg) {
-      RowdotLaunch rd;
-      rd.W = p->W;
-      rd.h = offset_rows(p->hidden_states, r0, H, L.es);
-      rd.H = H;
-      rd.ncols = (int32_t)rows;
-      rd.vocab = (int32_t)p->vocab;
-      rd.y1 = ce_lab ? sv.y_label + r0 : nullptr;
-      rd.y2 = ce_arg ? sv.y_arg + r0 : nullptr;
-      rd.out1 = zy;
-      rd.out2 = zy + Nc;
-      TRACED(tr, K_ROWDOT, 2.0 * rows * H * L.es * ((ce_lab ? 1 : 0) + (ce_arg ? 1 : 0)), launch_rowdot(bf16, rd, stream));
-    }
-
-    if (k.pass2) {
-      DivLaunch dv;
-      dv.Az = op(p->W, H, p->vocab);
-      dv.Bz = Bh;
-      dv.Au = op(p->W_t, H, p->vocab);
-      dv.Bu = target_operand(p, r0, rows, L.es);
-      dv.k_len = (int32_t)H;
-      dv.vocab = (int32_t)p->vocab;
-      dv.tiles_m = (int32_t)L.Tv;
-      dv.tiles_n = (int32_t)cdiv(rows, 128);
-      dv.ncols = (int32_t)rows;
-      dv.ldp = (int32_t)Nc;
-      dv.lse_q = sv.lse_q + r0;
-      dv.lse_p = sv.lse_p + r0;
-      dv.need = k.need;
-      dv.part = p2;
-      dv.part_stride = tile_cols;
-      TRACED(tr, K_DIV, 4.0 * rows * H * p->vocab, launch_div(bf16, dv, stream));
-    }
-
-    Combine2Launch c2;
-    c2.tiles_m = (int32_t)L.Tv;
-    c2.ncols = (int32_t)rows;
-    c2.ldp = (int32_t)Nc;
-    c2.part = p2;
-    c2.part_stride = tile_cols;
-    c2.need = k.need;
-    memcpy(c2.w, p->weights, sizeof(c2.w));
-    c2.flags = sv.flags + r0;
-    c2.lse_q = sv.lse_q + r0;
-    c2.zy_lab = ce_lab ? zy : nullptr;
-    c2.zy_arg = ce_arg ? zy + Nc : nullptr;
-    c2.loss = loss + r0;
-    c2.term = terms + r0;
-    c2.term_stride = N;
-    c2.alpha = sv.alpha + r0;
-    c2.S = sv.S + r0;
-    c2.rkl = sv.rkl + r0;
-    c2.eqg = sv.eqg + r0;
-    TRACED(tr, K_COMBINE2, (double)rows * 4 * (2 + __builtin_popcount(k.need) * L.Tv), launch_combine2(c2, stream));
+    TRY(fwd_chunk(p, k, L, b, sv, loss, terms, r0, rows, nullptr, tr, stream));
   }
-
-  if (reduced) {
-    ReduceLaunch rl;
-    rl.n = N;
-    rl.loss = loss;
-    rl.term = terms;
-    rl.term_stride = N;
-    rl.active = k.active;
-    rl.counts = counts;
-    rl.reduced = reduced;
-    TRACED(tr, K_REDUCE, (double)N * 4 * (1 + __builtin_popcount(k.active)), launch_reduce(rl, stream));
-  }
-  if (lse_q) TRACED(tr, K_COPY, (double)N * 8, hipMemcpyAsync(lse_q, sv.lse_q, (size_t)N * 4, hipMemcpyDeviceToDevice, stream));
+  if (reduced) TRY(launch_reduce_for(p, k, loss, terms, counts, reduced, tr, stream));
+  if (lse_q)
+    TRACED(tr, K_COPY, (double)N * 8,
+           hipMemcpyAsync(lse_q, sv.lse_q, (size_t)N * 4, hipMemcpyDeviceToDevice, stream));
   return SPECLOSS_OK;
 }
 
@@ -435,18 +579,12 @@ int lmhead_loss_bwd(const specloss_problem* p, const float* grad_loss, const flo
                     void* dhidden, int32_t dh_dtype, float* dW, int accumulate_dW,
                     hipStream_t stream) {
   KindSet k;
-  int rc = check_problem(p, &k);
-  if (rc) return rc;
+  TRY(check_problem(p, &k));
   if (!saved || !counts) return SPECLOSS_E_INVAL;
-  if (!grad_loss && !grad_mean) return SPECLOSS_E_INVAL;
-  if (!dhidden && !dW) return SPECLOSS_E_INVAL;
-  if (dh_dtype != SPECLOSS_F32 && dh_dtype != SPECLOSS_BF16) return SPECLOSS_E_UNSUPPORTED;
-  if (!aligned(grad_loss, 4) || !aligned(grad_mean, 4) || !aligned(counts, 8) ||
-      !aligned(saved, 4) || !aligned(dW, 4) ||
-      !aligned(dhidden, dh_dtype == SPECLOSS_F32 ? 4 : 2))
-    return SPECLOSS_E_UNSUPPORTED;
+  TRY(check_bwd_args(grad_loss, grad_mean, dhidden, dh_dtype, dW));
+  if (!aligned(counts, 8) || !aligned(saved, 4)) return SPECLOSS_E_UNSUPPORTED;
   if (!workspace || !aligned(workspace, kAlign)) return SPECLOSS_E_WORKSPACE;
-  const int64_t Nc = pick_chunk(p, k, ws_bytes, true);
+  const int64_t Nc = pick_chunk(p, k, ws_bytes, REGION_BWD);
   if (Nc <= 0) return SPECLOSS_E_WORKSPACE;
   const Layout L = plan(p, k, Nc);
   char* ws = static_cast<char*>(workspace);
@@ -458,24 +596,18 @@ int lmhead_loss_bwd(const specloss_problem* p, const float* grad_loss, const flo
   void* ht = ws + L.ht;
   void* dz = ws + L.dz;
   void* dzt = ws + L.dzt;
-  const size_t dh_es = dh_dtype == SPECLOSS_BF16 ? 2 : 4;
   Tracer tr{p->trace, stream};
 
-  SeedLaunch sd;
-  sd.n = N;
-  sd.flags = sv.flags;
-  sd.grad_loss = grad_loss;
-  sd.grad_mean = grad_mean;
-  sd.counts = counts;
-  sd.seed = seed;
-  TRACED(tr, K_SEED, (double)N * 12, launch_seed(sd, stream));
-  if (dhidden) TRACED(tr, K_TRANSPOSE_W, 2.0 * Vp * H * L.es, launch_transpose(bf16, p->W, V, H, wt, Vp, stream));
+  TRY(launch_seed_for(p, sv, grad_loss, grad_mean, counts, seed, tr, stream));
+  if (dhidden)
+    TRACED(tr, K_TRANSPOSE_W, 2.0 * Vp * H * L.es, launch_transpose(bf16, p->W, V, H, wt, Vp, stream));
 
   int chunk = 0;
   for (int64_t r0 = 0; r0 < N; r0 += Nc, ++chunk) {
     const int64_t rows = (N - r0) < Nc ? (N - r0) : Nc;
     const void* hc = offset_rows(p->hidden_states, r0, H, L.es);
-    if (dW) TRACED(tr, K_TRANSPOSE_H, 2.0 * Nc * H * L.es, launch_transpose(bf16, hc, rows, H, ht, Nc, stream));
+    if (dW)
+      TRACED(tr, K_TRANSPOSE_H, 2.0 * Nc * H * L.es, launch_transpose(bf16, hc, rows, H, ht, Nc, stream));
 
     DzLaunch dl;
     dl.Az = op(p->W, H, V);
@@ -501,38 +633,88 @@ int lmhead_loss_bwd(const specloss_problem* p, const float* grad_loss, const flo
     dl.dzt = dzt;
     dl.ld_dzt = Nc;
     TRACED(tr, K_DZ, (k.dual_bwd ? 4.0 : 2.0) * rows * H * V, launch_dz(bf16, k.dual_bwd, dl, stream));
-
-    if (dhidden) {
-      GemmLaunch g;
-      g.A = op(dz, Vp, Nc);
-      g.B = op(wt, Vp, H);
-      g.k_len = (int32_t)Vp;
-      g.tiles_m = (int32_t)cdiv(rows, 256);
-      g.tiles_n = (int32_t)cdiv(H, 256);
-      g.m_valid = (int32_t)rows;
-      g.n_valid = (int32_t)H;
-      g.C = static_cast<char*>(dhidden) + (size_t)r0 * H * dh_es;
-      g.ldc = H;
-      g.accumulate = 0;
-      g.out_bf16 = dh_dtype == SPECLOSS_BF16;
-      TRACED(tr, K_GEMM_DH, 2.0 * rows * H * V, launch_gemm(bf16, g, stream));
-    }
-    if (dW) {
-      GemmLaunch g;
-      g.A = op(dzt, Nc, Vp);
-      g.B = op(ht, Nc, H);
-      g.k_len = (int32_t)round_up(rows, 64);
-      g.tiles_m = (int32_t)L.Tv;
-      g.tiles_n = (int32_t)cdiv(H, 256);
-      g.m_valid = (int32_t)V;
-      g.n_valid = (int32_t)H;
-      g.C = dW;
-      g.ldc = H;
-      g.accumulate = (chunk > 0 || accumulate_dW) ? 1 : 0;
-      g.out_bf16 = 0;
-      TRACED(tr, K_GEMM_DW, 2.0 * rows * H * V, launch_gemm(bf16, g, stream));
-    }
+    TRY(bwd_contract(p, L, Nc, dz, dzt, wt, ht, r0, rows, chunk > 0 || accumulate_dW, dhidden,
+                     dh_dtype, dW, tr, stream));
   }
+  return SPECLOSS_OK;
+}
+
+int lmhead_loss_fwd_bwd(const specloss_problem* p, void* workspace, size_t ws_bytes, float* loss,
+                        float* term_loss, float* lse_q, void* saved, int64_t* counts,
+                        float* reduced, const float* grad_loss, const float* grad_mean,
+                        void* dhidden, int32_t dh_dtype, float* dW, int accumulate_dW,
+                        hipStream_t stream) {
+  KindSet k;
+  TRY(check_problem(p, &k));
+  TRY(check_fwd_outputs(loss, term_loss, lse_q, saved, counts, reduced));
+  TRY(check_bwd_args(grad_loss, grad_mean, dhidden, dh_dtype, dW));
+  if (!workspace || !aligned(workspace, kAlign)) return SPECLOSS_E_WORKSPACE;
+  if (k.dual_bwd) {
+    // kinds whose gradient needs the target distribution: the forward and
+    // backward sequences run back to back on the same workspace
+    char* ws = static_cast<char*>(workspace);
+    const Layout L0 = plan(p, k, kChunkQuantum);
+    void* sv_base = saved ? saved : ws + L0.saved;
+    TRY(lmhead_loss_fwd(p, workspace, ws_bytes, loss, term_loss, lse_q, sv_base, counts, reduced,
+                        stream));
+    return lmhead_loss_bwd(p, grad_loss, grad_mean, counts, sv_base, workspace, ws_bytes, dhidden,
+                           dh_dtype, dW, accumulate_dW, stream);
+  }
+  // label / argmax cross-entropies: pass 1 stages e = exp(z - m_tile) per
+  // chunk, the logit gradient is formed from it without recomputing logits
+  const int64_t Nc = pick_chunk(p, k, ws_bytes, REGION_FUSED);
+  if (Nc <= 0) return SPECLOSS_E_WORKSPACE;
+  const Layout L = plan(p, k, Nc);
+  char* ws = static_cast<char*>(workspace);
+  const bool bf16 = p->in_dtype == SPECLOSS_BF16;
+  const int64_t N = L.N, H = L.H, V = L.V, Vp = L.Vp;
+  const SavedView sv = saved_view(saved ? saved : ws + L.saved, N);
+  float* terms = term_loss ? term_loss : reinterpret_cast<float*>(ws + L.terms);
+  float* seed = reinterpret_cast<float*>(ws + L.seed);
+  const FwdBufs b{reinterpret_cast<float*>(ws + L.f_pz), reinterpret_cast<float*>(ws + L.f_pu),
+                  nullptr, reinterpret_cast<float*>(ws + L.f_zy), Nc};
+  void* wt = ws + L.f_wt;
+  void* ht = ws + L.f_ht;
+  void* dz = ws + L.f_dz;
+  void* dzt = ws + L.f_dzt;
+  Tracer tr{p->trace, stream};
+
+  TRY(launch_validity_for(p, k, sv, counts, tr, stream));
+  TRY(launch_seed_for(p, sv, grad_loss, grad_mean, counts, seed, tr, stream));
+  if (dhidden)
+    TRACED(tr, K_TRANSPOSE_W, 2.0 * Vp * H * L.es, launch_transpose(bf16, p->W, V, H, wt, Vp, stream));
+  int chunk = 0;
+  for (int64_t r0 = 0; r0 < N; r0 += Nc, ++chunk) {
+    const int64_t rows = (N - r0) < Nc ? (N - r0) : Nc;
+    TRY(fwd_chunk(p, k, L, b, sv, loss, terms, r0, rows, dz, tr, stream));
+    DzStageLaunch ds;
+    ds.tiles_m = (int32_t)L.Tv;
+    ds.ncols = (int32_t)rows;
+    ds.vocab = (int32_t)V;
+    ds.ldp = (int32_t)Nc;
+    ds.r0 = r0;
+    ds.pm = b.pz;
+    ds.seed = seed;
+    ds.sv = sv;
+    ds.w_lab = p->weights[SPECLOSS_CE_LABEL];
+    ds.w_arg = p->weights[SPECLOSS_CE_ARGMAX_P];
+    ds.dz = dz;
+    ds.ld_dz = Vp;
+    ds.dzt = dzt;
+    ds.ld_dzt = Nc;
+    ds.row_blocks = (int32_t)(cdiv(rows, 256) * 4);
+    TRACED(tr, K_DZ_STAGE, (double)ds.row_blocks * 64 * Vp * L.es * 3,
+           launch_dz_stage(bf16, ds, stream));
+    const void* hc = offset_rows(p->hidden_states, r0, H, L.es);
+    if (dW)
+      TRACED(tr, K_TRANSPOSE_H, 2.0 * Nc * H * L.es, launch_transpose(bf16, hc, rows, H, ht, Nc, stream));
+    TRY(bwd_contract(p, L, Nc, dz, dzt, wt, ht, r0, rows, chunk > 0 || accumulate_dW, dhidden,
+                     dh_dtype, dW, tr, stream));
+  }
+  if (reduced) TRY(launch_reduce_for(p, k, loss, terms, counts, reduced, tr, stream));
+  if (lse_q)
+    TRACED(tr, K_COPY, (double)N * 8,
+           hipMemcpyAsync(lse_q, sv.lse_q, (size_t)N * 4, hipMemcpyDeviceToDevice, stream));
   return SPECLOSS_OK;
 }
 
@@ -575,7 +757,7 @@ specloss_trace* specloss_trace_create(int32_t capacity) {
   for (; ok && made < 2 * capacity; ++made)
     if (hipEventCreate(&t->ev[made]) != hipSuccess) ok = false;
   if (!ok) {
-    for (int i = 0; i + 1 < made; ++i) hipEventDestroy(t->ev[i]);
+    for (int i = 0; i + 1 < made; ++i) (void)hipEventDestroy(t->ev[i]);
     t->capacity = 0;
     specloss_trace_destroy(t);
     return nullptr;
@@ -586,7 +768,7 @@ specloss_trace* specloss_trace_create(int32_t capacity) {
 void specloss_trace_destroy(specloss_trace* t) {
   if (!t) return;
   if (t->ev)
-    for (int i = 0; i < 2 * t->capacity; ++i) hipEventDestroy(t->ev[i]);
+    for (int i = 0; i < 2 * t->capacity; ++i) (void)hipEventDestroy(t->ev[i]);
   delete[] t->ev;
   delete[] t->ids;
   delete[] t->work;

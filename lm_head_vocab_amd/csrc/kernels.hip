@@ -33,6 +33,20 @@ __device__ __forceinline__ Operand<T> as_op(const GemmOperand& g) {
   return Operand<T>{static_cast<const T*>(g.base), g.ld, g.n_rows, g.map, g.map_len};
 }
 
+// The four lanes l, l^16, l^32, l^48 hold the same output column.  These
+// butterflies combine their values in a fixed order (lower lane first at each
+// level), so every lane ends with the same, repeatable result.
+__device__ __forceinline__ float col_sum(float x, int lane) {
+  float o = __shfl_xor(x, 16);
+  x = (lane & 16) ? o + x : x + o;
+  o = __shfl_xor(x, 32);
+  return (lane & 32) ? o + x : x + o;
+}
+__device__ __forceinline__ float col_max(float x) {
+  x = fmaxf(x, __shfl_xor(x, 16));
+  return fmaxf(x, __shfl_xor(x, 32));
+}
+
 // Merge two (max, sum of exp(x - max)) pairs; `a` is the lower-index side.
 __device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2) {
   const float mn = fmaxf(m, m2);
@@ -41,193 +55,6 @@ __device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2
   m = mn;
 }
 
-// ============================================================================
-// pass 1: per-tile softmax statistics
-// ============================================================================
-template <typename T, bool ARGMAX>
-__global__ __launch_bounds__(kThreads, 1) void k_stats(StatsLaunch a) {
-  using Cfg = TileCfg<T, 256, 256>;
-  __shared__ __attribute__((aligned(16))) char smem[Cfg::LDS_BYTES];
-  int tm, tn;
-  if (!tile_of(a.tiles_m, a.tiles_n, 4, tm, tn)) return;
-
-  f32x16_t acc[Cfg::FM][Cfg::FN];
-  zero_acc<Cfg>(acc);
-  tile_mainloop<T, Cfg>(acc, as_op<T>(a.A), tm * Cfg::BM, as_op<T>(a.B), tn * Cfg::BN, a.k_len,
-                        smem);
-
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int v_base = tm * Cfg::BM + wm * Cfg::WM;
-  const bool tail = tm * Cfg::BM + Cfg::BM > a.vocab;
-
-  float mj[Cfg::FN], sj[Cfg::FN];
-  int ij[Cfg::FN];
-#pragma unroll
-  for (int j = 0; j < Cfg::FN; ++j) {
-    float mx = -INFINITY;
-    int idx = 0x7fffffff;
-#pragma unroll
-    for (int i = 0; i < Cfg::FM; ++i)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int v = v_base + i * 32 + frag_row(r, lane);
-        float x = acc[i][j][r];
-        if (tail && v >= a.vocab) x = -INFINITY;
-        if (ARGMAX) {
-          if (x > mx) { mx = x; idx = v; }  // strict: keeps the lowest index
-        } else {
-          mx = fmaxf(mx, x);
-        }
-      }
-    float s = 0.0f;
-    if (mx != -INFINITY) {
-      const float mb = mx * kLog2e;
-#pragma unroll
-      for (int i = 0; i < Cfg::FM; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int v = v_base + i * 32 + frag_row(r, lane);
-          float x = acc[i][j][r];
-          if (tail && v >= a.vocab) x = -INFINITY;
-          s += fast_exp2(fmaf(x, kLog2e, -mb));
-        }
-    }
-    // the two half-waves hold the same token column, rows 4 apart
-    const float mo = __shfl_xor(mx, 32);
-    const float so = __shfl_xor(s, 32);
-    const int io = ARGMAX ? __shfl_xor(idx, 32) : 0;
-    const bool lo = lane < 32;
-    float m1 = lo ? mx : mo, s1 = lo ? s : so;
-    const float m2 = lo ? mo : mx, s2 = lo ? so : s;
-    int i1 = lo ? idx : io;
-    const int i2 = lo ? io : idx;
-    if (ARGMAX) i1 = (m2 > m1) ? i2 : ((m2 == m1) ? min(i1, i2) : i1);
-    lse_merge(m1, s1, m2, s2);
-    mj[j] = m1;
-    sj[j] = s1;
-    ij[j] = i1;
-  }
-
-  // the two wave rows (wm) share token columns: wm = 1 hands its values over
-  float* red = reinterpret_cast<float*>(smem);
-  if (wm == 1 && lane < 32) {
-#pragma unroll
-    for (int j = 0; j < Cfg::FN; ++j) {
-      const int c = wn * Cfg::WN + j * 32 + lane;
-      red[c * 3 + 0] = mj[j];
-      red[c * 3 + 1] = sj[j];
-      red[c * 3 + 2] = __int_as_float(ij[j]);
-    }
-  }
-  __syncthreads();
-  if (wm == 0 && lane < 32) {
-#pragma unroll
-    for (int j = 0; j < Cfg::FN; ++j) {
-      const int c = wn * Cfg::WN + j * 32 + lane;
-      float m = mj[j], s = sj[j];
-      int id = ij[j];
-      const float m2 = red[c * 3 + 0], s2 = red[c * 3 + 1];
-      const int i2 = __float_as_int(red[c * 3 + 2]);
-      if (ARGMAX) id = (m2 > m) ? i2 : ((m2 == m) ? min(id, i2) : id);
-      lse_merge(m, s, m2, s2);
-      const int col = tn * Cfg::BN + c;
-      if (col < a.ncols) {
-        const int64_t o = (int64_t)tm * a.ldp + col;
-        a.pm[o] = m;
-        a.ps[o] = s;
-        if (ARGMAX) a.pi[o] = id;
-      }
-    }
-  }
-}
-
-// ============================================================================
-// pass 2: divergence sums with the final logsumexps
-// ============================================================================
-template <typename T>
-__global__ __launch_bounds__(kThreads, 1) void k_div(DivLaunch a) {
-  using Cfg = TileCfg<T, 256, 128>;
-  __shared__ __attribute__((aligned(16))) char smem[Cfg::LDS_BYTES];
-  int tm, tn;
-  if (!tile_of(a.tiles_m, a.tiles_n, 4, tm, tn)) return;
-
-  f32x16_t az[Cfg::FM][Cfg::FN], au[Cfg::FM][Cfg::FN];
-  zero_acc<Cfg>(az);
-  zero_acc<Cfg>(au);
-  tile_mainloop<T, Cfg>(az, as_op<T>(a.Az), tm * Cfg::BM, as_op<T>(a.Bz), tn * Cfg::BN, a.k_len,
-                        smem);
-  tile_mainloop<T, Cfg>(au, as_op<T>(a.Au), tm * Cfg::BM, as_op<T>(a.Bu), tn * Cfg::BN, a.k_len,
-                        smem);
-
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int v_base = tm * Cfg::BM + wm * Cfg::WM;
-  const bool tail = tm * Cfg::BM + Cfg::BM > a.vocab;
-  const uint32_t need = a.need;
-
-  float sums[Cfg::FN][kNumSums];
-#pragma unroll
-  for (int j = 0; j < Cfg::FN; ++j) {
-    const int col = min(tn * Cfg::BN + wn * Cfg::WN + j * 32 + (lane & 31), a.ncols - 1);
-    const float lq0 = a.lse_q[col], lp0 = a.lse_p[col];
-    float s_alpha = 0.f, s_s = 0.f, s_kl = 0.f, s_rkl = 0.f, s_jsd = 0.f, s_eqg = 0.f;
-#pragma unroll
-    for (int i = 0; i < Cfg::FM; ++i)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int v = v_base + i * 32 + frag_row(r, lane);
-        if (tail && v >= a.vocab) continue;
-        const float lq = az[i][j][r] - lq0;
-        const float lp = au[i][j][r] - lp0;
-        const float q = fast_exp2(lq * kLog2e);
-        const float p = fast_exp2(lp * kLog2e);
-        if (need & SUM_ALPHA) s_alpha += fminf(p, q);
-        if (need & SUM_S) s_s += (q < p) ? q : ((q == p) ? 0.5f * q : 0.0f);
-        if (need & SUM_KL) s_kl += p * (lp - lq);
-        if (need & SUM_RKL) s_rkl += q * (lq - lp);
-        if (need & (SUM_JSD | SUM_EQG)) {
-          const float lm = fast_log2(0.5f * (p + q)) * kLn2;
-          if (need & SUM_JSD) s_jsd += 0.5f * (p * (lp - lm) + q * (lq - lm));
-          if (need & SUM_EQG) s_eqg += 0.5f * q * (lq - lm);
-        }
-      }
-    float v6[kNumSums] = {s_alpha, s_s, s_kl, s_rkl, s_jsd, s_eqg};
-    const bool lo = lane < 32;
-#pragma unroll
-    for (int f = 0; f < kNumSums; ++f) {
-      const float o = __shfl_xor(v6[f], 32);
-      sums[j][f] = lo ? (v6[f] + o) : (o + v6[f]);
-    }
-  }
-
-  float* red = reinterpret_cast<float*>(smem);  // [BN][kNumSums]
-  if (wm == 1 && lane < 32) {
-#pragma unroll
-    for (int j = 0; j < Cfg::FN; ++j) {
-      const int c = wn * Cfg::WN + j * 32 + lane;
-#pragma unroll
-      for (int f = 0; f < kNumSums; ++f) red[c * kNumSums + f] = sums[j][f];
-    }
-  }
-  __syncthreads();
-  if (wm == 0 && lane < 32) {
-#pragma unroll
-    for (int j = 0; j < Cfg::FN; ++j) {
-      const int c = wn * Cfg::WN + j * 32 + lane;
-      const int col = tn * Cfg::BN + c;
-      if (col >= a.ncols) continue;
-#pragma unroll
-      for (int f = 0; f < kNumSums; ++f)
-        if (need & (1u << f))
-          a.part[f * a.part_stride + (int64_t)tm * a.ldp + col] = sums[j][f] + red[c * kNumSums + f];
-    }
-  }
-}
-
-// ============================================================================
-// backward recompute: logit gradient tile -> staged chunk (two layouts)
-// ============================================================================
 template <typename T>
 __device__ __forceinline__ void store4(T* dst, float a0, float a1, float a2, float a3);
 template <>
@@ -252,6 +79,355 @@ __device__ __forceinline__ void store1<float>(float* dst, float x) {
   *dst = x;
 }
 
+// ============================================================================
+// pass 1: per-tile softmax statistics
+// ============================================================================
+template <typename T, bool ARGMAX>
+__global__ __launch_bounds__(kThreads, 1) void k_stats(StatsLaunch a) {
+  using Cfg = TileCfg<T, 256, 256>;
+  __shared__ __attribute__((aligned(16))) char smem[Cfg::LDS_BYTES];
+  int tm, tn;
+  if (!tile_of(a.tiles_m, a.tiles_n, 4, tm, tn)) return;
+
+  f32x4_t acc[Cfg::FM][Cfg::FN];
+  zero_acc<Cfg>(acc);
+  tile_mainloop<T, Cfg>(acc, as_op<T>(a.A), tm * Cfg::BM, as_op<T>(a.B), tn * Cfg::BN, a.k_len,
+                        smem);
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int v_base = tm * Cfg::BM + wm * Cfg::WM;
+  const bool tail = tm * Cfg::BM + Cfg::BM > a.vocab;
+
+  float mj[Cfg::FN], sj[Cfg::FN];
+  int ij[Cfg::FN];
+#pragma unroll
+  for (int j = 0; j < Cfg::FN; ++j) {
+    float mx = -INFINITY;
+    int idx = 0x7fffffff;
+#pragma unroll
+    for (int i = 0; i < Cfg::FM; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int v = v_base + i * kFrag + frag_row(r, lane);
+        float x = acc[i][j][r];
+        if (tail && v >= a.vocab) x = -INFINITY;
+        if (ARGMAX) {
+          if (x > mx) { mx = x; idx = v; }  // strict: keeps the lowest index
+        } else {
+          mx = fmaxf(mx, x);
+        }
+      }
+    const float m = col_max(mx);
+    float s = 0.0f;
+    if (m != -INFINITY) {
+      const float mb = m * kLog2e;
+#pragma unroll
+      for (int i = 0; i < Cfg::FM; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int v = v_base + i * kFrag + frag_row(r, lane);
+          if (!tail || v < a.vocab) s += fast_exp2(fmaf(acc[i][j][r], kLog2e, -mb));
+        }
+    }
+    mj[j] = m;
+    sj[j] = col_sum(s, lane);
+    if (ARGMAX) {
+      // lowest index among the lanes that reach the column maximum
+      int cand = (mx == m) ? idx : 0x7fffffff;
+      cand = min(cand, __shfl_xor(cand, 16));
+      ij[j] = min(cand, __shfl_xor(cand, 32));
+    } else {
+      ij[j] = 0;
+    }
+  }
+
+  // the two wave rows (wm) share token columns: wm = 1 hands its values over
+  float* red = reinterpret_cast<float*>(smem);
+  if (wm == 1 && lane < kFrag) {
+#pragma unroll
+    for (int j = 0; j < Cfg::FN; ++j) {
+      const int c = wn * Cfg::WN + j * kFrag + lane;
+      red[c * 3 + 0] = mj[j];
+      red[c * 3 + 1] = sj[j];
+      red[c * 3 + 2] = __int_as_float(ij[j]);
+    }
+  }
+  __syncthreads();
+  if (wm == 0 && lane < kFrag) {
+#pragma unroll
+    for (int j = 0; j < Cfg::FN; ++j) {
+      const int c = wn * Cfg::WN + j * kFrag + lane;
+      float m = mj[j], s = sj[j];
+      int id = ij[j];
+      const float m2 = red[c * 3 + 0], s2 = red[c * 3 + 1];
+      const int i2 = __float_as_int(red[c * 3 + 2]);
+      if (ARGMAX) id = (m2 > m) ? i2 : ((m2 == m) ? min(id, i2) : id);
+      lse_merge(m, s, m2, s2);
+      const int col = tn * Cfg::BN + c;
+      if (col < a.ncols) {
+        const int64_t o = (int64_t)tm * a.ldp + col;
+        a.pm[o] = m;
+        a.ps[o] = s;
+        if (ARGMAX) a.pi[o] = id;
+      }
+    }
+  }
+}
+
+// ============================================================================
+// pass 1 with staging: the tile's column maxima are merged across the two
+// half-waves and the two wave rows first, then e = exp(z - m_tile) is both
+// summed and stored (rounded to the storage type) for the backward.
+template <typename T>
+__global__ __launch_bounds__(kThreads, 1) void k_stats_stage(StatsStageLaunch a) {
+  using Cfg = TileCfg<T, 256, 256>;
+  __shared__ __attribute__((aligned(16))) char smem[Cfg::LDS_BYTES];
+  const StatsLaunch& st = a.st;
+  int tm, tn;
+  if (!tile_of(st.tiles_m, st.tiles_n, 4, tm, tn)) return;
+
+  f32x4_t acc[Cfg::FM][Cfg::FN];
+  zero_acc<Cfg>(acc);
+  tile_mainloop<T, Cfg>(acc, as_op<T>(st.A), tm * Cfg::BM, as_op<T>(st.B), tn * Cfg::BN,
+                        st.k_len, smem);
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int v_base = tm * Cfg::BM + wm * Cfg::WM;
+  const bool tail = tm * Cfg::BM + Cfg::BM > st.vocab;
+  float* red = reinterpret_cast<float*>(smem);  // [2 wave rows][BN]
+
+  float mj[Cfg::FN];
+#pragma unroll
+  for (int j = 0; j < Cfg::FN; ++j) {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < Cfg::FM; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int v = v_base + i * kFrag + frag_row(r, lane);
+        if (!tail || v < st.vocab) mx = fmaxf(mx, acc[i][j][r]);
+      }
+    mj[j] = col_max(mx);
+    if (lane < kFrag) red[wm * Cfg::BN + wn * Cfg::WN + j * kFrag + lane] = mj[j];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < Cfg::FN; ++j) {
+    const int c = wn * Cfg::WN + j * kFrag + frag_col(lane);
+    mj[j] = fmaxf(red[c], red[Cfg::BN + c]);
+  }
+
+  T* E = static_cast<T*>(a.stage);
+  float sj[Cfg::FN];
+#pragma unroll
+  for (int j = 0; j < Cfg::FN; ++j) {
+    const int col = tn * Cfg::BN + wn * Cfg::WN + j * kFrag + frag_col(lane);  // chunk row
+    const float mb = mj[j] * kLog2e;
+    float s = 0.0f;
+#pragma unroll
+    for (int i = 0; i < Cfg::FM; ++i) {
+      float e[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int v = v_base + i * kFrag + frag_row(r, lane);
+        e[r] = (!tail || v < st.vocab) ? fast_exp2(fmaf(acc[i][j][r], kLog2e, -mb)) : 0.0f;
+        s += e[r];
+      }
+      const int v0 = v_base + i * kFrag + frag_row(0, lane);
+      store4<T>(E + (int64_t)col * a.ld_stage + v0, e[0], e[1], e[2], e[3]);
+    }
+    sj[j] = col_sum(s, lane);
+  }
+  __syncthreads();
+  if (lane < kFrag) {
+#pragma unroll
+    for (int j = 0; j < Cfg::FN; ++j)
+      red[wm * Cfg::BN + wn * Cfg::WN + j * kFrag + lane] = sj[j];
+  }
+  __syncthreads();
+  if (wm == 0 && lane < kFrag) {
+#pragma unroll
+    for (int j = 0; j < Cfg::FN; ++j) {
+      const int c = wn * Cfg::WN + j * kFrag + lane;
+      const int col = tn * Cfg::BN + c;
+      if (col < st.ncols) {
+        const int64_t o = (int64_t)tm * st.ldp + col;
+        st.pm[o] = mj[j];
+        st.ps[o] = red[c] + red[Cfg::BN + c];
+      }
+    }
+  }
+}
+
+// dz from the staged e, one workgroup per (256-wide vocabulary tile, 64 rows):
+// rows are read and written back coalesced (16 bytes per lane), and the
+// block is transposed through LDS into dz^T.
+template <typename T>
+__global__ __launch_bounds__(256) void k_dz_stage(DzStageLaunch a) {
+  constexpr int VT = kVocabTile, RB = 64;
+  constexpr int KC = ElemTraits<T>::kPerChunk;       // elements per 16 bytes
+  constexpr int CPR = VT / KC;                        // 16-byte chunks per row
+  constexpr int STRIDE = VT * (int)sizeof(T) + 16;    // LDS row stride (bytes), padded
+  __shared__ __attribute__((aligned(16))) char tile[RB * STRIDE];
+  const int vt = blockIdx.x % a.tiles_m;
+  const int rb = blockIdx.x / a.tiles_m;
+  T* dz = static_cast<T*>(a.dz);
+  T* dzt = static_cast<T*>(a.dzt);
+
+  for (int idx = threadIdx.x; idx < RB * CPR; idx += 256) {
+    const int rr = idx / CPR, ch = idx % CPR;
+    const int c = rb * RB + rr;                    // chunk row
+    const int v0 = vt * VT + ch * KC;
+    T* p = dz + (int64_t)c * a.ld_dz + v0;
+    const i32x4_t raw = *reinterpret_cast<const i32x4_t*>(p);
+    float e[KC];
+    if constexpr (sizeof(T) == 2) {
+      const bf16x8_t b = __builtin_bit_cast(bf16x8_t, raw);
+#pragma unroll
+      for (int q = 0; q < KC; ++q) e[q] = (float)b[q];
+    } else {
+#pragma unroll
+      for (int q = 0; q < KC; ++q) e[q] = __int_as_float(raw[q]);
+    }
+    float sd = 0.0f, scale = 0.0f;
+    int yl = -1, ya = -1;
+    if (c < a.ncols) {
+      const int64_t gr = a.r0 + c;
+      sd = a.seed[gr];
+      if (sd != 0.0f) {
+        scale = sd * (a.w_lab + a.w_arg) *
+                fast_exp2((a.pm[(int64_t)vt * a.ldp + c] - a.sv.lse_q[gr]) * kLog2e);
+        yl = a.sv.y_label[gr];
+        ya = a.sv.y_arg[gr];
+      }
+    }
+    float d[KC];
+#pragma unroll
+    for (int q = 0; q < KC; ++q) {
+      const int v = v0 + q;
+      float x = e[q] * scale;
+      if (v == yl) x -= sd * a.w_lab;
+      if (v == ya) x -= sd * a.w_arg;
+      d[q] = (sd != 0.0f && v < a.vocab) ? x : 0.0f;
+    }
+    i32x4_t out;
+    if constexpr (sizeof(T) == 2) {
+      bf16x8_t b;
+#pragma unroll
+      for (int q = 0; q < KC; ++q) b[q] = (__bf16)d[q];
+      out = __builtin_bit_cast(i32x4_t, b);
+    } else {
+#pragma unroll
+      for (int q = 0; q < KC; ++q) out[q] = __float_as_int(d[q]);
+    }
+    *reinterpret_cast<i32x4_t*>(p) = out;
+    *reinterpret_cast<i32x4_t*>(tile + rr * STRIDE + ch * 16) = out;
+  }
+  __syncthreads();
+  // dz^T rows: vocabulary entry v of this tile, 64 chunk rows = RB elements
+  constexpr int PER_ROW = RB / KC;  // 16-byte pieces per dz^T row segment
+  for (int idx = threadIdx.x; idx < VT * PER_ROW; idx += 256) {
+    const int v = idx / PER_ROW, q = idx % PER_ROW;
+    i32x4_t out;
+    if constexpr (sizeof(T) == 2) {
+      bf16x8_t b;
+#pragma unroll
+      for (int e = 0; e < KC; ++e)
+        b[e] = *reinterpret_cast<const __bf16*>(tile + (q * KC + e) * STRIDE + v * 2);
+      out = __builtin_bit_cast(i32x4_t, b);
+    } else {
+#pragma unroll
+      for (int e = 0; e < KC; ++e)
+        out[e] = *reinterpret_cast<const int*>(tile + (q * KC + e) * STRIDE + v * 4);
+    }
+    *reinterpret_cast<i32x4_t*>(dzt + (int64_t)(vt * VT + v) * a.ld_dzt + rb * RB + q * KC) = out;
+  }
+}
+
+// ============================================================================
+// pass 2: divergence sums with the final logsumexps
+// ============================================================================
+template <typename T>
+__global__ __launch_bounds__(kThreads, 1) void k_div(DivLaunch a) {
+  using Cfg = TileCfg<T, 256, 128>;
+  __shared__ __attribute__((aligned(16))) char smem[Cfg::LDS_BYTES];
+  int tm, tn;
+  if (!tile_of(a.tiles_m, a.tiles_n, 4, tm, tn)) return;
+
+  f32x4_t az[Cfg::FM][Cfg::FN], au[Cfg::FM][Cfg::FN];
+  zero_acc<Cfg>(az);
+  zero_acc<Cfg>(au);
+  tile_mainloop<T, Cfg>(az, as_op<T>(a.Az), tm * Cfg::BM, as_op<T>(a.Bz), tn * Cfg::BN, a.k_len,
+                        smem);
+  tile_mainloop<T, Cfg>(au, as_op<T>(a.Au), tm * Cfg::BM, as_op<T>(a.Bu), tn * Cfg::BN, a.k_len,
+                        smem);
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int v_base = tm * Cfg::BM + wm * Cfg::WM;
+  const bool tail = tm * Cfg::BM + Cfg::BM > a.vocab;
+  const uint32_t need = a.need;
+
+  float sums[Cfg::FN][kNumSums];
+#pragma unroll
+  for (int j = 0; j < Cfg::FN; ++j) {
+    const int col = min(tn * Cfg::BN + wn * Cfg::WN + j * kFrag + frag_col(lane), a.ncols - 1);
+    const float lq0 = a.lse_q[col], lp0 = a.lse_p[col];
+    float s_alpha = 0.f, s_s = 0.f, s_kl = 0.f, s_rkl = 0.f, s_jsd = 0.f, s_eqg = 0.f;
+#pragma unroll
+    for (int i = 0; i < Cfg::FM; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int v = v_base + i * kFrag + frag_row(r, lane);
+        if (tail && v >= a.vocab) continue;
+        const float lq = az[i][j][r] - lq0;
+        const float lp = au[i][j][r] - lp0;
+        const float q = fast_exp2(lq * kLog2e);
+        const float p = fast_exp2(lp * kLog2e);
+        if (need & SUM_ALPHA) s_alpha += fminf(p, q);
+        if (need & SUM_S) s_s += (q < p) ? q : ((q == p) ? 0.5f * q : 0.0f);
+        if (need & SUM_KL) s_kl += p * (lp - lq);
+        if (need & SUM_RKL) s_rkl += q * (lq - lp);
+        if (need & (SUM_JSD | SUM_EQG)) {
+          const float lm = fast_log2(0.5f * (p + q)) * kLn2;
+          if (need & SUM_JSD) s_jsd += 0.5f * (p * (lp - lm) + q * (lq - lm));
+          if (need & SUM_EQG) s_eqg += 0.5f * q * (lq - lm);
+        }
+      }
+    const float v6[kNumSums] = {s_alpha, s_s, s_kl, s_rkl, s_jsd, s_eqg};
+#pragma unroll
+    for (int f = 0; f < kNumSums; ++f) sums[j][f] = col_sum(v6[f], lane);
+  }
+
+  float* red = reinterpret_cast<float*>(smem);  // [BN][kNumSums]
+  if (wm == 1 && lane < kFrag) {
+#pragma unroll
+    for (int j = 0; j < Cfg::FN; ++j) {
+      const int c = wn * Cfg::WN + j * kFrag + lane;
+#pragma unroll
+      for (int f = 0; f < kNumSums; ++f) red[c * kNumSums + f] = sums[j][f];
+    }
+  }
+  __syncthreads();
+  if (wm == 0 && lane < kFrag) {
+#pragma unroll
+    for (int j = 0; j < Cfg::FN; ++j) {
+      const int c = wn * Cfg::WN + j * kFrag + lane;
+      const int col = tn * Cfg::BN + c;
+      if (col >= a.ncols) continue;
+#pragma unroll
+      for (int f = 0; f < kNumSums; ++f)
+        if (need & (1u << f))
+          a.part[f * a.part_stride + (int64_t)tm * a.ldp + col] = sums[j][f] + red[c * kNumSums + f];
+    }
+  }
+}
+
+// ============================================================================
+// backward recompute: logit gradient tile -> staged chunk (two layouts)
+// ============================================================================
 struct RowCoef {
   float seed, lse_q, lse_p, alpha, S, rkl, eqg, lam;
   int y_lab, y_arg;
@@ -292,8 +468,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_dz(DzLaunch a) {
   int tm, tn;
   if (!tile_of(a.tiles_m, a.tiles_n, 4, tm, tn)) return;
 
-  f32x16_t az[Cfg::FM][Cfg::FN];
-  f32x16_t au[DUAL ? Cfg::FM : 1][DUAL ? Cfg::FN : 1];
+  f32x4_t az[Cfg::FM][Cfg::FN];
+  f32x4_t au[DUAL ? Cfg::FM : 1][DUAL ? Cfg::FN : 1];
   zero_acc<Cfg>(az);
   tile_mainloop<T, Cfg>(az, as_op<T>(a.Az), tm * Cfg::BM, as_op<T>(a.Bz), tn * Cfg::BN, a.k_len,
                         smem);
@@ -311,7 +487,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_dz(DzLaunch a) {
 
 #pragma unroll
   for (int j = 0; j < Cfg::FN; ++j) {
-    const int c = tn * Cfg::BN + wn * Cfg::WN + j * 32 + (lane & 31);  // chunk row
+    const int c = tn * Cfg::BN + wn * Cfg::WN + j * kFrag + frag_col(lane);  // chunk row
     const int64_t gr = a.r0 + min(c, a.ncols - 1);
     RowCoef rc;
     rc.seed = (c < a.ncols) ? a.seed[gr] : 0.0f;
@@ -328,60 +504,58 @@ __global__ __launch_bounds__(kThreads, 1) void k_dz(DzLaunch a) {
     }
     const bool live = rc.seed != 0.0f;
 #pragma unroll
-    for (int i = 0; i < Cfg::FM; ++i)
+    for (int i = 0; i < Cfg::FM; ++i) {
+      float o[4];
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        float o[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = g4 * 4 + e;
-          const int v = v_base + i * 32 + frag_row(r, lane);
-          float d = 0.0f;
-          if (live && v < a.vocab) {
-            const float u = DUAL ? au[DUAL ? i : 0][DUAL ? j : 0][r] : 0.0f;
-            d = rc.seed * dz_elem<DUAL>(rc, a.w, az[i][j][r], u, v);
-          }
-          o[e] = d;
+      for (int r = 0; r < 4; ++r) {
+        const int v = v_base + i * kFrag + frag_row(r, lane);
+        float d = 0.0f;
+        if (live && v < a.vocab) {
+          const float u = DUAL ? au[DUAL ? i : 0][DUAL ? j : 0][r] : 0.0f;
+          d = rc.seed * dz_elem<DUAL>(rc, a.w, az[i][j][r], u, v);
         }
-        const int v0 = v_base + i * 32 + frag_row(g4 * 4, lane);
-        store4<T>(dz + (int64_t)c * a.ld_dz + v0, o[0], o[1], o[2], o[3]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) store1<T>(dzt + (int64_t)(v0 + e) * a.ld_dzt + c, o[e]);
+        o[r] = d;
       }
+      const int v0 = v_base + i * kFrag + frag_row(0, lane);
+      store4<T>(dz + (int64_t)c * a.ld_dz + v0, o[0], o[1], o[2], o[3]);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) store1<T>(dzt + (int64_t)(v0 + r) * a.ld_dzt + c, o[r]);
+    }
   }
 }
 
 // ============================================================================
 // plain contraction with store / accumulate epilogue
 // ============================================================================
-template <typename T, typename OutT>
+// ROLE only separates the two backward contractions in profiles (0: dh, 1: dW).
+template <typename T, typename OutT, int ROLE>
 __global__ __launch_bounds__(kThreads, 1) void k_gemm(GemmLaunch a) {
   using Cfg = TileCfg<T, 256, 256>;
   __shared__ __attribute__((aligned(16))) char smem[Cfg::LDS_BYTES];
   int tm, tn;
   if (!tile_of(a.tiles_m, a.tiles_n, 4, tm, tn)) return;
-  f32x16_t acc[Cfg::FM][Cfg::FN];
+  f32x4_t acc[Cfg::FM][Cfg::FN];
   zero_acc<Cfg>(acc);
   tile_mainloop<T, Cfg>(acc, as_op<T>(a.A), tm * Cfg::BM, as_op<T>(a.B), tn * Cfg::BN, a.k_len,
                         smem);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   OutT* C = static_cast<OutT*>(a.C);
-  // Two fragments at a time: all their old values are loaded first (32 loads
-  // in flight), then added and stored.
-  constexpr int FB = 2;
+  // Four fragments at a time: all their old values are loaded first (16
+  // loads in flight), then added and stored.
+  constexpr int FB = 4;
 #pragma unroll
   for (int j = 0; j < Cfg::FN; ++j) {
-    const int col = tn * Cfg::BN + wn * Cfg::WN + j * 32 + (lane & 31);
+    const int col = tn * Cfg::BN + wn * Cfg::WN + j * kFrag + frag_col(lane);
     const bool col_ok = col < a.n_valid;
 #pragma unroll
     for (int i0 = 0; i0 < Cfg::FM; i0 += FB) {
-      float old[FB][16];
+      float old[FB][4];
 #pragma unroll
       for (int ii = 0; ii < FB; ++ii)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = tm * Cfg::BM + wm * Cfg::WM + (i0 + ii) * 32 + frag_row(r, lane);
+        for (int r = 0; r < 4; ++r) {
+          const int row = tm * Cfg::BM + wm * Cfg::WM + (i0 + ii) * kFrag + frag_row(r, lane);
           old[ii][r] = 0.0f;
           if (a.accumulate && col_ok && row < a.m_valid) {
             const OutT* p = C + (int64_t)row * a.ldc + col;
@@ -392,8 +566,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(GemmLaunch a) {
 #pragma unroll
       for (int ii = 0; ii < FB; ++ii)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = tm * Cfg::BM + wm * Cfg::WM + (i0 + ii) * 32 + frag_row(r, lane);
+        for (int r = 0; r < 4; ++r) {
+          const int row = tm * Cfg::BM + wm * Cfg::WM + (i0 + ii) * kFrag + frag_row(r, lane);
           if (!col_ok || row >= a.m_valid) continue;
           OutT* p = C + (int64_t)row * a.ldc + col;
           const float x = acc[i0 + ii][j][r] + old[ii][r];
@@ -489,34 +663,67 @@ __global__ __launch_bounds__(256) void k_rowdot(RowdotLaunch a) {
   }
 }
 
-__global__ __launch_bounds__(256) void k_combine1(Combine1Launch a) {
-  const int c = blockIdx.x * 256 + threadIdx.x;
-  if (c >= a.ncols) return;
-  {
-    float m = -INFINITY;
-    for (int t = 0; t < a.tiles_m; ++t) m = fmaxf(m, a.pm_z[(int64_t)t * a.ldp + c]);
-    float s = 0.0f;
-    for (int t = 0; t < a.tiles_m; ++t) {
-      const int64_t o = (int64_t)t * a.ldp + c;
-      s += a.ps_z[o] * expf(a.pm_z[o] - m);
-    }
-    a.lse_q[c] = m + logf(s);
+// One workgroup per 32 rows; the 8 threads of a row each merge a contiguous
+// segment of vocabulary tiles (max pass, then sum pass), then the segments
+// are merged in order.  The argmax keeps the first tile holding the maximum,
+// i.e. the lowest vocabulary index.
+__device__ __forceinline__ void seg_lse(const float* pm, const float* ps, int64_t ldp, int c,
+                                        int t0, int t1, float& m, float& s, int& best) {
+  m = -INFINITY;
+  best = -1;
+  for (int t = t0; t < t1; ++t) {
+    const float x = pm[(int64_t)t * ldp + c];
+    if (x > m) { m = x; best = t; }
   }
-  if (a.pm_u) {
+  s = 0.0f;
+  if (m != -INFINITY)
+    for (int t = t0; t < t1; ++t) {
+      const int64_t o = (int64_t)t * ldp + c;
+      s += ps[o] * fast_exp2((pm[o] - m) * kLog2e);
+    }
+}
+
+__global__ __launch_bounds__(256) void k_combine1(Combine1Launch a) {
+  constexpr int SEG = 8, RPB = 32;
+  __shared__ float sm[2][SEG][RPB], ss[2][SEG][RPB];
+  __shared__ int sb[SEG][RPB];
+  const int rr = threadIdx.x % RPB, seg = threadIdx.x / RPB;
+  const int c = blockIdx.x * RPB + rr;
+  const int per = (a.tiles_m + SEG - 1) / SEG;
+  const int t0 = min(a.tiles_m, seg * per), t1 = min(a.tiles_m, t0 + per);
+  if (c < a.ncols) {
+    float m, s;
+    int best;
+    seg_lse(a.pm_z, a.ps_z, a.ldp, c, t0, t1, m, s, best);
+    sm[0][seg][rr] = m;
+    ss[0][seg][rr] = s;
+    if (a.pm_u) {
+      seg_lse(a.pm_u, a.ps_u, a.ldp, c, t0, t1, m, s, best);
+      sm[1][seg][rr] = m;
+      ss[1][seg][rr] = s;
+      sb[seg][rr] = best;
+    }
+  }
+  __syncthreads();
+  if (seg != 0 || c >= a.ncols) return;
+  for (int side = 0; side < (a.pm_u ? 2 : 1); ++side) {
     float m = -INFINITY;
-    int best = 0;
-    for (int t = 0; t < a.tiles_m; ++t) {
-      const float x = a.pm_u[(int64_t)t * a.ldp + c];
-      if (x > m) { m = x; best = t; }  // first tile holding the max: lowest index
-    }
+    int bseg = 0;
+    for (int q = 0; q < SEG; ++q)
+      if (sm[side][q][rr] > m) { m = sm[side][q][rr]; bseg = q; }
     float s = 0.0f;
-    for (int t = 0; t < a.tiles_m; ++t) {
-      const int64_t o = (int64_t)t * a.ldp + c;
-      s += a.ps_u[o] * expf(a.pm_u[o] - m);
+    for (int q = 0; q < SEG; ++q)
+      if (sm[side][q][rr] != -INFINITY) s += ss[side][q][rr] * fast_exp2((sm[side][q][rr] - m) * kLog2e);
+    const float lse = m + logf(s);
+    if (side == 0) {
+      a.lse_q[c] = lse;
+    } else {
+      a.lse_p[c] = lse;
+      const int bt = sb[bseg][rr];  // -1 only when no tile has a finite maximum
+      a.y_arg[c] = bt >= 0 ? a.pi_u[(int64_t)bt * a.ldp + c] : -1;
     }
-    a.lse_p[c] = m + logf(s);
-    a.y_arg[c] = a.pi_u[(int64_t)best * a.ldp + c];
-  } else {
+  }
+  if (!a.pm_u) {
     a.lse_p[c] = 0.0f;
     a.y_arg[c] = -1;
   }
@@ -654,6 +861,20 @@ hipError_t launch_stats(bool bf16, bool argmax, const StatsLaunch& a, hipStream_
   return hipGetLastError();
 }
 
+hipError_t launch_stats_stage(bool bf16, const StatsStageLaunch& a, hipStream_t s) {
+  const dim3 grid(grid_for_tiles(a.st.tiles_m * a.st.tiles_n)), block(kThreads);
+  if (bf16) hipLaunchKernelGGL(k_stats_stage<bf16_bits>, grid, block, 0, s, a);
+  else hipLaunchKernelGGL(k_stats_stage<float>, grid, block, 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_dz_stage(bool bf16, const DzStageLaunch& a, hipStream_t s) {
+  const dim3 grid((unsigned)(a.tiles_m * a.row_blocks)), block(256);
+  if (bf16) hipLaunchKernelGGL(k_dz_stage<bf16_bits>, grid, block, 0, s, a);
+  else hipLaunchKernelGGL(k_dz_stage<float>, grid, block, 0, s, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_div(bool bf16, const DivLaunch& a, hipStream_t s) {
   const dim3 grid(grid_for_tiles(a.tiles_m * a.tiles_n)), block(kThreads);
   if (bf16) hipLaunchKernelGGL(k_div<bf16_bits>, grid, block, 0, s, a);
@@ -673,15 +894,21 @@ hipError_t launch_dz(bool bf16, bool dual, const DzLaunch& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_gemm(bool bf16, const GemmLaunch& a, hipStream_t s) {
+template <int ROLE>
+static void launch_gemm_role(bool bf16, const GemmLaunch& a, hipStream_t s) {
   const dim3 grid(grid_for_tiles(a.tiles_m * a.tiles_n)), block(kThreads);
   if (bf16) {
-    if (a.out_bf16) hipLaunchKernelGGL((k_gemm<bf16_bits, bf16_bits>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((k_gemm<bf16_bits, float>), grid, block, 0, s, a);
+    if (a.out_bf16) hipLaunchKernelGGL((k_gemm<bf16_bits, bf16_bits, ROLE>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((k_gemm<bf16_bits, float, ROLE>), grid, block, 0, s, a);
   } else {
-    if (a.out_bf16) hipLaunchKernelGGL((k_gemm<float, bf16_bits>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((k_gemm<float, float>), grid, block, 0, s, a);
+    if (a.out_bf16) hipLaunchKernelGGL((k_gemm<float, bf16_bits, ROLE>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((k_gemm<float, float, ROLE>), grid, block, 0, s, a);
   }
+}
+
+hipError_t launch_gemm(bool bf16, const GemmLaunch& a, hipStream_t s) {
+  if (a.role == 0) launch_gemm_role<0>(bf16, a, s);
+  else launch_gemm_role<1>(bf16, a, s);
   return hipGetLastError();
 }
 
@@ -698,7 +925,7 @@ hipError_t launch_rowdot(bool bf16, const RowdotLaunch& a, hipStream_t s) {
 }
 
 hipError_t launch_combine1(const Combine1Launch& a, hipStream_t s) {
-  hipLaunchKernelGGL(k_combine1, dim3((a.ncols + 255) / 256), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(k_combine1, dim3((a.ncols + 31) / 32), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -52,6 +52,33 @@ struct StatsLaunch {
 };
 hipError_t launch_stats(bool bf16, bool argmax, const StatsLaunch& a, hipStream_t s);
 
+// pass 1 for the single-call forward+backward: also stores
+// e = exp(z - m_tile) of every (row, vocab) into `stage` ([cap][Vp], row-major)
+struct StatsStageLaunch {
+  StatsLaunch st;
+  void* stage;
+  int64_t ld_stage;
+};
+hipError_t launch_stats_stage(bool bf16, const StatsStageLaunch& a, hipStream_t s);
+
+// logit gradient of the label / argmax cross-entropies from the staged e:
+// dz = seed * ((w_lab + w_arg) e exp(m_tile - lse) - w_lab [v == y_lab] - w_arg [v == y_arg]),
+// written over e and, transposed, into dzt ([Vp][cap])
+struct DzStageLaunch {
+  int32_t tiles_m, ncols, vocab, ldp;
+  int64_t r0;
+  const float* pm;     // chunk partial maxima [tiles_m][ldp]
+  const float* seed;   // [N], global rows
+  SavedView sv;        // global rows
+  float w_lab, w_arg;
+  void* dz;            // in: e, out: dz; [cap][Vp]
+  int64_t ld_dz;
+  void* dzt;           // [Vp][cap]
+  int64_t ld_dzt;
+  int32_t row_blocks;  // 64-row blocks covered (multiple of the 256-row tiles)
+};
+hipError_t launch_dz_stage(bool bf16, const DzStageLaunch& a, hipStream_t s);
+
 struct DivLaunch {
   GemmOperand Az, Bz, Au, Bu;
   int32_t k_len, vocab, tiles_m, tiles_n, ncols, ldp;
@@ -86,6 +113,7 @@ struct GemmLaunch {
   int64_t ldc;
   int accumulate;
   int out_bf16;
+  int role;  // 0: dh, 1: dW (separate kernel names in profiles)
 };
 hipError_t launch_gemm(bool bf16, const GemmLaunch& a, hipStream_t s);
 

@@ -8,8 +8,10 @@
 //
 // gfx950 mapping:
 //  * 256 threads = 4 wave64s in a 2 x 2 grid; a wave owns a (BM/2) x (BN/2)
-//    sub-tile made of 32 x 32 MFMA fragments (v_mfma_f32_32x32x16_bf16 for
-//    bf16, v_mfma_f32_32x32x2_f32 for fp32), fp32 accumulators.
+//    sub-tile made of 16 x 16 MFMA fragments (v_mfma_f32_16x16x32_bf16 for
+//    bf16, v_mfma_f32_16x16x4_f32 for fp32), fp32 accumulators.  The 16x16
+//    shape moves half the accumulator traffic per flop of the 32x32 one,
+//    which measures faster on this power-limited part.
 //  * K advances in slabs of 128 bytes per row (64 bf16 / 32 fp32).  A slab of
 //    A and B sits in LDS as rows of eight 16-byte chunks, chunk c of row r
 //    stored at position c ^ (r & 7): eight consecutive rows read at the same
@@ -52,13 +54,16 @@ struct ElemTraits<float> {
   static constexpr int kPerChunk = 4;
 };
 
+constexpr int kFrag = 16;   // MFMA output fragment: 16 x 16
+constexpr int kSteps = 2;   // k-steps per slab (4 chunks of 16 bytes per step)
+
 template <typename T, int BM_, int BN_>
 struct TileCfg {
   static constexpr int BM = BM_, BN = BN_;
   static constexpr int KC = ElemTraits<T>::kPerChunk;  // elements per 16-byte chunk
   static constexpr int BK = 8 * KC;                    // elements per slab row (128 bytes)
   static constexpr int WM = BM / 2, WN = BN / 2;       // wave sub-tile
-  static constexpr int FM = WM / 32, FN = WN / 32;     // 32x32 fragments per wave
+  static constexpr int FM = WM / kFrag, FN = WN / kFrag;  // 16x16 fragments per wave
   static constexpr int STAGE = (BM + BN) * kRowBytes;  // bytes of one LDS stage
   static constexpr int LDS_BYTES = 2 * STAGE;
 };
@@ -88,31 +93,32 @@ __device__ __forceinline__ const T* row_ptr(const Operand<T>& op, int32_t r) {
   return op.base + (int64_t)src * op.ld;
 }
 
-// Accumulator fragment element -> tile coordinates (32x32 MFMA output layout):
-// register r of lane l holds row (r/4)*8 + (l/32)*4 + r%4 and column l%32.
-__device__ __forceinline__ int frag_row(int r, int lane) {
-  return ((r >> 2) << 3) + ((lane >> 5) << 2) + (r & 3);
-}
+// Accumulator fragment element -> tile coordinates (16x16 MFMA output layout):
+// register r of lane l holds row 4*(l/16) + r and column l%16, so the four
+// lanes l%16 == c share column c and each holds four consecutive rows.
+__device__ __forceinline__ int frag_row(int r, int lane) { return ((lane >> 4) << 2) + r; }
+__device__ __forceinline__ int frag_col(int lane) { return lane & 15; }
 
 template <typename T>
-__device__ __forceinline__ void mfma_slab_step(f32x16_t& acc, const i32x4_t& a, const i32x4_t& b);
+__device__ __forceinline__ void mfma_slab_step(f32x4_t& acc, const i32x4_t& a, const i32x4_t& b);
 
+// bf16: lane l holds 8 consecutive k of row l%16 (k group l/16)
 template <>
-__device__ __forceinline__ void mfma_slab_step<bf16_bits>(f32x16_t& acc, const i32x4_t& a,
+__device__ __forceinline__ void mfma_slab_step<bf16_bits>(f32x4_t& acc, const i32x4_t& a,
                                                           const i32x4_t& b) {
-  acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                 __builtin_bit_cast(bf16x8_t, b), acc, 0, 0, 0);
 }
 
 // fp32: each lane holds four consecutive k of its row; instruction e pairs
-// element e of the low and high half-waves.  A and B use the same k
-// assignment, so the four instructions together sum over all eight k.
+// element e of the four lane groups.  A and B use the same k assignment, so
+// the four instructions together sum over all sixteen k of the step.
 template <>
-__device__ __forceinline__ void mfma_slab_step<float>(f32x16_t& acc, const i32x4_t& a,
+__device__ __forceinline__ void mfma_slab_step<float>(f32x4_t& acc, const i32x4_t& a,
                                                       const i32x4_t& b) {
 #pragma unroll
   for (int e = 0; e < 4; ++e)
-    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__int_as_float(a[e]), __int_as_float(b[e]), acc,
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__int_as_float(a[e]), __int_as_float(b[e]), acc,
                                                0, 0, 0);
 }
 
@@ -178,29 +184,29 @@ template <typename Cfg>
 __device__ __forceinline__ void read_frags(const char* sa, const char* sb, int s, int lane,
                                            int wm, int wn, i32x4_t (&af)[Cfg::FM],
                                            i32x4_t (&bf)[Cfg::FN]) {
-  const int frow = lane & 31;
-  const int chunk = 2 * s + (lane >> 5);
+  const int frow = lane & 15;
+  const int chunk = 4 * s + (lane >> 4);
 #pragma unroll
   for (int i = 0; i < Cfg::FM; ++i) {
-    const int r = wm * Cfg::WM + i * 32 + frow;
+    const int r = wm * Cfg::WM + i * kFrag + frow;
     af[i] = *reinterpret_cast<const i32x4_t*>(sa + r * kRowBytes + ((chunk ^ (r & 7)) << 4));
   }
 #pragma unroll
   for (int j = 0; j < Cfg::FN; ++j) {
-    const int r = wn * Cfg::WN + j * 32 + frow;
+    const int r = wn * Cfg::WN + j * kFrag + frow;
     bf[j] = *reinterpret_cast<const i32x4_t*>(sb + r * kRowBytes + ((chunk ^ (r & 7)) << 4));
   }
 }
 
-// One slab = four k-steps of MFMAs.  Step 0 issues the second half of slab
-// k+1's loads (unless FIRST: the prologue loaded all of it); steps 0-2 read
-// the next step's fragments; step 3 (unless LAST) waits for slab k+1, meets
-// the other waves at the barrier (all of them now hold step 3's fragments,
-// so this stage is free), issues the first half of slab k+2 into it and
-// reads slab k+1's step-0 fragments.  Inside a step, fragment reads and
+// One slab = two k-steps of MFMAs.  Step 0 issues the second half of slab
+// k+1's loads (unless FIRST: the prologue loaded all of it) and reads step
+// 1's fragments; step 1 (unless LAST) waits for slab k+1, meets the other
+// waves at the barrier (all of them now hold step 1's fragments, so this
+// stage is free), issues the first half of slab k+2 into it and reads slab
+// k+1's step-0 fragments.  Inside a step, fragment reads and
 // loads are interleaved with the MFMAs so they land while the rest run.
 template <typename T, typename Cfg, int PER_WAVE, bool FIRST, bool LAST>
-__device__ __forceinline__ void slab_steps(f32x16_t (&acc)[Cfg::FM][Cfg::FN],
+__device__ __forceinline__ void slab_steps(f32x4_t (&acc)[Cfg::FM][Cfg::FN],
                                            i32x4_t (&fa)[2][Cfg::FM], i32x4_t (&fb)[2][Cfg::FN],
                                            char* smem, int stage, int lane, int wm, int wn,
                                            const SlabLoads<PER_WAVE>& L, int64_t next_kbytes,
@@ -208,14 +214,14 @@ __device__ __forceinline__ void slab_steps(f32x16_t (&acc)[Cfg::FM][Cfg::FN],
   constexpr int kR = Cfg::FM + Cfg::FN;
   constexpr int kH = PER_WAVE / 2;
   constexpr int kSlots = Cfg::FM * Cfg::FN - kR;  // MFMA slots left after the reads
-  constexpr int kPerSlot = (kH + kSlots - 1) / kSlots;
+  constexpr int kPerSlot = (PER_WAVE + kSlots - 1) / kSlots;
   const char* sa = smem + stage * Cfg::STAGE;
   const char* sb = sa + Cfg::BM * kRowBytes;
 #pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    const bool loads = (s == 0 && !FIRST) || (s == 3 && !LAST);
+  for (int s = 0; s < kSteps; ++s) {
+    const bool loads = (s == 0 && !FIRST) || (s == kSteps - 1 && !LAST);
     if (s == 0 && !FIRST) issue_groups<PER_WAVE, kH, PER_WAVE, Cfg>(L, stage ^ 1, pend_kbytes);
-    if (s < 3) {
+    if (s < kSteps - 1) {
       read_frags<Cfg>(sa, sb, s + 1, lane, wm, wn, fa[(s + 1) & 1], fb[(s + 1) & 1]);
     } else if (!LAST) {
       wait_vmem();
@@ -228,7 +234,7 @@ __device__ __forceinline__ void slab_steps(f32x16_t (&acc)[Cfg::FM][Cfg::FN],
     for (int i = 0; i < Cfg::FM; ++i)
 #pragma unroll
       for (int j = 0; j < Cfg::FN; ++j) mfma_slab_step<T>(acc[i][j], fa[s & 1][i], fb[s & 1][j]);
-    if (s < 3 || !LAST) {
+    if (s < kSteps - 1 || !LAST) {
 #pragma unroll
       for (int q = 0; q < kR; ++q) {
         __builtin_amdgcn_sched_group_barrier(0x008, kMfmaPerPair<T>, 0);  // MFMA
@@ -257,7 +263,7 @@ __device__ __forceinline__ void slab_steps(f32x16_t (&acc)[Cfg::FM][Cfg::FN],
 // lane i landing at byte 16 i; lane i therefore fetches logical chunk
 // (i % 8) ^ (row % 8) of row i / 8, which realises the XOR swizzle.
 template <typename T, typename Cfg>
-__device__ __forceinline__ void tile_mainloop(f32x16_t (&acc)[Cfg::FM][Cfg::FN],
+__device__ __forceinline__ void tile_mainloop(f32x4_t (&acc)[Cfg::FM][Cfg::FN],
                                               const Operand<T>& A, int32_t a_row0,
                                               const Operand<T>& B, int32_t b_row0, int32_t k_len,
                                               char* smem) {
@@ -312,13 +318,13 @@ __device__ __forceinline__ void tile_mainloop(f32x16_t (&acc)[Cfg::FM][Cfg::FN],
 }
 
 template <typename Cfg>
-__device__ __forceinline__ void zero_acc(f32x16_t (&acc)[Cfg::FM][Cfg::FN]) {
+__device__ __forceinline__ void zero_acc(f32x4_t (&acc)[Cfg::FM][Cfg::FN]) {
 #pragma unroll
   for (int i = 0; i < Cfg::FM; ++i)
 #pragma unroll
     for (int j = 0; j < Cfg::FN; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+      for (int r = 0; r < 4; ++r) acc[i][j][r] = 0.0f;
 }
 
 // Workgroup -> tile.  Workgroups are dealt to the 8 XCDs round-robin

@@ -55,6 +55,22 @@ class LossRun:
                           self.workspace, dhidden, dW, accumulate_dW, stream)
         return dhidden, dW
 
+    def forward_backward(self, grad_loss: Optional[torch.Tensor] = None,
+                         grad_mean: Optional[torch.Tensor] = None,
+                         dhidden: Optional[torch.Tensor] = None, dW: Optional[torch.Tensor] = None,
+                         accumulate_dW: bool = False, want_dh: bool = True, want_dW: bool = True,
+                         stream=None):
+        """Single call: forward outputs plus the gradients for the given seed."""
+        h, W = self.inputs["hidden"], self.inputs["W"]
+        if dhidden is None and want_dh:
+            dhidden = torch.empty(h.shape, dtype=torch.float32, device=h.device)
+        if dW is None and want_dW:
+            dW = torch.empty(W.shape, dtype=torch.float32, device=W.device)
+        B.lmhead_loss_fwd_bwd(self.problem, self.workspace, self.loss, self.term, self.lse_q,
+                              self.saved, self.counts, self.reduced, grad_loss, grad_mean,
+                              dhidden, dW, accumulate_dW, stream)
+        return dhidden, dW
+
     def saved_field(self, i: int, dtype=torch.float32) -> torch.Tensor:
         """View of saved field i (see SavedView in csrc/launch.hpp) as an N-vector."""
         stride = ((self.n_rows * 4 + 255) // 256) * 256

@@ -70,13 +70,20 @@ def check_argmax(gpu_y: np.ndarray, prob, rows, valid) -> None:
     assert np.array_equal(gpu_y[decisive], ref[decisive])
 
 
-def full_parity(prob, *, max_chunk_rows=0, check_grads=True, tag=""):
-    """Run fwd (+bwd with the mean seed) on the GPU and compare every output with the oracle."""
+def full_parity(prob, *, max_chunk_rows=0, check_grads=True, tag="", single_call=False):
+    """Run fwd (+bwd with the mean seed) on the GPU and compare every output with the oracle.
+
+    single_call: use lmhead_loss_fwd_bwd instead of the two calls.
+    """
     say(f"[parity] {tag} {prob.name} N={prob.n_rows} H={prob.hidden_dim} V={prob.vocab} "
-        f"dtype={prob.dtype} weights={prob.weights} chunk={max_chunk_rows}")
+        f"dtype={prob.dtype} weights={prob.weights} chunk={max_chunk_rows} single={single_call}")
     dev = to_device(prob)
     run = make_run(prob, dev, max_chunk_rows=max_chunk_rows)
-    run.forward()
+    gm = torch.ones(1, dtype=torch.float32, device="cuda")
+    if single_call:
+        dh_t, dW_t = run.forward_backward(grad_mean=gm)
+    else:
+        run.forward()
     torch.cuda.synchronize()
     ref = O.forward(prob)
     mean, term_means, n_valid = O.mean_loss(prob)
@@ -101,9 +108,11 @@ def full_parity(prob, *, max_chunk_rows=0, check_grads=True, tag=""):
         y = run.saved_field(3, torch.int32).cpu().numpy()
         check_argmax(y, prob, np.arange(prob.n_rows), ref.valid)
     out = dict(run=run, ref=ref, loss=loss)
-    if check_grads:
-        gm = torch.ones(1, dtype=torch.float32, device="cuda")
-        dh, dW = run.backward(grad_mean=gm)
+    if check_grads or single_call:
+        if single_call:
+            dh, dW = dh_t, dW_t
+        else:
+            dh, dW = run.backward(grad_mean=gm)
         torch.cuda.synchronize()
         rdh, rdW = O.backward(prob)
         dh_np, dW_np = dh.cpu().numpy(), dW.cpu().numpy()

@@ -46,15 +46,21 @@ def _sample_rows(n, seed):
     return np.array(sorted(rows), dtype=np.int64)
 
 
-@pytest.mark.parametrize("name", ["ce_bf16_1b", "ce_bf16_8b", "lk_hybrid_bf16_8b",
-                                  "multihead_bf16_405b"])
-def test_full_size_sampled(name):
+@pytest.mark.parametrize("name,single", [("ce_bf16_1b", False), ("ce_bf16_8b", False),
+                                         ("lk_hybrid_bf16_8b", False),
+                                         ("multihead_bf16_405b", False),
+                                         ("ce_bf16_1b", True), ("ce_bf16_8b", True)])
+def test_full_size_sampled(name, single):
+    """single: the same checks through the single call lmhead_loss_fwd_bwd."""
     prob = synthetic.make_problem(name)
     N, H, V = prob.n_rows, prob.hidden_dim, prob.vocab
-    say(f"[fullsize] {name} N={N} H={H} V={V} weights={prob.weights}")
+    say(f"[fullsize] {name} N={N} H={H} V={V} weights={prob.weights} single={single}")
     dev = to_device(prob)
     run = make_run(prob, dev, max_chunk_rows=CHUNK)
-    run.forward()
+    if single:
+        dh, dW = run.forward_backward(grad_mean=torch.ones(1, device="cuda"))
+    else:
+        run.forward()
     torch.cuda.synchronize()
     op = O.OracleProblem.of(prob)
     valid, bad = O.row_validity(op)
@@ -88,7 +94,8 @@ def test_full_size_sampled(name):
 
     # backward with the mean seed, as the benchmark calls it
     say("   backward, mean seed")
-    dh, dW = run.backward(grad_mean=torch.ones(1, device="cuda"))
+    if not single:
+        dh, dW = run.backward(grad_mean=torch.ones(1, device="cuda"))
     torch.cuda.synchronize()
     seed_mean = O.mean_seed(op)
     rdh, _ = O.backward(op, seed=seed_mean, rows=rows, want_dW=False, weights64=w64)
@@ -110,7 +117,7 @@ def test_full_size_sampled(name):
     seed[rows] = np.random.default_rng(7).uniform(0.5, 1.5, len(rows))
     seed = np.where(valid, seed, 0.0)
     g = torch.tensor(seed, dtype=torch.float32, device="cuda")
-    dh, dW = run.backward(grad_loss=g)
+    dh, dW = run.forward_backward(grad_loss=g) if single else run.backward(grad_loss=g)
     torch.cuda.synchronize()
     vsel = set(np.random.default_rng(11).choice(V, 512, replace=False).tolist())
     if prob.labels is not None:

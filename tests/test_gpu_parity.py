@@ -225,3 +225,52 @@ def test_autograd_wrapper():
     assert abs(loss.item() - mean) <= 1e-3 * abs(mean)
     assert rel_frob(h.grad.float().cpu().numpy(), rdh) <= GRAD_FROB
     assert rel_frob(W.grad.float().cpu().numpy(), rdW) <= GRAD_FROB
+
+
+# ---------------------------------------------------------------- single call
+@pytest.mark.parametrize("case", ["c1_full", "ce_ragged", "ce_chunked", "argmax_ce", "mix_ce",
+                                  "divergence"])
+def test_single_call_forward_backward(case):
+    """lmhead_loss_fwd_bwd: staged exp tiles for the cross-entropies, back-to-back otherwise."""
+    if case == "c1_full":
+        p, ch = synthetic.make_problem("ce_fp32_small"), 0
+    elif case == "ce_ragged":
+        p, ch = synthetic.make_problem("ce_bf16_1b", n_rows=600, hidden_dim=192, vocab=1100), 0
+    elif case == "ce_chunked":
+        p, ch = synthetic.make_problem("ce_bf16_1b", n_rows=600, hidden_dim=192, vocab=1100), 256
+    elif case == "argmax_ce":
+        p = synthetic.make_problem("multihead_bf16_405b", seq_len=150, hidden_dim=128, vocab=900,
+                                   weights={"ce": 1.0})
+        ch = 256
+    elif case == "mix_ce":
+        p = synthetic.make_problem("multihead_bf16_405b", seq_len=120, hidden_dim=128, vocab=700,
+                                   weights={"ce": 0.3, "ce_label": 0.7})
+        rng = np.random.default_rng(4)
+        p.labels = rng.integers(0, p.vocab, p.n_rows).astype(np.int32)
+        p.labels[::9] = -100
+        ch = 0
+    else:
+        p, ch = synthetic.make_problem("multihead_bf16_405b", seq_len=100, hidden_dim=128,
+                                      vocab=800), 256
+    full_parity(p, max_chunk_rows=ch, tag=f"single-{case}", single_call=True)
+
+
+def test_single_call_matches_two_calls_and_repeats():
+    p = synthetic.make_problem("ce_bf16_1b", n_rows=700, hidden_dim=128, vocab=900)
+    dev = to_device(p)
+    gm = torch.ones(1, device="cuda")
+    outs = []
+    for rep in range(2):
+        run = make_run(p, dev, max_chunk_rows=256)
+        dh, dW = run.forward_backward(grad_mean=gm)
+        torch.cuda.synchronize()
+        outs.append((run.loss.cpu(), dh.cpu(), dW.cpu()))
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
+    run = make_run(p, dev, max_chunk_rows=256)
+    run.forward()
+    dh2, dW2 = run.backward(grad_mean=gm)
+    torch.cuda.synchronize()
+    assert torch.allclose(run.loss.cpu(), outs[0][0], rtol=1e-5, atol=1e-5)
+    assert rel_frob(dh2.cpu().numpy(), outs[0][1].numpy()) < 1e-2
+    assert rel_frob(dW2.cpu().numpy(), outs[0][2].numpy()) < 1e-2

@@ -133,6 +133,21 @@ def test_bwd_checks(lib):
     assert call(wsb=100) == E_WS
 
 
+def test_fwd_bwd_checks(lib):
+    p = _problem()
+    f = lib.lmhead_loss_fwd_bwd
+
+    def call(gl=0x1000, gm=None, dh=0x4000, dW=0x5000, dt=B.F32, ws=0x100000, wsb=1 << 40):
+        return f(ctypes.byref(p), ws, wsb, 0x200000, None, None, None, 0x300000, None, gl, gm, dh,
+                 dt, dW, 0, None)
+
+    assert call(gl=None, gm=None) == E_INVAL
+    assert call(dh=None, dW=None) == E_INVAL
+    assert call(dt=3) == E_UNSUP
+    assert call(ws=0) == E_WS
+    assert call(wsb=64) == E_WS
+
+
 def test_workspace_size_grows_with_chunk_and_stays_below_logits(lib):
     p = _problem(N=32768, H=4096, V=128256)
     sizes = []
