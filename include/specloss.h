@@ -21,8 +21,9 @@
  * Conventions for every call:
  *  - All tensor pointers are DEVICE pointers owned by the caller; the
  *    library never allocates device memory.  Tensors are dense row-major.
- *    Floating tensors (hidden, W, target_hidden, W_t) must be 16-byte
- *    aligned; every other pointer 4-byte aligned (8 for counts).
+ *    Floating tensors (hidden, W, target_hidden, W_t) and the gradient
+ *    outputs (dhidden, dW) must be 16-byte aligned; every other pointer
+ *    4-byte aligned (8 for counts).
  *  - Work is enqueued on `stream` (NULL = the null stream) and is
  *    asynchronous: outputs are valid once the stream has synchronised.
  *  - Every argument is checked on the host before anything is enqueued.

@@ -514,8 +514,8 @@ int check_bwd_args(const float* grad_loss, const float* grad_mean, void* dhidden
   if (!grad_loss && !grad_mean) return SPECLOSS_E_INVAL;
   if (!dhidden && !dW) return SPECLOSS_E_INVAL;
   if (dh_dtype != SPECLOSS_F32 && dh_dtype != SPECLOSS_BF16) return SPECLOSS_E_UNSUPPORTED;
-  if (!aligned(grad_loss, 4) || !aligned(grad_mean, 4) || !aligned(dW, 4) ||
-      !aligned(dhidden, dh_dtype == SPECLOSS_F32 ? 4 : 2))
+  if (!aligned(grad_loss, 4) || !aligned(grad_mean, 4) || !aligned(dW, 16) ||
+      !aligned(dhidden, 16))
     return SPECLOSS_E_UNSUPPORTED;
   return SPECLOSS_OK;
 }

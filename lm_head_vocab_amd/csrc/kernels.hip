@@ -528,10 +528,21 @@ __global__ __launch_bounds__(kThreads, 1) void k_dz(DzLaunch a) {
 // plain contraction with store / accumulate epilogue
 // ============================================================================
 // ROLE only separates the two backward contractions in profiles (0: dh, 1: dW).
+//
+// Epilogue: the tile goes out in two halves of 128 rows.  The two waves that
+// own a half write their accumulators into LDS (rows padded to 1040 bytes so
+// the four row groups of a store land in different banks); then all threads
+// stream the half's rows: 16-byte loads of the old values (accumulate), add,
+// 16-byte stores, eight pieces in flight per thread.
+constexpr int kHalfRows = 128;
+constexpr int kEpiStride = 256 * 4 + 16;  // bytes per staged row
+
 template <typename T, typename OutT, int ROLE>
 __global__ __launch_bounds__(kThreads, 1) void k_gemm(GemmLaunch a) {
   using Cfg = TileCfg<T, 256, 256>;
-  __shared__ __attribute__((aligned(16))) char smem[Cfg::LDS_BYTES];
+  constexpr int kSmem = Cfg::LDS_BYTES > kHalfRows * kEpiStride ? Cfg::LDS_BYTES
+                                                               : kHalfRows * kEpiStride;
+  __shared__ __attribute__((aligned(16))) char smem[kSmem];
   int tm, tn;
   if (!tile_of(a.tiles_m, a.tiles_n, 4, tm, tn)) return;
   f32x4_t acc[Cfg::FM][Cfg::FN];
@@ -541,40 +552,56 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(GemmLaunch a) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   OutT* C = static_cast<OutT*>(a.C);
-  // Four fragments at a time: all their old values are loaded first (16
-  // loads in flight), then added and stored.
-  constexpr int FB = 4;
+  constexpr int kPieces = kHalfRows * 64;         // 16-byte pieces (4 values) per half
+  constexpr int kPerThread = kPieces / kThreads;  // 32
+  constexpr int kBatch = 8;
+#pragma unroll 1
+  for (int h = 0; h < 2; ++h) {
+    if (wm == h) {
 #pragma unroll
-  for (int j = 0; j < Cfg::FN; ++j) {
-    const int col = tn * Cfg::BN + wn * Cfg::WN + j * kFrag + frag_col(lane);
-    const bool col_ok = col < a.n_valid;
+      for (int i = 0; i < Cfg::FM; ++i)
 #pragma unroll
-    for (int i0 = 0; i0 < Cfg::FM; i0 += FB) {
-      float old[FB][4];
+        for (int j = 0; j < Cfg::FN; ++j)
 #pragma unroll
-      for (int ii = 0; ii < FB; ++ii)
+          for (int r = 0; r < 4; ++r) {
+            const int row = i * kFrag + frag_row(r, lane);
+            const int col = wn * Cfg::WN + j * kFrag + frag_col(lane);
+            *reinterpret_cast<float*>(smem + row * kEpiStride + col * 4) = acc[i][j][r];
+          }
+    }
+    __syncthreads();
+#pragma unroll 1
+    for (int b0 = 0; b0 < kPerThread; b0 += kBatch) {
+      f32x4_t old[kBatch];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int row = tm * Cfg::BM + wm * Cfg::WM + (i0 + ii) * kFrag + frag_row(r, lane);
-          old[ii][r] = 0.0f;
-          if (a.accumulate && col_ok && row < a.m_valid) {
-            const OutT* p = C + (int64_t)row * a.ldc + col;
-            if constexpr (sizeof(OutT) == 4) old[ii][r] = *reinterpret_cast<const float*>(p);
-            else old[ii][r] = (float)*reinterpret_cast<const __bf16*>(p);
+      for (int q = 0; q < kBatch; ++q) {
+        const int piece = (b0 + q) * kThreads + threadIdx.x;
+        const int row = piece >> 6, c4 = (piece & 63) * 4;
+        const int grow = tm * Cfg::BM + h * kHalfRows + row, gcol = tn * Cfg::BN + c4;
+        old[q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        if (a.accumulate && grow < a.m_valid && gcol < a.n_valid) {
+          const OutT* p = C + (int64_t)grow * a.ldc + gcol;
+          if constexpr (sizeof(OutT) == 4) {
+            old[q] = *reinterpret_cast<const f32x4_t*>(p);
+          } else {
+            const bf16x4_t v = *reinterpret_cast<const bf16x4_t*>(p);
+            old[q] = f32x4_t{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
           }
         }
+      }
 #pragma unroll
-      for (int ii = 0; ii < FB; ++ii)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int row = tm * Cfg::BM + wm * Cfg::WM + (i0 + ii) * kFrag + frag_row(r, lane);
-          if (!col_ok || row >= a.m_valid) continue;
-          OutT* p = C + (int64_t)row * a.ldc + col;
-          const float x = acc[i0 + ii][j][r] + old[ii][r];
-          if constexpr (sizeof(OutT) == 4) *reinterpret_cast<float*>(p) = x;
-          else *reinterpret_cast<__bf16*>(p) = (__bf16)x;
-        }
+      for (int q = 0; q < kBatch; ++q) {
+        const int piece = (b0 + q) * kThreads + threadIdx.x;
+        const int row = piece >> 6, c4 = (piece & 63) * 4;
+        const int grow = tm * Cfg::BM + h * kHalfRows + row, gcol = tn * Cfg::BN + c4;
+        if (grow >= a.m_valid || gcol >= a.n_valid) continue;
+        const f32x4_t x = *reinterpret_cast<const f32x4_t*>(smem + row * kEpiStride + c4 * 4) + old[q];
+        OutT* p = C + (int64_t)grow * a.ldc + gcol;
+        if constexpr (sizeof(OutT) == 4) store4<float>(reinterpret_cast<float*>(p), x[0], x[1], x[2], x[3]);
+        else store4<bf16_bits>(reinterpret_cast<bf16_bits*>(p), x[0], x[1], x[2], x[3]);
+      }
     }
+    __syncthreads();
   }
 }
 
