@@ -34,7 +34,38 @@ def parse():
     ap.add_argument("--chunk", type=int, default=8192, help="max rows per chunk")
     ap.add_argument("--cpu-sample-rows", type=int, default=64)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also copy a buffer of known size (for counter calibration)")
+    ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic_ce_bf16_8b.json"),
+                    help="counter summary giving HBM bytes per launch")
     return ap.parse_args()
+
+
+COPY_BYTES = 1 << 30
+
+
+def copy_calibration():
+    """A plain device copy of COPY_BYTES bytes (its counters scale the others)."""
+    import torch
+    x = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    torch.cuda.synchronize()
+    y.copy_(x)
+    torch.cuda.synchronize()
+    del x, y
+
+
+def load_traffic(path, kernel):
+    """Bytes per launch of `kernel` from a counter summary, None if absent or stale."""
+    try:
+        from lm_head_vocab_amd.profiling import source_digest
+        with open(path) as f:
+            t = json.load(f)
+        if t.get("source_digest") != source_digest():
+            return None
+        return t["kernels"].get(kernel, {}).get("bytes_per_launch")
+    except (OSError, ValueError, KeyError):
+        return None
 
 
 def main():
@@ -56,6 +87,8 @@ def main():
         sys.exit(1)
     L.load_library()
     dev = torch.device("cuda", 0)
+    if args.calibrate_copy:
+        copy_calibration()
 
     t0 = time.time()
     prob = synthetic.make_problem(args.workload)
@@ -126,7 +159,7 @@ def main():
     achieved = d["work_per_launch"] / (d["ms_avg"] * 1e-3) / 1e12
     kern = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 1),
             "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
-            "traffic": None, "flops_per_launch": d["work_per_launch"],
+            "traffic": load_traffic(args.traffic, dom), "flops_per_launch": d["work_per_launch"],
             "avg_launch_ms": round(d["ms_avg"], 4), "launches_per_step": d["launches_per_step"]}
 
     result = {
