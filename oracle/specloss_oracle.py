@@ -176,6 +176,20 @@ DIVERGENCES = {
 }
 
 
+def flatness(logp: np.ndarray) -> np.ndarray:
+    """Cosine similarity of each row's distribution p to the uniform distribution.
+
+    "Flatter Tokens are More Valuable for Speculative Draft Model Training"
+    (summary, Approach): a token's importance score is the cosine similarity of
+    the target distribution to the uniform one,
+    cos(p, 1/V) = sum_v p_v / (sqrt(V) * ||p||_2).
+    """
+    p = np.exp(logp)
+    V = p.shape[1]
+    ones = np.full(V, 1.0 / V)
+    return (p @ ones) / (np.linalg.norm(p, axis=1) * np.linalg.norm(ones))
+
+
 def argmax_lowest(u: np.ndarray) -> np.ndarray:
     """Index of the row maximum, lowest index among equal maxima (hard label of ce)."""
     return np.argmax(u, axis=1).astype(np.int64)
@@ -288,6 +302,7 @@ class OracleResult:
     n_valid: int                     # over the whole problem
     n_bad: int
     dz: Optional[np.ndarray] = None  # d(loss_t)/dz rows, weighted, before the seed
+    flat: Optional[np.ndarray] = None  # flatness of p, where a target exists
 
 
 def _target_rows(prob: OracleProblem, idx: np.ndarray, valid: np.ndarray) -> np.ndarray:
@@ -308,7 +323,7 @@ def _block(prob: OracleProblem, idx: np.ndarray, Wd: np.ndarray, Wt: Optional[np
     B, V = z.shape
     terms: Dict[str, np.ndarray] = {}
     dzs: Dict[str, np.ndarray] = {}
-    lse_p = alpha = None
+    lse_p = alpha = flat = None
     label = np.full(B, -1, dtype=np.int64)
     if any(k in TARGET_KINDS for k in act):
         g = widen(prob.target_hidden[_target_rows(prob, idx, valid)], prob.dtype)
@@ -316,6 +331,7 @@ def _block(prob: OracleProblem, idx: np.ndarray, Wd: np.ndarray, Wt: Optional[np
         lse_p = logsumexp_rows(u)
         logp = u - lse_p[:, None]
         alpha = overlap(logp, logq)
+        flat = flatness(logp)
         if "ce" in act:
             y = argmax_lowest(u)
             label = y
@@ -337,7 +353,7 @@ def _block(prob: OracleProblem, idx: np.ndarray, Wd: np.ndarray, Wt: Optional[np
             dz += w * dzs[k]
     if want_dz:
         dz[~valid] = 0.0
-    return loss, terms, lse_q, lse_p, label, alpha, valid, dz
+    return loss, terms, lse_q, lse_p, label, alpha, valid, dz, flat
 
 
 def _weights64(prob: OracleProblem):
@@ -373,7 +389,7 @@ def forward(prob, rows: Optional[Iterable[int]] = None, block: int = 64,
     return OracleResult(rows=sel, loss=cat(0) if parts else np.zeros(0), terms=terms,
                         lse_q=cat(2), lse_p=cat(3), label=cat(4), alpha=cat(5),
                         valid=cat(6), n_valid=int(valid_all.sum()), n_bad=int(bad_all.sum()),
-                        dz=cat(7) if want_dz else None)
+                        dz=cat(7) if want_dz else None, flat=cat(8))
 
 
 def mean_loss(prob) -> Tuple[float, Dict[str, float], int]:
@@ -422,7 +438,7 @@ def backward(prob, seed: Optional[np.ndarray] = None, rows: Optional[Iterable[in
     dW = np.zeros((len(vsel), H)) if want_dW else None
     for b0 in range(0, len(sel), block):
         idx = sel[b0:b0 + block]
-        *_, dz = _block(prob, idx, Wd, Wt, valid_all, True)
+        dz = _block(prob, idx, Wd, Wt, valid_all, True)[7]
         dz = dz * seed[idx][:, None]
         dh[b0:b0 + len(idx)] = dz @ Wd
         if want_dW:

@@ -377,3 +377,27 @@ def test_validity_bad_rows():
     valid, bad = O.row_validity(p)
     assert list(valid) == [True, False, False, False, True]
     assert list(bad) == [False, False, True, False, False]
+
+
+# --------------------------------------------------------------- flatness
+def test_flatness_closed_forms():
+    """Uniform p gives 1; a one-hot p gives 1/sqrt(V); two equal peaks give sqrt(2/V)."""
+    V = 64
+    uni = np.log(np.full((1, V), 1.0 / V))
+    assert abs(O.flatness(uni)[0] - 1.0) < 1e-14
+    onehot = np.full((1, V), -1e4)
+    onehot[0, 3] = 0.0
+    logp = ssp.log_softmax(onehot, axis=1)
+    assert abs(O.flatness(logp)[0] - 1 / math.sqrt(V)) < 1e-12
+    two = np.full((1, V), -1e4)
+    two[0, [1, 9]] = 0.0
+    assert abs(O.flatness(ssp.log_softmax(two, axis=1))[0] - math.sqrt(2 / V)) < 1e-12
+
+
+def test_flatness_scipy_cosine():
+    """Library route: scipy's cosine distance between p and the all-ones vector."""
+    rng = np.random.default_rng(12)
+    u = rng.standard_normal((5, 300)) * 2
+    logp = ssp.log_softmax(u, axis=1)
+    ref = [1 - ssd.cosine(np.exp(logp[i]), np.ones(300)) for i in range(5)]
+    assert np.allclose(O.flatness(logp), ref, rtol=1e-12)
