@@ -76,8 +76,25 @@ enum {
 
 #define SPECLOSS_IGNORE_INDEX (-100)
 
-/* Per-row statistics the forward saves for the backward (opaque layout). */
-#define SPECLOSS_SAVED_FIELDS 9
+/*
+ * Per-row state the forward saves for the backward: SPECLOSS_SAVED_FIELDS
+ * arrays of N 4-byte values each (see specloss_saved_offset).  The fields a
+ * caller may want to read are listed here; the others are internal.
+ */
+enum {
+  SPECLOSS_SAVED_LSE_Q = 0,     /* fp32: logsumexp of the draft logits z */
+  SPECLOSS_SAVED_LSE_P = 1,     /* fp32: logsumexp of the target logits u (0 without a target) */
+  SPECLOSS_SAVED_Y_ARG = 3,     /* int32: argmax of u, lowest index on ties (-1 without a target) */
+  SPECLOSS_SAVED_ALPHA = 4,     /* fp32: alpha = sum_v min(p_v, q_v), written when a
+                                   divergence kind is on ("Available Losses", tv) */
+  SPECLOSS_SAVED_VALID = 8,     /* int32: 1 on valid rows, 0 on masked or bad rows */
+  SPECLOSS_SAVED_FLATNESS = 9,  /* fp32: flatness of the target distribution,
+                                   cos(p, uniform) = 1 / (sqrt(V) |p|_2), in [1/sqrt(V), 1]
+                                   ("Flatter Tokens are More Valuable for Speculative Draft
+                                   Model Training", Approach: per-token flatness); written
+                                   whenever a target is given, 0 on invalid rows */
+  SPECLOSS_SAVED_FIELDS = 10
+};
 
 /* Opaque kernel trace (see specloss_trace_create). */
 typedef struct specloss_trace specloss_trace;
@@ -124,6 +141,14 @@ int lmhead_loss_workspace_size(const specloss_problem* p, int64_t max_chunk_rows
 
 /* Bytes of the `saved` buffer for n_rows rows (256-byte aligned arrays). */
 size_t specloss_saved_bytes(int64_t n_rows);
+
+/*
+ * Byte offset of saved field `field` (SPECLOSS_SAVED_*) inside a saved buffer
+ * for n_rows rows; the field is n_rows 4-byte values from there.  Host only,
+ * no device access.  SPECLOSS_E_INVAL for n_rows <= 0, an unknown field or
+ * a NULL offset.
+ */
+int specloss_saved_offset(int64_t n_rows, int32_t field, size_t* offset);
 
 /*
  * Forward.  Outputs (device):

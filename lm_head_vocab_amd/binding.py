@@ -57,6 +57,7 @@ _lib: Optional[ctypes.CDLL] = None
 EXPORTS = (
     "lmhead_loss_workspace_size",
     "specloss_saved_bytes",
+    "specloss_saved_offset",
     "lmhead_loss_fwd",
     "lmhead_loss_bwd",
     "lmhead_loss_fwd_bwd",
@@ -87,6 +88,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.lmhead_loss_workspace_size.restype = ctypes.c_int
     lib.specloss_saved_bytes.argtypes = [i64]
     lib.specloss_saved_bytes.restype = sz
+    lib.specloss_saved_offset.argtypes = [i64, i32, ctypes.POINTER(sz)]
+    lib.specloss_saved_offset.restype = ctypes.c_int
     lib.lmhead_loss_fwd.argtypes = [P, vp, sz, vp, vp, vp, vp, vp, vp, vp]
     lib.lmhead_loss_fwd.restype = ctypes.c_int
     lib.lmhead_loss_bwd.argtypes = [P, vp, vp, vp, vp, vp, sz, vp, i32, vp, ctypes.c_int, vp]
@@ -183,6 +186,17 @@ def lmhead_loss_workspace_size(problem: Problem, max_chunk_rows: int = 0) -> int
 
 def specloss_saved_bytes(n_rows: int) -> int:
     return int(load_library().specloss_saved_bytes(n_rows))
+
+
+# public saved fields (SPECLOSS_SAVED_* in include/specloss.h)
+SAVED_LSE_Q, SAVED_LSE_P, SAVED_Y_ARG, SAVED_ALPHA, SAVED_VALID, SAVED_FLATNESS = 0, 1, 3, 4, 8, 9
+
+
+def specloss_saved_offset(n_rows: int, field: int) -> int:
+    out = ctypes.c_size_t(0)
+    _check(load_library().specloss_saved_offset(n_rows, field, ctypes.byref(out)),
+           "specloss_saved_offset")
+    return out.value
 
 
 def lmhead_loss_fwd(problem: Problem, workspace: torch.Tensor, loss: torch.Tensor,

@@ -136,7 +136,7 @@ Layout plan(const specloss_problem* p, const KindSet& k, int64_t Nc) {
   L.head_end = o;
   const size_t tile_cols = (size_t)L.Tv * Nc * 4;
   L.pz = take(2 * tile_cols);
-  L.pu = take(k.target ? 3 * tile_cols : 0);
+  L.pu = take(k.target ? 4 * tile_cols : 0);
   L.p2 = take(k.pass2 ? (size_t)kNumSums * tile_cols : 0);
   L.zy = take(2 * (size_t)Nc * 4);
   L.fwd_end = o;
@@ -148,7 +148,7 @@ Layout plan(const specloss_problem* p, const KindSet& k, int64_t Nc) {
   L.bwd_end = o;
   o = L.head_end;
   L.f_pz = take(2 * tile_cols);
-  L.f_pu = take(k.target ? 3 * tile_cols : 0);
+  L.f_pu = take(k.target ? 4 * tile_cols : 0);
   L.f_zy = take(2 * (size_t)Nc * 4);
   L.f_wt = take((size_t)L.H * L.Vp * L.es);
   L.f_ht = take((size_t)L.H * Nc * L.es);
@@ -194,6 +194,7 @@ SavedView saved_view(void* base, int64_t n) {
   v.rkl = reinterpret_cast<float*>(b + 6 * stride);
   v.eqg = reinterpret_cast<float*>(b + 7 * stride);
   v.flags = reinterpret_cast<int32_t*>(b + 8 * stride);
+  v.flat = reinterpret_cast<float*>(b + 9 * stride);
   return v;
 }
 
@@ -325,6 +326,7 @@ int fwd_chunk(const specloss_problem* p, const KindSet& k, const Layout& L, cons
   sz.pm = b.pz;
   sz.ps = b.pz + tile_cols;
   sz.pi = nullptr;
+  sz.pq = nullptr;
   if (stage) {
     StatsStageLaunch ss;
     ss.st = sz;
@@ -342,6 +344,7 @@ int fwd_chunk(const specloss_problem* p, const KindSet& k, const Layout& L, cons
     su.pm = b.pu;
     su.ps = b.pu + tile_cols;
     su.pi = reinterpret_cast<int32_t*>(b.pu + 2 * tile_cols);
+    su.pq = b.pu + 3 * tile_cols;
     TRACED(tr, K_STATS_P, 2.0 * rows * H * p->vocab, launch_stats(bf16, true, su, stream));
   }
 
@@ -354,10 +357,14 @@ int fwd_chunk(const specloss_problem* p, const KindSet& k, const Layout& L, cons
   c1.pm_u = k.target ? b.pu : nullptr;
   c1.ps_u = k.target ? b.pu + tile_cols : nullptr;
   c1.pi_u = k.target ? reinterpret_cast<const int32_t*>(b.pu + 2 * tile_cols) : nullptr;
+  c1.pq_u = k.target ? b.pu + 3 * tile_cols : nullptr;
+  c1.vocab = (int32_t)p->vocab;
+  c1.flags = sv.flags + r0;
   c1.lse_q = sv.lse_q + r0;
   c1.lse_p = sv.lse_p + r0;
   c1.y_arg = sv.y_arg + r0;
-  TRACED(tr, K_COMBINE1, (k.target ? 5.0 : 2.0) * L.Tv * rows * 4, launch_combine1(c1, stream));
+  c1.flat = sv.flat + r0;
+  TRACED(tr, K_COMBINE1, (k.target ? 6.0 : 2.0) * L.Tv * rows * 4, launch_combine1(c1, stream));
 
   const bool ce_lab = (k.active >> SPECLOSS_CE_LABEL) & 1u;
   const bool ce_arg = (k.active >> SPECLOSS_CE_ARGMAX_P) & 1u;
@@ -527,6 +534,13 @@ extern "C" {
 size_t specloss_saved_bytes(int64_t n_rows) {
   if (n_rows <= 0) return 0;
   return (size_t)SPECLOSS_SAVED_FIELDS * align_up((size_t)n_rows * 4, kAlign);
+}
+
+int specloss_saved_offset(int64_t n_rows, int32_t field, size_t* offset) {
+  if (n_rows <= 0 || field < 0 || field >= SPECLOSS_SAVED_FIELDS || !offset)
+    return SPECLOSS_E_INVAL;
+  *offset = (size_t)field * align_up((size_t)n_rows * 4, kAlign);
+  return SPECLOSS_OK;
 }
 
 int lmhead_loss_workspace_size(const specloss_problem* p, int64_t max_chunk_rows, size_t* bytes) {

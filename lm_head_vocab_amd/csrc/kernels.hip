@@ -25,6 +25,11 @@
 
 namespace specloss {
 
+// Height (in tiles) of the tile blocks each XCD walks, see tile_of: blocks of
+// 4 x 8 tiles measured best for every contraction of the path (1, 2 and 8
+// were slower at the 8B shape).
+constexpr int kGroupM = 4;
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
@@ -55,6 +60,18 @@ __device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2
   m = mn;
 }
 
+// as lse_merge, also carrying q = sum exp(2 (x - m)) (the squared norm of the
+// unnormalised distribution) relative to the same running maximum
+__device__ __forceinline__ void lse_merge_sq(float& m, float& s, float& q, float m2, float s2,
+                                             float q2) {
+  const float mn = fmaxf(m, m2);
+  if (mn == -INFINITY) return;
+  const float a = fast_exp2((m - mn) * kLog2e), b = fast_exp2((m2 - mn) * kLog2e);
+  s = s * a + s2 * b;
+  q = q * a * a + q2 * b * b;
+  m = mn;
+}
+
 template <typename T>
 __device__ __forceinline__ void store4(T* dst, float a0, float a1, float a2, float a3);
 template <>
@@ -82,12 +99,15 @@ __device__ __forceinline__ void store1<float>(float* dst, float x) {
 // ============================================================================
 // pass 1: per-tile softmax statistics
 // ============================================================================
-template <typename T, bool ARGMAX>
+// TARGET (the target distribution p): also the lowest-index argmax and the sum
+// of e^2, e = exp(u - m_tile), from which the flatness score is formed.
+template <typename T, bool TARGET>
 __global__ __launch_bounds__(kThreads, 1) void k_stats(StatsLaunch a) {
+  constexpr bool ARGMAX = TARGET;
   using Cfg = TileCfg<T, 256, 256>;
   __shared__ __attribute__((aligned(16))) char smem[Cfg::LDS_BYTES];
   int tm, tn;
-  if (!tile_of(a.tiles_m, a.tiles_n, 4, tm, tn)) return;
+  if (!tile_of(a.tiles_m, a.tiles_n, kGroupM, tm, tn)) return;
 
   f32x4_t acc[Cfg::FM][Cfg::FN];
   zero_acc<Cfg>(acc);
@@ -99,7 +119,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_stats(StatsLaunch a) {
   const int v_base = tm * Cfg::BM + wm * Cfg::WM;
   const bool tail = tm * Cfg::BM + Cfg::BM > a.vocab;
 
-  float mj[Cfg::FN], sj[Cfg::FN];
+  float mj[Cfg::FN], sj[Cfg::FN], qj[Cfg::FN];
   int ij[Cfg::FN];
 #pragma unroll
   for (int j = 0; j < Cfg::FN; ++j) {
@@ -119,7 +139,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_stats(StatsLaunch a) {
         }
       }
     const float m = col_max(mx);
-    float s = 0.0f;
+    float s = 0.0f, q = 0.0f;
     if (m != -INFINITY) {
       const float mb = m * kLog2e;
 #pragma unroll
@@ -127,11 +147,16 @@ __global__ __launch_bounds__(kThreads, 1) void k_stats(StatsLaunch a) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int v = v_base + i * kFrag + frag_row(r, lane);
-          if (!tail || v < a.vocab) s += fast_exp2(fmaf(acc[i][j][r], kLog2e, -mb));
+          if (!tail || v < a.vocab) {
+            const float e = fast_exp2(fmaf(acc[i][j][r], kLog2e, -mb));
+            s += e;
+            if (TARGET) q = fmaf(e, e, q);
+          }
         }
     }
     mj[j] = m;
     sj[j] = col_sum(s, lane);
+    qj[j] = TARGET ? col_sum(q, lane) : 0.0f;
     if (ARGMAX) {
       // lowest index among the lanes that reach the column maximum
       int cand = (mx == m) ? idx : 0x7fffffff;
@@ -148,9 +173,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_stats(StatsLaunch a) {
 #pragma unroll
     for (int j = 0; j < Cfg::FN; ++j) {
       const int c = wn * Cfg::WN + j * kFrag + lane;
-      red[c * 3 + 0] = mj[j];
-      red[c * 3 + 1] = sj[j];
-      red[c * 3 + 2] = __int_as_float(ij[j]);
+      red[c * 4 + 0] = mj[j];
+      red[c * 4 + 1] = sj[j];
+      red[c * 4 + 2] = __int_as_float(ij[j]);
+      red[c * 4 + 3] = qj[j];
     }
   }
   __syncthreads();
@@ -158,18 +184,22 @@ __global__ __launch_bounds__(kThreads, 1) void k_stats(StatsLaunch a) {
 #pragma unroll
     for (int j = 0; j < Cfg::FN; ++j) {
       const int c = wn * Cfg::WN + j * kFrag + lane;
-      float m = mj[j], s = sj[j];
+      float m = mj[j], s = sj[j], q = qj[j];
       int id = ij[j];
-      const float m2 = red[c * 3 + 0], s2 = red[c * 3 + 1];
-      const int i2 = __float_as_int(red[c * 3 + 2]);
+      const float m2 = red[c * 4 + 0], s2 = red[c * 4 + 1];
+      const int i2 = __float_as_int(red[c * 4 + 2]);
       if (ARGMAX) id = (m2 > m) ? i2 : ((m2 == m) ? min(id, i2) : id);
-      lse_merge(m, s, m2, s2);
+      if (TARGET)
+        lse_merge_sq(m, s, q, m2, s2, red[c * 4 + 3]);
+      else
+        lse_merge(m, s, m2, s2);
       const int col = tn * Cfg::BN + c;
       if (col < a.ncols) {
         const int64_t o = (int64_t)tm * a.ldp + col;
         a.pm[o] = m;
         a.ps[o] = s;
         if (ARGMAX) a.pi[o] = id;
+        if (TARGET) a.pq[o] = q;
       }
     }
   }
@@ -185,7 +215,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_stats_stage(StatsStageLaunch a)
   __shared__ __attribute__((aligned(16))) char smem[Cfg::LDS_BYTES];
   const StatsLaunch& st = a.st;
   int tm, tn;
-  if (!tile_of(st.tiles_m, st.tiles_n, 4, tm, tn)) return;
+  if (!tile_of(st.tiles_m, st.tiles_n, kGroupM, tm, tn)) return;
 
   f32x4_t acc[Cfg::FM][Cfg::FN];
   zero_acc<Cfg>(acc);
@@ -354,7 +384,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_div(DivLaunch a) {
   using Cfg = TileCfg<T, 256, 128>;
   __shared__ __attribute__((aligned(16))) char smem[Cfg::LDS_BYTES];
   int tm, tn;
-  if (!tile_of(a.tiles_m, a.tiles_n, 4, tm, tn)) return;
+  if (!tile_of(a.tiles_m, a.tiles_n, kGroupM, tm, tn)) return;
 
   f32x4_t az[Cfg::FM][Cfg::FN], au[Cfg::FM][Cfg::FN];
   zero_acc<Cfg>(az);
@@ -466,7 +496,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_dz(DzLaunch a) {
   using Cfg = TileCfg<T, 256, (DUAL ? 128 : 256)>;
   __shared__ __attribute__((aligned(16))) char smem[Cfg::LDS_BYTES];
   int tm, tn;
-  if (!tile_of(a.tiles_m, a.tiles_n, 4, tm, tn)) return;
+  if (!tile_of(a.tiles_m, a.tiles_n, kGroupM, tm, tn)) return;
 
   f32x4_t az[Cfg::FM][Cfg::FN];
   f32x4_t au[DUAL ? Cfg::FM : 1][DUAL ? Cfg::FN : 1];
@@ -544,7 +574,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(GemmLaunch a) {
                                                                : kHalfRows * kEpiStride;
   __shared__ __attribute__((aligned(16))) char smem[kSmem];
   int tm, tn;
-  if (!tile_of(a.tiles_m, a.tiles_n, 4, tm, tn)) return;
+  if (!tile_of(a.tiles_m, a.tiles_n, kGroupM, tm, tn)) return;
   f32x4_t acc[Cfg::FM][Cfg::FN];
   zero_acc<Cfg>(acc);
   tile_mainloop<T, Cfg>(acc, as_op<T>(a.A), tm * Cfg::BM, as_op<T>(a.B), tn * Cfg::BN, a.k_len,
@@ -694,8 +724,10 @@ __global__ __launch_bounds__(256) void k_rowdot(RowdotLaunch a) {
 // segment of vocabulary tiles (max pass, then sum pass), then the segments
 // are merged in order.  The argmax keeps the first tile holding the maximum,
 // i.e. the lowest vocabulary index.
-__device__ __forceinline__ void seg_lse(const float* pm, const float* ps, int64_t ldp, int c,
-                                        int t0, int t1, float& m, float& s, int& best) {
+// pq (may be null): per-tile sums of e^2, merged into q the same way
+__device__ __forceinline__ void seg_lse(const float* pm, const float* ps, const float* pq,
+                                        int64_t ldp, int c, int t0, int t1, float& m, float& s,
+                                        float& q, int& best) {
   m = -INFINITY;
   best = -1;
   for (int t = t0; t < t1; ++t) {
@@ -703,31 +735,35 @@ __device__ __forceinline__ void seg_lse(const float* pm, const float* ps, int64_
     if (x > m) { m = x; best = t; }
   }
   s = 0.0f;
+  q = 0.0f;
   if (m != -INFINITY)
     for (int t = t0; t < t1; ++t) {
       const int64_t o = (int64_t)t * ldp + c;
-      s += ps[o] * fast_exp2((pm[o] - m) * kLog2e);
+      const float f = fast_exp2((pm[o] - m) * kLog2e);
+      s += ps[o] * f;
+      if (pq) q += pq[o] * f * f;
     }
 }
 
 __global__ __launch_bounds__(256) void k_combine1(Combine1Launch a) {
   constexpr int SEG = 8, RPB = 32;
-  __shared__ float sm[2][SEG][RPB], ss[2][SEG][RPB];
+  __shared__ float sm[2][SEG][RPB], ss[2][SEG][RPB], sq[SEG][RPB];
   __shared__ int sb[SEG][RPB];
   const int rr = threadIdx.x % RPB, seg = threadIdx.x / RPB;
   const int c = blockIdx.x * RPB + rr;
   const int per = (a.tiles_m + SEG - 1) / SEG;
   const int t0 = min(a.tiles_m, seg * per), t1 = min(a.tiles_m, t0 + per);
   if (c < a.ncols) {
-    float m, s;
+    float m, s, q;
     int best;
-    seg_lse(a.pm_z, a.ps_z, a.ldp, c, t0, t1, m, s, best);
+    seg_lse(a.pm_z, a.ps_z, nullptr, a.ldp, c, t0, t1, m, s, q, best);
     sm[0][seg][rr] = m;
     ss[0][seg][rr] = s;
     if (a.pm_u) {
-      seg_lse(a.pm_u, a.ps_u, a.ldp, c, t0, t1, m, s, best);
+      seg_lse(a.pm_u, a.ps_u, a.pq_u, a.ldp, c, t0, t1, m, s, q, best);
       sm[1][seg][rr] = m;
       ss[1][seg][rr] = s;
+      sq[seg][rr] = q;
       sb[seg][rr] = best;
     }
   }
@@ -736,11 +772,15 @@ __global__ __launch_bounds__(256) void k_combine1(Combine1Launch a) {
   for (int side = 0; side < (a.pm_u ? 2 : 1); ++side) {
     float m = -INFINITY;
     int bseg = 0;
-    for (int q = 0; q < SEG; ++q)
-      if (sm[side][q][rr] > m) { m = sm[side][q][rr]; bseg = q; }
-    float s = 0.0f;
-    for (int q = 0; q < SEG; ++q)
-      if (sm[side][q][rr] != -INFINITY) s += ss[side][q][rr] * fast_exp2((sm[side][q][rr] - m) * kLog2e);
+    for (int g = 0; g < SEG; ++g)
+      if (sm[side][g][rr] > m) { m = sm[side][g][rr]; bseg = g; }
+    float s = 0.0f, q = 0.0f;
+    for (int g = 0; g < SEG; ++g)
+      if (sm[side][g][rr] != -INFINITY) {
+        const float f = fast_exp2((sm[side][g][rr] - m) * kLog2e);
+        s += ss[side][g][rr] * f;
+        if (side == 1) q += sq[g][rr] * f * f;
+      }
     const float lse = m + logf(s);
     if (side == 0) {
       a.lse_q[c] = lse;
@@ -748,11 +788,14 @@ __global__ __launch_bounds__(256) void k_combine1(Combine1Launch a) {
       a.lse_p[c] = lse;
       const int bt = sb[bseg][rr];  // -1 only when no tile has a finite maximum
       a.y_arg[c] = bt >= 0 ? a.pi_u[(int64_t)bt * a.ldp + c] : -1;
+      // cos(p, uniform) = sum p / (sqrt(V) |p|) = s / (sqrt(V q)), with p = e / s
+      a.flat[c] = (bt >= 0 && a.flags[c]) ? s / sqrtf((float)a.vocab * q) : 0.0f;
     }
   }
   if (!a.pm_u) {
     a.lse_p[c] = 0.0f;
     a.y_arg[c] = -1;
+    a.flat[c] = 0.0f;
   }
 }
 
@@ -876,13 +919,13 @@ __global__ __launch_bounds__(256) void k_align(AlignLaunch a) {
 // ============================================================================
 // launchers
 // ============================================================================
-hipError_t launch_stats(bool bf16, bool argmax, const StatsLaunch& a, hipStream_t s) {
+hipError_t launch_stats(bool bf16, bool target, const StatsLaunch& a, hipStream_t s) {
   const dim3 grid(grid_for_tiles(a.tiles_m * a.tiles_n)), block(kThreads);
   if (bf16) {
-    if (argmax) hipLaunchKernelGGL((k_stats<bf16_bits, true>), grid, block, 0, s, a);
+    if (target) hipLaunchKernelGGL((k_stats<bf16_bits, true>), grid, block, 0, s, a);
     else hipLaunchKernelGGL((k_stats<bf16_bits, false>), grid, block, 0, s, a);
   } else {
-    if (argmax) hipLaunchKernelGGL((k_stats<float, true>), grid, block, 0, s, a);
+    if (target) hipLaunchKernelGGL((k_stats<float, true>), grid, block, 0, s, a);
     else hipLaunchKernelGGL((k_stats<float, false>), grid, block, 0, s, a);
   }
   return hipGetLastError();

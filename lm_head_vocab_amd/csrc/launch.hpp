@@ -32,6 +32,7 @@ struct SavedView {
   float* rkl;
   float* eqg;
   int32_t* flags;    // 1 = valid row
+  float* flat;       // flatness of p: cos(p, uniform), 0 when no target or invalid
 };
 
 struct GemmOperand {
@@ -48,9 +49,11 @@ struct StatsLaunch {
   int32_t k_len, vocab, tiles_m, tiles_n, ncols, ldp;
   float* pm;
   float* ps;
-  int32_t* pi;  // only for the argmax variant
+  int32_t* pi;  // target variant only: lowest-index argmax per tile
+  float* pq;    // target variant only: sum exp(2 (u - m_tile)) per tile
 };
-hipError_t launch_stats(bool bf16, bool argmax, const StatsLaunch& a, hipStream_t s);
+// target: the variant for the target logits u (argmax and e^2 sums as well)
+hipError_t launch_stats(bool bf16, bool target, const StatsLaunch& a, hipStream_t s);
 
 // pass 1 for the single-call forward+backward: also stores
 // e = exp(z - m_tile) of every (row, vocab) into `stage` ([cap][Vp], row-major)
@@ -153,9 +156,13 @@ struct Combine1Launch {
   const float* pm_u;  // null when no target
   const float* ps_u;
   const int32_t* pi_u;
+  const float* pq_u;
+  int32_t vocab;
+  const int32_t* flags;  // chunk-local
   float* lse_q;  // chunk-local
   float* lse_p;
   int32_t* y_arg;
+  float* flat;
 };
 hipError_t launch_combine1(const Combine1Launch& a, hipStream_t s);
 

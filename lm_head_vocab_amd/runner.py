@@ -72,10 +72,14 @@ class LossRun:
         return dhidden, dW
 
     def saved_field(self, i: int, dtype=torch.float32) -> torch.Tensor:
-        """View of saved field i (see SavedView in csrc/launch.hpp) as an N-vector."""
-        stride = ((self.n_rows * 4 + 255) // 256) * 256
-        raw = self.saved[i * stride:i * stride + self.n_rows * 4]
-        return raw.view(dtype)
+        """View of saved field i (SPECLOSS_SAVED_* / SavedView order) as an N-vector."""
+        o = B.specloss_saved_offset(self.n_rows, i)
+        return self.saved[o:o + self.n_rows * 4].view(dtype)
+
+    @property
+    def flatness(self) -> torch.Tensor:
+        """Per-row flatness of the target distribution, cos(p, uniform)."""
+        return self.saved_field(B.SAVED_FLATNESS)
 
 
 class _LMHeadLoss(torch.autograd.Function):

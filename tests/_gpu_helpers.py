@@ -58,6 +58,12 @@ def check_tokens(gpu: np.ndarray, ref: np.ndarray, what: str) -> None:
                            f"{int(np.argmax(err))}: gpu {gpu[np.argmax(err)]} ref {ref[np.argmax(err)]}")
 
 
+def check_flatness(gpu: np.ndarray, ref: np.ndarray, valid: np.ndarray) -> None:
+    """Flatness within the per-token bar on valid rows, exactly 0 on the others."""
+    check_tokens(gpu[valid], ref[valid], "flatness")
+    assert np.all(gpu[~valid] == 0.0), "flatness of invalid rows must be 0"
+
+
 def check_argmax(gpu_y: np.ndarray, prob, rows, valid) -> None:
     """Hard labels equal the oracle's wherever its top-2 target logits differ by >= ARGMAX_GAP."""
     Wt = O.widen(prob.W_t, prob.dtype)
@@ -107,6 +113,8 @@ def full_parity(prob, *, max_chunk_rows=0, check_grads=True, tag="", single_call
     if "ce" in prob.weights:
         y = run.saved_field(3, torch.int32).cpu().numpy()
         check_argmax(y, prob, np.arange(prob.n_rows), ref.valid)
+    if ref.flat is not None:
+        check_flatness(run.flatness.cpu().numpy(), ref.flat, ref.valid)
     out = dict(run=run, ref=ref, loss=loss)
     if check_grads or single_call:
         if single_call:

@@ -19,8 +19,8 @@ import torch
 
 import synthetic
 from oracle import specloss_oracle as O
-from tests._gpu_helpers import (ARGMAX_GAP, GRAD_FROB, check_tokens, make_run, rel_frob, say,
-                                to_device)
+from tests._gpu_helpers import (ARGMAX_GAP, GRAD_FROB, check_flatness, check_tokens, make_run,
+                                rel_frob, say, to_device)
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
@@ -83,6 +83,8 @@ def test_full_size_sampled(name, single):
     if ref.alpha is not None and any(k != "ce" and k != "ce_label" for k in prob.weights):
         alpha = run.saved_field(4).cpu().numpy()[rows]
         assert np.allclose(alpha[ref.valid], ref.alpha[ref.valid], atol=1e-4)
+    if ref.flat is not None:
+        check_flatness(run.flatness.cpu().numpy()[rows], ref.flat, ref.valid)
     if "ce" in prob.weights:
         y = run.saved_field(3, torch.int32).cpu().numpy()[rows]
         tr = rows if prob.target_row is None else prob.target_row[rows]

@@ -93,7 +93,7 @@ def test_determinism_bitwise():
         run.forward()
         dh, dW = run.backward(grad_mean=torch.ones(1, device="cuda"))
         torch.cuda.synchronize()
-        fields = [run.saved_field(i, torch.int32).cpu() for i in range(9)]  # bitwise; padding excluded
+        fields = [run.saved_field(i, torch.int32).cpu() for i in range(10)]  # bitwise; padding excluded
         outs.append((run.loss.cpu(), run.term.cpu(), *fields, dh.cpu(), dW.cpu()))
     for a, b in zip(*outs):
         assert torch.equal(a, b)
@@ -274,3 +274,45 @@ def test_single_call_matches_two_calls_and_repeats():
     assert torch.allclose(run.loss.cpu(), outs[0][0], rtol=1e-5, atol=1e-5)
     assert rel_frob(dh2.cpu().numpy(), outs[0][1].numpy()) < 1e-2
     assert rel_frob(dW2.cpu().numpy(), outs[0][2].numpy()) < 1e-2
+
+
+def test_flatness_range_and_uniform_rows():
+    """Flatness over target rows from uniform to sharply peaked.
+
+    Rows whose target hidden state is zero have u = 0, so p is exactly uniform
+    and the score is 1; scaling a row up sharpens p toward one-hot, whose score
+    is 1/sqrt(V).  Every valid row is compared with the oracle; invalid rows
+    (masked here) read exactly 0.
+    """
+    p = synthetic.make_problem("lk_hybrid_bf16_8b", n_rows=520, hidden_dim=128, vocab=1300,
+                               weights={"ce": 1.0, "tv": 0.5})
+    th = synthetic.bf16_bits_to_f32(p.target_hidden)
+    scale = np.geomspace(0.05, 40.0, p.n_rows)
+    scale[::37] = 0.0
+    p.target_hidden = synthetic.f32_to_bf16_bits(th * scale[:, None])
+    p.mask = (np.arange(p.n_rows) % 11 != 5).astype(np.uint8)
+    out = full_parity(p, tag="flatness", check_grads=False)
+    flat = out["run"].flatness.cpu().numpy()
+    zero = (scale == 0.0) & out["ref"].valid
+    assert np.allclose(flat[zero], 1.0, rtol=1e-6), flat[zero]
+    v = out["ref"].valid
+    assert np.all(flat[v] >= 1.0 / np.sqrt(p.vocab) * (1 - 1e-6)) and np.all(flat[v] <= 1 + 1e-6)
+    assert flat[v].min() < 0.2 and flat[v].max() > 0.99   # the sweep spans the range
+
+
+def test_flatness_single_call_and_chunks():
+    """The single call and chunked forwards write the same flatness bits as one unchunked forward."""
+    p = synthetic.make_problem("lk_hybrid_bf16_8b", n_rows=700, hidden_dim=128, vocab=900,
+                               weights={"ce": 1.0})
+    dev = to_device(p)
+    a = make_run(p, dev)
+    a.forward()
+    b = make_run(p, dev, max_chunk_rows=256)
+    b.forward_backward(grad_mean=torch.ones(1, device="cuda"))
+    torch.cuda.synchronize()
+    fa = a.flatness.view(torch.int32).cpu().numpy()
+    fb = b.flatness.view(torch.int32).cpu().numpy()
+    assert np.array_equal(fa, fb)
+    ref = O.forward(p)
+    from tests._gpu_helpers import check_flatness
+    check_flatness(a.flatness.cpu().numpy(), ref.flat, ref.valid)

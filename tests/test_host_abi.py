@@ -162,8 +162,20 @@ def test_workspace_size_grows_with_chunk_and_stays_below_logits(lib):
 
 def test_saved_bytes(lib):
     assert L.specloss_saved_bytes(0) == 0
-    assert L.specloss_saved_bytes(1) == 9 * 256
-    assert L.specloss_saved_bytes(1000) == 9 * 4096
+    assert L.specloss_saved_bytes(1) == 10 * 256
+    assert L.specloss_saved_bytes(1000) == 10 * 4096
+
+
+def test_saved_offsets(lib):
+    """Fields are consecutive 256-byte aligned arrays of N 4-byte values; bad fields are rejected."""
+    for n in (1, 1000, 4097):
+        stride = (n * 4 + 255) // 256 * 256
+        for f in range(10):
+            assert B.specloss_saved_offset(n, f) == f * stride
+        assert B.specloss_saved_offset(n, B.SAVED_FLATNESS) + n * 4 <= L.specloss_saved_bytes(n)
+    for bad in ((0, 0), (10, -1), (10, 10)):
+        with pytest.raises(B.SpecLossError):
+            B.specloss_saved_offset(*bad)
 
 
 def test_align_heads_validation(lib):
