@@ -1,11 +1,14 @@
 #!/usr/bin/env python3
-"""Benchmark of the streaming LM-head + cross-entropy step (forward + backward).
+"""Benchmark of the streaming LM-head + loss step (forward + backward).
 
-One step = the forward and backward of the mean loss over the whole batch at
-the Llama-3.1-8B shape (N = 32768 tokens of one 32k sequence, H = 4096,
-V = 128256, bf16 inputs, fp32 accumulation), inputs resident in HBM: the
-single call lmhead_loss_fwd_bwd (headline), and the two calls
-lmhead_loss_fwd + lmhead_loss_bwd (reported beside it).
+One step = the forward and backward of the mean loss over the whole batch,
+inputs resident in HBM: the single call lmhead_loss_fwd_bwd (headline), and
+the two calls lmhead_loss_fwd + lmhead_loss_bwd (reported beside it).  The
+default workload is label cross-entropy at the Llama-3.1-8B shape
+(N = 32768 tokens of one 32k sequence, H = 4096, V = 128256, bf16 inputs,
+fp32 accumulation); --workload selects another synthetic workload, e.g. the
+lk_hybrid divergence (lk_hybrid_bf16_8b) or the three-head ce + tv loss at
+the Llama-3.1-405B shape (multihead_bf16_405b).
 Prints one JSON line with tokens/s, the MFMA fractions, peak HBM, the
 roofline of the dominant kernel and the fp64 CPU oracle timed on a sample.
 """
@@ -36,8 +39,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also copy a buffer of known size (for counter calibration)")
-    ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic_ce_bf16_8b.json"),
-                    help="counter summary giving HBM bytes per launch")
+    ap.add_argument("--traffic", default=None,
+                    help="counter summary giving HBM bytes per launch "
+                         "(default profiles/traffic_<workload>.json)")
     return ap.parse_args()
 
 
@@ -95,19 +99,28 @@ def main():
     gen_s = time.time() - t0
     N, H, V = prob.n_rows, prob.hidden_dim, prob.vocab
 
+    if prob.dtype != "bf16":
+        print("bench.py times the bf16 workloads", file=sys.stderr)
+        sys.exit(2)
+
     def up(x):
+        if x is None:
+            return None
         return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    def up_i(x, dt):
+        return None if x is None else torch.from_numpy(np.ascontiguousarray(x).astype(dt)).to(dev)
 
     h = up(prob.hidden)
     W = up(prob.W)
-    labels = torch.from_numpy(prob.labels).to(dev)
-    mask = None if prob.mask is None else torch.from_numpy(prob.mask).to(dev)
+    inputs = dict(labels=up_i(prob.labels, np.int32), mask=up_i(prob.mask, np.uint8),
+                  target_hidden=up(prob.target_hidden), W_t=up(prob.W_t),
+                  target_row=up_i(prob.target_row, np.int32))
     torch.cuda.synchronize()
     torch.cuda.reset_peak_memory_stats()
     base_alloc = torch.cuda.memory_allocated()
 
-    run = LossRun(h, W, prob.weights, labels=labels, mask=mask, max_chunk_rows=args.chunk,
-                  want_terms=False)
+    run = LossRun(h, W, prob.weights, max_chunk_rows=args.chunk, want_terms=False, **inputs)
     dh = torch.empty((N, H), dtype=torch.float32, device=dev)
     dW = torch.empty((V, H), dtype=torch.float32, device=dev)
     gmean = torch.ones(1, dtype=torch.float32, device=dev)
@@ -146,20 +159,33 @@ def main():
     ms_two, ms_two_med, kernels_two, _ = timed(step_two, max(2, args.steps // 2), 1)
     peak_bytes = torch.cuda.max_memory_allocated()
 
-    # MFMA flops per step: single call 6NHV (forward, dh, dW); two calls 8NHV
-    # (forward, backward recompute, dh, dW).  Model flops: 6NHV.
+    # Executed MFMA flops per step: the library's own count for every
+    # contraction launch of the step (e.g. 6NHV for the single-call label
+    # cross-entropy: forward, dh, dW).  Model flops: one pass over the draft
+    # logits (2NHV), one over each distinct target row (2 N_t HV) and the two
+    # gradient contractions (4NHV), so that recompute cannot raise the fraction.
     nhv = float(N) * H * V
-    exec_flops = 6.0 * nhv
-    model_flops = 6.0 * nhv
+    n_t = 0
+    if prob.target_hidden is not None:
+        n_t = N if prob.target_row is None else int(prob.target_hidden.shape[0])
+    model_flops = 6.0 * nhv + 2.0 * n_t * H * V
+
+    def flops_per_step(ks):
+        return sum(v["work_per_launch"] * v["launches_per_step"] for v in ks.values()
+                   if v["is_flops"])
+
+    exec_flops = flops_per_step(kernels)
+    exec_two = flops_per_step(kernels_two)
     tflops = exec_flops / (ms_mean * 1e-3) / 1e12
     model_tflops = model_flops / (ms_mean * 1e-3) / 1e12
+    traffic_path = args.traffic or os.path.join(ROOT, "profiles", f"traffic_{args.workload}.json")
 
     dom = max(kernels, key=lambda k: kernels[k]["ms_total"])
     d = kernels[dom]
     achieved = d["work_per_launch"] / (d["ms_avg"] * 1e-3) / 1e12
     kern = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 1),
             "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
-            "traffic": load_traffic(args.traffic, dom), "flops_per_launch": d["work_per_launch"],
+            "traffic": load_traffic(traffic_path, dom), "flops_per_launch": d["work_per_launch"],
             "avg_launch_ms": round(d["ms_avg"], 4), "launches_per_step": d["launches_per_step"]}
 
     result = {
@@ -175,21 +201,22 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
-        "data": "synthetic (seeded; h ~ N(0,1), W ~ N(0,0.02), labels uniform)",
+        "data": f"synthetic (seeded; {prob.recipe})",
         "config": {"workload": args.workload, "tokens": N, "hidden": H, "vocab": V,
-                   "loss": "ce_label", "chunk_rows": args.chunk, "call": "lmhead_loss_fwd_bwd",
-                   "parallelism": "none (1 GPU)"},
+                   "loss": prob.weights, "chunk_rows": args.chunk,
+                   "call": "lmhead_loss_fwd_bwd", "parallelism": "none (1 GPU)"},
         "mfma_frac_executed": round(tflops / BF16_PEAK_TFLOPS, 4),
         "mfma_frac_model": round(model_tflops / BF16_PEAK_TFLOPS, 4),
         "executed_tflops": round(tflops, 1),
+        "executed_flops_per_step_over_nhv": round(exec_flops / nhv, 3),
         "peak_hbm_gib": round(peak_bytes / 2**30, 3),
         "peak_hbm_gib_above_inputs": round((peak_bytes - base_alloc) / 2**30, 3),
         "logits_sized_limit_gib": round(N * V * 2 / 2**30, 3),
         "workspace_gib": round(run.workspace.numel() / 2**30, 3),
         "roofline": kern,
         "two_calls": {"value": round(N / (ms_two * 1e-3), 1), "ms_per_step": round(ms_two, 3),
-                      "mfma_frac_executed": round(8.0 * nhv / (ms_two * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
-                      "mfma_frac_model": round(6.0 * nhv / (ms_two * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)},
+                      "mfma_frac_executed": round(exec_two / (ms_two * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+                      "mfma_frac_model": round(model_flops / (ms_two * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)},
         "kernels": {k: {"ms_per_step": round(v["ms_total"] / args.steps, 3),
                         "launches_per_step": v["launches_per_step"],
                         "tflops": round(v["work_per_launch"] / (v["ms_avg"] * 1e-3) / 1e12, 1)
@@ -203,7 +230,8 @@ def main():
     print(json.dumps(result), flush=True)
 
 
-FLOP_KERNELS = ("stats_q", "stats_p", "stats_stage", "div", "dz", "gemm_dh", "gemm_dW")
+FLOP_KERNELS = ("stats_q", "stats_p", "stats_stage", "div", "div_stage", "dz", "gemm_dh",
+                "gemm_dW")
 
 
 def summarize_trace(entries, steps):

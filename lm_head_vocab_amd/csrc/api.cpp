@@ -41,6 +41,7 @@ struct KindSet {
   bool target = false;  // any kind needing the target side
   bool pass2 = false;   // any divergence needing a second sweep
   bool dual_bwd = false;
+  bool stage_div = false;  // single call: pass 2 stages q and q - p (no rkl / jsd)
   uint32_t need = 0;    // SUM_* bits
 };
 
@@ -59,6 +60,7 @@ KindSet kinds_of(const float* w) {
   if (k.need) k.need |= SUM_ALPHA;  // alpha is reported whenever a second sweep runs
   k.pass2 = k.need != 0;
   k.dual_bwd = (k.active & ~((1u << SPECLOSS_CE_LABEL) | (1u << SPECLOSS_CE_ARGMAX_P))) != 0;
+  k.stage_div = k.dual_bwd && !on(SPECLOSS_RKL) && !on(SPECLOSS_JSD);
   return k;
 }
 
@@ -112,7 +114,7 @@ struct Layout {
   // backward
   size_t wt, ht, dz, dzt, bwd_end;
   // single-call forward+backward: forward partials and backward buffers at once
-  size_t f_pz, f_pu, f_zy, f_wt, f_ht, f_dz, f_dzt, fused_end;
+  size_t f_pz, f_pu, f_p2, f_zy, f_wt, f_ht, f_dz, f_dd, f_dzt, fused_end;
 };
 
 Layout plan(const specloss_problem* p, const KindSet& k, int64_t Nc) {
@@ -149,10 +151,12 @@ Layout plan(const specloss_problem* p, const KindSet& k, int64_t Nc) {
   o = L.head_end;
   L.f_pz = take(2 * tile_cols);
   L.f_pu = take(k.target ? 4 * tile_cols : 0);
+  L.f_p2 = take(k.stage_div ? (size_t)kNumSums * tile_cols : 0);
   L.f_zy = take(2 * (size_t)Nc * 4);
   L.f_wt = take((size_t)L.H * L.Vp * L.es);
   L.f_ht = take((size_t)L.H * Nc * L.es);
   L.f_dz = take((size_t)Nc * L.Vp * L.es);
+  L.f_dd = take(k.stage_div ? (size_t)Nc * L.Vp * L.es : 0);
   L.f_dzt = take((size_t)L.Vp * Nc * L.es);
   L.fused_end = o;
   return L;
@@ -227,12 +231,12 @@ GemmOperand target_operand(const specloss_problem* p, int64_t r0, int64_t rows, 
 enum KernelId : int32_t {
   K_VALIDITY, K_STATS_Q, K_STATS_P, K_COMBINE1, K_ROWDOT, K_DIV, K_COMBINE2, K_REDUCE, K_COPY,
   K_SEED, K_TRANSPOSE_W, K_TRANSPOSE_H, K_DZ, K_GEMM_DH, K_GEMM_DW, K_STATS_STAGE, K_DZ_STAGE,
-  K_NUM_IDS
+  K_DIV_STAGE, K_DZ_DIV, K_NUM_IDS
 };
 const char* const kKernelNames[K_NUM_IDS] = {
     "validity", "stats_q", "stats_p", "combine1", "rowdot", "div", "combine2", "reduce",
     "copy_lse", "seed", "transpose_W", "transpose_h", "dz", "gemm_dh", "gemm_dW",
-    "stats_stage", "dz_stage"};
+    "stats_stage", "dz_stage", "div_stage", "dz_div"};
 
 // Brackets launches with the trace's events when the problem carries one.
 struct Tracer {
@@ -279,7 +283,7 @@ namespace {
 
 struct FwdBufs {
   float* pz;   // q-side partials [2][Tv][Nc]
-  float* pu;   // p-side partials [3][Tv][Nc]
+  float* pu;   // p-side partials [4][Tv][Nc]
   float* p2;   // pass-2 partials [kNumSums][Tv][Nc]
   float* zy;   // gathered logits [2][Nc]
   int64_t Nc;
@@ -303,12 +307,14 @@ int launch_validity_for(const specloss_problem* p, const KindSet& k, const Saved
   return SPECLOSS_OK;
 }
 
-// Forward of chunk rows [r0, r0 + rows): pass 1 (q side, staged into `stage`
-// when given; p side with argmax), merge, label-logit gather, pass 2 and the
-// per-row losses.
+// Forward of chunk rows [r0, r0 + rows): pass 1 (q side; p side with argmax
+// and flatness), merge, label-logit gather, pass 2 and the per-row losses.
+// Staging for the logit gradient ([Nc][Vp] buffers): with `stage` alone,
+// pass 1 stores e = exp(z - m_tile) there; with `stage` and `stage_d`,
+// pass 2 stores q there and q - p in stage_d.
 int fwd_chunk(const specloss_problem* p, const KindSet& k, const Layout& L, const FwdBufs& b,
               const SavedView& sv, float* loss, float* terms, int64_t r0, int64_t rows,
-              void* stage, Tracer& tr, hipStream_t stream) {
+              void* stage, void* stage_d, Tracer& tr, hipStream_t stream) {
   const bool bf16 = p->in_dtype == SPECLOSS_BF16;
   const int64_t H = L.H, Nc = b.Nc;
   const int64_t tile_cols = L.Tv * Nc;
@@ -327,7 +333,7 @@ int fwd_chunk(const specloss_problem* p, const KindSet& k, const Layout& L, cons
   sz.ps = b.pz + tile_cols;
   sz.pi = nullptr;
   sz.pq = nullptr;
-  if (stage) {
+  if (stage && !stage_d) {
     StatsStageLaunch ss;
     ss.st = sz;
     ss.stage = stage;
@@ -400,7 +406,11 @@ int fwd_chunk(const specloss_problem* p, const KindSet& k, const Layout& L, cons
     dv.need = k.need;
     dv.part = b.p2;
     dv.part_stride = tile_cols;
-    TRACED(tr, K_DIV, 4.0 * rows * H * p->vocab, launch_div(bf16, dv, stream));
+    dv.stage_q = stage_d ? stage : nullptr;
+    dv.stage_d = stage_d;
+    dv.ld_stage = L.Vp;
+    TRACED(tr, stage_d ? K_DIV_STAGE : K_DIV, 4.0 * rows * H * p->vocab,
+           launch_div(bf16, dv, stream));
   }
 
   Combine2Launch c2;
@@ -579,7 +589,7 @@ int lmhead_loss_fwd(const specloss_problem* p, void* workspace, size_t ws_bytes,
   TRY(launch_validity_for(p, k, sv, counts, tr, stream));
   for (int64_t r0 = 0; r0 < N; r0 += Nc) {
     const int64_t rows = (N - r0) < Nc ? (N - r0) : Nc;
-    TRY(fwd_chunk(p, k, L, b, sv, loss, terms, r0, rows, nullptr, tr, stream));
+    TRY(fwd_chunk(p, k, L, b, sv, loss, terms, r0, rows, nullptr, nullptr, tr, stream));
   }
   if (reduced) TRY(launch_reduce_for(p, k, loss, terms, counts, reduced, tr, stream));
   if (lse_q)
@@ -663,8 +673,8 @@ int lmhead_loss_fwd_bwd(const specloss_problem* p, void* workspace, size_t ws_by
   TRY(check_fwd_outputs(loss, term_loss, lse_q, saved, counts, reduced));
   TRY(check_bwd_args(grad_loss, grad_mean, dhidden, dh_dtype, dW));
   if (!workspace || !aligned(workspace, kAlign)) return SPECLOSS_E_WORKSPACE;
-  if (k.dual_bwd) {
-    // kinds whose gradient needs the target distribution: the forward and
+  if (k.dual_bwd && !k.stage_div) {
+    // rkl / jsd gradients need log p and log m per element: the forward and
     // backward sequences run back to back on the same workspace
     char* ws = static_cast<char*>(workspace);
     const Layout L0 = plan(p, k, kChunkQuantum);
@@ -675,7 +685,8 @@ int lmhead_loss_fwd_bwd(const specloss_problem* p, void* workspace, size_t ws_by
                            dh_dtype, dW, accumulate_dW, stream);
   }
   // label / argmax cross-entropies: pass 1 stages e = exp(z - m_tile) per
-  // chunk, the logit gradient is formed from it without recomputing logits
+  // chunk; with kl_div / tv / nla / lk_hybrid, pass 2 stages q and q - p.  The
+  // logit gradient is formed from the staged values without recomputing logits.
   const int64_t Nc = pick_chunk(p, k, ws_bytes, REGION_FUSED);
   if (Nc <= 0) return SPECLOSS_E_WORKSPACE;
   const Layout L = plan(p, k, Nc);
@@ -686,10 +697,12 @@ int lmhead_loss_fwd_bwd(const specloss_problem* p, void* workspace, size_t ws_by
   float* terms = term_loss ? term_loss : reinterpret_cast<float*>(ws + L.terms);
   float* seed = reinterpret_cast<float*>(ws + L.seed);
   const FwdBufs b{reinterpret_cast<float*>(ws + L.f_pz), reinterpret_cast<float*>(ws + L.f_pu),
-                  nullptr, reinterpret_cast<float*>(ws + L.f_zy), Nc};
+                  k.stage_div ? reinterpret_cast<float*>(ws + L.f_p2) : nullptr,
+                  reinterpret_cast<float*>(ws + L.f_zy), Nc};
   void* wt = ws + L.f_wt;
   void* ht = ws + L.f_ht;
   void* dz = ws + L.f_dz;
+  void* dd = k.stage_div ? ws + L.f_dd : nullptr;
   void* dzt = ws + L.f_dzt;
   Tracer tr{p->trace, stream};
 
@@ -700,7 +713,7 @@ int lmhead_loss_fwd_bwd(const specloss_problem* p, void* workspace, size_t ws_by
   int chunk = 0;
   for (int64_t r0 = 0; r0 < N; r0 += Nc, ++chunk) {
     const int64_t rows = (N - r0) < Nc ? (N - r0) : Nc;
-    TRY(fwd_chunk(p, k, L, b, sv, loss, terms, r0, rows, dz, tr, stream));
+    TRY(fwd_chunk(p, k, L, b, sv, loss, terms, r0, rows, dz, dd, tr, stream));
     DzStageLaunch ds;
     ds.tiles_m = (int32_t)L.Tv;
     ds.ncols = (int32_t)rows;
@@ -712,12 +725,17 @@ int lmhead_loss_fwd_bwd(const specloss_problem* p, void* workspace, size_t ws_by
     ds.sv = sv;
     ds.w_lab = p->weights[SPECLOSS_CE_LABEL];
     ds.w_arg = p->weights[SPECLOSS_CE_ARGMAX_P];
+    ds.w_kl = p->weights[SPECLOSS_KL];
+    ds.w_tv = p->weights[SPECLOSS_TV];
+    ds.w_nla = p->weights[SPECLOSS_NLA];
+    ds.w_lk = p->weights[SPECLOSS_LK_HYBRID];
+    ds.dd = dd;
     ds.dz = dz;
     ds.ld_dz = Vp;
     ds.dzt = dzt;
     ds.ld_dzt = Nc;
     ds.row_blocks = (int32_t)(cdiv(rows, 256) * 4);
-    TRACED(tr, K_DZ_STAGE, (double)ds.row_blocks * 64 * Vp * L.es * 3,
+    TRACED(tr, dd ? K_DZ_DIV : K_DZ_STAGE, (double)ds.row_blocks * 64 * Vp * L.es * (dd ? 4 : 3),
            launch_dz_stage(bf16, ds, stream));
     const void* hc = offset_rows(p->hidden_states, r0, H, L.es);
     if (dW)

@@ -96,6 +96,20 @@ __device__ __forceinline__ void store1<float>(float* dst, float x) {
   *dst = x;
 }
 
+// 16 bytes of T (8 bf16 or 4 fp32) widened to fp32
+template <typename T, int KC>
+__device__ __forceinline__ void load_chunk(const T* src, float (&out)[KC]) {
+  const i32x4_t raw = *reinterpret_cast<const i32x4_t*>(src);
+  if constexpr (sizeof(T) == 2) {
+    const bf16x8_t b = __builtin_bit_cast(bf16x8_t, raw);
+#pragma unroll
+    for (int q = 0; q < KC; ++q) out[q] = (float)b[q];
+  } else {
+#pragma unroll
+    for (int q = 0; q < KC; ++q) out[q] = __int_as_float(raw[q]);
+  }
+}
+
 // ============================================================================
 // pass 1: per-tile softmax statistics
 // ============================================================================
@@ -291,10 +305,17 @@ __global__ __launch_bounds__(kThreads, 1) void k_stats_stage(StatsStageLaunch a)
   }
 }
 
-// dz from the staged e, one workgroup per (256-wide vocabulary tile, 64 rows):
+// dz from staged values, one workgroup per (256-wide vocabulary tile, 64 rows):
 // rows are read and written back coalesced (16 bytes per lane), and the
 // block is transposed through LDS into dz^T.
-template <typename T>
+//   DIV = false: the buffer holds e = exp(z - m_tile) (label / argmax
+//                cross-entropies only).
+//   DIV = true:  the buffer holds q and `dd` holds d = q - p; with
+//                c = [q < p] (1/2 on ties) read from the sign of d,
+//                dz = seed (A q + B d - C q (c - S) - w_lab [v = y_lab] - w_arg [v = y_arg])
+//                where A = w_lab + w_arg, B = w_kl + w_lk lam,
+//                C = w_tv + w_nla / alpha + w_lk (1 - lam), lam = exp(-3 alpha).
+template <typename T, bool DIV>
 __global__ __launch_bounds__(256) void k_dz_stage(DzStageLaunch a) {
   constexpr int VT = kVocabTile, RB = 64;
   constexpr int KC = ElemTraits<T>::kPerChunk;       // elements per 16 bytes
@@ -311,24 +332,27 @@ __global__ __launch_bounds__(256) void k_dz_stage(DzStageLaunch a) {
     const int c = rb * RB + rr;                    // chunk row
     const int v0 = vt * VT + ch * KC;
     T* p = dz + (int64_t)c * a.ld_dz + v0;
-    const i32x4_t raw = *reinterpret_cast<const i32x4_t*>(p);
-    float e[KC];
-    if constexpr (sizeof(T) == 2) {
-      const bf16x8_t b = __builtin_bit_cast(bf16x8_t, raw);
-#pragma unroll
-      for (int q = 0; q < KC; ++q) e[q] = (float)b[q];
-    } else {
-#pragma unroll
-      for (int q = 0; q < KC; ++q) e[q] = __int_as_float(raw[q]);
-    }
-    float sd = 0.0f, scale = 0.0f;
+    float e[KC], dd[KC];
+    load_chunk<T, KC>(p, e);
+    if (DIV) load_chunk<T, KC>(static_cast<const T*>(a.dd) + (int64_t)c * a.ld_dz + v0, dd);
+    float sd = 0.0f, scale = 0.0f, cb = 0.0f, cc = 0.0f, S = 0.0f;
     int yl = -1, ya = -1;
     if (c < a.ncols) {
       const int64_t gr = a.r0 + c;
       sd = a.seed[gr];
       if (sd != 0.0f) {
-        scale = sd * (a.w_lab + a.w_arg) *
-                fast_exp2((a.pm[(int64_t)vt * a.ldp + c] - a.sv.lse_q[gr]) * kLog2e);
+        if (DIV) {
+          const float alpha = a.sv.alpha[gr];
+          const float lam = __expf(-3.0f * alpha);
+          scale = sd * (a.w_lab + a.w_arg);
+          cb = sd * (a.w_kl + a.w_lk * lam);
+          cc = sd * (a.w_tv + (a.w_nla != 0.0f ? a.w_nla / alpha : 0.0f) +
+                     a.w_lk * (1.0f - lam));
+          S = a.sv.S[gr];
+        } else {
+          scale = sd * (a.w_lab + a.w_arg) *
+                  fast_exp2((a.pm[(int64_t)vt * a.ldp + c] - a.sv.lse_q[gr]) * kLog2e);
+        }
         yl = a.sv.y_label[gr];
         ya = a.sv.y_arg[gr];
       }
@@ -338,6 +362,10 @@ __global__ __launch_bounds__(256) void k_dz_stage(DzStageLaunch a) {
     for (int q = 0; q < KC; ++q) {
       const int v = v0 + q;
       float x = e[q] * scale;
+      if (DIV) {
+        const float ci = dd[q] < 0.0f ? 1.0f : (dd[q] == 0.0f ? 0.5f : 0.0f);
+        x = fmaf(cb, dd[q], x) - cc * e[q] * (ci - S);
+      }
       if (v == yl) x -= sd * a.w_lab;
       if (v == ya) x -= sd * a.w_arg;
       d[q] = (sd != 0.0f && v < a.vocab) ? x : 0.0f;
@@ -379,7 +407,10 @@ __global__ __launch_bounds__(256) void k_dz_stage(DzStageLaunch a) {
 // ============================================================================
 // pass 2: divergence sums with the final logsumexps
 // ============================================================================
-template <typename T>
+// STAGE: also store q and d = q - p of every (row, vocab) for the logit
+// gradient (rounded to the storage type; d keeps the sign of q - p, zero on
+// ties, so the indicator [q < p] is unchanged by the rounding).
+template <typename T, bool STAGE>
 __global__ __launch_bounds__(kThreads, 1) void k_div(DivLaunch a) {
   using Cfg = TileCfg<T, 256, 128>;
   __shared__ __attribute__((aligned(16))) char smem[Cfg::LDS_BYTES];
@@ -403,19 +434,25 @@ __global__ __launch_bounds__(kThreads, 1) void k_div(DivLaunch a) {
   float sums[Cfg::FN][kNumSums];
 #pragma unroll
   for (int j = 0; j < Cfg::FN; ++j) {
-    const int col = min(tn * Cfg::BN + wn * Cfg::WN + j * kFrag + frag_col(lane), a.ncols - 1);
+    const int c_tile = tn * Cfg::BN + wn * Cfg::WN + j * kFrag + frag_col(lane);  // chunk row
+    const int col = min(c_tile, a.ncols - 1);
     const float lq0 = a.lse_q[col], lp0 = a.lse_p[col];
     float s_alpha = 0.f, s_s = 0.f, s_kl = 0.f, s_rkl = 0.f, s_jsd = 0.f, s_eqg = 0.f;
 #pragma unroll
-    for (int i = 0; i < Cfg::FM; ++i)
+    for (int i = 0; i < Cfg::FM; ++i) {
+      float sq[4], sd[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int v = v_base + i * kFrag + frag_row(r, lane);
+        sq[r] = 0.0f;
+        sd[r] = 0.0f;
         if (tail && v >= a.vocab) continue;
         const float lq = az[i][j][r] - lq0;
         const float lp = au[i][j][r] - lp0;
         const float q = fast_exp2(lq * kLog2e);
         const float p = fast_exp2(lp * kLog2e);
+        sq[r] = q;
+        sd[r] = q - p;
         if (need & SUM_ALPHA) s_alpha += fminf(p, q);
         if (need & SUM_S) s_s += (q < p) ? q : ((q == p) ? 0.5f * q : 0.0f);
         if (need & SUM_KL) s_kl += p * (lp - lq);
@@ -426,6 +463,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_div(DivLaunch a) {
           if (need & SUM_EQG) s_eqg += 0.5f * q * (lq - lm);
         }
       }
+      if (STAGE) {
+        const int64_t o = (int64_t)c_tile * a.ld_stage + v_base + i * kFrag + frag_row(0, lane);
+        store4<T>(static_cast<T*>(a.stage_q) + o, sq[0], sq[1], sq[2], sq[3]);
+        store4<T>(static_cast<T*>(a.stage_d) + o, sd[0], sd[1], sd[2], sd[3]);
+      }
+    }
     const float v6[kNumSums] = {s_alpha, s_s, s_kl, s_rkl, s_jsd, s_eqg};
 #pragma unroll
     for (int f = 0; f < kNumSums; ++f) sums[j][f] = col_sum(v6[f], lane);
@@ -940,15 +983,26 @@ hipError_t launch_stats_stage(bool bf16, const StatsStageLaunch& a, hipStream_t 
 
 hipError_t launch_dz_stage(bool bf16, const DzStageLaunch& a, hipStream_t s) {
   const dim3 grid((unsigned)(a.tiles_m * a.row_blocks)), block(256);
-  if (bf16) hipLaunchKernelGGL(k_dz_stage<bf16_bits>, grid, block, 0, s, a);
-  else hipLaunchKernelGGL(k_dz_stage<float>, grid, block, 0, s, a);
+  if (bf16) {
+    if (a.dd) hipLaunchKernelGGL((k_dz_stage<bf16_bits, true>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((k_dz_stage<bf16_bits, false>), grid, block, 0, s, a);
+  } else {
+    if (a.dd) hipLaunchKernelGGL((k_dz_stage<float, true>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((k_dz_stage<float, false>), grid, block, 0, s, a);
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_div(bool bf16, const DivLaunch& a, hipStream_t s) {
   const dim3 grid(grid_for_tiles(a.tiles_m * a.tiles_n)), block(kThreads);
-  if (bf16) hipLaunchKernelGGL(k_div<bf16_bits>, grid, block, 0, s, a);
-  else hipLaunchKernelGGL(k_div<float>, grid, block, 0, s, a);
+  const bool stage = a.stage_q != nullptr;
+  if (bf16) {
+    if (stage) hipLaunchKernelGGL((k_div<bf16_bits, true>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((k_div<bf16_bits, false>), grid, block, 0, s, a);
+  } else {
+    if (stage) hipLaunchKernelGGL((k_div<float, true>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((k_div<float, false>), grid, block, 0, s, a);
+  }
   return hipGetLastError();
 }
 

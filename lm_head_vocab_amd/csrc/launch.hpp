@@ -64,17 +64,22 @@ struct StatsStageLaunch {
 };
 hipError_t launch_stats_stage(bool bf16, const StatsStageLaunch& a, hipStream_t s);
 
-// logit gradient of the label / argmax cross-entropies from the staged e:
-// dz = seed * ((w_lab + w_arg) e exp(m_tile - lse) - w_lab [v == y_lab] - w_arg [v == y_arg]),
-// written over e and, transposed, into dzt ([Vp][cap])
+// logit gradient from staged values, written over them and, transposed, into
+// dzt ([Vp][cap]).  Without dd (label / argmax cross-entropies) the buffer
+// holds e = exp(z - m_tile):
+//   dz = seed * ((w_lab + w_arg) e exp(m_tile - lse) - w_lab [v == y_lab] - w_arg [v == y_arg]);
+// with dd it holds q and dd holds q - p, and the divergence terms
+// (kl_div, tv, nla, lk_hybrid) are added from the saved alpha and S.
 struct DzStageLaunch {
   int32_t tiles_m, ncols, vocab, ldp;
   int64_t r0;
-  const float* pm;     // chunk partial maxima [tiles_m][ldp]
+  const float* pm;     // chunk partial maxima [tiles_m][ldp] (e mode only)
   const float* seed;   // [N], global rows
   SavedView sv;        // global rows
   float w_lab, w_arg;
-  void* dz;            // in: e, out: dz; [cap][Vp]
+  float w_kl, w_tv, w_nla, w_lk;  // divergence weights (dd mode only)
+  const void* dd;      // [cap][Vp] q - p, or null
+  void* dz;            // in: e or q, out: dz; [cap][Vp]
   int64_t ld_dz;
   void* dzt;           // [Vp][cap]
   int64_t ld_dzt;
@@ -90,6 +95,9 @@ struct DivLaunch {
   uint32_t need;
   float* part;          // [kNumSums][tiles_m][ldp]
   int64_t part_stride;  // tiles_m * ldp
+  void* stage_q;        // null, or [cap][ld_stage]: q of every (chunk row, vocab)
+  void* stage_d;        // [cap][ld_stage]: q - p (with stage_q)
+  int64_t ld_stage;
 };
 hipError_t launch_div(bool bf16, const DivLaunch& a, hipStream_t s);
 

@@ -46,8 +46,8 @@ def trace_name(kernel: str) -> str:
              "k_rowdot": "rowdot", "k_transpose": "transpose", "k_validity": "validity",
              "k_reduce": "reduce", "k_seed": "seed", "k_align": "align"}
     name = names.get(base, base)
-    if base == "k_stats" and "true" in targs:
-        name = "stats_p"
+    if "true" in targs:
+        name = {"k_stats": "stats_p", "k_div": "div_stage", "k_dz_stage": "dz_div"}.get(base, name)
     return name
 
 

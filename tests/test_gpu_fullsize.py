@@ -49,7 +49,9 @@ def _sample_rows(n, seed):
 @pytest.mark.parametrize("name,single", [("ce_bf16_1b", False), ("ce_bf16_8b", False),
                                          ("lk_hybrid_bf16_8b", False),
                                          ("multihead_bf16_405b", False),
-                                         ("ce_bf16_1b", True), ("ce_bf16_8b", True)])
+                                         ("ce_bf16_1b", True), ("ce_bf16_8b", True),
+                                         ("lk_hybrid_bf16_8b", True),
+                                         ("multihead_bf16_405b", True)])
 def test_full_size_sampled(name, single):
     """single: the same checks through the single call lmhead_loss_fwd_bwd."""
     prob = synthetic.make_problem(name)

@@ -255,6 +255,63 @@ def test_single_call_forward_backward(case):
     full_parity(p, max_chunk_rows=ch, tag=f"single-{case}", single_call=True)
 
 
+@pytest.mark.parametrize("kind", ["kl_div", "tv", "nla", "lk_hybrid", "rkl", "jsd"])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_single_call_each_divergence(kind, dtype):
+    """Single call per divergence kind over two chunks (the second ragged).
+
+    kl_div, tv, nla and lk_hybrid take the staged path (pass 2 stores q and
+    q - p, the logit gradient is formed from them); rkl and jsd run the
+    forward and backward back to back.
+    """
+    p = synthetic.make_problem("lk_hybrid_bf16_8b", n_rows=280, hidden_dim=128, vocab=600,
+                               weights={kind: 1.0, "ce_label": 0.25})
+    rng = np.random.default_rng(5)
+    p.labels = rng.integers(0, p.vocab, p.n_rows).astype(np.int32)
+    p.mask = (np.arange(p.n_rows) % 7 != 3).astype(np.uint8)
+    if dtype == "f32":
+        p.dtype = "f32"
+        for f in ("hidden", "W", "target_hidden", "W_t"):
+            setattr(p, f, synthetic.bf16_bits_to_f32(getattr(p, f)).copy())
+    full_parity(p, max_chunk_rows=256, tag=f"single-{kind}-{dtype}", single_call=True)
+
+
+def test_single_call_identical_target_ties():
+    """Draft and target identical: p == q exactly, every vocabulary entry is a tie.
+
+    The indicator [q < p] is 1/2 on ties on both sides, so alpha = 1, S = 1/2
+    and the tv and kl gradients vanish; only the label cross-entropy is left.
+    """
+    p = synthetic.make_problem("lk_hybrid_bf16_8b", n_rows=300, hidden_dim=128, vocab=700,
+                               weights={"tv": 1.0, "kl_div": 0.5, "ce_label": 1.0})
+    p.W_t = p.W.copy()
+    p.target_hidden = p.hidden.copy()
+    rng = np.random.default_rng(6)
+    p.labels = rng.integers(0, p.vocab, p.n_rows).astype(np.int32)
+    out = full_parity(p, tag="single-ties", single_call=True)
+    run = out["run"]
+    assert np.allclose(run.saved_field(4).cpu().numpy(), 1.0, atol=1e-5)  # alpha
+    assert np.allclose(run.saved_field(5).cpu().numpy(), 0.5, atol=1e-5)  # S
+
+
+def test_single_call_divergence_matches_two_calls():
+    """Staged-divergence single call against the two calls: same losses bit for bit
+    (the forward kernels are the same), gradients within the bar of each other."""
+    p = synthetic.make_problem("lk_hybrid_bf16_8b", n_rows=700, hidden_dim=128, vocab=900)
+    dev = to_device(p)
+    gm = torch.ones(1, device="cuda")
+    a = make_run(p, dev, max_chunk_rows=256)
+    dh1, dW1 = a.forward_backward(grad_mean=gm)
+    b = make_run(p, dev, max_chunk_rows=256)
+    b.forward()
+    dh2, dW2 = b.backward(grad_mean=gm)
+    torch.cuda.synchronize()
+    assert torch.equal(a.loss, b.loss)
+    assert torch.equal(a.reduced, b.reduced)
+    assert rel_frob(dh1.cpu().numpy(), dh2.cpu().numpy()) < 1e-2
+    assert rel_frob(dW1.cpu().numpy(), dW2.cpu().numpy()) < 1e-2
+
+
 def test_single_call_matches_two_calls_and_repeats():
     p = synthetic.make_problem("ce_bf16_1b", n_rows=700, hidden_dim=128, vocab=900)
     dev = to_device(p)
