@@ -35,6 +35,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="ce_bf16_8b")
     ap.add_argument("--chunk", type=int, default=8192, help="max rows per chunk")
+    ap.add_argument("--shards", type=int, default=1,
+                    help="G > 1: time one vocabulary shard's calls (V/G rows of W) and the "
+                         "merges, i.e. one device's step of a G-way vocabulary-parallel group")
     ap.add_argument("--cpu-sample-rows", type=int, default=64)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -84,7 +87,7 @@ def main():
 
     import synthetic
     import lm_head_vocab_amd as L
-    from lm_head_vocab_amd.runner import LossRun
+    from lm_head_vocab_amd.runner import LossRun, ShardedLossRun
 
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
@@ -120,18 +123,42 @@ def main():
     torch.cuda.reset_peak_memory_stats()
     base_alloc = torch.cuda.memory_allocated()
 
-    run = LossRun(h, W, prob.weights, max_chunk_rows=args.chunk, want_terms=False, **inputs)
     dh = torch.empty((N, H), dtype=torch.float32, device=dev)
     dW = torch.empty((V, H), dtype=torch.float32, device=dev)
     gmean = torch.ones(1, dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
-
-    def step_single():
-        run.forward_backward(grad_mean=gmean, dhidden=dh, dW=dW, stream=stream)
-
-    def step_two():
+    G = args.shards
+    if G > 1:
+        # every shard runs once so the exchange holds real records; the timed
+        # step is shard 0's calls plus the merges (one device's share)
+        run = ShardedLossRun(h, W, prob.weights, G, max_chunk_rows=args.chunk, **inputs)
         run.forward(stream)
         run.backward(grad_mean=gmean, dhidden=dh, dW=dW, stream=stream)
+        p0, s0 = run.problems[0], run.shards[0]
+        v_shard = run.bounds[1]
+        dh_part = torch.empty((N, H), dtype=torch.float32, device=dev)
+        terms = torch.empty(L.binding.NUM_KINDS, N, dtype=torch.float32, device=dev)
+
+        def step_single():
+            B = L.binding
+            B.lmhead_shard_pass1(p0, s0, run.workspace, stream)
+            B.lmhead_shard_merge1(p0, s0, run.saved, run.counts, stream)
+            B.lmhead_shard_pass2(p0, s0, run.saved, run.workspace, stream)
+            B.lmhead_shard_merge2(p0, s0, run.saved, run.counts, run.loss, terms, None,
+                                  run.reduced, stream)
+            B.lmhead_shard_bwd(p0, s0, None, gmean, run.counts, run.saved, run.workspace,
+                               dh_part, dW[:v_shard], False, stream)
+        step_two = None
+    else:
+        run = LossRun(h, W, prob.weights, max_chunk_rows=args.chunk, want_terms=False, **inputs)
+        v_shard = V
+
+        def step_single():
+            run.forward_backward(grad_mean=gmean, dhidden=dh, dW=dW, stream=stream)
+
+        def step_two():
+            run.forward(stream)
+            run.backward(grad_mean=gmean, dhidden=dh, dW=dW, stream=stream)
 
     def timed(step, steps, warmup):
         for _ in range(warmup):
@@ -156,7 +183,8 @@ def main():
         return sum(per) / steps, per[len(per) // 2], kernels, wall
 
     ms_mean, ms_med, kernels, wall = timed(step_single, args.steps, args.warmup)
-    ms_two, ms_two_med, kernels_two, _ = timed(step_two, max(2, args.steps // 2), 1)
+    if step_two is not None:
+        ms_two, ms_two_med, kernels_two, _ = timed(step_two, max(2, args.steps // 2), 1)
     peak_bytes = torch.cuda.max_memory_allocated()
 
     # Executed MFMA flops per step: the library's own count for every
@@ -164,18 +192,17 @@ def main():
     # cross-entropy: forward, dh, dW).  Model flops: one pass over the draft
     # logits (2NHV), one over each distinct target row (2 N_t HV) and the two
     # gradient contractions (4NHV), so that recompute cannot raise the fraction.
-    nhv = float(N) * H * V
+    nhv = float(N) * H * v_shard
     n_t = 0
     if prob.target_hidden is not None:
         n_t = N if prob.target_row is None else int(prob.target_hidden.shape[0])
-    model_flops = 6.0 * nhv + 2.0 * n_t * H * V
+    model_flops = 6.0 * nhv + 2.0 * n_t * H * v_shard
 
     def flops_per_step(ks):
         return sum(v["work_per_launch"] * v["launches_per_step"] for v in ks.values()
                    if v["is_flops"])
 
     exec_flops = flops_per_step(kernels)
-    exec_two = flops_per_step(kernels_two)
     tflops = exec_flops / (ms_mean * 1e-3) / 1e12
     model_tflops = model_flops / (ms_mean * 1e-3) / 1e12
     traffic_path = args.traffic or os.path.join(ROOT, "profiles", f"traffic_{args.workload}.json")
@@ -204,7 +231,10 @@ def main():
         "data": f"synthetic (seeded; {prob.recipe})",
         "config": {"workload": args.workload, "tokens": N, "hidden": H, "vocab": V,
                    "loss": prob.weights, "chunk_rows": args.chunk,
-                   "call": "lmhead_loss_fwd_bwd", "parallelism": "none (1 GPU)"},
+                   "call": "lmhead_loss_fwd_bwd" if G == 1 else
+                   "lmhead_shard_pass1/merge1/pass2/merge2/bwd of shard 0",
+                   "parallelism": "none (1 GPU)" if G == 1 else
+                   f"vocab shard 0 of {G} (rows 0..{v_shard}), exchanges not timed"},
         "mfma_frac_executed": round(tflops / BF16_PEAK_TFLOPS, 4),
         "mfma_frac_model": round(model_tflops / BF16_PEAK_TFLOPS, 4),
         "executed_tflops": round(tflops, 1),
@@ -214,9 +244,11 @@ def main():
         "logits_sized_limit_gib": round(N * V * 2 / 2**30, 3),
         "workspace_gib": round(run.workspace.numel() / 2**30, 3),
         "roofline": kern,
-        "two_calls": {"value": round(N / (ms_two * 1e-3), 1), "ms_per_step": round(ms_two, 3),
-                      "mfma_frac_executed": round(exec_two / (ms_two * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
-                      "mfma_frac_model": round(model_flops / (ms_two * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)},
+        "two_calls": None if step_two is None else {
+            "value": round(N / (ms_two * 1e-3), 1), "ms_per_step": round(ms_two, 3),
+            "mfma_frac_executed": round(flops_per_step(kernels_two) / (ms_two * 1e-3) / 1e12
+                                        / BF16_PEAK_TFLOPS, 4),
+            "mfma_frac_model": round(model_flops / (ms_two * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)},
         "kernels": {k: {"ms_per_step": round(v["ms_total"] / args.steps, 3),
                         "launches_per_step": v["launches_per_step"],
                         "tflops": round(v["work_per_launch"] / (v["ms_avg"] * 1e-3) / 1e12, 1)

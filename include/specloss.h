@@ -219,6 +219,75 @@ int specloss_align_heads(int64_t seq_len, int64_t batch, int32_t n_heads, const 
                          hipStream_t stream);
 
 /*
+ * Vocabulary-parallel variant (blog, "Backward pass": the loss is orthogonal
+ * to the surrounding parallelism; the vocabulary split is the tensor-parallel
+ * layout of the LM head).  Each of G shards owns rows
+ * [vocab_offset, vocab_offset + p->vocab) of W (and of W_t): the problem
+ * passed to the shard calls is the full problem with W / W_t pointing at the
+ * shard's rows and `vocab` the shard's row count; labels stay global indices.
+ * The shards exchange per-row records through `exchange`
+ * (specloss_exchange_bytes(N, G) bytes, record g written only by shard g; on
+ * several GPUs each would hold a copy filled by an all-gather).  Order:
+ *   1. every shard: lmhead_shard_pass1   (its tiles -> record g, part 1)
+ *   2. once:        lmhead_shard_merge1  (validity, lse_q, lse_p, argmax p,
+ *                                         flatness into `saved`; counts)
+ *   3. every shard: lmhead_shard_pass2   (label / argmax logits and the
+ *                                         divergence sums of its tiles -> record g, part 2)
+ *   4. once:        lmhead_shard_merge2  (per-row losses, means, saved alpha ...)
+ *   5. every shard: lmhead_shard_bwd     (its dW rows; its fp32 partial of dh)
+ *   6. once:        specloss_sum_partials over the G dh partials
+ * Records are merged in shard order with the same fixed-order rules as the
+ * tiles of one call, so the results equal lmhead_loss_fwd / _bwd on the whole
+ * head up to the rounding of the merges.  Workspace: lmhead_loss_workspace_size
+ * of the shard problem.  Errors: SPECLOSS_E_INVAL for an inconsistent shard
+ * (offset or count out of range, vocab_offset + vocab > vocab_total), as for
+ * the unsharded calls otherwise.
+ */
+typedef struct {
+  int64_t vocab_offset;  /* first vocabulary row of this shard */
+  int64_t vocab_total;   /* V of the whole head, < 2^31 */
+  int32_t shard;         /* g in [0, n_shards) */
+  int32_t n_shards;      /* G >= 1 */
+  void* exchange;        /* device, specloss_exchange_bytes(N, G) bytes, 256-byte aligned */
+} specloss_shard;
+
+size_t specloss_exchange_bytes(int64_t n_rows, int32_t n_shards);
+
+int lmhead_shard_pass1(const specloss_problem* p, const specloss_shard* sh, void* workspace,
+                       size_t ws_bytes, hipStream_t stream);
+
+/* saved: specloss_saved_bytes(N); counts [2] int64 as for lmhead_loss_fwd. */
+int lmhead_shard_merge1(const specloss_problem* p, const specloss_shard* sh, void* saved,
+                        int64_t* counts, hipStream_t stream);
+
+int lmhead_shard_pass2(const specloss_problem* p, const specloss_shard* sh, const void* saved,
+                       void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/* Outputs as for lmhead_loss_fwd (loss required; term_loss, lse_q, reduced optional). */
+int lmhead_shard_merge2(const specloss_problem* p, const specloss_shard* sh, void* saved,
+                        const int64_t* counts, float* loss, float* term_loss, float* lse_q,
+                        float* reduced, hipStream_t stream);
+
+/*
+ * Backward of one shard for the seed of lmhead_loss_bwd: dW [vocab, H] fp32
+ * of the shard's rows (accumulate_dW as there), and dh_partial [N, H] fp32
+ * (overwritten, or NULL) = this shard's term of dhidden.
+ */
+int lmhead_shard_bwd(const specloss_problem* p, const specloss_shard* sh, const float* grad_loss,
+                     const float* grad_mean, const int64_t* counts, const void* saved,
+                     void* workspace, size_t ws_bytes, float* dh_partial, float* dW,
+                     int accumulate_dW, hipStream_t stream);
+
+/*
+ * out[i] = sum over g of parts[g * n + i], g = 0 .. n_parts - 1 in order
+ * (the dh reduction of the vocabulary-parallel backward).  parts: device fp32
+ * [n_parts][n], 16-byte aligned, n a multiple of 4; out: device, out_dtype
+ * fp32 or bf16.  SPECLOSS_E_UNSUPPORTED otherwise.
+ */
+int specloss_sum_partials(const float* parts, int64_t n, int32_t n_parts, void* out,
+                          int32_t out_dtype, hipStream_t stream);
+
+/*
  * Kernel trace for measurement.  specloss_trace_create makes `capacity`
  * pairs of HIP events on the current device (the only HIP objects the
  * library ever creates; NULL on failure).  While a problem's `trace` field

@@ -69,7 +69,25 @@ EXPORTS = (
     "specloss_trace_reset",
     "specloss_trace_read",
     "specloss_kernel_name",
+    "specloss_exchange_bytes",
+    "lmhead_shard_pass1",
+    "lmhead_shard_merge1",
+    "lmhead_shard_pass2",
+    "lmhead_shard_merge2",
+    "lmhead_shard_bwd",
+    "specloss_sum_partials",
 )
+
+
+class Shard(ctypes.Structure):
+    """specloss_shard (include/specloss.h)."""
+    _fields_ = [
+        ("vocab_offset", ctypes.c_int64),
+        ("vocab_total", ctypes.c_int64),
+        ("shard", ctypes.c_int32),
+        ("n_shards", ctypes.c_int32),
+        ("exchange", ctypes.c_void_p),
+    ]
 
 
 def load_library(path: Optional[str] = None) -> ctypes.CDLL:
@@ -99,6 +117,18 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.lmhead_loss_fwd_bwd.restype = ctypes.c_int
     lib.specloss_align_heads.argtypes = [i64, i64, i32, ctypes.POINTER(i32), vp, vp, vp, vp]
     lib.specloss_align_heads.restype = ctypes.c_int
+    S = ctypes.POINTER(Shard)
+    lib.specloss_exchange_bytes.argtypes = [i64, i32]
+    lib.specloss_exchange_bytes.restype = sz
+    lib.lmhead_shard_pass1.argtypes = [P, S, vp, sz, vp]
+    lib.lmhead_shard_merge1.argtypes = [P, S, vp, vp, vp]
+    lib.lmhead_shard_pass2.argtypes = [P, S, vp, vp, sz, vp]
+    lib.lmhead_shard_merge2.argtypes = [P, S, vp, vp, vp, vp, vp, vp, vp]
+    lib.lmhead_shard_bwd.argtypes = [P, S, vp, vp, vp, vp, vp, sz, vp, vp, ctypes.c_int, vp]
+    lib.specloss_sum_partials.argtypes = [vp, i64, i32, vp, i32, vp]
+    for name in ("lmhead_shard_pass1", "lmhead_shard_merge1", "lmhead_shard_pass2",
+                 "lmhead_shard_merge2", "lmhead_shard_bwd", "specloss_sum_partials"):
+        getattr(lib, name).restype = ctypes.c_int
     lib.specloss_strerror.argtypes = [ctypes.c_int]
     lib.specloss_strerror.restype = ctypes.c_char_p
     lib.specloss_kind_name.argtypes = [ctypes.c_int]
@@ -240,6 +270,71 @@ def specloss_align_heads(seq_len: int, batch: int, shifts, loss_mask: Optional[t
     _check(load_library().specloss_align_heads(seq_len, batch, len(shifts), arr, _ptr(loss_mask),
                                                _ptr(target_row_out), _ptr(mask_out),
                                                _stream(stream)), "specloss_align_heads")
+
+
+def specloss_exchange_bytes(n_rows: int, n_shards: int) -> int:
+    return int(load_library().specloss_exchange_bytes(n_rows, n_shards))
+
+
+def _nbytes(t: torch.Tensor) -> int:
+    return t.numel() * t.element_size()
+
+
+def lmhead_shard_pass1(problem: Problem, shard: Shard, workspace: torch.Tensor,
+                       stream=None) -> None:
+    _check(load_library().lmhead_shard_pass1(ctypes.byref(problem), ctypes.byref(shard),
+                                             _ptr(workspace), _nbytes(workspace),
+                                             _stream(stream)), "lmhead_shard_pass1")
+
+
+def lmhead_shard_merge1(problem: Problem, shard: Shard, saved: torch.Tensor, counts: torch.Tensor,
+                        stream=None) -> None:
+    _check(load_library().lmhead_shard_merge1(ctypes.byref(problem), ctypes.byref(shard),
+                                              _ptr(saved), _ptr(counts), _stream(stream)),
+           "lmhead_shard_merge1")
+
+
+def lmhead_shard_pass2(problem: Problem, shard: Shard, saved: torch.Tensor,
+                       workspace: torch.Tensor, stream=None) -> None:
+    _check(load_library().lmhead_shard_pass2(ctypes.byref(problem), ctypes.byref(shard),
+                                             _ptr(saved), _ptr(workspace), _nbytes(workspace),
+                                             _stream(stream)), "lmhead_shard_pass2")
+
+
+def lmhead_shard_merge2(problem: Problem, shard: Shard, saved: torch.Tensor, counts: torch.Tensor,
+                        loss: torch.Tensor, term_loss: Optional[torch.Tensor],
+                        lse_q: Optional[torch.Tensor], reduced: Optional[torch.Tensor],
+                        stream=None) -> None:
+    _check(load_library().lmhead_shard_merge2(ctypes.byref(problem), ctypes.byref(shard),
+                                              _ptr(saved), _ptr(counts), _ptr(loss),
+                                              _ptr(term_loss), _ptr(lse_q), _ptr(reduced),
+                                              _stream(stream)), "lmhead_shard_merge2")
+
+
+def lmhead_shard_bwd(problem: Problem, shard: Shard, grad_loss: Optional[torch.Tensor],
+                     grad_mean: Optional[torch.Tensor], counts: torch.Tensor, saved: torch.Tensor,
+                     workspace: torch.Tensor, dh_partial: Optional[torch.Tensor],
+                     dW: Optional[torch.Tensor], accumulate_dW: bool = False,
+                     stream=None) -> None:
+    for t in (dh_partial, dW):
+        if t is not None and t.dtype != torch.float32:
+            raise TypeError("dh_partial and dW are fp32")
+    _check(load_library().lmhead_shard_bwd(
+        ctypes.byref(problem), ctypes.byref(shard), _ptr(grad_loss), _ptr(grad_mean),
+        _ptr(counts), _ptr(saved), _ptr(workspace), _nbytes(workspace), _ptr(dh_partial),
+        _ptr(dW), int(bool(accumulate_dW)), _stream(stream)), "lmhead_shard_bwd")
+
+
+def specloss_sum_partials(parts: torch.Tensor, out: torch.Tensor, stream=None) -> None:
+    """out = parts.sum(0) in order over the leading axis, by the library's kernel."""
+    if parts.dtype != torch.float32 or not parts.is_contiguous() or not out.is_contiguous():
+        raise TypeError("parts: contiguous fp32 [n_parts, ...]; out: contiguous")
+    n = out.numel()
+    if parts.numel() != n * parts.shape[0]:
+        raise ValueError("parts must hold n_parts copies of out's shape")
+    dt = BF16 if out.dtype == torch.bfloat16 else F32
+    _check(load_library().specloss_sum_partials(_ptr(parts), n, parts.shape[0], _ptr(out), dt,
+                                                _stream(stream)), "specloss_sum_partials")
 
 
 class Trace:

@@ -231,12 +231,12 @@ GemmOperand target_operand(const specloss_problem* p, int64_t r0, int64_t rows, 
 enum KernelId : int32_t {
   K_VALIDITY, K_STATS_Q, K_STATS_P, K_COMBINE1, K_ROWDOT, K_DIV, K_COMBINE2, K_REDUCE, K_COPY,
   K_SEED, K_TRANSPOSE_W, K_TRANSPOSE_H, K_DZ, K_GEMM_DH, K_GEMM_DW, K_STATS_STAGE, K_DZ_STAGE,
-  K_DIV_STAGE, K_DZ_DIV, K_NUM_IDS
+  K_DIV_STAGE, K_DZ_DIV, K_TILE_SUM, K_SUM_PARTS, K_NUM_IDS
 };
 const char* const kKernelNames[K_NUM_IDS] = {
     "validity", "stats_q", "stats_p", "combine1", "rowdot", "div", "combine2", "reduce",
     "copy_lse", "seed", "transpose_W", "transpose_h", "dz", "gemm_dh", "gemm_dW",
-    "stats_stage", "dz_stage", "div_stage", "dz_div"};
+    "stats_stage", "dz_stage", "div_stage", "dz_div", "tile_sum", "sum_partials"};
 
 // Brackets launches with the trace's events when the problem carries one.
 struct Tracer {
@@ -290,8 +290,8 @@ struct FwdBufs {
 };
 
 int launch_validity_for(const specloss_problem* p, const KindSet& k, const SavedView& sv,
-                        int64_t* counts, Tracer& tr, hipStream_t stream) {
-  ValidityLaunch va;
+                        int64_t* counts, Tracer& tr, hipStream_t stream, int64_t vocab = 0) {
+  ValidityLaunch va{};
   va.n = p->n_rows;
   va.mask = p->mask;
   va.labels = p->labels;
@@ -299,7 +299,7 @@ int launch_validity_for(const specloss_problem* p, const KindSet& k, const Saved
   va.target_row = p->target_row;
   va.n_target = p->n_target_rows;
   va.use_target = k.target;
-  va.vocab = (int32_t)p->vocab;
+  va.vocab = (int32_t)(vocab > 0 ? vocab : p->vocab);
   va.flags = sv.flags;
   va.y_label = sv.y_label;
   va.counts = counts;
@@ -312,15 +312,16 @@ int launch_validity_for(const specloss_problem* p, const KindSet& k, const Saved
 // Staging for the logit gradient ([Nc][Vp] buffers): with `stage` alone,
 // pass 1 stores e = exp(z - m_tile) there; with `stage` and `stage_d`,
 // pass 2 stores q there and q - p in stage_d.
-int fwd_chunk(const specloss_problem* p, const KindSet& k, const Layout& L, const FwdBufs& b,
-              const SavedView& sv, float* loss, float* terms, int64_t r0, int64_t rows,
-              void* stage, void* stage_d, Tracer& tr, hipStream_t stream) {
+// Pass-1 contractions of chunk rows [r0, r0 + rows) into the per-(tile, row)
+// partials b.pz (and b.pu for the target side); `stage` as for fwd_chunk.
+int launch_pass1(const specloss_problem* p, const KindSet& k, const Layout& L, const FwdBufs& b,
+                 int64_t r0, int64_t rows, void* stage, Tracer& tr, hipStream_t stream) {
   const bool bf16 = p->in_dtype == SPECLOSS_BF16;
   const int64_t H = L.H, Nc = b.Nc;
   const int64_t tile_cols = L.Tv * Nc;
   const GemmOperand Bh = op(offset_rows(p->hidden_states, r0, H, L.es), H, rows);
 
-  StatsLaunch sz;
+  StatsLaunch sz{};
   sz.A = op(p->W, H, p->vocab);
   sz.B = Bh;
   sz.k_len = (int32_t)H;
@@ -333,8 +334,8 @@ int fwd_chunk(const specloss_problem* p, const KindSet& k, const Layout& L, cons
   sz.ps = b.pz + tile_cols;
   sz.pi = nullptr;
   sz.pq = nullptr;
-  if (stage && !stage_d) {
-    StatsStageLaunch ss;
+  if (stage) {
+    StatsStageLaunch ss{};
     ss.st = sz;
     ss.stage = stage;
     ss.ld_stage = L.Vp;
@@ -353,8 +354,52 @@ int fwd_chunk(const specloss_problem* p, const KindSet& k, const Layout& L, cons
     su.pq = b.pu + 3 * tile_cols;
     TRACED(tr, K_STATS_P, 2.0 * rows * H * p->vocab, launch_stats(bf16, true, su, stream));
   }
+  return SPECLOSS_OK;
+}
 
-  Combine1Launch c1;
+// Pass-2 divergence sums of chunk rows [r0, r0 + rows) into b.p2, with the
+// final logsumexps in `sv`; stage_q / stage_d as for fwd_chunk (or null).
+int launch_pass2(const specloss_problem* p, const KindSet& k, const Layout& L, const FwdBufs& b,
+                 const SavedView& sv, int64_t r0, int64_t rows, void* stage_q, void* stage_d,
+                 Tracer& tr, hipStream_t stream) {
+  const bool bf16 = p->in_dtype == SPECLOSS_BF16;
+  const int64_t H = L.H, Nc = b.Nc;
+  DivLaunch dv{};
+  dv.Az = op(p->W, H, p->vocab);
+  dv.Bz = op(offset_rows(p->hidden_states, r0, H, L.es), H, rows);
+  dv.Au = op(p->W_t, H, p->vocab);
+  dv.Bu = target_operand(p, r0, rows, L.es);
+  dv.k_len = (int32_t)H;
+  dv.vocab = (int32_t)p->vocab;
+  dv.tiles_m = (int32_t)L.Tv;
+  dv.tiles_n = (int32_t)cdiv(rows, 128);
+  dv.ncols = (int32_t)rows;
+  dv.ldp = (int32_t)Nc;
+  dv.lse_q = sv.lse_q + r0;
+  dv.lse_p = sv.lse_p + r0;
+  dv.need = k.need;
+  dv.part = b.p2;
+  dv.part_stride = L.Tv * Nc;
+  dv.stage_q = stage_d ? stage_q : nullptr;
+  dv.stage_d = stage_d;
+  dv.ld_stage = L.Vp;
+  TRACED(tr, stage_d ? K_DIV_STAGE : K_DIV, 4.0 * rows * H * p->vocab,
+         launch_div(bf16, dv, stream));
+  return SPECLOSS_OK;
+}
+
+int fwd_chunk(const specloss_problem* p, const KindSet& k, const Layout& L, const FwdBufs& b,
+              const SavedView& sv, float* loss, float* terms, int64_t r0, int64_t rows,
+              void* stage, void* stage_d, Tracer& tr, hipStream_t stream) {
+  const bool bf16 = p->in_dtype == SPECLOSS_BF16;
+  const int64_t H = L.H, Nc = b.Nc;
+  const int64_t tile_cols = L.Tv * Nc;
+  {
+    const int rc = launch_pass1(p, k, L, b, r0, rows, stage_d ? nullptr : stage, tr, stream);
+    if (rc) return rc;
+  }
+
+  Combine1Launch c1{};
   c1.tiles_m = (int32_t)L.Tv;
   c1.ncols = (int32_t)rows;
   c1.ldp = (int32_t)Nc;
@@ -375,7 +420,7 @@ int fwd_chunk(const specloss_problem* p, const KindSet& k, const Layout& L, cons
   const bool ce_lab = (k.active >> SPECLOSS_CE_LABEL) & 1u;
   const bool ce_arg = (k.active >> SPECLOSS_CE_ARGMAX_P) & 1u;
   if (ce_lab || ce_arg) {
-    RowdotLaunch rd;
+    RowdotLaunch rd{};
     rd.W = p->W;
     rd.h = offset_rows(p->hidden_states, r0, H, L.es);
     rd.H = H;
@@ -390,30 +435,11 @@ int fwd_chunk(const specloss_problem* p, const KindSet& k, const Layout& L, cons
   }
 
   if (k.pass2) {
-    DivLaunch dv;
-    dv.Az = op(p->W, H, p->vocab);
-    dv.Bz = Bh;
-    dv.Au = op(p->W_t, H, p->vocab);
-    dv.Bu = target_operand(p, r0, rows, L.es);
-    dv.k_len = (int32_t)H;
-    dv.vocab = (int32_t)p->vocab;
-    dv.tiles_m = (int32_t)L.Tv;
-    dv.tiles_n = (int32_t)cdiv(rows, 128);
-    dv.ncols = (int32_t)rows;
-    dv.ldp = (int32_t)Nc;
-    dv.lse_q = sv.lse_q + r0;
-    dv.lse_p = sv.lse_p + r0;
-    dv.need = k.need;
-    dv.part = b.p2;
-    dv.part_stride = tile_cols;
-    dv.stage_q = stage_d ? stage : nullptr;
-    dv.stage_d = stage_d;
-    dv.ld_stage = L.Vp;
-    TRACED(tr, stage_d ? K_DIV_STAGE : K_DIV, 4.0 * rows * H * p->vocab,
-           launch_div(bf16, dv, stream));
+    const int rc = launch_pass2(p, k, L, b, sv, r0, rows, stage, stage_d, tr, stream);
+    if (rc) return rc;
   }
 
-  Combine2Launch c2;
+  Combine2Launch c2{};
   c2.tiles_m = (int32_t)L.Tv;
   c2.ncols = (int32_t)rows;
   c2.ldp = (int32_t)Nc;
@@ -425,6 +451,7 @@ int fwd_chunk(const specloss_problem* p, const KindSet& k, const Layout& L, cons
   c2.lse_q = sv.lse_q + r0;
   c2.zy_lab = ce_lab ? b.zy : nullptr;
   c2.zy_arg = ce_arg ? b.zy + Nc : nullptr;
+  c2.zy_count = 1;
   c2.loss = loss + r0;
   c2.term = terms + r0;
   c2.term_stride = p->n_rows;
@@ -440,7 +467,7 @@ int fwd_chunk(const specloss_problem* p, const KindSet& k, const Layout& L, cons
 int launch_reduce_for(const specloss_problem* p, const KindSet& k, const float* loss,
                       const float* terms, const int64_t* counts, float* reduced, Tracer& tr,
                       hipStream_t stream) {
-  ReduceLaunch rl;
+  ReduceLaunch rl{};
   rl.n = p->n_rows;
   rl.loss = loss;
   rl.term = terms;
@@ -456,7 +483,7 @@ int launch_reduce_for(const specloss_problem* p, const KindSet& k, const float* 
 int launch_seed_for(const specloss_problem* p, const SavedView& sv, const float* grad_loss,
                     const float* grad_mean, const int64_t* counts, float* seed, Tracer& tr,
                     hipStream_t stream) {
-  SeedLaunch sd;
+  SeedLaunch sd{};
   sd.n = p->n_rows;
   sd.flags = sv.flags;
   sd.grad_loss = grad_loss;
@@ -477,7 +504,7 @@ int bwd_contract(const specloss_problem* p, const Layout& L, int64_t Nc, const v
   const int64_t H = L.H, V = L.V, Vp = L.Vp;
   const size_t dh_es = dh_dtype == SPECLOSS_BF16 ? 2 : 4;
   if (dhidden) {
-    GemmLaunch g;
+    GemmLaunch g{};
     g.A = op(dz, Vp, Nc);
     g.B = op(wt, Vp, H);
     g.k_len = (int32_t)Vp;
@@ -493,7 +520,7 @@ int bwd_contract(const specloss_problem* p, const Layout& L, int64_t Nc, const v
     TRACED(tr, K_GEMM_DH, 2.0 * rows * H * V, launch_gemm(bf16, g, stream));
   }
   if (dW) {
-    GemmLaunch g;
+    GemmLaunch g{};
     g.A = op(dzt, Nc, Vp);
     g.B = op(ht, Nc, H);
     g.k_len = (int32_t)round_up(rows, 64);
@@ -534,6 +561,107 @@ int check_bwd_args(const float* grad_loss, const float* grad_mean, void* dhidden
   if (!aligned(grad_loss, 4) || !aligned(grad_mean, 4) || !aligned(dW, 16) ||
       !aligned(dhidden, 16))
     return SPECLOSS_E_UNSUPPORTED;
+  return SPECLOSS_OK;
+}
+
+int check_bwd_inputs(const float* grad_loss, const float* grad_mean, const int64_t* counts,
+                     const void* saved, void* dhidden, int32_t dh_dtype, float* dW,
+                     void* workspace) {
+  if (!saved || !counts) return SPECLOSS_E_INVAL;
+  TRY(check_bwd_args(grad_loss, grad_mean, dhidden, dh_dtype, dW));
+  if (!aligned(counts, 8) || !aligned(saved, 4)) return SPECLOSS_E_UNSUPPORTED;
+  if (!workspace || !aligned(workspace, kAlign)) return SPECLOSS_E_WORKSPACE;
+  return SPECLOSS_OK;
+}
+
+// Backward by recompute: per chunk, the logit gradient tile is recomputed from
+// the saved per-row state, staged in two layouts and contracted into dh, dW.
+// vocab_offset: global index of W's first row (saved labels are global).
+int bwd_recompute(const specloss_problem* p, const KindSet& k, const float* grad_loss,
+                  const float* grad_mean, const int64_t* counts, const void* saved,
+                  void* workspace, size_t ws_bytes, void* dhidden, int32_t dh_dtype, float* dW,
+                  int accumulate_dW, int64_t vocab_offset, hipStream_t stream) {
+  const int64_t Nc = pick_chunk(p, k, ws_bytes, REGION_BWD);
+  if (Nc <= 0) return SPECLOSS_E_WORKSPACE;
+  const Layout L = plan(p, k, Nc);
+  char* ws = static_cast<char*>(workspace);
+  const bool bf16 = p->in_dtype == SPECLOSS_BF16;
+  const int64_t N = L.N, H = L.H, V = L.V, Vp = L.Vp;
+  const SavedView sv = saved_view(const_cast<void*>(saved), N);
+  float* seed = reinterpret_cast<float*>(ws + L.seed);
+  void* wt = ws + L.wt;
+  void* ht = ws + L.ht;
+  void* dz = ws + L.dz;
+  void* dzt = ws + L.dzt;
+  Tracer tr{p->trace, stream};
+
+  TRY(launch_seed_for(p, sv, grad_loss, grad_mean, counts, seed, tr, stream));
+  if (dhidden)
+    TRACED(tr, K_TRANSPOSE_W, 2.0 * Vp * H * L.es, launch_transpose(bf16, p->W, V, H, wt, Vp, stream));
+
+  int chunk = 0;
+  for (int64_t r0 = 0; r0 < N; r0 += Nc, ++chunk) {
+    const int64_t rows = (N - r0) < Nc ? (N - r0) : Nc;
+    const void* hc = offset_rows(p->hidden_states, r0, H, L.es);
+    if (dW)
+      TRACED(tr, K_TRANSPOSE_H, 2.0 * Nc * H * L.es, launch_transpose(bf16, hc, rows, H, ht, Nc, stream));
+
+    DzLaunch dl{};
+    dl.Az = op(p->W, H, V);
+    dl.Bz = op(hc, H, rows);
+    if (k.dual_bwd) {
+      dl.Au = op(p->W_t, H, V);
+      dl.Bu = target_operand(p, r0, rows, L.es);
+    } else {
+      dl.Au = dl.Az;
+      dl.Bu = dl.Bz;
+    }
+    dl.k_len = (int32_t)H;
+    dl.vocab = (int32_t)V;
+    dl.tiles_m = (int32_t)L.Tv;
+    dl.tiles_n = (int32_t)cdiv(rows, k.dual_bwd ? 128 : 256);
+    dl.ncols = (int32_t)rows;
+    dl.r0 = r0;
+    dl.seed = seed;
+    dl.sv = sv;
+    memcpy(dl.w, p->weights, sizeof(dl.w));
+    dl.dz = dz;
+    dl.ld_dz = Vp;
+    dl.dzt = dzt;
+    dl.ld_dzt = Nc;
+    dl.vocab_offset = (int32_t)vocab_offset;
+    TRACED(tr, K_DZ, (k.dual_bwd ? 4.0 : 2.0) * rows * H * V, launch_dz(bf16, k.dual_bwd, dl, stream));
+    TRY(bwd_contract(p, L, Nc, dz, dzt, wt, ht, r0, rows, chunk > 0 || accumulate_dW, dhidden,
+                     dh_dtype, dW, tr, stream));
+  }
+  return SPECLOSS_OK;
+}
+
+// ---- vocabulary-parallel variant ----
+// Exchange buffer: part 1 = m_q, s_q, m_p, s_p, q2_p, argmax (global index);
+// part 2 = the kNumSums divergence sums, label logit, argmax-p logit.  Each
+// field is [G][Ns] 4-byte entries, Ns = N rounded up to 64.
+constexpr int kExch1 = 6, kExch2 = kNumSums + 2;
+
+struct Exchange {
+  char* base;
+  int64_t Ns;
+  int32_t G;
+  float* f(int field) const { return reinterpret_cast<float*>(base) + (int64_t)field * G * Ns; }
+  float* at(int field, int g, int64_t r0 = 0) const { return f(field) + (int64_t)g * Ns + r0; }
+};
+
+Exchange exchange_of(const specloss_shard* sh, int64_t n) {
+  return Exchange{static_cast<char*>(sh->exchange), round_up(n, 64), sh->n_shards};
+}
+
+int check_shard(const specloss_problem* p, const specloss_shard* sh) {
+  if (!sh || !sh->exchange) return SPECLOSS_E_INVAL;
+  if (!aligned(sh->exchange, kAlign)) return SPECLOSS_E_UNSUPPORTED;
+  if (sh->n_shards < 1 || sh->shard < 0 || sh->shard >= sh->n_shards) return SPECLOSS_E_INVAL;
+  if (sh->vocab_total <= 0 || sh->vocab_total > INT32_MAX / 2) return SPECLOSS_E_INVAL;
+  if (sh->vocab_offset < 0 || sh->vocab_offset + p->vocab > sh->vocab_total)
+    return SPECLOSS_E_INVAL;
   return SPECLOSS_OK;
 }
 
@@ -604,63 +732,9 @@ int lmhead_loss_bwd(const specloss_problem* p, const float* grad_loss, const flo
                     hipStream_t stream) {
   KindSet k;
   TRY(check_problem(p, &k));
-  if (!saved || !counts) return SPECLOSS_E_INVAL;
-  TRY(check_bwd_args(grad_loss, grad_mean, dhidden, dh_dtype, dW));
-  if (!aligned(counts, 8) || !aligned(saved, 4)) return SPECLOSS_E_UNSUPPORTED;
-  if (!workspace || !aligned(workspace, kAlign)) return SPECLOSS_E_WORKSPACE;
-  const int64_t Nc = pick_chunk(p, k, ws_bytes, REGION_BWD);
-  if (Nc <= 0) return SPECLOSS_E_WORKSPACE;
-  const Layout L = plan(p, k, Nc);
-  char* ws = static_cast<char*>(workspace);
-  const bool bf16 = p->in_dtype == SPECLOSS_BF16;
-  const int64_t N = L.N, H = L.H, V = L.V, Vp = L.Vp;
-  const SavedView sv = saved_view(const_cast<void*>(saved), N);
-  float* seed = reinterpret_cast<float*>(ws + L.seed);
-  void* wt = ws + L.wt;
-  void* ht = ws + L.ht;
-  void* dz = ws + L.dz;
-  void* dzt = ws + L.dzt;
-  Tracer tr{p->trace, stream};
-
-  TRY(launch_seed_for(p, sv, grad_loss, grad_mean, counts, seed, tr, stream));
-  if (dhidden)
-    TRACED(tr, K_TRANSPOSE_W, 2.0 * Vp * H * L.es, launch_transpose(bf16, p->W, V, H, wt, Vp, stream));
-
-  int chunk = 0;
-  for (int64_t r0 = 0; r0 < N; r0 += Nc, ++chunk) {
-    const int64_t rows = (N - r0) < Nc ? (N - r0) : Nc;
-    const void* hc = offset_rows(p->hidden_states, r0, H, L.es);
-    if (dW)
-      TRACED(tr, K_TRANSPOSE_H, 2.0 * Nc * H * L.es, launch_transpose(bf16, hc, rows, H, ht, Nc, stream));
-
-    DzLaunch dl;
-    dl.Az = op(p->W, H, V);
-    dl.Bz = op(hc, H, rows);
-    if (k.dual_bwd) {
-      dl.Au = op(p->W_t, H, V);
-      dl.Bu = target_operand(p, r0, rows, L.es);
-    } else {
-      dl.Au = dl.Az;
-      dl.Bu = dl.Bz;
-    }
-    dl.k_len = (int32_t)H;
-    dl.vocab = (int32_t)V;
-    dl.tiles_m = (int32_t)L.Tv;
-    dl.tiles_n = (int32_t)cdiv(rows, k.dual_bwd ? 128 : 256);
-    dl.ncols = (int32_t)rows;
-    dl.r0 = r0;
-    dl.seed = seed;
-    dl.sv = sv;
-    memcpy(dl.w, p->weights, sizeof(dl.w));
-    dl.dz = dz;
-    dl.ld_dz = Vp;
-    dl.dzt = dzt;
-    dl.ld_dzt = Nc;
-    TRACED(tr, K_DZ, (k.dual_bwd ? 4.0 : 2.0) * rows * H * V, launch_dz(bf16, k.dual_bwd, dl, stream));
-    TRY(bwd_contract(p, L, Nc, dz, dzt, wt, ht, r0, rows, chunk > 0 || accumulate_dW, dhidden,
-                     dh_dtype, dW, tr, stream));
-  }
-  return SPECLOSS_OK;
+  TRY(check_bwd_inputs(grad_loss, grad_mean, counts, saved, dhidden, dh_dtype, dW, workspace));
+  return bwd_recompute(p, k, grad_loss, grad_mean, counts, saved, workspace, ws_bytes, dhidden,
+                       dh_dtype, dW, accumulate_dW, 0, stream);
 }
 
 int lmhead_loss_fwd_bwd(const specloss_problem* p, void* workspace, size_t ws_bytes, float* loss,
@@ -714,7 +788,7 @@ int lmhead_loss_fwd_bwd(const specloss_problem* p, void* workspace, size_t ws_by
   for (int64_t r0 = 0; r0 < N; r0 += Nc, ++chunk) {
     const int64_t rows = (N - r0) < Nc ? (N - r0) : Nc;
     TRY(fwd_chunk(p, k, L, b, sv, loss, terms, r0, rows, dz, dd, tr, stream));
-    DzStageLaunch ds;
+    DzStageLaunch ds{};
     ds.tiles_m = (int32_t)L.Tv;
     ds.ncols = (int32_t)rows;
     ds.vocab = (int32_t)V;
@@ -759,7 +833,7 @@ int specloss_align_heads(int64_t seq_len, int64_t batch, int32_t n_heads, const 
       (int64_t)n_heads * batch * seq_len > INT32_MAX / 2)
     return SPECLOSS_E_UNSUPPORTED;
   if (!aligned(target_row_out, 4)) return SPECLOSS_E_UNSUPPORTED;
-  AlignLaunch a;
+  AlignLaunch a{};
   a.seq_len = seq_len;
   a.batch = batch;
   a.n_heads = n_heads;
@@ -848,6 +922,214 @@ const char* specloss_kind_name(int kind) {
                                          "jsd",      "tv", "nla",    "lk_hybrid"};
   if (kind < 0 || kind >= kNumKinds) return nullptr;
   return names[kind];
+}
+
+}  // extern "C"
+
+extern "C" {
+
+size_t specloss_exchange_bytes(int64_t n_rows, int32_t n_shards) {
+  if (n_rows <= 0 || n_shards <= 0) return 0;
+  return (size_t)(kExch1 + kExch2) * n_shards * round_up(n_rows, 64) * 4;
+}
+
+int lmhead_shard_pass1(const specloss_problem* p, const specloss_shard* sh, void* workspace,
+                       size_t ws_bytes, hipStream_t stream) {
+  KindSet k;
+  TRY(check_problem(p, &k));
+  TRY(check_shard(p, sh));
+  if (!workspace || !aligned(workspace, kAlign)) return SPECLOSS_E_WORKSPACE;
+  const int64_t Nc = pick_chunk(p, k, ws_bytes, REGION_FWD);
+  if (Nc <= 0) return SPECLOSS_E_WORKSPACE;
+  const Layout L = plan(p, k, Nc);
+  char* ws = static_cast<char*>(workspace);
+  const FwdBufs b{reinterpret_cast<float*>(ws + L.pz), reinterpret_cast<float*>(ws + L.pu),
+                  reinterpret_cast<float*>(ws + L.p2), reinterpret_cast<float*>(ws + L.zy), Nc};
+  const Exchange X = exchange_of(sh, L.N);
+  const int g = sh->shard;
+  const int64_t tile_cols = L.Tv * Nc;
+  Tracer tr{p->trace, stream};
+  for (int64_t r0 = 0; r0 < L.N; r0 += Nc) {
+    const int64_t rows = (L.N - r0) < Nc ? (L.N - r0) : Nc;
+    TRY(launch_pass1(p, k, L, b, r0, rows, nullptr, tr, stream));
+    Combine1Launch c1{};
+    c1.tiles_m = (int32_t)L.Tv;
+    c1.ncols = (int32_t)rows;
+    c1.ldp = (int32_t)Nc;
+    c1.pm_z = b.pz;
+    c1.ps_z = b.pz + tile_cols;
+    c1.pm_u = k.target ? b.pu : nullptr;
+    c1.ps_u = k.target ? b.pu + tile_cols : nullptr;
+    c1.pi_u = k.target ? reinterpret_cast<const int32_t*>(b.pu + 2 * tile_cols) : nullptr;
+    c1.pq_u = k.target ? b.pu + 3 * tile_cols : nullptr;
+    c1.vocab = (int32_t)p->vocab;
+    c1.raw_m[0] = X.at(0, g, r0);
+    c1.raw_s[0] = X.at(1, g, r0);
+    c1.raw_m[1] = X.at(2, g, r0);
+    c1.raw_s[1] = X.at(3, g, r0);
+    c1.raw_q2 = X.at(4, g, r0);
+    c1.raw_idx = reinterpret_cast<int32_t*>(X.at(5, g, r0));
+    c1.idx_offset = (int32_t)sh->vocab_offset;
+    TRACED(tr, K_COMBINE1, (k.target ? 6.0 : 2.0) * L.Tv * rows * 4, launch_combine1(c1, stream));
+  }
+  return SPECLOSS_OK;
+}
+
+int lmhead_shard_merge1(const specloss_problem* p, const specloss_shard* sh, void* saved,
+                        int64_t* counts, hipStream_t stream) {
+  KindSet k;
+  TRY(check_problem(p, &k));
+  TRY(check_shard(p, sh));
+  if (!saved || !counts) return SPECLOSS_E_INVAL;
+  if (!aligned(saved, 4) || !aligned(counts, 8)) return SPECLOSS_E_UNSUPPORTED;
+  const int64_t N = p->n_rows;
+  const SavedView sv = saved_view(saved, N);
+  const Exchange X = exchange_of(sh, N);
+  Tracer tr{p->trace, stream};
+  TRY(launch_validity_for(p, k, sv, counts, tr, stream, sh->vocab_total));
+  Combine1Launch c1{};
+  c1.tiles_m = X.G;  // the G shard records merge like G vocabulary tiles
+  c1.ncols = (int32_t)N;
+  c1.ldp = (int32_t)X.Ns;
+  c1.pm_z = X.f(0);
+  c1.ps_z = X.f(1);
+  c1.pm_u = k.target ? X.f(2) : nullptr;
+  c1.ps_u = k.target ? X.f(3) : nullptr;
+  c1.pq_u = k.target ? X.f(4) : nullptr;
+  c1.pi_u = k.target ? reinterpret_cast<const int32_t*>(X.f(5)) : nullptr;
+  c1.vocab = (int32_t)sh->vocab_total;
+  c1.flags = sv.flags;
+  c1.lse_q = sv.lse_q;
+  c1.lse_p = sv.lse_p;
+  c1.y_arg = sv.y_arg;
+  c1.flat = sv.flat;
+  TRACED(tr, K_COMBINE1, (k.target ? 6.0 : 2.0) * X.G * N * 4, launch_combine1(c1, stream));
+  return SPECLOSS_OK;
+}
+
+int lmhead_shard_pass2(const specloss_problem* p, const specloss_shard* sh, const void* saved,
+                       void* workspace, size_t ws_bytes, hipStream_t stream) {
+  KindSet k;
+  TRY(check_problem(p, &k));
+  TRY(check_shard(p, sh));
+  if (!saved) return SPECLOSS_E_INVAL;
+  if (!aligned(saved, 4)) return SPECLOSS_E_UNSUPPORTED;
+  if (!workspace || !aligned(workspace, kAlign)) return SPECLOSS_E_WORKSPACE;
+  const int64_t Nc = pick_chunk(p, k, ws_bytes, REGION_FWD);
+  if (Nc <= 0) return SPECLOSS_E_WORKSPACE;
+  const Layout L = plan(p, k, Nc);
+  char* ws = static_cast<char*>(workspace);
+  const FwdBufs b{reinterpret_cast<float*>(ws + L.pz), reinterpret_cast<float*>(ws + L.pu),
+                  reinterpret_cast<float*>(ws + L.p2), reinterpret_cast<float*>(ws + L.zy), Nc};
+  const bool bf16 = p->in_dtype == SPECLOSS_BF16;
+  const SavedView sv = saved_view(const_cast<void*>(saved), L.N);
+  const Exchange X = exchange_of(sh, L.N);
+  const int g = sh->shard;
+  const bool ce_lab = (k.active >> SPECLOSS_CE_LABEL) & 1u;
+  const bool ce_arg = (k.active >> SPECLOSS_CE_ARGMAX_P) & 1u;
+  Tracer tr{p->trace, stream};
+  for (int64_t r0 = 0; r0 < L.N; r0 += Nc) {
+    const int64_t rows = (L.N - r0) < Nc ? (L.N - r0) : Nc;
+    if (ce_lab || ce_arg) {
+      RowdotLaunch rd{};
+      rd.W = p->W;
+      rd.h = offset_rows(p->hidden_states, r0, L.H, L.es);
+      rd.H = L.H;
+      rd.ncols = (int32_t)rows;
+      rd.vocab = (int32_t)p->vocab;
+      rd.vocab_offset = (int32_t)sh->vocab_offset;
+      rd.outside = -INFINITY;  // the shard holding the row's label supplies the logit
+      rd.y1 = ce_lab ? sv.y_label + r0 : nullptr;
+      rd.y2 = ce_arg ? sv.y_arg + r0 : nullptr;
+      rd.out1 = X.at(kExch1 + kNumSums, g, r0);
+      rd.out2 = X.at(kExch1 + kNumSums + 1, g, r0);
+      TRACED(tr, K_ROWDOT, 2.0 * rows * L.H * L.es * ((ce_lab ? 1 : 0) + (ce_arg ? 1 : 0)),
+             launch_rowdot(bf16, rd, stream));
+    }
+    if (k.pass2) {
+      TRY(launch_pass2(p, k, L, b, sv, r0, rows, nullptr, nullptr, tr, stream));
+      TileSumLaunch ts{};
+      ts.tiles_m = (int32_t)L.Tv;
+      ts.ncols = (int32_t)rows;
+      ts.ldp = (int32_t)Nc;
+      ts.need = k.need;
+      ts.part = b.p2;
+      ts.part_stride = L.Tv * Nc;
+      ts.out = X.at(kExch1, g, r0);
+      ts.out_stride = (int64_t)X.G * X.Ns;
+      TRACED(tr, K_TILE_SUM, (double)__builtin_popcount(k.need) * (L.Tv + 1) * rows * 4,
+             launch_tile_sum(ts, stream));
+    }
+  }
+  return SPECLOSS_OK;
+}
+
+int lmhead_shard_merge2(const specloss_problem* p, const specloss_shard* sh, void* saved,
+                        const int64_t* counts, float* loss, float* term_loss, float* lse_q,
+                        float* reduced, hipStream_t stream) {
+  KindSet k;
+  TRY(check_problem(p, &k));
+  TRY(check_shard(p, sh));
+  if (!saved) return SPECLOSS_E_INVAL;
+  TRY(check_fwd_outputs(loss, term_loss, lse_q, saved, counts, reduced));
+  if (reduced && !term_loss) return SPECLOSS_E_INVAL;  // the per-kind means read the terms
+  const int64_t N = p->n_rows;
+  const SavedView sv = saved_view(saved, N);
+  const Exchange X = exchange_of(sh, N);
+  const bool ce_lab = (k.active >> SPECLOSS_CE_LABEL) & 1u;
+  const bool ce_arg = (k.active >> SPECLOSS_CE_ARGMAX_P) & 1u;
+  Tracer tr{p->trace, stream};
+  Combine2Launch c2{};
+  c2.tiles_m = X.G;  // the G shard sums add like G vocabulary tiles
+  c2.ncols = (int32_t)N;
+  c2.ldp = (int32_t)X.Ns;
+  c2.part = X.f(kExch1);
+  c2.part_stride = (int64_t)X.G * X.Ns;
+  c2.need = k.need;
+  memcpy(c2.w, p->weights, sizeof(c2.w));
+  c2.flags = sv.flags;
+  c2.lse_q = sv.lse_q;
+  c2.zy_lab = ce_lab ? X.f(kExch1 + kNumSums) : nullptr;
+  c2.zy_arg = ce_arg ? X.f(kExch1 + kNumSums + 1) : nullptr;
+  c2.zy_count = X.G;
+  c2.zy_stride = X.Ns;
+  c2.loss = loss;
+  c2.term = term_loss;
+  c2.term_stride = N;
+  c2.alpha = sv.alpha;
+  c2.S = sv.S;
+  c2.rkl = sv.rkl;
+  c2.eqg = sv.eqg;
+  TRACED(tr, K_COMBINE2, (double)N * 4 * (2 + __builtin_popcount(k.need) * X.G),
+         launch_combine2(c2, stream));
+  if (reduced) TRY(launch_reduce_for(p, k, loss, term_loss, counts, reduced, tr, stream));
+  if (lse_q)
+    TRACED(tr, K_COPY, (double)N * 8,
+           hipMemcpyAsync(lse_q, sv.lse_q, (size_t)N * 4, hipMemcpyDeviceToDevice, stream));
+  return SPECLOSS_OK;
+}
+
+int lmhead_shard_bwd(const specloss_problem* p, const specloss_shard* sh, const float* grad_loss,
+                     const float* grad_mean, const int64_t* counts, const void* saved,
+                     void* workspace, size_t ws_bytes, float* dh_partial, float* dW,
+                     int accumulate_dW, hipStream_t stream) {
+  KindSet k;
+  TRY(check_problem(p, &k));
+  TRY(check_shard(p, sh));
+  TRY(check_bwd_inputs(grad_loss, grad_mean, counts, saved, dh_partial, SPECLOSS_F32, dW,
+                       workspace));
+  return bwd_recompute(p, k, grad_loss, grad_mean, counts, saved, workspace, ws_bytes, dh_partial,
+                       SPECLOSS_F32, dW, accumulate_dW, sh->vocab_offset, stream);
+}
+
+int specloss_sum_partials(const float* parts, int64_t n, int32_t n_parts, void* out,
+                          int32_t out_dtype, hipStream_t stream) {
+  if (!parts || !out || n <= 0 || n_parts < 1) return SPECLOSS_E_INVAL;
+  if (out_dtype != SPECLOSS_F32 && out_dtype != SPECLOSS_BF16) return SPECLOSS_E_UNSUPPORTED;
+  if (!aligned(parts, 16) || n % 4 != 0 || !aligned(out, out_dtype == SPECLOSS_F32 ? 4 : 2))
+    return SPECLOSS_E_UNSUPPORTED;
+  HIP_TRY(launch_sum_parts(parts, n, n_parts, out, out_dtype == SPECLOSS_BF16, stream));
+  return SPECLOSS_OK;
 }
 
 }  // extern "C"

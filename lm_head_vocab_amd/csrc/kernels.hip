@@ -565,8 +565,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_dz(DzLaunch a) {
     RowCoef rc;
     rc.seed = (c < a.ncols) ? a.seed[gr] : 0.0f;
     rc.lse_q = a.sv.lse_q[gr];
-    rc.y_lab = a.sv.y_label[gr];
-    rc.y_arg = a.sv.y_arg[gr];
+    rc.y_lab = a.sv.y_label[gr] >= 0 ? a.sv.y_label[gr] - a.vocab_offset : -1;
+    rc.y_arg = a.sv.y_arg[gr] >= 0 ? a.sv.y_arg[gr] - a.vocab_offset : -1;
     if (DUAL) {
       rc.lse_p = a.sv.lse_p[gr];
       rc.alpha = a.sv.alpha[gr];
@@ -738,7 +738,7 @@ __global__ __launch_bounds__(256) void k_rowdot(RowdotLaunch a) {
     const int32_t* y = which ? a.y2 : a.y1;
     float* out = which ? a.out2 : a.out1;
     if (!y) continue;
-    const int lab = y[row];
+    const int lab = y[row] >= 0 ? y[row] - a.vocab_offset : -1;
     const bool ok = lab >= 0 && lab < a.vocab;
     float acc = 0.0f;
     if (ok) {
@@ -759,7 +759,7 @@ __global__ __launch_bounds__(256) void k_rowdot(RowdotLaunch a) {
     }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o);
-    if (lane == 0) out[row] = ok ? acc : 0.0f;
+    if (lane == 0) out[row] = ok ? acc : a.outside;
   }
 }
 
@@ -824,6 +824,17 @@ __global__ __launch_bounds__(256) void k_combine1(Combine1Launch a) {
         s += ss[side][g][rr] * f;
         if (side == 1) q += sq[g][rr] * f * f;
       }
+    const int bt_best = side == 1 ? sb[bseg][rr] : -1;
+    if (a.raw_m[0]) {
+      // a vocabulary shard's record: the merged partials themselves
+      a.raw_m[side][c] = m;
+      a.raw_s[side][c] = s;
+      if (side == 1) {
+        a.raw_q2[c] = q;
+        a.raw_idx[c] = bt_best >= 0 ? a.pi_u[(int64_t)bt_best * a.ldp + c] + a.idx_offset : -1;
+      }
+      continue;
+    }
     const float lse = m + logf(s);
     if (side == 0) {
       a.lse_q[c] = lse;
@@ -835,11 +846,45 @@ __global__ __launch_bounds__(256) void k_combine1(Combine1Launch a) {
       a.flat[c] = (bt >= 0 && a.flags[c]) ? s / sqrtf((float)a.vocab * q) : 0.0f;
     }
   }
-  if (!a.pm_u) {
+  if (!a.pm_u && !a.raw_m[0]) {
     a.lse_p[c] = 0.0f;
     a.y_arg[c] = -1;
     a.flat[c] = 0.0f;
   }
+}
+
+// sums over the vocabulary tiles of one shard: out[f][c] = sum_t part[f][t][c]
+// (fixed order) for every requested sum f
+__global__ __launch_bounds__(256) void k_tile_sum(TileSumLaunch a) {
+  const int c = blockIdx.x * 256 + threadIdx.x;
+  if (c >= a.ncols) return;
+  for (int f = 0; f < kNumSums; ++f) {
+    if (!(a.need & (1u << f))) continue;
+    float acc = 0.0f;
+    for (int t = 0; t < a.tiles_m; ++t) acc += a.part[f * a.part_stride + (int64_t)t * a.ldp + c];
+    a.out[f * a.out_stride + c] = acc;
+  }
+}
+
+// out[i] = sum_g parts[g][i] in shard order (fp32 partials; fp32 or bf16 out)
+template <typename OutT>
+__global__ __launch_bounds__(256) void k_sum_parts(const float* parts, int64_t n, int32_t n_parts,
+                                                   OutT* out) {
+  const int64_t i4 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i4 >= n) return;
+  float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  const int lim = (int)(n - i4 < 4 ? n - i4 : 4);
+  for (int g = 0; g < n_parts; ++g) {
+    const float* src = parts + (int64_t)g * n + i4;
+    if (lim == 4) {
+      const f32x4_t v = *reinterpret_cast<const f32x4_t*>(src);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] += v[e];
+    } else {
+      for (int e = 0; e < lim; ++e) acc[e] += src[e];
+    }
+  }
+  for (int e = 0; e < lim; ++e) store1<OutT>(out + i4 + e, acc[e]);
 }
 
 __global__ __launch_bounds__(256) void k_combine2(Combine2Launch a) {
@@ -855,8 +900,13 @@ __global__ __launch_bounds__(256) void k_combine2(Combine2Launch a) {
   const float alpha = sum[0], S = sum[1], kl = sum[2], rkl = sum[3], jsd = sum[4], eqg = sum[5];
   const bool valid = a.flags[c] != 0;
   float L[kNumKinds];
-  L[0] = a.zy_lab ? a.lse_q[c] - a.zy_lab[c] : 0.0f;
-  L[1] = a.zy_arg ? a.lse_q[c] - a.zy_arg[c] : 0.0f;
+  float zl = -INFINITY, za = -INFINITY;
+  for (int g = 0; g < a.zy_count; ++g) {  // one entry, or one per vocabulary shard
+    if (a.zy_lab) zl = fmaxf(zl, a.zy_lab[g * a.zy_stride + c]);
+    if (a.zy_arg) za = fmaxf(za, a.zy_arg[g * a.zy_stride + c]);
+  }
+  L[0] = a.zy_lab ? a.lse_q[c] - zl : 0.0f;
+  L[1] = a.zy_arg ? a.lse_q[c] - za : 0.0f;
   L[2] = kl;
   L[3] = rkl;
   L[4] = jsd;
@@ -870,7 +920,7 @@ __global__ __launch_bounds__(256) void k_combine2(Combine2Launch a) {
     if (a.w[k] == 0.0f) continue;
     const float lk = valid ? L[k] : 0.0f;
     total += a.w[k] * lk;
-    a.term[k * a.term_stride + c] = lk;
+    if (a.term) a.term[k * a.term_stride + c] = lk;
   }
   a.loss[c] = valid ? total : 0.0f;
   a.alpha[c] = (a.need & SUM_ALPHA) ? alpha : 1.0f;
@@ -1055,6 +1105,23 @@ hipError_t launch_combine1(const Combine1Launch& a, hipStream_t s) {
 
 hipError_t launch_combine2(const Combine2Launch& a, hipStream_t s) {
   hipLaunchKernelGGL(k_combine2, dim3((a.ncols + 255) / 256), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_tile_sum(const TileSumLaunch& a, hipStream_t s) {
+  hipLaunchKernelGGL(k_tile_sum, dim3((a.ncols + 255) / 256), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_sum_parts(const float* parts, int64_t n, int32_t n_parts, void* out,
+                            bool out_bf16, hipStream_t s) {
+  const dim3 grid((unsigned)((n + 1023) / 1024)), block(256);
+  if (out_bf16)
+    hipLaunchKernelGGL(k_sum_parts<bf16_bits>, grid, block, 0, s, parts, n, n_parts,
+                       static_cast<bf16_bits*>(out));
+  else
+    hipLaunchKernelGGL(k_sum_parts<float>, grid, block, 0, s, parts, n, n_parts,
+                       static_cast<float*>(out));
   return hipGetLastError();
 }
 

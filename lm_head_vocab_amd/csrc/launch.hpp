@@ -112,6 +112,7 @@ struct DzLaunch {
   int64_t ld_dz;
   void* dzt;          // [Vp][cap]
   int64_t ld_dzt;
+  int32_t vocab_offset;  // first vocabulary row of A (saved labels are global indices)
 };
 // dual: also recompute the target logits (kinds that need p)
 hipError_t launch_dz(bool bf16, bool dual, const DzLaunch& a, hipStream_t s);
@@ -149,8 +150,11 @@ struct RowdotLaunch {
   const void* h;        // chunk base
   int64_t H;
   int32_t ncols;
-  int32_t vocab;        // labels outside [0, vocab) give 0 and are never dereferenced
-  const int32_t* y1;    // chunk-local label arrays, or null
+  int32_t vocab;        // rows of W
+  int32_t vocab_offset; // global index of W's first row; labels outside
+                        // [offset, offset + vocab) give `outside` and are never dereferenced
+  float outside;
+  const int32_t* y1;    // chunk-local label arrays (global indices), or null
   const int32_t* y2;
   float* out1;
   float* out2;
@@ -171,8 +175,30 @@ struct Combine1Launch {
   float* lse_p;
   int32_t* y_arg;
   float* flat;
+  // record mode (raw_m[0] != null): write the merged partials of this call's
+  // tiles instead of the final values: m and sum-exp per side, e^2 sum and
+  // argmax (plus idx_offset) of the target side
+  float* raw_m[2];
+  float* raw_s[2];
+  float* raw_q2;
+  int32_t* raw_idx;
+  int32_t idx_offset;
 };
 hipError_t launch_combine1(const Combine1Launch& a, hipStream_t s);
+
+struct TileSumLaunch {
+  int32_t tiles_m, ncols, ldp;
+  uint32_t need;
+  const float* part;    // [kNumSums][tiles_m][ldp]
+  int64_t part_stride;
+  float* out;           // [kNumSums][out_stride]
+  int64_t out_stride;
+};
+hipError_t launch_tile_sum(const TileSumLaunch& a, hipStream_t s);
+
+// out[i] = sum over g < n_parts of parts[g * n + i] (fixed order)
+hipError_t launch_sum_parts(const float* parts, int64_t n, int32_t n_parts, void* out,
+                            bool out_bf16, hipStream_t s);
 
 struct Combine2Launch {
   int32_t tiles_m, ncols, ldp;
@@ -184,6 +210,8 @@ struct Combine2Launch {
   const float* lse_q;
   const float* zy_lab;    // chunk-local label logits (null if unused)
   const float* zy_arg;
+  int32_t zy_count;       // entries per row (max taken): 1, or one per vocabulary shard
+  int64_t zy_stride;
   float* loss;            // chunk-local
   float* term;            // chunk-local, stride term_stride between kinds
   int64_t term_stride;

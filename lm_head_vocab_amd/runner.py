@@ -103,3 +103,94 @@ def lmhead_loss(hidden: torch.Tensor, W: torch.Tensor, weights: Dict[str, float]
     """Mean streaming LM-head loss with autograd; gradients flow to hidden and W."""
     run = LossRun(hidden.detach(), W.detach(), weights, **kw)
     return _LMHeadLoss.apply(hidden, W, run)
+
+
+class ShardedLossRun(LossRun):
+    """The vocabulary-parallel sequence on one device: G shards of W (and W_t).
+
+    Shard g owns vocabulary rows [bounds[g], bounds[g+1]) (by default whole
+    256-row tiles except the last shard's end); the G shard calls run one after another on the same
+    stream, with one exchange buffer that every shard writes its record into.
+    On G devices each shard's calls would run on its own device, the exchange
+    being an all-gather of the records and the dh sum an all-reduce.
+    """
+
+    def __init__(self, hidden: torch.Tensor, W: torch.Tensor, weights: Dict[str, float],
+                 n_shards: int, *, labels: Optional[torch.Tensor] = None,
+                 mask: Optional[torch.Tensor] = None,
+                 target_hidden: Optional[torch.Tensor] = None, W_t: Optional[torch.Tensor] = None,
+                 target_row: Optional[torch.Tensor] = None, max_chunk_rows: int = 0,
+                 want_terms: bool = True, bounds: Optional[list] = None):
+        dev = hidden.device
+        V = W.shape[0]
+        if bounds is None:
+            step = -(-V // (n_shards * 256)) * 256
+            bounds = [min(V, g * step) for g in range(n_shards)] + [V]
+        self.bounds = [int(b) for b in bounds]
+        if len(self.bounds) != n_shards + 1 or self.bounds[0] != 0 or self.bounds[-1] != V:
+            raise ValueError("bounds must run from 0 to V in n_shards steps")
+        if any(b1 <= b0 for b0, b1 in zip(self.bounds, self.bounds[1:])):
+            raise ValueError(f"{n_shards} shards of whole 256-row tiles do not fit V={V}")
+        self.inputs = dict(hidden=hidden, W=W, labels=labels, mask=mask,
+                           target_hidden=target_hidden, W_t=W_t, target_row=target_row)
+        self.weights = dict(weights)
+        N = hidden.shape[0]
+        self.n_rows = N
+        self.n_shards = n_shards
+        self.exchange = torch.empty(B.specloss_exchange_bytes(N, n_shards), dtype=torch.uint8,
+                                    device=dev)
+        self.problems, self.shards = [], []
+        ws = 256
+        for g in range(n_shards):
+            v0, v1 = self.bounds[g], self.bounds[g + 1]
+            prob = B.make_problem(hidden, W[v0:v1], weights, labels=labels, mask=mask,
+                                  target_hidden=target_hidden,
+                                  W_t=None if W_t is None else W_t[v0:v1], target_row=target_row)
+            sh = B.Shard(vocab_offset=v0, vocab_total=V, shard=g, n_shards=n_shards,
+                         exchange=self.exchange.data_ptr())
+            self.problems.append(prob)
+            self.shards.append(sh)
+            ws = max(ws, B.lmhead_loss_workspace_size(prob, max_chunk_rows))
+        self.problem = self.problems[0]
+        self.workspace = torch.empty(ws, dtype=torch.uint8, device=dev)
+        self.loss = torch.empty(N, dtype=torch.float32, device=dev)
+        self.term = torch.zeros(B.NUM_KINDS, N, dtype=torch.float32, device=dev) if want_terms else None
+        self.lse_q = torch.empty(N, dtype=torch.float32, device=dev)
+        self.saved = torch.empty(B.specloss_saved_bytes(N), dtype=torch.uint8, device=dev)
+        self.counts = torch.zeros(2, dtype=torch.int64, device=dev)
+        self.reduced = torch.empty(1 + B.NUM_KINDS, dtype=torch.float32, device=dev)
+
+    def forward(self, stream=None) -> None:
+        for prob, sh in zip(self.problems, self.shards):
+            B.lmhead_shard_pass1(prob, sh, self.workspace, stream)
+        B.lmhead_shard_merge1(self.problems[0], self.shards[0], self.saved, self.counts, stream)
+        for prob, sh in zip(self.problems, self.shards):
+            B.lmhead_shard_pass2(prob, sh, self.saved, self.workspace, stream)
+        B.lmhead_shard_merge2(self.problems[0], self.shards[0], self.saved, self.counts, self.loss,
+                              self.term, self.lse_q,
+                              self.reduced if self.term is not None else None, stream)
+
+    def backward(self, grad_loss: Optional[torch.Tensor] = None,
+                 grad_mean: Optional[torch.Tensor] = None, dhidden: Optional[torch.Tensor] = None,
+                 dW: Optional[torch.Tensor] = None, accumulate_dW: bool = False,
+                 want_dh: bool = True, want_dW: bool = True, stream=None):
+        h, W = self.inputs["hidden"], self.inputs["W"]
+        if dhidden is None and want_dh:
+            dhidden = torch.empty(h.shape, dtype=torch.float32, device=h.device)
+        if dW is None and want_dW:
+            dW = torch.empty(W.shape, dtype=torch.float32, device=W.device)
+        parts = None
+        if dhidden is not None:
+            parts = torch.empty((self.n_shards,) + tuple(h.shape), dtype=torch.float32,
+                                device=h.device)
+        for g, (prob, sh) in enumerate(zip(self.problems, self.shards)):
+            v0, v1 = self.bounds[g], self.bounds[g + 1]
+            B.lmhead_shard_bwd(prob, sh, grad_loss, grad_mean, self.counts, self.saved,
+                               self.workspace, None if parts is None else parts[g],
+                               None if dW is None else dW[v0:v1], accumulate_dW, stream)
+        if parts is not None:
+            B.specloss_sum_partials(parts, dhidden, stream)
+        return dhidden, dW
+
+    def forward_backward(self, *a, **kw):
+        raise NotImplementedError("the vocabulary-parallel sequence is forward, then backward")

@@ -8,7 +8,7 @@ import numpy as np
 import torch
 
 import lm_head_vocab_amd as L
-from lm_head_vocab_amd.runner import LossRun
+from lm_head_vocab_amd.runner import LossRun, ShardedLossRun
 from oracle import specloss_oracle as O
 
 # acceptance bars (fixed by the benchmark spec of the path)
@@ -80,15 +80,25 @@ def check_argmax(gpu_y: np.ndarray, prob, rows, valid) -> None:
     assert np.array_equal(gpu_y[decisive], ref[decisive])
 
 
-def full_parity(prob, *, max_chunk_rows=0, check_grads=True, tag="", single_call=False):
+def full_parity(prob, *, max_chunk_rows=0, check_grads=True, tag="", single_call=False,
+                shards=None):
     """Run fwd (+bwd with the mean seed) on the GPU and compare every output with the oracle.
 
     single_call: use lmhead_loss_fwd_bwd instead of the two calls.
+    shards: (G, bounds or None) to run the vocabulary-parallel sequence instead.
     """
     say(f"[parity] {tag} {prob.name} N={prob.n_rows} H={prob.hidden_dim} V={prob.vocab} "
-        f"dtype={prob.dtype} weights={prob.weights} chunk={max_chunk_rows} single={single_call}")
+        f"dtype={prob.dtype} weights={prob.weights} chunk={max_chunk_rows} single={single_call} "
+        f"shards={shards}")
     dev = to_device(prob)
-    run = make_run(prob, dev, max_chunk_rows=max_chunk_rows)
+    if shards:
+        run = ShardedLossRun(dev["hidden"], dev["W"], prob.weights, shards[0],
+                             labels=dev["labels"], mask=dev["mask"],
+                             target_hidden=dev["target_hidden"], W_t=dev["W_t"],
+                             target_row=dev["target_row"], max_chunk_rows=max_chunk_rows,
+                             bounds=shards[1])
+    else:
+        run = make_run(prob, dev, max_chunk_rows=max_chunk_rows)
     gm = torch.ones(1, dtype=torch.float32, device="cuda")
     if single_call:
         dh_t, dW_t = run.forward_backward(grad_mean=gm)

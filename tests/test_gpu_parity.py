@@ -13,6 +13,7 @@ import torch
 
 import synthetic
 from oracle import specloss_oracle as O
+from lm_head_vocab_amd.runner import ShardedLossRun
 from tests._gpu_helpers import (GRAD_FROB, full_parity, make_run, rel_frob, say, to_device)
 
 pytestmark = pytest.mark.gpu
@@ -373,3 +374,81 @@ def test_flatness_single_call_and_chunks():
     ref = O.forward(p)
     from tests._gpu_helpers import check_flatness
     check_flatness(a.flatness.cpu().numpy(), ref.flat, ref.valid)
+
+
+
+# ---------------------------------------------------------- vocabulary-parallel
+@pytest.mark.parametrize("case", ["ce_label_3", "lk_ce_2_ragged", "multihead_4", "kinds_3_f32",
+                                  "one_shard"])
+def test_vocab_parallel_matches_oracle(case):
+    """The shard sequence (pass 1 per shard, merge, pass 2 per shard, merge, local
+    backward, dh partial sum) against the oracle, with shard ends inside tiles."""
+    if case == "ce_label_3":
+        p = synthetic.make_problem("ce_bf16_1b", n_rows=600, hidden_dim=192, vocab=1100)
+        sh, ch = (3, [0, 300, 700, 1100]), 256
+    elif case == "lk_ce_2_ragged":
+        p = synthetic.make_problem("lk_hybrid_bf16_8b", n_rows=300, hidden_dim=128, vocab=777,
+                                   weights={"lk_hybrid": 1.0, "ce": 0.5})
+        sh, ch = (2, [0, 333, 777]), 0
+    elif case == "multihead_4":
+        p = synthetic.make_problem("multihead_bf16_405b", seq_len=100, hidden_dim=128, vocab=1000)
+        sh, ch = (4, None), 256
+    elif case == "kinds_3_f32":
+        p = synthetic.make_problem("lk_hybrid_bf16_8b", n_rows=280, hidden_dim=128, vocab=900,
+                                   weights={"kl_div": 0.3, "rkl": 0.2, "jsd": 0.4, "nla": 0.1,
+                                            "ce_label": 0.5})
+        rng = np.random.default_rng(8)
+        p.labels = rng.integers(0, p.vocab, p.n_rows).astype(np.int32)
+        p.labels[::13] = -100
+        p.dtype = "f32"
+        for f in ("hidden", "W", "target_hidden", "W_t"):
+            setattr(p, f, synthetic.bf16_bits_to_f32(getattr(p, f)).copy())
+        sh, ch = (3, [0, 256, 512, 900]), 0
+    else:
+        p = synthetic.make_problem("lk_hybrid_bf16_8b", n_rows=200, hidden_dim=128, vocab=600,
+                                   weights={"tv": 1.0})
+        sh, ch = (1, None), 0
+    full_parity(p, max_chunk_rows=ch, tag=f"vp-{case}", shards=sh)
+
+
+def test_vocab_parallel_argmax_tie_across_shards():
+    """Two target rows with identical weights in different shards tie on every
+    token; where they hold the maximum the merged argmax is the lower index."""
+    p = synthetic.make_problem("lk_hybrid_bf16_8b", n_rows=256, hidden_dim=128, vocab=768,
+                               weights={"ce": 1.0})
+    Wt = synthetic.bf16_bits_to_f32(p.W_t)
+    hot = synthetic.bf16_bits_to_f32(p.target_hidden).mean(axis=0)
+    hot = 3.0 * hot / np.linalg.norm(hot)
+    a, b = 100, 600                     # shard 0 and shard 1 of [0, 384, 768]
+    Wt[a] = Wt[b] = hot
+    p.W_t = synthetic.f32_to_bf16_bits(Wt)
+    out = full_parity(p, tag="vp-tie", shards=(2, [0, 384, 768]), check_grads=False)
+    y = out["run"].saved_field(3, torch.int32).cpu().numpy()
+    g = synthetic.bf16_bits_to_f32(p.target_hidden).astype(np.float64)
+    u = g @ synthetic.bf16_bits_to_f32(p.W_t).astype(np.float64).T
+    top = u.argmax(axis=1)
+    assert np.any(top == a)
+    assert np.all(y[top == a] == a)
+
+
+def test_vocab_parallel_matches_unsharded():
+    """Sharded and unsharded runs agree to fp32 rounding (losses, stats) and the bar (grads)."""
+    p = synthetic.make_problem("lk_hybrid_bf16_8b", n_rows=500, hidden_dim=128, vocab=1300,
+                               weights={"lk_hybrid": 1.0, "ce": 0.25})
+    dev = to_device(p)
+    gm = torch.ones(1, device="cuda")
+    a = make_run(p, dev, max_chunk_rows=256)
+    a.forward()
+    dh1, dW1 = a.backward(grad_mean=gm)
+    b = ShardedLossRun(dev["hidden"], dev["W"], p.weights, 3, target_hidden=dev["target_hidden"],
+                       W_t=dev["W_t"], max_chunk_rows=256)
+    b.forward()
+    dh2, dW2 = b.backward(grad_mean=gm)
+    torch.cuda.synchronize()
+    assert torch.equal(a.counts, b.counts)
+    assert torch.allclose(a.loss, b.loss, rtol=1e-5, atol=1e-6)
+    assert torch.allclose(a.lse_q, b.lse_q, rtol=1e-6, atol=1e-5)
+    assert torch.equal(a.saved_field(3, torch.int32), b.saved_field(3, torch.int32))
+    assert torch.allclose(a.flatness, b.flatness, rtol=1e-5)
+    assert rel_frob(dh1.cpu().numpy(), dh2.cpu().numpy()) < 1e-3
+    assert rel_frob(dW1.cpu().numpy(), dW2.cpu().numpy()) < 1e-3

@@ -205,3 +205,49 @@ def test_binding_rejects_bad_dtypes():
         B.make_problem(torch.zeros(4, 64, dtype=torch.float16), torch.zeros(8, 64, dtype=torch.float16), {"ce_label": 1})
     with pytest.raises(ValueError):
         B.make_problem(torch.zeros(4, 64), torch.zeros(8, 64), {"bogus": 1})
+
+
+def _shard(**kw):
+    return B.Shard(vocab_offset=kw.get("off", 0), vocab_total=kw.get("VT", 8192),
+                   shard=kw.get("g", 0), n_shards=kw.get("G", 2), exchange=kw.get("x", 0x50000))
+
+
+def test_exchange_bytes(lib):
+    assert L.binding.specloss_exchange_bytes(0, 2) == 0
+    assert L.binding.specloss_exchange_bytes(10, 0) == 0
+    # 14 fields of [G][round_up(N, 64)] 4-byte entries
+    assert L.binding.specloss_exchange_bytes(100, 3) == 14 * 3 * 128 * 4
+
+
+@pytest.mark.parametrize("bad,code", [
+    (dict(g=2), E_INVAL), (dict(g=-1), E_INVAL), (dict(G=0), E_INVAL),
+    (dict(off=4097), E_INVAL),            # offset + shard vocab beyond the head
+    (dict(VT=0), E_INVAL), (dict(off=-1), E_INVAL),
+    (dict(x=0), E_INVAL), (dict(x=0x50010), E_UNSUP),
+])
+def test_shard_validation(lib, bad, code):
+    p = _problem(V=4096)
+    sh = _shard(**bad)
+    ws = ctypes.c_void_p(0x100000)
+    assert lib.lmhead_shard_pass1(ctypes.byref(p), ctypes.byref(sh), ws, 1 << 30, None) == code
+    assert lib.lmhead_shard_merge1(ctypes.byref(p), ctypes.byref(sh), ctypes.c_void_p(0x60000),
+                                   ctypes.c_void_p(0x70000), None) == code
+
+
+def test_shard_merge2_needs_terms_for_means(lib):
+    p = _problem(V=4096)
+    sh = _shard()
+    rc = lib.lmhead_shard_merge2(ctypes.byref(p), ctypes.byref(sh), ctypes.c_void_p(0x60000),
+                                 ctypes.c_void_p(0x70000), ctypes.c_void_p(0x80000), None, None,
+                                 ctypes.c_void_p(0x90000), None)
+    assert rc == E_INVAL
+
+
+def test_sum_partials_validation(lib):
+    f = lib.specloss_sum_partials
+    assert f(None, 16, 2, ctypes.c_void_p(0x1000), B.F32, None) == E_INVAL
+    assert f(ctypes.c_void_p(0x1000), 0, 2, ctypes.c_void_p(0x2000), B.F32, None) == E_INVAL
+    assert f(ctypes.c_void_p(0x1000), 16, 0, ctypes.c_void_p(0x2000), B.F32, None) == E_INVAL
+    assert f(ctypes.c_void_p(0x1000), 18, 2, ctypes.c_void_p(0x2000), B.F32, None) == E_UNSUP
+    assert f(ctypes.c_void_p(0x1008), 16, 2, ctypes.c_void_p(0x2000), B.F32, None) == E_UNSUP
+    assert f(ctypes.c_void_p(0x1000), 16, 2, ctypes.c_void_p(0x2000), 7, None) == E_UNSUP
