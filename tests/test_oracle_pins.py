@@ -401,3 +401,30 @@ def test_flatness_scipy_cosine():
     logp = ssp.log_softmax(u, axis=1)
     ref = [1 - ssd.cosine(np.exp(logp[i]), np.ones(300)) for i in range(5)]
     assert np.allclose(O.flatness(logp), ref, rtol=1e-12)
+
+
+def test_tv_tie_rule_central_difference():
+    """At exact ties the TV gradient is the central difference of the loss.
+
+    p is q with two entries swapped, so every other entry ties bit for bit; the
+    loss 1 - sum min(p, q(z)) has a kink there, and a central difference
+    returns the mean of the two one-sided derivatives, i.e. the tie counted as
+    1/2 (R5).  Counting ties as 0 or 1 gives a one-sided derivative instead.
+    """
+    rng = np.random.default_rng(13)
+    V = 9
+    z0 = rng.standard_normal(V)
+    logq0 = ssp.log_softmax(z0)
+    logp = logq0.copy()
+    logp[[2, 6]] = logp[[6, 2]]
+    _, dz = O.total_variation(logp[None, :], logq0[None, :])
+
+    def tv(z):
+        return 1.0 - np.minimum(np.exp(logp), np.exp(ssp.log_softmax(z))).sum()
+
+    eps = 1e-6
+    num = np.array([(tv(z0 + eps * np.eye(V)[j]) - tv(z0 - eps * np.eye(V)[j])) / (2 * eps)
+                    for j in range(V)])
+    assert np.count_nonzero(np.exp(logp) == np.exp(logq0)) == V - 2
+    # O(eps) error: the second derivatives differ on the two sides of the kink
+    assert np.allclose(dz[0], num, rtol=0, atol=1e-6), (dz[0], num)
