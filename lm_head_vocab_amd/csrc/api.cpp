@@ -107,6 +107,7 @@ int check_problem(const specloss_problem* p, KindSet* ks) {
 struct Layout {
   int64_t N, H, V, Vp, Tv, Nc;
   size_t es;
+  bool copies;  // the backward contractions read transposed copies (W^T, h^T, dz^T)
   // head
   size_t terms, saved, seed, head_end;
   // forward
@@ -117,7 +118,11 @@ struct Layout {
   size_t f_pz, f_pu, f_p2, f_zy, f_wt, f_ht, f_dz, f_dd, f_dzt, fused_end;
 };
 
-Layout plan(const specloss_problem* p, const KindSet& k, int64_t Nc) {
+// copies: make transposed copies for the backward contractions (always for
+// fp32).  Without them (bf16 only) the contractions read W, h and dz as
+// MN-major operands through the transposing LDS load, which needs about half
+// the workspace but runs the contractions about 1.5x slower.
+Layout plan(const specloss_problem* p, const KindSet& k, int64_t Nc, bool copies = true) {
   Layout L;
   L.N = p->n_rows;
   L.H = p->hidden;
@@ -142,22 +147,23 @@ Layout plan(const specloss_problem* p, const KindSet& k, int64_t Nc) {
   L.p2 = take(k.pass2 ? (size_t)kNumSums * tile_cols : 0);
   L.zy = take(2 * (size_t)Nc * 4);
   L.fwd_end = o;
+  L.copies = copies || L.es == 4;
   o = L.head_end;
-  L.wt = take((size_t)L.H * L.Vp * L.es);
-  L.ht = take((size_t)L.H * Nc * L.es);
+  L.wt = take(L.copies ? (size_t)L.H * L.Vp * L.es : 0);
+  L.ht = take(L.copies ? (size_t)L.H * Nc * L.es : 0);
   L.dz = take((size_t)Nc * L.Vp * L.es);
-  L.dzt = take((size_t)L.Vp * Nc * L.es);
+  L.dzt = take(L.copies ? (size_t)L.Vp * Nc * L.es : 0);
   L.bwd_end = o;
   o = L.head_end;
   L.f_pz = take(2 * tile_cols);
   L.f_pu = take(k.target ? 4 * tile_cols : 0);
   L.f_p2 = take(k.stage_div ? (size_t)kNumSums * tile_cols : 0);
   L.f_zy = take(2 * (size_t)Nc * 4);
-  L.f_wt = take((size_t)L.H * L.Vp * L.es);
-  L.f_ht = take((size_t)L.H * Nc * L.es);
+  L.f_wt = take(L.copies ? (size_t)L.H * L.Vp * L.es : 0);
+  L.f_ht = take(L.copies ? (size_t)L.H * Nc * L.es : 0);
   L.f_dz = take((size_t)Nc * L.Vp * L.es);
   L.f_dd = take(k.stage_div ? (size_t)Nc * L.Vp * L.es : 0);
-  L.f_dzt = take((size_t)L.Vp * Nc * L.es);
+  L.f_dzt = take(L.copies ? (size_t)L.Vp * Nc * L.es : 0);
   L.fused_end = o;
   return L;
 }
@@ -169,12 +175,13 @@ size_t region_end(const Layout& L, Region r) {
   return r == REGION_FWD ? L.fwd_end : (r == REGION_BWD ? L.bwd_end : L.fused_end);
 }
 
-int64_t pick_chunk(const specloss_problem* p, const KindSet& k, size_t ws_bytes, Region region) {
+int64_t largest_chunk(const specloss_problem* p, const KindSet& k, size_t ws_bytes,
+                      Region region, bool copies) {
   const int64_t top = round_up(p->n_rows, kChunkQuantum);
   int64_t lo = 1, hi = top / kChunkQuantum, best = 0;
   while (lo <= hi) {  // the requirement grows with the chunk
     const int64_t mid = (lo + hi) / 2;
-    const Layout L = plan(p, k, mid * kChunkQuantum);
+    const Layout L = plan(p, k, mid * kChunkQuantum, copies);
     if (region_end(L, region) <= ws_bytes) {
       best = mid;
       lo = mid + 1;
@@ -183,6 +190,25 @@ int64_t pick_chunk(const specloss_problem* p, const KindSet& k, size_t ws_bytes,
     }
   }
   return best * kChunkQuantum;
+}
+
+// Chunk for a region, and (backward regions) whether to make transposed
+// copies: with copies when the workspace holds them at a chunk of at least
+// min(N, 1024) rows; otherwise (bf16) without, if that allows a larger chunk.
+// (The copy-free contractions run about 1.5x slower; below about 1000 rows
+// per chunk the fp32 read-modify-write of dW per chunk costs more than that
+// at the large shapes.)
+int64_t pick_chunk(const specloss_problem* p, const KindSet& k, size_t ws_bytes, Region region,
+                   bool* copies = nullptr) {
+  const int64_t with = largest_chunk(p, k, ws_bytes, region, true);
+  if (copies) *copies = true;
+  if (!copies || p->in_dtype != SPECLOSS_BF16) return with;
+  const int64_t top = round_up(p->n_rows, kChunkQuantum);
+  if (with >= (top < 1024 ? top : 1024)) return with;
+  const int64_t without = largest_chunk(p, k, ws_bytes, region, false);
+  if (without <= with) return with;
+  *copies = false;
+  return without;
 }
 
 SavedView saved_view(void* base, int64_t n) {
@@ -204,7 +230,7 @@ SavedView saved_view(void* base, int64_t n) {
 
 GemmOperand op(const void* base, int64_t ld, int64_t n_rows, const int32_t* map = nullptr,
                int64_t map_len = 0) {
-  GemmOperand g;
+  GemmOperand g{};
   g.base = base;
   g.ld = ld;
   g.n_rows = (int32_t)n_rows;
@@ -494,8 +520,10 @@ int launch_seed_for(const specloss_problem* p, const SavedView& sv, const float*
   return SPECLOSS_OK;
 }
 
-// dh rows [r0, r0 + rows) = dz W and dW (+)= dz^T h for one chunk, from the
-// staged dz [Nc][Vp], dz^T [Vp][Nc], W^T [H][Vp] and h^T [H][Nc].
+// dh rows [r0, r0 + rows) = dz W and dW (+)= dz^T h for one chunk from the
+// staged dz [Nc][Vp] and the copies W^T [H][Vp], h^T [H][Nc], dz^T [Vp][Nc];
+// without copies (bf16), W, the hidden chunk and dz are read as they are
+// (MN-major operands).
 int bwd_contract(const specloss_problem* p, const Layout& L, int64_t Nc, const void* dz,
                  const void* dzt, const void* wt, const void* ht, int64_t r0, int64_t rows,
                  bool accumulate, void* dhidden, int32_t dh_dtype, float* dW, Tracer& tr,
@@ -503,11 +531,19 @@ int bwd_contract(const specloss_problem* p, const Layout& L, int64_t Nc, const v
   const bool bf16 = p->in_dtype == SPECLOSS_BF16;
   const int64_t H = L.H, V = L.V, Vp = L.Vp;
   const size_t dh_es = dh_dtype == SPECLOSS_BF16 ? 2 : 4;
+  const bool lean = !L.copies;
   if (dhidden) {
     GemmLaunch g{};
     g.A = op(dz, Vp, Nc);
-    g.B = op(wt, Vp, H);
-    g.k_len = (int32_t)Vp;
+    g.lean = lean;
+    if (lean) {
+      g.B = op(p->W, H, H);  // element (h, v) at W[v * H + h]
+      g.B.k_valid = (int32_t)V;
+      g.k_len = (int32_t)round_up(V, 64);
+    } else {
+      g.B = op(wt, Vp, H);
+      g.k_len = (int32_t)Vp;
+    }
     g.tiles_m = (int32_t)cdiv(rows, 256);
     g.tiles_n = (int32_t)cdiv(H, 256);
     g.m_valid = (int32_t)rows;
@@ -521,9 +557,17 @@ int bwd_contract(const specloss_problem* p, const Layout& L, int64_t Nc, const v
   }
   if (dW) {
     GemmLaunch g{};
-    g.A = op(dzt, Nc, Vp);
-    g.B = op(ht, Nc, H);
     g.k_len = (int32_t)round_up(rows, 64);
+    g.lean = lean;
+    if (lean) {
+      g.A = op(dz, Vp, Vp);  // element (v, c) at dz[c * Vp + v]; rows >= `rows` hold 0
+      g.A.k_valid = (int32_t)Nc;
+      g.B = op(offset_rows(p->hidden_states, r0, H, L.es), H, H);  // (h, c) at h[c * H + h]
+      g.B.k_valid = (int32_t)(L.N - r0);
+    } else {
+      g.A = op(dzt, Nc, Vp);
+      g.B = op(ht, Nc, H);
+    }
     g.tiles_m = (int32_t)L.Tv;
     g.tiles_n = (int32_t)cdiv(H, 256);
     g.m_valid = (int32_t)V;
@@ -581,29 +625,31 @@ int bwd_recompute(const specloss_problem* p, const KindSet& k, const float* grad
                   const float* grad_mean, const int64_t* counts, const void* saved,
                   void* workspace, size_t ws_bytes, void* dhidden, int32_t dh_dtype, float* dW,
                   int accumulate_dW, int64_t vocab_offset, hipStream_t stream) {
-  const int64_t Nc = pick_chunk(p, k, ws_bytes, REGION_BWD);
+  bool with_copies = true;
+  const int64_t Nc = pick_chunk(p, k, ws_bytes, REGION_BWD, &with_copies);
   if (Nc <= 0) return SPECLOSS_E_WORKSPACE;
-  const Layout L = plan(p, k, Nc);
+  const Layout L = plan(p, k, Nc, with_copies);
   char* ws = static_cast<char*>(workspace);
   const bool bf16 = p->in_dtype == SPECLOSS_BF16;
   const int64_t N = L.N, H = L.H, V = L.V, Vp = L.Vp;
   const SavedView sv = saved_view(const_cast<void*>(saved), N);
   float* seed = reinterpret_cast<float*>(ws + L.seed);
-  void* wt = ws + L.wt;
-  void* ht = ws + L.ht;
+  const bool copies = L.copies;
+  void* wt = copies ? ws + L.wt : nullptr;
+  void* ht = copies ? ws + L.ht : nullptr;
   void* dz = ws + L.dz;
-  void* dzt = ws + L.dzt;
+  void* dzt = copies ? ws + L.dzt : nullptr;
   Tracer tr{p->trace, stream};
 
   TRY(launch_seed_for(p, sv, grad_loss, grad_mean, counts, seed, tr, stream));
-  if (dhidden)
+  if (dhidden && copies)
     TRACED(tr, K_TRANSPOSE_W, 2.0 * Vp * H * L.es, launch_transpose(bf16, p->W, V, H, wt, Vp, stream));
 
   int chunk = 0;
   for (int64_t r0 = 0; r0 < N; r0 += Nc, ++chunk) {
     const int64_t rows = (N - r0) < Nc ? (N - r0) : Nc;
     const void* hc = offset_rows(p->hidden_states, r0, H, L.es);
-    if (dW)
+    if (dW && copies)
       TRACED(tr, K_TRANSPOSE_H, 2.0 * Nc * H * L.es, launch_transpose(bf16, hc, rows, H, ht, Nc, stream));
 
     DzLaunch dl{};
@@ -761,9 +807,10 @@ int lmhead_loss_fwd_bwd(const specloss_problem* p, void* workspace, size_t ws_by
   // label / argmax cross-entropies: pass 1 stages e = exp(z - m_tile) per
   // chunk; with kl_div / tv / nla / lk_hybrid, pass 2 stages q and q - p.  The
   // logit gradient is formed from the staged values without recomputing logits.
-  const int64_t Nc = pick_chunk(p, k, ws_bytes, REGION_FUSED);
+  bool with_copies = true;
+  const int64_t Nc = pick_chunk(p, k, ws_bytes, REGION_FUSED, &with_copies);
   if (Nc <= 0) return SPECLOSS_E_WORKSPACE;
-  const Layout L = plan(p, k, Nc);
+  const Layout L = plan(p, k, Nc, with_copies);
   char* ws = static_cast<char*>(workspace);
   const bool bf16 = p->in_dtype == SPECLOSS_BF16;
   const int64_t N = L.N, H = L.H, V = L.V, Vp = L.Vp;
@@ -773,16 +820,17 @@ int lmhead_loss_fwd_bwd(const specloss_problem* p, void* workspace, size_t ws_by
   const FwdBufs b{reinterpret_cast<float*>(ws + L.f_pz), reinterpret_cast<float*>(ws + L.f_pu),
                   k.stage_div ? reinterpret_cast<float*>(ws + L.f_p2) : nullptr,
                   reinterpret_cast<float*>(ws + L.f_zy), Nc};
-  void* wt = ws + L.f_wt;
-  void* ht = ws + L.f_ht;
+  const bool copies = L.copies;
+  void* wt = copies ? ws + L.f_wt : nullptr;
+  void* ht = copies ? ws + L.f_ht : nullptr;
   void* dz = ws + L.f_dz;
   void* dd = k.stage_div ? ws + L.f_dd : nullptr;
-  void* dzt = ws + L.f_dzt;
+  void* dzt = copies ? ws + L.f_dzt : nullptr;
   Tracer tr{p->trace, stream};
 
   TRY(launch_validity_for(p, k, sv, counts, tr, stream));
   TRY(launch_seed_for(p, sv, grad_loss, grad_mean, counts, seed, tr, stream));
-  if (dhidden)
+  if (dhidden && copies)
     TRACED(tr, K_TRANSPOSE_W, 2.0 * Vp * H * L.es, launch_transpose(bf16, p->W, V, H, wt, Vp, stream));
   int chunk = 0;
   for (int64_t r0 = 0; r0 < N; r0 += Nc, ++chunk) {
@@ -809,10 +857,11 @@ int lmhead_loss_fwd_bwd(const specloss_problem* p, void* workspace, size_t ws_by
     ds.dzt = dzt;
     ds.ld_dzt = Nc;
     ds.row_blocks = (int32_t)(cdiv(rows, 256) * 4);
-    TRACED(tr, dd ? K_DZ_DIV : K_DZ_STAGE, (double)ds.row_blocks * 64 * Vp * L.es * (dd ? 4 : 3),
+    TRACED(tr, dd ? K_DZ_DIV : K_DZ_STAGE,
+           (double)ds.row_blocks * 64 * Vp * L.es * ((dd ? 3 : 2) + (dzt ? 1 : 0)),
            launch_dz_stage(bf16, ds, stream));
     const void* hc = offset_rows(p->hidden_states, r0, H, L.es);
-    if (dW)
+    if (dW && copies)
       TRACED(tr, K_TRANSPOSE_H, 2.0 * Nc * H * L.es, launch_transpose(bf16, hc, rows, H, ht, Nc, stream));
     TRY(bwd_contract(p, L, Nc, dz, dzt, wt, ht, r0, rows, chunk > 0 || accumulate_dW, dhidden,
                      dh_dtype, dW, tr, stream));

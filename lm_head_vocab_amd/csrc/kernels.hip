@@ -35,7 +35,7 @@ __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_lo
 
 template <typename T>
 __device__ __forceinline__ Operand<T> as_op(const GemmOperand& g) {
-  return Operand<T>{static_cast<const T*>(g.base), g.ld, g.n_rows, g.map, g.map_len};
+  return Operand<T>{static_cast<const T*>(g.base), g.ld, g.n_rows, g.map, g.map_len, g.k_valid};
 }
 
 // The four lanes l, l^16, l^32, l^48 hold the same output column.  These
@@ -381,8 +381,9 @@ __global__ __launch_bounds__(256) void k_dz_stage(DzStageLaunch a) {
       for (int q = 0; q < KC; ++q) out[q] = __float_as_int(d[q]);
     }
     *reinterpret_cast<i32x4_t*>(p) = out;
-    *reinterpret_cast<i32x4_t*>(tile + rr * STRIDE + ch * 16) = out;
+    if (dzt) *reinterpret_cast<i32x4_t*>(tile + rr * STRIDE + ch * 16) = out;
   }
+  if (!dzt) return;  // bf16: the dW contraction reads dz itself
   __syncthreads();
   // dz^T rows: vocabulary entry v of this tile, 64 chunk rows = RB elements
   constexpr int PER_ROW = RB / KC;  // 16-byte pieces per dz^T row segment
@@ -591,8 +592,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_dz(DzLaunch a) {
       }
       const int v0 = v_base + i * kFrag + frag_row(0, lane);
       store4<T>(dz + (int64_t)c * a.ld_dz + v0, o[0], o[1], o[2], o[3]);
+      if (dzt)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) store1<T>(dzt + (int64_t)(v0 + r) * a.ld_dzt + c, o[r]);
+        for (int r = 0; r < 4; ++r) store1<T>(dzt + (int64_t)(v0 + r) * a.ld_dzt + c, o[r]);
     }
   }
 }
@@ -600,7 +602,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_dz(DzLaunch a) {
 // ============================================================================
 // plain contraction with store / accumulate epilogue
 // ============================================================================
-// ROLE only separates the two backward contractions in profiles (0: dh, 1: dW).
+// ROLE 0: dh = dz W, A = dz, B = W^T; ROLE 1: dW = dz^T h, A = dz^T, B = h^T,
+// all K-major (transposed copies).  LEAN (bf16 only): no copies; dh reads W
+// as an MN-major B (its rows are k), dW reads dz and the hidden chunk as
+// MN-major A and B.
 //
 // Epilogue: the tile goes out in two halves of 128 rows.  The two waves that
 // own a half write their accumulators into LDS (rows padded to 1040 bytes so
@@ -610,9 +615,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_dz(DzLaunch a) {
 constexpr int kHalfRows = 128;
 constexpr int kEpiStride = 256 * 4 + 16;  // bytes per staged row
 
-template <typename T, typename OutT, int ROLE>
+template <typename T, typename OutT, int ROLE, bool LEAN>
 __global__ __launch_bounds__(kThreads, 1) void k_gemm(GemmLaunch a) {
   using Cfg = TileCfg<T, 256, 256>;
+  constexpr bool kA_MN = LEAN && ROLE == 1;
+  constexpr bool kB_MN = LEAN;
   constexpr int kSmem = Cfg::LDS_BYTES > kHalfRows * kEpiStride ? Cfg::LDS_BYTES
                                                                : kHalfRows * kEpiStride;
   __shared__ __attribute__((aligned(16))) char smem[kSmem];
@@ -620,8 +627,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(GemmLaunch a) {
   if (!tile_of(a.tiles_m, a.tiles_n, kGroupM, tm, tn)) return;
   f32x4_t acc[Cfg::FM][Cfg::FN];
   zero_acc<Cfg>(acc);
-  tile_mainloop<T, Cfg>(acc, as_op<T>(a.A), tm * Cfg::BM, as_op<T>(a.B), tn * Cfg::BN, a.k_len,
-                        smem);
+  tile_mainloop<T, Cfg, kA_MN, kB_MN>(acc, as_op<T>(a.A), tm * Cfg::BM, as_op<T>(a.B),
+                                      tn * Cfg::BN, a.k_len, smem);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   OutT* C = static_cast<OutT*>(a.C);
@@ -1071,12 +1078,15 @@ hipError_t launch_dz(bool bf16, bool dual, const DzLaunch& a, hipStream_t s) {
 template <int ROLE>
 static void launch_gemm_role(bool bf16, const GemmLaunch& a, hipStream_t s) {
   const dim3 grid(grid_for_tiles(a.tiles_m * a.tiles_n)), block(kThreads);
-  if (bf16) {
-    if (a.out_bf16) hipLaunchKernelGGL((k_gemm<bf16_bits, bf16_bits, ROLE>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((k_gemm<bf16_bits, float, ROLE>), grid, block, 0, s, a);
+  if (bf16 && a.lean) {
+    if (a.out_bf16) hipLaunchKernelGGL((k_gemm<bf16_bits, bf16_bits, ROLE, true>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((k_gemm<bf16_bits, float, ROLE, true>), grid, block, 0, s, a);
+  } else if (bf16) {
+    if (a.out_bf16) hipLaunchKernelGGL((k_gemm<bf16_bits, bf16_bits, ROLE, false>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((k_gemm<bf16_bits, float, ROLE, false>), grid, block, 0, s, a);
   } else {
-    if (a.out_bf16) hipLaunchKernelGGL((k_gemm<float, bf16_bits, ROLE>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((k_gemm<float, float, ROLE>), grid, block, 0, s, a);
+    if (a.out_bf16) hipLaunchKernelGGL((k_gemm<float, bf16_bits, ROLE, false>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((k_gemm<float, float, ROLE, false>), grid, block, 0, s, a);
   }
 }
 

@@ -35,12 +35,16 @@ struct SavedView {
   float* flat;       // flatness of p: cos(p, uniform), 0 when no target or invalid
 };
 
+// K-major: row r at base + r * ld (n_rows valid, optional gather map).
+// MN-major (bf16 contractions of the backward): element (m, k) at
+// base + k * ld + m, n_rows valid m, k_valid readable k-rows.
 struct GemmOperand {
   const void* base;
   int64_t ld;
   int32_t n_rows;
   const int32_t* map;
   int32_t map_len;
+  int32_t k_valid;
 };
 
 // ---- vocab-tiled passes (A = a vocabulary-row weight, B = hidden rows) ----
@@ -81,7 +85,7 @@ struct DzStageLaunch {
   const void* dd;      // [cap][Vp] q - p, or null
   void* dz;            // in: e or q, out: dz; [cap][Vp]
   int64_t ld_dz;
-  void* dzt;           // [Vp][cap]
+  void* dzt;           // [Vp][cap], or null (not needed by bf16 contractions)
   int64_t ld_dzt;
   int32_t row_blocks;  // 64-row blocks covered (multiple of the 256-row tiles)
 };
@@ -110,7 +114,7 @@ struct DzLaunch {
   float w[kNumKinds];
   void* dz;           // [cap][Vp], row = chunk row
   int64_t ld_dz;
-  void* dzt;          // [Vp][cap]
+  void* dzt;          // [Vp][cap], or null (not needed by bf16 contractions)
   int64_t ld_dzt;
   int32_t vocab_offset;  // first vocabulary row of A (saved labels are global indices)
 };
@@ -126,6 +130,7 @@ struct GemmLaunch {
   int accumulate;
   int out_bf16;
   int role;  // 0: dh, 1: dW (separate kernel names in profiles)
+  int lean;  // bf16 only: B (and for dW also A) are MN-major, read without copies
 };
 hipError_t launch_gemm(bool bf16, const GemmLaunch& a, hipStream_t s);
 

@@ -1,10 +1,11 @@
 // Tile machinery shared by every contraction of the streaming LM-head loss.
 //
-// One shape of contraction serves the whole path: C[m][n] = sum_k A[m][k] B[n][k]
-// with both operands K-contiguous ("NT").  The forward and the recompute take
-// A = W (vocabulary rows) and B = hidden rows; the backward contractions take
-// the staged logit gradient and transposed copies of W and of the hidden chunk,
-// so they are NT as well.
+// Every contraction is C[m][n] = sum_k A[m][k] B[n][k].  An operand is either
+// K-major (row m holds its k values contiguously: W and the hidden rows in the
+// forward, the staged logit gradient dz in the dh contraction) or MN-major
+// (k-row k holds the m values contiguously: W as the right operand of dh, and
+// dz and the hidden chunk as the operands of dW), so no transposed copy is
+// ever made of a bf16 operand.
 //
 // gfx950 mapping:
 //  * 256 threads = 4 wave64s in a 2 x 2 grid; a wave owns a (BM/2) x (BN/2)
@@ -16,6 +17,14 @@
 //    A and B sits in LDS as rows of eight 16-byte chunks, chunk c of row r
 //    stored at position c ^ (r & 7): eight consecutive rows read at the same
 //    logical chunk hit eight different bank groups (conflict-free ds_read_b128).
+//  * An MN-major slab is 64 k-rows of BM (or BN) values; the 16-byte chunk c
+//    of k-row k is stored at position c ^ f(k), f(k) = 2 ((k & 3) | (k & 8) >> 1),
+//    and fragments are read with the transposing LDS load ds_read_b64_tr_b16:
+//    in each 16-lane group, lane L receives element L % 4 of the 8-byte loads
+//    of lanes 4 j + L / 4 (j = 0..3), so lanes that load four consecutive m
+//    of k-rows kb + j hand every lane four consecutive k of one m.  The
+//    swizzle puts the four k-rows of a 16-lane group, and the two groups of
+//    a 32-lane half, in different bank groups.
 //  * Two LDS stages filled by direct-to-LDS loads: the next slab streams in
 //    while the MFMAs consume the current stage (one barrier per slab).
 //  * Workgroups are dealt round-robin to the 8 XCDs; `tile_of` renumbers them
@@ -29,6 +38,7 @@
 namespace specloss {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4_tr_t;
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
@@ -68,17 +78,20 @@ struct TileCfg {
   static constexpr int LDS_BYTES = 2 * STAGE;
 };
 
-// Rows of a K-contiguous operand.  Tile row r reads source row
-// map ? map[r] : r (relative to `base`), clamped into [0, n_rows): rows past
-// the end or unmapped rows still load valid memory and their results are
-// discarded by the epilogues.
+// A K-major operand: tile row r reads source row map ? map[r] : r (relative
+// to `base`), clamped into [0, n_rows): rows past the end or unmapped rows
+// still load valid memory and their results are discarded by the epilogues.
+// An MN-major operand (bf16 only): element (m, k) at base[k * ld + m]; m is
+// clamped below n_rows (a multiple of 8) and k below k_valid the same way,
+// so every load stays inside the tensor.
 template <typename T>
 struct Operand {
   const T* base;
-  int64_t ld;            // elements between rows
-  int32_t n_rows;        // valid source rows
-  const int32_t* map;    // optional gather map indexed by tile row (already offset)
+  int64_t ld;            // elements between rows (K-major) or k-rows (MN-major)
+  int32_t n_rows;        // valid source rows (K-major) or m values (MN-major)
+  const int32_t* map;    // optional gather map indexed by tile row (K-major only)
   int32_t map_len;       // entries readable in map
+  int32_t k_valid;       // MN-major: k-rows readable from the start of the contraction
 };
 
 __device__ __forceinline__ int32_t clamp_row(int32_t r, int32_t n) {
@@ -142,24 +155,47 @@ __device__ __forceinline__ lds_void_t* to_lds(char* p) {
 // pointer (kept in SGPRs) plus a per-lane 32-bit byte offset, so a load costs
 // one scalar M0 write and the load itself, with no per-load vector address
 // arithmetic.
+//
+// A wave's groups all belong to one operand when an operand is MN-major (the
+// 256 x 256 tiles); `kstride` is the bytes one slab advances in that operand
+// (128 for K-major, 64 k-rows for MN-major).  For an MN-major operand a group
+// is two k-rows; in a slab that runs past k_valid the k-rows are clamped to
+// the last valid one (only such slabs pay for the clamp).
 template <int PER_WAVE>
 struct SlabLoads {
   const char* base[PER_WAVE];  // uniform per group
   uint32_t off[PER_WAVE];      // per lane: row offset + swizzled chunk
   char* dst;                   // uniform: LDS address of group 0 in stage 0
+  int64_t kstride;             // uniform: bytes per slab along K
+  uint32_t ldb;                // uniform (MN-major): bytes between k-rows
+  int32_t kvalid;              // uniform (MN-major): readable k-rows, else INT32_MAX
+  int32_t krow0;               // uniform (MN-major): k-row of group 0's first half
 };
 
-// Issue groups [U0, U1) of a slab at byte offset kbytes along K into `stage`.
-// The builtin exists only for the device pass of the single-source compile.
+// Issue groups [U0, U1) of slab `slab` into `stage`.  The builtin exists only
+// for the device pass of the single-source compile.
 template <int PER_WAVE, int U0, int U1, typename Cfg>
-__device__ __forceinline__ void issue_groups(const SlabLoads<PER_WAVE>& L, int stage,
-                                             int64_t kbytes) {
+__device__ __forceinline__ void issue_groups(const SlabLoads<PER_WAVE>& L, int stage, int slab) {
 #if defined(__HIP_DEVICE_COMPILE__)
   char* dst = L.dst + stage * Cfg::STAGE;
+  const int64_t kb = (int64_t)slab * L.kstride;
+  if ((slab + 1) * 64 > L.kvalid) {
+    const int lane = threadIdx.x & 63;
 #pragma unroll
-  for (int u = U0; u < U1; ++u)
-    __builtin_amdgcn_global_load_lds(L.base[u] + kbytes + L.off[u], to_lds(dst + u * 1024), 16,
-                                     0, 0);
+    for (int u = U0; u < U1; ++u) {
+      // k-rows past the last valid one read that row (signed: the slab may
+      // start past it)
+      const int over = slab * 64 + L.krow0 + 2 * u + (lane >> 5) - (L.kvalid - 1);
+      const int64_t back = over > 0 ? (int64_t)over * L.ldb : 0;
+      __builtin_amdgcn_global_load_lds(L.base[u] + kb + (int64_t)L.off[u] - back,
+                                       to_lds(dst + u * 1024), 16, 0, 0);
+    }
+  } else {
+#pragma unroll
+    for (int u = U0; u < U1; ++u)
+      __builtin_amdgcn_global_load_lds(L.base[u] + kb + L.off[u], to_lds(dst + u * 1024), 16,
+                                       0, 0);
+  }
 #endif
 }
 
@@ -180,22 +216,69 @@ __device__ __forceinline__ void group_source(const Operand<T>& op, int32_t row0,
   }
 }
 
-template <typename Cfg>
-__device__ __forceinline__ void read_frags(const char* sa, const char* sb, int s, int lane,
-                                           int wm, int wn, i32x4_t (&af)[Cfg::FM],
-                                           i32x4_t (&bf)[Cfg::FN]) {
+// MN-major slab of one operand: group source of the two k-rows 2 ga, 2 ga + 1.
+// Lane p loads k-row 2 ga + p / 32, logical chunk (p % 32) ^ f(k) of the
+// tile's m range [m0, m0 + 256), the chunk clamped into the valid m.
+template <typename T>
+__device__ __forceinline__ void group_source_mn(const Operand<T>& op, int32_t m0, int ga,
+                                                int lane, const char*& base, uint32_t& off) {
+  const int k = 2 * ga + (lane >> 5);
+  int chunk = (lane & 31) ^ (2 * ((k & 3) | ((k & 8) >> 1)));
+  const int last = (op.n_rows - m0) / 8 - 1;  // last chunk holding valid m
+  if (chunk > last) chunk = last < 0 ? 0 : last;
+  base = reinterpret_cast<const char*>(op.base + m0);
+  off = (uint32_t)((int64_t)k * op.ld * (int64_t)sizeof(T)) + chunk * 16;
+}
+
+// Fragments of one K-major operand for k-step s (rows of kRowBytes).
+template <int F>
+__device__ __forceinline__ void read_frags_k(const char* so, int s, int lane, int m_wave,
+                                             i32x4_t (&f)[F]) {
   const int frow = lane & 15;
   const int chunk = 4 * s + (lane >> 4);
 #pragma unroll
-  for (int i = 0; i < Cfg::FM; ++i) {
-    const int r = wm * Cfg::WM + i * kFrag + frow;
-    af[i] = *reinterpret_cast<const i32x4_t*>(sa + r * kRowBytes + ((chunk ^ (r & 7)) << 4));
+  for (int i = 0; i < F; ++i) {
+    const int r = m_wave + i * kFrag + frow;
+    f[i] = *reinterpret_cast<const i32x4_t*>(so + r * kRowBytes + ((chunk ^ (r & 7)) << 4));
   }
+}
+
+// Fragments of one MN-major operand (k-rows of `pitch` bytes) for k-step s:
+// two transposing loads per fragment, k-rows 32 s + 8 g + j and + 4, where
+// lane l = 16 g + 4 j + q loads m values 4 q .. 4 q + 3 of the fragment.
+template <int F, int PITCH>
+__device__ __forceinline__ void read_frags_mn(const char* so, int s, int lane, int m_wave,
+                                              i32x4_t (&f)[F]) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const int g = lane >> 4, j = (lane >> 2) & 3, q = lane & 3;
+  const int x = (2 * (j | ((g & 1) << 2))) | (q >> 1);
+  const char* row = so + (32 * s + 8 * g + j) * PITCH + (q & 1) * 8;
 #pragma unroll
-  for (int j = 0; j < Cfg::FN; ++j) {
-    const int r = wn * Cfg::WN + j * kFrag + frow;
-    bf[j] = *reinterpret_cast<const i32x4_t*>(sb + r * kRowBytes + ((chunk ^ (r & 7)) << 4));
+  for (int i = 0; i < F; ++i) {
+    const char* p = row + ((((m_wave + i * kFrag) >> 3) ^ x) << 4);
+    typedef __attribute__((address_space(3))) bf16x4_tr_t lds_bf16x4;
+    const bf16x4_tr_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+        (lds_bf16x4*)((__attribute__((address_space(3))) char*)(p)));
+    const bf16x4_tr_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+        (lds_bf16x4*)((__attribute__((address_space(3))) char*)(p + 4 * PITCH)));
+    const i32x2_t l2 = __builtin_bit_cast(i32x2_t, lo), h2 = __builtin_bit_cast(i32x2_t, hi);
+    f[i] = i32x4_t{l2[0], l2[1], h2[0], h2[1]};
   }
+#else
+  (void)so, (void)s, (void)lane, (void)m_wave;
+#pragma unroll
+  for (int i = 0; i < F; ++i) f[i] = i32x4_t{0, 0, 0, 0};
+#endif
+}
+
+template <typename Cfg, bool A_MN, bool B_MN>
+__device__ __forceinline__ void read_frags(const char* sa, const char* sb, int s, int lane,
+                                           int wm, int wn, i32x4_t (&af)[Cfg::FM],
+                                           i32x4_t (&bf)[Cfg::FN]) {
+  if constexpr (A_MN) read_frags_mn<Cfg::FM, Cfg::BM * 2>(sa, s, lane, wm * Cfg::WM, af);
+  else read_frags_k<Cfg::FM>(sa, s, lane, wm * Cfg::WM, af);
+  if constexpr (B_MN) read_frags_mn<Cfg::FN, Cfg::BN * 2>(sb, s, lane, wn * Cfg::WN, bf);
+  else read_frags_k<Cfg::FN>(sb, s, lane, wn * Cfg::WN, bf);
 }
 
 // One slab = two k-steps of MFMAs.  Step 0 issues the second half of slab
@@ -205,13 +288,14 @@ __device__ __forceinline__ void read_frags(const char* sa, const char* sb, int s
 // stage is free), issues the first half of slab k+2 into it and reads slab
 // k+1's step-0 fragments.  Inside a step, fragment reads and
 // loads are interleaved with the MFMAs so they land while the rest run.
-template <typename T, typename Cfg, int PER_WAVE, bool FIRST, bool LAST>
+template <typename T, typename Cfg, int PER_WAVE, bool FIRST, bool LAST, bool A_MN, bool B_MN>
 __device__ __forceinline__ void slab_steps(f32x4_t (&acc)[Cfg::FM][Cfg::FN],
                                            i32x4_t (&fa)[2][Cfg::FM], i32x4_t (&fb)[2][Cfg::FN],
                                            char* smem, int stage, int lane, int wm, int wn,
-                                           const SlabLoads<PER_WAVE>& L, int64_t next_kbytes,
-                                           int64_t pend_kbytes) {
-  constexpr int kR = Cfg::FM + Cfg::FN;
+                                           const SlabLoads<PER_WAVE>& L, int next_slab,
+                                           int pend_slab) {
+  // LDS read instructions per step: one per K-major fragment, two per MN-major one
+  constexpr int kR = Cfg::FM * (A_MN ? 2 : 1) + Cfg::FN * (B_MN ? 2 : 1);
   constexpr int kH = PER_WAVE / 2;
   constexpr int kSlots = Cfg::FM * Cfg::FN - kR;  // MFMA slots left after the reads
   constexpr int kPerSlot = (PER_WAVE + kSlots - 1) / kSlots;
@@ -220,15 +304,15 @@ __device__ __forceinline__ void slab_steps(f32x4_t (&acc)[Cfg::FM][Cfg::FN],
 #pragma unroll
   for (int s = 0; s < kSteps; ++s) {
     const bool loads = (s == 0 && !FIRST) || (s == kSteps - 1 && !LAST);
-    if (s == 0 && !FIRST) issue_groups<PER_WAVE, kH, PER_WAVE, Cfg>(L, stage ^ 1, pend_kbytes);
+    if (s == 0 && !FIRST) issue_groups<PER_WAVE, kH, PER_WAVE, Cfg>(L, stage ^ 1, pend_slab);
     if (s < kSteps - 1) {
-      read_frags<Cfg>(sa, sb, s + 1, lane, wm, wn, fa[(s + 1) & 1], fb[(s + 1) & 1]);
+      read_frags<Cfg, A_MN, B_MN>(sa, sb, s + 1, lane, wm, wn, fa[(s + 1) & 1], fb[(s + 1) & 1]);
     } else if (!LAST) {
       wait_vmem();
       __syncthreads();
-      issue_groups<PER_WAVE, 0, kH, Cfg>(L, stage, next_kbytes);
+      issue_groups<PER_WAVE, 0, kH, Cfg>(L, stage, next_slab);
       const char* na = smem + (stage ^ 1) * Cfg::STAGE;
-      read_frags<Cfg>(na, na + Cfg::BM * kRowBytes, 0, lane, wm, wn, fa[0], fb[0]);
+      read_frags<Cfg, A_MN, B_MN>(na, na + Cfg::BM * kRowBytes, 0, lane, wm, wn, fa[0], fb[0]);
     }
 #pragma unroll
     for (int i = 0; i < Cfg::FM; ++i)
@@ -262,7 +346,7 @@ __device__ __forceinline__ void slab_steps(f32x4_t (&acc)[Cfg::FM][Cfg::FN],
 // (global_load_lds_dwordx4): one wave instruction fills 1 KB = 8 slab rows,
 // lane i landing at byte 16 i; lane i therefore fetches logical chunk
 // (i % 8) ^ (row % 8) of row i / 8, which realises the XOR swizzle.
-template <typename T, typename Cfg>
+template <typename T, typename Cfg, bool A_MN = false, bool B_MN = false>
 __device__ __forceinline__ void tile_mainloop(f32x4_t (&acc)[Cfg::FM][Cfg::FN],
                                               const Operand<T>& A, int32_t a_row0,
                                               const Operand<T>& B, int32_t b_row0, int32_t k_len,
@@ -272,7 +356,10 @@ __device__ __forceinline__ void tile_mainloop(f32x4_t (&acc)[Cfg::FM][Cfg::FN],
   constexpr int PER_WAVE = GROUPS / 4;  // per wave
   static_assert(GROUPS % 4 == 0 && PER_WAVE % 2 == 0 && Cfg::BM % 8 == 0,
                 "slab must split into 8-row groups");
-  static_assert(Cfg::FM * Cfg::FN > Cfg::FM + Cfg::FN, "too few MFMAs per step");
+  static_assert(Cfg::FM * Cfg::FN > Cfg::FM * (A_MN ? 2 : 1) + Cfg::FN * (B_MN ? 2 : 1),
+                "too few MFMAs per step");
+  static_assert(!(A_MN || B_MN) || (sizeof(T) == 2 && Cfg::BM == 256 && Cfg::BN == 256),
+                "MN-major operands: bf16, 256 x 256 tiles (a wave's groups in one operand)");
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave >> 1, wn = wave & 1;
@@ -280,38 +367,51 @@ __device__ __forceinline__ void tile_mainloop(f32x4_t (&acc)[Cfg::FM][Cfg::FN],
   const int lchunk = (lane & 7) ^ prow;
 
   SlabLoads<PER_WAVE> L;
+  const bool wave_b = wave * PER_WAVE * 8 >= Cfg::BM;  // uniform: this wave loads B
+  const bool wave_mn = wave_b ? B_MN : A_MN;
+  const Operand<T>& O = wave_b ? B : A;
+  L.kstride = wave_mn ? (int64_t)64 * O.ld * (int64_t)sizeof(T) : kRowBytes;
+  L.ldb = (uint32_t)(O.ld * (int64_t)sizeof(T));
+  L.kvalid = wave_mn ? O.k_valid : 0x7fffffff;
+  L.krow0 = 2 * (wave * PER_WAVE - (wave_b ? Cfg::BM / 8 : 0));
 #pragma unroll
   for (int u = 0; u < PER_WAVE; ++u) {
-    const int g = wave * PER_WAVE + u;  // uniform: which 8-row group
-    if (g * 8 < Cfg::BM) group_source(A, a_row0, g * 8 + prow, lchunk, L.base[u], L.off[u]);
-    else group_source(B, b_row0, g * 8 - Cfg::BM + prow, lchunk, L.base[u], L.off[u]);
+    const int g = wave * PER_WAVE + u;  // uniform: which 1 KB group
+    if (g * 8 < Cfg::BM) {
+      if (A_MN) group_source_mn(A, a_row0, g, lane, L.base[u], L.off[u]);
+      else group_source(A, a_row0, g * 8 + prow, lchunk, L.base[u], L.off[u]);
+    } else {
+      if (B_MN) group_source_mn(B, b_row0, g - Cfg::BM / 8, lane, L.base[u], L.off[u]);
+      else group_source(B, b_row0, g * 8 - Cfg::BM + prow, lchunk, L.base[u], L.off[u]);
+    }
   }
   L.dst = smem + wave * PER_WAVE * 1024;
 
   const int nslab = k_len / Cfg::BK;
-  const int64_t last_kbytes = (int64_t)(nslab - 1) * kRowBytes;
   // slab 0 into stage 0; slab 1 (with a single slab, a harmless reload of
   // slab 0) into stage 1
   issue_groups<PER_WAVE, 0, PER_WAVE, Cfg>(L, 0, 0);
   wait_vmem();
   __syncthreads();
-  issue_groups<PER_WAVE, 0, PER_WAVE, Cfg>(L, 1, nslab > 1 ? kRowBytes : 0);
+  issue_groups<PER_WAVE, 0, PER_WAVE, Cfg>(L, 1, nslab > 1 ? 1 : 0);
   i32x4_t fa[2][Cfg::FM], fb[2][Cfg::FN];
-  read_frags<Cfg>(smem, smem + Cfg::BM * kRowBytes, 0, lane, wm, wn, fa[0], fb[0]);
+  read_frags<Cfg, A_MN, B_MN>(smem, smem + Cfg::BM * kRowBytes, 0, lane, wm, wn, fa[0], fb[0]);
   __builtin_amdgcn_sched_barrier(0);
 
   // slab k+2's loads (clamped to the last slab: a reload into a stage that is
-  // never read again) start at slab k's step 3 and finish at slab k+1's step 0
-  auto clampk = [&](int k) { return k < nslab ? (int64_t)k * kRowBytes : last_kbytes; };
+  // never read again) start at slab k's last step and finish at slab k+1's step 0
+  auto clampk = [&](int k) { return k < nslab ? k : nslab - 1; };
   if (nslab > 1) {
-    slab_steps<T, Cfg, PER_WAVE, true, false>(acc, fa, fb, smem, 0, lane, wm, wn, L, clampk(2), 0);
+    slab_steps<T, Cfg, PER_WAVE, true, false, A_MN, B_MN>(acc, fa, fb, smem, 0, lane, wm, wn, L,
+                                                          clampk(2), 0);
     for (int ks = 1; ks + 1 < nslab; ++ks)
-      slab_steps<T, Cfg, PER_WAVE, false, false>(acc, fa, fb, smem, ks & 1, lane, wm, wn, L,
-                                                 clampk(ks + 2), clampk(ks + 1));
-    slab_steps<T, Cfg, PER_WAVE, false, true>(acc, fa, fb, smem, (nslab - 1) & 1, lane, wm, wn, L,
-                                              0, clampk(nslab));
+      slab_steps<T, Cfg, PER_WAVE, false, false, A_MN, B_MN>(acc, fa, fb, smem, ks & 1, lane, wm,
+                                                             wn, L, clampk(ks + 2), clampk(ks + 1));
+    slab_steps<T, Cfg, PER_WAVE, false, true, A_MN, B_MN>(acc, fa, fb, smem, (nslab - 1) & 1, lane,
+                                                          wm, wn, L, 0, clampk(nslab));
   } else {
-    slab_steps<T, Cfg, PER_WAVE, true, true>(acc, fa, fb, smem, 0, lane, wm, wn, L, 0, 0);
+    slab_steps<T, Cfg, PER_WAVE, true, true, A_MN, B_MN>(acc, fa, fb, smem, 0, lane, wm, wn, L, 0,
+                                                         0);
   }
   wait_vmem();      // reloads must land before LDS is reused
   __syncthreads();  // LDS is handed to the epilogue

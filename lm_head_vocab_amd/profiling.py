@@ -39,8 +39,9 @@ def trace_name(kernel: str) -> str:
     if not m:
         return kernel
     base, targs = m.group(1), m.group(2) or ""
-    if base == "k_gemm":
-        return "gemm_dW" if targs.rstrip(">").endswith("1") else "gemm_dh"
+    if base == "k_gemm":  # k_gemm<T, OutT, ROLE, LEAN>
+        args = [a.strip() for a in targs.strip("<>").split(",")]
+        return "gemm_dW" if len(args) > 2 and args[2] == "1" else "gemm_dh"
     names = {"k_stats": "stats_q", "k_stats_stage": "stats_stage", "k_dz_stage": "dz_stage",
              "k_dz": "dz", "k_div": "div", "k_combine1": "combine1", "k_combine2": "combine2",
              "k_rowdot": "rowdot", "k_transpose": "transpose", "k_validity": "validity",

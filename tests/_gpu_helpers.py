@@ -81,11 +81,14 @@ def check_argmax(gpu_y: np.ndarray, prob, rows, valid) -> None:
 
 
 def full_parity(prob, *, max_chunk_rows=0, check_grads=True, tag="", single_call=False,
-                shards=None):
+                shards=None, workspace_bytes=None, expect_copies=None):
     """Run fwd (+bwd with the mean seed) on the GPU and compare every output with the oracle.
 
     single_call: use lmhead_loss_fwd_bwd instead of the two calls.
     shards: (G, bounds or None) to run the vocabulary-parallel sequence instead.
+    workspace_bytes: workspace to give the calls (default: the library's size).
+    expect_copies: if not None, whether the backward must make transposed
+    copies (read from the kernel trace).
     """
     say(f"[parity] {tag} {prob.name} N={prob.n_rows} H={prob.hidden_dim} V={prob.vocab} "
         f"dtype={prob.dtype} weights={prob.weights} chunk={max_chunk_rows} single={single_call} "
@@ -98,7 +101,11 @@ def full_parity(prob, *, max_chunk_rows=0, check_grads=True, tag="", single_call
                              target_row=dev["target_row"], max_chunk_rows=max_chunk_rows,
                              bounds=shards[1])
     else:
-        run = make_run(prob, dev, max_chunk_rows=max_chunk_rows)
+        run = make_run(prob, dev, max_chunk_rows=max_chunk_rows, workspace_bytes=workspace_bytes)
+    trace = None
+    if expect_copies is not None:
+        trace = L.binding.Trace(capacity=4096)
+        trace.attach(run.problem)
     gm = torch.ones(1, dtype=torch.float32, device="cuda")
     if single_call:
         dh_t, dW_t = run.forward_backward(grad_mean=gm)
@@ -143,4 +150,9 @@ def full_parity(prob, *, max_chunk_rows=0, check_grads=True, tag="", single_call
         assert e_dh <= GRAD_FROB and e_dW <= GRAD_FROB
         assert np.all(dh_np[~ref.valid] == 0.0), "masked rows must get a zero gradient"
         out.update(dh=dh_np, dW=dW_np, rdh=rdh, rdW=rdW)
+    if trace is not None:
+        names = {name for name, _, _ in trace.read()}
+        run.problem.trace = None
+        trace.close()
+        assert ("gemm_dh" in names) and (("transpose_W" in names) == expect_copies), names
     return out

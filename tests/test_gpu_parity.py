@@ -452,3 +452,35 @@ def test_vocab_parallel_matches_unsharded():
     assert torch.allclose(a.flatness, b.flatness, rtol=1e-5)
     assert rel_frob(dh1.cpu().numpy(), dh2.cpu().numpy()) < 1e-3
     assert rel_frob(dW1.cpu().numpy(), dW2.cpu().numpy()) < 1e-3
+
+
+
+# ------------------------------------------------------ backward without copies
+@pytest.mark.parametrize("case", ["ce_two_calls", "ce_single", "lk_single", "kinds_two_calls",
+                                  "multihead_single"])
+def test_backward_without_transposed_copies(case):
+    """A workspace too small for the transposed copies of W, h and dz selects the
+    copy-free contractions (MN-major operands through the transposing LDS
+    load); same bar against the oracle, and no transpose in the trace."""
+    single = case.endswith("single")
+    if case.startswith("ce"):
+        p = synthetic.make_problem("ce_bf16_1b", n_rows=600, hidden_dim=192, vocab=1100)
+    elif case == "lk_single":
+        p = synthetic.make_problem("lk_hybrid_bf16_8b", n_rows=700, hidden_dim=128, vocab=900,
+                                   weights={"lk_hybrid": 1.0, "ce": 0.3})
+    elif case == "kinds_two_calls":
+        p = synthetic.make_problem("lk_hybrid_bf16_8b", n_rows=300, hidden_dim=256, vocab=777,
+                                   weights={"rkl": 0.5, "jsd": 0.5, "tv": 1.0})
+    else:
+        p = synthetic.make_problem("multihead_bf16_405b", seq_len=150, hidden_dim=128, vocab=1000)
+    import lm_head_vocab_amd as L
+    dev = to_device(p)
+    probe = make_run(p, dev, max_chunk_rows=256)
+    full = probe.workspace.numel()
+    Vp = -(-p.vocab // 256) * 256
+    copies = p.hidden_dim * Vp * 2 + p.hidden_dim * 256 * 2 + Vp * 256 * 2
+    del probe
+    full_parity(p, max_chunk_rows=256, tag=f"lean-{case}", single_call=single,
+                workspace_bytes=full - copies, expect_copies=False)
+    # and the default workspace (chunk = all rows here) makes the copies
+    full_parity(p, tag=f"copies-{case}", single_call=single, expect_copies=True)
