@@ -109,7 +109,11 @@ struct Layout {
   size_t es;
   bool copies;  // the backward contractions read transposed copies (W^T, h^T, dz^T)
   // head
-  size_t terms, saved, seed, head_end;
+  size_t terms, saved, seed, tstat, head_end;
+  // rows share target rows (a row map onto fewer target rows than rows): the
+  // target statistics are computed once per target row, then gathered
+  bool shared_target;
+  int64_t Nt;
   // forward
   size_t pz, pu, p2, zy, fwd_end;
   // backward
@@ -137,9 +141,12 @@ Layout plan(const specloss_problem* p, const KindSet& k, int64_t Nc, bool copies
     o = align_up(o + bytes, kAlign);
     return at;
   };
+  L.shared_target = k.target && p->target_row && p->n_target_rows < p->n_rows;
+  L.Nt = p->n_target_rows;
   L.terms = take((size_t)kNumKinds * L.N * 4);
   L.saved = take(specloss_saved_bytes(L.N));
   L.seed = take((size_t)L.N * 4);
+  L.tstat = take(L.shared_target ? 3 * align_up((size_t)L.Nt * 4, kAlign) : 0);
   L.head_end = o;
   const size_t tile_cols = (size_t)L.Tv * Nc * 4;
   L.pz = take(2 * tile_cols);
@@ -257,12 +264,13 @@ GemmOperand target_operand(const specloss_problem* p, int64_t r0, int64_t rows, 
 enum KernelId : int32_t {
   K_VALIDITY, K_STATS_Q, K_STATS_P, K_COMBINE1, K_ROWDOT, K_DIV, K_COMBINE2, K_REDUCE, K_COPY,
   K_SEED, K_TRANSPOSE_W, K_TRANSPOSE_H, K_DZ, K_GEMM_DH, K_GEMM_DW, K_STATS_STAGE, K_DZ_STAGE,
-  K_DIV_STAGE, K_DZ_DIV, K_TILE_SUM, K_SUM_PARTS, K_NUM_IDS
+  K_DIV_STAGE, K_DZ_DIV, K_TILE_SUM, K_SUM_PARTS, K_TARGET_GATHER, K_NUM_IDS
 };
 const char* const kKernelNames[K_NUM_IDS] = {
     "validity", "stats_q", "stats_p", "combine1", "rowdot", "div", "combine2", "reduce",
     "copy_lse", "seed", "transpose_W", "transpose_h", "dz", "gemm_dh", "gemm_dW",
-    "stats_stage", "dz_stage", "div_stage", "dz_div", "tile_sum", "sum_partials"};
+    "stats_stage", "dz_stage", "div_stage", "dz_div", "tile_sum", "sum_partials",
+    "target_gather"};
 
 // Brackets launches with the trace's events when the problem carries one.
 struct Tracer {
@@ -313,7 +321,50 @@ struct FwdBufs {
   float* p2;   // pass-2 partials [kNumSums][Tv][Nc]
   float* zy;   // gathered logits [2][Nc]
   int64_t Nc;
+  void* tstat = nullptr;  // per-target-row lse_p, argmax, flatness (shared targets)
 };
+
+// Target statistics once per target row (rows that share target rows):
+// pass 1 of W_t over target_hidden in chunks of Nc rows, merged per target row
+// into b.tstat.
+int target_prepass(const specloss_problem* p, const Layout& L, const FwdBufs& b, Tracer& tr,
+                   hipStream_t stream) {
+  const bool bf16 = p->in_dtype == SPECLOSS_BF16;
+  const int64_t H = L.H, Nc = b.Nc, tile_cols = L.Tv * Nc;
+  char* tb = static_cast<char*>(b.tstat);
+  const size_t fs = align_up((size_t)L.Nt * 4, kAlign);
+  for (int64_t t0 = 0; t0 < L.Nt; t0 += Nc) {
+    const int64_t rows = (L.Nt - t0) < Nc ? (L.Nt - t0) : Nc;
+    StatsLaunch su{};
+    su.A = op(p->W_t, H, p->vocab);
+    su.B = op(offset_rows(p->target_hidden, t0, H, L.es), H, rows);
+    su.k_len = (int32_t)H;
+    su.vocab = (int32_t)p->vocab;
+    su.tiles_m = (int32_t)L.Tv;
+    su.tiles_n = (int32_t)cdiv(rows, 256);
+    su.ncols = (int32_t)rows;
+    su.ldp = (int32_t)Nc;
+    su.pm = b.pu;
+    su.ps = b.pu + tile_cols;
+    su.pi = reinterpret_cast<int32_t*>(b.pu + 2 * tile_cols);
+    su.pq = b.pu + 3 * tile_cols;
+    TRACED(tr, K_STATS_P, 2.0 * rows * H * p->vocab, launch_stats(bf16, true, su, stream));
+    Combine1Launch c1{};
+    c1.tiles_m = (int32_t)L.Tv;
+    c1.ncols = (int32_t)rows;
+    c1.ldp = (int32_t)Nc;
+    c1.pm_u = b.pu;
+    c1.ps_u = b.pu + tile_cols;
+    c1.pi_u = reinterpret_cast<const int32_t*>(b.pu + 2 * tile_cols);
+    c1.pq_u = b.pu + 3 * tile_cols;
+    c1.vocab = (int32_t)p->vocab;
+    c1.lse_p = reinterpret_cast<float*>(tb) + t0;
+    c1.y_arg = reinterpret_cast<int32_t*>(tb + fs) + t0;
+    c1.flat = reinterpret_cast<float*>(tb + 2 * fs) + t0;
+    TRACED(tr, K_COMBINE1, 4.0 * L.Tv * rows * 4, launch_combine1(c1, stream));
+  }
+  return SPECLOSS_OK;
+}
 
 int launch_validity_for(const specloss_problem* p, const KindSet& k, const SavedView& sv,
                         int64_t* counts, Tracer& tr, hipStream_t stream, int64_t vocab = 0) {
@@ -341,7 +392,8 @@ int launch_validity_for(const specloss_problem* p, const KindSet& k, const Saved
 // Pass-1 contractions of chunk rows [r0, r0 + rows) into the per-(tile, row)
 // partials b.pz (and b.pu for the target side); `stage` as for fwd_chunk.
 int launch_pass1(const specloss_problem* p, const KindSet& k, const Layout& L, const FwdBufs& b,
-                 int64_t r0, int64_t rows, void* stage, Tracer& tr, hipStream_t stream) {
+                 int64_t r0, int64_t rows, void* stage, Tracer& tr, hipStream_t stream,
+                 bool skip_target = false) {
   const bool bf16 = p->in_dtype == SPECLOSS_BF16;
   const int64_t H = L.H, Nc = b.Nc;
   const int64_t tile_cols = L.Tv * Nc;
@@ -370,7 +422,7 @@ int launch_pass1(const specloss_problem* p, const KindSet& k, const Layout& L, c
     TRACED(tr, K_STATS_Q, 2.0 * rows * H * p->vocab, launch_stats(bf16, false, sz, stream));
   }
 
-  if (k.target) {
+  if (k.target && !skip_target) {
     StatsLaunch su = sz;
     su.A = op(p->W_t, H, p->vocab);
     su.B = target_operand(p, r0, rows, L.es);
@@ -420,8 +472,10 @@ int fwd_chunk(const specloss_problem* p, const KindSet& k, const Layout& L, cons
   const bool bf16 = p->in_dtype == SPECLOSS_BF16;
   const int64_t H = L.H, Nc = b.Nc;
   const int64_t tile_cols = L.Tv * Nc;
+  const bool own_target = k.target && !L.shared_target;
   {
-    const int rc = launch_pass1(p, k, L, b, r0, rows, stage_d ? nullptr : stage, tr, stream);
+    const int rc = launch_pass1(p, k, L, b, r0, rows, stage_d ? nullptr : stage, tr, stream,
+                                !own_target);
     if (rc) return rc;
   }
 
@@ -431,17 +485,33 @@ int fwd_chunk(const specloss_problem* p, const KindSet& k, const Layout& L, cons
   c1.ldp = (int32_t)Nc;
   c1.pm_z = b.pz;
   c1.ps_z = b.pz + tile_cols;
-  c1.pm_u = k.target ? b.pu : nullptr;
-  c1.ps_u = k.target ? b.pu + tile_cols : nullptr;
-  c1.pi_u = k.target ? reinterpret_cast<const int32_t*>(b.pu + 2 * tile_cols) : nullptr;
-  c1.pq_u = k.target ? b.pu + 3 * tile_cols : nullptr;
+  c1.pm_u = own_target ? b.pu : nullptr;
+  c1.ps_u = own_target ? b.pu + tile_cols : nullptr;
+  c1.pi_u = own_target ? reinterpret_cast<const int32_t*>(b.pu + 2 * tile_cols) : nullptr;
+  c1.pq_u = own_target ? b.pu + 3 * tile_cols : nullptr;
   c1.vocab = (int32_t)p->vocab;
   c1.flags = sv.flags + r0;
   c1.lse_q = sv.lse_q + r0;
   c1.lse_p = sv.lse_p + r0;
   c1.y_arg = sv.y_arg + r0;
   c1.flat = sv.flat + r0;
-  TRACED(tr, K_COMBINE1, (k.target ? 6.0 : 2.0) * L.Tv * rows * 4, launch_combine1(c1, stream));
+  TRACED(tr, K_COMBINE1, (own_target ? 6.0 : 2.0) * L.Tv * rows * 4, launch_combine1(c1, stream));
+  if (L.shared_target) {
+    const char* tb = reinterpret_cast<const char*>(b.tstat);
+    const size_t fs = align_up((size_t)L.Nt * 4, kAlign);
+    TargetGatherLaunch tg{};
+    tg.ncols = (int32_t)rows;
+    tg.r0 = r0;
+    tg.flags = sv.flags;
+    tg.target_row = p->target_row;
+    tg.t_lse_p = reinterpret_cast<const float*>(tb);
+    tg.t_y_arg = reinterpret_cast<const int32_t*>(tb + fs);
+    tg.t_flat = reinterpret_cast<const float*>(tb + 2 * fs);
+    tg.lse_p = sv.lse_p;
+    tg.y_arg = sv.y_arg;
+    tg.flat = sv.flat;
+    TRACED(tr, K_TARGET_GATHER, (double)rows * 24, launch_target_gather(tg, stream));
+  }
 
   const bool ce_lab = (k.active >> SPECLOSS_CE_LABEL) & 1u;
   const bool ce_arg = (k.active >> SPECLOSS_CE_ARGMAX_P) & 1u;
@@ -757,10 +827,12 @@ int lmhead_loss_fwd(const specloss_problem* p, void* workspace, size_t ws_bytes,
   const SavedView sv = saved_view(saved ? saved : ws + L.saved, N);
   float* terms = term_loss ? term_loss : reinterpret_cast<float*>(ws + L.terms);
   const FwdBufs b{reinterpret_cast<float*>(ws + L.pz), reinterpret_cast<float*>(ws + L.pu),
-                  reinterpret_cast<float*>(ws + L.p2), reinterpret_cast<float*>(ws + L.zy), Nc};
+                  reinterpret_cast<float*>(ws + L.p2), reinterpret_cast<float*>(ws + L.zy), Nc,
+                  ws + L.tstat};
   Tracer tr{p->trace, stream};
 
   TRY(launch_validity_for(p, k, sv, counts, tr, stream));
+  if (L.shared_target) TRY(target_prepass(p, L, b, tr, stream));
   for (int64_t r0 = 0; r0 < N; r0 += Nc) {
     const int64_t rows = (N - r0) < Nc ? (N - r0) : Nc;
     TRY(fwd_chunk(p, k, L, b, sv, loss, terms, r0, rows, nullptr, nullptr, tr, stream));
@@ -819,7 +891,7 @@ int lmhead_loss_fwd_bwd(const specloss_problem* p, void* workspace, size_t ws_by
   float* seed = reinterpret_cast<float*>(ws + L.seed);
   const FwdBufs b{reinterpret_cast<float*>(ws + L.f_pz), reinterpret_cast<float*>(ws + L.f_pu),
                   k.stage_div ? reinterpret_cast<float*>(ws + L.f_p2) : nullptr,
-                  reinterpret_cast<float*>(ws + L.f_zy), Nc};
+                  reinterpret_cast<float*>(ws + L.f_zy), Nc, ws + L.tstat};
   const bool copies = L.copies;
   void* wt = copies ? ws + L.f_wt : nullptr;
   void* ht = copies ? ws + L.f_ht : nullptr;
@@ -830,6 +902,7 @@ int lmhead_loss_fwd_bwd(const specloss_problem* p, void* workspace, size_t ws_by
 
   TRY(launch_validity_for(p, k, sv, counts, tr, stream));
   TRY(launch_seed_for(p, sv, grad_loss, grad_mean, counts, seed, tr, stream));
+  if (L.shared_target) TRY(target_prepass(p, L, b, tr, stream));
   if (dhidden && copies)
     TRACED(tr, K_TRANSPOSE_W, 2.0 * Vp * H * L.es, launch_transpose(bf16, p->W, V, H, wt, Vp, stream));
   int chunk = 0;

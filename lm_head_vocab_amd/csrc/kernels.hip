@@ -806,9 +806,11 @@ __global__ __launch_bounds__(256) void k_combine1(Combine1Launch a) {
   if (c < a.ncols) {
     float m, s, q;
     int best;
-    seg_lse(a.pm_z, a.ps_z, nullptr, a.ldp, c, t0, t1, m, s, q, best);
-    sm[0][seg][rr] = m;
-    ss[0][seg][rr] = s;
+    if (a.pm_z) {
+      seg_lse(a.pm_z, a.ps_z, nullptr, a.ldp, c, t0, t1, m, s, q, best);
+      sm[0][seg][rr] = m;
+      ss[0][seg][rr] = s;
+    }
     if (a.pm_u) {
       seg_lse(a.pm_u, a.ps_u, a.pq_u, a.ldp, c, t0, t1, m, s, q, best);
       sm[1][seg][rr] = m;
@@ -819,7 +821,7 @@ __global__ __launch_bounds__(256) void k_combine1(Combine1Launch a) {
   }
   __syncthreads();
   if (seg != 0 || c >= a.ncols) return;
-  for (int side = 0; side < (a.pm_u ? 2 : 1); ++side) {
+  for (int side = a.pm_z ? 0 : 1; side < (a.pm_u ? 2 : 1); ++side) {
     float m = -INFINITY;
     int bseg = 0;
     for (int g = 0; g < SEG; ++g)
@@ -850,7 +852,7 @@ __global__ __launch_bounds__(256) void k_combine1(Combine1Launch a) {
       const int bt = sb[bseg][rr];  // -1 only when no tile has a finite maximum
       a.y_arg[c] = bt >= 0 ? a.pi_u[(int64_t)bt * a.ldp + c] : -1;
       // cos(p, uniform) = sum p / (sqrt(V) |p|) = s / (sqrt(V q)), with p = e / s
-      a.flat[c] = (bt >= 0 && a.flags[c]) ? s / sqrtf((float)a.vocab * q) : 0.0f;
+      a.flat[c] = (bt >= 0 && (!a.flags || a.flags[c])) ? s / sqrtf((float)a.vocab * q) : 0.0f;
     }
   }
   if (!a.pm_u && !a.raw_m[0]) {
@@ -858,6 +860,19 @@ __global__ __launch_bounds__(256) void k_combine1(Combine1Launch a) {
     a.y_arg[c] = -1;
     a.flat[c] = 0.0f;
   }
+}
+
+// Target statistics of rows that share target rows: row gr takes those of
+// its target row (valid rows), or the no-target values.
+__global__ __launch_bounds__(256) void k_target_gather(TargetGatherLaunch a) {
+  const int c = blockIdx.x * 256 + threadIdx.x;
+  if (c >= a.ncols) return;
+  const int64_t gr = a.r0 + c;
+  const bool valid = a.flags[gr] != 0;
+  const int32_t t = valid ? a.target_row[gr] : 0;  // in range on valid rows
+  a.lse_p[gr] = valid ? a.t_lse_p[t] : 0.0f;
+  a.y_arg[gr] = valid ? a.t_y_arg[t] : -1;
+  a.flat[gr] = valid ? a.t_flat[t] : 0.0f;
 }
 
 // sums over the vocabulary tiles of one shard: out[f][c] = sum_t part[f][t][c]
@@ -1115,6 +1130,11 @@ hipError_t launch_combine1(const Combine1Launch& a, hipStream_t s) {
 
 hipError_t launch_combine2(const Combine2Launch& a, hipStream_t s) {
   hipLaunchKernelGGL(k_combine2, dim3((a.ncols + 255) / 256), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_target_gather(const TargetGatherLaunch& a, hipStream_t s) {
+  hipLaunchKernelGGL(k_target_gather, dim3((a.ncols + 255) / 256), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -166,6 +166,7 @@ struct RowdotLaunch {
 };
 hipError_t launch_rowdot(bool bf16, const RowdotLaunch& a, hipStream_t s);
 
+// pm_z null: target side only; flags null: every column counts as valid
 struct Combine1Launch {
   int32_t tiles_m, ncols, ldp;
   const float* pm_z;
@@ -190,6 +191,21 @@ struct Combine1Launch {
   int32_t idx_offset;
 };
 hipError_t launch_combine1(const Combine1Launch& a, hipStream_t s);
+
+// per-row target statistics from per-target-row ones (rows sharing target rows)
+struct TargetGatherLaunch {
+  int32_t ncols;
+  int64_t r0;                 // global row of chunk column 0
+  const int32_t* flags;       // [N] global
+  const int32_t* target_row;  // [N] global
+  const float* t_lse_p;       // [n_target_rows]
+  const int32_t* t_y_arg;
+  const float* t_flat;
+  float* lse_p;               // [N] global
+  int32_t* y_arg;
+  float* flat;
+};
+hipError_t launch_target_gather(const TargetGatherLaunch& a, hipStream_t s);
 
 struct TileSumLaunch {
   int32_t tiles_m, ncols, ldp;

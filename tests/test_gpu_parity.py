@@ -484,3 +484,36 @@ def test_backward_without_transposed_copies(case):
                 workspace_bytes=full - copies, expect_copies=False)
     # and the default workspace (chunk = all rows here) makes the copies
     full_parity(p, tag=f"copies-{case}", single_call=single, expect_copies=True)
+
+
+@pytest.mark.parametrize("single", [False, True])
+def test_shared_target_rows_match_per_row(single):
+    """Rows that share target rows (three aligned heads) take their target
+    statistics from one pass over the distinct target rows; the same problem
+    with every row's target copied out (no sharing) gives the same bits."""
+    p = synthetic.make_problem("multihead_bf16_405b", seq_len=200, hidden_dim=128, vocab=900,
+                               weights={"ce": 0.4, "tv": 0.6})
+    assert p.target_hidden.shape[0] < p.n_rows
+    tr = np.where(p.target_row >= 0, p.target_row, 0)
+    q = synthetic.make_problem("multihead_bf16_405b", seq_len=200, hidden_dim=128, vocab=900,
+                               weights={"ce": 0.4, "tv": 0.6})
+    q.target_hidden = p.target_hidden[tr].copy()
+    q.target_row = None
+    gm = torch.ones(1, device="cuda")
+    outs = []
+    for prob in (p, q):
+        run = make_run(prob, to_device(prob), max_chunk_rows=256)
+        if single:
+            dh, dW = run.forward_backward(grad_mean=gm)
+        else:
+            run.forward()
+            dh, dW = run.backward(grad_mean=gm)
+        torch.cuda.synchronize()
+        outs.append(dict(loss=run.loss.cpu(), lse_p=run.saved_field(1).cpu(),
+                         y=run.saved_field(3, torch.int32).cpu(), alpha=run.saved_field(4).cpu(),
+                         flat=run.flatness.cpu(), dh=dh.cpu(), dW=dW.cpu()))
+    a, b = outs
+    valid = torch.from_numpy(p.mask.astype(bool))
+    for k in ("loss", "lse_p", "y", "alpha", "flat"):
+        assert torch.equal(a[k][valid], b[k][valid]), k
+    assert torch.equal(a["dh"], b["dh"]) and torch.equal(a["dW"], b["dW"])
