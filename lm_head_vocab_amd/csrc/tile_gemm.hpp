@@ -286,8 +286,8 @@ __device__ __forceinline__ void read_frags(const char* sa, const char* sb, int s
 // 1's fragments; step 1 (unless LAST) waits for slab k+1, meets the other
 // waves at the barrier (all of them now hold step 1's fragments, so this
 // stage is free), issues the first half of slab k+2 into it and reads slab
-// k+1's step-0 fragments.  Inside a step, fragment reads and
-// loads are interleaved with the MFMAs so they land while the rest run.
+// k+1's step-0 fragments.  Inside a step, loads and fragment reads are
+// interleaved with the MFMAs so they land while the rest run.
 template <typename T, typename Cfg, int PER_WAVE, bool FIRST, bool LAST, bool A_MN, bool B_MN>
 __device__ __forceinline__ void slab_steps(f32x4_t (&acc)[Cfg::FM][Cfg::FN],
                                            i32x4_t (&fa)[2][Cfg::FM], i32x4_t (&fb)[2][Cfg::FN],
@@ -297,8 +297,8 @@ __device__ __forceinline__ void slab_steps(f32x4_t (&acc)[Cfg::FM][Cfg::FN],
   // LDS read instructions per step: one per K-major fragment, two per MN-major one
   constexpr int kR = Cfg::FM * (A_MN ? 2 : 1) + Cfg::FN * (B_MN ? 2 : 1);
   constexpr int kH = PER_WAVE / 2;
-  constexpr int kSlots = Cfg::FM * Cfg::FN - kR;  // MFMA slots left after the reads
-  constexpr int kPerSlot = (PER_WAVE + kSlots - 1) / kSlots;
+  constexpr int kRest = Cfg::FM * Cfg::FN - kH - kR;  // MFMAs after the loads and reads
+  static_assert(kRest >= 0, "too few MFMAs per step for the interleave");
   const char* sa = smem + stage * Cfg::STAGE;
   const char* sb = sa + Cfg::BM * kRowBytes;
 #pragma unroll
@@ -319,20 +319,24 @@ __device__ __forceinline__ void slab_steps(f32x4_t (&acc)[Cfg::FM][Cfg::FN],
 #pragma unroll
       for (int j = 0; j < Cfg::FN; ++j) mfma_slab_step<T>(acc[i][j], fa[s & 1][i], fb[s & 1][j]);
     if (s < kSteps - 1 || !LAST) {
+      // the step's slab loads go first, one per MFMA, then the fragment reads
+      // for the next step, one per MFMA, then the remaining MFMAs (measured
+      // about 2% faster than reads first)
+      if (loads) {
+#pragma unroll
+        for (int q = 0; q < kH; ++q) {
+          __builtin_amdgcn_sched_group_barrier(0x008, kMfmaPerPair<T>, 0);  // MFMA
+          __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);                 // slab load
+        }
+      } else {
+        __builtin_amdgcn_sched_group_barrier(0x008, kH * kMfmaPerPair<T>, 0);
+      }
 #pragma unroll
       for (int q = 0; q < kR; ++q) {
         __builtin_amdgcn_sched_group_barrier(0x008, kMfmaPerPair<T>, 0);  // MFMA
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                 // LDS read
       }
-      if (loads) {
-#pragma unroll
-        for (int q = 0; q < kSlots; ++q) {
-          __builtin_amdgcn_sched_group_barrier(0x008, kMfmaPerPair<T>, 0);  // MFMA
-          __builtin_amdgcn_sched_group_barrier(0x020, kPerSlot, 0);          // slab loads
-        }
-      } else {
-        __builtin_amdgcn_sched_group_barrier(0x008, kSlots * kMfmaPerPair<T>, 0);
-      }
+      __builtin_amdgcn_sched_group_barrier(0x008, kRest * kMfmaPerPair<T>, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
   }
