@@ -29,6 +29,9 @@ namespace specloss {
 // 4 x 8 tiles measured best for every contraction of the path (1, 2 and 8
 // were slower at the 8B shape).
 constexpr int kGroupM = 4;
+// MFMAs between consecutive slab loads in pass 1 (3) and in the plain
+// contractions (1): measured best of 1 to 4 on each at the 8B shape.
+constexpr int kStatsLoadGap = 3;
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
@@ -118,7 +121,7 @@ __device__ __forceinline__ void load_chunk(const T* src, float (&out)[KC]) {
 template <typename T, bool TARGET>
 __global__ __launch_bounds__(kThreads, 1) void k_stats(StatsLaunch a) {
   constexpr bool ARGMAX = TARGET;
-  using Cfg = TileCfg<T, 256, 256>;
+  using Cfg = TileCfg<T, 256, 256, kStatsLoadGap>;
   __shared__ __attribute__((aligned(16))) char smem[Cfg::LDS_BYTES];
   int tm, tn;
   if (!tile_of(a.tiles_m, a.tiles_n, kGroupM, tm, tn)) return;
@@ -225,7 +228,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_stats(StatsLaunch a) {
 // summed and stored (rounded to the storage type) for the backward.
 template <typename T>
 __global__ __launch_bounds__(kThreads, 1) void k_stats_stage(StatsStageLaunch a) {
-  using Cfg = TileCfg<T, 256, 256>;
+  using Cfg = TileCfg<T, 256, 256, kStatsLoadGap>;
   __shared__ __attribute__((aligned(16))) char smem[Cfg::LDS_BYTES];
   const StatsLaunch& st = a.st;
   int tm, tn;

@@ -67,9 +67,10 @@ struct ElemTraits<float> {
 constexpr int kFrag = 16;   // MFMA output fragment: 16 x 16
 constexpr int kSteps = 2;   // k-steps per slab (4 chunks of 16 bytes per step)
 
-template <typename T, int BM_, int BN_>
+// LGAP: MFMAs between consecutive slab loads of a step
+template <typename T, int BM_, int BN_, int LGAP_ = 1>
 struct TileCfg {
-  static constexpr int BM = BM_, BN = BN_;
+  static constexpr int BM = BM_, BN = BN_, LGAP = LGAP_;
   static constexpr int KC = ElemTraits<T>::kPerChunk;  // elements per 16-byte chunk
   static constexpr int BK = 8 * KC;                    // elements per slab row (128 bytes)
   static constexpr int WM = BM / 2, WN = BN / 2;       // wave sub-tile
@@ -297,7 +298,7 @@ __device__ __forceinline__ void slab_steps(f32x4_t (&acc)[Cfg::FM][Cfg::FN],
   // LDS read instructions per step: one per K-major fragment, two per MN-major one
   constexpr int kR = Cfg::FM * (A_MN ? 2 : 1) + Cfg::FN * (B_MN ? 2 : 1);
   constexpr int kH = PER_WAVE / 2;
-  constexpr int kRest = Cfg::FM * Cfg::FN - kH - kR;  // MFMAs after the loads and reads
+  constexpr int kRest = Cfg::FM * Cfg::FN - kH * Cfg::LGAP - kR;  // MFMAs after loads and reads
   static_assert(kRest >= 0, "too few MFMAs per step for the interleave");
   const char* sa = smem + stage * Cfg::STAGE;
   const char* sb = sa + Cfg::BM * kRowBytes;
@@ -329,17 +330,17 @@ __device__ __forceinline__ void slab_steps(f32x4_t (&acc)[Cfg::FM][Cfg::FN],
       mfma_slab_step<T>(acc[q / Cfg::FN][q % Cfg::FN], fa[s & 1][q / Cfg::FN],
                         fb[s & 1][q % Cfg::FN]);
     if (s < kSteps - 1 || !LAST) {
-      // the step's slab loads go first, one per MFMA, then the fragment reads
-      // for the next step, one per MFMA, then the remaining MFMAs (measured
-      // about 2% faster than reads first)
+      // the step's slab loads go first, one per LGAP MFMAs, then the fragment
+      // reads for the next step, one per MFMA, then the remaining MFMAs
+      // (measured about 2% faster than reads first)
       if (loads) {
 #pragma unroll
         for (int q = 0; q < kH; ++q) {
-          __builtin_amdgcn_sched_group_barrier(0x008, kMfmaPerPair<T>, 0);  // MFMA
-          __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);                 // slab load
+          __builtin_amdgcn_sched_group_barrier(0x008, Cfg::LGAP * kMfmaPerPair<T>, 0);  // MFMA
+          __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // slab load
         }
       } else {
-        __builtin_amdgcn_sched_group_barrier(0x008, kH * kMfmaPerPair<T>, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, kH * Cfg::LGAP * kMfmaPerPair<T>, 0);
       }
 #pragma unroll
       for (int q = 0; q < kR; ++q) {
