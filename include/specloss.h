@@ -77,6 +77,16 @@ enum {
 #define SPECLOSS_IGNORE_INDEX (-100)
 
 /*
+ * Backward layout choice (specloss_problem.flags).  0: automatic (see
+ * lmhead_loss_workspace_size).  SPECLOSS_FLAG_COPIES: always make the
+ * transposed copies (SPECLOSS_E_WORKSPACE if they do not fit).
+ * SPECLOSS_FLAG_NO_COPIES: never (bf16 only, SPECLOSS_E_UNSUPPORTED for fp32).
+ * Other values: SPECLOSS_E_INVAL.
+ */
+#define SPECLOSS_FLAG_COPIES 1
+#define SPECLOSS_FLAG_NO_COPIES 2
+
+/*
  * Per-row state the forward saves for the backward: SPECLOSS_SAVED_FIELDS
  * arrays of N 4-byte values each (see specloss_saved_offset).  The fields a
  * caller may want to read are listed here; the others are internal.
@@ -115,7 +125,7 @@ typedef struct {
   int64_t hidden;              /* H > 0, multiple of 64 */
   int64_t vocab;               /* V > 0, < 2^31 */
   int32_t in_dtype;            /* specloss_dtype of hidden_states, W, target_hidden, W_t */
-  int32_t reserved;            /* must be 0 */
+  int32_t flags;               /* 0, or one of SPECLOSS_FLAG_* (backward layout choice) */
   const void* hidden_states;   /* [N, H] draft hidden states */
   const void* W;               /* [V, H] draft LM-head weight */
   const int32_t* labels;       /* [N] token labels, or NULL when no label kind is on */

@@ -38,7 +38,7 @@ class Problem(ctypes.Structure):
         ("hidden", ctypes.c_int64),
         ("vocab", ctypes.c_int64),
         ("in_dtype", ctypes.c_int32),
-        ("reserved", ctypes.c_int32),
+        ("flags", ctypes.c_int32),
         ("hidden_states", ctypes.c_void_p),
         ("W", ctypes.c_void_p),
         ("labels", ctypes.c_void_p),
@@ -182,8 +182,11 @@ def _check(code: int, what: str) -> None:
 def make_problem(hidden: torch.Tensor, W: torch.Tensor, weights: Dict[str, float], *,
                  labels: Optional[torch.Tensor] = None, mask: Optional[torch.Tensor] = None,
                  target_hidden: Optional[torch.Tensor] = None, W_t: Optional[torch.Tensor] = None,
-                 target_row: Optional[torch.Tensor] = None) -> Problem:
-    """Fill a ``specloss_problem`` from torch tensors (no copies, no checks beyond dtype)."""
+                 target_row: Optional[torch.Tensor] = None, flags: int = 0) -> Problem:
+    """Fill a ``specloss_problem`` from torch tensors (no copies, no checks beyond dtype).
+
+    flags: 0 (automatic), FLAG_COPIES or FLAG_NO_COPIES (backward layout).
+    """
     if hidden.dtype not in (torch.float32, torch.bfloat16) or W.dtype != hidden.dtype:
         raise ValueError("hidden and W must both be float32 or both bfloat16")
     p = Problem()
@@ -191,7 +194,7 @@ def make_problem(hidden: torch.Tensor, W: torch.Tensor, weights: Dict[str, float
     p.hidden = hidden.shape[1]
     p.vocab = W.shape[0]
     p.in_dtype = BF16 if hidden.dtype == torch.bfloat16 else F32
-    p.reserved = 0
+    p.flags = flags
     p.hidden_states = _ptr(hidden)
     p.W = _ptr(W)
     p.labels = _ptr(labels)
@@ -217,6 +220,9 @@ def lmhead_loss_workspace_size(problem: Problem, max_chunk_rows: int = 0) -> int
 def specloss_saved_bytes(n_rows: int) -> int:
     return int(load_library().specloss_saved_bytes(n_rows))
 
+
+# backward layout choice (SPECLOSS_FLAG_* in include/specloss.h)
+FLAG_COPIES, FLAG_NO_COPIES = 1, 2
 
 # public saved fields (SPECLOSS_SAVED_* in include/specloss.h)
 SAVED_LSE_Q, SAVED_LSE_P, SAVED_Y_ARG, SAVED_ALPHA, SAVED_VALID, SAVED_FLATNESS = 0, 1, 3, 4, 8, 9

@@ -71,9 +71,12 @@ int check_problem(const specloss_problem* p, KindSet* ks) {
   if (p->n_rows <= 0 || p->hidden <= 0 || p->vocab <= 0) return SPECLOSS_E_INVAL;
   if (p->n_rows > INT32_MAX / 2 || p->vocab > INT32_MAX / 2 || p->hidden > INT32_MAX / 2)
     return SPECLOSS_E_UNSUPPORTED;
-  if (p->reserved != 0) return SPECLOSS_E_INVAL;
+  if (p->flags != 0 && p->flags != SPECLOSS_FLAG_COPIES && p->flags != SPECLOSS_FLAG_NO_COPIES)
+    return SPECLOSS_E_INVAL;
   if (p->in_dtype != SPECLOSS_F32 && p->in_dtype != SPECLOSS_BF16) return SPECLOSS_E_UNSUPPORTED;
   if (p->hidden % 64 != 0) return SPECLOSS_E_UNSUPPORTED;
+  if (p->flags == SPECLOSS_FLAG_NO_COPIES && p->in_dtype != SPECLOSS_BF16)
+    return SPECLOSS_E_UNSUPPORTED;
   if (!p->hidden_states || !p->W) return SPECLOSS_E_INVAL;
   if (!aligned(p->hidden_states, 16) || !aligned(p->W, 16)) return SPECLOSS_E_UNSUPPORTED;
   for (int i = 0; i < kNumKinds; ++i)
@@ -182,6 +185,7 @@ size_t region_end(const Layout& L, Region r) {
   return r == REGION_FWD ? L.fwd_end : (r == REGION_BWD ? L.bwd_end : L.fused_end);
 }
 
+// Largest chunk (multiple of 256) whose region fits.
 int64_t largest_chunk(const specloss_problem* p, const KindSet& k, size_t ws_bytes,
                       Region region, bool copies) {
   const int64_t top = round_up(p->n_rows, kChunkQuantum);
@@ -205,17 +209,25 @@ int64_t largest_chunk(const specloss_problem* p, const KindSet& k, size_t ws_byt
 // (The copy-free contractions run about 1.5x slower; below about 1000 rows
 // per chunk the fp32 read-modify-write of dW per chunk costs more than that
 // at the large shapes.)
+// flags force the choice (SPECLOSS_FLAG_COPIES / _NO_COPIES).
 int64_t pick_chunk(const specloss_problem* p, const KindSet& k, size_t ws_bytes, Region region,
                    bool* copies = nullptr) {
-  const int64_t with = largest_chunk(p, k, ws_bytes, region, true);
+  if (copies && p->flags == SPECLOSS_FLAG_NO_COPIES) {
+    *copies = false;
+    return largest_chunk(p, k, ws_bytes, region, false);
+  }
+  int64_t nc = largest_chunk(p, k, ws_bytes, region, true);
   if (copies) *copies = true;
-  if (!copies || p->in_dtype != SPECLOSS_BF16) return with;
+  if (!copies) return nc;
   const int64_t top = round_up(p->n_rows, kChunkQuantum);
-  if (with >= (top < 1024 ? top : 1024)) return with;
-  const int64_t without = largest_chunk(p, k, ws_bytes, region, false);
-  if (without <= with) return with;
-  *copies = false;
-  return without;
+  if (p->flags == 0 && p->in_dtype == SPECLOSS_BF16 && nc < (top < 1024 ? top : 1024)) {
+    const int64_t without = largest_chunk(p, k, ws_bytes, region, false);
+    if (without > nc) {
+      *copies = false;
+      return without;
+    }
+  }
+  return nc;
 }
 
 SavedView saved_view(void* base, int64_t n) {
@@ -590,65 +602,70 @@ int launch_seed_for(const specloss_problem* p, const SavedView& sv, const float*
   return SPECLOSS_OK;
 }
 
-// dh rows [r0, r0 + rows) = dz W and dW (+)= dz^T h for one chunk from the
-// staged dz [Nc][Vp] and the copies W^T [H][Vp], h^T [H][Nc], dz^T [Vp][Nc];
-// without copies (bf16), W, the hidden chunk and dz are read as they are
-// (MN-major operands).
-int bwd_contract(const specloss_problem* p, const Layout& L, int64_t Nc, const void* dz,
-                 const void* dzt, const void* wt, const void* ht, int64_t r0, int64_t rows,
-                 bool accumulate, void* dhidden, int32_t dh_dtype, float* dW, Tracer& tr,
-                 hipStream_t stream) {
+// dh rows [r0, r0 + rows) = dz W for one chunk from the staged dz [Nc][Vp]
+// and the copy W^T [H][Vp]; without copies (bf16), W is read as it is (an
+// MN-major operand).
+int contract_dh(const specloss_problem* p, const Layout& L, int64_t Nc, const void* dz,
+                const void* wt, int64_t r0, int64_t rows, void* dhidden, int32_t dh_dtype,
+                Tracer& tr, hipStream_t stream) {
   const bool bf16 = p->in_dtype == SPECLOSS_BF16;
   const int64_t H = L.H, V = L.V, Vp = L.Vp;
   const size_t dh_es = dh_dtype == SPECLOSS_BF16 ? 2 : 4;
-  const bool lean = !L.copies;
-  if (dhidden) {
-    GemmLaunch g{};
-    g.A = op(dz, Vp, Nc);
-    g.lean = lean;
-    if (lean) {
-      g.B = op(p->W, H, H);  // element (h, v) at W[v * H + h]
-      g.B.k_valid = (int32_t)V;
-      g.k_len = (int32_t)round_up(V, 64);
-    } else {
-      g.B = op(wt, Vp, H);
-      g.k_len = (int32_t)Vp;
-    }
-    g.tiles_m = (int32_t)cdiv(rows, 256);
-    g.tiles_n = (int32_t)cdiv(H, 256);
-    g.m_valid = (int32_t)rows;
-    g.n_valid = (int32_t)H;
-    g.C = static_cast<char*>(dhidden) + (size_t)r0 * H * dh_es;
-    g.ldc = H;
-    g.accumulate = 0;
-    g.out_bf16 = dh_dtype == SPECLOSS_BF16;
-    g.role = 0;
-    TRACED(tr, K_GEMM_DH, 2.0 * rows * H * V, launch_gemm(bf16, g, stream));
+  GemmLaunch g{};
+  g.A = op(dz, Vp, Nc);
+  g.lean = !L.copies;
+  if (g.lean) {
+    g.B = op(p->W, H, H);  // element (h, v) at W[v * H + h]
+    g.B.k_valid = (int32_t)V;
+    g.k_len = (int32_t)round_up(V, 64);
+  } else {
+    g.B = op(wt, Vp, H);
+    g.k_len = (int32_t)Vp;
   }
-  if (dW) {
-    GemmLaunch g{};
-    g.k_len = (int32_t)round_up(rows, 64);
-    g.lean = lean;
-    if (lean) {
-      g.A = op(dz, Vp, Vp);  // element (v, c) at dz[c * Vp + v]; rows >= `rows` hold 0
-      g.A.k_valid = (int32_t)Nc;
-      g.B = op(offset_rows(p->hidden_states, r0, H, L.es), H, H);  // (h, c) at h[c * H + h]
-      g.B.k_valid = (int32_t)(L.N - r0);
-    } else {
-      g.A = op(dzt, Nc, Vp);
-      g.B = op(ht, Nc, H);
-    }
-    g.tiles_m = (int32_t)L.Tv;
-    g.tiles_n = (int32_t)cdiv(H, 256);
-    g.m_valid = (int32_t)V;
-    g.n_valid = (int32_t)H;
-    g.C = dW;
-    g.ldc = H;
-    g.accumulate = accumulate ? 1 : 0;
-    g.out_bf16 = 0;
-    g.role = 1;
-    TRACED(tr, K_GEMM_DW, 2.0 * rows * H * V, launch_gemm(bf16, g, stream));
+  g.tiles_m = (int32_t)cdiv(rows, 256);
+  g.tiles_n = (int32_t)cdiv(H, 256);
+  g.m_valid = (int32_t)rows;
+  g.n_valid = (int32_t)H;
+  g.C = static_cast<char*>(dhidden) + (size_t)r0 * H * dh_es;
+  g.ldc = H;
+  g.accumulate = 0;
+  g.out_bf16 = dh_dtype == SPECLOSS_BF16;
+  g.role = 0;
+  TRACED(tr, K_GEMM_DH, 2.0 * rows * H * V, launch_gemm(bf16, g, stream));
+  return SPECLOSS_OK;
+}
+
+// dW (+)= dz^T h over `rows` consecutive rows starting at global row r0:
+// with copies from dz^T [Vp][ld] and h^T [H][ld] (their first `rows` columns;
+// columns up to the next multiple of 64 hold zeros); without copies (bf16)
+// from dz [Nc][Vp] and the hidden rows themselves (MN-major operands).
+int contract_dW(const specloss_problem* p, const Layout& L, int64_t Nc, const void* dz,
+                const void* dzt, const void* ht, int64_t ld, int64_t r0, int64_t rows,
+                bool accumulate, float* dW, Tracer& tr, hipStream_t stream) {
+  const bool bf16 = p->in_dtype == SPECLOSS_BF16;
+  const int64_t H = L.H, V = L.V, Vp = L.Vp;
+  GemmLaunch g{};
+  g.k_len = (int32_t)round_up(rows, 64);
+  g.lean = !L.copies;
+  if (g.lean) {
+    g.A = op(dz, Vp, Vp);  // element (v, c) at dz[c * Vp + v]; rows >= `rows` hold 0
+    g.A.k_valid = (int32_t)Nc;
+    g.B = op(offset_rows(p->hidden_states, r0, H, L.es), H, H);  // (h, c) at h[c * H + h]
+    g.B.k_valid = (int32_t)(L.N - r0);
+  } else {
+    g.A = op(dzt, ld, Vp);
+    g.B = op(ht, ld, H);
   }
+  g.tiles_m = (int32_t)L.Tv;
+  g.tiles_n = (int32_t)cdiv(H, 256);
+  g.m_valid = (int32_t)V;
+  g.n_valid = (int32_t)H;
+  g.C = dW;
+  g.ldc = H;
+  g.accumulate = accumulate ? 1 : 0;
+  g.out_bf16 = 0;
+  g.role = 1;
+  TRACED(tr, K_GEMM_DW, 2.0 * rows * H * V, launch_gemm(bf16, g, stream));
   return SPECLOSS_OK;
 }
 
@@ -747,8 +764,10 @@ int bwd_recompute(const specloss_problem* p, const KindSet& k, const float* grad
     dl.ld_dzt = Nc;
     dl.vocab_offset = (int32_t)vocab_offset;
     TRACED(tr, K_DZ, (k.dual_bwd ? 4.0 : 2.0) * rows * H * V, launch_dz(bf16, k.dual_bwd, dl, stream));
-    TRY(bwd_contract(p, L, Nc, dz, dzt, wt, ht, r0, rows, chunk > 0 || accumulate_dW, dhidden,
-                     dh_dtype, dW, tr, stream));
+    if (dhidden) TRY(contract_dh(p, L, Nc, dz, wt, r0, rows, dhidden, dh_dtype, tr, stream));
+    if (dW)
+      TRY(contract_dW(p, L, Nc, dz, dzt, ht, Nc, r0, rows, chunk > 0 || accumulate_dW, dW, tr,
+                      stream));
   }
   return SPECLOSS_OK;
 }
@@ -936,8 +955,10 @@ int lmhead_loss_fwd_bwd(const specloss_problem* p, void* workspace, size_t ws_by
     const void* hc = offset_rows(p->hidden_states, r0, H, L.es);
     if (dW && copies)
       TRACED(tr, K_TRANSPOSE_H, 2.0 * Nc * H * L.es, launch_transpose(bf16, hc, rows, H, ht, Nc, stream));
-    TRY(bwd_contract(p, L, Nc, dz, dzt, wt, ht, r0, rows, chunk > 0 || accumulate_dW, dhidden,
-                     dh_dtype, dW, tr, stream));
+    if (dhidden) TRY(contract_dh(p, L, Nc, dz, wt, r0, rows, dhidden, dh_dtype, tr, stream));
+    if (dW)
+      TRY(contract_dW(p, L, Nc, dz, dzt, ht, Nc, r0, rows, chunk > 0 || accumulate_dW, dW, tr,
+                      stream));
   }
   if (reduced) TRY(launch_reduce_for(p, k, loss, terms, counts, reduced, tr, stream));
   if (lse_q)

@@ -19,13 +19,15 @@ class LossRun:
                  labels: Optional[torch.Tensor] = None, mask: Optional[torch.Tensor] = None,
                  target_hidden: Optional[torch.Tensor] = None, W_t: Optional[torch.Tensor] = None,
                  target_row: Optional[torch.Tensor] = None, max_chunk_rows: int = 0,
-                 workspace_bytes: Optional[int] = None, want_terms: bool = True):
+                 workspace_bytes: Optional[int] = None, want_terms: bool = True,
+                 flags: int = 0):
         dev = hidden.device
         self.inputs = dict(hidden=hidden, W=W, labels=labels, mask=mask,
                            target_hidden=target_hidden, W_t=W_t, target_row=target_row)
         self.weights = dict(weights)
         self.problem = B.make_problem(hidden, W, weights, labels=labels, mask=mask,
-                                      target_hidden=target_hidden, W_t=W_t, target_row=target_row)
+                                      target_hidden=target_hidden, W_t=W_t, target_row=target_row,
+                                      flags=flags)
         N = hidden.shape[0]
         self.n_rows = N
         ws = workspace_bytes if workspace_bytes is not None else \
@@ -120,7 +122,7 @@ class ShardedLossRun(LossRun):
                  mask: Optional[torch.Tensor] = None,
                  target_hidden: Optional[torch.Tensor] = None, W_t: Optional[torch.Tensor] = None,
                  target_row: Optional[torch.Tensor] = None, max_chunk_rows: int = 0,
-                 want_terms: bool = True, bounds: Optional[list] = None):
+                 want_terms: bool = True, bounds: Optional[list] = None, flags: int = 0):
         dev = hidden.device
         V = W.shape[0]
         if bounds is None:
@@ -145,7 +147,8 @@ class ShardedLossRun(LossRun):
             v0, v1 = self.bounds[g], self.bounds[g + 1]
             prob = B.make_problem(hidden, W[v0:v1], weights, labels=labels, mask=mask,
                                   target_hidden=target_hidden,
-                                  W_t=None if W_t is None else W_t[v0:v1], target_row=target_row)
+                                  W_t=None if W_t is None else W_t[v0:v1], target_row=target_row,
+                                  flags=flags)
             sh = B.Shard(vocab_offset=v0, vocab_total=V, shard=g, n_shards=n_shards,
                          exchange=self.exchange.data_ptr())
             self.problems.append(prob)

@@ -44,6 +44,12 @@ def to_device(prob, dev="cuda"):
 
 
 def make_run(prob, dev_inputs, **kw) -> LossRun:
+    """LossRun of a synthetic problem; the transposed copies are forced unless
+    flags or a workspace size are given (chunked cases then test that path)."""
+    if "flags" not in kw and "workspace_bytes" not in kw:
+        kw["flags"] = L.binding.FLAG_COPIES
+    elif kw.get("flags") is None:
+        kw["flags"] = 0
     return LossRun(dev_inputs["hidden"], dev_inputs["W"], prob.weights,
                    labels=dev_inputs["labels"], mask=dev_inputs["mask"],
                    target_hidden=dev_inputs["target_hidden"], W_t=dev_inputs["W_t"],
@@ -81,7 +87,7 @@ def check_argmax(gpu_y: np.ndarray, prob, rows, valid) -> None:
 
 
 def full_parity(prob, *, max_chunk_rows=0, check_grads=True, tag="", single_call=False,
-                shards=None, workspace_bytes=None, expect_copies=None):
+                shards=None, workspace_bytes=None, expect_copies=None, flags=None):
     """Run fwd (+bwd with the mean seed) on the GPU and compare every output with the oracle.
 
     single_call: use lmhead_loss_fwd_bwd instead of the two calls.
@@ -89,7 +95,12 @@ def full_parity(prob, *, max_chunk_rows=0, check_grads=True, tag="", single_call
     workspace_bytes: workspace to give the calls (default: the library's size).
     expect_copies: if not None, whether the backward must make transposed
     copies (read from the kernel trace).
+    flags: backward layout flags; by default the transposed copies are forced
+    (FLAG_COPIES) so chunked cases exercise that path, except when
+    workspace_bytes is given (then the library chooses).
     """
+    if flags is None:
+        flags = 0 if workspace_bytes is not None else L.binding.FLAG_COPIES
     say(f"[parity] {tag} {prob.name} N={prob.n_rows} H={prob.hidden_dim} V={prob.vocab} "
         f"dtype={prob.dtype} weights={prob.weights} chunk={max_chunk_rows} single={single_call} "
         f"shards={shards}")
@@ -99,9 +110,10 @@ def full_parity(prob, *, max_chunk_rows=0, check_grads=True, tag="", single_call
                              labels=dev["labels"], mask=dev["mask"],
                              target_hidden=dev["target_hidden"], W_t=dev["W_t"],
                              target_row=dev["target_row"], max_chunk_rows=max_chunk_rows,
-                             bounds=shards[1])
+                             bounds=shards[1], flags=flags)
     else:
-        run = make_run(prob, dev, max_chunk_rows=max_chunk_rows, workspace_bytes=workspace_bytes)
+        run = make_run(prob, dev, max_chunk_rows=max_chunk_rows, workspace_bytes=workspace_bytes,
+                       flags=flags)
     trace = None
     if expect_copies is not None:
         trace = L.binding.Trace(capacity=4096)

@@ -483,7 +483,10 @@ def test_backward_without_transposed_copies(case):
     full_parity(p, max_chunk_rows=256, tag=f"lean-{case}", single_call=single,
                 workspace_bytes=full - copies, expect_copies=False)
     # and the default workspace (chunk = all rows here) makes the copies
-    full_parity(p, tag=f"copies-{case}", single_call=single, expect_copies=True)
+    full_parity(p, tag=f"copies-{case}", single_call=single, expect_copies=True, flags=0)
+    # forced either way at 256-row chunks
+    full_parity(p, max_chunk_rows=256, tag=f"nocopies-{case}", single_call=single,
+                expect_copies=False, flags=L.binding.FLAG_NO_COPIES)
 
 
 @pytest.mark.parametrize("single", [False, True])
@@ -517,3 +520,5 @@ def test_shared_target_rows_match_per_row(single):
     for k in ("loss", "lse_p", "y", "alpha", "flat"):
         assert torch.equal(a[k][valid], b[k][valid]), k
     assert torch.equal(a["dh"], b["dh"]) and torch.equal(a["dW"], b["dW"])
+
+

@@ -95,10 +95,14 @@ def test_validation(lib, mut, code):
     assert _fwd(lib, p) == code
 
 
-def test_reserved_field_and_null_problem(lib):
+def test_flags_field_and_null_problem(lib):
     p = _problem()
-    p.reserved = 1
-    assert _fwd(lib, p) == E_INVAL
+    for bad in (3, 4, -1):
+        p.flags = bad
+        assert _fwd(lib, p) == E_INVAL
+    p.flags = B.FLAG_NO_COPIES
+    p.in_dtype = B.F32
+    assert _fwd(lib, p) == E_UNSUP  # the copy-free backward is bf16 only
     out = ctypes.c_size_t()
     assert lib.lmhead_loss_workspace_size(None, 0, ctypes.byref(out)) == E_INVAL
     assert lib.lmhead_loss_fwd(None, 0, 0, 0, None, None, None, 0, None, None) == E_INVAL
