@@ -323,21 +323,52 @@ __global__ __launch_bounds__(256) void k_dz_stage(DzStageLaunch a) {
   constexpr int VT = kVocabTile, RB = 64;
   constexpr int KC = ElemTraits<T>::kPerChunk;       // elements per 16 bytes
   constexpr int CPR = VT / KC;                        // 16-byte chunks per row
-  constexpr int STRIDE = VT * (int)sizeof(T) + 16;    // LDS row stride (bytes), padded
+  // LDS: row rr holds its 16-byte chunk ch at position ch ^ (rr / KC), so the
+  // KC-row column reads of the transpose hit distinct banks
+  constexpr int STRIDE = VT * (int)sizeof(T);
   __shared__ __attribute__((aligned(16))) char tile[RB * STRIDE];
   const int vt = blockIdx.x % a.tiles_m;
   const int rb = blockIdx.x / a.tiles_m;
   T* dz = static_cast<T*>(a.dz);
   T* dzt = static_cast<T*>(a.dzt);
 
-  for (int idx = threadIdx.x; idx < RB * CPR; idx += 256) {
+  constexpr int IT = RB * CPR / 256;  // 16-byte chunks per thread
+  static_assert(RB * CPR % 256 == 0, "chunks must split evenly over the block");
+  i32x4_t raw[IT], rawd[DIV ? IT : 1];
+  // all of this thread's loads first, so they are in flight together
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int idx = it * 256 + threadIdx.x;
+    const int rr = idx / CPR, ch = idx % CPR;
+    const int64_t o = (int64_t)(rb * RB + rr) * a.ld_dz + vt * VT + ch * KC;
+    raw[it] = *reinterpret_cast<const i32x4_t*>(dz + o);
+    if constexpr (DIV) rawd[it] = *reinterpret_cast<const i32x4_t*>(static_cast<const T*>(a.dd) + o);
+  }
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int idx = it * 256 + threadIdx.x;
     const int rr = idx / CPR, ch = idx % CPR;
     const int c = rb * RB + rr;                    // chunk row
     const int v0 = vt * VT + ch * KC;
     T* p = dz + (int64_t)c * a.ld_dz + v0;
     float e[KC], dd[KC];
-    load_chunk<T, KC>(p, e);
-    if (DIV) load_chunk<T, KC>(static_cast<const T*>(a.dd) + (int64_t)c * a.ld_dz + v0, dd);
+    if constexpr (sizeof(T) == 2) {
+      const bf16x8_t b = __builtin_bit_cast(bf16x8_t, raw[it]);
+#pragma unroll
+      for (int q = 0; q < KC; ++q) e[q] = (float)b[q];
+      if constexpr (DIV) {
+        const bf16x8_t bd = __builtin_bit_cast(bf16x8_t, rawd[it]);
+#pragma unroll
+        for (int q = 0; q < KC; ++q) dd[q] = (float)bd[q];
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < KC; ++q) e[q] = __int_as_float(raw[it][q]);
+      if constexpr (DIV) {
+#pragma unroll
+        for (int q = 0; q < KC; ++q) dd[q] = __int_as_float(rawd[DIV ? it : 0][q]);
+      }
+    }
     float sd = 0.0f, scale = 0.0f, cb = 0.0f, cc = 0.0f, S = 0.0f;
     int yl = -1, ya = -1;
     if (c < a.ncols) {
@@ -384,7 +415,7 @@ __global__ __launch_bounds__(256) void k_dz_stage(DzStageLaunch a) {
       for (int q = 0; q < KC; ++q) out[q] = __float_as_int(d[q]);
     }
     *reinterpret_cast<i32x4_t*>(p) = out;
-    if (dzt) *reinterpret_cast<i32x4_t*>(tile + rr * STRIDE + ch * 16) = out;
+    if (dzt) *reinterpret_cast<i32x4_t*>(tile + rr * STRIDE + ((ch ^ (rr / KC)) << 4)) = out;
   }
   if (!dzt) return;  // bf16: the dW contraction reads dz itself
   __syncthreads();
@@ -393,16 +424,17 @@ __global__ __launch_bounds__(256) void k_dz_stage(DzStageLaunch a) {
   for (int idx = threadIdx.x; idx < VT * PER_ROW; idx += 256) {
     const int v = idx / PER_ROW, q = idx % PER_ROW;
     i32x4_t out;
+    const char* col = tile + (((v / KC) ^ q) << 4) + (v % KC) * (int)sizeof(T);
     if constexpr (sizeof(T) == 2) {
       bf16x8_t b;
 #pragma unroll
       for (int e = 0; e < KC; ++e)
-        b[e] = *reinterpret_cast<const __bf16*>(tile + (q * KC + e) * STRIDE + v * 2);
+        b[e] = *reinterpret_cast<const __bf16*>(col + (q * KC + e) * STRIDE);
       out = __builtin_bit_cast(i32x4_t, b);
     } else {
 #pragma unroll
       for (int e = 0; e < KC; ++e)
-        out[e] = *reinterpret_cast<const int*>(tile + (q * KC + e) * STRIDE + v * 4);
+        out[e] = *reinterpret_cast<const int*>(col + (q * KC + e) * STRIDE);
     }
     *reinterpret_cast<i32x4_t*>(dzt + (int64_t)(vt * VT + v) * a.ld_dzt + rb * RB + q * KC) = out;
   }
@@ -993,22 +1025,56 @@ __global__ __launch_bounds__(256) void k_seed(SeedLaunch a) {
   a.seed[r] = s;
 }
 
-// 64 x 64 tile transpose through LDS; pads columns [rows, ld_out) with zeros
+// 64 x 64 tile transpose through LDS with 16-byte global loads and stores.
+// Source rows past `rows` read as zeros, which pads output columns
+// [rows, ld_out) with zeros.  cols and ld_out are multiples of 64 (the host
+// requires a hidden size that is a multiple of 64; ld_out is the padded
+// vocabulary or chunk size).  In LDS, source row y keeps its 16-byte chunk
+// ch at position ch ^ (y / KC): the column gathers of the second half read
+// KC rows y = KC q + e at one chunk, and the XOR with q spreads them over
+// distinct banks.
 template <typename T>
 __global__ __launch_bounds__(256) void k_transpose(const T* in, int64_t rows, int64_t cols, T* out,
                                                    int64_t ld_out) {
-  __shared__ T tile[64][65];
-  const int64_t c0 = (int64_t)blockIdx.x * 64;  // source row block (becomes out column)
-  const int64_t j0 = (int64_t)blockIdx.y * 64;  // source column block (becomes out row)
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-  for (int y = ty; y < 64; y += 4) {
-    const int64_t r = c0 + y, j = j0 + tx;
-    tile[y][tx] = (r < rows && j < cols) ? in[r * cols + j] : T(0);
+  constexpr int KC = 16 / (int)sizeof(T);  // elements per 16-byte chunk
+  constexpr int CPR = 64 / KC;             // chunks per 64-element row
+  constexpr int IT = 64 * CPR / 256;       // chunks per thread
+  constexpr int ROWB = 64 * (int)sizeof(T);
+  __shared__ __attribute__((aligned(16))) char tile[64 * ROWB];
+  const int64_t c0 = (int64_t)blockIdx.x * 64;  // source row block (becomes out columns)
+  const int64_t j0 = (int64_t)blockIdx.y * 64;  // source column block (becomes out rows)
+  i32x4_t v[IT];
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int idx = it * 256 + threadIdx.x;
+    const int y = idx / CPR, ch = idx % CPR;
+    const int64_t r = c0 + y;
+    v[it] = r < rows ? *reinterpret_cast<const i32x4_t*>(in + r * cols + j0 + ch * KC)
+                     : i32x4_t{0, 0, 0, 0};
+  }
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int idx = it * 256 + threadIdx.x;
+    const int y = idx / CPR, ch = idx % CPR;
+    *reinterpret_cast<i32x4_t*>(tile + y * ROWB + ((ch ^ (y / KC)) << 4)) = v[it];
   }
   __syncthreads();
-  for (int y = ty; y < 64; y += 4) {
-    const int64_t j = j0 + y, c = c0 + tx;
-    if (j < cols && c < ld_out) out[j * ld_out + c] = tile[tx][y];
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int idx = it * 256 + threadIdx.x;
+    const int x = idx / CPR, q = idx % CPR;  // out row j0 + x, chunk q = source rows KC q ..
+    const char* col = tile + (((x / KC) ^ q) << 4) + (x % KC) * (int)sizeof(T);
+    i32x4_t o;
+    if constexpr (sizeof(T) == 2) {
+      bf16x8_t b;
+#pragma unroll
+      for (int e = 0; e < KC; ++e) b[e] = *reinterpret_cast<const __bf16*>(col + (q * KC + e) * ROWB);
+      o = __builtin_bit_cast(i32x4_t, b);
+    } else {
+#pragma unroll
+      for (int e = 0; e < KC; ++e) o[e] = *reinterpret_cast<const int*>(col + (q * KC + e) * ROWB);
+    }
+    *reinterpret_cast<i32x4_t*>(out + (j0 + x) * ld_out + c0 + q * KC) = o;
   }
 }
 
@@ -1170,7 +1236,9 @@ hipError_t launch_seed(const SeedLaunch& a, hipStream_t s) {
 
 hipError_t launch_transpose(bool bf16, const void* in, int64_t rows, int64_t cols, void* out,
                             int64_t ld_out, hipStream_t s) {
-  const dim3 grid((unsigned)((ld_out + 63) / 64), (unsigned)((cols + 63) / 64)), block(256);
+  // whole 64 x 64 tiles on the column side and 16-byte aligned rows
+  if (cols % 64 != 0 || ld_out % 64 != 0 || rows > ld_out) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)(ld_out / 64), (unsigned)(cols / 64)), block(256);
   if (bf16)
     hipLaunchKernelGGL(k_transpose<bf16_bits>, grid, block, 0, s,
                        static_cast<const bf16_bits*>(in), rows, cols, static_cast<bf16_bits*>(out),
