@@ -42,6 +42,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also copy a buffer of known size (for counter calibration)")
+    ap.add_argument("--blas-reference", action="store_true",
+                    help="also time hipBLASLt (torch.matmul) on the step's three contraction "
+                         "shapes with the same operands (label cross-entropy workloads)")
     ap.add_argument("--traffic", default=None,
                     help="counter summary giving HBM bytes per launch "
                          "(default profiles/traffic_<workload>.json)")
@@ -257,9 +260,57 @@ def main():
         "wall_s_timed": round(wall, 3),
         "input_gen_s": round(gen_s, 1),
     }
+    if args.blas_reference and G == 1 and inputs["labels"] is not None:
+        result["blas_reference"] = blas_reference(h, W, inputs["labels"], min(args.chunk, N), N,
+                                                  kernels)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(prob, args.cpu_sample_rows)
     print(json.dumps(result), flush=True)
+
+
+def blas_reference(h, W, labels, nc, N, kernels):
+    """The vendor GEMM on the step's contraction shapes, same process and operands.
+
+    One chunk of hidden rows against W (the forward logits), and that chunk's
+    label cross-entropy logit gradient (softmax minus one-hot, over N tokens)
+    against W (dh shape) and, transposed, against the hidden rows (dW shape).
+    torch.matmul runs hipBLASLt with bf16 inputs, fp32 accumulation and bf16
+    output, i.e. without the fused epilogues of the library's kernels.
+    """
+    import torch
+    c = h[:nc]
+    z = torch.matmul(c, W.t())
+    p = torch.softmax(z.float(), dim=1)
+    del z
+    p[torch.arange(nc, device=h.device), labels[:nc].long()] -= 1.0
+    dz = (p / N).to(torch.bfloat16)
+    del p
+    dzt = dz.t().contiguous()
+    flops = 2.0 * nc * h.shape[1] * W.shape[0]
+
+    def rate(fn):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(5):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b))
+        return round(flops / (sorted(ts)[2] * 1e-3) / 1e12, 1)
+
+    ours = {k: round(kernels[k]["work_per_launch"] / (kernels[k]["ms_avg"] * 1e-3) / 1e12, 1)
+            for k in ("stats_stage", "gemm_dh", "gemm_dW") if k in kernels}
+    return {"library": "hipBLASLt via torch.matmul (bf16 in, fp32 accumulate, bf16 out)",
+            "shapes": {"pass1": [nc, W.shape[0], h.shape[1]], "dh": [nc, h.shape[1], W.shape[0]],
+                       "dW": [W.shape[0], h.shape[1], nc]},
+            "tflops": {"pass1": rate(lambda: torch.matmul(c, W.t())),
+                       "dh": rate(lambda: torch.matmul(dz, W)),
+                       "dW": rate(lambda: torch.matmul(dzt, c))},
+            "ours_tflops": ours}
 
 
 FLOP_KERNELS = ("stats_q", "stats_p", "stats_stage", "div", "div_stage", "dz", "gemm_dh",

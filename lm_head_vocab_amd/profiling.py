@@ -9,7 +9,12 @@ kilobytes into bytes.  The summary records a digest of the kernel sources;
 bench.py reports the traffic only while the digest still matches.
 
     python -m lm_head_vocab_amd.profiling --fetch <fetch csv> --write <write csv> \
-        --copy-bytes <n> --out profiles/<name>.json
+        --copy-bytes <n> --out profiles/<name>.json \
+        [--stats <rocprofv3 kernel_stats.csv> --md profiles/<name>.md]
+
+With --stats and --md it also writes a markdown summary: the per-kernel
+durations of a `rocprofv3 --kernel-trace --stats` run of the same benchmark
+and the calibrated bytes per launch.
 """
 from __future__ import annotations
 
@@ -86,16 +91,63 @@ def summarize(fetch_csv: str, write_csv: str, copy_bytes: int):
             "factor_write": f_write, "source_digest": source_digest(), "kernels": out}
 
 
+TRACE_CMD = ("rocprofv3 --kernel-trace --stats --output-format csv -d <out> -o run -- "
+             "python3 <repo>/bench.py --steps 3 --warmup 1 --no-cpu-baseline")
+PMC_CMD = ("rocprofv3 --pmc {c} --output-format csv -d <{d}> -o pmc -- python3 <repo>/bench.py "
+           "--steps 1 --warmup 0 --no-cpu-baseline --calibrate-copy")
+
+
+def markdown(stats_csv: str, traffic: dict, workload: str) -> str:
+    """Markdown summary of a kernel-trace stats run and the counter passes."""
+    rows = list(csv.DictReader(open(stats_csv)))
+    out = [f"# Kernel durations and HBM traffic: `{workload}` fwd+bwd", "",
+           "One bench.py process runs the single call `lmhead_loss_fwd_bwd` (the headline) and the",
+           "two calls `lmhead_loss_fwd` + `lmhead_loss_bwd` (beside it), so both sets of kernels",
+           "appear.  Written by `python -m lm_head_vocab_amd.profiling` from the runs below.", "",
+           "## Durations", "", "Command (from /tmp with TMPDIR=/tmp):", "", "```", TRACE_CMD, "```",
+           "", "| kernel | calls | avg ms | total ms | % |", "|---|---:|---:|---:|---:|"]
+    for r in rows:
+        name = r["Name"].replace("specloss::", "").replace("|", "\\|")
+        if len(name) > 72:
+            name = name[:69] + "..."
+        out.append(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e6:.4f} | "
+                   f"{float(r['TotalDurationNs']) / 1e6:.3f} | {float(r['Percentage']):.2f} |")
+    out += ["", "`k_gemm<T, OutT, 1, ...>` is the dW contraction, `k_gemm<T, OutT, 0, ...>` the dh "
+            "contraction (the last template argument selects the copy-free variant).", "",
+            "## HBM bytes per launch", "", "Commands (two passes, each its own run):", "", "```",
+            PMC_CMD.format(c="FETCH_SIZE", d="fetch"), PMC_CMD.format(c="WRITE_SIZE", d="write"),
+            "python -m lm_head_vocab_amd.profiling --fetch <fetch>/pmc_counter_collection.csv "
+            "--write <write>/pmc_counter_collection.csv --copy-bytes "
+            f"{traffic['copy_bytes']} --out profiles/traffic_{workload}.json --stats "
+            "<out>/run_kernel_stats.csv --md <this file>", "```", "",
+            f"`--calibrate-copy` copies {traffic['copy_bytes'] / 2**30:g} GiB inside the same "
+            f"process; the counters of that copy (`{traffic['copy_kernel']}`) give the scale "
+            f"factors FETCH_SIZE x {traffic['factor_fetch']:.3f}, WRITE_SIZE x "
+            f"{(traffic['factor_write'] or 0):.3f}.  Source digest of the profiled kernels: "
+            f"`{traffic['source_digest']}` ({', '.join(os.path.basename(x) for x in SOURCES)}).",
+            "", "| kernel | fetched GB | written GB | total GB per launch |", "|---|---:|---:|---:|"]
+    for k, v in sorted(traffic["kernels"].items(), key=lambda kv: -kv[1]["bytes_per_launch"]):
+        out.append(f"| {k} | {v['fetch_bytes'] / 1e9:.3f} | {(v['write_bytes'] or 0) / 1e9:.3f} | "
+                   f"{v['bytes_per_launch'] / 1e9:.3f} |")
+    return "\n".join(out) + "\n"
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--fetch", required=True)
     ap.add_argument("--write", required=True)
     ap.add_argument("--copy-bytes", type=int, required=True)
     ap.add_argument("--out", required=True)
+    ap.add_argument("--stats", default=None, help="rocprofv3 kernel_stats.csv of the same benchmark")
+    ap.add_argument("--md", default=None, help="markdown summary to write (needs --stats)")
+    ap.add_argument("--workload", default="ce_bf16_8b")
     a = ap.parse_args()
     s = summarize(a.fetch, a.write, a.copy_bytes)
     with open(a.out, "w") as f:
         json.dump(s, f, indent=1)
+    if a.md and a.stats:
+        with open(a.md, "w") as f:
+            f.write(markdown(a.stats, s, a.workload))
     print(json.dumps({k: round(v["bytes_per_launch"] / 1e9, 3) for k, v in s["kernels"].items()}))
 
 
