@@ -88,6 +88,34 @@ __device__ __forceinline__ void store4<float>(float* dst, float a0, float a1, fl
   f32x4_t v = {a0, a1, a2, a3};
   *reinterpret_cast<f32x4_t*>(dst) = v;
 }
+// Two accumulator fragments that share their 16 rows and sit in adjacent
+// 16-column blocks, stored through a layout whose rows are contiguous and
+// whose columns are `ld` apart; p0 addresses (row 0, column 0) of the first.
+// Each lane holds rows 4 g .. 4 g + 3 (g = lane / 16) of column lane % 16 of
+// both (`a`, `b`).  For bf16, v_permlane16_swap exchanges the odd 16-lane rows
+// of the first with the even rows of the second, after which lanes of row g
+// hold the eight rows 8 (g / 2) .. + 7 of column block g % 2: one 16-byte
+// store per lane instead of two 8-byte ones.
+template <typename T>
+__device__ __forceinline__ void store_frag_pair(T* p0, int64_t ld, const float (&a)[4],
+                                                const float (&b)[4], int lane) {
+  if constexpr (sizeof(T) == 2) {
+    const bf16x4_t va = {(__bf16)a[0], (__bf16)a[1], (__bf16)a[2], (__bf16)a[3]};
+    const bf16x4_t vb = {(__bf16)b[0], (__bf16)b[1], (__bf16)b[2], (__bf16)b[3]};
+    const i32x2_t ia = __builtin_bit_cast(i32x2_t, va), ib = __builtin_bit_cast(i32x2_t, vb);
+    const auto s0 = __builtin_amdgcn_permlane16_swap(ia[0], ib[0], false, false);
+    const auto s1 = __builtin_amdgcn_permlane16_swap(ia[1], ib[1], false, false);
+    const int g = lane >> 4;
+    const i32x4_t out = {(int)s0[0], (int)s1[0], (int)s0[1], (int)s1[1]};
+    *reinterpret_cast<i32x4_t*>(p0 + (int64_t)(16 * (g & 1) + (lane & 15)) * ld + 8 * (g >> 1)) =
+        out;
+  } else {
+    const int r0 = 4 * (lane >> 4), c = lane & 15;
+    store4<T>(p0 + (int64_t)c * ld + r0, a[0], a[1], a[2], a[3]);
+    store4<T>(p0 + (int64_t)(16 + c) * ld + r0, b[0], b[1], b[2], b[3]);
+  }
+}
+
 template <typename T>
 __device__ __forceinline__ void store1(T* dst, float x);
 template <>
@@ -268,24 +296,29 @@ __global__ __launch_bounds__(kThreads, 1) void k_stats_stage(StatsStageLaunch a)
 
   T* E = static_cast<T*>(a.stage);
   float sj[Cfg::FN];
+  static_assert(Cfg::FN % 2 == 0, "column blocks are stored in pairs");
 #pragma unroll
-  for (int j = 0; j < Cfg::FN; ++j) {
-    const int col = tn * Cfg::BN + wn * Cfg::WN + j * kFrag + frag_col(lane);  // chunk row
-    const float mb = mj[j] * kLog2e;
-    float s = 0.0f;
+  for (int j = 0; j < Cfg::FN; j += 2) {
+    // E row = chunk row (this tile's column), contiguous along the vocabulary
+    T* e0 = E + (int64_t)(tn * Cfg::BN + wn * Cfg::WN + j * kFrag) * a.ld_stage + v_base;
+    const float mb0 = mj[j] * kLog2e, mb1 = mj[j + 1] * kLog2e;
+    float s0 = 0.0f, s1 = 0.0f;
 #pragma unroll
     for (int i = 0; i < Cfg::FM; ++i) {
-      float e[4];
+      float e[4], f[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int v = v_base + i * kFrag + frag_row(r, lane);
-        e[r] = (!tail || v < st.vocab) ? fast_exp2(fmaf(acc[i][j][r], kLog2e, -mb)) : 0.0f;
-        s += e[r];
+        const bool in = !tail || v < st.vocab;
+        e[r] = in ? fast_exp2(fmaf(acc[i][j][r], kLog2e, -mb0)) : 0.0f;
+        f[r] = in ? fast_exp2(fmaf(acc[i][j + 1][r], kLog2e, -mb1)) : 0.0f;
+        s0 += e[r];
+        s1 += f[r];
       }
-      const int v0 = v_base + i * kFrag + frag_row(0, lane);
-      store4<T>(E + (int64_t)col * a.ld_stage + v0, e[0], e[1], e[2], e[3]);
+      store_frag_pair<T>(e0 + i * kFrag, a.ld_stage, e, f, lane);
     }
-    sj[j] = col_sum(s, lane);
+    sj[j] = col_sum(s0, lane);
+    sj[j + 1] = col_sum(s1, lane);
   }
   __syncthreads();
   if (lane < kFrag) {
