@@ -603,10 +603,59 @@ __device__ __forceinline__ float dz_elem(const RowCoef& c, const float* w, float
   return g;
 }
 
+// A tile's values (in the accumulator layout) stored to a row-major output
+// whose rows are the tile's M index, as 16-byte pieces: the tile goes out in
+// two halves of 128 rows, each staged through LDS as fp32 (rows padded to
+// BN * 4 + 16 bytes so the row groups of a fragment store land in different
+// banks), then streamed row by row.  Rounding to T happens at the store.
+template <typename T, typename Cfg>
+__device__ __forceinline__ void store_tile_rows(const f32x4_t (&acc)[Cfg::FM][Cfg::FN], T* out,
+                                                int64_t ld, int64_t row0, int64_t col0,
+                                                char* smem) {
+  constexpr int kHalf = Cfg::BM / 2;
+  constexpr int kStride = Cfg::BN * 4 + 16;
+  constexpr int kPieces = Cfg::BN / 8;  // 8-value pieces per row
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+#pragma unroll 1
+  for (int h = 0; h < 2; ++h) {
+    if (wm == h) {
+#pragma unroll
+      for (int i = 0; i < Cfg::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < Cfg::FN; ++j)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int row = i * kFrag + frag_row(r, lane);
+            const int col = wn * Cfg::WN + j * kFrag + frag_col(lane);
+            *reinterpret_cast<float*>(smem + row * kStride + col * 4) = acc[i][j][r];
+          }
+    }
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < kHalf * kPieces; idx += kThreads) {
+      const int row = idx / kPieces, pc = idx % kPieces;
+      const f32x4_t x0 = *reinterpret_cast<const f32x4_t*>(smem + row * kStride + pc * 32);
+      const f32x4_t x1 = *reinterpret_cast<const f32x4_t*>(smem + row * kStride + pc * 32 + 16);
+      T* p = out + (row0 + h * kHalf + row) * ld + col0 + pc * 8;
+      if constexpr (sizeof(T) == 2) {
+        const bf16x8_t b = {(__bf16)x0[0], (__bf16)x0[1], (__bf16)x0[2], (__bf16)x0[3],
+                            (__bf16)x1[0], (__bf16)x1[1], (__bf16)x1[2], (__bf16)x1[3]};
+        *reinterpret_cast<bf16x8_t*>(p) = b;
+      } else {
+        *reinterpret_cast<f32x4_t*>(p) = x0;
+        *reinterpret_cast<f32x4_t*>(p + 4) = x1;
+      }
+    }
+    __syncthreads();
+  }
+}
+
 template <typename T, bool DUAL>
 __global__ __launch_bounds__(kThreads, 1) void k_dz(DzLaunch a) {
   using Cfg = TileCfg<T, 256, (DUAL ? 128 : 256)>;
-  __shared__ __attribute__((aligned(16))) char smem[Cfg::LDS_BYTES];
+  constexpr int kRowsSmem = (Cfg::BM / 2) * (Cfg::BN * 4 + 16);  // store_tile_rows staging
+  constexpr int kSmem = Cfg::LDS_BYTES > kRowsSmem ? Cfg::LDS_BYTES : kRowsSmem;
+  __shared__ __attribute__((aligned(16))) char smem[kSmem];
   int tm, tn;
   if (!tile_of(a.tiles_m, a.tiles_n, kGroupM, tm, tn)) return;
 
@@ -627,44 +676,56 @@ __global__ __launch_bounds__(kThreads, 1) void k_dz(DzLaunch a) {
   T* dz = static_cast<T*>(a.dz);
   T* dzt = static_cast<T*>(a.dzt);
 
+  // dz rows (chunk row, contiguous along the vocabulary): column blocks j,
+  // j + 1 go out together as 16-byte pieces; the values replace the
+  // accumulators for the dz^T epilogue
+  static_assert(Cfg::FN % 2 == 0, "column blocks are stored in pairs");
 #pragma unroll
-  for (int j = 0; j < Cfg::FN; ++j) {
-    const int c = tn * Cfg::BN + wn * Cfg::WN + j * kFrag + frag_col(lane);  // chunk row
-    const int64_t gr = a.r0 + min(c, a.ncols - 1);
-    RowCoef rc;
-    rc.seed = (c < a.ncols) ? a.seed[gr] : 0.0f;
-    rc.lse_q = a.sv.lse_q[gr];
-    rc.y_lab = a.sv.y_label[gr] >= 0 ? a.sv.y_label[gr] - a.vocab_offset : -1;
-    rc.y_arg = a.sv.y_arg[gr] >= 0 ? a.sv.y_arg[gr] - a.vocab_offset : -1;
-    if (DUAL) {
-      rc.lse_p = a.sv.lse_p[gr];
-      rc.alpha = a.sv.alpha[gr];
-      rc.S = a.sv.S[gr];
-      rc.rkl = a.sv.rkl[gr];
-      rc.eqg = a.sv.eqg[gr];
-      rc.lam = __expf(-3.0f * rc.alpha);
+  for (int j = 0; j < Cfg::FN; j += 2) {
+    RowCoef rc[2];
+    bool live[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int c = tn * Cfg::BN + wn * Cfg::WN + (j + h) * kFrag + frag_col(lane);  // chunk row
+      const int64_t gr = a.r0 + min(c, a.ncols - 1);
+      rc[h].seed = (c < a.ncols) ? a.seed[gr] : 0.0f;
+      rc[h].lse_q = a.sv.lse_q[gr];
+      rc[h].y_lab = a.sv.y_label[gr] >= 0 ? a.sv.y_label[gr] - a.vocab_offset : -1;
+      rc[h].y_arg = a.sv.y_arg[gr] >= 0 ? a.sv.y_arg[gr] - a.vocab_offset : -1;
+      if (DUAL) {
+        rc[h].lse_p = a.sv.lse_p[gr];
+        rc[h].alpha = a.sv.alpha[gr];
+        rc[h].S = a.sv.S[gr];
+        rc[h].rkl = a.sv.rkl[gr];
+        rc[h].eqg = a.sv.eqg[gr];
+        rc[h].lam = __expf(-3.0f * rc[h].alpha);
+      }
+      live[h] = rc[h].seed != 0.0f;
     }
-    const bool live = rc.seed != 0.0f;
 #pragma unroll
     for (int i = 0; i < Cfg::FM; ++i) {
-      float o[4];
+      float o[2][4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int v = v_base + i * kFrag + frag_row(r, lane);
-        float d = 0.0f;
-        if (live && v < a.vocab) {
-          const float u = DUAL ? au[DUAL ? i : 0][DUAL ? j : 0][r] : 0.0f;
-          d = rc.seed * dz_elem<DUAL>(rc, a.w, az[i][j][r], u, v);
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int v = v_base + i * kFrag + frag_row(r, lane);
+          float d = 0.0f;
+          if (live[h] && v < a.vocab) {
+            const float u = DUAL ? au[DUAL ? i : 0][DUAL ? j + h : 0][r] : 0.0f;
+            d = rc[h].seed * dz_elem<DUAL>(rc[h], a.w, az[i][j + h][r], u, v);
+          }
+          o[h][r] = d;
+          az[i][j + h][r] = d;
         }
-        o[r] = d;
-      }
-      const int v0 = v_base + i * kFrag + frag_row(0, lane);
-      store4<T>(dz + (int64_t)c * a.ld_dz + v0, o[0], o[1], o[2], o[3]);
-      if (dzt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) store1<T>(dzt + (int64_t)(v0 + r) * a.ld_dzt + c, o[r]);
+      store_frag_pair<T>(dz + (int64_t)(tn * Cfg::BN + wn * Cfg::WN + j * kFrag) * a.ld_dz + v_base +
+                             i * kFrag,
+                         a.ld_dz, o[0], o[1], lane);
     }
   }
+  // dz^T rows (vocabulary entry, contiguous along the chunk rows)
+  if (dzt)
+    store_tile_rows<T, Cfg>(az, dzt, a.ld_dzt, (int64_t)tm * Cfg::BM, (int64_t)tn * Cfg::BN, smem);
 }
 
 // ============================================================================
