@@ -92,9 +92,9 @@ def summarize(fetch_csv: str, write_csv: str, copy_bytes: int):
 
 
 TRACE_CMD = ("rocprofv3 --kernel-trace --stats --output-format csv -d <out> -o run -- "
-             "python3 <repo>/bench.py --steps 3 --warmup 1 --no-cpu-baseline")
+             "python3 <repo>/bench.py --workload {w} --steps 3 --warmup 1 --no-cpu-baseline")
 PMC_CMD = ("rocprofv3 --pmc {c} --output-format csv -d <{d}> -o pmc -- python3 <repo>/bench.py "
-           "--steps 1 --warmup 0 --no-cpu-baseline --calibrate-copy")
+           "--workload {w} --steps 1 --warmup 0 --no-cpu-baseline --calibrate-copy")
 
 
 def markdown(stats_csv: str, traffic: dict, workload: str) -> str:
@@ -104,7 +104,7 @@ def markdown(stats_csv: str, traffic: dict, workload: str) -> str:
            "One bench.py process runs the single call `lmhead_loss_fwd_bwd` (the headline) and the",
            "two calls `lmhead_loss_fwd` + `lmhead_loss_bwd` (beside it), so both sets of kernels",
            "appear.  Written by `python -m lm_head_vocab_amd.profiling` from the runs below.", "",
-           "## Durations", "", "Command (from /tmp with TMPDIR=/tmp):", "", "```", TRACE_CMD, "```",
+           "## Durations", "", "Command (from /tmp with TMPDIR=/tmp):", "", "```", TRACE_CMD.format(w=workload), "```",
            "", "| kernel | calls | avg ms | total ms | % |", "|---|---:|---:|---:|---:|"]
     for r in rows:
         name = r["Name"].replace("specloss::", "").replace("|", "\\|")
@@ -115,11 +115,12 @@ def markdown(stats_csv: str, traffic: dict, workload: str) -> str:
     out += ["", "`k_gemm<T, OutT, 1, ...>` is the dW contraction, `k_gemm<T, OutT, 0, ...>` the dh "
             "contraction (the last template argument selects the copy-free variant).", "",
             "## HBM bytes per launch", "", "Commands (two passes, each its own run):", "", "```",
-            PMC_CMD.format(c="FETCH_SIZE", d="fetch"), PMC_CMD.format(c="WRITE_SIZE", d="write"),
+            PMC_CMD.format(c="FETCH_SIZE", d="fetch", w=workload),
+            PMC_CMD.format(c="WRITE_SIZE", d="write", w=workload),
             "python -m lm_head_vocab_amd.profiling --fetch <fetch>/pmc_counter_collection.csv "
             "--write <write>/pmc_counter_collection.csv --copy-bytes "
             f"{traffic['copy_bytes']} --out profiles/traffic_{workload}.json --stats "
-            "<out>/run_kernel_stats.csv --md <this file>", "```", "",
+            "<out>/run_kernel_stats.csv --md <this file> --workload " + workload, "```", "",
             f"`--calibrate-copy` copies {traffic['copy_bytes'] / 2**30:g} GiB inside the same "
             f"process; the counters of that copy (`{traffic['copy_kernel']}`) give the scale "
             f"factors FETCH_SIZE x {traffic['factor_fetch']:.3f}, WRITE_SIZE x "
