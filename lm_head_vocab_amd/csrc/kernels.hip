@@ -11,6 +11,11 @@
 //   k_dz     backward recompute: forms the logit gradient of the weighted loss
 //            in registers and stages it (bf16 for bf16 inputs) for the two
 //            contractions (blog "Backward pass").
+//   k_stats_stage  pass 1 of the single forward+backward call: as k_stats,
+//            and stores e = exp(z - m_tile) of every (token, vocab) for the
+//            backward, so no logits tile is computed twice.
+// Memory-bound k_dz_stage: the logit gradient from the staged values, in
+// place, plus its transpose for the dW contraction.
 // Plain contraction k_gemm: dh = dz W and dW (+)= dz^T h.
 // Row kernels: validity/counts, label-logit gather, partial merges, means,
 // gradient seeds, transposes and head alignment.
