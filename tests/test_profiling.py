@@ -1,0 +1,49 @@
+"""Host logic of the counter summaries (no GPU): kernel-name mapping, the
+comment-insensitive source digest and the copy calibration."""
+import csv
+
+from lm_head_vocab_amd import profiling as P
+
+
+def test_trace_name_mapping():
+    assert P.trace_name("void specloss::k_gemm<unsigned short, float, 1, false>(specloss::GemmLaunch)") == "gemm_dW"
+    assert P.trace_name("void specloss::k_gemm<unsigned short, float, 0, false>(specloss::GemmLaunch)") == "gemm_dh"
+    assert P.trace_name("void specloss::k_stats<unsigned short, true>(specloss::StatsLaunch)") == "stats_p"
+    assert P.trace_name("void specloss::k_stats<unsigned short, false>(specloss::StatsLaunch)") == "stats_q"
+    assert P.trace_name("void specloss::k_div<unsigned short, true>(specloss::DivLaunch)") == "div_stage"
+    assert P.trace_name("void specloss::k_stats_stage<unsigned short>(specloss::StatsStageLaunch)") == "stats_stage"
+    assert P.trace_name("__amd_rocclr_copyBuffer") == "__amd_rocclr_copyBuffer"
+
+
+def test_code_only_ignores_comments_and_layout():
+    a = "int x = 1; // one\n/* block\n comment */ int y = 2;\n"
+    b = "int x = 1;\n\n   int y = 2;   // two\n"
+    assert P._code_only(a) == P._code_only(b) == "int x = 1; int y = 2;"
+    assert P._code_only("int x = 1;") != P._code_only("int x = 2;")
+
+
+def _write(path, rows):
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Kernel_Name", "Counter_Name", "Counter_Value"])
+        w.writeheader()
+        w.writerows(rows)
+
+
+def test_summarize_scales_by_the_copy(tmp_path):
+    copy, gemm = "__amd_rocclr_copyBuffer", "void specloss::k_gemm<unsigned short, float, 1, false>(x)"
+    # the copy of 1 MiB reads as 512 KiB fetched and 1024 KiB written
+    _write(tmp_path / "f.csv", [
+        {"Kernel_Name": copy, "Counter_Name": "FETCH_SIZE", "Counter_Value": 512.0},
+        {"Kernel_Name": gemm, "Counter_Name": "FETCH_SIZE", "Counter_Value": 100.0},
+        {"Kernel_Name": gemm, "Counter_Name": "FETCH_SIZE", "Counter_Value": 300.0}])
+    _write(tmp_path / "w.csv", [
+        {"Kernel_Name": copy, "Counter_Name": "WRITE_SIZE", "Counter_Value": 1024.0},
+        {"Kernel_Name": gemm, "Counter_Name": "WRITE_SIZE", "Counter_Value": 10.0}])
+    s = P.summarize(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"), 1 << 20)
+    assert s["factor_fetch"] == 2.0 and s["factor_write"] == 1.0
+    k = s["kernels"]["gemm_dW"]
+    assert k["dispatches"] == 2
+    assert k["fetch_bytes"] == 200.0 * 1024 * 2.0      # mean of the dispatches, scaled
+    assert k["write_bytes"] == 10.0 * 1024 * 1.0
+    assert s["source_digest"] == P.source_digest()
+
