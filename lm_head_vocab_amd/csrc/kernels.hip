@@ -745,7 +745,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_dz(DzLaunch a) {
 // own a half write their accumulators into LDS (rows padded to 1040 bytes so
 // the four row groups of a store land in different banks); then all threads
 // stream the half's rows: 16-byte loads of the old values (accumulate), add,
-// 16-byte stores, eight pieces in flight per thread.
+// 16-byte stores, eight pieces in flight per thread.  fp32 outputs are read
+// and written nontemporally: the next touch of a dW row is a whole chunk
+// later, and cached dW lines would only displace the operand slabs that the
+// other tiles of a round re-read (measured: gemm_dW 2.6 % faster).
 constexpr int kHalfRows = 128;
 constexpr int kEpiStride = 256 * 4 + 16;  // bytes per staged row
 
@@ -796,7 +799,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(GemmLaunch a) {
         if (a.accumulate && grow < a.m_valid && gcol < a.n_valid) {
           const OutT* p = C + (int64_t)grow * a.ldc + gcol;
           if constexpr (sizeof(OutT) == 4) {
-            old[q] = *reinterpret_cast<const f32x4_t*>(p);
+            old[q] = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(p));
           } else {
             const bf16x4_t v = *reinterpret_cast<const bf16x4_t*>(p);
             old[q] = f32x4_t{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
@@ -811,7 +814,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(GemmLaunch a) {
         if (grow >= a.m_valid || gcol >= a.n_valid) continue;
         const f32x4_t x = *reinterpret_cast<const f32x4_t*>(smem + row * kEpiStride + c4 * 4) + old[q];
         OutT* p = C + (int64_t)grow * a.ldc + gcol;
-        if constexpr (sizeof(OutT) == 4) store4<float>(reinterpret_cast<float*>(p), x[0], x[1], x[2], x[3]);
+        if constexpr (sizeof(OutT) == 4) __builtin_nontemporal_store(x, reinterpret_cast<f32x4_t*>(p));
         else store4<bf16_bits>(reinterpret_cast<bf16_bits*>(p), x[0], x[1], x[2], x[3]);
       }
     }
