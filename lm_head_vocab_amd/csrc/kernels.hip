@@ -1012,17 +1012,56 @@ __global__ __launch_bounds__(256) void k_target_gather(TargetGatherLaunch a) {
   a.flat[gr] = valid ? a.t_flat[t] : 0.0f;
 }
 
+// Sums over the vocabulary tiles of the pass-2 partials of kSegRows rows:
+// the tiles of a row are split into kSegs contiguous segments, one thread
+// each, and the segment sums are added in segment order (a fixed order, so
+// results are bitwise repeatable).  Threads (rr, seg) = (tid % kSegRows,
+// tid / kSegRows); on return, threads of segment 0 hold the row's sums.
+constexpr int kSegRows = 32, kSegs = 32;
+__device__ __forceinline__ void tile_sums(const float* part, int64_t part_stride, int64_t ldp,
+                                          int tiles_m, uint32_t need, int c, bool row_ok,
+                                          float (&sum)[kNumSums]) {
+  __shared__ float sp[kNumSums][kSegs][kSegRows];
+  const int rr = threadIdx.x % kSegRows, seg = threadIdx.x / kSegRows;
+  const int per = (tiles_m + kSegs - 1) / kSegs;
+  const int t0 = min(tiles_m, seg * per), t1 = min(tiles_m, t0 + per);
+#pragma unroll
+  for (int f = 0; f < kNumSums; ++f) {
+    float acc = 0.0f;
+    if (row_ok && (need & (1u << f))) {
+      const float* p = part + f * part_stride + c;
+      int t = t0;
+      for (; t + 4 <= t1; t += 4) {
+        const float x0 = p[(int64_t)t * ldp], x1 = p[(int64_t)(t + 1) * ldp];
+        const float x2 = p[(int64_t)(t + 2) * ldp], x3 = p[(int64_t)(t + 3) * ldp];
+        acc += x0;
+        acc += x1;
+        acc += x2;
+        acc += x3;
+      }
+      for (; t < t1; ++t) acc += p[(int64_t)t * ldp];
+    }
+    sp[f][seg][rr] = acc;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int f = 0; f < kNumSums; ++f) {
+    float acc = 0.0f;
+    if (seg == 0)
+      for (int g = 0; g < kSegs; ++g) acc += sp[f][g][rr];
+    sum[f] = acc;
+  }
+}
+
 // sums over the vocabulary tiles of one shard: out[f][c] = sum_t part[f][t][c]
 // (fixed order) for every requested sum f
-__global__ __launch_bounds__(256) void k_tile_sum(TileSumLaunch a) {
-  const int c = blockIdx.x * 256 + threadIdx.x;
-  if (c >= a.ncols) return;
-  for (int f = 0; f < kNumSums; ++f) {
-    if (!(a.need & (1u << f))) continue;
-    float acc = 0.0f;
-    for (int t = 0; t < a.tiles_m; ++t) acc += a.part[f * a.part_stride + (int64_t)t * a.ldp + c];
-    a.out[f * a.out_stride + c] = acc;
-  }
+__global__ __launch_bounds__(kSegRows * kSegs) void k_tile_sum(TileSumLaunch a) {
+  const int c = blockIdx.x * kSegRows + (int)(threadIdx.x % kSegRows);
+  float sum[kNumSums];
+  tile_sums(a.part, a.part_stride, a.ldp, a.tiles_m, a.need, c, c < a.ncols, sum);
+  if (threadIdx.x >= kSegRows || c >= a.ncols) return;
+  for (int f = 0; f < kNumSums; ++f)
+    if (a.need & (1u << f)) a.out[f * a.out_stride + c] = sum[f];
 }
 
 // out[i] = sum_g parts[g][i] in shard order (fp32 partials; fp32 or bf16 out)
@@ -1046,16 +1085,11 @@ __global__ __launch_bounds__(256) void k_sum_parts(const float* parts, int64_t n
   for (int e = 0; e < lim; ++e) store1<OutT>(out + i4 + e, acc[e]);
 }
 
-__global__ __launch_bounds__(256) void k_combine2(Combine2Launch a) {
-  const int c = blockIdx.x * 256 + threadIdx.x;
-  if (c >= a.ncols) return;
+__global__ __launch_bounds__(kSegRows * kSegs) void k_combine2(Combine2Launch a) {
+  const int c = blockIdx.x * kSegRows + (int)(threadIdx.x % kSegRows);
   float sum[kNumSums];
-#pragma unroll
-  for (int f = 0; f < kNumSums; ++f) {
-    sum[f] = 0.0f;
-    if (a.need & (1u << f))
-      for (int t = 0; t < a.tiles_m; ++t) sum[f] += a.part[f * a.part_stride + (int64_t)t * a.ldp + c];
-  }
+  tile_sums(a.part, a.part_stride, a.ldp, a.tiles_m, a.need, c, c < a.ncols, sum);
+  if (threadIdx.x >= kSegRows || c >= a.ncols) return;
   const float alpha = sum[0], S = sum[1], kl = sum[2], rkl = sum[3], jsd = sum[4], eqg = sum[5];
   const bool valid = a.flags[c] != 0;
   float L[kNumKinds];
@@ -1300,7 +1334,8 @@ hipError_t launch_combine1(const Combine1Launch& a, hipStream_t s) {
 }
 
 hipError_t launch_combine2(const Combine2Launch& a, hipStream_t s) {
-  hipLaunchKernelGGL(k_combine2, dim3((a.ncols + 255) / 256), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(k_combine2, dim3((a.ncols + kSegRows - 1) / kSegRows), dim3(kSegRows * kSegs),
+                     0, s, a);
   return hipGetLastError();
 }
 
@@ -1310,7 +1345,8 @@ hipError_t launch_target_gather(const TargetGatherLaunch& a, hipStream_t s) {
 }
 
 hipError_t launch_tile_sum(const TileSumLaunch& a, hipStream_t s) {
-  hipLaunchKernelGGL(k_tile_sum, dim3((a.ncols + 255) / 256), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(k_tile_sum, dim3((a.ncols + kSegRows - 1) / kSegRows), dim3(kSegRows * kSegs),
+                     0, s, a);
   return hipGetLastError();
 }
 
