@@ -912,6 +912,10 @@ __global__ __launch_bounds__(256) void k_rowdot(RowdotLaunch a) {
 // are merged in order.  The argmax keeps the first tile holding the maximum,
 // i.e. the lowest vocabulary index.
 // pq (may be null): per-tile sums of e^2, merged into q the same way
+// k_combine1: 32 rows per block, each row's vocabulary tiles split over
+// kCombine1Threads / 32 segments (merged in segment order)
+constexpr int kCombine1Threads = 1024;
+
 __device__ __forceinline__ void seg_lse(const float* pm, const float* ps, const float* pq,
                                         int64_t ldp, int c, int t0, int t1, float& m, float& s,
                                         float& q, int& best) {
@@ -932,8 +936,8 @@ __device__ __forceinline__ void seg_lse(const float* pm, const float* ps, const 
     }
 }
 
-__global__ __launch_bounds__(256) void k_combine1(Combine1Launch a) {
-  constexpr int SEG = 8, RPB = 32;
+__global__ __launch_bounds__(kCombine1Threads) void k_combine1(Combine1Launch a) {
+  constexpr int SEG = kCombine1Threads / 32, RPB = 32;
   __shared__ float sm[2][SEG][RPB], ss[2][SEG][RPB], sq[SEG][RPB];
   __shared__ int sb[SEG][RPB];
   const int rr = threadIdx.x % RPB, seg = threadIdx.x / RPB;
@@ -1329,7 +1333,7 @@ hipError_t launch_rowdot(bool bf16, const RowdotLaunch& a, hipStream_t s) {
 }
 
 hipError_t launch_combine1(const Combine1Launch& a, hipStream_t s) {
-  hipLaunchKernelGGL(k_combine1, dim3((a.ncols + 31) / 32), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(k_combine1, dim3((a.ncols + 31) / 32), dim3(kCombine1Threads), 0, s, a);
   return hipGetLastError();
 }
 
