@@ -38,7 +38,7 @@ def parse():
     ap.add_argument("--shards", type=int, default=1,
                     help="G > 1: time one vocabulary shard's calls (V/G rows of W) and the "
                          "merges, i.e. one device's step of a G-way vocabulary-parallel group")
-    ap.add_argument("--cpu-sample-rows", type=int, default=1024)
+    ap.add_argument("--cpu-sample-rows", type=int, default=1536)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also copy a buffer of known size (for counter calibration)")
