@@ -86,16 +86,24 @@ def summarize(fetch_csv: str, write_csv: str, copy_bytes: int):
     ck = max(copies, key=lambda k: max(fetch[k]))
     f_fetch = copy_bytes / (max(fetch[ck]) * 1024.0)
     f_write = copy_bytes / (max(write.get(ck, [0.0])) * 1024.0) if write.get(ck) else None
+    # Kernels that share a trace name (e.g. one contraction built for two tile
+    # shapes) are counted as one entry of the library's trace: their bytes are
+    # added and divided by the dispatch count of the most frequent one.
+    groups = defaultdict(list)
+    for k in fetch:
+        if "specloss" in k:
+            groups[trace_name(k)].append(k)
     out = {}
-    for k, v in fetch.items():
-        if "specloss" not in k:
-            continue
-        fb = sum(v) / len(v) * 1024.0 * f_fetch
-        wv = write.get(k, [])
-        wb = (sum(wv) / len(wv) * 1024.0 * f_write) if (wv and f_write) else None
-        name = trace_name(k)
+    for name, ks in groups.items():
+        launches = max(len(fetch[k]) for k in ks)
+        fb = sum(sum(fetch[k]) for k in ks) / launches * 1024.0 * f_fetch
+        wb = None
+        if f_write and any(write.get(k) for k in ks):
+            w_launches = max(len(write.get(k, [])) for k in ks)
+            wb = sum(sum(write.get(k, [])) for k in ks) / w_launches * 1024.0 * f_write
         out[name] = {"fetch_bytes": fb, "write_bytes": wb,
-                     "bytes_per_launch": fb + (wb or 0.0), "dispatches": len(v)}
+                     "bytes_per_launch": fb + (wb or 0.0), "dispatches": launches,
+                     "kernels": len(ks)}
     return {"copy_kernel": ck, "copy_bytes": copy_bytes, "factor_fetch": f_fetch,
             "factor_write": f_write, "source_digest": source_digest(), "kernels": out}
 

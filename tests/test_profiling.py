@@ -47,3 +47,19 @@ def test_summarize_scales_by_the_copy(tmp_path):
     assert k["write_bytes"] == 10.0 * 1024 * 1.0
     assert s["source_digest"] == P.source_digest()
 
+
+def test_summarize_adds_kernels_of_one_launch(tmp_path):
+    copy = "__amd_rocclr_copyBuffer"
+    main = "void specloss::k_gemm<unsigned short, float, 1, false, 256>(x)"
+    tail = "void specloss::k_gemm<unsigned short, float, 1, false, 128>(x)"
+    rows = [{"Kernel_Name": copy, "Counter_Name": "FETCH_SIZE", "Counter_Value": 1024.0}]
+    for _ in range(3):
+        rows.append({"Kernel_Name": main, "Counter_Name": "FETCH_SIZE", "Counter_Value": 90.0})
+        rows.append({"Kernel_Name": tail, "Counter_Name": "FETCH_SIZE", "Counter_Value": 10.0})
+    _write(tmp_path / "f.csv", rows)
+    _write(tmp_path / "w.csv", [{"Kernel_Name": copy, "Counter_Name": "WRITE_SIZE", "Counter_Value": 1024.0}])
+    s = P.summarize(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"), 1 << 20)
+    k = s["kernels"]["gemm_dW"]
+    assert k["dispatches"] == 3 and k["kernels"] == 2
+    assert k["fetch_bytes"] == 100.0 * 1024      # main + tail per launch, factor 1
+
