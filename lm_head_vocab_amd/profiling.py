@@ -114,8 +114,9 @@ PMC_CMD = ("rocprofv3 --pmc {c} --output-format csv -d <{d}> -o pmc -- python3 <
            "--workload {w} --steps 1 --warmup 0 --no-cpu-baseline --calibrate-copy")
 
 
-def markdown(stats_csv: str, traffic: dict, workload: str) -> str:
-    """Markdown summary of a kernel-trace stats run and the counter passes."""
+def markdown(stats_csv: str, traffic: dict, workload: str, bench: dict = None) -> str:
+    """Markdown summary of a kernel-trace stats run and the counter passes
+    (and, if given, the bench.py line of a run on the same box)."""
     rows = list(csv.DictReader(open(stats_csv)))
     out = [f"# Kernel durations and HBM traffic: `{workload}` fwd+bwd", "",
            "One bench.py process runs the single call `lmhead_loss_fwd_bwd` (the headline) and the",
@@ -130,14 +131,22 @@ def markdown(stats_csv: str, traffic: dict, workload: str) -> str:
         out.append(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e6:.4f} | "
                    f"{float(r['TotalDurationNs']) / 1e6:.3f} | {float(r['Percentage']):.2f} |")
     out += ["", "`k_gemm<T, OutT, 1, ...>` is the dW contraction, `k_gemm<T, OutT, 0, ...>` the dh "
-            "contraction (the last template argument selects the copy-free variant).", "",
-            "## HBM bytes per launch", "", "Commands (two passes, each its own run):", "", "```",
+            "contraction (the last template argument selects the copy-free variant).", ""]
+    if bench:
+        r = bench["roofline"]
+        out += [f"`python3 bench.py --workload {workload}` on the same box, just before: "
+                f"{bench['value']:.0f} {bench['unit']}, {bench['ms_per_step']:.3f} ms per step; "
+                f"dominant kernel `{r['kernel']}` {r['avg_launch_ms']:.4f} ms per launch (HIP events "
+                f"on the library's stream), {r['achieved']:.1f} {r['unit']}, {r['frac']:.4f} of peak.",
+                ""]
+    out += ["## HBM bytes per launch", "", "Commands (two passes, each its own run):", "", "```",
             PMC_CMD.format(c="FETCH_SIZE", d="fetch", w=workload),
             PMC_CMD.format(c="WRITE_SIZE", d="write", w=workload),
             "python -m lm_head_vocab_amd.profiling --fetch <fetch>/pmc_counter_collection.csv "
             "--write <write>/pmc_counter_collection.csv --copy-bytes "
             f"{traffic['copy_bytes']} --out profiles/traffic_{workload}.json --stats "
-            "<out>/run_kernel_stats.csv --md <this file> --workload " + workload, "```", "",
+            "<out>/run_kernel_stats.csv --md <this file> --workload " + workload
+            + (" --bench-json <bench.py output>" if bench else ""), "```", "",
             f"`--calibrate-copy` copies {traffic['copy_bytes'] / 2**30:g} GiB inside the same "
             f"process; the counters of that copy (`{traffic['copy_kernel']}`) give the scale "
             f"factors FETCH_SIZE x {traffic['factor_fetch']:.3f}, WRITE_SIZE x "
@@ -159,13 +168,18 @@ def main():
     ap.add_argument("--stats", default=None, help="rocprofv3 kernel_stats.csv of the same benchmark")
     ap.add_argument("--md", default=None, help="markdown summary to write (needs --stats)")
     ap.add_argument("--workload", default="ce_bf16_8b")
+    ap.add_argument("--bench-json", default=None, help="bench.py output of a run on the same box")
     a = ap.parse_args()
     s = summarize(a.fetch, a.write, a.copy_bytes)
     with open(a.out, "w") as f:
         json.dump(s, f, indent=1)
     if a.md and a.stats:
+        bench = None
+        if a.bench_json:
+            with open(a.bench_json) as f:
+                bench = json.loads([l for l in f.read().splitlines() if l.strip()][-1])
         with open(a.md, "w") as f:
-            f.write(markdown(a.stats, s, a.workload))
+            f.write(markdown(a.stats, s, a.workload, bench))
     print(json.dumps({k: round(v["bytes_per_launch"] / 1e9, 3) for k, v in s["kernels"].items()}))
 
 

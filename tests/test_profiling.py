@@ -63,3 +63,21 @@ def test_summarize_adds_kernels_of_one_launch(tmp_path):
     assert k["dispatches"] == 3 and k["kernels"] == 2
     assert k["fetch_bytes"] == 100.0 * 1024      # main + tail per launch, factor 1
 
+
+
+def test_markdown_lists_kernels_traffic_and_bench(tmp_path):
+    with open(tmp_path / "stats.csv", "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Name", "Calls", "TotalDurationNs", "AverageNs", "Percentage"])
+        w.writeheader()
+        w.writerow({"Name": "void specloss::k_gemm<unsigned short, float, 1, false>(specloss::GemmLaunch)",
+                    "Calls": 4, "TotalDurationNs": 4e6, "AverageNs": 1e6, "Percentage": 100.0})
+    traffic = {"copy_kernel": "__amd_rocclr_copyBuffer", "copy_bytes": 1 << 30, "factor_fetch": 2.0,
+               "factor_write": 1.0, "source_digest": "abc",
+               "kernels": {"gemm_dW": {"fetch_bytes": 2e9, "write_bytes": 1e9, "bytes_per_launch": 3e9}}}
+    bench = {"value": 1000.0, "unit": "tokens/s", "ms_per_step": 4.0,
+             "roofline": {"kernel": "gemm_dW", "avg_launch_ms": 1.0, "achieved": 100.0,
+                          "unit": "TFLOP/s", "frac": 0.04}}
+    md = P.markdown(str(tmp_path / "stats.csv"), traffic, "ce_bf16_8b", bench)
+    assert "| `void k_gemm<unsigned short, float, 1, false>(GemmLaunch)` | 4 | 1.0000 |" in md
+    assert "| gemm_dW | 2.000 | 1.000 | 3.000 |" in md
+    assert "--workload ce_bf16_8b" in md and "`gemm_dW` 1.0000 ms per launch" in md
