@@ -6,6 +6,9 @@ notice it; at least one of them must fail.  The mutated functions are copies
 of the oracle's with the slip written in: a swapped p / q, a dropped term, a
 wrong sign, a transposed reduction, an off-by-one, a missing normalisation.
 """
+import inspect
+import textwrap
+
 import numpy as np
 import pytest
 
@@ -114,6 +117,29 @@ def _validity_ignores_mask(prob):
         prob.mask = saved
 
 
+def _rewrite(fn, *edits):
+    """A copy of oracle function `fn` with each (old, new) source edit applied
+    (the slip written into the oracle's own code), compiled in the oracle's
+    namespace."""
+    src = textwrap.dedent(inspect.getsource(fn))
+    for old, new in edits:
+        assert old in src, f"{fn.__name__} no longer contains {old!r}"
+        src = src.replace(old, new)
+    ns = dict(vars(O))
+    exec(compile(src, f"<mutant of {fn.__name__}>", "exec"), ns)
+    return ns[fn.__name__]
+
+
+# compositions inside the per-block forward, each slip planted in a copy of it
+_block_ce_from_draft = _rewrite(O._block, ("y = argmax_lowest(u)", "y = argmax_lowest(z)"))
+_block_normalised = _rewrite(
+    O._block, ("loss += w * terms[k]", "loss += w / sum(act.values()) * terms[k]"),
+    ("dz += w * dzs[k]", "dz += w / sum(act.values()) * dzs[k]"))
+_target_rows_off_by_one = _rewrite(
+    O._target_rows, ("tr = np.asarray(prob.target_row, dtype=np.int64)[idx]",
+                     "tr = np.asarray(prob.target_row, dtype=np.int64)[idx] - 1"))
+
+
 # (name, oracle attribute, replacement, whether DIVERGENCES holds it, pins that must notice)
 MUTATIONS = [
     ("kl swaps p and q", "kl_forward", _kl_swapped, "kl_div",
@@ -148,6 +174,12 @@ MUTATIONS = [
      [P.test_torch_cpu_fp64_ce_and_autograd]),
     ("mask ignored", "row_validity", _validity_ignores_mask, None,
      [P.test_validity_bad_rows, P.test_masked_rows_do_not_contribute]),
+    ("ce label taken from the draft logits", "_block", _block_ce_from_draft, None,
+     [P.test_ce_label_is_argmax_of_target_logits, P.test_weighted_combination_unnormalised]),
+    ("weights normalised by their sum", "_block", _block_normalised, None,
+     [P.test_weighted_combination_unnormalised]),
+    ("target row map off by one", "_target_rows", _target_rows_off_by_one, None,
+     [P.test_target_rows_follow_the_head_shift, P.test_statistical_sanity_multihead_alpha]),
 ]
 
 

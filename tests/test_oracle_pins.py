@@ -428,3 +428,102 @@ def test_tv_tie_rule_central_difference():
     assert np.count_nonzero(np.exp(logp) == np.exp(logq0)) == V - 2
     # O(eps) error: the second derivatives differ on the two sides of the kink
     assert np.allclose(dz[0], num, rtol=0, atol=1e-6), (dz[0], num)
+
+
+# --------------------------------------------------------------- compositions
+def _pair_problem(seed, N, H, V, weights, **kw):
+    """Draft and target sides drawn independently (f64), so their argmaxes differ."""
+    rng = np.random.default_rng(seed)
+    return O.OracleProblem(dtype="f64", vocab=V, hidden=rng.standard_normal((N, H)),
+                           W=rng.standard_normal((V, H)), weights=dict(weights),
+                           target_hidden=rng.standard_normal((N, H)),
+                           W_t=rng.standard_normal((V, H)), **kw)
+
+
+def test_ce_label_is_argmax_of_target_logits():
+    """"Available Losses", ce row: cross-entropy of the draft against argmax p.
+
+    Library route: torch CPU fp64 cross_entropy of the draft logits h W^T against
+    torch.argmax of the TARGET logits g W_t^T, and its autograd for dz, on rows
+    where the draft's own argmax is a different index (so a label taken from
+    the draft side fails).
+    """
+    prob = _pair_problem(21, N=12, H=16, V=40, weights={"ce": 1.0})
+    r = O.forward(prob, want_dz=True)
+    z = torch.tensor(prob.hidden) @ torch.tensor(prob.W).T
+    u = torch.tensor(prob.target_hidden) @ torch.tensor(prob.W_t).T
+    y = torch.argmax(u, dim=1)
+    assert int((y != torch.argmax(z, dim=1)).sum()) >= prob.n_rows // 2
+    assert np.array_equal(r.label, y.numpy())
+    ref = torch.nn.functional.cross_entropy(z, y, reduction="none")
+    assert np.allclose(r.terms["ce"], ref.numpy(), rtol=1e-12, atol=0)
+    zg = z.clone().requires_grad_(True)
+    torch.nn.functional.cross_entropy(zg, y, reduction="sum").backward()
+    assert np.allclose(r.dz, zg.grad.numpy(), rtol=1e-10, atol=1e-14)
+
+
+def test_weighted_combination_unnormalised():
+    """"Weighted Combinations": weights are used as given (not normalised) and each
+    term is reported before its weight.
+
+    {ce: 2, tv: 3}: torch CPU fp64 forms ce (cross_entropy against argmax u) and
+    tv (half the L1 distance of the two softmaxes) independently; the oracle's
+    per-row loss must be 2 ce + 3 tv exactly, its terms the unweighted ce and tv,
+    and its dh, dW the autograd of the mean of 2 ce + 3 tv.
+    """
+    prob = _pair_problem(22, N=10, H=12, V=30, weights={"ce": 2.0, "tv": 3.0})
+    r = O.forward(prob)
+    h = torch.tensor(prob.hidden, requires_grad=True)
+    W = torch.tensor(prob.W, requires_grad=True)
+    z = h @ W.T
+    u = torch.tensor(prob.target_hidden) @ torch.tensor(prob.W_t).T
+    ce = torch.nn.functional.cross_entropy(z, torch.argmax(u, dim=1), reduction="none")
+    tv = 0.5 * (torch.softmax(u, 1) - torch.softmax(z, 1)).abs().sum(1)
+    assert np.allclose(r.terms["ce"], ce.detach().numpy(), rtol=1e-12, atol=0)
+    assert np.allclose(r.terms["tv"], tv.detach().numpy(), rtol=1e-12, atol=0)
+    assert np.allclose(r.loss, (2.0 * ce + 3.0 * tv).detach().numpy(), rtol=1e-12, atol=0)
+    ((2.0 * ce + 3.0 * tv).sum() / prob.n_rows).backward()
+    dh, dW = O.backward(prob)
+    assert np.allclose(dh, h.grad.numpy(), rtol=1e-10, atol=1e-14)
+    assert np.allclose(dW, W.grad.numpy(), rtol=1e-10, atol=1e-14)
+
+
+def test_target_rows_follow_the_head_shift():
+    """Blog, "Correctness: alignment before chunking": head k at position t is paired
+    with target position t + shift_k.
+
+    Hand-built: target hidden g[t] = (t + 1) e_t and W_t = I, so the target
+    logits of a row are t' + 1 at t' = its target position and 0 elsewhere.
+    With shifts (1, 2) over 6 positions the valid rows' ce labels are, by hand,
+    1..5 then 2..5, and lse_p = ln(e^(t'+1) + V - 1).
+    """
+    S, V = 6, 8
+    g = np.zeros((S, V))
+    for t in range(S):
+        g[t, t] = t + 1.0
+    target_row = np.array([1, 2, 3, 4, 5, -1, 2, 3, 4, 5, -1, -1], np.int32)
+    mask = np.array([1, 1, 1, 1, 1, 0, 1, 1, 1, 1, 0, 0], np.uint8)
+    rng = np.random.default_rng(23)
+    prob = O.OracleProblem(dtype="f64", vocab=V, hidden=rng.standard_normal((12, V)),
+                           W=rng.standard_normal((V, V)), weights={"ce": 1.0},
+                           target_hidden=g, W_t=np.eye(V), target_row=target_row, mask=mask)
+    r = O.forward(prob)
+    valid = mask == 1
+    expect = [1, 2, 3, 4, 5, 2, 3, 4, 5]
+    assert list(r.label[valid]) == expect
+    assert np.allclose(r.lse_p[valid], [math.log(math.exp(t + 1) + V - 1) for t in expect],
+                       rtol=1e-14, atol=0)
+
+
+def test_statistical_sanity_multihead_alpha():
+    """Not parity: the three-head workload pairs draft h = g[t+k] with target row
+    t+k, so u - z = (W_t - W) g has a per-logit std delta = 0.005 sqrt(H) and the
+    mean alpha is about 2 Phi(-delta/2): 0.749 at H = 16384 (derived for large V,
+    not on the pages).  A row map off by one pairs independent rows instead
+    (alpha near 0.2)."""
+    p = synthetic.make_problem("multihead_bf16_405b", seq_len=16, hidden_dim=16384, vocab=2048)
+    r = O.forward(p)
+    delta = 0.005 * math.sqrt(16384)
+    expect = 2 * sst.norm.cdf(-delta / 2)
+    assert abs(expect - 0.749) < 1e-3
+    assert abs(r.alpha[r.valid].mean() - expect) < 0.015, r.alpha[r.valid].mean()
