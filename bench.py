@@ -34,7 +34,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="ce_bf16_8b")
-    ap.add_argument("--chunk", type=int, default=8192, help="max rows per chunk")
+    ap.add_argument("--chunk", type=int, default=0,
+                    help="max rows per chunk (0: the library's default streaming policy)")
     ap.add_argument("--shards", type=int, default=1,
                     help="G > 1: time one vocabulary shard's calls (V/G rows of W) and the "
                          "merges, i.e. one device's step of a G-way vocabulary-parallel group")
@@ -139,6 +140,8 @@ def main():
         run.backward(grad_mean=gmean, dhidden=dh, dW=dW, stream=stream)
         p0, s0 = run.problems[0], run.shards[0]
         v_shard = run.bounds[1]
+        chunk_rows, chunk_layout = L.binding.lmhead_loss_chunk(p0, run.workspace.numel(),
+                                                               L.binding.CALL_BWD)
         dh_part = torch.empty((N, H), dtype=torch.float32, device=dev)
         terms = torch.empty(L.binding.NUM_KINDS, N, dtype=torch.float32, device=dev)
 
@@ -155,6 +158,7 @@ def main():
     else:
         run = LossRun(h, W, prob.weights, max_chunk_rows=args.chunk, want_terms=False, **inputs)
         v_shard = V
+        chunk_rows, chunk_layout = run.chunk(L.binding.CALL_FWD_BWD)
 
         def step_single():
             run.forward_backward(grad_mean=gmean, dhidden=dh, dW=dW, stream=stream)
@@ -233,7 +237,7 @@ def main():
         "dtype": "bf16",
         "data": f"synthetic (seeded; {prob.recipe})",
         "config": {"workload": args.workload, "tokens": N, "hidden": H, "vocab": V,
-                   "loss": prob.weights, "chunk_rows": args.chunk,
+                   "loss": prob.weights, "chunk_rows": chunk_rows, "bwd_layout": chunk_layout,
                    "call": "lmhead_loss_fwd_bwd" if G == 1 else
                    "lmhead_shard_pass1/merge1/pass2/merge2/bwd of shard 0",
                    "parallelism": "none (1 GPU)" if G == 1 else
@@ -246,6 +250,7 @@ def main():
         "peak_hbm_gib_above_inputs": round((peak_bytes - base_alloc) / 2**30, 3),
         "logits_sized_limit_gib": round(N * V * 2 / 2**30, 3),
         "workspace_gib": round(run.workspace.numel() / 2**30, 3),
+        "workspace_below_logits": bool(run.workspace.numel() < N * V * 2),
         "roofline": kern,
         "two_calls": None if step_two is None else {
             "value": round(N / (ms_two * 1e-3), 1), "ms_per_step": round(ms_two, 3),
@@ -261,11 +266,14 @@ def main():
         "input_gen_s": round(gen_s, 1),
     }
     if args.blas_reference and G == 1 and inputs["labels"] is not None:
-        result["blas_reference"] = blas_reference(h, W, inputs["labels"], min(args.chunk, N), N,
+        result["blas_reference"] = blas_reference(h, W, inputs["labels"], min(chunk_rows, N), N,
                                                   kernels)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(prob, args.cpu_sample_rows)
     print(json.dumps(result), flush=True)
+    if not result["workspace_below_logits"]:
+        print(f"warning: the workspace ({result['workspace_gib']} GiB) is not below the [N, V] "
+              f"bf16 logits size ({result['logits_sized_limit_gib']} GiB)", file=sys.stderr)
 
 
 def blas_reference(h, W, labels, nc, N, kernels):

@@ -77,14 +77,19 @@ enum {
 #define SPECLOSS_IGNORE_INDEX (-100)
 
 /*
- * Backward layout choice (specloss_problem.flags).  0: automatic (see
- * lmhead_loss_workspace_size).  SPECLOSS_FLAG_COPIES: always make the
- * transposed copies (SPECLOSS_E_WORKSPACE if they do not fit).
- * SPECLOSS_FLAG_NO_COPIES: never (bf16 only, SPECLOSS_E_UNSUPPORTED for fp32).
+ * Backward layout choice (specloss_problem.flags).  The two gradient
+ * contractions read their operands either from transposed copies made in the
+ * workspace (W^T for dhidden; the chunk's hidden rows and logit gradient
+ * transposed for dW) or in place.  0: automatic (see
+ * lmhead_loss_workspace_size).  SPECLOSS_FLAG_COPIES: always make every copy
+ * (SPECLOSS_E_WORKSPACE if they do not fit).  SPECLOSS_FLAG_NO_WEIGHT_COPY:
+ * the dW copies but no W^T (dhidden reads W in place).  SPECLOSS_FLAG_NO_COPIES:
+ * no copy.  The last two are bf16 only (SPECLOSS_E_UNSUPPORTED for fp32).
  * Other values: SPECLOSS_E_INVAL.
  */
 #define SPECLOSS_FLAG_COPIES 1
 #define SPECLOSS_FLAG_NO_COPIES 2
+#define SPECLOSS_FLAG_NO_WEIGHT_COPY 3
 
 /*
  * Per-row state the forward saves for the backward: SPECLOSS_SAVED_FIELDS
@@ -121,9 +126,9 @@ typedef struct specloss_trace specloss_trace;
  * normalise by valid tokens, not by chunks).
  */
 typedef struct {
-  int64_t n_rows;              /* N > 0 */
-  int64_t hidden;              /* H > 0, multiple of 64 */
-  int64_t vocab;               /* V > 0, < 2^31 */
+  int64_t n_rows;              /* N > 0, < 2^30 */
+  int64_t hidden;              /* H > 0, multiple of 64, < 2^30 */
+  int64_t vocab;               /* V > 0, < 2^30 (SPECLOSS_E_UNSUPPORTED above) */
   int32_t in_dtype;            /* specloss_dtype of hidden_states, W, target_hidden, W_t */
   int32_t flags;               /* 0, or one of SPECLOSS_FLAG_* (backward layout choice) */
   const void* hidden_states;   /* [N, H] draft hidden states */
@@ -140,20 +145,50 @@ typedef struct {
 } specloss_problem;
 
 /*
- * Bytes of device workspace needed by any of the calls below when at most
- * `max_chunk_rows` rows are processed per chunk (rounded up to a multiple of
- * 256; <= 0 selects 8192).
- * The backward stages a bf16 (fp32 for fp32 inputs) logit-gradient chunk of
- * about 2 * chunk * V elements and a transposed copy of W; no buffer of
- * N x V elements is ever needed.  The calls pick the largest chunk that fits
- * the workspace they are given.  With bf16 inputs and a workspace that holds
- * the copies only at chunks below min(N, 1024) rows, the backward makes no
- * copies (its contractions read W, the hidden rows and the logit gradient as
- * they are, about 1.5x slower) and needs about half the workspace.
+ * Bytes of device workspace needed by any of the calls below.  The calls
+ * process the rows in chunks (blog, "Streaming Cross Entropy" and "Backward
+ * pass": per chunk, its logits, loss and gradients; only per-row statistics
+ * outlive a chunk).  The single call and the backward stage a logit-gradient
+ * chunk of about 2 x chunk x V elements (3 x for the staged divergences) in
+ * the input dtype, which is the blog's streaming bound chunk x vocab x
+ * dtype x 2, plus (by default) a transposed copy of W.
+ *   max_chunk_rows <= 0: the default policy.  The token set is streamed in
+ *     at least four balanced chunks of at most 8192 rows, and the whole
+ *     workspace stays strictly below N x V x (input element size) bytes, the
+ *     size of the full logits tensor ("Backward pass": the streaming loss
+ *     never stores the full logits).  Layouts are tried in the order every
+ *     copy, no W^T copy, no copy (bf16), each with the largest chunk that
+ *     fits; a layout is taken once its chunk reaches min(N, 1024) rows.  When
+ *     no chunk fits below that size (tiny problems, whose W^T copy alone
+ *     exceeds it), 256-row chunks with every copy are used.
+ *   max_chunk_rows > 0: that many rows per chunk (rounded up to a multiple
+ *     of 256, at most N rounded up), with every copy unless flags say
+ *     otherwise.
+ * The calls pick the largest chunk that fits the workspace they are given,
+ * with every copy when that chunk reaches min(N, 1024) rows, otherwise
+ * (bf16) without the W^T copy or without any copy if that allows a larger
+ * chunk; lmhead_loss_chunk reports the choice.  SPECLOSS_E_INVAL for a NULL
+ * `bytes` and as for the calls.
  */
 int lmhead_loss_workspace_size(const specloss_problem* p, int64_t max_chunk_rows, size_t* bytes);
 
-/* Bytes of the `saved` buffer for n_rows rows (256-byte aligned arrays). */
+/*
+ * The chunk the calls use with a workspace of ws_bytes: rows per chunk and
+ * the backward layout (0 every copy, 1 no W^T copy, 2 no copy), for `call`
+ * 0 = lmhead_loss_fwd, 1 = lmhead_loss_bwd, 2 = lmhead_loss_fwd_bwd.  Host
+ * only.  SPECLOSS_E_WORKSPACE when no chunk fits, SPECLOSS_E_INVAL for a NULL
+ * output or an unknown call, and as for the calls.
+ */
+int lmhead_loss_chunk(const specloss_problem* p, size_t ws_bytes, int32_t call,
+                      int64_t* chunk_rows, int32_t* layout);
+
+/*
+ * Bytes of the `saved` buffer for n_rows rows (SPECLOSS_SAVED_FIELDS arrays of
+ * n_rows 4-byte values, each 256-byte aligned); 0 for n_rows <= 0.  This is
+ * the per-row state that outlives a chunk (blog, "Streaming Cross Entropy":
+ * the loss of a token needs only its own logsumexp and label logit; the
+ * target-vs-draft sums of "Available Losses" per row).  Host only.
+ */
 size_t specloss_saved_bytes(int64_t n_rows);
 
 /*
@@ -165,7 +200,11 @@ size_t specloss_saved_bytes(int64_t n_rows);
 int specloss_saved_offset(int64_t n_rows, int32_t field, size_t* offset);
 
 /*
- * Forward.  Outputs (device):
+ * Forward (blog, "Streaming Cross Entropy": per chunk of tokens, the logits of
+ * the chunk, the per-token losses and their sum; "Backward pass": the mean
+ * divides by the valid tokens; speculators "Loss Functions", "Available
+ * Losses" and "Weighted Combinations" for the kinds and their weights).
+ * Outputs (device):
  *   loss      [N]    fp32, required: sum_k weights[k] * L_k(row), 0 on invalid rows.
  *   term_loss [K][N] fp32 or NULL: unweighted L_k(row) for every kind k
  *                    (rows of kinds that are off are left untouched); the
@@ -182,7 +221,10 @@ int lmhead_loss_fwd(const specloss_problem* p, void* workspace, size_t ws_bytes,
                     hipStream_t stream);
 
 /*
- * Backward of sum_r seed_r * loss_r, with
+ * Backward (blog, "Backward pass": per chunk, the logits gradient, the
+ * hidden-state gradient of the chunk, and the LM-head gradient accumulated
+ * over chunks; the chunk's logits tiles are recomputed here from the saved
+ * per-row state).  Gradient of sum_r seed_r * loss_r, with
  *   seed_r = (grad_loss ? grad_loss[r] : 0) + (grad_mean ? grad_mean[0] / n_valid : 0)
  * on valid rows and 0 elsewhere (grad_mean is the gradient of the mean
  * loss; counts and saved come from lmhead_loss_fwd on the same problem).

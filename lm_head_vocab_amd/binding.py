@@ -20,7 +20,7 @@ KINDS = ("ce_label", "ce", "kl_div", "rkl", "jsd", "tv", "nla", "lk_hybrid")
 NUM_KINDS = len(KINDS)
 F32, BF16 = 0, 1
 IGNORE_INDEX = -100
-SAVED_FIELDS = 9
+SAVED_FIELDS = 10
 
 
 class SpecLossError(RuntimeError):
@@ -56,6 +56,7 @@ _lib: Optional[ctypes.CDLL] = None
 
 EXPORTS = (
     "lmhead_loss_workspace_size",
+    "lmhead_loss_chunk",
     "specloss_saved_bytes",
     "specloss_saved_offset",
     "lmhead_loss_fwd",
@@ -104,6 +105,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     P = ctypes.POINTER(Problem)
     lib.lmhead_loss_workspace_size.argtypes = [P, i64, ctypes.POINTER(sz)]
     lib.lmhead_loss_workspace_size.restype = ctypes.c_int
+    lib.lmhead_loss_chunk.argtypes = [P, sz, i32, ctypes.POINTER(i64), ctypes.POINTER(i32)]
+    lib.lmhead_loss_chunk.restype = ctypes.c_int
     lib.specloss_saved_bytes.argtypes = [i64]
     lib.specloss_saved_bytes.restype = sz
     lib.specloss_saved_offset.argtypes = [i64, i32, ctypes.POINTER(sz)]
@@ -185,7 +188,7 @@ def make_problem(hidden: torch.Tensor, W: torch.Tensor, weights: Dict[str, float
                  target_row: Optional[torch.Tensor] = None, flags: int = 0) -> Problem:
     """Fill a ``specloss_problem`` from torch tensors (no copies, no checks beyond dtype).
 
-    flags: 0 (automatic), FLAG_COPIES or FLAG_NO_COPIES (backward layout).
+    flags: 0 (automatic), FLAG_COPIES, FLAG_NO_WEIGHT_COPY or FLAG_NO_COPIES (backward layout).
     """
     if hidden.dtype not in (torch.float32, torch.bfloat16) or W.dtype != hidden.dtype:
         raise ValueError("hidden and W must both be float32 or both bfloat16")
@@ -217,12 +220,25 @@ def lmhead_loss_workspace_size(problem: Problem, max_chunk_rows: int = 0) -> int
     return out.value
 
 
+CALL_FWD, CALL_BWD, CALL_FWD_BWD = 0, 1, 2
+LAYOUTS = ("copies", "no_weight_copy", "no_copies")
+
+
+def lmhead_loss_chunk(problem: Problem, ws_bytes: int, call: int = CALL_FWD_BWD):
+    """(rows per chunk, backward layout name) the call uses with ws_bytes of workspace."""
+    rows, lay = ctypes.c_int64(0), ctypes.c_int32(0)
+    _check(load_library().lmhead_loss_chunk(ctypes.byref(problem), ws_bytes, call,
+                                            ctypes.byref(rows), ctypes.byref(lay)),
+           "lmhead_loss_chunk")
+    return rows.value, LAYOUTS[lay.value]
+
+
 def specloss_saved_bytes(n_rows: int) -> int:
     return int(load_library().specloss_saved_bytes(n_rows))
 
 
 # backward layout choice (SPECLOSS_FLAG_* in include/specloss.h)
-FLAG_COPIES, FLAG_NO_COPIES = 1, 2
+FLAG_COPIES, FLAG_NO_COPIES, FLAG_NO_WEIGHT_COPY = 1, 2, 3
 
 # public saved fields (SPECLOSS_SAVED_* in include/specloss.h)
 SAVED_LSE_Q, SAVED_LSE_P, SAVED_Y_ARG, SAVED_ALPHA, SAVED_VALID, SAVED_FLATNESS = 0, 1, 3, 4, 8, 9

@@ -71,11 +71,13 @@ int check_problem(const specloss_problem* p, KindSet* ks) {
   if (p->n_rows <= 0 || p->hidden <= 0 || p->vocab <= 0) return SPECLOSS_E_INVAL;
   if (p->n_rows > INT32_MAX / 2 || p->vocab > INT32_MAX / 2 || p->hidden > INT32_MAX / 2)
     return SPECLOSS_E_UNSUPPORTED;
-  if (p->flags != 0 && p->flags != SPECLOSS_FLAG_COPIES && p->flags != SPECLOSS_FLAG_NO_COPIES)
+  if (p->flags != 0 && p->flags != SPECLOSS_FLAG_COPIES && p->flags != SPECLOSS_FLAG_NO_COPIES &&
+      p->flags != SPECLOSS_FLAG_NO_WEIGHT_COPY)
     return SPECLOSS_E_INVAL;
   if (p->in_dtype != SPECLOSS_F32 && p->in_dtype != SPECLOSS_BF16) return SPECLOSS_E_UNSUPPORTED;
   if (p->hidden % 64 != 0) return SPECLOSS_E_UNSUPPORTED;
-  if (p->flags == SPECLOSS_FLAG_NO_COPIES && p->in_dtype != SPECLOSS_BF16)
+  if ((p->flags == SPECLOSS_FLAG_NO_COPIES || p->flags == SPECLOSS_FLAG_NO_WEIGHT_COPY) &&
+      p->in_dtype != SPECLOSS_BF16)
     return SPECLOSS_E_UNSUPPORTED;
   if (!p->hidden_states || !p->W) return SPECLOSS_E_INVAL;
   if (!aligned(p->hidden_states, 16) || !aligned(p->W, 16)) return SPECLOSS_E_UNSUPPORTED;
@@ -104,13 +106,24 @@ int check_problem(const specloss_problem* p, KindSet* ks) {
   return SPECLOSS_OK;
 }
 
+// Which transposed copies the backward contractions read.  A K-major copy
+// lets a contraction read 16-byte fragments; without it the operand is read
+// in place (MN-major) through the transposing LDS load (bf16 only).
+enum BwdLayout : int32_t {
+  LAYOUT_COPIES = 0,     // W^T for dh; h^T and dz^T for dW
+  LAYOUT_DW_COPIES = 1,  // dh reads W in place; h^T and dz^T for dW
+  LAYOUT_NONE = 2        // dh reads W, dW reads dz and the hidden rows in place
+};
+
 // Workspace: a head used by both directions, then the forward and backward
 // regions, which overlap (the two directions never run at the same time on
 // one workspace).
 struct Layout {
   int64_t N, H, V, Vp, Tv, Nc;
   size_t es;
-  bool copies;  // the backward contractions read transposed copies (W^T, h^T, dz^T)
+  int32_t layout;   // BwdLayout
+  bool wt_copy;     // dh reads the copy W^T [H][Vp]
+  bool dw_copies;   // dW reads the copies h^T [H][Nc] and dz^T [Vp][Nc]
   // head
   size_t terms, saved, seed, tstat, head_end;
   // rows share target rows (a row map onto fewer target rows than rows): the
@@ -125,11 +138,9 @@ struct Layout {
   size_t f_pz, f_pu, f_p2, f_zy, f_wt, f_ht, f_dz, f_dd, f_dzt, fused_end;
 };
 
-// copies: make transposed copies for the backward contractions (always for
-// fp32).  Without them (bf16 only) the contractions read W, h and dz as
-// MN-major operands through the transposing LDS load, which needs about half
-// the workspace but runs the contractions about 1.5x slower.
-Layout plan(const specloss_problem* p, const KindSet& k, int64_t Nc, bool copies = true) {
+// fp32 inputs always take LAYOUT_COPIES (the transposing LDS load is bf16).
+Layout plan(const specloss_problem* p, const KindSet& k, int64_t Nc,
+            int32_t layout = LAYOUT_COPIES) {
   Layout L;
   L.N = p->n_rows;
   L.H = p->hidden;
@@ -138,6 +149,9 @@ Layout plan(const specloss_problem* p, const KindSet& k, int64_t Nc, bool copies
   L.Tv = L.Vp / kVocabTile;
   L.Nc = Nc;
   L.es = elem_size(p);
+  L.layout = L.es == 4 ? LAYOUT_COPIES : layout;
+  L.wt_copy = L.layout == LAYOUT_COPIES;
+  L.dw_copies = L.layout != LAYOUT_NONE;
   size_t o = 0;
   auto take = [&](size_t bytes) {
     const size_t at = o;
@@ -157,43 +171,47 @@ Layout plan(const specloss_problem* p, const KindSet& k, int64_t Nc, bool copies
   L.p2 = take(k.pass2 ? (size_t)kNumSums * tile_cols : 0);
   L.zy = take(2 * (size_t)Nc * 4);
   L.fwd_end = o;
-  L.copies = copies || L.es == 4;
   o = L.head_end;
-  L.wt = take(L.copies ? (size_t)L.H * L.Vp * L.es : 0);
-  L.ht = take(L.copies ? (size_t)L.H * Nc * L.es : 0);
+  L.wt = take(L.wt_copy ? (size_t)L.H * L.Vp * L.es : 0);
+  L.ht = take(L.dw_copies ? (size_t)L.H * Nc * L.es : 0);
   L.dz = take((size_t)Nc * L.Vp * L.es);
-  L.dzt = take(L.copies ? (size_t)L.Vp * Nc * L.es : 0);
+  L.dzt = take(L.dw_copies ? (size_t)L.Vp * Nc * L.es : 0);
   L.bwd_end = o;
   o = L.head_end;
   L.f_pz = take(2 * tile_cols);
   L.f_pu = take(k.target ? 4 * tile_cols : 0);
   L.f_p2 = take(k.stage_div ? (size_t)kNumSums * tile_cols : 0);
   L.f_zy = take(2 * (size_t)Nc * 4);
-  L.f_wt = take(L.copies ? (size_t)L.H * L.Vp * L.es : 0);
-  L.f_ht = take(L.copies ? (size_t)L.H * Nc * L.es : 0);
+  L.f_wt = take(L.wt_copy ? (size_t)L.H * L.Vp * L.es : 0);
+  L.f_ht = take(L.dw_copies ? (size_t)L.H * Nc * L.es : 0);
   L.f_dz = take((size_t)Nc * L.Vp * L.es);
   L.f_dd = take(k.stage_div ? (size_t)Nc * L.Vp * L.es : 0);
-  L.f_dzt = take(L.copies ? (size_t)L.Vp * Nc * L.es : 0);
+  L.f_dzt = take(L.dw_copies ? (size_t)L.Vp * Nc * L.es : 0);
   L.fused_end = o;
   return L;
 }
 
-// largest chunk (multiple of 256, at most the padded row count) whose region fits
 enum Region { REGION_FWD, REGION_BWD, REGION_FUSED };
 
 size_t region_end(const Layout& L, Region r) {
   return r == REGION_FWD ? L.fwd_end : (r == REGION_BWD ? L.bwd_end : L.fused_end);
 }
 
-// Largest chunk (multiple of 256) whose region fits.
+size_t workspace_end(const Layout& L) {
+  size_t b = L.fwd_end > L.bwd_end ? L.fwd_end : L.bwd_end;
+  return L.fused_end > b ? L.fused_end : b;
+}
+
+// Largest chunk (multiple of 256, at most `top` rows) whose region fits
+// `ws_bytes` (strictly below it when `strict`).
 int64_t largest_chunk(const specloss_problem* p, const KindSet& k, size_t ws_bytes,
-                      Region region, bool copies) {
-  const int64_t top = round_up(p->n_rows, kChunkQuantum);
+                      Region region, int32_t layout, int64_t top, bool strict = false) {
   int64_t lo = 1, hi = top / kChunkQuantum, best = 0;
   while (lo <= hi) {  // the requirement grows with the chunk
     const int64_t mid = (lo + hi) / 2;
-    const Layout L = plan(p, k, mid * kChunkQuantum, copies);
-    if (region_end(L, region) <= ws_bytes) {
+    const Layout L = plan(p, k, mid * kChunkQuantum, layout);
+    const size_t need = region_end(L, region);
+    if (strict ? need < ws_bytes : need <= ws_bytes) {
       best = mid;
       lo = mid + 1;
     } else {
@@ -203,31 +221,81 @@ int64_t largest_chunk(const specloss_problem* p, const KindSet& k, size_t ws_byt
   return best * kChunkQuantum;
 }
 
-// Chunk for a region, and (backward regions) whether to make transposed
-// copies: with copies when the workspace holds them at a chunk of at least
-// min(N, 1024) rows; otherwise (bf16) without, if that allows a larger chunk.
-// (The copy-free contractions run about 1.5x slower; below about 1000 rows
-// per chunk the fp32 read-modify-write of dW per chunk costs more than that
-// at the large shapes.)
-// flags force the choice (SPECLOSS_FLAG_COPIES / _NO_COPIES).
-int64_t pick_chunk(const specloss_problem* p, const KindSet& k, size_t ws_bytes, Region region,
-                   bool* copies = nullptr) {
-  if (copies && p->flags == SPECLOSS_FLAG_NO_COPIES) {
-    *copies = false;
-    return largest_chunk(p, k, ws_bytes, region, false);
+int32_t forced_layout(const specloss_problem* p) {
+  switch (p->flags) {
+    case SPECLOSS_FLAG_COPIES: return LAYOUT_COPIES;
+    case SPECLOSS_FLAG_NO_WEIGHT_COPY: return LAYOUT_DW_COPIES;
+    case SPECLOSS_FLAG_NO_COPIES: return LAYOUT_NONE;
+    default: return -1;
   }
-  int64_t nc = largest_chunk(p, k, ws_bytes, region, true);
-  if (copies) *copies = true;
-  if (!copies) return nc;
+}
+
+// Chunk for a region and the backward layout.  With every copy when the
+// workspace holds them at a chunk of at least min(N, 1024) rows; otherwise
+// (bf16) without the W^T copy, then without any copy, whichever allows a
+// larger chunk.  (The in-place operands run the contractions slower; below
+// about 1000 rows per chunk the fp32 read-modify-write of dW per chunk costs
+// more than that at the large shapes.)  flags force the layout.
+int64_t pick_chunk(const specloss_problem* p, const KindSet& k, size_t ws_bytes, Region region,
+                   int32_t* layout = nullptr) {
   const int64_t top = round_up(p->n_rows, kChunkQuantum);
-  if (p->flags == 0 && p->in_dtype == SPECLOSS_BF16 && nc < (top < 1024 ? top : 1024)) {
-    const int64_t without = largest_chunk(p, k, ws_bytes, region, false);
-    if (without > nc) {
-      *copies = false;
-      return without;
+  const int32_t forced = forced_layout(p);
+  if (forced >= 0) {
+    if (layout) *layout = forced;
+    return largest_chunk(p, k, ws_bytes, region, forced, top);
+  }
+  int64_t best = largest_chunk(p, k, ws_bytes, region, LAYOUT_COPIES, top);
+  if (layout) *layout = LAYOUT_COPIES;
+  if (!layout || p->in_dtype != SPECLOSS_BF16) return best;
+  const int64_t want = top < 1024 ? top : 1024;
+  for (int32_t lay : {LAYOUT_DW_COPIES, LAYOUT_NONE}) {
+    if (best >= want) break;
+    const int64_t nc = largest_chunk(p, k, ws_bytes, region, lay, top);
+    if (nc > best) {
+      best = nc;
+      *layout = lay;
     }
   }
-  return nc;
+  return best;
+}
+
+// The default chunk (workspace size for max_chunk_rows <= 0).  Blog, "Backward
+// pass" and "Choosing the chunk size": the loss path holds about
+// chunk x vocab x dtype x 2 bytes of logits-sized data and never the whole
+// [tokens, vocab] logits.  So the default streams the token set in at least
+// four balanced chunks of at most kDefaultChunk rows, with the whole workspace
+// (staged chunk buffers, transposed copies, partials) strictly below
+// N x V x (input dtype size) bytes, the size of the full logits; layouts are
+// tried in the order of pick_chunk.  Problems too small for any chunk to fit
+// below that size (the W^T copy alone exceeds it) take 256-row chunks.
+int64_t default_chunk(const specloss_problem* p, const KindSet& k, int32_t* layout) {
+  const int64_t N = p->n_rows;
+  const int64_t top = round_up(N, kChunkQuantum);
+  int64_t cap = round_up(cdiv(N, 4), kChunkQuantum);
+  if (cap > kDefaultChunk) cap = kDefaultChunk;
+  const size_t limit = (size_t)N * (size_t)p->vocab * elem_size(p);
+  const int64_t want = top < 1024 ? top : 1024;
+  const int32_t forced = forced_layout(p);
+  int32_t lays[3] = {LAYOUT_COPIES, LAYOUT_DW_COPIES, LAYOUT_NONE};
+  int n_lays = p->in_dtype == SPECLOSS_BF16 ? 3 : 1;
+  if (forced >= 0) {
+    lays[0] = forced;
+    n_lays = 1;
+  }
+  for (int i = 0; i < n_lays; ++i) {
+    int64_t nc = largest_chunk(p, k, limit, REGION_FWD, lays[i], cap, true);
+    const int64_t nb = largest_chunk(p, k, limit, REGION_BWD, lays[i], cap, true);
+    const int64_t nf = largest_chunk(p, k, limit, REGION_FUSED, lays[i], cap, true);
+    nc = nb < nc ? nb : nc;
+    nc = nf < nc ? nf : nc;
+    if (nc <= 0 || (nc < want && i + 1 < n_lays)) continue;
+    // balance: the fewest chunks of that size, then equal chunks
+    const int64_t nch = cdiv(N, nc);
+    *layout = lays[i];
+    return round_up(cdiv(N, nch), kChunkQuantum);
+  }
+  *layout = n_lays == 1 ? lays[0] : LAYOUT_COPIES;
+  return kChunkQuantum;
 }
 
 SavedView saved_view(void* base, int64_t n) {
@@ -603,7 +671,7 @@ int launch_seed_for(const specloss_problem* p, const SavedView& sv, const float*
 }
 
 // dh rows [r0, r0 + rows) = dz W for one chunk from the staged dz [Nc][Vp]
-// and the copy W^T [H][Vp]; without copies (bf16), W is read as it is (an
+// and the copy W^T [H][Vp]; without that copy (bf16), W is read as it is (an
 // MN-major operand).
 int contract_dh(const specloss_problem* p, const Layout& L, int64_t Nc, const void* dz,
                 const void* wt, int64_t r0, int64_t rows, void* dhidden, int32_t dh_dtype,
@@ -613,7 +681,7 @@ int contract_dh(const specloss_problem* p, const Layout& L, int64_t Nc, const vo
   const size_t dh_es = dh_dtype == SPECLOSS_BF16 ? 2 : 4;
   GemmLaunch g{};
   g.A = op(dz, Vp, Nc);
-  g.lean = !L.copies;
+  g.lean = !L.wt_copy;
   if (g.lean) {
     g.B = op(p->W, H, H);  // element (h, v) at W[v * H + h]
     g.B.k_valid = (int32_t)V;
@@ -646,7 +714,7 @@ int contract_dW(const specloss_problem* p, const Layout& L, int64_t Nc, const vo
   const int64_t H = L.H, V = L.V, Vp = L.Vp;
   GemmLaunch g{};
   g.k_len = (int32_t)round_up(rows, 64);
-  g.lean = !L.copies;
+  g.lean = !L.dw_copies;
   if (g.lean) {
     g.A = op(dz, Vp, Vp);  // element (v, c) at dz[c * Vp + v]; rows >= `rows` hold 0
     g.A.k_valid = (int32_t)Nc;
@@ -712,31 +780,30 @@ int bwd_recompute(const specloss_problem* p, const KindSet& k, const float* grad
                   const float* grad_mean, const int64_t* counts, const void* saved,
                   void* workspace, size_t ws_bytes, void* dhidden, int32_t dh_dtype, float* dW,
                   int accumulate_dW, int64_t vocab_offset, hipStream_t stream) {
-  bool with_copies = true;
-  const int64_t Nc = pick_chunk(p, k, ws_bytes, REGION_BWD, &with_copies);
+  int32_t layout = LAYOUT_COPIES;
+  const int64_t Nc = pick_chunk(p, k, ws_bytes, REGION_BWD, &layout);
   if (Nc <= 0) return SPECLOSS_E_WORKSPACE;
-  const Layout L = plan(p, k, Nc, with_copies);
+  const Layout L = plan(p, k, Nc, layout);
   char* ws = static_cast<char*>(workspace);
   const bool bf16 = p->in_dtype == SPECLOSS_BF16;
   const int64_t N = L.N, H = L.H, V = L.V, Vp = L.Vp;
   const SavedView sv = saved_view(const_cast<void*>(saved), N);
   float* seed = reinterpret_cast<float*>(ws + L.seed);
-  const bool copies = L.copies;
-  void* wt = copies ? ws + L.wt : nullptr;
-  void* ht = copies ? ws + L.ht : nullptr;
+  void* wt = L.wt_copy ? ws + L.wt : nullptr;
+  void* ht = L.dw_copies ? ws + L.ht : nullptr;
   void* dz = ws + L.dz;
-  void* dzt = copies ? ws + L.dzt : nullptr;
+  void* dzt = L.dw_copies ? ws + L.dzt : nullptr;
   Tracer tr{p->trace, stream};
 
   TRY(launch_seed_for(p, sv, grad_loss, grad_mean, counts, seed, tr, stream));
-  if (dhidden && copies)
+  if (dhidden && L.wt_copy)
     TRACED(tr, K_TRANSPOSE_W, 2.0 * Vp * H * L.es, launch_transpose(bf16, p->W, V, H, wt, Vp, stream));
 
   int chunk = 0;
   for (int64_t r0 = 0; r0 < N; r0 += Nc, ++chunk) {
     const int64_t rows = (N - r0) < Nc ? (N - r0) : Nc;
     const void* hc = offset_rows(p->hidden_states, r0, H, L.es);
-    if (dW && copies)
+    if (dW && L.dw_copies)
       TRACED(tr, K_TRANSPOSE_H, 2.0 * Nc * H * L.es, launch_transpose(bf16, hc, rows, H, ht, Nc, stream));
 
     DzLaunch dl{};
@@ -821,13 +888,38 @@ int lmhead_loss_workspace_size(const specloss_problem* p, int64_t max_chunk_rows
   const int rc = check_problem(p, &k);
   if (rc) return rc;
   if (!bytes) return SPECLOSS_E_INVAL;
-  int64_t nc = max_chunk_rows <= 0 ? kDefaultChunk : max_chunk_rows;
-  nc = round_up(nc, kChunkQuantum);
-  nc = nc < round_up(p->n_rows, kChunkQuantum) ? nc : round_up(p->n_rows, kChunkQuantum);
-  const Layout L = plan(p, k, nc);
-  size_t b = L.fwd_end > L.bwd_end ? L.fwd_end : L.bwd_end;
-  if (L.fused_end > b) b = L.fused_end;
-  *bytes = b;
+  int32_t layout = LAYOUT_COPIES;
+  int64_t nc;
+  if (max_chunk_rows <= 0) {
+    nc = default_chunk(p, k, &layout);
+  } else {
+    const int32_t forced = forced_layout(p);
+    layout = forced >= 0 ? forced : LAYOUT_COPIES;
+    nc = round_up(max_chunk_rows, kChunkQuantum);
+    nc = nc < round_up(p->n_rows, kChunkQuantum) ? nc : round_up(p->n_rows, kChunkQuantum);
+  }
+  *bytes = workspace_end(plan(p, k, nc, layout));
+  return SPECLOSS_OK;
+}
+
+int lmhead_loss_chunk(const specloss_problem* p, size_t ws_bytes, int32_t call,
+                      int64_t* chunk_rows, int32_t* layout) {
+  KindSet k;
+  TRY(check_problem(p, &k));
+  if (!chunk_rows || !layout || call < 0 || call > 2) return SPECLOSS_E_INVAL;
+  int32_t lay = LAYOUT_COPIES;
+  int64_t nc;
+  if (call == 0) {
+    nc = pick_chunk(p, k, ws_bytes, REGION_FWD);
+  } else if (call == 1 || (k.dual_bwd && !k.stage_div)) {
+    // the single call with rkl / jsd runs the backward of the two calls
+    nc = pick_chunk(p, k, ws_bytes, REGION_BWD, &lay);
+  } else {
+    nc = pick_chunk(p, k, ws_bytes, REGION_FUSED, &lay);
+  }
+  if (nc <= 0) return SPECLOSS_E_WORKSPACE;
+  *chunk_rows = nc;
+  *layout = plan(p, k, nc, lay).layout;
   return SPECLOSS_OK;
 }
 
@@ -886,7 +978,12 @@ int lmhead_loss_fwd_bwd(const specloss_problem* p, void* workspace, size_t ws_by
   if (!workspace || !aligned(workspace, kAlign)) return SPECLOSS_E_WORKSPACE;
   if (k.dual_bwd && !k.stage_div) {
     // rkl / jsd gradients need log p and log m per element: the forward and
-    // backward sequences run back to back on the same workspace
+    // backward sequences run back to back on the same workspace.  Both must
+    // fit before anything is enqueued.
+    int32_t bwd_layout = LAYOUT_COPIES;
+    if (pick_chunk(p, k, ws_bytes, REGION_FWD) <= 0 ||
+        pick_chunk(p, k, ws_bytes, REGION_BWD, &bwd_layout) <= 0)
+      return SPECLOSS_E_WORKSPACE;
     char* ws = static_cast<char*>(workspace);
     const Layout L0 = plan(p, k, kChunkQuantum);
     void* sv_base = saved ? saved : ws + L0.saved;
@@ -898,10 +995,10 @@ int lmhead_loss_fwd_bwd(const specloss_problem* p, void* workspace, size_t ws_by
   // label / argmax cross-entropies: pass 1 stages e = exp(z - m_tile) per
   // chunk; with kl_div / tv / nla / lk_hybrid, pass 2 stages q and q - p.  The
   // logit gradient is formed from the staged values without recomputing logits.
-  bool with_copies = true;
-  const int64_t Nc = pick_chunk(p, k, ws_bytes, REGION_FUSED, &with_copies);
+  int32_t layout = LAYOUT_COPIES;
+  const int64_t Nc = pick_chunk(p, k, ws_bytes, REGION_FUSED, &layout);
   if (Nc <= 0) return SPECLOSS_E_WORKSPACE;
-  const Layout L = plan(p, k, Nc, with_copies);
+  const Layout L = plan(p, k, Nc, layout);
   char* ws = static_cast<char*>(workspace);
   const bool bf16 = p->in_dtype == SPECLOSS_BF16;
   const int64_t N = L.N, H = L.H, V = L.V, Vp = L.Vp;
@@ -911,18 +1008,17 @@ int lmhead_loss_fwd_bwd(const specloss_problem* p, void* workspace, size_t ws_by
   const FwdBufs b{reinterpret_cast<float*>(ws + L.f_pz), reinterpret_cast<float*>(ws + L.f_pu),
                   k.stage_div ? reinterpret_cast<float*>(ws + L.f_p2) : nullptr,
                   reinterpret_cast<float*>(ws + L.f_zy), Nc, ws + L.tstat};
-  const bool copies = L.copies;
-  void* wt = copies ? ws + L.f_wt : nullptr;
-  void* ht = copies ? ws + L.f_ht : nullptr;
+  void* wt = L.wt_copy ? ws + L.f_wt : nullptr;
+  void* ht = L.dw_copies ? ws + L.f_ht : nullptr;
   void* dz = ws + L.f_dz;
   void* dd = k.stage_div ? ws + L.f_dd : nullptr;
-  void* dzt = copies ? ws + L.f_dzt : nullptr;
+  void* dzt = L.dw_copies ? ws + L.f_dzt : nullptr;
   Tracer tr{p->trace, stream};
 
   TRY(launch_validity_for(p, k, sv, counts, tr, stream));
   TRY(launch_seed_for(p, sv, grad_loss, grad_mean, counts, seed, tr, stream));
   if (L.shared_target) TRY(target_prepass(p, L, b, tr, stream));
-  if (dhidden && copies)
+  if (dhidden && L.wt_copy)
     TRACED(tr, K_TRANSPOSE_W, 2.0 * Vp * H * L.es, launch_transpose(bf16, p->W, V, H, wt, Vp, stream));
   int chunk = 0;
   for (int64_t r0 = 0; r0 < N; r0 += Nc, ++chunk) {
@@ -953,7 +1049,7 @@ int lmhead_loss_fwd_bwd(const specloss_problem* p, void* workspace, size_t ws_by
            (double)ds.row_blocks * 64 * Vp * L.es * ((dd ? 3 : 2) + (dzt ? 1 : 0)),
            launch_dz_stage(bf16, ds, stream));
     const void* hc = offset_rows(p->hidden_states, r0, H, L.es);
-    if (dW && copies)
+    if (dW && L.dw_copies)
       TRACED(tr, K_TRANSPOSE_H, 2.0 * Nc * H * L.es, launch_transpose(bf16, hc, rows, H, ht, Nc, stream));
     if (dhidden) TRY(contract_dh(p, L, Nc, dz, wt, r0, rows, dhidden, dh_dtype, tr, stream));
     if (dW)

@@ -24,6 +24,7 @@ def streaming_bound_bytes(chunk: int, vocab: int, dtype_bytes: int = 4) -> int:
     return chunk * vocab * dtype_bytes * 2
 
 
-def logits_sized_limit_bytes(tokens: int, vocab: int) -> int:
-    """No single buffer of the HIP path may reach a bf16 [tokens, vocab] tensor."""
-    return tokens * vocab * 2
+def logits_sized_limit_bytes(tokens: int, vocab: int, dtype_bytes: int = 2) -> int:
+    """Size of the [tokens, vocab] logits in the input dtype (bf16 by default): the
+    default workspace of the HIP path stays below it."""
+    return tokens * vocab * dtype_bytes

@@ -73,6 +73,14 @@ class LossRun:
                               dhidden, dW, accumulate_dW, stream)
         return dhidden, dW
 
+    @property
+    def workspace_bytes(self) -> int:
+        return self.workspace.numel()
+
+    def chunk(self, call: int = B.CALL_FWD_BWD):
+        """(rows per chunk, backward layout) the given call uses with this workspace."""
+        return B.lmhead_loss_chunk(self.problem, self.workspace_bytes, call)
+
     def saved_field(self, i: int, dtype=torch.float32) -> torch.Tensor:
         """View of saved field i (SPECLOSS_SAVED_* / SavedView order) as an N-vector."""
         o = B.specloss_saved_offset(self.n_rows, i)

@@ -86,6 +86,80 @@ def check_argmax(gpu_y: np.ndarray, prob, rows, valid) -> None:
     assert np.array_equal(gpu_y[decisive], ref[decisive])
 
 
+def ce_tie_candidates(prob, rows, valid, Wt64=None):
+    """Rows whose ce label is not unique at the pages' precision.
+
+    For each valid row of `rows` whose two largest target logits (oracle, fp64)
+    differ by less than ARGMAX_GAP, the labels within ARGMAX_GAP of the maximum:
+    any of them is a correct hard label there.  Returns {position in rows:
+    (the oracle's label, set of candidates)}.
+    """
+    if "ce" not in prob.weights:
+        return {}
+    Wt = Wt64 if Wt64 is not None else O.widen(prob.W_t, prob.dtype)
+    tr = rows if prob.target_row is None else np.asarray(prob.target_row)[rows]
+    g = O.widen(prob.target_hidden[np.where(valid, tr, 0)], prob.dtype)
+    u = g @ Wt.T
+    out = {}
+    for i in np.where(valid)[0]:
+        top = np.max(u[i])
+        cand = set(np.where(u[i] >= top - ARGMAX_GAP)[0].tolist())
+        if len(cand) > 1:
+            out[int(i)] = (int(O.argmax_lowest(u[i:i + 1])[0]), cand)
+    return out
+
+
+def retarget_ties(prob, rows, ref, ties, gpu_y, W64=None):
+    """Oracle values with the hard label of each near-tie row set to the GPU's
+    choice, after checking that the choice is one of the tied candidates.
+
+    The expected values stay the oracle's: for a row whose ce label moves from
+    y to c, the ce term becomes lse_q - z_c (the oracle's ce of that row with
+    label c), the weighted loss moves by w_ce times the difference, and the
+    row's logit gradient by seed * w_ce * (e_y - e_c).  Returns the adjusted
+    (loss, ce term) arrays and a list of (position, y, c) for the gradients.
+    """
+    loss, term = ref.loss.copy(), ref.terms["ce"].copy()
+    moved = []
+    if not ties:
+        return loss, term, moved
+    W = W64 if W64 is not None else O.widen(prob.W, prob.dtype)
+    w = float(prob.weights["ce"])
+    for i, (y, cand) in ties.items():
+        c = int(gpu_y[i])
+        assert c in cand, f"row {rows[i]}: label {c} is not among the tied labels {sorted(cand)}"
+        if c == y:
+            continue
+        z = O.widen(prob.hidden[rows[i]:rows[i] + 1], prob.dtype) @ W.T
+        alt, _ = O.ce_from_logits(z, np.array([c]))
+        loss[i] += w * (alt[0] - term[i])
+        term[i] = alt[0]
+        moved.append((i, y, c))
+    return loss, term, moved
+
+
+def apply_moved_labels(prob, rows, moved, seed, rdh=None, rdW=None, dW_rows=None, W64=None):
+    """Shift oracle gradients for the rows whose ce label moved (see retarget_ties):
+    dh_r += seed_r w_ce (W[y] - W[c]); dW[y] += seed_r w_ce h_r, dW[c] -= seed_r w_ce h_r."""
+    if not moved:
+        return rdh, rdW
+    W = W64 if W64 is not None else O.widen(prob.W, prob.dtype)
+    w = float(prob.weights["ce"])
+    vpos = None if dW_rows is None else {int(v): j for j, v in enumerate(dW_rows)}
+    for i, y, c in moved:
+        r = rows[i]
+        s = float(seed[r]) * w
+        if rdh is not None:
+            rdh[i] += s * (W[y] - W[c])
+        if rdW is not None:
+            h = O.widen(prob.hidden[r:r + 1], prob.dtype)[0]
+            for v, sign in ((y, 1.0), (c, -1.0)):
+                j = v if vpos is None else vpos.get(v)
+                if j is not None:
+                    rdW[j] += sign * s * h
+    return rdh, rdW
+
+
 def full_parity(prob, *, max_chunk_rows=0, check_grads=True, tag="", single_call=False,
                 shards=None, workspace_bytes=None, expect_copies=None, flags=None):
     """Run fwd (+bwd with the mean seed) on the GPU and compare every output with the oracle.
@@ -93,8 +167,9 @@ def full_parity(prob, *, max_chunk_rows=0, check_grads=True, tag="", single_call
     single_call: use lmhead_loss_fwd_bwd instead of the two calls.
     shards: (G, bounds or None) to run the vocabulary-parallel sequence instead.
     workspace_bytes: workspace to give the calls (default: the library's size).
-    expect_copies: if not None, whether the backward must make transposed
-    copies (read from the kernel trace).
+    expect_copies: if not None, the backward layout the trace must show: True
+    or "copies" (W^T and h^T copies), "no_weight_copy" (h^T only), False or
+    "no_copies" (no transpose).
     flags: backward layout flags; by default the transposed copies are forced
     (FLAG_COPIES) so chunked cases exercise that path, except when
     workspace_bytes is given (then the library chooses).
@@ -129,6 +204,16 @@ def full_parity(prob, *, max_chunk_rows=0, check_grads=True, tag="", single_call
     counts = run.counts.cpu().numpy()
     assert counts[0] == ref.n_valid and counts[1] == ref.n_bad
     loss = run.loss.cpu().numpy()
+    all_rows = np.arange(prob.n_rows)
+    ties = ce_tie_candidates(prob, all_rows, ref.valid)
+    moved = []
+    if ties:
+        gpu_y = run.saved_field(3, torch.int32).cpu().numpy()
+        ref_loss, ref_ce, moved = retarget_ties(prob, all_rows, ref, ties, gpu_y)
+        ref.loss, ref.terms["ce"] = ref_loss, ref_ce
+        mean = float(np.sum(ref.loss) / max(ref.n_valid, 1))
+        term_means["ce"] = float(np.sum(ref.terms["ce"]) / max(ref.n_valid, 1))
+        say(f"   {len(ties)} near-tie ce rows, {len(moved)} with the other label")
     check_tokens(loss, ref.loss, "per-token loss")
     assert np.all(loss[~ref.valid] == 0.0), "masked rows must contribute exactly 0"
     red = run.reduced.cpu().numpy()
@@ -156,6 +241,7 @@ def full_parity(prob, *, max_chunk_rows=0, check_grads=True, tag="", single_call
             dh, dW = run.backward(grad_mean=gm)
         torch.cuda.synchronize()
         rdh, rdW = O.backward(prob)
+        rdh, rdW = apply_moved_labels(prob, all_rows, moved, O.mean_seed(prob), rdh, rdW)
         dh_np, dW_np = dh.cpu().numpy(), dW.cpu().numpy()
         e_dh, e_dW = rel_frob(dh_np, rdh), rel_frob(dW_np, rdW)
         say(f"   rel frob dh {e_dh:.3e} dW {e_dW:.3e}")
@@ -166,5 +252,9 @@ def full_parity(prob, *, max_chunk_rows=0, check_grads=True, tag="", single_call
         names = {name for name, _, _ in trace.read()}
         run.problem.trace = None
         trace.close()
-        assert ("gemm_dh" in names) and (("transpose_W" in names) == expect_copies), names
+        lay = {True: "copies", False: "no_copies"}.get(expect_copies, expect_copies)
+        want_wt, want_ht = {"copies": (True, True), "no_weight_copy": (False, True),
+                            "no_copies": (False, False)}[lay]
+        assert "gemm_dh" in names, names
+        assert ("transpose_W" in names) == want_wt and ("transpose_h" in names) == want_ht, names
     return out

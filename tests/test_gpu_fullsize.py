@@ -1,9 +1,12 @@
-"""Parity at each workload's full size, in the launch configuration bench.py times.
+"""Parity at each workload's full size, in the launch configuration bench.py times
+(the library's default workspace: its streaming chunk policy and layout).
 
 The oracle cannot materialise every row's logits at these sizes, so:
+  * the default workspace stays below the size of the [N, V] bf16 logits
+    (blog, "Backward pass": the streaming loss never holds the full logits);
   * forward: per-row outputs of a seeded sample of rows (plus the first, the
-    last and the rows around each 8192-row chunk boundary) are compared with
-    the oracle one by one; counts are compared over all rows;
+    last and the rows around each chunk boundary of the calls) are compared
+    with the oracle one by one; counts are compared over all rows;
   * backward with the mean seed (the benchmark's call): dh of the sampled rows
     against the oracle, and the invariant sum_v dW[v, :] = 0 over the whole
     matrix (every loss here is a function of softmax(z), whose gradient sums
@@ -19,12 +22,14 @@ import torch
 
 import synthetic
 from oracle import specloss_oracle as O
-from tests._gpu_helpers import (ARGMAX_GAP, GRAD_FROB, check_flatness, check_tokens, make_run,
-                                rel_frob, say, to_device)
+import lm_head_vocab_amd as L
+from lm_head_vocab_amd.memory import logits_sized_limit_bytes
+from tests._gpu_helpers import (ARGMAX_GAP, GRAD_FROB, apply_moved_labels, ce_tie_candidates,
+                                check_flatness, check_tokens, make_run, rel_frob,
+                                retarget_ties, say, to_device)
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
-CHUNK = 8192  # bench.py's --chunk default
 N_SAMPLE = 24
 
 
@@ -37,12 +42,13 @@ def _gpu():
     yield
 
 
-def _sample_rows(n, seed):
+def _sample_rows(n, seed, chunks):
     rng = np.random.default_rng(seed)
     rows = set(rng.choice(n, size=min(N_SAMPLE, n), replace=False).tolist())
     rows |= {0, n - 1}
-    for b in range(CHUNK, n, CHUNK):
-        rows |= {b - 1, b}
+    for c in chunks:
+        for b in range(c, n, c):
+            rows |= {b - 1, b}
     return np.array(sorted(rows), dtype=np.int64)
 
 
@@ -58,7 +64,13 @@ def test_full_size_sampled(name, single):
     N, H, V = prob.n_rows, prob.hidden_dim, prob.vocab
     say(f"[fullsize] {name} N={N} H={H} V={V} weights={prob.weights} single={single}")
     dev = to_device(prob)
-    run = make_run(prob, dev, max_chunk_rows=CHUNK)
+    run = make_run(prob, dev, flags=None)  # the default workspace, as bench.py
+    limit = logits_sized_limit_bytes(N, V)
+    assert run.workspace_bytes < limit, (run.workspace_bytes / 2**30, limit / 2**30)
+    chunks = {run.chunk(c)[0] for c in (L.binding.CALL_FWD, L.binding.CALL_BWD,
+                                        L.binding.CALL_FWD_BWD)}
+    say(f"   workspace {run.workspace_bytes / 2**30:.2f} GiB (logits {limit / 2**30:.2f} GiB), "
+        f"chunks {sorted(chunks)}, single-call layout {run.chunk()[1]}")
     if single:
         dh, dW = run.forward_backward(grad_mean=torch.ones(1, device="cuda"))
     else:
@@ -69,16 +81,21 @@ def test_full_size_sampled(name, single):
     counts = run.counts.cpu().numpy()
     assert counts[0] == int(valid.sum()) and counts[1] == int(bad.sum())
 
-    rows = _sample_rows(N, prob.seed)
+    rows = _sample_rows(N, prob.seed, chunks)
     w64 = O._weights64(op)
     say(f"   oracle forward on {len(rows)} rows")
     ref = O.forward(op, rows=rows, weights64=w64)
+    ties = ce_tie_candidates(prob, rows, ref.valid, None if w64[1] is None else w64[1])
+    moved = []
+    if ties:
+        gpu_y = run.saved_field(3, torch.int32).cpu().numpy()[rows]
+        ref.loss, ref.terms["ce"], moved = retarget_ties(prob, rows, ref, ties, gpu_y, w64[0])
+        say(f"   {len(ties)} near-tie ce rows, {len(moved)} with the other label")
     loss = run.loss.cpu().numpy()[rows]
     check_tokens(loss, ref.loss, "sampled loss")
     assert np.all(loss[~ref.valid] == 0)
     lse = run.lse_q.cpu().numpy()[rows]
     assert np.allclose(lse[ref.valid], ref.lse_q[ref.valid], rtol=1e-5, atol=1e-4)
-    import lm_head_vocab_amd as L
     for k in prob.weights:
         got = run.term[L.KINDS.index(k)].cpu().numpy()[rows]
         check_tokens(got, ref.terms[k], f"term {k}")
@@ -103,6 +120,7 @@ def test_full_size_sampled(name, single):
     torch.cuda.synchronize()
     seed_mean = O.mean_seed(op)
     rdh, _ = O.backward(op, seed=seed_mean, rows=rows, want_dW=False, weights64=w64)
+    rdh, _ = apply_moved_labels(prob, rows, moved, seed_mean, rdh, None, W64=w64[0])
     dh_s = dh[torch.from_numpy(rows).cuda()].cpu().numpy()
     e = rel_frob(dh_s, rdh)
     say(f"   mean seed: sampled dh rel frob {e:.3e}")
@@ -130,6 +148,7 @@ def test_full_size_sampled(name, single):
         vsel |= {int(x) for x in run.saved_field(3, torch.int32).cpu().numpy()[rows] if x >= 0}
     vsel = np.array(sorted(vsel), dtype=np.int64)
     rdh, rdW = O.backward(op, seed=seed, rows=rows, dW_rows=vsel, weights64=w64)
+    rdh, rdW = apply_moved_labels(prob, rows, moved, seed, rdh, rdW, dW_rows=vsel, W64=w64[0])
     e_dh = rel_frob(dh[torch.from_numpy(rows).cuda()].cpu().numpy(), rdh)
     e_dW = rel_frob(dW[torch.from_numpy(vsel).cuda()].cpu().numpy(), rdW)
     say(f"   sampled seed: dh rel frob {e_dh:.3e}, dW[{len(vsel)} rows] rel frob {e_dW:.3e}")

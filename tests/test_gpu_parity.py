@@ -482,9 +482,12 @@ def test_backward_without_transposed_copies(case):
     del probe
     full_parity(p, max_chunk_rows=256, tag=f"lean-{case}", single_call=single,
                 workspace_bytes=full - copies, expect_copies=False)
-    # and the default workspace (chunk = all rows here) makes the copies
-    full_parity(p, tag=f"copies-{case}", single_call=single, expect_copies=True, flags=0)
-    # forced either way at 256-row chunks
+    # each layout forced: every copy with one chunk of all rows, and at
+    # 256-row chunks the dW copies without W^T, and no copy
+    full_parity(p, tag=f"copies-{case}", single_call=single, expect_copies=True,
+                flags=L.binding.FLAG_COPIES)
+    full_parity(p, max_chunk_rows=256, tag=f"noweightcopy-{case}", single_call=single,
+                expect_copies="no_weight_copy", flags=L.binding.FLAG_NO_WEIGHT_COPY)
     full_parity(p, max_chunk_rows=256, tag=f"nocopies-{case}", single_call=single,
                 expect_copies=False, flags=L.binding.FLAG_NO_COPIES)
 

@@ -97,12 +97,13 @@ def test_validation(lib, mut, code):
 
 def test_flags_field_and_null_problem(lib):
     p = _problem()
-    for bad in (3, 4, -1):
+    for bad in (4, 5, -1):
         p.flags = bad
         assert _fwd(lib, p) == E_INVAL
-    p.flags = B.FLAG_NO_COPIES
     p.in_dtype = B.F32
-    assert _fwd(lib, p) == E_UNSUP  # the copy-free backward is bf16 only
+    for flag in (B.FLAG_NO_COPIES, B.FLAG_NO_WEIGHT_COPY):
+        p.flags = flag
+        assert _fwd(lib, p) == E_UNSUP  # the in-place operands are bf16 only
     out = ctypes.c_size_t()
     assert lib.lmhead_loss_workspace_size(None, 0, ctypes.byref(out)) == E_INVAL
     assert lib.lmhead_loss_fwd(None, 0, 0, 0, None, None, None, 0, None, None) == E_INVAL
@@ -255,3 +256,81 @@ def test_sum_partials_validation(lib):
     assert f(ctypes.c_void_p(0x1000), 18, 2, ctypes.c_void_p(0x2000), B.F32, None) == E_UNSUP
     assert f(ctypes.c_void_p(0x1008), 16, 2, ctypes.c_void_p(0x2000), B.F32, None) == E_UNSUP
     assert f(ctypes.c_void_p(0x1000), 16, 2, ctypes.c_void_p(0x2000), 7, None) == E_UNSUP
+
+
+def _shape(name):
+    """Problem structs of the five workload shapes (host-only: fake aligned pointers)."""
+    if name == "ce_fp32_small":
+        return _problem(N=256, H=256, V=4096, dtype=B.F32)
+    if name == "ce_bf16_1b":
+        return _problem(N=8192, H=2048, V=128256)
+    if name == "ce_bf16_8b":
+        return _problem(N=32768, H=4096, V=128256)
+    if name == "lk_hybrid_bf16_8b":
+        return _problem(N=16384, H=4096, V=128256, weights={"lk_hybrid": 1.0}, target=16384)
+    p = _problem(N=3 * 4096, H=16384, V=128256, weights={"ce": 0.1, "tv": 0.9}, target=4096)
+    p.target_row = 0x60000
+    return p
+
+
+def _chunk(lib, p, ws, call):
+    rows, lay = ctypes.c_int64(), ctypes.c_int32()
+    rc = lib.lmhead_loss_chunk(ctypes.byref(p), ws, call, ctypes.byref(rows), ctypes.byref(lay))
+    return rc, rows.value, B.LAYOUTS[lay.value]
+
+
+@pytest.mark.parametrize("name,chunk,layout", [
+    ("ce_bf16_1b", 2048, "copies"),
+    ("ce_bf16_8b", 8192, "copies"),
+    ("lk_hybrid_bf16_8b", 3328, "copies"),
+    ("multihead_bf16_405b", 3072, "no_weight_copy"),
+])
+def test_default_chunk_streams_below_the_logits_size(lib, name, chunk, layout):
+    """Blog, "Backward pass" / "Choosing the chunk size": the default workspace
+    streams the token set in chunks well below the token count, and the whole
+    workspace stays below the size of the [N, V] logits in the input dtype."""
+    p = _shape(name)
+    rc, ws = _ws(lib, p)
+    assert rc == 0
+    limit = M.logits_sized_limit_bytes(p.n_rows, p.vocab)
+    assert ws < limit, (ws / 2**30, limit / 2**30)
+    assert _chunk(lib, p, ws, B.CALL_FWD_BWD) == (0, chunk, layout)
+    assert chunk <= -(-p.n_rows // 4 // 256) * 256
+    rc, rows_bwd, _ = _chunk(lib, p, ws, B.CALL_BWD)
+    assert rc == 0 and 0 < rows_bwd < p.n_rows
+
+
+def test_default_chunk_of_a_tiny_problem(lib):
+    """When even 256-row chunks do not fit below the logits size (the W^T copy
+    alone exceeds it), the smallest chunk with every copy is used."""
+    p = _shape("ce_fp32_small")
+    rc, ws = _ws(lib, p)
+    assert rc == 0 and ws > M.logits_sized_limit_bytes(256, 4096, 4)
+    assert _chunk(lib, p, ws, B.CALL_FWD_BWD) == (0, 256, "copies")
+
+
+def test_chunk_query_validation(lib):
+    p = _shape("ce_bf16_8b")
+    rows, lay = ctypes.c_int64(), ctypes.c_int32()
+    assert lib.lmhead_loss_chunk(ctypes.byref(p), 1 << 40, 3, ctypes.byref(rows),
+                                 ctypes.byref(lay)) == E_INVAL
+    assert lib.lmhead_loss_chunk(ctypes.byref(p), 1 << 40, 0, None, ctypes.byref(lay)) == E_INVAL
+    assert _chunk(lib, p, 1000, B.CALL_BWD)[0] == E_WS
+    # flags force the layout
+    p.flags = B.FLAG_NO_COPIES
+    rc, ws = _ws(lib, p)
+    assert rc == 0 and _chunk(lib, p, ws, B.CALL_FWD_BWD)[2] == "no_copies"
+
+
+@pytest.mark.parametrize("kind", ["rkl", "jsd"])
+def test_fwd_bwd_rejects_a_forward_only_workspace(lib, kind):
+    """rkl / jsd run the forward and backward sequences back to back: a workspace
+    that holds the forward region but not the backward one is rejected before
+    anything is enqueued (no launch happens here: there is no GPU)."""
+    p = _problem(N=4096, H=4096, V=128256, weights={kind: 1.0}, target=4096)
+    ws = 32 << 20
+    assert _chunk(lib, p, ws, B.CALL_FWD)[0] == 0
+    assert _chunk(lib, p, ws, B.CALL_BWD)[0] == E_WS
+    rc = lib.lmhead_loss_fwd_bwd(ctypes.byref(p), 0x100000, ws, 0x200000, None, None, None,
+                                 0x300000, None, None, 0x1000, 0x4000, B.F32, 0x5000, 0, None)
+    assert rc == E_WS
