@@ -221,6 +221,27 @@ int lmhead_loss_fwd(const specloss_problem* p, void* workspace, size_t ws_bytes,
                     hipStream_t stream);
 
 /*
+ * lmhead_loss_fwd without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight evaluation or
+ * serving loops, harnesses that forbid allocation).  The call uses a
+ * file-scope device array of SPECLOSS_NOALLOC_SCRATCH_BYTES bytes that the
+ * library holds on each device it runs on until the process ends (its
+ * address is looked up on the first call on a device); it calls no
+ * hipMalloc or hipFree.  Outputs, their ownership and errors as for
+ * lmhead_loss_fwd; SPECLOSS_E_WORKSPACE when the forward does not fit the
+ * array even at its smallest chunk (roughly N * 90 bytes of per-row state,
+ * less when term_loss and saved are given, plus 2 to 12 KiB of per-tile
+ * partials per chunk row).  Every call on one device shares that device's
+ * array: calls that overlap in time on one device race and must not be
+ * made.  Nothing in the array needs clearing between calls (each call
+ * writes every value it reads).
+ */
+#define SPECLOSS_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int lmhead_loss_fwd_noalloc(const specloss_problem* p, float* loss, float* term_loss,
+                            float* lse_q, void* saved, int64_t* counts, float* reduced,
+                            hipStream_t stream);
+
+/*
  * Backward (blog, "Backward pass": per chunk, the logits gradient, the
  * hidden-state gradient of the chunk, and the LM-head gradient accumulated
  * over chunks; the chunk's logits tiles are recomputed here from the saved

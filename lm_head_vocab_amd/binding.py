@@ -60,6 +60,7 @@ EXPORTS = (
     "specloss_saved_bytes",
     "specloss_saved_offset",
     "lmhead_loss_fwd",
+    "lmhead_loss_fwd_noalloc",
     "lmhead_loss_bwd",
     "lmhead_loss_fwd_bwd",
     "specloss_align_heads",
@@ -112,6 +113,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.specloss_saved_offset.argtypes = [i64, i32, ctypes.POINTER(sz)]
     lib.specloss_saved_offset.restype = ctypes.c_int
     lib.lmhead_loss_fwd.argtypes = [P, vp, sz, vp, vp, vp, vp, vp, vp, vp]
+    lib.lmhead_loss_fwd_noalloc.argtypes = [P, vp, vp, vp, vp, vp, vp, vp]
+    lib.lmhead_loss_fwd_noalloc.restype = ctypes.c_int
     lib.lmhead_loss_fwd.restype = ctypes.c_int
     lib.lmhead_loss_bwd.argtypes = [P, vp, vp, vp, vp, vp, sz, vp, i32, vp, ctypes.c_int, vp]
     lib.lmhead_loss_bwd.restype = ctypes.c_int
@@ -259,6 +262,16 @@ def lmhead_loss_fwd(problem: Problem, workspace: torch.Tensor, loss: torch.Tenso
         ctypes.byref(problem), _ptr(workspace), workspace.numel() * workspace.element_size(),
         _ptr(loss), _ptr(term_loss), _ptr(lse_q), _ptr(saved), _ptr(counts), _ptr(reduced),
         _stream(stream)), "lmhead_loss_fwd")
+
+
+def lmhead_loss_fwd_noalloc(problem: Problem, loss: torch.Tensor,
+                            term_loss: Optional[torch.Tensor], lse_q: Optional[torch.Tensor],
+                            saved: Optional[torch.Tensor], counts: torch.Tensor,
+                            reduced: Optional[torch.Tensor], stream=None) -> None:
+    """The forward on the library's fixed per-device scratch (no workspace)."""
+    _check(load_library().lmhead_loss_fwd_noalloc(
+        ctypes.byref(problem), _ptr(loss), _ptr(term_loss), _ptr(lse_q), _ptr(saved),
+        _ptr(counts), _ptr(reduced), _stream(stream)), "lmhead_loss_fwd_noalloc")
 
 
 def lmhead_loss_bwd(problem: Problem, grad_loss: Optional[torch.Tensor],

@@ -955,6 +955,20 @@ int lmhead_loss_fwd(const specloss_problem* p, void* workspace, size_t ws_bytes,
   return SPECLOSS_OK;
 }
 
+int lmhead_loss_fwd_noalloc(const specloss_problem* p, float* loss, float* term_loss,
+                            float* lse_q, void* saved, int64_t* counts, float* reduced,
+                            hipStream_t stream) {
+  KindSet k;
+  TRY(check_problem(p, &k));
+  TRY(check_fwd_outputs(loss, term_loss, lse_q, saved, counts, reduced));
+  // the forward region at its smallest chunk must fit the fixed scratch
+  if (pick_chunk(p, k, kNoAllocScratchBytes, REGION_FWD) <= 0) return SPECLOSS_E_WORKSPACE;
+  void* ws = nullptr;
+  HIP_TRY(noalloc_scratch(&ws));
+  return lmhead_loss_fwd(p, ws, kNoAllocScratchBytes, loss, term_loss, lse_q, saved, counts,
+                         reduced, stream);
+}
+
 int lmhead_loss_bwd(const specloss_problem* p, const float* grad_loss, const float* grad_mean,
                     const int64_t* counts, const void* saved, void* workspace, size_t ws_bytes,
                     void* dhidden, int32_t dh_dtype, float* dW, int accumulate_dW,

@@ -25,6 +25,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "launch.hpp"
 #include "tile_gemm.hpp"
 
@@ -1238,6 +1240,35 @@ __global__ __launch_bounds__(256) void k_align(AlignLaunch a) {
   }
   a.target_row[r] = tr;
   a.mask[r] = m;
+}
+
+// ============================================================================
+// scratch of the allocation-free forward
+// ============================================================================
+// One array per device (each device holds its own copy), kept until the
+// process ends.  Host code never uses the array's name as an address: the
+// device address comes from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxScratchDevices = 64;
+
+hipError_t noalloc_scratch(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+  static std::mutex mu;
+  static void* per_device[kMaxScratchDevices] = {};
+  std::lock_guard<std::mutex> lock(mu);
+  if (!per_device[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    per_device[dev] = p;
+  }
+  *ptr = per_device[dev];
+  return hipSuccess;
 }
 
 // ============================================================================

@@ -278,4 +278,13 @@ struct AlignLaunch {
 };
 hipError_t launch_align(const AlignLaunch& a, hipStream_t s);
 
+// ---- the allocation-free forward ----
+// Bytes of the file-scope device scratch array behind lmhead_loss_fwd_noalloc
+// (SPECLOSS_NOALLOC_SCRATCH_BYTES in the public header).
+constexpr size_t kNoAllocScratchBytes = (size_t)64 << 20;
+// Device address of the current device's scratch array: looked up with
+// hipGetSymbolAddress on the first call on each device (that device current)
+// and kept per device.
+hipError_t noalloc_scratch(void** ptr);
+
 }  // namespace specloss
