@@ -261,9 +261,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_stats(StatsLaunch a) {
 // pass 1 with staging: the tile's column maxima are merged across the two
 // half-waves and the two wave rows first, then e = exp(z - m_tile) is both
 // summed and stored (rounded to the storage type) for the backward.
-template <typename T>
-__global__ __launch_bounds__(kThreads, 1) void k_stats_stage(StatsStageLaunch a) {
-  using Cfg = TileCfg<T, 256, 256, kStatsLoadGap>;
+template <typename T, int WNW>
+__global__ __launch_bounds__(128 * WNW, 1) void k_stats_stage(StatsStageLaunch a) {
+  using Cfg = TileCfg<T, 256, 256, kStatsLoadGap, WNW>;
   __shared__ __attribute__((aligned(16))) char smem[Cfg::LDS_BYTES];
   const StatsLaunch& st = a.st;
   int tm, tn;
@@ -275,7 +275,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_stats_stage(StatsStageLaunch a)
                         st.k_len, smem);
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / Cfg::WNW, wn = wave % Cfg::WNW;
   const int v_base = tm * Cfg::BM + wm * Cfg::WM;
   const bool tail = tm * Cfg::BM + Cfg::BM > st.vocab;
   float* red = reinterpret_cast<float*>(smem);  // [2 wave rows][BN]
@@ -754,9 +754,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_dz(DzLaunch a) {
 constexpr int kHalfRows = 128;
 constexpr int kEpiStride = 256 * 4 + 16;  // bytes per staged row
 
-template <typename T, typename OutT, int ROLE, bool LEAN>
-__global__ __launch_bounds__(kThreads, 1) void k_gemm(GemmLaunch a) {
-  using Cfg = TileCfg<T, 256, 256>;
+template <typename T, typename OutT, int ROLE, bool LEAN, int WNW>
+__global__ __launch_bounds__(128 * WNW, 1) void k_gemm(GemmLaunch a) {
+  using Cfg = TileCfg<T, 256, 256, 1, WNW>;
   constexpr bool kA_MN = LEAN && ROLE == 1;
   constexpr bool kB_MN = LEAN;
   constexpr int kSmem = Cfg::LDS_BYTES > kHalfRows * kEpiStride ? Cfg::LDS_BYTES
@@ -769,10 +769,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(GemmLaunch a) {
   tile_mainloop<T, Cfg, kA_MN, kB_MN>(acc, as_op<T>(a.A), tm * Cfg::BM, as_op<T>(a.B),
                                       tn * Cfg::BN, a.k_len, smem);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / Cfg::WNW, wn = wave % Cfg::WNW;
   OutT* C = static_cast<OutT*>(a.C);
-  constexpr int kPieces = kHalfRows * 64;         // 16-byte pieces (4 values) per half
-  constexpr int kPerThread = kPieces / kThreads;  // 32
+  constexpr int kPieces = kHalfRows * 64;              // 16-byte pieces (4 values) per half
+  constexpr int kPerThread = kPieces / Cfg::THREADS;
   constexpr int kBatch = 8;
 #pragma unroll 1
   for (int h = 0; h < 2; ++h) {
@@ -794,7 +794,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(GemmLaunch a) {
       f32x4_t old[kBatch];
 #pragma unroll
       for (int q = 0; q < kBatch; ++q) {
-        const int piece = (b0 + q) * kThreads + threadIdx.x;
+        const int piece = (b0 + q) * Cfg::THREADS + threadIdx.x;
         const int row = piece >> 6, c4 = (piece & 63) * 4;
         const int grow = tm * Cfg::BM + h * kHalfRows + row, gcol = tn * Cfg::BN + c4;
         old[q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -810,7 +810,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(GemmLaunch a) {
       }
 #pragma unroll
       for (int q = 0; q < kBatch; ++q) {
-        const int piece = (b0 + q) * kThreads + threadIdx.x;
+        const int piece = (b0 + q) * Cfg::THREADS + threadIdx.x;
         const int row = piece >> 6, c4 = (piece & 63) * 4;
         const int grow = tm * Cfg::BM + h * kHalfRows + row, gcol = tn * Cfg::BN + c4;
         if (grow >= a.m_valid || gcol >= a.n_valid) continue;
@@ -1288,8 +1288,8 @@ hipError_t launch_stats(bool bf16, bool target, const StatsLaunch& a, hipStream_
 
 hipError_t launch_stats_stage(bool bf16, const StatsStageLaunch& a, hipStream_t s) {
   const dim3 grid(grid_for_tiles(a.st.tiles_m * a.st.tiles_n)), block(kThreads);
-  if (bf16) hipLaunchKernelGGL(k_stats_stage<bf16_bits>, grid, block, 0, s, a);
-  else hipLaunchKernelGGL(k_stats_stage<float>, grid, block, 0, s, a);
+  if (bf16) hipLaunchKernelGGL((k_stats_stage<bf16_bits, 2>), grid, block, 0, s, a);
+  else hipLaunchKernelGGL((k_stats_stage<float, 2>), grid, block, 0, s, a);
   return hipGetLastError();
 }
 
@@ -1330,18 +1330,27 @@ hipError_t launch_dz(bool bf16, bool dual, const DzLaunch& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Waves along N of the plain bf16 contractions with K-major operands: 4 (eight
+// waves, 128 x 64 each, two per SIMD).  Measured against four waves at the 8B
+// shape: gemm_dW 26.3 vs 27.5 ms per step (its fp32 read-modify-write
+// epilogue runs on twice the threads), gemm_dh about 1% faster; the MN-major
+// variants keep four waves (eight spill registers), as does pass 1 (slower
+// with eight: its softmax epilogue spills).
+constexpr int kGemmWNW = 4;
+
 template <int ROLE>
 static void launch_gemm_role(bool bf16, const GemmLaunch& a, hipStream_t s) {
-  const dim3 grid(grid_for_tiles(a.tiles_m * a.tiles_n)), block(kThreads);
+  constexpr int W = kGemmWNW;
+  const dim3 grid(grid_for_tiles(a.tiles_m * a.tiles_n)), block(128 * W);
   if (bf16 && a.lean) {
-    if (a.out_bf16) hipLaunchKernelGGL((k_gemm<bf16_bits, bf16_bits, ROLE, true>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((k_gemm<bf16_bits, float, ROLE, true>), grid, block, 0, s, a);
+    if (a.out_bf16) hipLaunchKernelGGL((k_gemm<bf16_bits, bf16_bits, ROLE, true, 2>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((k_gemm<bf16_bits, float, ROLE, true, 2>), grid, dim3(256), 0, s, a);
   } else if (bf16) {
-    if (a.out_bf16) hipLaunchKernelGGL((k_gemm<bf16_bits, bf16_bits, ROLE, false>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((k_gemm<bf16_bits, float, ROLE, false>), grid, block, 0, s, a);
+    if (a.out_bf16) hipLaunchKernelGGL((k_gemm<bf16_bits, bf16_bits, ROLE, false, W>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((k_gemm<bf16_bits, float, ROLE, false, W>), grid, block, 0, s, a);
   } else {
-    if (a.out_bf16) hipLaunchKernelGGL((k_gemm<float, bf16_bits, ROLE, false>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((k_gemm<float, float, ROLE, false>), grid, block, 0, s, a);
+    if (a.out_bf16) hipLaunchKernelGGL((k_gemm<float, bf16_bits, ROLE, false, 2>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((k_gemm<float, float, ROLE, false, 2>), grid, dim3(256), 0, s, a);
   }
 }
 

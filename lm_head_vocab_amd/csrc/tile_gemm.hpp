@@ -8,8 +8,8 @@
 // ever made of a bf16 operand.
 //
 // gfx950 mapping:
-//  * 256 threads = 4 wave64s in a 2 x 2 grid; a wave owns a (BM/2) x (BN/2)
-//    sub-tile made of 16 x 16 MFMA fragments (v_mfma_f32_16x16x32_bf16 for
+//  * 256 threads = 4 wave64s in a 2 x 2 grid (or 512 = 8 in 2 x 4, two per
+//    SIMD); a wave owns a (BM/2) x (BN/WNW) sub-tile made of 16 x 16 MFMA fragments (v_mfma_f32_16x16x32_bf16 for
 //    bf16, v_mfma_f32_16x16x4_f32 for fp32), fp32 accumulators.  The 16x16
 //    shape moves half the accumulator traffic per flop of the 32x32 one,
 //    which measures faster on this power-limited part.
@@ -67,13 +67,15 @@ struct ElemTraits<float> {
 constexpr int kFrag = 16;   // MFMA output fragment: 16 x 16
 constexpr int kSteps = 2;   // k-steps per slab (4 chunks of 16 bytes per step)
 
-// LGAP: MFMAs between consecutive slab loads of a step
-template <typename T, int BM_, int BN_, int LGAP_ = 1>
+// LGAP: MFMAs between consecutive slab loads of a step.  WNW: waves along N
+// (2: 4 waves, one per SIMD; 4: 8 waves, two per SIMD).
+template <typename T, int BM_, int BN_, int LGAP_ = 1, int WNW_ = 2>
 struct TileCfg {
-  static constexpr int BM = BM_, BN = BN_, LGAP = LGAP_;
+  static constexpr int BM = BM_, BN = BN_, LGAP = LGAP_, WNW = WNW_;
+  static constexpr int WAVES = 2 * WNW, THREADS = 64 * WAVES;
   static constexpr int KC = ElemTraits<T>::kPerChunk;  // elements per 16-byte chunk
   static constexpr int BK = 8 * KC;                    // elements per slab row (128 bytes)
-  static constexpr int WM = BM / 2, WN = BN / 2;       // wave sub-tile
+  static constexpr int WM = BM / 2, WN = BN / WNW;     // wave sub-tile
   static constexpr int FM = WM / kFrag, FN = WN / kFrag;  // 16x16 fragments per wave
   static constexpr int STAGE = (BM + BN) * kRowBytes;  // bytes of one LDS stage
   static constexpr int LDS_BYTES = 2 * STAGE;
@@ -368,9 +370,9 @@ __device__ __forceinline__ void tile_mainloop(f32x4_t (&acc)[Cfg::FM][Cfg::FN],
                                               const Operand<T>& B, int32_t b_row0, int32_t k_len,
                                               char* smem) {
   constexpr int ROWS = Cfg::BM + Cfg::BN;
-  constexpr int GROUPS = ROWS / 8;      // 1 KB load instructions per slab
-  constexpr int PER_WAVE = GROUPS / 4;  // per wave
-  static_assert(GROUPS % 4 == 0 && PER_WAVE % 2 == 0 && Cfg::BM % 8 == 0,
+  constexpr int GROUPS = ROWS / 8;               // 1 KB load instructions per slab
+  constexpr int PER_WAVE = GROUPS / Cfg::WAVES;  // per wave
+  static_assert(GROUPS % Cfg::WAVES == 0 && PER_WAVE % 2 == 0 && Cfg::BM % 8 == 0,
                 "slab must split into 8-row groups");
   static_assert(Cfg::FM * Cfg::FN > Cfg::FM * (A_MN ? 2 : 1) + Cfg::FN * (B_MN ? 2 : 1),
                 "too few MFMAs per step");
@@ -378,7 +380,7 @@ __device__ __forceinline__ void tile_mainloop(f32x4_t (&acc)[Cfg::FM][Cfg::FN],
                 "MN-major operands: bf16, 256 x 256 tiles (a wave's groups in one operand)");
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / Cfg::WNW, wn = wave % Cfg::WNW;
   const int prow = lane >> 3;
   const int lchunk = (lane & 7) ^ prow;
 
