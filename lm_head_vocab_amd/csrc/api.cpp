@@ -135,7 +135,7 @@ struct Layout {
   // backward
   size_t wt, ht, dz, dzt, bwd_end;
   // single-call forward+backward: forward partials and backward buffers at once
-  size_t f_pz, f_pu, f_p2, f_zy, f_wt, f_ht, f_dz, f_dd, f_dzt, fused_end;
+  size_t f_pz, f_pu, f_p2, f_zy, f_wt, f_ht, f_dz, f_dd, f_dzt, f_rs, fused_end;
 };
 
 // fp32 inputs always take LAYOUT_COPIES (the transposing LDS load is bf16).
@@ -187,6 +187,7 @@ Layout plan(const specloss_problem* p, const KindSet& k, int64_t Nc,
   L.f_dz = take((size_t)Nc * L.Vp * L.es);
   L.f_dd = take(k.stage_div ? (size_t)Nc * L.Vp * L.es : 0);
   L.f_dzt = take(L.dw_copies ? (size_t)L.Vp * Nc * L.es : 0);
+  L.f_rs = take(4 * (size_t)Nc * 4);
   L.fused_end = o;
   return L;
 }
@@ -344,13 +345,13 @@ GemmOperand target_operand(const specloss_problem* p, int64_t r0, int64_t rows, 
 enum KernelId : int32_t {
   K_VALIDITY, K_STATS_Q, K_STATS_P, K_COMBINE1, K_ROWDOT, K_DIV, K_COMBINE2, K_REDUCE, K_COPY,
   K_SEED, K_TRANSPOSE_W, K_TRANSPOSE_H, K_DZ, K_GEMM_DH, K_GEMM_DW, K_STATS_STAGE, K_DZ_STAGE,
-  K_DIV_STAGE, K_DZ_DIV, K_TILE_SUM, K_SUM_PARTS, K_TARGET_GATHER, K_NUM_IDS
+  K_DIV_STAGE, K_DZ_DIV, K_TILE_SUM, K_SUM_PARTS, K_TARGET_GATHER, K_STAGE_FIX, K_NUM_IDS
 };
 const char* const kKernelNames[K_NUM_IDS] = {
     "validity", "stats_q", "stats_p", "combine1", "rowdot", "div", "combine2", "reduce",
     "copy_lse", "seed", "transpose_W", "transpose_h", "dz", "gemm_dh", "gemm_dW",
     "stats_stage", "dz_stage", "div_stage", "dz_div", "tile_sum", "sum_partials",
-    "target_gather"};
+    "target_gather", "stage_fix"};
 
 // Brackets launches with the trace's events when the problem carries one.
 struct Tracer {
@@ -566,6 +567,7 @@ int fwd_chunk(const specloss_problem* p, const KindSet& k, const Layout& L, cons
   c1.pm_z = b.pz;
   c1.ps_z = b.pz + tile_cols;
   c1.pm_u = own_target ? b.pu : nullptr;
+  c1.target_absent = k.target ? 0 : 1;
   c1.ps_u = own_target ? b.pu + tile_cols : nullptr;
   c1.pi_u = own_target ? reinterpret_cast<const int32_t*>(b.pu + 2 * tile_cols) : nullptr;
   c1.pq_u = own_target ? b.pu + 3 * tile_cols : nullptr;
@@ -640,6 +642,168 @@ int fwd_chunk(const specloss_problem* p, const KindSet& k, const Layout& L, cons
   return SPECLOSS_OK;
 }
 
+// Forward of chunk rows [r0, r0 + rows) for the label / argmax
+// cross-entropies in the single call, staging the logit gradient for both
+// contractions without a pass of its own: the target side first (argmax p),
+// then the label logits, which are each row's staging reference, then pass 1
+// of the draft side, staging exp(z - reference) in both layouts, the merges,
+// the per-row losses and k_stage_fix (row factors, far rows, one-hot terms).
+// Afterwards dz = rscale[row] * e in e ([Nc][Vp]) and et ([Vp][Nc], or null).
+int ce_chunk_staged(const specloss_problem* p, const KindSet& k, const Layout& L,
+                    const FwdBufs& b, const SavedView& sv, float* loss, float* terms,
+                    const float* seed, int64_t r0, int64_t rows, void* e, void* et,
+                    float* rscale, Tracer& tr, hipStream_t stream) {
+  // rscale [Nc], then row maxima and the tiles' label logits ([Nc] each)
+  float* row_max = rscale + b.Nc;
+  float* zt_lab = rscale + 2 * b.Nc;
+  float* zt_arg = rscale + 3 * b.Nc;
+  const bool bf16 = p->in_dtype == SPECLOSS_BF16;
+  const int64_t H = L.H, Nc = b.Nc, tile_cols = L.Tv * Nc;
+  const bool ce_lab = (k.active >> SPECLOSS_CE_LABEL) & 1u;
+  const bool ce_arg = (k.active >> SPECLOSS_CE_ARGMAX_P) & 1u;
+
+  StatsLaunch sz{};
+  sz.A = op(p->W, H, p->vocab);
+  sz.B = op(offset_rows(p->hidden_states, r0, H, L.es), H, rows);
+  sz.k_len = (int32_t)H;
+  sz.vocab = (int32_t)p->vocab;
+  sz.tiles_m = (int32_t)L.Tv;
+  sz.tiles_n = (int32_t)cdiv(rows, 256);
+  sz.ncols = (int32_t)rows;
+  sz.ldp = (int32_t)Nc;
+  sz.pm = b.pz;
+  sz.ps = b.pz + tile_cols;
+
+  // target side: lse_p, argmax p, flatness
+  if (k.target && !L.shared_target) {
+    StatsLaunch su = sz;
+    su.A = op(p->W_t, H, p->vocab);
+    su.B = target_operand(p, r0, rows, L.es);
+    su.pm = b.pu;
+    su.ps = b.pu + tile_cols;
+    su.pi = reinterpret_cast<int32_t*>(b.pu + 2 * tile_cols);
+    su.pq = b.pu + 3 * tile_cols;
+    TRACED(tr, K_STATS_P, 2.0 * rows * H * p->vocab, launch_stats(bf16, true, su, stream));
+    Combine1Launch c1{};
+    c1.tiles_m = (int32_t)L.Tv;
+    c1.ncols = (int32_t)rows;
+    c1.ldp = (int32_t)Nc;
+    c1.pm_u = b.pu;
+    c1.ps_u = b.pu + tile_cols;
+    c1.pi_u = reinterpret_cast<const int32_t*>(b.pu + 2 * tile_cols);
+    c1.pq_u = b.pu + 3 * tile_cols;
+    c1.vocab = (int32_t)p->vocab;
+    c1.flags = sv.flags + r0;
+    c1.lse_p = sv.lse_p + r0;
+    c1.y_arg = sv.y_arg + r0;
+    c1.flat = sv.flat + r0;
+    TRACED(tr, K_COMBINE1, 4.0 * L.Tv * rows * 4, launch_combine1(c1, stream));
+  } else if (L.shared_target) {
+    const char* tb = reinterpret_cast<const char*>(b.tstat);
+    const size_t fs = align_up((size_t)L.Nt * 4, kAlign);
+    TargetGatherLaunch tg{};
+    tg.ncols = (int32_t)rows;
+    tg.r0 = r0;
+    tg.flags = sv.flags;
+    tg.target_row = p->target_row;
+    tg.t_lse_p = reinterpret_cast<const float*>(tb);
+    tg.t_y_arg = reinterpret_cast<const int32_t*>(tb + fs);
+    tg.t_flat = reinterpret_cast<const float*>(tb + 2 * fs);
+    tg.lse_p = sv.lse_p;
+    tg.y_arg = sv.y_arg;
+    tg.flat = sv.flat;
+    TRACED(tr, K_TARGET_GATHER, (double)rows * 24, launch_target_gather(tg, stream));
+  }
+
+  // label logits (each row's staging reference; also the losses' z_y)
+  RowdotLaunch rd{};
+  rd.W = p->W;
+  rd.h = offset_rows(p->hidden_states, r0, H, L.es);
+  rd.H = H;
+  rd.ncols = (int32_t)rows;
+  rd.vocab = (int32_t)p->vocab;
+  rd.y1 = ce_lab ? sv.y_label + r0 : nullptr;
+  rd.y2 = ce_arg ? sv.y_arg + r0 : nullptr;
+  rd.out1 = b.zy;
+  rd.out2 = b.zy + Nc;
+  TRACED(tr, K_ROWDOT, 2.0 * rows * H * L.es * ((ce_lab ? 1 : 0) + (ce_arg ? 1 : 0)),
+         launch_rowdot(bf16, rd, stream));
+
+  // draft side: pass 1 with staging relative to the reference
+  StatsStageLaunch ss{};
+  ss.st = sz;
+  ss.stage = e;
+  ss.ld_stage = L.Vp;
+  ss.stage_t = et;
+  ss.ld_stage_t = Nc;
+  ss.ref = ce_lab ? b.zy : b.zy + Nc;
+  ss.seed = seed + r0;
+  ss.y1 = ce_lab ? sv.y_label + r0 : nullptr;
+  ss.y2 = ce_arg ? sv.y_arg + r0 : nullptr;
+  ss.zt1 = zt_lab;
+  ss.zt2 = zt_arg;
+  TRACED(tr, K_STATS_STAGE, 2.0 * rows * H * p->vocab, launch_stats_stage(bf16, ss, stream));
+  Combine1Launch c1{};
+  c1.tiles_m = (int32_t)L.Tv;
+  c1.ncols = (int32_t)rows;
+  c1.ldp = (int32_t)Nc;
+  c1.pm_z = b.pz;
+  c1.ps_z = b.pz + tile_cols;
+  c1.vocab = (int32_t)p->vocab;
+  c1.flags = sv.flags + r0;
+  c1.lse_q = sv.lse_q + r0;
+  c1.lse_p = sv.lse_p + r0;
+  c1.y_arg = sv.y_arg + r0;
+  c1.flat = sv.flat + r0;
+  c1.row_max = row_max;
+  c1.target_absent = k.target ? 0 : 1;
+  TRACED(tr, K_COMBINE1, 2.0 * L.Tv * rows * 4, launch_combine1(c1, stream));
+
+  Combine2Launch c2{};
+  c2.tiles_m = (int32_t)L.Tv;
+  c2.ncols = (int32_t)rows;
+  c2.ldp = (int32_t)Nc;
+  c2.part = b.p2;
+  c2.part_stride = tile_cols;
+  c2.need = 0;
+  memcpy(c2.w, p->weights, sizeof(c2.w));
+  c2.flags = sv.flags + r0;
+  c2.lse_q = sv.lse_q + r0;
+  c2.zy_lab = ce_lab ? b.zy : nullptr;
+  c2.zy_arg = ce_arg ? b.zy + Nc : nullptr;
+  c2.zy_count = 1;
+  c2.loss = loss + r0;
+  c2.term = terms + r0;
+  c2.term_stride = p->n_rows;
+  c2.alpha = sv.alpha + r0;
+  c2.S = sv.S + r0;
+  c2.rkl = sv.rkl + r0;
+  c2.eqg = sv.eqg + r0;
+  TRACED(tr, K_COMBINE2, (double)rows * 4 * 2, launch_combine2(c2, stream));
+
+  StageFixLaunch sf{};
+  sf.ncols = (int32_t)rows;
+  sf.tiles_m = (int32_t)L.Tv;
+  sf.ldp = (int32_t)Nc;
+  sf.r0 = r0;
+  sf.pm = b.pz;
+  sf.ref = ss.ref;
+  sf.row_max = row_max;
+  sf.seed = seed;
+  sf.sv = sv;
+  sf.zt_lab = zt_lab;
+  sf.zt_arg = zt_arg;
+  sf.w_lab = p->weights[SPECLOSS_CE_LABEL];
+  sf.w_arg = p->weights[SPECLOSS_CE_ARGMAX_P];
+  sf.stage = e;
+  sf.ld_stage = L.Vp;
+  sf.stage_t = et;
+  sf.ld_stage_t = Nc;
+  sf.rscale = rscale;
+  TRACED(tr, K_STAGE_FIX, (double)rows * 32, launch_stage_fix(bf16, sf, stream));
+  return SPECLOSS_OK;
+}
+
 int launch_reduce_for(const specloss_problem* p, const KindSet& k, const float* loss,
                       const float* terms, const int64_t* counts, float* reduced, Tracer& tr,
                       hipStream_t stream) {
@@ -675,7 +839,7 @@ int launch_seed_for(const specloss_problem* p, const SavedView& sv, const float*
 // MN-major operand).
 int contract_dh(const specloss_problem* p, const Layout& L, int64_t Nc, const void* dz,
                 const void* wt, int64_t r0, int64_t rows, void* dhidden, int32_t dh_dtype,
-                Tracer& tr, hipStream_t stream) {
+                Tracer& tr, hipStream_t stream, const float* rscale = nullptr) {
   const bool bf16 = p->in_dtype == SPECLOSS_BF16;
   const int64_t H = L.H, V = L.V, Vp = L.Vp;
   const size_t dh_es = dh_dtype == SPECLOSS_BF16 ? 2 : 4;
@@ -699,6 +863,7 @@ int contract_dh(const specloss_problem* p, const Layout& L, int64_t Nc, const vo
   g.accumulate = 0;
   g.out_bf16 = dh_dtype == SPECLOSS_BF16;
   g.role = 0;
+  g.rscale = rscale;
   TRACED(tr, K_GEMM_DH, 2.0 * rows * H * V, launch_gemm(bf16, g, stream));
   return SPECLOSS_OK;
 }
@@ -1034,9 +1199,29 @@ int lmhead_loss_fwd_bwd(const specloss_problem* p, void* workspace, size_t ws_by
   if (L.shared_target) TRY(target_prepass(p, L, b, tr, stream));
   if (dhidden && L.wt_copy)
     TRACED(tr, K_TRANSPOSE_W, 2.0 * Vp * H * L.es, launch_transpose(bf16, p->W, V, H, wt, Vp, stream));
+  // label / argmax cross-entropies with the dW copies: pass 1 stages the
+  // logit gradient in both layouts up to a per-row factor (ce_chunk_staged)
+  // (not when w_lab + w_arg = 0: the row factor would vanish)
+  const bool staged_ce = !k.stage_div && L.dw_copies &&
+                         p->weights[SPECLOSS_CE_LABEL] + p->weights[SPECLOSS_CE_ARGMAX_P] != 0.0f;
+  float* rscale = reinterpret_cast<float*>(ws + L.f_rs);
   int chunk = 0;
   for (int64_t r0 = 0; r0 < N; r0 += Nc, ++chunk) {
     const int64_t rows = (N - r0) < Nc ? (N - r0) : Nc;
+    if (staged_ce) {
+      TRY(ce_chunk_staged(p, k, L, b, sv, loss, terms, seed, r0, rows, dz, dW ? dzt : nullptr,
+                          rscale, tr, stream));
+      const void* hc = offset_rows(p->hidden_states, r0, H, L.es);
+      if (dW)
+        TRACED(tr, K_TRANSPOSE_H, 2.0 * Nc * H * L.es,
+               launch_transpose(bf16, hc, rows, H, ht, Nc, stream, rscale));
+      if (dhidden)
+        TRY(contract_dh(p, L, Nc, dz, wt, r0, rows, dhidden, dh_dtype, tr, stream, rscale));
+      if (dW)
+        TRY(contract_dW(p, L, Nc, dz, dzt, ht, Nc, r0, rows, chunk > 0 || accumulate_dW, dW, tr,
+                        stream));
+      continue;
+    }
     TRY(fwd_chunk(p, k, L, b, sv, loss, terms, r0, rows, dz, dd, tr, stream));
     DzStageLaunch ds{};
     ds.tiles_m = (int32_t)L.Tv;
@@ -1212,6 +1397,7 @@ int lmhead_shard_pass1(const specloss_problem* p, const specloss_shard* sh, void
     c1.pm_z = b.pz;
     c1.ps_z = b.pz + tile_cols;
     c1.pm_u = k.target ? b.pu : nullptr;
+    c1.target_absent = k.target ? 0 : 1;
     c1.ps_u = k.target ? b.pu + tile_cols : nullptr;
     c1.pi_u = k.target ? reinterpret_cast<const int32_t*>(b.pu + 2 * tile_cols) : nullptr;
     c1.pq_u = k.target ? b.pu + 3 * tile_cols : nullptr;
@@ -1247,6 +1433,7 @@ int lmhead_shard_merge1(const specloss_problem* p, const specloss_shard* sh, voi
   c1.pm_z = X.f(0);
   c1.ps_z = X.f(1);
   c1.pm_u = k.target ? X.f(2) : nullptr;
+  c1.target_absent = k.target ? 0 : 1;
   c1.ps_u = k.target ? X.f(3) : nullptr;
   c1.pq_u = k.target ? X.f(4) : nullptr;
   c1.pi_u = k.target ? reinterpret_cast<const int32_t*>(X.f(5)) : nullptr;

@@ -124,6 +124,12 @@ __device__ __forceinline__ void store_frag_pair(T* p0, int64_t ld, const float (
 }
 
 template <typename T>
+__device__ __forceinline__ float load1(const T* src) {
+  if constexpr (sizeof(T) == 2) return (float)*reinterpret_cast<const __bf16*>(src);
+  else return *src;
+}
+
+template <typename T>
 __device__ __forceinline__ void store1(T* dst, float x);
 template <>
 __device__ __forceinline__ void store1<bf16_bits>(bf16_bits* dst, float x) {
@@ -145,6 +151,53 @@ __device__ __forceinline__ void load_chunk(const T* src, float (&out)[KC]) {
   } else {
 #pragma unroll
     for (int q = 0; q < KC; ++q) out[q] = __int_as_float(raw[q]);
+  }
+}
+
+// A tile's values (in the accumulator layout) stored to a row-major output
+// whose rows are the tile's M index, as 16-byte pieces: the tile goes out in
+// two halves of 128 rows, each staged through LDS as fp32 (rows padded to
+// BN * 4 + 16 bytes so the row groups of a fragment store land in different
+// banks), then streamed row by row.  Rounding to T happens at the store.
+template <typename T, typename Cfg>
+__device__ __forceinline__ void store_tile_rows(const f32x4_t (&acc)[Cfg::FM][Cfg::FN], T* out,
+                                                int64_t ld, int64_t row0, int64_t col0,
+                                                char* smem) {
+  constexpr int kHalf = Cfg::BM / 2;
+  constexpr int kStride = Cfg::BN * 4 + 16;
+  constexpr int kPieces = Cfg::BN / 8;  // 8-value pieces per row
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+#pragma unroll 1
+  for (int h = 0; h < 2; ++h) {
+    if (wm == h) {
+#pragma unroll
+      for (int i = 0; i < Cfg::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < Cfg::FN; ++j)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int row = i * kFrag + frag_row(r, lane);
+            const int col = wn * Cfg::WN + j * kFrag + frag_col(lane);
+            *reinterpret_cast<float*>(smem + row * kStride + col * 4) = acc[i][j][r];
+          }
+    }
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < kHalf * kPieces; idx += kThreads) {
+      const int row = idx / kPieces, pc = idx % kPieces;
+      const f32x4_t x0 = *reinterpret_cast<const f32x4_t*>(smem + row * kStride + pc * 32);
+      const f32x4_t x1 = *reinterpret_cast<const f32x4_t*>(smem + row * kStride + pc * 32 + 16);
+      T* p = out + (row0 + h * kHalf + row) * ld + col0 + pc * 8;
+      if constexpr (sizeof(T) == 2) {
+        const bf16x8_t b = {(__bf16)x0[0], (__bf16)x0[1], (__bf16)x0[2], (__bf16)x0[3],
+                            (__bf16)x1[0], (__bf16)x1[1], (__bf16)x1[2], (__bf16)x1[3]};
+        *reinterpret_cast<bf16x8_t*>(p) = b;
+      } else {
+        *reinterpret_cast<f32x4_t*>(p) = x0;
+        *reinterpret_cast<f32x4_t*>(p + 4) = x1;
+      }
+    }
+    __syncthreads();
   }
 }
 
@@ -259,12 +312,19 @@ __global__ __launch_bounds__(kThreads, 1) void k_stats(StatsLaunch a) {
 
 // ============================================================================
 // pass 1 with staging: the tile's column maxima are merged across the two
-// half-waves and the two wave rows first, then e = exp(z - m_tile) is both
-// summed and stored (rounded to the storage type) for the backward.
+// half-waves and the two wave rows first, then e = exp(z - m_tile) is summed
+// for the partials and stored for the backward (rounded to the storage type),
+// scaled to the row's reference when one is given: e' = e exp(m_tile - ref) =
+// exp(z - ref), unless the tile's max exceeds ref + kStageRange (then e
+// itself, so nothing overflows; such rows are rescaled by k_stage_fix), and 0
+// on rows whose seed is 0.  With stage_t the values also go out transposed,
+// as 16-byte pieces of rows through the LDS-staged row epilogue.
 template <typename T, int WNW>
 __global__ __launch_bounds__(128 * WNW, 1) void k_stats_stage(StatsStageLaunch a) {
   using Cfg = TileCfg<T, 256, 256, kStatsLoadGap, WNW>;
-  __shared__ __attribute__((aligned(16))) char smem[Cfg::LDS_BYTES];
+  constexpr int kRowsSmem = (Cfg::BM / 2) * (Cfg::BN * 4 + 16);  // store_tile_rows staging
+  constexpr int kSmem = Cfg::LDS_BYTES > kRowsSmem ? Cfg::LDS_BYTES : kRowsSmem;
+  __shared__ __attribute__((aligned(16))) char smem[kSmem];
   const StatsLaunch& st = a.st;
   int tm, tn;
   if (!tile_of(st.tiles_m, st.tiles_n, kGroupM, tm, tn)) return;
@@ -301,6 +361,32 @@ __global__ __launch_bounds__(128 * WNW, 1) void k_stats_stage(StatsStageLaunch a
     mj[j] = fmaxf(red[c], red[Cfg::BN + c]);
   }
 
+  // the fp32 logit at each row's labels, from the one tile that holds it (the
+  // staged bf16 value near 1 would lose the difference q_y - 1)
+  if (a.ref) {
+#pragma unroll
+    for (int j = 0; j < Cfg::FN; ++j) {
+      const int c = tn * Cfg::BN + wn * Cfg::WN + j * kFrag + frag_col(lane);
+      if (c >= st.ncols) continue;
+#pragma unroll
+      for (int w = 0; w < 2; ++w) {
+        const int32_t* yv = w ? a.y2 : a.y1;
+        if (!yv) continue;
+        const int y = yv[c];
+        if (y < 0 || (y >> 8) != tm) continue;
+        const int local = (y & 255) - wm * Cfg::WM;  // row within this wave's rows
+        if (local < 0 || local >= Cfg::WM || ((local & 15) >> 2) != (lane >> 4)) continue;
+        float z = 0.0f;
+#pragma unroll
+        for (int i = 0; i < Cfg::FM; ++i)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (i == (local >> 4) && r == (local & 3)) z = acc[i][j][r];
+        (w ? a.zt2 : a.zt1)[c] = z;
+      }
+    }
+  }
+
   T* E = static_cast<T*>(a.stage);
   float sj[Cfg::FN];
   static_assert(Cfg::FN % 2 == 0, "column blocks are stored in pairs");
@@ -309,6 +395,24 @@ __global__ __launch_bounds__(128 * WNW, 1) void k_stats_stage(StatsStageLaunch a
     // E row = chunk row (this tile's column), contiguous along the vocabulary
     T* e0 = E + (int64_t)(tn * Cfg::BN + wn * Cfg::WN + j * kFrag) * a.ld_stage + v_base;
     const float mb0 = mj[j] * kLog2e, mb1 = mj[j + 1] * kLog2e;
+    // staging factors of the two columns: exp(m_tile - ref), 1 or 0
+    float f0 = 1.0f, f1 = 1.0f;
+    if (a.ref) {
+      float fh[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int c = tn * Cfg::BN + wn * Cfg::WN + (j + h) * kFrag + frag_col(lane);
+        const float m = mj[j + h];
+        float f = 0.0f;
+        if (c < st.ncols && a.seed[c] != 0.0f) {
+          const float d = m - a.ref[c];
+          f = d > kStageRange ? 1.0f : fast_exp2(d * kLog2e);
+        }
+        fh[h] = f;
+      }
+      f0 = fh[0];
+      f1 = fh[1];
+    }
     float s0 = 0.0f, s1 = 0.0f;
 #pragma unroll
     for (int i = 0; i < Cfg::FM; ++i) {
@@ -321,6 +425,10 @@ __global__ __launch_bounds__(128 * WNW, 1) void k_stats_stage(StatsStageLaunch a
         f[r] = in ? fast_exp2(fmaf(acc[i][j + 1][r], kLog2e, -mb1)) : 0.0f;
         s0 += e[r];
         s1 += f[r];
+        e[r] *= f0;
+        f[r] *= f1;
+        acc[i][j][r] = e[r];
+        acc[i][j + 1][r] = f[r];
       }
       store_frag_pair<T>(e0 + i * kFrag, a.ld_stage, e, f, lane);
     }
@@ -345,6 +453,11 @@ __global__ __launch_bounds__(128 * WNW, 1) void k_stats_stage(StatsStageLaunch a
         st.ps[o] = red[c] + red[Cfg::BN + c];
       }
     }
+  }
+  if (a.stage_t) {
+    __syncthreads();  // the row epilogue reuses the reduction space
+    store_tile_rows<T, Cfg>(acc, static_cast<T*>(a.stage_t), a.ld_stage_t, (int64_t)tm * Cfg::BM,
+                            (int64_t)tn * Cfg::BN, smem);
   }
 }
 
@@ -610,53 +723,6 @@ __device__ __forceinline__ float dz_elem(const RowCoef& c, const float* w, float
   return g;
 }
 
-// A tile's values (in the accumulator layout) stored to a row-major output
-// whose rows are the tile's M index, as 16-byte pieces: the tile goes out in
-// two halves of 128 rows, each staged through LDS as fp32 (rows padded to
-// BN * 4 + 16 bytes so the row groups of a fragment store land in different
-// banks), then streamed row by row.  Rounding to T happens at the store.
-template <typename T, typename Cfg>
-__device__ __forceinline__ void store_tile_rows(const f32x4_t (&acc)[Cfg::FM][Cfg::FN], T* out,
-                                                int64_t ld, int64_t row0, int64_t col0,
-                                                char* smem) {
-  constexpr int kHalf = Cfg::BM / 2;
-  constexpr int kStride = Cfg::BN * 4 + 16;
-  constexpr int kPieces = Cfg::BN / 8;  // 8-value pieces per row
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-#pragma unroll 1
-  for (int h = 0; h < 2; ++h) {
-    if (wm == h) {
-#pragma unroll
-      for (int i = 0; i < Cfg::FM; ++i)
-#pragma unroll
-        for (int j = 0; j < Cfg::FN; ++j)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int row = i * kFrag + frag_row(r, lane);
-            const int col = wn * Cfg::WN + j * kFrag + frag_col(lane);
-            *reinterpret_cast<float*>(smem + row * kStride + col * 4) = acc[i][j][r];
-          }
-    }
-    __syncthreads();
-    for (int idx = threadIdx.x; idx < kHalf * kPieces; idx += kThreads) {
-      const int row = idx / kPieces, pc = idx % kPieces;
-      const f32x4_t x0 = *reinterpret_cast<const f32x4_t*>(smem + row * kStride + pc * 32);
-      const f32x4_t x1 = *reinterpret_cast<const f32x4_t*>(smem + row * kStride + pc * 32 + 16);
-      T* p = out + (row0 + h * kHalf + row) * ld + col0 + pc * 8;
-      if constexpr (sizeof(T) == 2) {
-        const bf16x8_t b = {(__bf16)x0[0], (__bf16)x0[1], (__bf16)x0[2], (__bf16)x0[3],
-                            (__bf16)x1[0], (__bf16)x1[1], (__bf16)x1[2], (__bf16)x1[3]};
-        *reinterpret_cast<bf16x8_t*>(p) = b;
-      } else {
-        *reinterpret_cast<f32x4_t*>(p) = x0;
-        *reinterpret_cast<f32x4_t*>(p + 4) = x1;
-      }
-    }
-    __syncthreads();
-  }
-}
-
 template <typename T, bool DUAL>
 __global__ __launch_bounds__(kThreads, 1) void k_dz(DzLaunch a) {
   using Cfg = TileCfg<T, 256, (DUAL ? 128 : 256)>;
@@ -814,7 +880,9 @@ __global__ __launch_bounds__(128 * WNW, 1) void k_gemm(GemmLaunch a) {
         const int row = piece >> 6, c4 = (piece & 63) * 4;
         const int grow = tm * Cfg::BM + h * kHalfRows + row, gcol = tn * Cfg::BN + c4;
         if (grow >= a.m_valid || gcol >= a.n_valid) continue;
-        const f32x4_t x = *reinterpret_cast<const f32x4_t*>(smem + row * kEpiStride + c4 * 4) + old[q];
+        f32x4_t x = *reinterpret_cast<const f32x4_t*>(smem + row * kEpiStride + c4 * 4);
+        if (a.rscale) x *= a.rscale[grow];
+        x += old[q];
         OutT* p = C + (int64_t)grow * a.ldc + gcol;
         if constexpr (sizeof(OutT) == 4) __builtin_nontemporal_store(x, reinterpret_cast<f32x4_t*>(p));
         else store4<bf16_bits>(reinterpret_cast<bf16_bits*>(p), x[0], x[1], x[2], x[3]);
@@ -990,6 +1058,7 @@ __global__ __launch_bounds__(kCombine1Threads) void k_combine1(Combine1Launch a)
     const float lse = m + logf(s);
     if (side == 0) {
       a.lse_q[c] = lse;
+      if (a.row_max) a.row_max[c] = m;
     } else {
       a.lse_p[c] = lse;
       const int bt = sb[bseg][rr];  // -1 only when no tile has a finite maximum
@@ -998,7 +1067,7 @@ __global__ __launch_bounds__(kCombine1Threads) void k_combine1(Combine1Launch a)
       a.flat[c] = (bt >= 0 && (!a.flags || a.flags[c])) ? s / sqrtf((float)a.vocab * q) : 0.0f;
     }
   }
-  if (!a.pm_u && !a.raw_m[0]) {
+  if (a.target_absent && !a.raw_m[0]) {
     a.lse_p[c] = 0.0f;
     a.y_arg[c] = -1;
     a.flat[c] = 0.0f;
@@ -1177,7 +1246,7 @@ __global__ __launch_bounds__(256) void k_seed(SeedLaunch a) {
 // distinct banks.
 template <typename T>
 __global__ __launch_bounds__(256) void k_transpose(const T* in, int64_t rows, int64_t cols, T* out,
-                                                   int64_t ld_out) {
+                                                   int64_t ld_out, const float* rscale) {
   constexpr int KC = 16 / (int)sizeof(T);  // elements per 16-byte chunk
   constexpr int CPR = 64 / KC;             // chunks per 64-element row
   constexpr int IT = 64 * CPR / 256;       // chunks per thread
@@ -1193,6 +1262,18 @@ __global__ __launch_bounds__(256) void k_transpose(const T* in, int64_t rows, in
     const int64_t r = c0 + y;
     v[it] = r < rows ? *reinterpret_cast<const i32x4_t*>(in + r * cols + j0 + ch * KC)
                      : i32x4_t{0, 0, 0, 0};
+    if (rscale && r < rows) {
+      const float f = rscale[r];
+      if constexpr (sizeof(T) == 2) {
+        bf16x8_t b = __builtin_bit_cast(bf16x8_t, v[it]);
+#pragma unroll
+        for (int e = 0; e < KC; ++e) b[e] = (__bf16)((float)b[e] * f);
+        v[it] = __builtin_bit_cast(i32x4_t, b);
+      } else {
+#pragma unroll
+        for (int e = 0; e < KC; ++e) v[it][e] = __float_as_int(__int_as_float(v[it][e]) * f);
+      }
+    }
   }
 #pragma unroll
   for (int it = 0; it < IT; ++it) {
@@ -1240,6 +1321,65 @@ __global__ __launch_bounds__(256) void k_align(AlignLaunch a) {
   }
   a.target_row[r] = tr;
   a.mask[r] = m;
+}
+
+// ============================================================================
+// staged cross-entropy values: row factor, rescue of far rows, one-hot terms
+// ============================================================================
+// One workgroup per chunk row.  The row's staged values are exp(z - ref) (and
+// exp(z - m_tile) in tiles whose max exceeds ref + kStageRange).  Normal rows
+// keep them, with factor seed (w_lab + w_arg) exp(ref - lse): dz = factor *
+// staged.  A row with such a tile is rescaled in place to exp(z - lse) (each
+// tile by exp(t_ref - lse) <= 1, t_ref the reference it was staged with), with
+// factor seed (w_lab + w_arg).  The entries of the row's labels, where dz =
+// seed ((w_lab + w_arg) q - w_lab [v = y_lab] - w_arg [v = y_arg]) carries the
+// one-hot terms, are rewritten from the tile's fp32 logit there (see
+// label_entry), by the thread that owns entry y (entry i of every tile
+// belongs to thread i).
+template <typename T>
+__global__ __launch_bounds__(256) void k_stage_fix(StageFixLaunch a) {
+  const int c = blockIdx.x;
+  const int64_t gr = a.r0 + c;
+  const float sd = a.seed[gr];
+  if (sd == 0.0f) {  // staged as zeros
+    if (threadIdx.x == 0) a.rscale[c] = 0.0f;
+    return;
+  }
+  const float lse = a.sv.lse_q[gr], ref = a.ref[c];
+  const bool far = a.row_max[c] - ref > kStageRange;
+  const float eref = far ? lse : ref;
+  const float factor = sd * (a.w_lab + a.w_arg) * fast_exp2((eref - lse) * kLog2e);
+  const int yl = a.w_lab != 0.0f ? a.sv.y_label[gr] : -1;
+  const int ya = a.w_arg != 0.0f ? a.sv.y_arg[gr] : -1;
+  // entry y of dz / factor = exp(lse - eref) (q_y - w_y / W), W = w_lab + w_arg,
+  // w_y the weights whose label is y; formed as expm1(z_y - lse) + (W - w_y) / W
+  // from the tile's fp32 logit so that q_y near 1 keeps its difference from 1
+  const float wsum = a.w_lab + a.w_arg;
+  auto label_entry = [&](int y, float zt) {
+    const float wy = (y == yl ? a.w_lab : 0.0f) + (y == ya ? a.w_arg : 0.0f);
+    return fast_exp2((lse - eref) * kLog2e) * (expm1f(zt - lse) + (wsum - wy) / wsum);
+  };
+  T* E = static_cast<T*>(a.stage) + (int64_t)c * a.ld_stage;
+  T* Et = static_cast<T*>(a.stage_t);
+  auto put = [&](int64_t v, float x) {
+    store1<T>(E + v, x);
+    if (Et) store1<T>(Et + v * a.ld_stage_t + c, x);
+  };
+  if (threadIdx.x == 0) a.rscale[c] = factor;
+  if (far) {
+    // thread i owns entry i of every tile
+    for (int t = 0; t < a.tiles_m; ++t) {
+      const float m = a.pm[(int64_t)t * a.ldp + c];
+      const float tref = m - ref > kStageRange ? m : ref;
+      const float f = fast_exp2((tref - lse) * kLog2e);
+      const int64_t v = (int64_t)t * kVocabTile + threadIdx.x;
+      if (v != yl && v != ya) put(v, load1<T>(E + v) * f);
+    }
+  }
+  // the label entries, by the thread that owns them
+  if (yl >= 0 && (yl & 255) == (int)threadIdx.x) put(yl, label_entry(yl, a.zt_lab[c]));
+  if (ya >= 0 && ya != yl && (ya & 255) == (int)threadIdx.x)
+    put(ya, label_entry(ya, a.zt_arg[c]));
 }
 
 // ============================================================================
@@ -1417,17 +1557,24 @@ hipError_t launch_seed(const SeedLaunch& a, hipStream_t s) {
 }
 
 hipError_t launch_transpose(bool bf16, const void* in, int64_t rows, int64_t cols, void* out,
-                            int64_t ld_out, hipStream_t s) {
+                            int64_t ld_out, hipStream_t s, const float* rscale) {
   // whole 64 x 64 tiles on the column side and 16-byte aligned rows
   if (cols % 64 != 0 || ld_out % 64 != 0 || rows > ld_out) return hipErrorInvalidValue;
   const dim3 grid((unsigned)(ld_out / 64), (unsigned)(cols / 64)), block(256);
   if (bf16)
     hipLaunchKernelGGL(k_transpose<bf16_bits>, grid, block, 0, s,
                        static_cast<const bf16_bits*>(in), rows, cols, static_cast<bf16_bits*>(out),
-                       ld_out);
+                       ld_out, rscale);
   else
     hipLaunchKernelGGL(k_transpose<float>, grid, block, 0, s, static_cast<const float*>(in), rows,
-                       cols, static_cast<float*>(out), ld_out);
+                       cols, static_cast<float*>(out), ld_out, rscale);
+  return hipGetLastError();
+}
+
+hipError_t launch_stage_fix(bool bf16, const StageFixLaunch& a, hipStream_t s) {
+  if (a.ncols <= 0) return hipSuccess;
+  if (bf16) hipLaunchKernelGGL(k_stage_fix<bf16_bits>, dim3(a.ncols), dim3(256), 0, s, a);
+  else hipLaunchKernelGGL(k_stage_fix<float>, dim3(a.ncols), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

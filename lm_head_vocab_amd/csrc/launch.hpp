@@ -59,12 +59,28 @@ struct StatsLaunch {
 // target: the variant for the target logits u (argmax and e^2 sums as well)
 hipError_t launch_stats(bool bf16, bool target, const StatsLaunch& a, hipStream_t s);
 
-// pass 1 for the single-call forward+backward: also stores
-// e = exp(z - m_tile) of every (row, vocab) into `stage` ([cap][Vp], row-major)
+// pass 1 for the single-call forward+backward: also stores staged values of
+// every (row, vocab) into `stage` ([cap][Vp], row-major) and, when stage_t is
+// set, transposed into stage_t ([Vp][cap]).  Without `ref` a row's values are
+// e = exp(z - m_tile).  With `ref` (per chunk row) they are e' = exp(z - ref)
+// in the tiles whose max is at most ref + kStageRange, e = exp(z - m_tile) in
+// the others (a row with such a tile is rescaled after the forward), and 0 on
+// rows whose seed is 0.
+constexpr float kStageRange = 64.0f;
 struct StatsStageLaunch {
   StatsLaunch st;
   void* stage;
   int64_t ld_stage;
+  void* stage_t;
+  int64_t ld_stage_t;
+  const float* ref;   // chunk-local, or null
+  const float* seed;  // chunk-local (with ref)
+  // with ref: the tile holding a row's label y1 (y2) writes the row's fp32
+  // logit there into zt1 (zt2); chunk-local, null when unused
+  const int32_t* y1;
+  const int32_t* y2;
+  float* zt1;
+  float* zt2;
 };
 hipError_t launch_stats_stage(bool bf16, const StatsStageLaunch& a, hipStream_t s);
 
@@ -131,6 +147,7 @@ struct GemmLaunch {
   int out_bf16;
   int role;  // 0: dh, 1: dW (separate kernel names in profiles)
   int lean;  // bf16 only: B (and for dW also A) are MN-major, read without copies
+  const float* rscale;  // per output row m, or null: C = rscale[m] * (A B^T) (no accumulate)
 };
 hipError_t launch_gemm(bool bf16, const GemmLaunch& a, hipStream_t s);
 
@@ -181,6 +198,8 @@ struct Combine1Launch {
   float* lse_p;
   int32_t* y_arg;
   float* flat;
+  float* row_max;        // chunk-local max of z per row, or null
+  int32_t target_absent; // no target in the problem: write its no-target values
   // record mode (raw_m[0] != null): write the merged partials of this call's
   // tiles instead of the final values: m and sum-exp per side, e^2 sum and
   // argmax (plus idx_offset) of the target side
@@ -191,6 +210,31 @@ struct Combine1Launch {
   int32_t idx_offset;
 };
 hipError_t launch_combine1(const Combine1Launch& a, hipStream_t s);
+
+// Finish the staged values of the label / argmax cross-entropies (single
+// call, pass 1 with `ref`), one workgroup per chunk row: the row factor
+// rscale = seed (w_lab + w_arg) exp(eref - lse_q) with eref = ref, or lse_q
+// for a row whose max exceeds ref + kStageRange (its tiles are first rescaled
+// to exp(z - lse_q)); then the one-hot terms go into the staged entries of
+// the row's labels, so that dz = rscale * staged in both layouts.
+struct StageFixLaunch {
+  int32_t ncols, tiles_m, ldp;
+  int64_t r0;            // global row of chunk column 0
+  const float* pm;       // [tiles_m][ldp] per-tile max of z
+  const float* ref;      // chunk-local
+  const float* row_max;  // chunk-local
+  const float* seed;     // global
+  SavedView sv;          // global
+  const float* zt_lab;   // chunk-local: the tile's logit at y_label (see StatsStageLaunch)
+  const float* zt_arg;   // chunk-local: the tile's logit at y_arg
+  float w_lab, w_arg;
+  void* stage;           // [cap][ld_stage]
+  int64_t ld_stage;
+  void* stage_t;         // [Vp][ld_stage_t]
+  int64_t ld_stage_t;
+  float* rscale;         // chunk-local output
+};
+hipError_t launch_stage_fix(bool bf16, const StageFixLaunch& a, hipStream_t s);
 
 // per-row target statistics from per-target-row ones (rows sharing target rows)
 struct TargetGatherLaunch {
@@ -265,8 +309,9 @@ struct SeedLaunch {
 hipError_t launch_seed(const SeedLaunch& a, hipStream_t s);
 
 // out[j][c] = c < rows ? in[c][j] : 0 for j < cols, c < ld_out
+// rscale (optional, per source row): out = rscale[row] * in, rounded to the type
 hipError_t launch_transpose(bool bf16, const void* in, int64_t rows, int64_t cols, void* out,
-                            int64_t ld_out, hipStream_t s);
+                            int64_t ld_out, hipStream_t s, const float* rscale = nullptr);
 
 struct AlignLaunch {
   int64_t seq_len, batch;

@@ -256,6 +256,41 @@ def test_single_call_forward_backward(case):
     full_parity(p, max_chunk_rows=ch, tag=f"single-{case}", single_call=True)
 
 
+@pytest.mark.parametrize("case", ["far", "far_f32", "near", "zero_sum"])
+def test_single_call_staged_ce_references(case):
+    """The single call stages exp(z - label logit) per row.  far: logits spread
+    by about 16 per unit (W ~ N(0,1), H = 256), so most rows have tiles whose
+    max exceeds the label logit by more than the staging range and are
+    rescaled after the forward; near: the label is the argmax by a wide
+    margin (the other staged values are tiny); zero_sum: label and argmax
+    weights that cancel, which takes the other staging variant."""
+    if case in ("far", "far_f32"):
+        p = synthetic.make_problem("ce_bf16_1b", n_rows=300, hidden_dim=256, vocab=1500)
+        W = synthetic.bf16_bits_to_f32(p.W) * 50.0  # std 1
+        p.W = synthetic.f32_to_bf16_bits(W)
+        if case == "far_f32":
+            p.dtype = "f32"
+            for f in ("hidden", "W"):
+                setattr(p, f, synthetic.bf16_bits_to_f32(getattr(p, f)).copy())
+    elif case == "near":
+        p = synthetic.make_problem("ce_bf16_1b", n_rows=300, hidden_dim=256, vocab=1500)
+        h = synthetic.bf16_bits_to_f32(p.hidden).copy()
+        W = synthetic.bf16_bits_to_f32(p.W)
+        valid = p.labels >= 0
+        # the label logit rises by 14: 1 - q_y is about 1500 e^-14 = 1e-3, the
+        # label entry of dz; far larger margins put it below the fp32
+        # resolution of lse (for any fp32 softmax) and the loss below its ulp
+        h[valid] += 14.0 * W[p.labels[valid]] / np.linalg.norm(W[p.labels[valid]], axis=1,
+                                                               keepdims=True) ** 2
+        p.hidden = synthetic.f32_to_bf16_bits(h)
+    else:
+        p = synthetic.make_problem("multihead_bf16_405b", seq_len=120, hidden_dim=128, vocab=700,
+                                   weights={"ce_label": 0.6, "ce": -0.6})
+        rng = np.random.default_rng(8)
+        p.labels = rng.integers(0, p.vocab, p.n_rows).astype(np.int32)
+    full_parity(p, max_chunk_rows=256, tag=f"staged-{case}", single_call=True)
+
+
 @pytest.mark.parametrize("kind", ["kl_div", "tv", "nla", "lk_hybrid", "rkl", "jsd"])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_single_call_each_divergence(kind, dtype):
