@@ -267,11 +267,12 @@ int lmhead_loss_bwd(const specloss_problem* p, const float* grad_loss, const flo
  *   seed_r = (grad_loss ? grad_loss[r] : 0) + (grad_mean ? grad_mean[0] / n_valid : 0)
  * on valid rows.  This is the per-chunk loop of the blog's "Backward pass"
  * section (logits, loss and gradients of one token chunk, LM-head gradient
- * accumulated over chunks): for the label and argmax-p cross-entropies the
- * forward pass leaves exp(z - tile max) of the chunk (bf16 for bf16 inputs)
- * in the workspace and the logit gradient is formed from it, so the logits
- * are not recomputed.  Other kinds run the forward and backward sequences
- * back to back.  `saved` may be NULL.  Errors as for the two calls.
+ * accumulated over chunks), and the logits are never recomputed: for the
+ * label and argmax-p cross-entropies the forward pass leaves exp(z - label
+ * logit) of the chunk (in the input dtype, both layouts) in the workspace;
+ * with divergences the second forward pass leaves q, q - p and, for rkl and
+ * jsd, log q - log p; the logit gradient is formed from these.  `saved` may
+ * be NULL.  Errors as for the two calls.
  */
 int lmhead_loss_fwd_bwd(const specloss_problem* p, void* workspace, size_t ws_bytes, float* loss,
                         float* term_loss, float* lse_q, void* saved, int64_t* counts,

@@ -41,7 +41,8 @@ struct KindSet {
   bool target = false;  // any kind needing the target side
   bool pass2 = false;   // any divergence needing a second sweep
   bool dual_bwd = false;
-  bool stage_div = false;  // single call: pass 2 stages q and q - p (no rkl / jsd)
+  bool stage_div = false;  // single call: pass 2 stages q and q - p (every divergence)
+  bool stage_log = false;  // ... and log q - log p (rkl, jsd)
   uint32_t need = 0;    // SUM_* bits
 };
 
@@ -60,7 +61,8 @@ KindSet kinds_of(const float* w) {
   if (k.need) k.need |= SUM_ALPHA;  // alpha is reported whenever a second sweep runs
   k.pass2 = k.need != 0;
   k.dual_bwd = (k.active & ~((1u << SPECLOSS_CE_LABEL) | (1u << SPECLOSS_CE_ARGMAX_P))) != 0;
-  k.stage_div = k.dual_bwd && !on(SPECLOSS_RKL) && !on(SPECLOSS_JSD);
+  k.stage_div = k.dual_bwd;
+  k.stage_log = on(SPECLOSS_RKL) || on(SPECLOSS_JSD);
   return k;
 }
 
@@ -135,7 +137,7 @@ struct Layout {
   // backward
   size_t wt, ht, dz, dzt, bwd_end;
   // single-call forward+backward: forward partials and backward buffers at once
-  size_t f_pz, f_pu, f_p2, f_zy, f_wt, f_ht, f_dz, f_dd, f_dzt, f_rs, fused_end;
+  size_t f_pz, f_pu, f_p2, f_zy, f_wt, f_ht, f_dz, f_dd, f_dl, f_dzt, f_rs, fused_end;
 };
 
 // fp32 inputs always take LAYOUT_COPIES (the transposing LDS load is bf16).
@@ -186,6 +188,7 @@ Layout plan(const specloss_problem* p, const KindSet& k, int64_t Nc,
   L.f_ht = take(L.dw_copies ? (size_t)L.H * Nc * L.es : 0);
   L.f_dz = take((size_t)Nc * L.Vp * L.es);
   L.f_dd = take(k.stage_div ? (size_t)Nc * L.Vp * L.es : 0);
+  L.f_dl = take(k.stage_log ? (size_t)Nc * L.Vp * L.es : 0);
   L.f_dzt = take(L.dw_copies ? (size_t)L.Vp * Nc * L.es : 0);
   L.f_rs = take(4 * (size_t)Nc * 4);
   L.fused_end = o;
@@ -520,7 +523,7 @@ int launch_pass1(const specloss_problem* p, const KindSet& k, const Layout& L, c
 // final logsumexps in `sv`; stage_q / stage_d as for fwd_chunk (or null).
 int launch_pass2(const specloss_problem* p, const KindSet& k, const Layout& L, const FwdBufs& b,
                  const SavedView& sv, int64_t r0, int64_t rows, void* stage_q, void* stage_d,
-                 Tracer& tr, hipStream_t stream) {
+                 Tracer& tr, hipStream_t stream, void* stage_l = nullptr) {
   const bool bf16 = p->in_dtype == SPECLOSS_BF16;
   const int64_t H = L.H, Nc = b.Nc;
   DivLaunch dv{};
@@ -541,6 +544,7 @@ int launch_pass2(const specloss_problem* p, const KindSet& k, const Layout& L, c
   dv.part_stride = L.Tv * Nc;
   dv.stage_q = stage_d ? stage_q : nullptr;
   dv.stage_d = stage_d;
+  dv.stage_l = stage_d ? stage_l : nullptr;
   dv.ld_stage = L.Vp;
   TRACED(tr, stage_d ? K_DIV_STAGE : K_DIV, 4.0 * rows * H * p->vocab,
          launch_div(bf16, dv, stream));
@@ -549,7 +553,8 @@ int launch_pass2(const specloss_problem* p, const KindSet& k, const Layout& L, c
 
 int fwd_chunk(const specloss_problem* p, const KindSet& k, const Layout& L, const FwdBufs& b,
               const SavedView& sv, float* loss, float* terms, int64_t r0, int64_t rows,
-              void* stage, void* stage_d, Tracer& tr, hipStream_t stream) {
+              void* stage, void* stage_d, Tracer& tr, hipStream_t stream,
+              void* stage_l = nullptr) {
   const bool bf16 = p->in_dtype == SPECLOSS_BF16;
   const int64_t H = L.H, Nc = b.Nc;
   const int64_t tile_cols = L.Tv * Nc;
@@ -613,7 +618,7 @@ int fwd_chunk(const specloss_problem* p, const KindSet& k, const Layout& L, cons
   }
 
   if (k.pass2) {
-    const int rc = launch_pass2(p, k, L, b, sv, r0, rows, stage, stage_d, tr, stream);
+    const int rc = launch_pass2(p, k, L, b, sv, r0, rows, stage, stage_d, tr, stream, stage_l);
     if (rc) return rc;
   }
 
@@ -1076,8 +1081,7 @@ int lmhead_loss_chunk(const specloss_problem* p, size_t ws_bytes, int32_t call,
   int64_t nc;
   if (call == 0) {
     nc = pick_chunk(p, k, ws_bytes, REGION_FWD);
-  } else if (call == 1 || (k.dual_bwd && !k.stage_div)) {
-    // the single call with rkl / jsd runs the backward of the two calls
+  } else if (call == 1) {
     nc = pick_chunk(p, k, ws_bytes, REGION_BWD, &lay);
   } else {
     nc = pick_chunk(p, k, ws_bytes, REGION_FUSED, &lay);
@@ -1155,25 +1159,10 @@ int lmhead_loss_fwd_bwd(const specloss_problem* p, void* workspace, size_t ws_by
   TRY(check_fwd_outputs(loss, term_loss, lse_q, saved, counts, reduced));
   TRY(check_bwd_args(grad_loss, grad_mean, dhidden, dh_dtype, dW));
   if (!workspace || !aligned(workspace, kAlign)) return SPECLOSS_E_WORKSPACE;
-  if (k.dual_bwd && !k.stage_div) {
-    // rkl / jsd gradients need log p and log m per element: the forward and
-    // backward sequences run back to back on the same workspace.  Both must
-    // fit before anything is enqueued.
-    int32_t bwd_layout = LAYOUT_COPIES;
-    if (pick_chunk(p, k, ws_bytes, REGION_FWD) <= 0 ||
-        pick_chunk(p, k, ws_bytes, REGION_BWD, &bwd_layout) <= 0)
-      return SPECLOSS_E_WORKSPACE;
-    char* ws = static_cast<char*>(workspace);
-    const Layout L0 = plan(p, k, kChunkQuantum);
-    void* sv_base = saved ? saved : ws + L0.saved;
-    TRY(lmhead_loss_fwd(p, workspace, ws_bytes, loss, term_loss, lse_q, sv_base, counts, reduced,
-                        stream));
-    return lmhead_loss_bwd(p, grad_loss, grad_mean, counts, sv_base, workspace, ws_bytes, dhidden,
-                           dh_dtype, dW, accumulate_dW, stream);
-  }
-  // label / argmax cross-entropies: pass 1 stages e = exp(z - m_tile) per
-  // chunk; with kl_div / tv / nla / lk_hybrid, pass 2 stages q and q - p.  The
-  // logit gradient is formed from the staged values without recomputing logits.
+  // label / argmax cross-entropies: pass 1 stages exp(z - ref) per chunk
+  // (ce_chunk_staged); with divergences, pass 2 stages q and q - p (and log q
+  // - log p for rkl and jsd).  The logit gradient is formed from the staged
+  // values without recomputing logits.
   int32_t layout = LAYOUT_COPIES;
   const int64_t Nc = pick_chunk(p, k, ws_bytes, REGION_FUSED, &layout);
   if (Nc <= 0) return SPECLOSS_E_WORKSPACE;
@@ -1191,6 +1180,7 @@ int lmhead_loss_fwd_bwd(const specloss_problem* p, void* workspace, size_t ws_by
   void* ht = L.dw_copies ? ws + L.f_ht : nullptr;
   void* dz = ws + L.f_dz;
   void* dd = k.stage_div ? ws + L.f_dd : nullptr;
+  void* dl = k.stage_log ? ws + L.f_dl : nullptr;
   void* dzt = L.dw_copies ? ws + L.f_dzt : nullptr;
   Tracer tr{p->trace, stream};
 
@@ -1222,7 +1212,7 @@ int lmhead_loss_fwd_bwd(const specloss_problem* p, void* workspace, size_t ws_by
                         stream));
       continue;
     }
-    TRY(fwd_chunk(p, k, L, b, sv, loss, terms, r0, rows, dz, dd, tr, stream));
+    TRY(fwd_chunk(p, k, L, b, sv, loss, terms, r0, rows, dz, dd, tr, stream, dl));
     DzStageLaunch ds{};
     ds.tiles_m = (int32_t)L.Tv;
     ds.ncols = (int32_t)rows;
@@ -1238,14 +1228,17 @@ int lmhead_loss_fwd_bwd(const specloss_problem* p, void* workspace, size_t ws_by
     ds.w_tv = p->weights[SPECLOSS_TV];
     ds.w_nla = p->weights[SPECLOSS_NLA];
     ds.w_lk = p->weights[SPECLOSS_LK_HYBRID];
+    ds.w_rkl = p->weights[SPECLOSS_RKL];
+    ds.w_jsd = p->weights[SPECLOSS_JSD];
     ds.dd = dd;
+    ds.dl = dl;
     ds.dz = dz;
     ds.ld_dz = Vp;
     ds.dzt = dzt;
     ds.ld_dzt = Nc;
     ds.row_blocks = (int32_t)(cdiv(rows, 256) * 4);
     TRACED(tr, dd ? K_DZ_DIV : K_DZ_STAGE,
-           (double)ds.row_blocks * 64 * Vp * L.es * ((dd ? 3 : 2) + (dzt ? 1 : 0)),
+           (double)ds.row_blocks * 64 * Vp * L.es * ((dd ? 3 : 2) + (dl ? 1 : 0) + (dzt ? 1 : 0)),
            launch_dz_stage(bf16, ds, stream));
     const void* hc = offset_rows(p->hidden_states, r0, H, L.es);
     if (dW && L.dw_copies)

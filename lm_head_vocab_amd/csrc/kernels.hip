@@ -471,7 +471,10 @@ __global__ __launch_bounds__(128 * WNW, 1) void k_stats_stage(StatsStageLaunch a
 //                dz = seed (A q + B d - C q (c - S) - w_lab [v = y_lab] - w_arg [v = y_arg])
 //                where A = w_lab + w_arg, B = w_kl + w_lk lam,
 //                C = w_tv + w_nla / alpha + w_lk (1 - lam), lam = exp(-3 alpha).
-template <typename T, bool DIV>
+//   LOG (with DIV): `dl` holds l = log q - log p, and the rkl and jsd terms
+//                are added: + seed q (w_rkl (l - rKL) + w_jsd (g - E_q[g])),
+//                g = (ln 2 - softplus(-l)) / 2 = (log q - log m) / 2.
+template <typename T, bool DIV, bool LOG>
 __global__ __launch_bounds__(256) void k_dz_stage(DzStageLaunch a) {
   constexpr int VT = kVocabTile, RB = 64;
   constexpr int KC = ElemTraits<T>::kPerChunk;       // elements per 16 bytes
@@ -487,7 +490,7 @@ __global__ __launch_bounds__(256) void k_dz_stage(DzStageLaunch a) {
 
   constexpr int IT = RB * CPR / 256;  // 16-byte chunks per thread
   static_assert(RB * CPR % 256 == 0, "chunks must split evenly over the block");
-  i32x4_t raw[IT], rawd[DIV ? IT : 1];
+  i32x4_t raw[IT], rawd[DIV ? IT : 1], rawl[LOG ? IT : 1];
   // all of this thread's loads first, so they are in flight together
 #pragma unroll
   for (int it = 0; it < IT; ++it) {
@@ -496,6 +499,7 @@ __global__ __launch_bounds__(256) void k_dz_stage(DzStageLaunch a) {
     const int64_t o = (int64_t)(rb * RB + rr) * a.ld_dz + vt * VT + ch * KC;
     raw[it] = *reinterpret_cast<const i32x4_t*>(dz + o);
     if constexpr (DIV) rawd[it] = *reinterpret_cast<const i32x4_t*>(static_cast<const T*>(a.dd) + o);
+    if constexpr (LOG) rawl[it] = *reinterpret_cast<const i32x4_t*>(static_cast<const T*>(a.dl) + o);
   }
 #pragma unroll
   for (int it = 0; it < IT; ++it) {
@@ -504,7 +508,7 @@ __global__ __launch_bounds__(256) void k_dz_stage(DzStageLaunch a) {
     const int c = rb * RB + rr;                    // chunk row
     const int v0 = vt * VT + ch * KC;
     T* p = dz + (int64_t)c * a.ld_dz + v0;
-    float e[KC], dd[KC];
+    float e[KC], dd[KC], ll[KC];
     if constexpr (sizeof(T) == 2) {
       const bf16x8_t b = __builtin_bit_cast(bf16x8_t, raw[it]);
 #pragma unroll
@@ -514,6 +518,11 @@ __global__ __launch_bounds__(256) void k_dz_stage(DzStageLaunch a) {
 #pragma unroll
         for (int q = 0; q < KC; ++q) dd[q] = (float)bd[q];
       }
+      if constexpr (LOG) {
+        const bf16x8_t bl = __builtin_bit_cast(bf16x8_t, rawl[LOG ? it : 0]);
+#pragma unroll
+        for (int q = 0; q < KC; ++q) ll[q] = (float)bl[q];
+      }
     } else {
 #pragma unroll
       for (int q = 0; q < KC; ++q) e[q] = __int_as_float(raw[it][q]);
@@ -521,8 +530,13 @@ __global__ __launch_bounds__(256) void k_dz_stage(DzStageLaunch a) {
 #pragma unroll
         for (int q = 0; q < KC; ++q) dd[q] = __int_as_float(rawd[DIV ? it : 0][q]);
       }
+      if constexpr (LOG) {
+#pragma unroll
+        for (int q = 0; q < KC; ++q) ll[q] = __int_as_float(rawl[LOG ? it : 0][q]);
+      }
     }
     float sd = 0.0f, scale = 0.0f, cb = 0.0f, cc = 0.0f, S = 0.0f;
+    float cr = 0.0f, cj = 0.0f, rkl = 0.0f, eqg = 0.0f;
     int yl = -1, ya = -1;
     if (c < a.ncols) {
       const int64_t gr = a.r0 + c;
@@ -536,6 +550,12 @@ __global__ __launch_bounds__(256) void k_dz_stage(DzStageLaunch a) {
           cc = sd * (a.w_tv + (a.w_nla != 0.0f ? a.w_nla / alpha : 0.0f) +
                      a.w_lk * (1.0f - lam));
           S = a.sv.S[gr];
+          if (LOG) {
+            cr = sd * a.w_rkl;
+            cj = sd * a.w_jsd;
+            rkl = a.sv.rkl[gr];
+            eqg = a.sv.eqg[gr];
+          }
         } else {
           scale = sd * (a.w_lab + a.w_arg) *
                   fast_exp2((a.pm[(int64_t)vt * a.ldp + c] - a.sv.lse_q[gr]) * kLog2e);
@@ -552,6 +572,13 @@ __global__ __launch_bounds__(256) void k_dz_stage(DzStageLaunch a) {
       if (DIV) {
         const float ci = dd[q] < 0.0f ? 1.0f : (dd[q] == 0.0f ? 0.5f : 0.0f);
         x = fmaf(cb, dd[q], x) - cc * e[q] * (ci - S);
+      }
+      if (LOG) {
+        // softplus(-l) = max(-l, 0) + log(1 + exp(-|l|))
+        const float l = ll[q];
+        const float sp = fmaxf(-l, 0.0f) + fast_log2(1.0f + fast_exp2(-fabsf(l) * kLog2e)) * kLn2;
+        const float g = 0.5f * (kLn2 - sp);
+        x += e[q] * (cr * (l - rkl) + cj * (g - eqg));
       }
       if (v == yl) x -= sd * a.w_lab;
       if (v == ya) x -= sd * a.w_arg;
@@ -629,12 +656,13 @@ __global__ __launch_bounds__(kThreads, 1) void k_div(DivLaunch a) {
     float s_alpha = 0.f, s_s = 0.f, s_kl = 0.f, s_rkl = 0.f, s_jsd = 0.f, s_eqg = 0.f;
 #pragma unroll
     for (int i = 0; i < Cfg::FM; ++i) {
-      float sq[4], sd[4];
+      float sq[4], sd[4], sl[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int v = v_base + i * kFrag + frag_row(r, lane);
         sq[r] = 0.0f;
         sd[r] = 0.0f;
+        sl[r] = 0.0f;
         if (tail && v >= a.vocab) continue;
         const float lq = az[i][j][r] - lq0;
         const float lp = au[i][j][r] - lp0;
@@ -642,6 +670,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_div(DivLaunch a) {
         const float p = fast_exp2(lp * kLog2e);
         sq[r] = q;
         sd[r] = q - p;
+        sl[r] = lq - lp;
         if (need & SUM_ALPHA) s_alpha += fminf(p, q);
         if (need & SUM_S) s_s += (q < p) ? q : ((q == p) ? 0.5f * q : 0.0f);
         if (need & SUM_KL) s_kl += p * (lp - lq);
@@ -656,6 +685,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_div(DivLaunch a) {
         const int64_t o = (int64_t)c_tile * a.ld_stage + v_base + i * kFrag + frag_row(0, lane);
         store4<T>(static_cast<T*>(a.stage_q) + o, sq[0], sq[1], sq[2], sq[3]);
         store4<T>(static_cast<T*>(a.stage_d) + o, sd[0], sd[1], sd[2], sd[3]);
+        if (a.stage_l) store4<T>(static_cast<T*>(a.stage_l) + o, sl[0], sl[1], sl[2], sl[3]);
       }
     }
     const float v6[kNumSums] = {s_alpha, s_s, s_kl, s_rkl, s_jsd, s_eqg};
@@ -1436,11 +1466,13 @@ hipError_t launch_stats_stage(bool bf16, const StatsStageLaunch& a, hipStream_t 
 hipError_t launch_dz_stage(bool bf16, const DzStageLaunch& a, hipStream_t s) {
   const dim3 grid((unsigned)(a.tiles_m * a.row_blocks)), block(256);
   if (bf16) {
-    if (a.dd) hipLaunchKernelGGL((k_dz_stage<bf16_bits, true>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((k_dz_stage<bf16_bits, false>), grid, block, 0, s, a);
+    if (a.dl) hipLaunchKernelGGL((k_dz_stage<bf16_bits, true, true>), grid, block, 0, s, a);
+    else if (a.dd) hipLaunchKernelGGL((k_dz_stage<bf16_bits, true, false>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((k_dz_stage<bf16_bits, false, false>), grid, block, 0, s, a);
   } else {
-    if (a.dd) hipLaunchKernelGGL((k_dz_stage<float, true>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((k_dz_stage<float, false>), grid, block, 0, s, a);
+    if (a.dl) hipLaunchKernelGGL((k_dz_stage<float, true, true>), grid, block, 0, s, a);
+    else if (a.dd) hipLaunchKernelGGL((k_dz_stage<float, true, false>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((k_dz_stage<float, false, false>), grid, block, 0, s, a);
   }
   return hipGetLastError();
 }

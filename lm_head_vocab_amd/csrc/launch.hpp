@@ -89,7 +89,9 @@ hipError_t launch_stats_stage(bool bf16, const StatsStageLaunch& a, hipStream_t 
 // holds e = exp(z - m_tile):
 //   dz = seed * ((w_lab + w_arg) e exp(m_tile - lse) - w_lab [v == y_lab] - w_arg [v == y_arg]);
 // with dd it holds q and dd holds q - p, and the divergence terms
-// (kl_div, tv, nla, lk_hybrid) are added from the saved alpha and S.
+// (kl_div, tv, nla, lk_hybrid) are added from the saved alpha and S; with dl
+// (log q - log p) also rkl, q (dl - rkl), and jsd, q (g - E_q[g]) with
+// g = (ln 2 - softplus(-dl)) / 2 = (log q - log m) / 2, m = (p + q) / 2.
 struct DzStageLaunch {
   int32_t tiles_m, ncols, vocab, ldp;
   int64_t r0;
@@ -98,7 +100,9 @@ struct DzStageLaunch {
   SavedView sv;        // global rows
   float w_lab, w_arg;
   float w_kl, w_tv, w_nla, w_lk;  // divergence weights (dd mode only)
+  float w_rkl, w_jsd;             // (dl mode only)
   const void* dd;      // [cap][Vp] q - p, or null
+  const void* dl;      // [cap][Vp] log q - log p (with dd, for rkl / jsd), or null
   void* dz;            // in: e or q, out: dz; [cap][Vp]
   int64_t ld_dz;
   void* dzt;           // [Vp][cap], or null (not needed by bf16 contractions)
@@ -117,6 +121,7 @@ struct DivLaunch {
   int64_t part_stride;  // tiles_m * ldp
   void* stage_q;        // null, or [cap][ld_stage]: q of every (chunk row, vocab)
   void* stage_d;        // [cap][ld_stage]: q - p (with stage_q)
+  void* stage_l;        // [cap][ld_stage]: log q - log p (with stage_q), or null
   int64_t ld_stage;
 };
 hipError_t launch_div(bool bf16, const DivLaunch& a, hipStream_t s);

@@ -296,9 +296,8 @@ def test_single_call_staged_ce_references(case):
 def test_single_call_each_divergence(kind, dtype):
     """Single call per divergence kind over two chunks (the second ragged).
 
-    kl_div, tv, nla and lk_hybrid take the staged path (pass 2 stores q and
-    q - p, the logit gradient is formed from them); rkl and jsd run the
-    forward and backward back to back.
+    Pass 2 stores q and q - p (and log q - log p for rkl and jsd) and the
+    logit gradient is formed from them, with no logits recomputed.
     """
     p = synthetic.make_problem("lk_hybrid_bf16_8b", n_rows=280, hidden_dim=128, vocab=600,
                                weights={kind: 1.0, "ce_label": 0.25})
@@ -310,6 +309,26 @@ def test_single_call_each_divergence(kind, dtype):
         for f in ("hidden", "W", "target_hidden", "W_t"):
             setattr(p, f, synthetic.bf16_bits_to_f32(getattr(p, f)).copy())
     full_parity(p, max_chunk_rows=256, tag=f"single-{kind}-{dtype}", single_call=True)
+
+
+def test_single_call_log_ratio_kinds_mix_and_two_calls():
+    """rkl, jsd, kl_div and tv together in one single call (staged log q - log p
+    beside q and q - p), against the oracle and against the two calls."""
+    w = {"rkl": 0.5, "jsd": 0.7, "kl_div": 0.2, "tv": 0.4, "ce": 0.1}
+    p = synthetic.make_problem("multihead_bf16_405b", seq_len=140, hidden_dim=128, vocab=900,
+                               weights=w)
+    full_parity(p, max_chunk_rows=256, tag="single-logmix", single_call=True)
+    dev = to_device(p)
+    gm = torch.ones(1, device="cuda")
+    a = make_run(p, dev, max_chunk_rows=256)
+    dh1, dW1 = a.forward_backward(grad_mean=gm)
+    b = make_run(p, dev, max_chunk_rows=256)
+    b.forward()
+    dh2, dW2 = b.backward(grad_mean=gm)
+    torch.cuda.synchronize()
+    assert torch.equal(a.loss, b.loss)
+    assert rel_frob(dh1.cpu().numpy(), dh2.cpu().numpy()) < 1e-2
+    assert rel_frob(dW1.cpu().numpy(), dW2.cpu().numpy()) < 1e-2
 
 
 def test_single_call_identical_target_ties():

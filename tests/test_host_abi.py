@@ -324,9 +324,9 @@ def test_chunk_query_validation(lib):
 
 @pytest.mark.parametrize("kind", ["rkl", "jsd"])
 def test_fwd_bwd_rejects_a_forward_only_workspace(lib, kind):
-    """rkl / jsd run the forward and backward sequences back to back: a workspace
-    that holds the forward region but not the backward one is rejected before
-    anything is enqueued (no launch happens here: there is no GPU)."""
+    """A workspace that holds the forward region but not the single call's is
+    rejected before anything is enqueued (no launch happens here: there is no
+    GPU)."""
     p = _problem(N=4096, H=4096, V=128256, weights={kind: 1.0}, target=4096)
     ws = 32 << 20
     assert _chunk(lib, p, ws, B.CALL_FWD)[0] == 0
