@@ -59,7 +59,7 @@ def trace_name(kernel: str) -> str:
         args = [a.strip() for a in targs.strip("<>").split(",")]
         return "gemm_dW" if len(args) > 2 and args[2] == "1" else "gemm_dh"
     names = {"k_stats": "stats_q", "k_stats_stage": "stats_stage", "k_dz_stage": "dz_stage",
-             "k_dz": "dz", "k_div": "div", "k_combine1": "combine1", "k_combine2": "combine2",
+             "k_dz": "dz", "k_div": "div", "k_combine1": "combine1", "k_combine2": "combine2", "k_stage_fix": "stage_fix",
              "k_rowdot": "rowdot", "k_transpose": "transpose", "k_validity": "validity",
              "k_reduce": "reduce", "k_seed": "seed", "k_align": "align"}
     name = names.get(base, base)
@@ -114,7 +114,38 @@ PMC_CMD = ("rocprofv3 --pmc {c} --output-format csv -d <{d}> -o pmc -- python3 <
            "--workload {w} --steps 1 --warmup 0 --no-cpu-baseline --calibrate-copy")
 
 
-def markdown(stats_csv: str, traffic: dict, workload: str, bench: dict = None) -> str:
+MFMA_COUNTERS = ("SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_INSTS_VALU_MFMA_MOPS_F32",
+                 "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CYCLES")
+SIMDS_PER_SE = 32  # MI355X: 32 shader engines (4 per XCD), 8 CUs x 4 SIMDs each
+
+
+def mfma_summary(pmc_csv: str) -> dict:
+    """Per trace name: executed MFMA flops per launch from the MOPS counters
+    (one MOP = 512 flops) and the MFMA-busy fraction of the kernel's busy
+    cycles, SQ_VALU_MFMA_BUSY_CYCLES / (SIMDS_PER_SE x SQ_BUSY_CYCLES) (the
+    busy cycles are summed over the shader engines, the MFMA cycles over the
+    SIMDs)."""
+    vals = defaultdict(lambda: defaultdict(list))
+    for row in csv.DictReader(open(pmc_csv)):
+        if "specloss" not in row["Kernel_Name"]:
+            continue
+        vals[trace_name(row["Kernel_Name"])][row["Counter_Name"]].append(float(row["Counter_Value"]))
+    out = {}
+    for name, c in vals.items():
+        n = max(len(v) for v in c.values())
+        avg = {k: sum(v) / len(v) for k, v in c.items()}
+        mops = avg.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0) + avg.get("SQ_INSTS_VALU_MFMA_MOPS_F32", 0.0)
+        if mops <= 0:
+            continue
+        busy = avg.get("SQ_BUSY_CYCLES", 0.0)
+        out[name] = {"flops_per_launch": mops * 512.0, "dispatches": n,
+                     "mfma_busy": avg.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / (SIMDS_PER_SE * busy)
+                     if busy else None}
+    return out
+
+
+def markdown(stats_csv: str, traffic: dict, workload: str, bench: dict = None,
+             mfma: dict = None) -> str:
     """Markdown summary of a kernel-trace stats run and the counter passes
     (and, if given, the bench.py line of a run on the same box)."""
     rows = list(csv.DictReader(open(stats_csv)))
@@ -156,6 +187,22 @@ def markdown(stats_csv: str, traffic: dict, workload: str, bench: dict = None) -
     for k, v in sorted(traffic["kernels"].items(), key=lambda kv: -kv[1]["bytes_per_launch"]):
         out.append(f"| {k} | {v['fetch_bytes'] / 1e9:.3f} | {(v['write_bytes'] or 0) / 1e9:.3f} | "
                    f"{v['bytes_per_launch'] / 1e9:.3f} |")
+    if mfma:
+        lib = {}
+        if bench:
+            lib = {k: v.get("tflops") for k, v in bench.get("kernels", {}).items()}
+        out += ["", "## MFMA counters per launch", "", "Command (its own run):", "", "```",
+                PMC_CMD.format(c=" ".join(MFMA_COUNTERS), d="mfma", w=workload).replace(
+                    " --calibrate-copy", ""), "```", "",
+                "Executed flops = `SQ_INSTS_VALU_MFMA_MOPS_*` x 512 (the library counts the same "
+                "contractions from its schedule); MFMA busy = `SQ_VALU_MFMA_BUSY_CYCLES` / "
+                f"({SIMDS_PER_SE} SIMDs per shader engine x `SQ_BUSY_CYCLES`), the fraction of "
+                "the kernel's cycles in which a SIMD's matrix pipe was busy (the clock under this "
+                "load is below the 2.4 GHz of the peak figure).", "",
+                "| kernel | counted TFLOP per launch | MFMA busy |", "|---|---:|---:|"]
+        for k, v in sorted(mfma.items(), key=lambda kv: -kv[1]["flops_per_launch"]):
+            busy = "" if v["mfma_busy"] is None else f"{v['mfma_busy']:.3f}"
+            out.append(f"| {k} | {v['flops_per_launch'] / 1e12:.3f} | {busy} |")
     return "\n".join(out) + "\n"
 
 
@@ -169,6 +216,7 @@ def main():
     ap.add_argument("--md", default=None, help="markdown summary to write (needs --stats)")
     ap.add_argument("--workload", default="ce_bf16_8b")
     ap.add_argument("--bench-json", default=None, help="bench.py output of a run on the same box")
+    ap.add_argument("--mfma", default=None, help="counter csv of the MFMA pass (MFMA_COUNTERS)")
     a = ap.parse_args()
     s = summarize(a.fetch, a.write, a.copy_bytes)
     with open(a.out, "w") as f:
@@ -178,8 +226,13 @@ def main():
         if a.bench_json:
             with open(a.bench_json) as f:
                 bench = json.loads([l for l in f.read().splitlines() if l.strip()][-1])
+        mf = mfma_summary(a.mfma) if a.mfma else None
+        if mf:
+            s["mfma"] = mf
+            with open(a.out, "w") as f:
+                json.dump(s, f, indent=1)
         with open(a.md, "w") as f:
-            f.write(markdown(a.stats, s, a.workload, bench))
+            f.write(markdown(a.stats, s, a.workload, bench, mf))
     print(json.dumps({k: round(v["bytes_per_launch"] / 1e9, 3) for k, v in s["kernels"].items()}))
 
 
