@@ -124,6 +124,7 @@ struct Layout {
   int64_t N, H, V, Vp, Tv, Nc;
   size_t es;
   int32_t layout;   // BwdLayout
+  int32_t dh_splits;  // split-K slices of the dh contraction (1: none)
   bool wt_copy;     // dh reads the copy W^T [H][Vp]
   bool dw_copies;   // dW reads the copies h^T [H][Nc] and dz^T [Vp][Nc]
   // head
@@ -135,10 +136,30 @@ struct Layout {
   // forward
   size_t pz, pu, p2, zy, fwd_end;
   // backward
-  size_t wt, ht, dz, dzt, bwd_end;
+  size_t wt, ht, dz, dzt, dhp, bwd_end;
   // single-call forward+backward: forward partials and backward buffers at once
-  size_t f_pz, f_pu, f_p2, f_zy, f_wt, f_ht, f_dz, f_dd, f_dl, f_dzt, f_rs, fused_end;
+  size_t f_pz, f_pu, f_p2, f_zy, f_wt, f_ht, f_dz, f_dd, f_dl, f_dzt, f_rs, f_dhp, fused_end;
 };
+
+// Split-K slices of the dh contraction of a chunk of Nc rows: its grid has
+// ceil(Nc / 256) x ceil(H / 256) tiles, and with few of them (small chunks)
+// most of the 256 CUs would idle.  S slices of the vocabulary run as
+// S times the tiles, each 1/S as long; S in [1, 8] minimises
+// ceil(tiles S / 256) / S (the launch's rounds of one slice's length), the
+// smallest S on ties.  The partials are added in slice order afterwards.
+int32_t dh_splits(int64_t Nc, int64_t H) {
+  const int64_t tiles = cdiv(Nc, 256) * cdiv(H, 256);
+  int32_t best = 1;
+  double best_t = (double)cdiv(tiles, 256);
+  for (int32_t s = 2; s <= 8; ++s) {
+    const double t = (double)cdiv(tiles * s, 256) / s;
+    if (t < best_t - 1e-9) {
+      best_t = t;
+      best = s;
+    }
+  }
+  return best;
+}
 
 // fp32 inputs always take LAYOUT_COPIES (the transposing LDS load is bf16).
 Layout plan(const specloss_problem* p, const KindSet& k, int64_t Nc,
@@ -178,6 +199,9 @@ Layout plan(const specloss_problem* p, const KindSet& k, int64_t Nc,
   L.ht = take(L.dw_copies ? (size_t)L.H * Nc * L.es : 0);
   L.dz = take((size_t)Nc * L.Vp * L.es);
   L.dzt = take(L.dw_copies ? (size_t)L.Vp * Nc * L.es : 0);
+  L.dh_splits = dh_splits(Nc, L.H);
+  const size_t dhp_bytes = L.dh_splits > 1 ? (size_t)L.dh_splits * Nc * L.H * 4 : 0;
+  L.dhp = take(dhp_bytes);
   L.bwd_end = o;
   o = L.head_end;
   L.f_pz = take(2 * tile_cols);
@@ -191,6 +215,7 @@ Layout plan(const specloss_problem* p, const KindSet& k, int64_t Nc,
   L.f_dl = take(k.stage_log ? (size_t)Nc * L.Vp * L.es : 0);
   L.f_dzt = take(L.dw_copies ? (size_t)L.Vp * Nc * L.es : 0);
   L.f_rs = take(4 * (size_t)Nc * 4);
+  L.f_dhp = take(dhp_bytes);
   L.fused_end = o;
   return L;
 }
@@ -844,7 +869,8 @@ int launch_seed_for(const specloss_problem* p, const SavedView& sv, const float*
 // MN-major operand).
 int contract_dh(const specloss_problem* p, const Layout& L, int64_t Nc, const void* dz,
                 const void* wt, int64_t r0, int64_t rows, void* dhidden, int32_t dh_dtype,
-                Tracer& tr, hipStream_t stream, const float* rscale = nullptr) {
+                Tracer& tr, hipStream_t stream, const float* rscale = nullptr,
+                float* dhp = nullptr) {
   const bool bf16 = p->in_dtype == SPECLOSS_BF16;
   const int64_t H = L.H, V = L.V, Vp = L.Vp;
   const size_t dh_es = dh_dtype == SPECLOSS_BF16 ? 2 : 4;
@@ -863,13 +889,27 @@ int contract_dh(const specloss_problem* p, const Layout& L, int64_t Nc, const vo
   g.tiles_n = (int32_t)cdiv(H, 256);
   g.m_valid = (int32_t)rows;
   g.n_valid = (int32_t)H;
-  g.C = static_cast<char*>(dhidden) + (size_t)r0 * H * dh_es;
+  char* out = static_cast<char*>(dhidden) + (size_t)r0 * H * dh_es;
+  g.C = out;
   g.ldc = H;
   g.accumulate = 0;
   g.out_bf16 = dh_dtype == SPECLOSS_BF16;
   g.role = 0;
   g.rscale = rscale;
+  g.splits = 1;
+  if (L.dh_splits > 1 && dhp) {
+    // slices of K, fp32 partials in the workspace, added in slice order
+    g.splits = L.dh_splits;
+    g.k_split = (int32_t)round_up(cdiv(g.k_len, g.splits), 64);
+    while (g.splits > 1 && (int64_t)(g.splits - 1) * g.k_split >= g.k_len) --g.splits;
+    g.C = dhp;
+    g.out_bf16 = 0;
+    g.part_stride = (int64_t)rows * H;
+  }
   TRACED(tr, K_GEMM_DH, 2.0 * rows * H * V, launch_gemm(bf16, g, stream));
+  if (g.splits > 1)
+    TRACED(tr, K_SUM_PARTS, 4.0 * rows * H * (g.splits + 1),
+           launch_sum_parts(dhp, rows * H, g.splits, out, dh_dtype == SPECLOSS_BF16, stream));
   return SPECLOSS_OK;
 }
 
@@ -903,6 +943,7 @@ int contract_dW(const specloss_problem* p, const Layout& L, int64_t Nc, const vo
   g.accumulate = accumulate ? 1 : 0;
   g.out_bf16 = 0;
   g.role = 1;
+  g.splits = 1;
   TRACED(tr, K_GEMM_DW, 2.0 * rows * H * V, launch_gemm(bf16, g, stream));
   return SPECLOSS_OK;
 }
@@ -1001,7 +1042,9 @@ int bwd_recompute(const specloss_problem* p, const KindSet& k, const float* grad
     dl.ld_dzt = Nc;
     dl.vocab_offset = (int32_t)vocab_offset;
     TRACED(tr, K_DZ, (k.dual_bwd ? 4.0 : 2.0) * rows * H * V, launch_dz(bf16, k.dual_bwd, dl, stream));
-    if (dhidden) TRY(contract_dh(p, L, Nc, dz, wt, r0, rows, dhidden, dh_dtype, tr, stream));
+    if (dhidden)
+      TRY(contract_dh(p, L, Nc, dz, wt, r0, rows, dhidden, dh_dtype, tr, stream, nullptr,
+                      reinterpret_cast<float*>(ws + L.dhp)));
     if (dW)
       TRY(contract_dW(p, L, Nc, dz, dzt, ht, Nc, r0, rows, chunk > 0 || accumulate_dW, dW, tr,
                       stream));
@@ -1206,7 +1249,8 @@ int lmhead_loss_fwd_bwd(const specloss_problem* p, void* workspace, size_t ws_by
         TRACED(tr, K_TRANSPOSE_H, 2.0 * Nc * H * L.es,
                launch_transpose(bf16, hc, rows, H, ht, Nc, stream, rscale));
       if (dhidden)
-        TRY(contract_dh(p, L, Nc, dz, wt, r0, rows, dhidden, dh_dtype, tr, stream, rscale));
+        TRY(contract_dh(p, L, Nc, dz, wt, r0, rows, dhidden, dh_dtype, tr, stream, rscale,
+                        reinterpret_cast<float*>(ws + L.f_dhp)));
       if (dW)
         TRY(contract_dW(p, L, Nc, dz, dzt, ht, Nc, r0, rows, chunk > 0 || accumulate_dW, dW, tr,
                         stream));
@@ -1243,7 +1287,9 @@ int lmhead_loss_fwd_bwd(const specloss_problem* p, void* workspace, size_t ws_by
     const void* hc = offset_rows(p->hidden_states, r0, H, L.es);
     if (dW && L.dw_copies)
       TRACED(tr, K_TRANSPOSE_H, 2.0 * Nc * H * L.es, launch_transpose(bf16, hc, rows, H, ht, Nc, stream));
-    if (dhidden) TRY(contract_dh(p, L, Nc, dz, wt, r0, rows, dhidden, dh_dtype, tr, stream));
+    if (dhidden)
+      TRY(contract_dh(p, L, Nc, dz, wt, r0, rows, dhidden, dh_dtype, tr, stream, nullptr,
+                      reinterpret_cast<float*>(ws + L.f_dhp)));
     if (dW)
       TRY(contract_dW(p, L, Nc, dz, dzt, ht, Nc, r0, rows, chunk > 0 || accumulate_dW, dW, tr,
                       stream));

@@ -859,14 +859,36 @@ __global__ __launch_bounds__(128 * WNW, 1) void k_gemm(GemmLaunch a) {
                                                                : kHalfRows * kEpiStride;
   __shared__ __attribute__((aligned(16))) char smem[kSmem];
   int tm, tn;
-  if (!tile_of(a.tiles_m, a.tiles_n, kGroupM, tm, tn)) return;
+  if (!tile_of(a.tiles_m * a.splits, a.tiles_n, kGroupM, tm, tn)) return;
+  // split-K slice of this tile row: its K range and its partial output
+  const int split = tm / a.tiles_m;
+  tm -= split * a.tiles_m;
+  Operand<T> opA = as_op<T>(a.A), opB = as_op<T>(a.B);
+  int32_t k_len = a.k_len;
+  OutT* C = static_cast<OutT*>(a.C);
+  if (split > 0) {
+    const int64_t k0 = (int64_t)split * a.k_split;
+    if (kA_MN) {
+      opA.base += k0 * opA.ld;
+      opA.k_valid -= (int32_t)k0;
+    } else {
+      opA.base += k0;
+    }
+    if (kB_MN) {
+      opB.base += k0 * opB.ld;
+      opB.k_valid -= (int32_t)k0;
+    } else {
+      opB.base += k0;
+    }
+    k_len -= (int32_t)k0;
+    C += split * a.part_stride;
+  }
+  if (a.splits > 1 && k_len > a.k_split) k_len = a.k_split;
   f32x4_t acc[Cfg::FM][Cfg::FN];
   zero_acc<Cfg>(acc);
-  tile_mainloop<T, Cfg, kA_MN, kB_MN>(acc, as_op<T>(a.A), tm * Cfg::BM, as_op<T>(a.B),
-                                      tn * Cfg::BN, a.k_len, smem);
+  tile_mainloop<T, Cfg, kA_MN, kB_MN>(acc, opA, tm * Cfg::BM, opB, tn * Cfg::BN, k_len, smem);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / Cfg::WNW, wn = wave % Cfg::WNW;
-  OutT* C = static_cast<OutT*>(a.C);
   constexpr int kPieces = kHalfRows * 64;              // 16-byte pieces (4 values) per half
   constexpr int kPerThread = kPieces / Cfg::THREADS;
   constexpr int kBatch = 8;
@@ -1513,7 +1535,7 @@ constexpr int kGemmWNW = 4;
 template <int ROLE>
 static void launch_gemm_role(bool bf16, const GemmLaunch& a, hipStream_t s) {
   constexpr int W = kGemmWNW;
-  const dim3 grid(grid_for_tiles(a.tiles_m * a.tiles_n)), block(128 * W);
+  const dim3 grid(grid_for_tiles(a.tiles_m * a.splits * a.tiles_n)), block(128 * W);
   if (bf16 && a.lean) {
     if (a.out_bf16) hipLaunchKernelGGL((k_gemm<bf16_bits, bf16_bits, ROLE, true, 2>), grid, dim3(256), 0, s, a);
     else hipLaunchKernelGGL((k_gemm<bf16_bits, float, ROLE, true, 2>), grid, dim3(256), 0, s, a);
@@ -1527,6 +1549,9 @@ static void launch_gemm_role(bool bf16, const GemmLaunch& a, hipStream_t s) {
 }
 
 hipError_t launch_gemm(bool bf16, const GemmLaunch& a, hipStream_t s) {
+  if (a.splits < 1 || (a.splits > 1 && (a.k_split <= 0 || a.k_split % 64 != 0 ||
+                                        (int64_t)(a.splits - 1) * a.k_split >= a.k_len)))
+    return hipErrorInvalidValue;
   if (a.role == 0) launch_gemm_role<0>(bf16, a, s);
   else launch_gemm_role<1>(bf16, a, s);
   return hipGetLastError();

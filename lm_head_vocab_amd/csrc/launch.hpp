@@ -153,6 +153,11 @@ struct GemmLaunch {
   int role;  // 0: dh, 1: dW (separate kernel names in profiles)
   int lean;  // bf16 only: B (and for dW also A) are MN-major, read without copies
   const float* rscale;  // per output row m, or null: C = rscale[m] * (A B^T) (no accumulate)
+  // split K: `splits` (>= 1) slices of k_split along K (the last one shorter);
+  // slice s writes its partial product to C + s * part_stride elements.
+  // The grid covers tiles_m * splits tile rows.
+  int32_t splits, k_split;
+  int64_t part_stride;
 };
 hipError_t launch_gemm(bool bf16, const GemmLaunch& a, hipStream_t s);
 

@@ -530,12 +530,30 @@ def test_backward_without_transposed_copies(case):
     import lm_head_vocab_amd as L
     dev = to_device(p)
     probe = make_run(p, dev, max_chunk_rows=256)
-    full = probe.workspace.numel()
-    Vp = -(-p.vocab // 256) * 256
-    copies = p.hidden_dim * Vp * 2 + p.hidden_dim * 256 * 2 + Vp * 256 * 2
+    # the smallest workspace that runs the backward at 256-row chunks: it
+    # holds none of the transposed copies
+    call = L.binding.CALL_FWD_BWD if single else L.binding.CALL_BWD
+    probe.problem.flags = 0  # the layout chosen by workspace size
+
+    def rows_at(ws):
+        try:
+            return L.binding.lmhead_loss_chunk(probe.problem, ws, call)[0]
+        except L.binding.SpecLossError:
+            return 0
+
+    lo, hi = 1, probe.workspace_bytes
+    while lo < hi:
+        mid = (lo + hi) // 2
+        if rows_at(mid) >= 256:
+            hi = mid
+        else:
+            lo = mid + 1
+    assert L.binding.lmhead_loss_chunk(probe.problem, lo, call) == (256, "no_copies")
+    if not single:
+        assert L.binding.lmhead_loss_chunk(probe.problem, lo, L.binding.CALL_FWD)[0] >= 256
     del probe
     full_parity(p, max_chunk_rows=256, tag=f"lean-{case}", single_call=single,
-                workspace_bytes=full - copies, expect_copies=False)
+                workspace_bytes=lo, expect_copies=False)
     # each layout forced: every copy with one chunk of all rows, and at
     # 256-row chunks the dW copies without W^T, and no copy
     full_parity(p, tag=f"copies-{case}", single_call=single, expect_copies=True,
