@@ -34,6 +34,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="ce_bf16_8b")
+    ap.add_argument("--weights", default=None,
+                    help="loss weights replacing the workload's, e.g. kl_div=1,ce=0.2 "
+                         "(the workload's inputs are kept)")
     ap.add_argument("--chunk", type=int, default=0,
                     help="max rows per chunk (0: the library's default streaming policy)")
     ap.add_argument("--shards", type=int, default=1,
@@ -103,6 +106,11 @@ def main():
 
     t0 = time.time()
     prob = synthetic.make_problem(args.workload)
+    if args.weights:
+        prob.weights = {k: float(v) for k, v in (kv.split("=") for kv in args.weights.split(","))}
+        if any(k != "ce_label" for k in prob.weights) and prob.target_hidden is None:
+            print("--weights: divergences need a workload with a target side", file=sys.stderr)
+            sys.exit(2)
     gen_s = time.time() - t0
     N, H, V = prob.n_rows, prob.hidden_dim, prob.vocab
 

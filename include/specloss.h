@@ -100,8 +100,10 @@ enum {
   SPECLOSS_SAVED_LSE_Q = 0,     /* fp32: logsumexp of the draft logits z */
   SPECLOSS_SAVED_LSE_P = 1,     /* fp32: logsumexp of the target logits u (0 without a target) */
   SPECLOSS_SAVED_Y_ARG = 3,     /* int32: argmax of u, lowest index on ties (-1 without a target) */
-  SPECLOSS_SAVED_ALPHA = 4,     /* fp32: alpha = sum_v min(p_v, q_v), written when a
-                                   divergence kind is on ("Available Losses", tv) */
+  SPECLOSS_SAVED_ALPHA = 4,     /* fp32: alpha = sum_v min(p_v, q_v) ("Available Losses",
+                                   tv), written when tv, nla, lk_hybrid or jsd is on;
+                                   1 otherwise (with kl_div and rkl as the only
+                                   divergences no sum of min(p, q) is formed) */
   SPECLOSS_SAVED_VALID = 8,     /* int32: 1 on valid rows, 0 on masked or bad rows */
   SPECLOSS_SAVED_FLATNESS = 9,  /* fp32: flatness of the target distribution,
                                    cos(p, uniform) = 1 / (sqrt(V) |p|_2), in [1/sqrt(V), 1]
@@ -215,6 +217,11 @@ int specloss_saved_offset(int64_t n_rows, int32_t field, size_t* offset);
  *                    out-of-range label or target row; treated as masked).
  *   reduced   [1+K]  fp32 or NULL: sum(loss)/n_valid, then sum(L_k)/n_valid
  *                    for each kind (0 when n_valid == 0).
+ * The divergences take a second sweep over the vocabulary after the
+ * logsumexps, except when kl_div and rkl are the only ones and every row has
+ * a target row of its own (no target_row map, or n_target_rows >= n_rows):
+ * then one sweep computes both sides of a row together and forms
+ * KL = E[log-ratio] - lse + lse from the same tiles.
  */
 int lmhead_loss_fwd(const specloss_problem* p, void* workspace, size_t ws_bytes, float* loss,
                     float* term_loss, float* lse_q, void* saved, int64_t* counts, float* reduced,

@@ -43,6 +43,10 @@ struct KindSet {
   bool dual_bwd = false;
   bool stage_div = false;  // single call: pass 2 stages q and q - p (every divergence)
   bool stage_log = false;  // ... and log q - log p (rkl, jsd)
+  // the only sums needed are the Kullback-Leibler ones: the two-call forward
+  // takes them from a dual pass 1 (no second sweep) when each row has its
+  // own target row
+  bool ratio_only = false;
   uint32_t need = 0;    // SUM_* bits
 };
 
@@ -58,8 +62,11 @@ KindSet kinds_of(const float* w) {
   if (on(SPECLOSS_JSD)) k.need |= SUM_JSD | SUM_EQG;
   if (on(SPECLOSS_TV) || on(SPECLOSS_NLA)) k.need |= SUM_ALPHA | SUM_S;
   if (on(SPECLOSS_LK_HYBRID)) k.need |= SUM_ALPHA | SUM_S | SUM_KL;
-  if (k.need) k.need |= SUM_ALPHA;  // alpha is reported whenever a second sweep runs
+  // alpha is reported whenever a kind other than the Kullback-Leibler ones needs a
+  // second sweep
+  if (k.need & ~(SUM_KL | SUM_RKL)) k.need |= SUM_ALPHA;
   k.pass2 = k.need != 0;
+  k.ratio_only = k.pass2 && (k.need & ~(SUM_KL | SUM_RKL)) == 0;
   k.dual_bwd = (k.active & ~((1u << SPECLOSS_CE_LABEL) | (1u << SPECLOSS_CE_ARGMAX_P))) != 0;
   k.stage_div = k.dual_bwd;
   k.stage_log = on(SPECLOSS_RKL) || on(SPECLOSS_JSD);
@@ -373,13 +380,14 @@ GemmOperand target_operand(const specloss_problem* p, int64_t r0, int64_t rows, 
 enum KernelId : int32_t {
   K_VALIDITY, K_STATS_Q, K_STATS_P, K_COMBINE1, K_ROWDOT, K_DIV, K_COMBINE2, K_REDUCE, K_COPY,
   K_SEED, K_TRANSPOSE_W, K_TRANSPOSE_H, K_DZ, K_GEMM_DH, K_GEMM_DW, K_STATS_STAGE, K_DZ_STAGE,
-  K_DIV_STAGE, K_DZ_DIV, K_TILE_SUM, K_SUM_PARTS, K_TARGET_GATHER, K_STAGE_FIX, K_NUM_IDS
+  K_DIV_STAGE, K_DZ_DIV, K_TILE_SUM, K_SUM_PARTS, K_TARGET_GATHER, K_STAGE_FIX, K_STATS_DUAL,
+  K_NUM_IDS
 };
 const char* const kKernelNames[K_NUM_IDS] = {
     "validity", "stats_q", "stats_p", "combine1", "rowdot", "div", "combine2", "reduce",
     "copy_lse", "seed", "transpose_W", "transpose_h", "dz", "gemm_dh", "gemm_dW",
     "stats_stage", "dz_stage", "div_stage", "dz_div", "tile_sum", "sum_partials",
-    "target_gather", "stage_fix"};
+    "target_gather", "stage_fix", "stats_dual"};
 
 // Brackets launches with the trace's events when the problem carries one.
 struct Tracer {
@@ -544,6 +552,38 @@ int launch_pass1(const specloss_problem* p, const KindSet& k, const Layout& L, c
   return SPECLOSS_OK;
 }
 
+// Pass 1 of both sides with the log-ratio sums (k_stats_dual), for problems
+// whose only divergences are kl_div and rkl: the per-tile log-ratio partials
+// go to the rows of b.p2 that hold the sums they replace (SUM_KL: pa, SUM_RKL:
+// pr), and the combine writes the merged divergences into tile row 0 there.
+int launch_pass1_dual(const specloss_problem* p, const Layout& L, const FwdBufs& b, int64_t r0,
+                      int64_t rows, Tracer& tr, hipStream_t stream) {
+  const bool bf16 = p->in_dtype == SPECLOSS_BF16;
+  const int64_t H = L.H, Nc = b.Nc;
+  const int64_t tile_cols = L.Tv * Nc;
+  DualStatsLaunch d{};
+  d.Az = op(p->W, H, p->vocab);
+  d.Bz = op(offset_rows(p->hidden_states, r0, H, L.es), H, rows);
+  d.Au = op(p->W_t, H, p->vocab);
+  d.Bu = target_operand(p, r0, rows, L.es);
+  d.k_len = (int32_t)H;
+  d.vocab = (int32_t)p->vocab;
+  d.tiles_m = (int32_t)L.Tv;
+  d.tiles_n = (int32_t)cdiv(rows, 128);
+  d.ncols = (int32_t)rows;
+  d.ldp = (int32_t)Nc;
+  d.pm_z = b.pz;
+  d.ps_z = b.pz + tile_cols;
+  d.pr_z = b.p2 + 3 * tile_cols;
+  d.pm_u = b.pu;
+  d.ps_u = b.pu + tile_cols;
+  d.pi_u = reinterpret_cast<int32_t*>(b.pu + 2 * tile_cols);
+  d.pq_u = b.pu + 3 * tile_cols;
+  d.pa_u = b.p2 + 2 * tile_cols;
+  TRACED(tr, K_STATS_DUAL, 4.0 * rows * H * p->vocab, launch_stats_dual(bf16, d, stream));
+  return SPECLOSS_OK;
+}
+
 // Pass-2 divergence sums of chunk rows [r0, r0 + rows) into b.p2, with the
 // final logsumexps in `sv`; stage_q / stage_d as for fwd_chunk (or null).
 int launch_pass2(const specloss_problem* p, const KindSet& k, const Layout& L, const FwdBufs& b,
@@ -584,7 +624,13 @@ int fwd_chunk(const specloss_problem* p, const KindSet& k, const Layout& L, cons
   const int64_t H = L.H, Nc = b.Nc;
   const int64_t tile_cols = L.Tv * Nc;
   const bool own_target = k.target && !L.shared_target;
-  {
+  // kl_div / rkl as the only divergences of a forward without staging: both
+  // sides in one pass that also yields the divergences
+  const bool dual = k.ratio_only && own_target && !stage && !stage_d;
+  if (dual) {
+    const int rc = launch_pass1_dual(p, L, b, r0, rows, tr, stream);
+    if (rc) return rc;
+  } else {
     const int rc = launch_pass1(p, k, L, b, r0, rows, stage_d ? nullptr : stage, tr, stream,
                                 !own_target);
     if (rc) return rc;
@@ -607,7 +653,14 @@ int fwd_chunk(const specloss_problem* p, const KindSet& k, const Layout& L, cons
   c1.lse_p = sv.lse_p + r0;
   c1.y_arg = sv.y_arg + r0;
   c1.flat = sv.flat + r0;
-  TRACED(tr, K_COMBINE1, (own_target ? 6.0 : 2.0) * L.Tv * rows * 4, launch_combine1(c1, stream));
+  if (dual) {
+    c1.pa_u = b.p2 + 2 * tile_cols;
+    c1.pr_z = b.p2 + 3 * tile_cols;
+    c1.kl_out = (k.need & SUM_KL) ? b.p2 + 2 * tile_cols : nullptr;
+    c1.rkl_out = (k.need & SUM_RKL) ? b.p2 + 3 * tile_cols : nullptr;
+  }
+  TRACED(tr, K_COMBINE1, (own_target ? (dual ? 8.0 : 6.0) : 2.0) * L.Tv * rows * 4,
+         launch_combine1(c1, stream));
   if (L.shared_target) {
     const char* tb = reinterpret_cast<const char*>(b.tstat);
     const size_t fs = align_up((size_t)L.Nt * 4, kAlign);
@@ -642,13 +695,13 @@ int fwd_chunk(const specloss_problem* p, const KindSet& k, const Layout& L, cons
            launch_rowdot(bf16, rd, stream));
   }
 
-  if (k.pass2) {
+  if (k.pass2 && !dual) {
     const int rc = launch_pass2(p, k, L, b, sv, r0, rows, stage, stage_d, tr, stream, stage_l);
     if (rc) return rc;
   }
 
   Combine2Launch c2{};
-  c2.tiles_m = (int32_t)L.Tv;
+  c2.tiles_m = dual ? 1 : (int32_t)L.Tv;  // dual: the divergences themselves, in tile row 0
   c2.ncols = (int32_t)rows;
   c2.ldp = (int32_t)Nc;
   c2.part = b.p2;
@@ -667,7 +720,7 @@ int fwd_chunk(const specloss_problem* p, const KindSet& k, const Layout& L, cons
   c2.S = sv.S + r0;
   c2.rkl = sv.rkl + r0;
   c2.eqg = sv.eqg + r0;
-  TRACED(tr, K_COMBINE2, (double)rows * 4 * (2 + __builtin_popcount(k.need) * L.Tv),
+  TRACED(tr, K_COMBINE2, (double)rows * 4 * (2 + __builtin_popcount(k.need) * c2.tiles_m),
          launch_combine2(c2, stream));
   return SPECLOSS_OK;
 }

@@ -310,6 +310,135 @@ __global__ __launch_bounds__(kThreads, 1) void k_stats(StatsLaunch a) {
   }
 }
 
+// (max, sum exp(x - max), sum exp(x - max) y) triples: y-sums merge as the sums do
+__device__ __forceinline__ void lse_merge_x(float& m, float& s, float& x, float m2, float s2,
+                                            float x2) {
+  const float mn = fmaxf(m, m2);
+  if (mn == -INFINITY) return;
+  const float a = fast_exp2((m - mn) * kLog2e), b = fast_exp2((m2 - mn) * kLog2e);
+  s = s * a + s2 * b;
+  x = x * a + x2 * b;
+  m = mn;
+}
+
+// Pass 1 of both sides of a row at once: the draft tile z and the target tile
+// u are both kept in registers (256 x 128 tiles, as in pass 2), so besides
+// the statistics of k_stats for each side the tile also yields the log-ratio
+// sums of the two Kullback-Leibler divergences relative to the tile maxima:
+// pa = sum exp(u - m_u) (u - z) and pr = sum exp(z - m_z) (z - u).
+template <typename T>
+__global__ __launch_bounds__(kThreads, 1) void k_stats_dual(DualStatsLaunch a) {
+  using Cfg = TileCfg<T, 256, 128>;
+  __shared__ __attribute__((aligned(16))) char smem[Cfg::LDS_BYTES];
+  int tm, tn;
+  if (!tile_of(a.tiles_m, a.tiles_n, kGroupM, tm, tn)) return;
+
+  f32x4_t az[Cfg::FM][Cfg::FN], au[Cfg::FM][Cfg::FN];
+  zero_acc<Cfg>(az);
+  zero_acc<Cfg>(au);
+  tile_mainloop<T, Cfg>(az, as_op<T>(a.Az), tm * Cfg::BM, as_op<T>(a.Bz), tn * Cfg::BN, a.k_len,
+                        smem);
+  tile_mainloop<T, Cfg>(au, as_op<T>(a.Au), tm * Cfg::BM, as_op<T>(a.Bu), tn * Cfg::BN, a.k_len,
+                        smem);
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int v_base = tm * Cfg::BM + wm * Cfg::WM;
+  const bool tail = tm * Cfg::BM + Cfg::BM > a.vocab;
+
+  // per column: m_z, s_z, pr, m_u, s_u, argmax, q_u, pa
+  constexpr int NV = 8;
+  float val[Cfg::FN][NV];
+#pragma unroll
+  for (int j = 0; j < Cfg::FN; ++j) {
+    float mz = -INFINITY, mu = -INFINITY;
+    int iu = 0x7fffffff;
+#pragma unroll
+    for (int i = 0; i < Cfg::FM; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int v = v_base + i * kFrag + frag_row(r, lane);
+        if (tail && v >= a.vocab) continue;
+        mz = fmaxf(mz, az[i][j][r]);
+        if (au[i][j][r] > mu) { mu = au[i][j][r]; iu = v; }  // strict: lowest index
+      }
+    const float Mz = col_max(mz), Mu = col_max(mu);
+    float sz = 0.0f, pr = 0.0f, su = 0.0f, qu = 0.0f, pa = 0.0f;
+    if (Mz != -INFINITY) {  // then Mu is finite too: the same entries are valid
+      const float mzb = Mz * kLog2e, mub = Mu * kLog2e;
+#pragma unroll
+      for (int i = 0; i < Cfg::FM; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int v = v_base + i * kFrag + frag_row(r, lane);
+          if (tail && v >= a.vocab) continue;
+          const float z = az[i][j][r], u = au[i][j][r], d = u - z;
+          const float ez = fast_exp2(fmaf(z, kLog2e, -mzb));
+          const float eu = fast_exp2(fmaf(u, kLog2e, -mub));
+          sz += ez;
+          pr = fmaf(ez, -d, pr);
+          su += eu;
+          qu = fmaf(eu, eu, qu);
+          pa = fmaf(eu, d, pa);
+        }
+    }
+    int cand = (mu == Mu) ? iu : 0x7fffffff;
+    cand = min(cand, __shfl_xor(cand, 16));
+    cand = min(cand, __shfl_xor(cand, 32));
+    val[j][0] = Mz;
+    val[j][1] = col_sum(sz, lane);
+    val[j][2] = col_sum(pr, lane);
+    val[j][3] = Mu;
+    val[j][4] = col_sum(su, lane);
+    val[j][5] = __int_as_float(cand);
+    val[j][6] = col_sum(qu, lane);
+    val[j][7] = col_sum(pa, lane);
+  }
+
+  // the two wave rows (wm) share token columns: wm = 1 hands its values over
+  float* red = reinterpret_cast<float*>(smem);  // [BN][NV]
+  if (wm == 1 && lane < kFrag) {
+#pragma unroll
+    for (int j = 0; j < Cfg::FN; ++j) {
+      const int c = wn * Cfg::WN + j * kFrag + lane;
+#pragma unroll
+      for (int f = 0; f < NV; ++f) red[c * NV + f] = val[j][f];
+    }
+  }
+  __syncthreads();
+  if (wm == 0 && lane < kFrag) {
+#pragma unroll
+    for (int j = 0; j < Cfg::FN; ++j) {
+      const int c = wn * Cfg::WN + j * kFrag + lane;
+      const int col = tn * Cfg::BN + c;
+      if (col >= a.ncols) continue;
+      const float* o2 = red + c * NV;
+      float mz = val[j][0], sz = val[j][1], pr = val[j][2];
+      lse_merge_x(mz, sz, pr, o2[0], o2[1], o2[2]);
+      float mu = val[j][3], su = val[j][4], qu = val[j][6], pa = val[j][7];
+      int id = __float_as_int(val[j][5]);
+      const int i2 = __float_as_int(o2[5]);
+      id = (o2[3] > mu) ? i2 : ((o2[3] == mu) ? min(id, i2) : id);
+      {
+        // the pair (s, q) and the pair (s, pa) share the rescaling of s
+        float s1 = su, q1 = qu, m1 = mu;
+        lse_merge_sq(m1, s1, q1, o2[3], o2[4], o2[6]);
+        lse_merge_x(mu, su, pa, o2[3], o2[4], o2[7]);
+        qu = q1;
+      }
+      const int64_t o = (int64_t)tm * a.ldp + col;
+      a.pm_z[o] = mz;
+      a.ps_z[o] = sz;
+      a.pr_z[o] = pr;
+      a.pm_u[o] = mu;
+      a.ps_u[o] = su;
+      a.pi_u[o] = id;
+      a.pq_u[o] = qu;
+      a.pa_u[o] = pa;
+    }
+  }
+}
+
 // ============================================================================
 // pass 1 with staging: the tile's column maxima are merged across the two
 // half-waves and the two wave rows first, then e = exp(z - m_tile) is summed
@@ -1038,64 +1167,76 @@ __global__ __launch_bounds__(256) void k_rowdot(RowdotLaunch a) {
 // kCombine1Threads / 32 segments (merged in segment order)
 constexpr int kCombine1Threads = 1024;
 
+// px (may be null): per-tile sums relative to the tile maximum, merged into x
+// as s is
 __device__ __forceinline__ void seg_lse(const float* pm, const float* ps, const float* pq,
-                                        int64_t ldp, int c, int t0, int t1, float& m, float& s,
-                                        float& q, int& best) {
+                                        const float* px, int64_t ldp, int c, int t0, int t1,
+                                        float& m, float& s, float& q, float& x, int& best) {
   m = -INFINITY;
   best = -1;
   for (int t = t0; t < t1; ++t) {
-    const float x = pm[(int64_t)t * ldp + c];
-    if (x > m) { m = x; best = t; }
+    const float v = pm[(int64_t)t * ldp + c];
+    if (v > m) { m = v; best = t; }
   }
   s = 0.0f;
   q = 0.0f;
+  x = 0.0f;
   if (m != -INFINITY)
     for (int t = t0; t < t1; ++t) {
       const int64_t o = (int64_t)t * ldp + c;
       const float f = fast_exp2((pm[o] - m) * kLog2e);
       s += ps[o] * f;
       if (pq) q += pq[o] * f * f;
+      if (px) x += px[o] * f;
     }
 }
 
 __global__ __launch_bounds__(kCombine1Threads) void k_combine1(Combine1Launch a) {
   constexpr int SEG = kCombine1Threads / 32, RPB = 32;
-  __shared__ float sm[2][SEG][RPB], ss[2][SEG][RPB], sq[SEG][RPB];
+  __shared__ float sm[2][SEG][RPB], ss[2][SEG][RPB], sx[2][SEG][RPB], sq[SEG][RPB];
   __shared__ int sb[SEG][RPB];
   const int rr = threadIdx.x % RPB, seg = threadIdx.x / RPB;
   const int c = blockIdx.x * RPB + rr;
   const int per = (a.tiles_m + SEG - 1) / SEG;
   const int t0 = min(a.tiles_m, seg * per), t1 = min(a.tiles_m, t0 + per);
+  const bool ratio = a.pa_u != nullptr;  // log-ratio partials of the dual pass 1
   if (c < a.ncols) {
-    float m, s, q;
+    float m, s, q, x;
     int best;
     if (a.pm_z) {
-      seg_lse(a.pm_z, a.ps_z, nullptr, a.ldp, c, t0, t1, m, s, q, best);
+      seg_lse(a.pm_z, a.ps_z, nullptr, a.pr_z, a.ldp, c, t0, t1, m, s, q, x, best);
       sm[0][seg][rr] = m;
       ss[0][seg][rr] = s;
+      sx[0][seg][rr] = x;
     }
     if (a.pm_u) {
-      seg_lse(a.pm_u, a.ps_u, a.pq_u, a.ldp, c, t0, t1, m, s, q, best);
+      seg_lse(a.pm_u, a.ps_u, a.pq_u, a.pa_u, a.ldp, c, t0, t1, m, s, q, x, best);
       sm[1][seg][rr] = m;
       ss[1][seg][rr] = s;
+      sx[1][seg][rr] = x;
       sq[seg][rr] = q;
       sb[seg][rr] = best;
     }
   }
   __syncthreads();
   if (seg != 0 || c >= a.ncols) return;
+  float lse_side[2] = {0.0f, 0.0f}, ex_side[2] = {0.0f, 0.0f};
   for (int side = a.pm_z ? 0 : 1; side < (a.pm_u ? 2 : 1); ++side) {
     float m = -INFINITY;
     int bseg = 0;
     for (int g = 0; g < SEG; ++g)
       if (sm[side][g][rr] > m) { m = sm[side][g][rr]; bseg = g; }
-    float s = 0.0f, q = 0.0f;
+    float s = 0.0f, q = 0.0f, x = 0.0f;
     for (int g = 0; g < SEG; ++g)
       if (sm[side][g][rr] != -INFINITY) {
         const float f = fast_exp2((sm[side][g][rr] - m) * kLog2e);
         s += ss[side][g][rr] * f;
+        if (ratio) x += sx[side][g][rr] * f;
         if (side == 1) q += sq[g][rr] * f * f;
       }
+    // expectation of the side's log-ratio under its own distribution:
+    // E_q[z - u] (side 0), E_p[u - z] (side 1)
+    if (ratio) ex_side[side] = x / s;
     const int bt_best = side == 1 ? sb[bseg][rr] : -1;
     if (a.raw_m[0]) {
       // a vocabulary shard's record: the merged partials themselves
@@ -1108,6 +1249,7 @@ __global__ __launch_bounds__(kCombine1Threads) void k_combine1(Combine1Launch a)
       continue;
     }
     const float lse = m + logf(s);
+    lse_side[side] = lse;
     if (side == 0) {
       a.lse_q[c] = lse;
       if (a.row_max) a.row_max[c] = m;
@@ -1123,6 +1265,12 @@ __global__ __launch_bounds__(kCombine1Threads) void k_combine1(Combine1Launch a)
     a.lse_p[c] = 0.0f;
     a.y_arg[c] = -1;
     a.flat[c] = 0.0f;
+  }
+  if (ratio) {
+    // KL(p||q) = E_p[u - z] - lse_p + lse_q, KL(q||p) = E_q[z - u] - lse_q + lse_p
+    const float dl = lse_side[1] - lse_side[0];
+    if (a.kl_out) a.kl_out[c] = ex_side[1] - dl;
+    if (a.rkl_out) a.rkl_out[c] = ex_side[0] + dl;
   }
 }
 
@@ -1496,6 +1644,15 @@ hipError_t launch_dz_stage(bool bf16, const DzStageLaunch& a, hipStream_t s) {
     else if (a.dd) hipLaunchKernelGGL((k_dz_stage<float, true, false>), grid, block, 0, s, a);
     else hipLaunchKernelGGL((k_dz_stage<float, false, false>), grid, block, 0, s, a);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_stats_dual(bool bf16, const DualStatsLaunch& a, hipStream_t s) {
+  const dim3 grid(grid_for_tiles(a.tiles_m * a.tiles_n)), block(kThreads);
+  if (bf16)
+    hipLaunchKernelGGL(k_stats_dual<bf16_bits>, grid, block, 0, s, a);
+  else
+    hipLaunchKernelGGL(k_stats_dual<float>, grid, block, 0, s, a);
   return hipGetLastError();
 }
 

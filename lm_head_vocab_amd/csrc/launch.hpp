@@ -59,6 +59,27 @@ struct StatsLaunch {
 // target: the variant for the target logits u (argmax and e^2 sums as well)
 hipError_t launch_stats(bool bf16, bool target, const StatsLaunch& a, hipStream_t s);
 
+// pass 1 of both sides at once (draft z = W h and target u = W_t g of the
+// same rows, 256 x 128 tiles): the per-tile statistics of launch_stats for
+// each side, plus, relative to the same tile maxima, the unnormalised
+// expectations of the log-ratio pa_u = sum_v exp(u_v - m_u) (u_v - z_v) and
+// pr_z = sum_v exp(z_v - m_z) (z_v - u_v), from which the combine forms
+// KL(p||q) = pa_u / s_u - lse_p + lse_q and KL(q||p) = pr_z / s_z - lse_q +
+// lse_p without a second sweep.
+struct DualStatsLaunch {
+  GemmOperand Az, Bz, Au, Bu;
+  int32_t k_len, vocab, tiles_m, tiles_n, ncols, ldp;
+  float* pm_z;
+  float* ps_z;
+  float* pr_z;
+  float* pm_u;
+  float* ps_u;
+  int32_t* pi_u;
+  float* pq_u;
+  float* pa_u;
+};
+hipError_t launch_stats_dual(bool bf16, const DualStatsLaunch& a, hipStream_t s);
+
 // pass 1 for the single-call forward+backward: also stores staged values of
 // every (row, vocab) into `stage` ([cap][Vp], row-major) and, when stage_t is
 // set, transposed into stage_t ([Vp][cap]).  Without `ref` a row's values are
@@ -210,6 +231,12 @@ struct Combine1Launch {
   float* flat;
   float* row_max;        // chunk-local max of z per row, or null
   int32_t target_absent; // no target in the problem: write its no-target values
+  // log-ratio partials of launch_stats_dual (or null): the merged KL(p||q)
+  // and KL(q||p) go to kl_out and rkl_out (chunk-local)
+  const float* pa_u;
+  const float* pr_z;
+  float* kl_out;
+  float* rkl_out;
   // record mode (raw_m[0] != null): write the merged partials of this call's
   // tiles instead of the final values: m and sum-exp per side, e^2 sum and
   // argmax (plus idx_offset) of the target side

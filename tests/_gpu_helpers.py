@@ -161,7 +161,8 @@ def apply_moved_labels(prob, rows, moved, seed, rdh=None, rdW=None, dW_rows=None
 
 
 def full_parity(prob, *, max_chunk_rows=0, check_grads=True, tag="", single_call=False,
-                shards=None, workspace_bytes=None, expect_copies=None, flags=None):
+                shards=None, workspace_bytes=None, expect_copies=None, flags=None,
+                expect_kernels=None):
     """Run fwd (+bwd with the mean seed) on the GPU and compare every output with the oracle.
 
     single_call: use lmhead_loss_fwd_bwd instead of the two calls.
@@ -173,6 +174,8 @@ def full_parity(prob, *, max_chunk_rows=0, check_grads=True, tag="", single_call
     flags: backward layout flags; by default the transposed copies are forced
     (FLAG_COPIES) so chunked cases exercise that path, except when
     workspace_bytes is given (then the library chooses).
+    expect_kernels: (present, absent) kernel names the trace of the calls must
+    and must not show.
     """
     if flags is None:
         flags = 0 if workspace_bytes is not None else L.binding.FLAG_COPIES
@@ -190,7 +193,7 @@ def full_parity(prob, *, max_chunk_rows=0, check_grads=True, tag="", single_call
         run = make_run(prob, dev, max_chunk_rows=max_chunk_rows, workspace_bytes=workspace_bytes,
                        flags=flags)
     trace = None
-    if expect_copies is not None:
+    if expect_copies is not None or expect_kernels is not None:
         trace = L.binding.Trace(capacity=4096)
         trace.attach(run.problem)
     gm = torch.ones(1, dtype=torch.float32, device="cuda")
@@ -224,10 +227,13 @@ def full_parity(prob, *, max_chunk_rows=0, check_grads=True, tag="", single_call
         check_tokens(run.term[L.KINDS.index(k)].cpu().numpy(), ref.terms[k], f"term {k}")
     lse = run.lse_q.cpu().numpy()
     assert np.allclose(lse[ref.valid], ref.lse_q[ref.valid], rtol=1e-5, atol=1e-4)
-    if ref.alpha is not None and any(k in ("tv", "nla", "lk_hybrid", "kl_div", "rkl", "jsd")
+    if ref.alpha is not None and any(k in ("tv", "nla", "lk_hybrid", "jsd")
                                      for k in prob.weights):
         alpha = run.saved_field(4).cpu().numpy()
         assert np.allclose(alpha[ref.valid], ref.alpha[ref.valid], atol=1e-4)
+    elif any(k in ("kl_div", "rkl") for k in prob.weights):
+        # only the Kullback-Leibler divergences: no sum of min(p, q) is formed
+        assert np.all(run.saved_field(4).cpu().numpy()[ref.valid] == 1.0)
     if "ce" in prob.weights:
         y = run.saved_field(3, torch.int32).cpu().numpy()
         check_argmax(y, prob, np.arange(prob.n_rows), ref.valid)
@@ -252,9 +258,14 @@ def full_parity(prob, *, max_chunk_rows=0, check_grads=True, tag="", single_call
         names = {name for name, _, _ in trace.read()}
         run.problem.trace = None
         trace.close()
-        lay = {True: "copies", False: "no_copies"}.get(expect_copies, expect_copies)
-        want_wt, want_ht = {"copies": (True, True), "no_weight_copy": (False, True),
-                            "no_copies": (False, False)}[lay]
-        assert "gemm_dh" in names, names
-        assert ("transpose_W" in names) == want_wt and ("transpose_h" in names) == want_ht, names
+        if expect_kernels is not None:
+            present, absent = expect_kernels
+            assert set(present) <= names and not (set(absent) & names), names
+        if expect_copies is not None:
+            lay = {True: "copies", False: "no_copies"}.get(expect_copies, expect_copies)
+            want_wt, want_ht = {"copies": (True, True), "no_weight_copy": (False, True),
+                                "no_copies": (False, False)}[lay]
+            assert "gemm_dh" in names, names
+            assert (("transpose_W" in names) == want_wt
+                    and ("transpose_h" in names) == want_ht), names
     return out

@@ -99,7 +99,7 @@ def test_full_size_sampled(name, single):
     for k in prob.weights:
         got = run.term[L.KINDS.index(k)].cpu().numpy()[rows]
         check_tokens(got, ref.terms[k], f"term {k}")
-    if ref.alpha is not None and any(k != "ce" and k != "ce_label" for k in prob.weights):
+    if ref.alpha is not None and any(k in ("tv", "nla", "lk_hybrid", "jsd") for k in prob.weights):
         alpha = run.saved_field(4).cpu().numpy()[rows]
         assert np.allclose(alpha[ref.valid], ref.alpha[ref.valid], atol=1e-4)
     if ref.flat is not None:

@@ -84,6 +84,39 @@ def test_weighted_mix_all_kinds():
     full_parity(p, tag="mix")
 
 
+@pytest.mark.parametrize("case", ["kl", "rkl", "mix", "identical"])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_kl_forward_in_one_sweep(case, dtype):
+    """With kl_div and rkl as the only divergences (each row with a target row
+    of its own), the two-call forward takes both divergences from one pass
+    over both sides (no second sweep, no separate target pass): several
+    vocabulary tiles with a ragged tail, 256-row chunks with a ragged last
+    one, masked rows, against the oracle; the backward then reads the KL(q||p)
+    that pass saved.  Identical distributions give KL = 0."""
+    weights = {"kl": {"kl_div": 1.0}, "rkl": {"rkl": 1.0}, "identical": {"kl_div": 1.0, "rkl": 1.0},
+               "mix": {"kl_div": 0.5, "rkl": 0.7, "ce": 0.2, "ce_label": 0.3}}[case]
+    p = synthetic.make_problem("lk_hybrid_bf16_8b", n_rows=700, hidden_dim=192, vocab=1500,
+                               weights=weights)
+    rng = np.random.default_rng(17)
+    p.labels = rng.integers(0, p.vocab, p.n_rows).astype(np.int32)
+    p.labels[::13] = -100
+    p.mask = (np.arange(p.n_rows) % 9 != 4).astype(np.uint8)
+    if case == "identical":
+        p.W_t = p.W.copy()
+        p.target_hidden = p.hidden.copy()
+    if dtype == "f32":
+        p.dtype = "f32"
+        for f in ("hidden", "W", "target_hidden", "W_t"):
+            setattr(p, f, synthetic.bf16_bits_to_f32(getattr(p, f)).copy())
+    out = full_parity(p, max_chunk_rows=256, tag=f"kl-one-sweep-{case}-{dtype}",
+                      expect_kernels=(["stats_dual"], ["div", "stats_q", "stats_p"]))
+    if case == "identical":
+        import lm_head_vocab_amd as L
+        run = out["run"]
+        for k in ("kl_div", "rkl"):
+            assert np.all(run.term[L.KINDS.index(k)].cpu().numpy() == 0.0)
+
+
 def test_determinism_bitwise():
     p = synthetic.make_problem("multihead_bf16_405b", seq_len=100, hidden_dim=128, vocab=900)
     dev = to_device(p)
