@@ -14,7 +14,8 @@ from typing import Dict, Optional
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libspecloss.so")
+# SPECLOSS_LIBRARY may name another build of the same sources (the host-sanitized one)
+LIB_PATH = os.environ.get("SPECLOSS_LIBRARY") or os.path.join(_PKG, "libspecloss.so")
 
 KINDS = ("ce_label", "ce", "kl_div", "rkl", "jsd", "tv", "nla", "lk_hybrid")
 NUM_KINDS = len(KINDS)
