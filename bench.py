@@ -130,7 +130,7 @@ def main():
     W = up(prob.W)
     inputs = dict(labels=up_i(prob.labels, np.int32), mask=up_i(prob.mask, np.uint8),
                   target_hidden=up(prob.target_hidden), W_t=up(prob.W_t),
-                  target_row=up_i(prob.target_row, np.int32))
+                  target_row=up_i(prob.target_row, np.int32), heads=prob.shifts)
     torch.cuda.synchronize()
     torch.cuda.reset_peak_memory_stats()
     base_alloc = torch.cuda.memory_allocated()
@@ -329,8 +329,8 @@ def blas_reference(h, W, labels, nc, N, kernels):
             "ours_tflops": ours}
 
 
-FLOP_KERNELS = ("stats_q", "stats_p", "stats_stage", "div", "div_stage", "dz", "gemm_dh",
-                "gemm_dW")
+FLOP_KERNELS = ("stats_q", "stats_p", "stats_stage", "stats_dual", "div", "div_stage",
+                "div_heads", "div_heads_stage", "dz", "gemm_dh", "gemm_dW")
 
 
 def summarize_trace(entries, steps):

@@ -66,6 +66,9 @@ typedef enum {
 
 typedef enum { SPECLOSS_F32 = 0, SPECLOSS_BF16 = 1 } specloss_dtype;
 
+/* Aligned draft heads a problem may declare (specloss_problem.n_heads). */
+#define SPECLOSS_MAX_HEADS 4
+
 enum {
   SPECLOSS_OK = 0,
   SPECLOSS_E_INVAL = -1,       /* null/inconsistent argument, bad size, no nonzero weight */
@@ -144,6 +147,16 @@ typedef struct {
   const uint8_t* mask;         /* [N] 0 = masked, or NULL = no mask */
   float weights[SPECLOSS_NUM_KINDS]; /* per-kind weight, used as given (not normalised); 0 = off */
   specloss_trace* trace;       /* NULL, or a trace that records every launch of the call */
+  /* Aligned draft heads (blog, "Correctness: alignment before chunking"; the
+   * layout specloss_align_heads writes): 0, or K in [1, SPECLOSS_MAX_HEADS]
+   * when the rows are token-major heads, row T * K + k being head k at token
+   * T, whose target row is T + head_shift[k].  n_rows must be a multiple of
+   * K and target_row given; a row that is valid otherwise but has another
+   * target row counts as bad.  With K = 2 or 3 (bf16) the second divergence
+   * sweep computes each target tile once for the K rows it serves instead of
+   * once per row.  Ignored when no kind needs the target side. */
+  int32_t n_heads;
+  int32_t head_shift[SPECLOSS_MAX_HEADS]; /* 0 <= shift <= 65536 */
 } specloss_problem;
 
 /*
@@ -290,7 +303,8 @@ int lmhead_loss_fwd_bwd(const specloss_problem* p, void* workspace, size_t ws_by
 /*
  * Alignment before chunking for draft heads (blog, "Correctness: alignment
  * before chunking"): head k predicts `shifts[k]` tokens ahead.  Rows are
- * head-major, row = (k * batch + b) * seq_len + t, and its target row is
+ * token-major, row = (b * seq_len + t) * n_heads + k (a chunk of consecutive
+ * rows holds every head of a run of tokens), and its target row is
  * b * seq_len + t + shifts[k] when that position is inside the sequence
  * and (if loss_mask != NULL) loss_mask of that position is nonzero; then
  * mask_out = 1, else mask_out = 0 and target_row_out = -1.

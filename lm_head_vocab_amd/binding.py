@@ -9,7 +9,7 @@ from __future__ import annotations
 
 import ctypes
 import os
-from typing import Dict, Optional
+from typing import Dict, Optional, Sequence
 
 import torch
 
@@ -19,6 +19,7 @@ LIB_PATH = os.environ.get("SPECLOSS_LIBRARY") or os.path.join(_PKG, "libspecloss
 
 KINDS = ("ce_label", "ce", "kl_div", "rkl", "jsd", "tv", "nla", "lk_hybrid")
 NUM_KINDS = len(KINDS)
+MAX_HEADS = 4  # SPECLOSS_MAX_HEADS
 F32, BF16 = 0, 1
 IGNORE_INDEX = -100
 SAVED_FIELDS = 10
@@ -50,6 +51,8 @@ class Problem(ctypes.Structure):
         ("mask", ctypes.c_void_p),
         ("weights", ctypes.c_float * NUM_KINDS),
         ("trace", ctypes.c_void_p),
+        ("n_heads", ctypes.c_int32),
+        ("head_shift", ctypes.c_int32 * MAX_HEADS),
     ]
 
 
@@ -189,10 +192,12 @@ def _check(code: int, what: str) -> None:
 def make_problem(hidden: torch.Tensor, W: torch.Tensor, weights: Dict[str, float], *,
                  labels: Optional[torch.Tensor] = None, mask: Optional[torch.Tensor] = None,
                  target_hidden: Optional[torch.Tensor] = None, W_t: Optional[torch.Tensor] = None,
-                 target_row: Optional[torch.Tensor] = None, flags: int = 0) -> Problem:
+                 target_row: Optional[torch.Tensor] = None, flags: int = 0,
+                 heads: Optional[Sequence[int]] = None) -> Problem:
     """Fill a ``specloss_problem`` from torch tensors (no copies, no checks beyond dtype).
 
     flags: 0 (automatic), FLAG_COPIES, FLAG_NO_WEIGHT_COPY or FLAG_NO_COPIES (backward layout).
+    heads: the shifts of token-major aligned heads (specloss_align_heads's layout), or None.
     """
     if hidden.dtype not in (torch.float32, torch.bfloat16) or W.dtype != hidden.dtype:
         raise ValueError("hidden and W must both be float32 or both bfloat16")
@@ -214,6 +219,12 @@ def make_problem(hidden: torch.Tensor, W: torch.Tensor, weights: Dict[str, float
         if k not in KINDS:
             raise ValueError(f"unknown loss kind {k!r}; known: {KINDS}")
         p.weights[KINDS.index(k)] = float(w)
+    if heads:
+        if len(heads) > MAX_HEADS:
+            raise ValueError(f"at most {MAX_HEADS} aligned heads can be declared")
+        p.n_heads = len(heads)
+        for i, sh in enumerate(heads):
+            p.head_shift[i] = int(sh)
     return p
 
 

@@ -111,6 +111,13 @@ int check_problem(const specloss_problem* p, KindSet* ks) {
       return SPECLOSS_E_INVAL;  // identity map needs a target row per row
     }
   }
+  if (p->n_heads != 0) {
+    if (p->n_heads < 1 || p->n_heads > SPECLOSS_MAX_HEADS || p->n_rows % p->n_heads != 0)
+      return SPECLOSS_E_INVAL;
+    for (int i = 0; i < p->n_heads; ++i)
+      if (p->head_shift[i] < 0 || p->head_shift[i] > 65536) return SPECLOSS_E_INVAL;
+    if (k.target && !p->target_row) return SPECLOSS_E_INVAL;
+  }
   *ks = k;
   return SPECLOSS_OK;
 }
@@ -141,12 +148,37 @@ struct Layout {
   bool shared_target;
   int64_t Nt;
   // forward
-  size_t pz, pu, p2, zy, fwd_end;
+  size_t pz, pu, p2, zy, hmap, fwd_end;
   // backward
   size_t wt, ht, dz, dzt, dhp, bwd_end;
   // single-call forward+backward: forward partials and backward buffers at once
-  size_t f_pz, f_pu, f_p2, f_zy, f_wt, f_ht, f_dz, f_dd, f_dl, f_dzt, f_rs, f_dhp, fused_end;
+  size_t f_pz, f_pu, f_p2, f_zy, f_hmap, f_wt, f_ht, f_dz, f_dd, f_dl, f_dzt, f_rs, f_dhp, fused_end;
 };
+
+// The second sweep of a problem with aligned heads shares target tiles
+// between the heads (k_div_heads): K = 2 or 3, bf16, a target side with a
+// row map.  The tiles of a chunk of Nc rows span at most Nc / K + 2 tokens
+// plus the spread of the shifts.
+bool heads_pass2(const specloss_problem* p, const KindSet& k) {
+  return k.pass2 && k.target && p->target_row && p->in_dtype == SPECLOSS_BF16 &&
+         (p->n_heads == 2 || p->n_heads == 3);
+}
+
+void shift_range(const specloss_problem* p, int32_t& lo, int32_t& hi) {
+  lo = p->head_shift[0];
+  hi = p->head_shift[0];
+  for (int i = 1; i < p->n_heads; ++i) {
+    lo = p->head_shift[i] < lo ? p->head_shift[i] : lo;
+    hi = p->head_shift[i] > hi ? p->head_shift[i] : hi;
+  }
+}
+
+int64_t heads_map_entries(const specloss_problem* p, int64_t Nc) {
+  int32_t lo, hi;
+  shift_range(p, lo, hi);
+  const int64_t span = Nc / p->n_heads + 2 + (hi - lo);
+  return cdiv(span, 64) * 64 * p->n_heads;
+}
 
 // Split-K slices of the dh contraction of a chunk of Nc rows: its grid has
 // ceil(Nc / 256) x ceil(H / 256) tiles, and with few of them (small chunks)
@@ -200,6 +232,8 @@ Layout plan(const specloss_problem* p, const KindSet& k, int64_t Nc,
   L.pu = take(k.target ? 4 * tile_cols : 0);
   L.p2 = take(k.pass2 ? (size_t)kNumSums * tile_cols : 0);
   L.zy = take(2 * (size_t)Nc * 4);
+  const size_t hmap_bytes = heads_pass2(p, k) ? (size_t)heads_map_entries(p, Nc) * 4 : 0;
+  L.hmap = take(hmap_bytes);
   L.fwd_end = o;
   o = L.head_end;
   L.wt = take(L.wt_copy ? (size_t)L.H * L.Vp * L.es : 0);
@@ -215,6 +249,7 @@ Layout plan(const specloss_problem* p, const KindSet& k, int64_t Nc,
   L.f_pu = take(k.target ? 4 * tile_cols : 0);
   L.f_p2 = take(k.stage_div ? (size_t)kNumSums * tile_cols : 0);
   L.f_zy = take(2 * (size_t)Nc * 4);
+  L.f_hmap = take(k.stage_div ? hmap_bytes : 0);
   L.f_wt = take(L.wt_copy ? (size_t)L.H * L.Vp * L.es : 0);
   L.f_ht = take(L.dw_copies ? (size_t)L.H * Nc * L.es : 0);
   L.f_dz = take((size_t)Nc * L.Vp * L.es);
@@ -381,13 +416,14 @@ enum KernelId : int32_t {
   K_VALIDITY, K_STATS_Q, K_STATS_P, K_COMBINE1, K_ROWDOT, K_DIV, K_COMBINE2, K_REDUCE, K_COPY,
   K_SEED, K_TRANSPOSE_W, K_TRANSPOSE_H, K_DZ, K_GEMM_DH, K_GEMM_DW, K_STATS_STAGE, K_DZ_STAGE,
   K_DIV_STAGE, K_DZ_DIV, K_TILE_SUM, K_SUM_PARTS, K_TARGET_GATHER, K_STAGE_FIX, K_STATS_DUAL,
-  K_NUM_IDS
+  K_DIV_HEADS, K_DIV_HEADS_STAGE, K_HEADS_MAP, K_NUM_IDS
 };
 const char* const kKernelNames[K_NUM_IDS] = {
     "validity", "stats_q", "stats_p", "combine1", "rowdot", "div", "combine2", "reduce",
     "copy_lse", "seed", "transpose_W", "transpose_h", "dz", "gemm_dh", "gemm_dW",
     "stats_stage", "dz_stage", "div_stage", "dz_div", "tile_sum", "sum_partials",
-    "target_gather", "stage_fix", "stats_dual"};
+    "target_gather", "stage_fix", "stats_dual", "div_heads", "div_heads_stage",
+    "heads_map"};
 
 // Brackets launches with the trace's events when the problem carries one.
 struct Tracer {
@@ -439,6 +475,7 @@ struct FwdBufs {
   float* zy;   // gathered logits [2][Nc]
   int64_t Nc;
   void* tstat = nullptr;  // per-target-row lse_p, argmax, flatness (shared targets)
+  int32_t* hmap = nullptr;  // row map of the aligned-heads second sweep
 };
 
 // Target statistics once per target row (rows that share target rows):
@@ -497,6 +534,10 @@ int launch_validity_for(const specloss_problem* p, const KindSet& k, const Saved
   va.flags = sv.flags;
   va.y_label = sv.y_label;
   va.counts = counts;
+  if (k.target && p->target_row && p->n_heads > 0) {
+    va.n_heads = p->n_heads;
+    for (int i = 0; i < p->n_heads; ++i) va.shifts[i] = p->head_shift[i];
+  }
   TRACED(tr, K_VALIDITY, (double)p->n_rows * 10, launch_validity(va, stream));
   return SPECLOSS_OK;
 }
@@ -611,6 +652,34 @@ int launch_pass2(const specloss_problem* p, const KindSet& k, const Layout& L, c
   dv.stage_d = stage_d;
   dv.stage_l = stage_d ? stage_l : nullptr;
   dv.ld_stage = L.Vp;
+  if (heads_pass2(p, k) && b.hmap) {
+    // aligned heads: target rows [jlo, jhi) serve the chunk's rows, each
+    // target tile computed once
+    const int32_t K = p->n_heads;
+    int32_t s_lo, s_hi;
+    shift_range(p, s_lo, s_hi);
+    const int64_t t_lo = r0 / K, t_hi = (r0 + rows - 1) / K + 1;
+    const int64_t jlo = t_lo + s_lo, jhi = t_hi + s_hi;
+    const int32_t tiles_n = (int32_t)cdiv(jhi - jlo, 64);
+    if ((int64_t)tiles_n * 64 * K > heads_map_entries(p, Nc)) return SPECLOSS_E_INVAL;
+    TRACED(tr, K_HEADS_MAP, (double)tiles_n * 64 * K * 4,
+           launch_heads_map(b.hmap, tiles_n, K, p->head_shift, jlo, r0, (int32_t)rows, stream));
+    DivHeadsLaunch hv{};
+    hv.d = dv;
+    hv.d.Bz = op(offset_rows(p->hidden_states, r0, H, L.es), H, rows, b.hmap,
+                 (int64_t)tiles_n * 64 * K);
+    const int64_t jb = jlo < p->n_target_rows ? jlo : p->n_target_rows - 1;
+    hv.d.Bu = op(offset_rows(p->target_hidden, jb, H, L.es), H, p->n_target_rows - jb);
+    hv.d.tiles_n = tiles_n;
+    hv.n_heads = K;
+    for (int i = 0; i < K; ++i) hv.shifts[i] = p->head_shift[i];
+    hv.jlo = jlo;
+    hv.r0 = r0;
+    hv.rows = (int32_t)rows;
+    TRACED(tr, stage_d ? K_DIV_HEADS_STAGE : K_DIV_HEADS,
+           2.0 * (double)(rows + (jhi - jlo)) * H * p->vocab, launch_div_heads(bf16, hv, stream));
+    return SPECLOSS_OK;
+  }
   TRACED(tr, stage_d ? K_DIV_STAGE : K_DIV, 4.0 * rows * H * p->vocab,
          launch_div(bf16, dv, stream));
   return SPECLOSS_OK;
@@ -1204,7 +1273,7 @@ int lmhead_loss_fwd(const specloss_problem* p, void* workspace, size_t ws_bytes,
   float* terms = term_loss ? term_loss : reinterpret_cast<float*>(ws + L.terms);
   const FwdBufs b{reinterpret_cast<float*>(ws + L.pz), reinterpret_cast<float*>(ws + L.pu),
                   reinterpret_cast<float*>(ws + L.p2), reinterpret_cast<float*>(ws + L.zy), Nc,
-                  ws + L.tstat};
+                  ws + L.tstat, reinterpret_cast<int32_t*>(ws + L.hmap)};
   Tracer tr{p->trace, stream};
 
   TRY(launch_validity_for(p, k, sv, counts, tr, stream));
@@ -1271,7 +1340,8 @@ int lmhead_loss_fwd_bwd(const specloss_problem* p, void* workspace, size_t ws_by
   float* seed = reinterpret_cast<float*>(ws + L.seed);
   const FwdBufs b{reinterpret_cast<float*>(ws + L.f_pz), reinterpret_cast<float*>(ws + L.f_pu),
                   k.stage_div ? reinterpret_cast<float*>(ws + L.f_p2) : nullptr,
-                  reinterpret_cast<float*>(ws + L.f_zy), Nc, ws + L.tstat};
+                  reinterpret_cast<float*>(ws + L.f_zy), Nc, ws + L.tstat,
+                  reinterpret_cast<int32_t*>(ws + L.f_hmap)};
   void* wt = L.wt_copy ? ws + L.f_wt : nullptr;
   void* ht = L.dw_copies ? ws + L.f_ht : nullptr;
   void* dz = ws + L.f_dz;

@@ -755,9 +755,9 @@ __global__ __launch_bounds__(256) void k_dz_stage(DzStageLaunch a) {
 // STAGE: also store q and d = q - p of every (row, vocab) for the logit
 // gradient (rounded to the storage type; d keeps the sign of q - p, zero on
 // ties, so the indicator [q < p] is unchanged by the rounding).
-template <typename T, bool STAGE>
-__global__ __launch_bounds__(kThreads, 1) void k_div(DivLaunch a) {
-  using Cfg = TileCfg<T, 256, 128>;
+template <typename T, bool STAGE, int WNW>
+__global__ __launch_bounds__(128 * WNW, 1) void k_div(DivLaunch a) {
+  using Cfg = TileCfg<T, 256, 128, 1, WNW>;
   __shared__ __attribute__((aligned(16))) char smem[Cfg::LDS_BYTES];
   int tm, tn;
   if (!tile_of(a.tiles_m, a.tiles_n, kGroupM, tm, tn)) return;
@@ -771,7 +771,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_div(DivLaunch a) {
                         smem);
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WNW, wn = wave % WNW;
   const int v_base = tm * Cfg::BM + wm * Cfg::WM;
   const bool tail = tm * Cfg::BM + Cfg::BM > a.vocab;
   const uint32_t need = a.need;
@@ -844,6 +844,141 @@ __global__ __launch_bounds__(kThreads, 1) void k_div(DivLaunch a) {
           a.part[f * a.part_stride + (int64_t)tm * a.ldp + col] = sums[j][f] + red[c * kNumSums + f];
     }
   }
+}
+
+// Pass 2 for aligned heads: a tile covers 256 vocabulary rows and 64 target
+// rows, and the target tile u is computed once for the K draft rows each
+// target row serves.  The draft tile has 64 K columns ordered so that wave
+// column wn holds, for each head k, the same 32 target rows as its u
+// columns: z column wn * 32 K + k * 32 + jj pairs with u column wn * 32 + jj
+// (the map puts the matching draft row there).  Per (vocabulary row, draft
+// row) the arithmetic is that of k_div, in the same order, so the sums and
+// staged values are the same bits.
+template <typename T, bool STAGE, int K>
+__global__ __launch_bounds__(kThreads, 1) void k_div_heads(DivHeadsLaunch h) {
+  using CfgZ = TileCfg<T, 256, 64 * K>;
+  using CfgU = TileCfg<T, 256, 64>;
+  constexpr int kSmem = CfgZ::LDS_BYTES > CfgU::LDS_BYTES ? CfgZ::LDS_BYTES : CfgU::LDS_BYTES;
+  __shared__ __attribute__((aligned(16))) char smem[kSmem];
+  const DivLaunch& a = h.d;
+  int tm, tn;
+  if (!tile_of(a.tiles_m, a.tiles_n, kGroupM, tm, tn)) return;
+
+  f32x4_t az[CfgZ::FM][CfgZ::FN], au[CfgU::FM][CfgU::FN];
+  zero_acc<CfgZ>(az);
+  zero_acc<CfgU>(au);
+  tile_mainloop<T, CfgZ>(az, as_op<T>(a.Az), tm * CfgZ::BM, as_op<T>(a.Bz), tn * CfgZ::BN,
+                         a.k_len, smem);
+  tile_mainloop<T, CfgU>(au, as_op<T>(a.Au), tm * CfgU::BM, as_op<T>(a.Bu), tn * CfgU::BN,
+                         a.k_len, smem);
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int v_base = tm * CfgU::BM + wm * CfgU::WM;
+  const bool tail = tm * CfgU::BM + CfgU::BM > a.vocab;
+  const uint32_t need = a.need;
+  static_assert(CfgU::FN == 2 && CfgZ::FN == 2 * K && CfgU::WN == 32, "heads tile layout");
+
+  // per (head, u fragment column): chunk row or -1, and the six sums
+  float sums[K][CfgU::FN][kNumSums];
+  int crow[K][CfgU::FN];
+#pragma unroll
+  for (int j = 0; j < CfgU::FN; ++j) {
+    const int64_t tj = h.jlo + tn * 64 + wn * CfgU::WN + j * kFrag + frag_col(lane);  // target row
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      const int64_t lr = (tj - h.shifts[k]) * K + k - h.r0;  // chunk row of head k
+      const bool ok = tj - h.shifts[k] >= 0 && lr >= 0 && lr < h.rows;
+      crow[k][j] = ok ? (int)lr : -1;
+      const int col = ok ? (int)lr : 0;
+      const float lq0 = a.lse_q[col], lp0 = a.lse_p[col];
+      float s_alpha = 0.f, s_s = 0.f, s_kl = 0.f, s_rkl = 0.f, s_jsd = 0.f, s_eqg = 0.f;
+#pragma unroll
+      for (int i = 0; i < CfgU::FM; ++i) {
+        float sq[4], sd[4], sl[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int v = v_base + i * kFrag + frag_row(r, lane);
+          sq[r] = 0.0f;
+          sd[r] = 0.0f;
+          sl[r] = 0.0f;
+          if (tail && v >= a.vocab) continue;
+          const float lq = az[i][k * CfgU::FN + j][r] - lq0;
+          const float lp = au[i][j][r] - lp0;
+          const float q = fast_exp2(lq * kLog2e);
+          const float p = fast_exp2(lp * kLog2e);
+          sq[r] = q;
+          sd[r] = q - p;
+          sl[r] = lq - lp;
+          if (need & SUM_ALPHA) s_alpha += fminf(p, q);
+          if (need & SUM_S) s_s += (q < p) ? q : ((q == p) ? 0.5f * q : 0.0f);
+          if (need & SUM_KL) s_kl += p * (lp - lq);
+          if (need & SUM_RKL) s_rkl += q * (lq - lp);
+          if (need & (SUM_JSD | SUM_EQG)) {
+            const float lm = fast_log2(0.5f * (p + q)) * kLn2;
+            if (need & SUM_JSD) s_jsd += 0.5f * (p * (lp - lm) + q * (lq - lm));
+            if (need & SUM_EQG) s_eqg += 0.5f * q * (lq - lm);
+          }
+        }
+        if (STAGE && ok) {
+          const int64_t o = lr * a.ld_stage + v_base + i * kFrag + frag_row(0, lane);
+          store4<T>(static_cast<T*>(a.stage_q) + o, sq[0], sq[1], sq[2], sq[3]);
+          store4<T>(static_cast<T*>(a.stage_d) + o, sd[0], sd[1], sd[2], sd[3]);
+          if (a.stage_l) store4<T>(static_cast<T*>(a.stage_l) + o, sl[0], sl[1], sl[2], sl[3]);
+        }
+      }
+      const float v6[kNumSums] = {s_alpha, s_s, s_kl, s_rkl, s_jsd, s_eqg};
+#pragma unroll
+      for (int f = 0; f < kNumSums; ++f) sums[k][j][f] = col_sum(v6[f], lane);
+    }
+  }
+
+  // the two wave rows (wm) share target columns: wm = 1 hands its sums over
+  float* red = reinterpret_cast<float*>(smem);  // [K][64][kNumSums]
+  if (wm == 1 && lane < kFrag) {
+#pragma unroll
+    for (int k = 0; k < K; ++k)
+#pragma unroll
+      for (int j = 0; j < CfgU::FN; ++j) {
+        const int c = wn * CfgU::WN + j * kFrag + lane;
+#pragma unroll
+        for (int f = 0; f < kNumSums; ++f) red[(k * 64 + c) * kNumSums + f] = sums[k][j][f];
+      }
+  }
+  __syncthreads();
+  if (wm == 0 && lane < kFrag) {
+#pragma unroll
+    for (int k = 0; k < K; ++k)
+#pragma unroll
+      for (int j = 0; j < CfgU::FN; ++j) {
+        const int c = wn * CfgU::WN + j * kFrag + lane;
+        const int col = crow[k][j];
+        if (col < 0) continue;
+#pragma unroll
+        for (int f = 0; f < kNumSums; ++f)
+          if (need & (1u << f))
+            a.part[f * a.part_stride + (int64_t)tm * a.ldp + col] =
+                sums[k][j][f] + red[(k * 64 + c) * kNumSums + f];
+      }
+  }
+}
+
+// Draft rows of the heads tiles: entry tn * 64 K + r is the chunk row of z
+// tile row r of tile column tn (clamped into the chunk; rows outside it are
+// discarded by the kernel).
+__global__ __launch_bounds__(256) void k_heads_map(int32_t* map, int32_t tiles_n, int32_t K,
+                                                   ShiftArg sh, int64_t jlo, int64_t r0,
+                                                   int32_t rows) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t n = (int64_t)tiles_n * 64 * K;
+  if (idx >= n) return;
+  const int tn = (int)(idx / (64 * K)), r = (int)(idx % (64 * K));
+  const int wn = r / (32 * K), k = (r % (32 * K)) / 32, jj = r % 32;
+  const int64_t tj = jlo + (int64_t)tn * 64 + wn * 32 + jj;
+  int64_t lr = (tj - sh.v[k]) * K + k - r0;
+  if (tj - sh.v[k] < 0 || lr < 0) lr = 0;
+  if (lr >= rows) lr = rows - 1;
+  map[idx] = (int32_t)lr;
 }
 
 // ============================================================================
@@ -1094,7 +1229,9 @@ __global__ __launch_bounds__(1024) void k_validity(ValidityLaunch a) {
     }
     if (a.use_target && a.target_row) {
       const int tr = a.target_row[r];
-      if (tr < 0 || tr >= a.n_target) {
+      const bool off_layout =
+          a.n_heads > 0 && (int64_t)tr != r / a.n_heads + a.shifts[r % a.n_heads];
+      if (tr < 0 || tr >= a.n_target || off_layout) {
         bad |= valid;
         valid = 0;
       }
@@ -1505,10 +1642,11 @@ __global__ __launch_bounds__(256) void k_align(AlignLaunch a) {
   const int64_t n = (int64_t)a.n_heads * a.batch * a.seq_len;
   const int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (r >= n) return;
-  const int64_t t = r % a.seq_len;
-  const int64_t kb = r / a.seq_len;
-  const int64_t b = kb % a.batch;
-  const int k = (int)(kb / a.batch);
+  // token-major: row r = (b * seq_len + t) * n_heads + k
+  const int k = (int)(r % a.n_heads);
+  const int64_t bt = r / a.n_heads;
+  const int64_t t = bt % a.seq_len;
+  const int64_t b = bt / a.seq_len;
   const int64_t tt = t + a.shifts[k];
   int32_t tr = -1;
   uint8_t m = 0;
@@ -1656,15 +1794,45 @@ hipError_t launch_stats_dual(bool bf16, const DualStatsLaunch& a, hipStream_t s)
   return hipGetLastError();
 }
 
+#ifndef SPECLOSS_DIV_WNW
+#define SPECLOSS_DIV_WNW 2
+#endif
+constexpr int kDivWNW = SPECLOSS_DIV_WNW;
+
+hipError_t launch_heads_map(int32_t* map, int32_t tiles_n, int32_t n_heads, const int32_t* shifts,
+                            int64_t jlo, int64_t r0, int32_t rows, hipStream_t s) {
+  ShiftArg sh{};
+  for (int k = 0; k < n_heads && k < kMaxHeads; ++k) sh.v[k] = shifts[k];
+  const int64_t n = (int64_t)tiles_n * 64 * n_heads;
+  hipLaunchKernelGGL(k_heads_map, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, map,
+                     tiles_n, n_heads, sh, jlo, r0, rows);
+  return hipGetLastError();
+}
+
+hipError_t launch_div_heads(bool bf16, const DivHeadsLaunch& a, hipStream_t s) {
+  if (!bf16 || a.n_heads < 2 || a.n_heads > 3) return hipErrorInvalidValue;
+  const dim3 grid(grid_for_tiles(a.d.tiles_m * a.d.tiles_n)), block(kThreads);
+  const bool stage = a.d.stage_q != nullptr;
+  if (a.n_heads == 2) {
+    if (stage) hipLaunchKernelGGL((k_div_heads<bf16_bits, true, 2>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((k_div_heads<bf16_bits, false, 2>), grid, block, 0, s, a);
+  } else {
+    if (stage) hipLaunchKernelGGL((k_div_heads<bf16_bits, true, 3>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((k_div_heads<bf16_bits, false, 3>), grid, block, 0, s, a);
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_div(bool bf16, const DivLaunch& a, hipStream_t s) {
-  const dim3 grid(grid_for_tiles(a.tiles_m * a.tiles_n)), block(kThreads);
+  constexpr int W = kDivWNW;
+  const dim3 grid(grid_for_tiles(a.tiles_m * a.tiles_n)), block(128 * W);
   const bool stage = a.stage_q != nullptr;
   if (bf16) {
-    if (stage) hipLaunchKernelGGL((k_div<bf16_bits, true>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((k_div<bf16_bits, false>), grid, block, 0, s, a);
+    if (stage) hipLaunchKernelGGL((k_div<bf16_bits, true, W>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((k_div<bf16_bits, false, W>), grid, block, 0, s, a);
   } else {
-    if (stage) hipLaunchKernelGGL((k_div<float, true>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((k_div<float, false>), grid, block, 0, s, a);
+    if (stage) hipLaunchKernelGGL((k_div<float, true, 2>), dim3(grid), dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((k_div<float, false, 2>), dim3(grid), dim3(256), 0, s, a);
   }
   return hipGetLastError();
 }

@@ -18,6 +18,10 @@ enum : uint32_t {
   SUM_EQG = 1u << 5,    // sum_v q (log q - log m) / 2
 };
 constexpr int kNumSums = 6;
+constexpr int kMaxHeads = 4;  // aligned heads a problem may declare
+struct ShiftArg {
+  int32_t v[kMaxHeads];
+};
 constexpr int kNumKinds = 8;
 constexpr int kVocabTile = 256;  // vocabulary rows per tile in every vocab-tiled pass
 
@@ -147,6 +151,26 @@ struct DivLaunch {
 };
 hipError_t launch_div(bool bf16, const DivLaunch& a, hipStream_t s);
 
+// pass 2 for aligned heads (rows token-major: chunk row r - r0 of global row
+// r = T * K + k is head k at token T, whose target row is T + shifts[k]):
+// tiles of 256 vocabulary rows x 64 target rows j = jlo + tn * 64 + c, each
+// target tile computed once for the K <= 3 draft rows (j - shifts[k]) * K + k
+// it serves that lie in the chunk.  Bz rows come through `map` (filled by
+// launch_heads_map: [tiles_n][64 K] chunk-local rows, clamped into the
+// chunk); Bu starts at target row jlo.  Sums, partials and staging as for
+// launch_div, indexed by chunk row.
+struct DivHeadsLaunch {
+  DivLaunch d;     // Bz: the chunk's rows with `map`; Bu: target rows from jlo
+  int32_t n_heads;
+  int32_t shifts[kMaxHeads];
+  int64_t jlo;     // first target row of the tiles
+  int64_t r0;      // global row of chunk row 0
+  int32_t rows;    // chunk rows
+};
+hipError_t launch_div_heads(bool bf16, const DivHeadsLaunch& a, hipStream_t s);
+hipError_t launch_heads_map(int32_t* map, int32_t tiles_n, int32_t n_heads, const int32_t* shifts,
+                            int64_t jlo, int64_t r0, int32_t rows, hipStream_t s);
+
 struct DzLaunch {
   GemmOperand Az, Bz, Au, Bu;
   int32_t k_len, vocab, tiles_m, tiles_n, ncols;
@@ -195,6 +219,10 @@ struct ValidityLaunch {
   int32_t* flags;
   int32_t* y_label;
   int64_t* counts;
+  // aligned heads (n_heads > 0): a valid row r must have target row
+  // r / n_heads + shifts[r % n_heads]; a row that does not is bad
+  int32_t n_heads;
+  int32_t shifts[kMaxHeads];
 };
 hipError_t launch_validity(const ValidityLaunch& a, hipStream_t s);
 

@@ -212,10 +212,12 @@ __device__ __forceinline__ void group_source(const Operand<T>& op, int32_t row0,
     base = reinterpret_cast<const char*>(op.base);
     off = (uint32_t)((int64_t)src * op.ld * (int64_t)sizeof(T)) + lchunk * 16;
   } else {
-    // contiguous rows: offsets from the tile's first row
+    // contiguous rows: offsets from the tile's first row, itself clamped into
+    // the tensor (a tile may start past the last row; the offsets stay >= 0)
+    const int32_t first = clamp_row(row0, op.n_rows);
     const int32_t src = clamp_row(row0 + r, op.n_rows);
-    base = reinterpret_cast<const char*>(op.base + (int64_t)row0 * op.ld);
-    off = (uint32_t)((int64_t)(src - row0) * op.ld * (int64_t)sizeof(T)) + lchunk * 16;
+    base = reinterpret_cast<const char*>(op.base + (int64_t)first * op.ld);
+    off = (uint32_t)((int64_t)(src - first) * op.ld * (int64_t)sizeof(T)) + lchunk * 16;
   }
 }
 

@@ -61,10 +61,13 @@ def trace_name(kernel: str) -> str:
     names = {"k_stats": "stats_q", "k_stats_stage": "stats_stage", "k_dz_stage": "dz_stage",
              "k_dz": "dz", "k_div": "div", "k_combine1": "combine1", "k_combine2": "combine2", "k_stage_fix": "stage_fix",
              "k_rowdot": "rowdot", "k_transpose": "transpose", "k_validity": "validity",
-             "k_reduce": "reduce", "k_seed": "seed", "k_align": "align"}
+             "k_reduce": "reduce", "k_seed": "seed", "k_align": "align",
+             "k_stats_dual": "stats_dual", "k_div_heads": "div_heads", "k_heads_map": "heads_map",
+             "k_sum_parts": "sum_partials"}
     name = names.get(base, base)
     if "true" in targs:
-        name = {"k_stats": "stats_p", "k_div": "div_stage", "k_dz_stage": "dz_div"}.get(base, name)
+        name = {"k_stats": "stats_p", "k_div": "div_stage", "k_dz_stage": "dz_div",
+                "k_div_heads": "div_heads_stage"}.get(base, name)
     return name
 
 

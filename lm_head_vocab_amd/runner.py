@@ -5,7 +5,7 @@ the work itself is the C-ABI calls ``lmhead_loss_fwd`` / ``lmhead_loss_bwd``.
 """
 from __future__ import annotations
 
-from typing import Dict, Optional
+from typing import Dict, Optional, Sequence
 
 import torch
 
@@ -20,14 +20,14 @@ class LossRun:
                  target_hidden: Optional[torch.Tensor] = None, W_t: Optional[torch.Tensor] = None,
                  target_row: Optional[torch.Tensor] = None, max_chunk_rows: int = 0,
                  workspace_bytes: Optional[int] = None, want_terms: bool = True,
-                 flags: int = 0):
+                 flags: int = 0, heads: Optional[Sequence[int]] = None):
         dev = hidden.device
         self.inputs = dict(hidden=hidden, W=W, labels=labels, mask=mask,
                            target_hidden=target_hidden, W_t=W_t, target_row=target_row)
         self.weights = dict(weights)
         self.problem = B.make_problem(hidden, W, weights, labels=labels, mask=mask,
                                       target_hidden=target_hidden, W_t=W_t, target_row=target_row,
-                                      flags=flags)
+                                      flags=flags, heads=heads)
         N = hidden.shape[0]
         self.n_rows = N
         ws = workspace_bytes if workspace_bytes is not None else \
@@ -130,7 +130,8 @@ class ShardedLossRun(LossRun):
                  mask: Optional[torch.Tensor] = None,
                  target_hidden: Optional[torch.Tensor] = None, W_t: Optional[torch.Tensor] = None,
                  target_row: Optional[torch.Tensor] = None, max_chunk_rows: int = 0,
-                 want_terms: bool = True, bounds: Optional[list] = None, flags: int = 0):
+                 want_terms: bool = True, bounds: Optional[list] = None, flags: int = 0,
+                 heads: Optional[Sequence[int]] = None):
         dev = hidden.device
         V = W.shape[0]
         if bounds is None:
@@ -156,7 +157,7 @@ class ShardedLossRun(LossRun):
             prob = B.make_problem(hidden, W[v0:v1], weights, labels=labels, mask=mask,
                                   target_hidden=target_hidden,
                                   W_t=None if W_t is None else W_t[v0:v1], target_row=target_row,
-                                  flags=flags)
+                                  flags=flags, heads=heads)
             sh = B.Shard(vocab_offset=v0, vocab_total=V, shard=g, n_shards=n_shards,
                          exchange=self.exchange.data_ptr())
             self.problems.append(prob)

@@ -202,19 +202,20 @@ def align_heads(seq_len: int, shifts: Sequence[int], batch: int = 1,
                 loss_mask: Optional[np.ndarray] = None) -> Tuple[np.ndarray, np.ndarray]:
     """Aligned target row and mask for draft heads that predict ``shift`` tokens ahead.
 
-    Rows are head-major: row ``k*batch*seq_len + b*seq_len + t`` is head k at
+    Rows are token-major: row ``(b*seq_len + t)*K + k`` is head k (of K) at
     position t of sequence b.  Its target is position ``t + shift_k`` of the same
     sequence; it is valid iff that position exists and (if given) the loss mask
     of the target position is 1.  Invalid rows get target row -1.  This is done
     for the whole token set before any chunking.
     """
-    n = len(shifts) * batch * seq_len
+    K = len(shifts)
+    n = K * batch * seq_len
     target_row = np.full(n, -1, dtype=np.int64)
     mask = np.zeros(n, dtype=np.uint8)
     for k, sh in enumerate(shifts):
         for b in range(batch):
             for t in range(seq_len):
-                r = (k * batch + b) * seq_len + t
+                r = (b * seq_len + t) * K + k
                 tt = t + sh
                 if 0 <= tt < seq_len:
                     src = b * seq_len + tt

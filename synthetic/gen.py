@@ -125,7 +125,8 @@ class Problem:
     W_t: Optional[np.ndarray] = None            # [V, H]
     target_row: Optional[np.ndarray] = None     # int32 [N]: row of target_hidden per row
     seq_len: Optional[int] = None               # multi-head layout: positions per head
-    shifts: Optional[Tuple[int, ...]] = None    # multi-head layout: target shift per head
+    shifts: Optional[Tuple[int, ...]] = None    # multi-head layout (token-major rows,
+                                                # row t * K + k): target shift per head
     seed: int = 0
     recipe: str = ""
 
@@ -219,15 +220,18 @@ def make_problem(name: str, *, n_rows: Optional[int] = None, hidden_dim: Optiona
         hidden = np.empty((N, H), dtype=g.dtype)
         target_row = np.full(N, -1, dtype=np.int32)
         mask = np.zeros(N, dtype=np.uint8)
+        # token-major rows: row t * K + k is head k at position t (the layout
+        # of specloss_align_heads); tail rows draw from the tail stream in head
+        # order
         ti = 0
         for k, sh in enumerate(shifts):
             keep = max(0, S - sh)
-            r0 = k * S
-            hidden[r0:r0 + keep] = g[sh:sh + keep]
-            target_row[r0:r0 + keep] = np.arange(sh, sh + keep, dtype=np.int32)
-            mask[r0:r0 + keep] = 1
+            rows = np.arange(S) * K + k
+            hidden[rows[:keep]] = g[sh:sh + keep]
+            target_row[rows[:keep]] = np.arange(sh, sh + keep, dtype=np.int32)
+            mask[rows[:keep]] = 1
             nt = S - keep
-            hidden[r0 + keep:r0 + S] = tail[ti:ti + nt]
+            hidden[rows[keep:]] = tail[ti:ti + nt]
             ti += nt
         return Problem(name=name, dtype=spec["dtype"], n_rows=N, hidden_dim=H, vocab=V,
                        hidden=hidden, W=W, mask=mask, target_hidden=g, W_t=Wt,

@@ -50,6 +50,7 @@ def make_run(prob, dev_inputs, **kw) -> LossRun:
         kw["flags"] = L.binding.FLAG_COPIES
     elif kw.get("flags") is None:
         kw["flags"] = 0
+    kw.setdefault("heads", prob.shifts)  # aligned heads declare their layout
     return LossRun(dev_inputs["hidden"], dev_inputs["W"], prob.weights,
                    labels=dev_inputs["labels"], mask=dev_inputs["mask"],
                    target_hidden=dev_inputs["target_hidden"], W_t=dev_inputs["W_t"],
@@ -188,7 +189,7 @@ def full_parity(prob, *, max_chunk_rows=0, check_grads=True, tag="", single_call
                              labels=dev["labels"], mask=dev["mask"],
                              target_hidden=dev["target_hidden"], W_t=dev["W_t"],
                              target_row=dev["target_row"], max_chunk_rows=max_chunk_rows,
-                             bounds=shards[1], flags=flags)
+                             bounds=shards[1], flags=flags, heads=prob.shifts)
     else:
         run = make_run(prob, dev, max_chunk_rows=max_chunk_rows, workspace_bytes=workspace_bytes,
                        flags=flags)

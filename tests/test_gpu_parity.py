@@ -610,6 +610,7 @@ def test_shared_target_rows_match_per_row(single):
                                weights={"ce": 0.4, "tv": 0.6})
     q.target_hidden = p.target_hidden[tr].copy()
     q.target_row = None
+    q.shifts = None  # no aligned-heads layout without a row map
     gm = torch.ones(1, device="cuda")
     outs = []
     for prob in (p, q):
@@ -630,3 +631,78 @@ def test_shared_target_rows_match_per_row(single):
     assert torch.equal(a["dh"], b["dh"]) and torch.equal(a["dW"], b["dW"])
 
 
+
+
+# ------------------------------------------------------ aligned heads: shared target tiles
+def _heads_problem(S, shifts, batch, H, V, weights, seed):
+    """Token-major aligned heads (specloss_align_heads's layout) over `batch`
+    sequences of S positions: valid rows carry the target hidden state of their
+    target position, the others fresh N(0,1) rows; W ~ N(0, 0.1), W_t = W +
+    N(0, 0.02) (bf16)."""
+    rng = np.random.default_rng(seed)
+    K = len(shifts)
+    bf = synthetic.f32_to_bf16_bits
+    g = rng.standard_normal((batch * S, H), dtype=np.float32)
+    tr, mk = O.align_heads(S, shifts, batch=batch)
+    hidden = rng.standard_normal((K * batch * S, H), dtype=np.float32)
+    hidden[tr >= 0] = g[tr[tr >= 0]]
+    W = 0.1 * rng.standard_normal((V, H), dtype=np.float32)
+    Wt = W + 0.02 * rng.standard_normal((V, H), dtype=np.float32)
+    p = synthetic.Problem(name="aligned_heads", dtype="bf16", n_rows=K * batch * S, hidden_dim=H,
+                          vocab=V, hidden=bf(hidden), W=bf(W), weights=dict(weights),
+                          mask=mk.astype(np.uint8), target_hidden=bf(g), W_t=bf(Wt),
+                          target_row=tr.astype(np.int32), seq_len=S, shifts=tuple(shifts))
+    p.labels = rng.integers(0, V, p.n_rows).astype(np.int32)
+    return p
+
+
+@pytest.mark.parametrize("case", ["k3_single", "k3_two_calls", "k2_batch_single",
+                                  "k3_far_shifts_single", "k3_lean_single"])
+def test_aligned_heads_share_target_tiles(case):
+    """Declared token-major heads: the second sweep computes each target tile once
+    for the heads it serves (k_div_heads) instead of once per row.  Against the
+    oracle (the bar), and bit for bit against the same problem without the
+    declaration (per-row second sweep): losses, terms, saved state, gradients.
+    256-row chunks split tokens between chunks (256 is no multiple of 3)."""
+    import lm_head_vocab_amd as L
+    single = case.endswith("single")
+    shifts, batch = {"k3_single": ((1, 2, 3), 1), "k3_two_calls": ((1, 2, 3), 1),
+                     "k2_batch_single": ((2, 0), 3), "k3_far_shifts_single": ((0, 7, 70), 2),
+                     "k3_lean_single": ((1, 2, 3), 1)}[case]
+    weights = ({"tv": 0.7, "ce": 0.2, "kl_div": 0.4, "rkl": 0.3, "jsd": 0.5, "nla": 0.2,
+                "lk_hybrid": 0.6, "ce_label": 0.1} if case != "k2_batch_single"
+               else {"lk_hybrid": 1.0, "ce": 0.3})
+    S = 310 if batch == 1 else 170
+    p = _heads_problem(S, shifts, batch, 128, 900, weights, seed=71)
+    flags = L.binding.FLAG_NO_COPIES if case == "k3_lean_single" else None
+    stage = "div_heads_stage" if single else "div_heads"
+    plain = "div_stage" if single else "div"
+    out = full_parity(p, max_chunk_rows=256, tag=f"heads-{case}", single_call=single, flags=flags,
+                      expect_kernels=([stage], [plain]))
+    run = out["run"]
+    dev = to_device(p)
+    ref = make_run(p, dev, max_chunk_rows=256, heads=None,
+                   **({"flags": flags} if flags is not None else {}))
+    trace = L.binding.Trace(capacity=4096)
+    trace.attach(ref.problem)
+    gm = torch.ones(1, dtype=torch.float32, device="cuda")
+    if single:
+        dh, dW = ref.forward_backward(grad_mean=gm)
+    else:
+        ref.forward()
+        dh, dW = ref.backward(grad_mean=gm)
+    torch.cuda.synchronize()
+    names = {n for n, _, _ in trace.read()}
+    ref.problem.trace = None
+    trace.close()
+    assert plain in names and stage not in names, names
+    assert torch.equal(run.loss, ref.loss)
+    assert torch.equal(run.term, ref.term)
+    assert torch.equal(run.counts, ref.counts)
+    # saved state of valid rows (masked rows pair with a different unused target row)
+    valid = torch.from_numpy(p.mask.astype(bool)).cuda()
+    for f in range(L.binding.SAVED_FIELDS):
+        a_f, b_f = run.saved_field(f, torch.int32), ref.saved_field(f, torch.int32)
+        assert torch.equal(a_f[valid], b_f[valid]), f"saved field {f}"
+    assert np.array_equal(out["dh"], dh.cpu().numpy())
+    assert np.array_equal(out["dW"], dW.cpu().numpy())

@@ -7,6 +7,7 @@ import ctypes
 import json
 import os
 import re
+import subprocess
 
 import pytest
 import torch
@@ -35,9 +36,23 @@ def test_library_exports_every_header_symbol(lib):
         assert hasattr(lib, name), name
 
 
-def test_struct_layout_matches_header():
-    assert ctypes.sizeof(B.Problem) == 136
-    assert B.Problem.weights.offset == 96
+def test_struct_layout_matches_header(tmp_path):
+    """The ctypes mirror has the C compiler's size and offsets of specloss_problem."""
+    src = tmp_path / "layout.c"
+    src.write_text(
+        "#include <stddef.h>\n#include <stdio.h>\n#include \"specloss.h\"\n"
+        "int main(void) { printf(\"%zu %zu %zu %zu %zu\\n\", sizeof(specloss_problem), "
+        "offsetof(specloss_problem, weights), offsetof(specloss_problem, trace), "
+        "offsetof(specloss_problem, n_heads), offsetof(specloss_problem, head_shift)); "
+        "return 0; }\n")
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-D__HIP_PLATFORM_AMD__", f"-I{os.path.join(ROOT, 'include')}",
+                    "-I/opt/rocm/include", str(src), "-o", str(exe)], check=True)
+    got = [int(x) for x in subprocess.run([str(exe)], check=True, capture_output=True,
+                                          text=True).stdout.split()]
+    assert got == [ctypes.sizeof(B.Problem), B.Problem.weights.offset, B.Problem.trace.offset,
+                   B.Problem.n_heads.offset, B.Problem.head_shift.offset]
+    assert ctypes.sizeof(B.Problem) == 160 and B.Problem.weights.offset == 96
 
 
 def test_kind_names_and_errors(lib):
@@ -189,6 +204,30 @@ def test_align_heads_validation(lib):
     arr = (ctypes.c_int32 * 1)(1)
     assert lib.specloss_align_heads(0, 1, 1, arr, None, 0x1000, 0x2000, None) == E_INVAL
     assert lib.specloss_align_heads(10, 1, 65, arr, None, 0x1000, 0x2000, None) == E_UNSUP
+
+
+def test_declared_heads_validation(lib):
+    """A declared aligned-heads layout: 1..4 heads, rows a multiple of the head
+    count, shifts in [0, 65536], and a target row map when a target kind is on."""
+    def heads_problem(K, shifts, N=300, map_=True):
+        p = _problem(N=N, weights={"tv": 1.0}, target=100)
+        p.target_row = 0x60000 if map_ else None
+        p.n_heads = K
+        for i, sh in enumerate(shifts):
+            p.head_shift[i] = sh
+        return p
+    assert _ws(lib, heads_problem(3, (1, 2, 3)))[0] == 0
+    assert _ws(lib, heads_problem(2, (0, 65536), N=302))[0] == 0
+    assert _ws(lib, heads_problem(5, (1, 2, 3, 4)))[0] == E_INVAL
+    assert _ws(lib, heads_problem(-1, ()))[0] == E_INVAL
+    assert _ws(lib, heads_problem(3, (1, 2, 3), N=301))[0] == E_INVAL
+    assert _ws(lib, heads_problem(2, (1, -2)))[0] == E_INVAL
+    assert _ws(lib, heads_problem(2, (1, 65537)))[0] == E_INVAL
+    assert _ws(lib, heads_problem(3, (1, 2, 3), map_=False))[0] == E_INVAL
+    # the second sweep's row map of the heads tiles is part of the workspace
+    plain = heads_problem(3, (1, 2, 3))
+    plain.n_heads = 0
+    assert _ws(lib, heads_problem(3, (1, 2, 3)))[1] > _ws(lib, plain)[1]
 
 
 def test_memory_model_reproduces_page_figures():

@@ -360,9 +360,10 @@ def test_masked_rows_do_not_contribute():
 # --------------------------------------------------------------------------- alignment
 def test_align_heads_hand_example_and_generator():
     """Targets shift per head before chunking; tails past the sequence are masked."""
+    # token-major rows (t, k): t = 0 -> 1, 2; t = 1 -> 2, 3; ... t = 3 -> 4, tail
     tr, m = O.align_heads(5, (1, 2))
-    assert list(tr) == [1, 2, 3, 4, -1, 2, 3, 4, -1, -1]
-    assert list(m) == [1, 1, 1, 1, 0, 1, 1, 1, 0, 0]
+    assert list(tr) == [1, 2, 2, 3, 3, 4, 4, -1, -1, -1]
+    assert list(m) == [1, 1, 1, 1, 1, 1, 1, 0, 0, 0]
     tr2, m2 = O.align_heads(3, (1,), batch=2, loss_mask=np.array([1, 1, 0, 1, 1, 1], np.uint8))
     assert list(tr2) == [1, -1, -1, 4, 5, -1]
     p = synthetic.make_problem("multihead_bf16_405b", seq_len=40, hidden_dim=64, vocab=128)

@@ -45,7 +45,7 @@ def _check_against_workspace_call(prob, with_saved):
     dev = to_device(prob)
     ref = LossRun(dev["hidden"], dev["W"], prob.weights, labels=dev["labels"], mask=dev["mask"],
                   target_hidden=dev["target_hidden"], W_t=dev["W_t"],
-                  target_row=dev["target_row"])
+                  target_row=dev["target_row"], heads=prob.shifts)
     ref.forward()
     out = _outputs(prob.n_rows)
     B.lmhead_loss_fwd_noalloc(ref.problem, out["loss"], out["term"], out["lse"],
