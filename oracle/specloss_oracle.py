@@ -29,6 +29,8 @@ Readings taken where the pages are silent (each is listed in the design notes):
   not ignore_index (-100).  An unmasked row whose label (or target row) is
   out of range counts as "bad" and is treated as masked.
 * With no valid row the mean is 0 and every gradient is 0.
+* Aligned heads are laid out token-major: row ``(b*S + t)*K + k`` is head k at
+  position t of sequence b, paired with target position ``t + shift_k``.
 
 Parity pins: every function here is checked against closed forms, library
 routines or finite differences by ``tests/test_oracle_pins.py``.
