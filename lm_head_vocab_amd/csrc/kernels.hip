@@ -82,6 +82,16 @@ __device__ __forceinline__ void lse_merge_sq(float& m, float& s, float& q, float
   m = mn;
 }
 
+// log of the mixture m = (p + q) / 2 for the Jensen-Shannon terms.  Where
+// both probabilities are below the smallest normal float (exp underflow) the
+// terms p (log p - log m) and q (log q - log m) are below 1e-36 (x log x ->
+// 0), and any finite value serves; the hardware logarithm takes a denormal
+// input as 0, which would give 0 * inf.
+__device__ __forceinline__ float log_mixture(float p, float q) {
+  const float m = 0.5f * (p + q);
+  return m >= 1.17549435e-38f ? fast_log2(m) * kLn2 : 0.0f;
+}
+
 template <typename T>
 __device__ __forceinline__ void store4(T* dst, float a0, float a1, float a2, float a3);
 template <>
@@ -805,7 +815,7 @@ __global__ __launch_bounds__(128 * WNW, 1) void k_div(DivLaunch a) {
         if (need & SUM_KL) s_kl += p * (lp - lq);
         if (need & SUM_RKL) s_rkl += q * (lq - lp);
         if (need & (SUM_JSD | SUM_EQG)) {
-          const float lm = fast_log2(0.5f * (p + q)) * kLn2;
+          const float lm = log_mixture(p, q);
           if (need & SUM_JSD) s_jsd += 0.5f * (p * (lp - lm) + q * (lq - lm));
           if (need & SUM_EQG) s_eqg += 0.5f * q * (lq - lm);
         }
@@ -915,7 +925,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_div_heads(DivHeadsLaunch h) {
           if (need & SUM_KL) s_kl += p * (lp - lq);
           if (need & SUM_RKL) s_rkl += q * (lq - lp);
           if (need & (SUM_JSD | SUM_EQG)) {
-            const float lm = fast_log2(0.5f * (p + q)) * kLn2;
+            const float lm = log_mixture(p, q);
             if (need & SUM_JSD) s_jsd += 0.5f * (p * (lp - lm) + q * (lq - lm));
             if (need & SUM_EQG) s_eqg += 0.5f * q * (lq - lm);
           }
@@ -1003,7 +1013,7 @@ __device__ __forceinline__ float dz_elem(const RowCoef& c, const float* w, float
     if (w[2] != 0.0f) g += w[2] * (q - p);
     if (w[3] != 0.0f) g += w[3] * q * (lq - lp - c.rkl);
     if (w[4] != 0.0f) {
-      const float lm = fast_log2(0.5f * (p + q)) * kLn2;
+      const float lm = log_mixture(p, q);
       g += w[4] * q * (0.5f * (lq - lm) - c.eqg);
     }
     if (w[5] != 0.0f || w[6] != 0.0f || w[7] != 0.0f) {

@@ -64,9 +64,10 @@ def rel_frob(a: np.ndarray, b: np.ndarray) -> float:
 
 def check_tokens(gpu: np.ndarray, ref: np.ndarray, what: str) -> None:
     err = np.abs(gpu.astype(np.float64) - ref)
-    bad = err > TOKEN_RTOL * np.abs(ref) + TOKEN_ATOL
+    bad = ~(err <= TOKEN_RTOL * np.abs(ref) + TOKEN_ATOL)  # a NaN is out of tolerance too
+    worst = int(np.argmax(np.where(np.isnan(err), np.inf, err))) if err.size else 0
     assert not bad.any(), (f"{what}: {int(bad.sum())} rows out of tolerance; worst row "
-                           f"{int(np.argmax(err))}: gpu {gpu[np.argmax(err)]} ref {ref[np.argmax(err)]}")
+                           f"{worst}: gpu {gpu[worst]} ref {ref[worst]}")
 
 
 def check_flatness(gpu: np.ndarray, ref: np.ndarray, valid: np.ndarray) -> None:

@@ -706,3 +706,25 @@ def test_aligned_heads_share_target_tiles(case):
         assert torch.equal(a_f[valid], b_f[valid]), f"saved field {f}"
     assert np.array_equal(out["dh"], dh.cpu().numpy())
     assert np.array_equal(out["dW"], dW.cpu().numpy())
+
+
+@pytest.mark.parametrize("single", [False, True])
+def test_jsd_with_underflowing_probabilities(single):
+    """Logits spread over hundreds of nats: most p_v and q_v underflow to 0 in
+    fp32, where the Jensen-Shannon terms p log(p/m) and q log(q/m) must vanish
+    (x log x -> 0) rather than turn into 0 * inf; every output stays finite
+    and within the bar of the fp64 oracle (JSD is insensitive to a common
+    error in log p and log q, so fp32's resolution of such large logits does
+    not enter).  The vocabulary (777) ends inside a tile, so padded rows are
+    covered too."""
+    p = synthetic.make_problem("lk_hybrid_bf16_8b", n_rows=300, hidden_dim=128, vocab=777,
+                               weights={"jsd": 1.0})
+    wide = lambda x: synthetic.bf16_bits_to_f32(x).astype(np.float32)
+    p.W = synthetic.f32_to_bf16_bits(wide(p.W) * 300.0)
+    p.W_t = synthetic.f32_to_bf16_bits(wide(p.W_t) * 300.0)
+    ref = O.forward(p)
+    z = wide(p.hidden).astype(np.float64) @ wide(p.W).astype(np.float64).T
+    assert np.mean(z.max(axis=1, keepdims=True) - z > 110.0) > 0.3  # exp underflows in fp32
+    out = full_parity(p, max_chunk_rows=256, tag=f"jsd-underflow-{single}", single_call=single)
+    assert np.all(np.isfinite(out["loss"])) and np.all(np.isfinite(out["dh"]))
+    assert np.all(np.isfinite(out["dW"]))
