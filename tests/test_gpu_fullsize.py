@@ -57,10 +57,16 @@ def _sample_rows(n, seed, chunks):
                                          ("multihead_bf16_405b", False),
                                          ("ce_bf16_1b", True), ("ce_bf16_8b", True),
                                          ("lk_hybrid_bf16_8b", True),
-                                         ("multihead_bf16_405b", True)])
+                                         ("multihead_bf16_405b", True),
+                                         ("lk_hybrid_bf16_8b:kl_div", False),
+                                         ("lk_hybrid_bf16_8b:rkl", True),
+                                         ("lk_hybrid_bf16_8b:jsd", True)])
 def test_full_size_sampled(name, single):
-    """single: the same checks through the single call lmhead_loss_fwd_bwd."""
-    prob = synthetic.make_problem(name)
+    """single: the same checks through the single call lmhead_loss_fwd_bwd.
+    name:kind runs the workload's inputs with that loss kind alone (kl_div's
+    two-call forward takes one sweep; rkl and jsd stage log q - log p)."""
+    name, _, kind = name.partition(":")
+    prob = synthetic.make_problem(name, weights={kind: 1.0} if kind else None)
     N, H, V = prob.n_rows, prob.hidden_dim, prob.vocab
     say(f"[fullsize] {name} N={N} H={H} V={V} weights={prob.weights} single={single}")
     dev = to_device(prob)
