@@ -765,7 +765,9 @@ __global__ __launch_bounds__(256) void k_dz_stage(DzStageLaunch a) {
 // STAGE: also store q and d = q - p of every (row, vocab) for the logit
 // gradient (rounded to the storage type; d keeps the sign of q - p, zero on
 // ties, so the indicator [q < p] is unchanged by the rounding).
-template <typename T, bool STAGE, int WNW>
+// NEED != 0: the set of sums as a compile-time constant (the common sets),
+// so the per-element tests of `need` disappear; NEED == 0 reads a.need.
+template <typename T, bool STAGE, int WNW, uint32_t NEED = 0>
 __global__ __launch_bounds__(128 * WNW, 1) void k_div(DivLaunch a) {
   using Cfg = TileCfg<T, 256, 128, 1, WNW>;
   __shared__ __attribute__((aligned(16))) char smem[Cfg::LDS_BYTES];
@@ -784,7 +786,7 @@ __global__ __launch_bounds__(128 * WNW, 1) void k_div(DivLaunch a) {
   const int wm = wave / WNW, wn = wave % WNW;
   const int v_base = tm * Cfg::BM + wm * Cfg::WM;
   const bool tail = tm * Cfg::BM + Cfg::BM > a.vocab;
-  const uint32_t need = a.need;
+  const uint32_t need = NEED ? NEED : a.need;
 
   float sums[Cfg::FN][kNumSums];
 #pragma unroll
@@ -864,7 +866,7 @@ __global__ __launch_bounds__(128 * WNW, 1) void k_div(DivLaunch a) {
 // (the map puts the matching draft row there).  Per (vocabulary row, draft
 // row) the arithmetic is that of k_div, in the same order, so the sums and
 // staged values are the same bits.
-template <typename T, bool STAGE, int K>
+template <typename T, bool STAGE, int K, uint32_t NEED = 0>
 __global__ __launch_bounds__(kThreads, 1) void k_div_heads(DivHeadsLaunch h) {
   using CfgZ = TileCfg<T, 256, 64 * K>;
   using CfgU = TileCfg<T, 256, 64>;
@@ -886,7 +888,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_div_heads(DivHeadsLaunch h) {
   const int wm = wave >> 1, wn = wave & 1;
   const int v_base = tm * CfgU::BM + wm * CfgU::WM;
   const bool tail = tm * CfgU::BM + CfgU::BM > a.vocab;
-  const uint32_t need = a.need;
+  const uint32_t need = NEED ? NEED : a.need;  // as in k_div
   static_assert(CfgU::FN == 2 && CfgZ::FN == 2 * K && CfgU::WN == 32, "heads tile layout");
 
   // per (head, u fragment column): chunk row or -1, and the six sums
@@ -1804,10 +1806,8 @@ hipError_t launch_stats_dual(bool bf16, const DualStatsLaunch& a, hipStream_t s)
   return hipGetLastError();
 }
 
-#ifndef SPECLOSS_DIV_WNW
-#define SPECLOSS_DIV_WNW 2
-#endif
-constexpr int kDivWNW = SPECLOSS_DIV_WNW;
+// four waves (2 x 2); eight (2 x 4, two per SIMD) measured the same
+constexpr int kDivWNW = 2;
 
 hipError_t launch_heads_map(int32_t* map, int32_t tiles_n, int32_t n_heads, const int32_t* shifts,
                             int64_t jlo, int64_t r0, int32_t rows, hipStream_t s) {
@@ -1823,11 +1823,14 @@ hipError_t launch_div_heads(bool bf16, const DivHeadsLaunch& a, hipStream_t s) {
   if (!bf16 || a.n_heads < 2 || a.n_heads > 3) return hipErrorInvalidValue;
   const dim3 grid(grid_for_tiles(a.d.tiles_m * a.d.tiles_n)), block(kThreads);
   const bool stage = a.d.stage_q != nullptr;
+  constexpr uint32_t kTv = SUM_ALPHA | SUM_S;
   if (a.n_heads == 2) {
     if (stage) hipLaunchKernelGGL((k_div_heads<bf16_bits, true, 2>), grid, block, 0, s, a);
     else hipLaunchKernelGGL((k_div_heads<bf16_bits, false, 2>), grid, block, 0, s, a);
   } else {
-    if (stage) hipLaunchKernelGGL((k_div_heads<bf16_bits, true, 3>), grid, block, 0, s, a);
+    if (stage && a.d.need == kTv)
+      hipLaunchKernelGGL((k_div_heads<bf16_bits, true, 3, kTv>), grid, block, 0, s, a);
+    else if (stage) hipLaunchKernelGGL((k_div_heads<bf16_bits, true, 3>), grid, block, 0, s, a);
     else hipLaunchKernelGGL((k_div_heads<bf16_bits, false, 3>), grid, block, 0, s, a);
   }
   return hipGetLastError();
@@ -1837,8 +1840,15 @@ hipError_t launch_div(bool bf16, const DivLaunch& a, hipStream_t s) {
   constexpr int W = kDivWNW;
   const dim3 grid(grid_for_tiles(a.tiles_m * a.tiles_n)), block(128 * W);
   const bool stage = a.stage_q != nullptr;
+  // the second sweep's common sum sets (lk_hybrid; tv / nla) as constants:
+  // measured 2% faster than reading them per element
+  constexpr uint32_t kLk = SUM_ALPHA | SUM_S | SUM_KL, kTv = SUM_ALPHA | SUM_S;
   if (bf16) {
-    if (stage) hipLaunchKernelGGL((k_div<bf16_bits, true, W>), grid, block, 0, s, a);
+    if (stage && a.need == kLk)
+      hipLaunchKernelGGL((k_div<bf16_bits, true, W, kLk>), grid, block, 0, s, a);
+    else if (stage && a.need == kTv)
+      hipLaunchKernelGGL((k_div<bf16_bits, true, W, kTv>), grid, block, 0, s, a);
+    else if (stage) hipLaunchKernelGGL((k_div<bf16_bits, true, W>), grid, block, 0, s, a);
     else hipLaunchKernelGGL((k_div<bf16_bits, false, W>), grid, block, 0, s, a);
   } else {
     if (stage) hipLaunchKernelGGL((k_div<float, true, 2>), dim3(grid), dim3(256), 0, s, a);
