@@ -657,28 +657,38 @@ def _heads_problem(S, shifts, batch, H, V, weights, seed):
 
 
 @pytest.mark.parametrize("case", ["k3_single", "k3_two_calls", "k2_batch_single",
-                                  "k3_far_shifts_single", "k3_lean_single"])
+                                  "k3_far_shifts_single", "k3_lean_single", "k3_tv_single",
+                                  "k4_single_per_row", "k3_f32_two_calls_per_row"])
 def test_aligned_heads_share_target_tiles(case):
     """Declared token-major heads: the second sweep computes each target tile once
     for the heads it serves (k_div_heads) instead of once per row.  Against the
     oracle (the bar), and bit for bit against the same problem without the
     declaration (per-row second sweep): losses, terms, saved state, gradients.
-    256-row chunks split tokens between chunks (256 is no multiple of 3)."""
+    256-row chunks split tokens between chunks (256 is no multiple of 3).
+    Four heads and fp32 inputs keep the per-row sweep (same checks)."""
     import lm_head_vocab_amd as L
-    single = case.endswith("single")
+    single = "single" in case
     shifts, batch = {"k3_single": ((1, 2, 3), 1), "k3_two_calls": ((1, 2, 3), 1),
                      "k2_batch_single": ((2, 0), 3), "k3_far_shifts_single": ((0, 7, 70), 2),
-                     "k3_lean_single": ((1, 2, 3), 1)}[case]
+                     "k3_lean_single": ((1, 2, 3), 1), "k3_tv_single": ((1, 2, 3), 1),
+                     "k4_single_per_row": ((1, 2, 3, 4), 1),
+                     "k3_f32_two_calls_per_row": ((1, 2, 3), 1)}[case]
     weights = ({"tv": 0.7, "ce": 0.2, "kl_div": 0.4, "rkl": 0.3, "jsd": 0.5, "nla": 0.2,
-                "lk_hybrid": 0.6, "ce_label": 0.1} if case != "k2_batch_single"
-               else {"lk_hybrid": 1.0, "ce": 0.3})
+                "lk_hybrid": 0.6, "ce_label": 0.1} if case not in ("k2_batch_single", "k3_tv_single")
+               else {"lk_hybrid": 1.0, "ce": 0.3} if case == "k2_batch_single"
+               else {"tv": 0.9, "ce": 0.1})  # tv + ce: the sum set taken as a constant
     S = 310 if batch == 1 else 170
     p = _heads_problem(S, shifts, batch, 128, 900, weights, seed=71)
+    if "f32" in case:
+        p.dtype = "f32"
+        for f in ("hidden", "W", "target_hidden", "W_t"):
+            setattr(p, f, synthetic.bf16_bits_to_f32(getattr(p, f)).copy())
     flags = L.binding.FLAG_NO_COPIES if case == "k3_lean_single" else None
-    stage = "div_heads_stage" if single else "div_heads"
+    shared = "div_heads_stage" if single else "div_heads"
     plain = "div_stage" if single else "div"
+    stage, absent = (plain, shared) if case.endswith("per_row") else (shared, plain)
     out = full_parity(p, max_chunk_rows=256, tag=f"heads-{case}", single_call=single, flags=flags,
-                      expect_kernels=([stage], [plain]))
+                      expect_kernels=([stage], [absent]))
     run = out["run"]
     dev = to_device(p)
     ref = make_run(p, dev, max_chunk_rows=256, heads=None,
@@ -695,7 +705,7 @@ def test_aligned_heads_share_target_tiles(case):
     names = {n for n, _, _ in trace.read()}
     ref.problem.trace = None
     trace.close()
-    assert plain in names and stage not in names, names
+    assert plain in names and shared not in names, names
     assert torch.equal(run.loss, ref.loss)
     assert torch.equal(run.term, ref.term)
     assert torch.equal(run.counts, ref.counts)
