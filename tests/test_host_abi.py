@@ -373,3 +373,20 @@ def test_fwd_bwd_rejects_a_forward_only_workspace(lib, kind):
     rc = lib.lmhead_loss_fwd_bwd(ctypes.byref(p), 0x100000, ws, 0x200000, None, None, None,
                                  0x300000, None, None, 0x1000, 0x4000, B.F32, 0x5000, 0, None)
     assert rc == E_WS
+
+
+def test_size_limits(lib):
+    """N, V and H below 2^30 are accepted (and the sizing arithmetic stays in
+    range); at 2^30 the library answers SPECLOSS_E_UNSUPPORTED."""
+    big = (1 << 30) - 64
+    for kw in (dict(N=big), dict(V=big), dict(H=big)):
+        rc, ws = _ws(lib, _problem(**kw))
+        assert rc == 0 and 0 < ws < (1 << 62), (kw, rc, ws)
+    for kw in (dict(N=1 << 30), dict(V=1 << 30), dict(H=1 << 30)):
+        assert _ws(lib, _problem(**kw))[0] == E_UNSUP, kw
+    # the default policy at the largest row count: at least four chunks
+    p = _problem(N=big, V=128256, H=4096)
+    rc, ws = _ws(lib, p)
+    rows, lay = ctypes.c_int64(), ctypes.c_int32()
+    assert lib.lmhead_loss_chunk(ctypes.byref(p), ws, 2, ctypes.byref(rows), ctypes.byref(lay)) == 0
+    assert 0 < rows.value <= 8192
