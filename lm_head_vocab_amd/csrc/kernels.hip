@@ -177,7 +177,7 @@ __device__ __forceinline__ void store_tile_rows(const f32x4_t (&acc)[Cfg::FM][Cf
   constexpr int kStride = Cfg::BN * 4 + 16;
   constexpr int kPieces = Cfg::BN / 8;  // 8-value pieces per row
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / Cfg::WNW, wn = wave % Cfg::WNW;
 #pragma unroll 1
   for (int h = 0; h < 2; ++h) {
     if (wm == h) {
@@ -193,7 +193,7 @@ __device__ __forceinline__ void store_tile_rows(const f32x4_t (&acc)[Cfg::FM][Cf
           }
     }
     __syncthreads();
-    for (int idx = threadIdx.x; idx < kHalf * kPieces; idx += kThreads) {
+    for (int idx = threadIdx.x; idx < kHalf * kPieces; idx += Cfg::THREADS) {
       const int row = idx / kPieces, pc = idx % kPieces;
       const f32x4_t x0 = *reinterpret_cast<const f32x4_t*>(smem + row * kStride + pc * 32);
       const f32x4_t x1 = *reinterpret_cast<const f32x4_t*>(smem + row * kStride + pc * 32 + 16);
@@ -216,10 +216,10 @@ __device__ __forceinline__ void store_tile_rows(const f32x4_t (&acc)[Cfg::FM][Cf
 // ============================================================================
 // TARGET (the target distribution p): also the lowest-index argmax and the sum
 // of e^2, e = exp(u - m_tile), from which the flatness score is formed.
-template <typename T, bool TARGET>
-__global__ __launch_bounds__(kThreads, 1) void k_stats(StatsLaunch a) {
+template <typename T, bool TARGET, int WNW = 2>
+__global__ __launch_bounds__(128 * WNW, 1) void k_stats(StatsLaunch a) {
   constexpr bool ARGMAX = TARGET;
-  using Cfg = TileCfg<T, 256, 256, kStatsLoadGap>;
+  using Cfg = TileCfg<T, 256, 256, (WNW == 2 ? kStatsLoadGap : 1), WNW>;
   __shared__ __attribute__((aligned(16))) char smem[Cfg::LDS_BYTES];
   int tm, tn;
   if (!tile_of(a.tiles_m, a.tiles_n, kGroupM, tm, tn)) return;
@@ -230,7 +230,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_stats(StatsLaunch a) {
                         smem);
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WNW, wn = wave % WNW;
   const int v_base = tm * Cfg::BM + wm * Cfg::WM;
   const bool tail = tm * Cfg::BM + Cfg::BM > a.vocab;
 
@@ -460,7 +460,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_stats_dual(DualStatsLaunch a) {
 // as 16-byte pieces of rows through the LDS-staged row epilogue.
 template <typename T, int WNW>
 __global__ __launch_bounds__(128 * WNW, 1) void k_stats_stage(StatsStageLaunch a) {
-  using Cfg = TileCfg<T, 256, 256, kStatsLoadGap, WNW>;
+  // four waves: a load every three MFMAs; eight: every MFMA (as the contractions)
+  using Cfg = TileCfg<T, 256, 256, (WNW == 2 ? kStatsLoadGap : 1), WNW>;
   constexpr int kRowsSmem = (Cfg::BM / 2) * (Cfg::BN * 4 + 16);  // store_tile_rows staging
   constexpr int kSmem = Cfg::LDS_BYTES > kRowsSmem ? Cfg::LDS_BYTES : kRowsSmem;
   __shared__ __attribute__((aligned(16))) char smem[kSmem];
@@ -1764,11 +1765,15 @@ hipError_t noalloc_scratch(void** ptr) {
 // ============================================================================
 // launchers
 // ============================================================================
+// bf16 pass 1 without staging: eight waves too (lk_hybrid stats_p and stats_q
+// 1.6 % faster than with four)
+constexpr int kStatsWNW = 4;
 hipError_t launch_stats(bool bf16, bool target, const StatsLaunch& a, hipStream_t s) {
   const dim3 grid(grid_for_tiles(a.tiles_m * a.tiles_n)), block(kThreads);
+  constexpr int W = kStatsWNW;
   if (bf16) {
-    if (target) hipLaunchKernelGGL((k_stats<bf16_bits, true>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((k_stats<bf16_bits, false>), grid, block, 0, s, a);
+    if (target) hipLaunchKernelGGL((k_stats<bf16_bits, true, W>), grid, dim3(128 * W), 0, s, a);
+    else hipLaunchKernelGGL((k_stats<bf16_bits, false, W>), grid, dim3(128 * W), 0, s, a);
   } else {
     if (target) hipLaunchKernelGGL((k_stats<float, true>), grid, block, 0, s, a);
     else hipLaunchKernelGGL((k_stats<float, false>), grid, block, 0, s, a);
@@ -1776,9 +1781,13 @@ hipError_t launch_stats(bool bf16, bool target, const StatsLaunch& a, hipStream_
   return hipGetLastError();
 }
 
+// bf16 pass 1 with staging runs eight waves (two per SIMD): 3 % faster than
+// four at the 8B shape despite a few spills outside its inner loop
+constexpr int kStageWNW = 4;
 hipError_t launch_stats_stage(bool bf16, const StatsStageLaunch& a, hipStream_t s) {
   const dim3 grid(grid_for_tiles(a.st.tiles_m * a.st.tiles_n)), block(kThreads);
-  if (bf16) hipLaunchKernelGGL((k_stats_stage<bf16_bits, 2>), grid, block, 0, s, a);
+  if (bf16) hipLaunchKernelGGL((k_stats_stage<bf16_bits, kStageWNW>), grid,
+                               dim3(128 * kStageWNW), 0, s, a);
   else hipLaunchKernelGGL((k_stats_stage<float, 2>), grid, block, 0, s, a);
   return hipGetLastError();
 }
@@ -1873,8 +1882,8 @@ hipError_t launch_dz(bool bf16, bool dual, const DzLaunch& a, hipStream_t s) {
 // waves, 128 x 64 each, two per SIMD).  Measured against four waves at the 8B
 // shape: gemm_dW 26.3 vs 27.5 ms per step (its fp32 read-modify-write
 // epilogue runs on twice the threads), gemm_dh about 1% faster; the MN-major
-// variants keep four waves (eight spill registers), as does pass 1 (slower
-// with eight: its softmax epilogue spills).
+// variants keep four waves (eight spill registers).  bf16 pass 1 runs eight
+// too, with a load every MFMA (kStageWNW, kStatsWNW).
 constexpr int kGemmWNW = 4;
 
 template <int ROLE>
