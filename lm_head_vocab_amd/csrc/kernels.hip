@@ -1030,9 +1030,9 @@ __device__ __forceinline__ float dz_elem(const RowCoef& c, const float* w, float
   return g;
 }
 
-template <typename T, bool DUAL>
-__global__ __launch_bounds__(kThreads, 1) void k_dz(DzLaunch a) {
-  using Cfg = TileCfg<T, 256, (DUAL ? 128 : 256)>;
+template <typename T, bool DUAL, int WNW = 2>
+__global__ __launch_bounds__(128 * WNW, 1) void k_dz(DzLaunch a) {
+  using Cfg = TileCfg<T, 256, (DUAL ? 128 : 256), 1, WNW>;
   constexpr int kRowsSmem = (Cfg::BM / 2) * (Cfg::BN * 4 + 16);  // store_tile_rows staging
   constexpr int kSmem = Cfg::LDS_BYTES > kRowsSmem ? Cfg::LDS_BYTES : kRowsSmem;
   __shared__ __attribute__((aligned(16))) char smem[kSmem];
@@ -1051,7 +1051,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_dz(DzLaunch a) {
   }
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WNW, wn = wave % WNW;
   const int v_base = tm * Cfg::BM + wm * Cfg::WM;
   T* dz = static_cast<T*>(a.dz);
   T* dzt = static_cast<T*>(a.dzt);
@@ -1869,8 +1869,10 @@ hipError_t launch_div(bool bf16, const DivLaunch& a, hipStream_t s) {
 hipError_t launch_dz(bool bf16, bool dual, const DzLaunch& a, hipStream_t s) {
   const dim3 grid(grid_for_tiles(a.tiles_m * a.tiles_n)), block(kThreads);
   if (bf16) {
+    // the single-contraction recompute runs eight waves like pass 1 (two-call
+    // CE step 0.3 % faster); the dual one keeps four
     if (dual) hipLaunchKernelGGL((k_dz<bf16_bits, true>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((k_dz<bf16_bits, false>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((k_dz<bf16_bits, false, 4>), grid, dim3(512), 0, s, a);
   } else {
     if (dual) hipLaunchKernelGGL((k_dz<float, true>), grid, block, 0, s, a);
     else hipLaunchKernelGGL((k_dz<float, false>), grid, block, 0, s, a);
