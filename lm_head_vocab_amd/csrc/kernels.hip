@@ -1883,18 +1883,22 @@ hipError_t launch_dz(bool bf16, bool dual, const DzLaunch& a, hipStream_t s) {
 // Waves along N of the plain bf16 contractions with K-major operands: 4 (eight
 // waves, 128 x 64 each, two per SIMD).  Measured against four waves at the 8B
 // shape: gemm_dW 26.3 vs 27.5 ms per step (its fp32 read-modify-write
-// epilogue runs on twice the threads), gemm_dh about 1% faster; the MN-major
-// variants keep four waves (eight spill registers).  bf16 pass 1 runs eight
-// too, with a load every MFMA (kStageWNW, kStatsWNW).
+// epilogue runs on twice the threads), gemm_dh about 1% faster.  The
+// contractions with MN-major operands (W or the hidden rows read in place)
+// run eight waves too despite a few spills outside the inner loop: the dh
+// contraction of the 405B shape (W in place) 56.1 -> 46.7 ms per step.  bf16
+// pass 1 runs eight as well, with a load every MFMA (kStageWNW, kStatsWNW).
 constexpr int kGemmWNW = 4;
+constexpr int kLeanWNW = 4;
 
 template <int ROLE>
 static void launch_gemm_role(bool bf16, const GemmLaunch& a, hipStream_t s) {
   constexpr int W = kGemmWNW;
   const dim3 grid(grid_for_tiles(a.tiles_m * a.splits * a.tiles_n)), block(128 * W);
   if (bf16 && a.lean) {
-    if (a.out_bf16) hipLaunchKernelGGL((k_gemm<bf16_bits, bf16_bits, ROLE, true, 2>), grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((k_gemm<bf16_bits, float, ROLE, true, 2>), grid, dim3(256), 0, s, a);
+    constexpr int LW = kLeanWNW;
+    if (a.out_bf16) hipLaunchKernelGGL((k_gemm<bf16_bits, bf16_bits, ROLE, true, LW>), grid, dim3(128 * LW), 0, s, a);
+    else hipLaunchKernelGGL((k_gemm<bf16_bits, float, ROLE, true, LW>), grid, dim3(128 * LW), 0, s, a);
   } else if (bf16) {
     if (a.out_bf16) hipLaunchKernelGGL((k_gemm<bf16_bits, bf16_bits, ROLE, false, W>), grid, block, 0, s, a);
     else hipLaunchKernelGGL((k_gemm<bf16_bits, float, ROLE, false, W>), grid, block, 0, s, a);
