@@ -329,8 +329,8 @@ def blas_reference(h, W, labels, nc, N, kernels):
             "ours_tflops": ours}
 
 
-FLOP_KERNELS = ("stats_q", "stats_p", "stats_stage", "stats_dual", "div", "div_stage",
-                "div_heads", "div_heads_stage", "dz", "gemm_dh", "gemm_dW")
+FLOP_KERNELS = ("stats_q", "stats_p", "stats_stage", "stats_dual", "div", "div_heads", "dz",
+                "gemm_dh", "gemm_dW")
 
 
 def summarize_trace(entries, steps):

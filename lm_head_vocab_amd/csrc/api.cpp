@@ -41,8 +41,7 @@ struct KindSet {
   bool target = false;  // any kind needing the target side
   bool pass2 = false;   // any divergence needing a second sweep
   bool dual_bwd = false;
-  bool stage_div = false;  // single call: pass 2 stages q and q - p (every divergence)
-  bool stage_log = false;  // ... and log q - log p (rkl, jsd)
+  bool stage_div = false;  // single call: pass 1 keeps both raw logit rows (every divergence)
   // the only sums needed are the Kullback-Leibler ones: the two-call forward
   // takes them from a dual pass 1 (no second sweep) when each row has its
   // own target row
@@ -69,7 +68,6 @@ KindSet kinds_of(const float* w) {
   k.ratio_only = k.pass2 && (k.need & ~(SUM_KL | SUM_RKL)) == 0;
   k.dual_bwd = (k.active & ~((1u << SPECLOSS_CE_LABEL) | (1u << SPECLOSS_CE_ARGMAX_P))) != 0;
   k.stage_div = k.dual_bwd;
-  k.stage_log = on(SPECLOSS_RKL) || on(SPECLOSS_JSD);
   return k;
 }
 
@@ -151,8 +149,11 @@ struct Layout {
   size_t pz, pu, p2, zy, hmap, fwd_end;
   // backward
   size_t wt, ht, dz, dzt, dhp, bwd_end;
-  // single-call forward+backward: forward partials and backward buffers at once
-  size_t f_pz, f_pu, f_p2, f_zy, f_hmap, f_wt, f_ht, f_dz, f_dd, f_dl, f_dzt, f_rs, f_dhp, fused_end;
+  // single-call forward+backward: forward partials and backward buffers at once;
+  // the divergences keep the chunk's raw fp32 logits (f_zr: Nc draft rows,
+  // f_ur: Nu target rows) and the target partials have pu_cols columns
+  int64_t Nu, pu_cols;
+  size_t f_pz, f_pu, f_p2, f_zy, f_wt, f_ht, f_dz, f_zr, f_ur, f_dzt, f_rs, f_dhp, fused_end;
 };
 
 // The second sweep of a problem with aligned heads shares target tiles
@@ -173,11 +174,25 @@ void shift_range(const specloss_problem* p, int32_t& lo, int32_t& hi) {
   }
 }
 
-int64_t heads_map_entries(const specloss_problem* p, int64_t Nc) {
+// Target rows [jlo, jhi) that chunk rows [r0, r0 + rows) of a problem with
+// aligned heads use (token-major rows: row T K + k has target T + shift_k).
+void heads_span(const specloss_problem* p, int64_t r0, int64_t rows, int64_t& jlo, int64_t& jhi) {
+  const int32_t K = p->n_heads;
+  int32_t s_lo, s_hi;
+  shift_range(p, s_lo, s_hi);
+  jlo = r0 / K + s_lo;
+  jhi = (r0 + rows - 1) / K + 1 + s_hi;
+}
+
+// at most Nc / K + 2 tokens plus the spread of the shifts
+int64_t heads_span_cap(const specloss_problem* p, int64_t Nc) {
   int32_t lo, hi;
   shift_range(p, lo, hi);
-  const int64_t span = Nc / p->n_heads + 2 + (hi - lo);
-  return cdiv(span, 64) * 64 * p->n_heads;
+  return Nc / p->n_heads + 2 + (hi - lo);
+}
+
+int64_t heads_map_entries(const specloss_problem* p, int64_t Nc) {
+  return cdiv(heads_span_cap(p, Nc), 64) * 64 * p->n_heads;
 }
 
 // Split-K slices of the dh contraction of a chunk of Nc rows: its grid has
@@ -245,16 +260,17 @@ Layout plan(const specloss_problem* p, const KindSet& k, int64_t Nc,
   L.dhp = take(dhp_bytes);
   L.bwd_end = o;
   o = L.head_end;
+  L.Nu = k.stage_div ? (heads_pass2(p, k) ? heads_span_cap(p, Nc) : Nc) : 0;
+  L.pu_cols = L.Nu > Nc ? L.Nu : Nc;
   L.f_pz = take(2 * tile_cols);
-  L.f_pu = take(k.target ? 4 * tile_cols : 0);
+  L.f_pu = take(k.target ? 4 * (size_t)L.Tv * L.pu_cols * 4 : 0);
   L.f_p2 = take(k.stage_div ? (size_t)kNumSums * tile_cols : 0);
   L.f_zy = take(2 * (size_t)Nc * 4);
-  L.f_hmap = take(k.stage_div ? hmap_bytes : 0);
   L.f_wt = take(L.wt_copy ? (size_t)L.H * L.Vp * L.es : 0);
   L.f_ht = take(L.dw_copies ? (size_t)L.H * Nc * L.es : 0);
   L.f_dz = take((size_t)Nc * L.Vp * L.es);
-  L.f_dd = take(k.stage_div ? (size_t)Nc * L.Vp * L.es : 0);
-  L.f_dl = take(k.stage_log ? (size_t)Nc * L.Vp * L.es : 0);
+  L.f_zr = take(k.stage_div ? (size_t)Nc * L.Vp * 4 : 0);
+  L.f_ur = take(k.stage_div ? (size_t)L.Nu * L.Vp * 4 : 0);
   L.f_dzt = take(L.dw_copies ? (size_t)L.Vp * Nc * L.es : 0);
   L.f_rs = take(4 * (size_t)Nc * 4);
   L.f_dhp = take(dhp_bytes);
@@ -407,6 +423,12 @@ GemmOperand target_operand(const specloss_problem* p, int64_t r0, int64_t rows, 
   return op(offset_rows(p->target_hidden, r0, p->hidden, es), p->hidden, rows);
 }
 
+#define TRY(expr)                   \
+  do {                              \
+    const int rc_ = (expr);         \
+    if (rc_) return rc_;            \
+  } while (0)
+
 #define HIP_TRY(expr)                                   \
   do {                                                  \
     if ((expr) != hipSuccess) return SPECLOSS_E_HIP;    \
@@ -415,15 +437,14 @@ GemmOperand target_operand(const specloss_problem* p, int64_t r0, int64_t rows, 
 enum KernelId : int32_t {
   K_VALIDITY, K_STATS_Q, K_STATS_P, K_COMBINE1, K_ROWDOT, K_DIV, K_COMBINE2, K_REDUCE, K_COPY,
   K_SEED, K_TRANSPOSE_W, K_TRANSPOSE_H, K_DZ, K_GEMM_DH, K_GEMM_DW, K_STATS_STAGE, K_DZ_STAGE,
-  K_DIV_STAGE, K_DZ_DIV, K_TILE_SUM, K_SUM_PARTS, K_TARGET_GATHER, K_STAGE_FIX, K_STATS_DUAL,
-  K_DIV_HEADS, K_DIV_HEADS_STAGE, K_HEADS_MAP, K_NUM_IDS
+  K_TILE_SUM, K_SUM_PARTS, K_TARGET_GATHER, K_STAGE_FIX, K_STATS_DUAL, K_DIV_HEADS, K_HEADS_MAP,
+  K_DIV_RAW, K_DZ_RAW, K_SPAN_CARRY, K_NUM_IDS
 };
 const char* const kKernelNames[K_NUM_IDS] = {
     "validity", "stats_q", "stats_p", "combine1", "rowdot", "div", "combine2", "reduce",
     "copy_lse", "seed", "transpose_W", "transpose_h", "dz", "gemm_dh", "gemm_dW",
-    "stats_stage", "dz_stage", "div_stage", "dz_div", "tile_sum", "sum_partials",
-    "target_gather", "stage_fix", "stats_dual", "div_heads", "div_heads_stage",
-    "heads_map"};
+    "stats_stage", "dz_stage", "tile_sum", "sum_partials", "target_gather", "stage_fix",
+    "stats_dual", "div_heads", "heads_map", "div_raw", "dz_raw", "span_carry"};
 
 // Brackets launches with the trace's events when the problem carries one.
 struct Tracer {
@@ -542,11 +563,6 @@ int launch_validity_for(const specloss_problem* p, const KindSet& k, const Saved
   return SPECLOSS_OK;
 }
 
-// Forward of chunk rows [r0, r0 + rows): pass 1 (q side; p side with argmax
-// and flatness), merge, label-logit gather, pass 2 and the per-row losses.
-// Staging for the logit gradient ([Nc][Vp] buffers): with `stage` alone,
-// pass 1 stores e = exp(z - m_tile) there; with `stage` and `stage_d`,
-// pass 2 stores q there and q - p in stage_d.
 // Pass-1 contractions of chunk rows [r0, r0 + rows) into the per-(tile, row)
 // partials b.pz (and b.pu for the target side); `stage` as for fwd_chunk.
 int launch_pass1(const specloss_problem* p, const KindSet& k, const Layout& L, const FwdBufs& b,
@@ -626,10 +642,9 @@ int launch_pass1_dual(const specloss_problem* p, const Layout& L, const FwdBufs&
 }
 
 // Pass-2 divergence sums of chunk rows [r0, r0 + rows) into b.p2, with the
-// final logsumexps in `sv`; stage_q / stage_d as for fwd_chunk (or null).
+// final logsumexps in `sv` (the second sweep recomputes both tiles).
 int launch_pass2(const specloss_problem* p, const KindSet& k, const Layout& L, const FwdBufs& b,
-                 const SavedView& sv, int64_t r0, int64_t rows, void* stage_q, void* stage_d,
-                 Tracer& tr, hipStream_t stream, void* stage_l = nullptr) {
+                 const SavedView& sv, int64_t r0, int64_t rows, Tracer& tr, hipStream_t stream) {
   const bool bf16 = p->in_dtype == SPECLOSS_BF16;
   const int64_t H = L.H, Nc = b.Nc;
   DivLaunch dv{};
@@ -648,10 +663,6 @@ int launch_pass2(const specloss_problem* p, const KindSet& k, const Layout& L, c
   dv.need = k.need;
   dv.part = b.p2;
   dv.part_stride = L.Tv * Nc;
-  dv.stage_q = stage_d ? stage_q : nullptr;
-  dv.stage_d = stage_d;
-  dv.stage_l = stage_d ? stage_l : nullptr;
-  dv.ld_stage = L.Vp;
   if (heads_pass2(p, k) && b.hmap) {
     // aligned heads: target rows [jlo, jhi) serve the chunk's rows, each
     // target tile computed once
@@ -676,35 +687,22 @@ int launch_pass2(const specloss_problem* p, const KindSet& k, const Layout& L, c
     hv.jlo = jlo;
     hv.r0 = r0;
     hv.rows = (int32_t)rows;
-    TRACED(tr, stage_d ? K_DIV_HEADS_STAGE : K_DIV_HEADS,
-           2.0 * (double)(rows + (jhi - jlo)) * H * p->vocab, launch_div_heads(bf16, hv, stream));
+    TRACED(tr, K_DIV_HEADS, 2.0 * (double)(rows + (jhi - jlo)) * H * p->vocab,
+           launch_div_heads(bf16, hv, stream));
     return SPECLOSS_OK;
   }
-  TRACED(tr, stage_d ? K_DIV_STAGE : K_DIV, 4.0 * rows * H * p->vocab,
-         launch_div(bf16, dv, stream));
+  TRACED(tr, K_DIV, 4.0 * rows * H * p->vocab, launch_div(bf16, dv, stream));
   return SPECLOSS_OK;
 }
 
-int fwd_chunk(const specloss_problem* p, const KindSet& k, const Layout& L, const FwdBufs& b,
-              const SavedView& sv, float* loss, float* terms, int64_t r0, int64_t rows,
-              void* stage, void* stage_d, Tracer& tr, hipStream_t stream,
-              void* stage_l = nullptr) {
-  const bool bf16 = p->in_dtype == SPECLOSS_BF16;
-  const int64_t H = L.H, Nc = b.Nc;
-  const int64_t tile_cols = L.Tv * Nc;
+// Merge of a chunk's pass-1 partials: both sides when each row has its own
+// target row (with the log-ratio sums of the dual pass 1 when `dual`), the
+// draft side plus the gathered per-target-row statistics otherwise.
+int merge_pass1(const specloss_problem* p, const KindSet& k, const Layout& L, const FwdBufs& b,
+                const SavedView& sv, int64_t r0, int64_t rows, bool dual, Tracer& tr,
+                hipStream_t stream) {
+  const int64_t Nc = b.Nc, tile_cols = L.Tv * Nc;
   const bool own_target = k.target && !L.shared_target;
-  // kl_div / rkl as the only divergences of a forward without staging: both
-  // sides in one pass that also yields the divergences
-  const bool dual = k.ratio_only && own_target && !stage && !stage_d;
-  if (dual) {
-    const int rc = launch_pass1_dual(p, L, b, r0, rows, tr, stream);
-    if (rc) return rc;
-  } else {
-    const int rc = launch_pass1(p, k, L, b, r0, rows, stage_d ? nullptr : stage, tr, stream,
-                                !own_target);
-    if (rc) return rc;
-  }
-
   Combine1Launch c1{};
   c1.tiles_m = (int32_t)L.Tv;
   c1.ncols = (int32_t)rows;
@@ -746,35 +744,45 @@ int fwd_chunk(const specloss_problem* p, const KindSet& k, const Layout& L, cons
     tg.flat = sv.flat;
     TRACED(tr, K_TARGET_GATHER, (double)rows * 24, launch_target_gather(tg, stream));
   }
+  return SPECLOSS_OK;
+}
 
+// The label logit z_y (ce_label) and z at argmax p (ce) of each chunk row.
+int gather_label_logits(const specloss_problem* p, const KindSet& k, const Layout& L,
+                        const FwdBufs& b, const SavedView& sv, int64_t r0, int64_t rows,
+                        Tracer& tr, hipStream_t stream) {
   const bool ce_lab = (k.active >> SPECLOSS_CE_LABEL) & 1u;
   const bool ce_arg = (k.active >> SPECLOSS_CE_ARGMAX_P) & 1u;
-  if (ce_lab || ce_arg) {
-    RowdotLaunch rd{};
-    rd.W = p->W;
-    rd.h = offset_rows(p->hidden_states, r0, H, L.es);
-    rd.H = H;
-    rd.ncols = (int32_t)rows;
-    rd.vocab = (int32_t)p->vocab;
-    rd.y1 = ce_lab ? sv.y_label + r0 : nullptr;
-    rd.y2 = ce_arg ? sv.y_arg + r0 : nullptr;
-    rd.out1 = b.zy;
-    rd.out2 = b.zy + Nc;
-    TRACED(tr, K_ROWDOT, 2.0 * rows * H * L.es * ((ce_lab ? 1 : 0) + (ce_arg ? 1 : 0)),
-           launch_rowdot(bf16, rd, stream));
-  }
+  if (!ce_lab && !ce_arg) return SPECLOSS_OK;
+  RowdotLaunch rd{};
+  rd.W = p->W;
+  rd.h = offset_rows(p->hidden_states, r0, L.H, L.es);
+  rd.H = L.H;
+  rd.ncols = (int32_t)rows;
+  rd.vocab = (int32_t)p->vocab;
+  rd.y1 = ce_lab ? sv.y_label + r0 : nullptr;
+  rd.y2 = ce_arg ? sv.y_arg + r0 : nullptr;
+  rd.out1 = b.zy;
+  rd.out2 = b.zy + b.Nc;
+  TRACED(tr, K_ROWDOT, 2.0 * rows * L.H * L.es * ((ce_lab ? 1 : 0) + (ce_arg ? 1 : 0)),
+         launch_rowdot(p->in_dtype == SPECLOSS_BF16, rd, stream));
+  return SPECLOSS_OK;
+}
 
-  if (k.pass2 && !dual) {
-    const int rc = launch_pass2(p, k, L, b, sv, r0, rows, stage, stage_d, tr, stream, stage_l);
-    if (rc) return rc;
-  }
-
+// Per-row weighted losses, unweighted terms and saved sums of a chunk from
+// the pass-2 partials (tiles_m tile rows of them).
+int combine_losses(const specloss_problem* p, const KindSet& k, const Layout& L, const FwdBufs& b,
+                   const SavedView& sv, float* loss, float* terms, int64_t r0, int64_t rows,
+                   int32_t tiles_m, Tracer& tr, hipStream_t stream) {
+  const int64_t Nc = b.Nc;
+  const bool ce_lab = (k.active >> SPECLOSS_CE_LABEL) & 1u;
+  const bool ce_arg = (k.active >> SPECLOSS_CE_ARGMAX_P) & 1u;
   Combine2Launch c2{};
-  c2.tiles_m = dual ? 1 : (int32_t)L.Tv;  // dual: the divergences themselves, in tile row 0
+  c2.tiles_m = tiles_m;
   c2.ncols = (int32_t)rows;
   c2.ldp = (int32_t)Nc;
   c2.part = b.p2;
-  c2.part_stride = tile_cols;
+  c2.part_stride = L.Tv * Nc;
   c2.need = k.need;
   memcpy(c2.w, p->weights, sizeof(c2.w));
   c2.flags = sv.flags + r0;
@@ -792,6 +800,159 @@ int fwd_chunk(const specloss_problem* p, const KindSet& k, const Layout& L, cons
   TRACED(tr, K_COMBINE2, (double)rows * 4 * (2 + __builtin_popcount(k.need) * c2.tiles_m),
          launch_combine2(c2, stream));
   return SPECLOSS_OK;
+}
+
+// Forward of chunk rows [r0, r0 + rows): pass 1 (q side; p side with argmax
+// and flatness), merge, label-logit gather, pass 2 and the per-row losses.
+// With `stage` ([Nc][Vp], label / argmax cross-entropies of the single call)
+// pass 1 also stores e = exp(z - m_tile) there for the logit gradient.
+int fwd_chunk(const specloss_problem* p, const KindSet& k, const Layout& L, const FwdBufs& b,
+              const SavedView& sv, float* loss, float* terms, int64_t r0, int64_t rows,
+              void* stage, Tracer& tr, hipStream_t stream) {
+  const bool own_target = k.target && !L.shared_target;
+  // kl_div / rkl as the only divergences of a forward without staging: both
+  // sides in one pass that also yields the divergences
+  const bool dual = k.ratio_only && own_target && !stage;
+  if (dual) TRY(launch_pass1_dual(p, L, b, r0, rows, tr, stream));
+  else TRY(launch_pass1(p, k, L, b, r0, rows, stage, tr, stream, !own_target));
+  TRY(merge_pass1(p, k, L, b, sv, r0, rows, dual, tr, stream));
+  TRY(gather_label_logits(p, k, L, b, sv, r0, rows, tr, stream));
+  if (k.pass2 && !dual) TRY(launch_pass2(p, k, L, b, sv, r0, rows, tr, stream));
+  // dual: the divergences themselves, in tile row 0
+  return combine_losses(p, k, L, b, sv, loss, terms, r0, rows, dual ? 1 : (int32_t)L.Tv, tr,
+                        stream);
+}
+
+// Forward of chunk rows [r0, r0 + rows) for the divergences in the single
+// call.  Pass 1 of each side keeps the raw fp32 logits (z into zr, u into
+// ur, both [.][Vp]), so the second sweep (k_div_raw) and later the logit
+// gradient read them instead of computing both contractions again (blog
+// "Backward pass": at most chunk x vocab x 2 logits-sized values are held,
+// here in fp32).  With aligned heads the target side runs once over the
+// chunk's span of target rows [jlo, jhi): its statistics are merged per
+// target row and gathered, and ur holds one row per token of the span.  Other
+// shared target rows take their statistics from the prepass, with u kept per
+// chunk row.  Fills `rr` for the logit gradient.
+//
+// Consecutive chunks' spans overlap by a few target rows (the spread of the
+// shifts): `carry` holds the previous chunk's span, whose last rows are moved
+// to the front of ur instead of being computed again, so every chunk after
+// the first contracts only its Nc / K new target rows (whole 256-row tiles
+// when Nc / K is a multiple of 256).
+struct SpanCarry {
+  int64_t jlo = 0, jhi = 0;
+  bool valid = false;
+};
+
+int div_chunk_raw(const specloss_problem* p, const KindSet& k, const Layout& L, const FwdBufs& b,
+                  const SavedView& sv, float* loss, float* terms, int64_t r0, int64_t rows,
+                  float* zr, float* ur, RawRows& rr, SpanCarry& carry, Tracer& tr,
+                  hipStream_t stream) {
+  const bool bf16 = p->in_dtype == SPECLOSS_BF16;
+  const int64_t H = L.H, Nc = b.Nc, tile_cols = L.Tv * Nc;
+  rr = RawRows{zr, L.Vp, ur, L.Vp, nullptr, 0, (int32_t)Nc};
+
+  StatsLaunch sz{};
+  sz.A = op(p->W, H, p->vocab);
+  sz.B = op(offset_rows(p->hidden_states, r0, H, L.es), H, rows);
+  sz.k_len = (int32_t)H;
+  sz.vocab = (int32_t)p->vocab;
+  sz.tiles_m = (int32_t)L.Tv;
+  sz.tiles_n = (int32_t)cdiv(rows, 256);
+  sz.ncols = (int32_t)rows;
+  sz.ldp = (int32_t)Nc;
+  sz.pm = b.pz;
+  sz.ps = b.pz + tile_cols;
+  sz.raw = zr;
+  sz.ld_raw = L.Vp;
+  TRACED(tr, K_STATS_Q, 2.0 * rows * H * p->vocab, launch_stats(bf16, false, sz, stream));
+
+  StatsLaunch su = sz;
+  su.A = op(p->W_t, H, p->vocab);
+  su.raw = ur;
+  if (L.shared_target && heads_pass2(p, k)) {
+    int64_t jlo, jhi;
+    heads_span(p, r0, rows, jlo, jhi);
+    const int64_t nu = jhi - jlo, Nt = p->n_target_rows;
+    if (nu > L.Nu) return SPECLOSS_E_INVAL;
+    int64_t keep = 0;  // leading rows of the span already computed
+    if (carry.valid && jlo >= carry.jlo && jlo < carry.jhi) {
+      keep = (carry.jhi < jhi ? carry.jhi : jhi) - jlo;
+      const int64_t from = jlo - carry.jlo;  // their rows in ur
+      if (from < keep) {
+        keep = 0;  // source and destination would overlap: compute them again
+      } else {
+        const size_t bytes = (size_t)keep * L.Vp * 4;
+        TRACED(tr, K_SPAN_CARRY, 2.0 * bytes,
+               hipMemcpyAsync(ur, ur + from * L.Vp, bytes, hipMemcpyDeviceToDevice, stream));
+      }
+    }
+    carry = SpanCarry{jlo, jhi, true};
+    const int64_t j0 = jlo + keep, nn = jhi - j0;  // new rows [j0, jhi)
+    if (nn > 0) {
+      // rows past the last target row serve masked rows only: the operand
+      // clamps them into the tensor
+      const int64_t jb = j0 < Nt ? j0 : Nt - 1;
+      const int64_t ucols = L.pu_cols, ufield = L.Tv * ucols;
+      su.B = op(offset_rows(p->target_hidden, jb, H, L.es), H, Nt - jb);
+      su.tiles_n = (int32_t)cdiv(nn, 256);
+      su.ncols = (int32_t)nn;
+      su.ldp = (int32_t)ucols;
+      su.pm = b.pu;
+      su.ps = b.pu + ufield;
+      su.pi = reinterpret_cast<int32_t*>(b.pu + 2 * ufield);
+      su.pq = b.pu + 3 * ufield;
+      su.raw = ur + keep * L.Vp;
+      TRACED(tr, K_STATS_P, 2.0 * nn * H * p->vocab, launch_stats(bf16, true, su, stream));
+      if (j0 < Nt) {
+        // statistics per target row
+        char* tb = static_cast<char*>(b.tstat);
+        const size_t fs = align_up((size_t)Nt * 4, kAlign);
+        const int64_t nt = nn < Nt - j0 ? nn : Nt - j0;
+        Combine1Launch c1{};
+        c1.tiles_m = (int32_t)L.Tv;
+        c1.ncols = (int32_t)nt;
+        c1.ldp = (int32_t)ucols;
+        c1.pm_u = su.pm;
+        c1.ps_u = su.ps;
+        c1.pi_u = su.pi;
+        c1.pq_u = su.pq;
+        c1.vocab = (int32_t)p->vocab;
+        c1.lse_p = reinterpret_cast<float*>(tb) + j0;
+        c1.y_arg = reinterpret_cast<int32_t*>(tb + fs) + j0;
+        c1.flat = reinterpret_cast<float*>(tb + 2 * fs) + j0;
+        TRACED(tr, K_COMBINE1, 4.0 * L.Tv * nt * 4, launch_combine1(c1, stream));
+      }
+    }
+    rr.urow = p->target_row + r0;
+    rr.ushift = jlo;
+    rr.n_u = (int32_t)nu;
+  } else {
+    su.B = target_operand(p, r0, rows, L.es);
+    su.pm = b.pu;
+    su.ps = b.pu + tile_cols;
+    su.pi = reinterpret_cast<int32_t*>(b.pu + 2 * tile_cols);
+    su.pq = b.pu + 3 * tile_cols;
+    // shared target rows: the statistics come from the prepass, only u is kept
+    TRACED(tr, K_STATS_P, 2.0 * rows * H * p->vocab,
+           launch_stats(bf16, !L.shared_target, su, stream));
+  }
+  TRY(merge_pass1(p, k, L, b, sv, r0, rows, false, tr, stream));
+  TRY(gather_label_logits(p, k, L, b, sv, r0, rows, tr, stream));
+
+  DivRawLaunch dv{};
+  dv.r = rr;
+  dv.tiles_m = (int32_t)L.Tv;
+  dv.ncols = (int32_t)rows;
+  dv.vocab = (int32_t)p->vocab;
+  dv.ldp = (int32_t)Nc;
+  dv.lse_q = sv.lse_q + r0;
+  dv.lse_p = sv.lse_p + r0;
+  dv.need = k.need;
+  dv.part = b.p2;
+  dv.part_stride = tile_cols;
+  TRACED(tr, K_DIV_RAW, (double)rows * L.Vp * 8, launch_div_raw(dv, stream));
+  return combine_losses(p, k, L, b, sv, loss, terms, r0, rows, (int32_t)L.Tv, tr, stream);
 }
 
 // Forward of chunk rows [r0, r0 + rows) for the label / argmax
@@ -1070,12 +1231,6 @@ int contract_dW(const specloss_problem* p, const Layout& L, int64_t Nc, const vo
   return SPECLOSS_OK;
 }
 
-#define TRY(expr)                   \
-  do {                              \
-    const int rc_ = (expr);         \
-    if (rc_) return rc_;            \
-  } while (0)
-
 int check_fwd_outputs(const float* loss, const float* term_loss, const float* lse_q,
                       const void* saved, const int64_t* counts, const float* reduced) {
   if (!loss || !counts) return SPECLOSS_E_INVAL;
@@ -1280,7 +1435,7 @@ int lmhead_loss_fwd(const specloss_problem* p, void* workspace, size_t ws_bytes,
   if (L.shared_target) TRY(target_prepass(p, L, b, tr, stream));
   for (int64_t r0 = 0; r0 < N; r0 += Nc) {
     const int64_t rows = (N - r0) < Nc ? (N - r0) : Nc;
-    TRY(fwd_chunk(p, k, L, b, sv, loss, terms, r0, rows, nullptr, nullptr, tr, stream));
+    TRY(fwd_chunk(p, k, L, b, sv, loss, terms, r0, rows, nullptr, tr, stream));
   }
   if (reduced) TRY(launch_reduce_for(p, k, loss, terms, counts, reduced, tr, stream));
   if (lse_q)
@@ -1325,9 +1480,9 @@ int lmhead_loss_fwd_bwd(const specloss_problem* p, void* workspace, size_t ws_by
   TRY(check_bwd_args(grad_loss, grad_mean, dhidden, dh_dtype, dW));
   if (!workspace || !aligned(workspace, kAlign)) return SPECLOSS_E_WORKSPACE;
   // label / argmax cross-entropies: pass 1 stages exp(z - ref) per chunk
-  // (ce_chunk_staged); with divergences, pass 2 stages q and q - p (and log q
-  // - log p for rkl and jsd).  The logit gradient is formed from the staged
-  // values without recomputing logits.
+  // (ce_chunk_staged); with divergences, pass 1 keeps both raw logit rows
+  // (div_chunk_raw), from which the sums and then the logit gradient are
+  // formed.  No logits tile is computed twice.
   int32_t layout = LAYOUT_COPIES;
   const int64_t Nc = pick_chunk(p, k, ws_bytes, REGION_FUSED, &layout);
   if (Nc <= 0) return SPECLOSS_E_WORKSPACE;
@@ -1340,19 +1495,20 @@ int lmhead_loss_fwd_bwd(const specloss_problem* p, void* workspace, size_t ws_by
   float* seed = reinterpret_cast<float*>(ws + L.seed);
   const FwdBufs b{reinterpret_cast<float*>(ws + L.f_pz), reinterpret_cast<float*>(ws + L.f_pu),
                   k.stage_div ? reinterpret_cast<float*>(ws + L.f_p2) : nullptr,
-                  reinterpret_cast<float*>(ws + L.f_zy), Nc, ws + L.tstat,
-                  reinterpret_cast<int32_t*>(ws + L.f_hmap)};
+                  reinterpret_cast<float*>(ws + L.f_zy), Nc, ws + L.tstat, nullptr};
   void* wt = L.wt_copy ? ws + L.f_wt : nullptr;
   void* ht = L.dw_copies ? ws + L.f_ht : nullptr;
   void* dz = ws + L.f_dz;
-  void* dd = k.stage_div ? ws + L.f_dd : nullptr;
-  void* dl = k.stage_log ? ws + L.f_dl : nullptr;
+  float* zr = k.stage_div ? reinterpret_cast<float*>(ws + L.f_zr) : nullptr;
+  float* ur = k.stage_div ? reinterpret_cast<float*>(ws + L.f_ur) : nullptr;
   void* dzt = L.dw_copies ? ws + L.f_dzt : nullptr;
   Tracer tr{p->trace, stream};
 
   TRY(launch_validity_for(p, k, sv, counts, tr, stream));
   TRY(launch_seed_for(p, sv, grad_loss, grad_mean, counts, seed, tr, stream));
-  if (L.shared_target) TRY(target_prepass(p, L, b, tr, stream));
+  // aligned heads with divergences: the target statistics come per chunk
+  if (L.shared_target && !(k.stage_div && heads_pass2(p, k)))
+    TRY(target_prepass(p, L, b, tr, stream));
   if (dhidden && L.wt_copy)
     TRACED(tr, K_TRANSPOSE_W, 2.0 * Vp * H * L.es, launch_transpose(bf16, p->W, V, H, wt, Vp, stream));
   // label / argmax cross-entropies with the dW copies: pass 1 stages the
@@ -1361,6 +1517,7 @@ int lmhead_loss_fwd_bwd(const specloss_problem* p, void* workspace, size_t ws_by
   const bool staged_ce = !k.stage_div && L.dw_copies &&
                          p->weights[SPECLOSS_CE_LABEL] + p->weights[SPECLOSS_CE_ARGMAX_P] != 0.0f;
   float* rscale = reinterpret_cast<float*>(ws + L.f_rs);
+  SpanCarry carry;
   int chunk = 0;
   for (int64_t r0 = 0; r0 < N; r0 += Nc, ++chunk) {
     const int64_t rows = (N - r0) < Nc ? (N - r0) : Nc;
@@ -1379,34 +1536,53 @@ int lmhead_loss_fwd_bwd(const specloss_problem* p, void* workspace, size_t ws_by
                         stream));
       continue;
     }
-    TRY(fwd_chunk(p, k, L, b, sv, loss, terms, r0, rows, dz, dd, tr, stream, dl));
-    DzStageLaunch ds{};
-    ds.tiles_m = (int32_t)L.Tv;
-    ds.ncols = (int32_t)rows;
-    ds.vocab = (int32_t)V;
-    ds.ldp = (int32_t)Nc;
-    ds.r0 = r0;
-    ds.pm = b.pz;
-    ds.seed = seed;
-    ds.sv = sv;
-    ds.w_lab = p->weights[SPECLOSS_CE_LABEL];
-    ds.w_arg = p->weights[SPECLOSS_CE_ARGMAX_P];
-    ds.w_kl = p->weights[SPECLOSS_KL];
-    ds.w_tv = p->weights[SPECLOSS_TV];
-    ds.w_nla = p->weights[SPECLOSS_NLA];
-    ds.w_lk = p->weights[SPECLOSS_LK_HYBRID];
-    ds.w_rkl = p->weights[SPECLOSS_RKL];
-    ds.w_jsd = p->weights[SPECLOSS_JSD];
-    ds.dd = dd;
-    ds.dl = dl;
-    ds.dz = dz;
-    ds.ld_dz = Vp;
-    ds.dzt = dzt;
-    ds.ld_dzt = Nc;
-    ds.row_blocks = (int32_t)(cdiv(rows, 256) * 4);
-    TRACED(tr, dd ? K_DZ_DIV : K_DZ_STAGE,
-           (double)ds.row_blocks * 64 * Vp * L.es * ((dd ? 3 : 2) + (dl ? 1 : 0) + (dzt ? 1 : 0)),
-           launch_dz_stage(bf16, ds, stream));
+    if (k.stage_div) {
+      RawRows rr{};
+      TRY(div_chunk_raw(p, k, L, b, sv, loss, terms, r0, rows, zr, ur, rr, carry, tr, stream));
+      DzRawLaunch dr{};
+      dr.r = rr;
+      dr.tiles_m = (int32_t)L.Tv;
+      dr.ncols = (int32_t)rows;
+      dr.vocab = (int32_t)V;
+      dr.r0 = r0;
+      dr.seed = seed;
+      dr.sv = sv;
+      dr.w_lab = p->weights[SPECLOSS_CE_LABEL];
+      dr.w_arg = p->weights[SPECLOSS_CE_ARGMAX_P];
+      dr.w_kl = p->weights[SPECLOSS_KL];
+      dr.w_tv = p->weights[SPECLOSS_TV];
+      dr.w_nla = p->weights[SPECLOSS_NLA];
+      dr.w_lk = p->weights[SPECLOSS_LK_HYBRID];
+      dr.w_rkl = p->weights[SPECLOSS_RKL];
+      dr.w_jsd = p->weights[SPECLOSS_JSD];
+      dr.dz = dz;
+      dr.ld_dz = Vp;
+      dr.dzt = dzt;
+      dr.ld_dzt = Nc;
+      dr.row_blocks = (int32_t)(cdiv(rows, 256) * 4);
+      TRACED(tr, K_DZ_RAW, (double)dr.row_blocks * 64 * Vp * (8.0 + L.es * (dzt ? 2 : 1)),
+             launch_dz_raw(bf16, dr, stream));
+    } else {
+      TRY(fwd_chunk(p, k, L, b, sv, loss, terms, r0, rows, dz, tr, stream));
+      DzStageLaunch ds{};
+      ds.tiles_m = (int32_t)L.Tv;
+      ds.ncols = (int32_t)rows;
+      ds.vocab = (int32_t)V;
+      ds.ldp = (int32_t)Nc;
+      ds.r0 = r0;
+      ds.pm = b.pz;
+      ds.seed = seed;
+      ds.sv = sv;
+      ds.w_lab = p->weights[SPECLOSS_CE_LABEL];
+      ds.w_arg = p->weights[SPECLOSS_CE_ARGMAX_P];
+      ds.dz = dz;
+      ds.ld_dz = Vp;
+      ds.dzt = dzt;
+      ds.ld_dzt = Nc;
+      ds.row_blocks = (int32_t)(cdiv(rows, 256) * 4);
+      TRACED(tr, K_DZ_STAGE, (double)ds.row_blocks * 64 * Vp * L.es * (2 + (dzt ? 1 : 0)),
+             launch_dz_stage(bf16, ds, stream));
+    }
     const void* hc = offset_rows(p->hidden_states, r0, H, L.es);
     if (dW && L.dw_copies)
       TRACED(tr, K_TRANSPOSE_H, 2.0 * Nc * H * L.es, launch_transpose(bf16, hc, rows, H, ht, Nc, stream));
@@ -1649,7 +1825,7 @@ int lmhead_shard_pass2(const specloss_problem* p, const specloss_shard* sh, cons
              launch_rowdot(bf16, rd, stream));
     }
     if (k.pass2) {
-      TRY(launch_pass2(p, k, L, b, sv, r0, rows, nullptr, nullptr, tr, stream));
+      TRY(launch_pass2(p, k, L, b, sv, r0, rows, tr, stream));
       TileSumLaunch ts{};
       ts.tiles_m = (int32_t)L.Tv;
       ts.ncols = (int32_t)rows;

@@ -14,8 +14,11 @@
 //   k_stats_stage  pass 1 of the single forward+backward call: as k_stats,
 //            and stores e = exp(z - m_tile) of every (token, vocab) for the
 //            backward, so no logits tile is computed twice.
-// Memory-bound k_dz_stage: the logit gradient from the staged values, in
-// place, plus its transpose for the dW contraction.
+// Memory-bound passes of the single call: k_dz_stage forms the logit
+// gradient of the cross-entropies from the staged values, in place, plus its
+// transpose for the dW contraction; for the divergences pass 1 keeps both
+// raw logit rows, and k_div_raw (the second sweep's sums) and k_dz_raw (the
+// logit gradient and its transpose) read them.
 // Plain contraction k_gemm: dh = dz W and dW (+)= dz^T h.
 // Row kernels: validity/counts, label-logit gather, partial merges, means,
 // gradient seeds, transposes and head alignment.
@@ -216,7 +219,11 @@ __device__ __forceinline__ void store_tile_rows(const f32x4_t (&acc)[Cfg::FM][Cf
 // ============================================================================
 // TARGET (the target distribution p): also the lowest-index argmax and the sum
 // of e^2, e = exp(u - m_tile), from which the flatness score is formed.
-template <typename T, bool TARGET, int WNW = 2>
+// RAW: the tile's logits also go out as fp32 (a.raw), each lane storing its
+// four consecutive vocabulary entries of a row as one 16-byte nontemporal
+// store before the statistics are formed, so the stores drain under that
+// arithmetic.
+template <typename T, bool TARGET, int WNW = 2, bool RAW = false>
 __global__ __launch_bounds__(128 * WNW, 1) void k_stats(StatsLaunch a) {
   constexpr bool ARGMAX = TARGET;
   using Cfg = TileCfg<T, 256, 256, (WNW == 2 ? kStatsLoadGap : 1), WNW>;
@@ -233,6 +240,19 @@ __global__ __launch_bounds__(128 * WNW, 1) void k_stats(StatsLaunch a) {
   const int wm = wave / WNW, wn = wave % WNW;
   const int v_base = tm * Cfg::BM + wm * Cfg::WM;
   const bool tail = tm * Cfg::BM + Cfg::BM > a.vocab;
+
+  if constexpr (RAW) {
+#pragma unroll
+    for (int j = 0; j < Cfg::FN; ++j) {
+      const int c = tn * Cfg::BN + wn * Cfg::WN + j * kFrag + frag_col(lane);
+      if (c < a.ncols) {
+        float* row = a.raw + (int64_t)c * a.ld_raw + v_base + frag_row(0, lane);
+#pragma unroll
+        for (int i = 0; i < Cfg::FM; ++i)
+          __builtin_nontemporal_store(acc[i][j], reinterpret_cast<f32x4_t*>(row + i * kFrag));
+      }
+    }
+  }
 
   float mj[Cfg::FN], sj[Cfg::FN], qj[Cfg::FN];
   int ij[Cfg::FN];
@@ -601,20 +621,41 @@ __global__ __launch_bounds__(128 * WNW, 1) void k_stats_stage(StatsStageLaunch a
   }
 }
 
-// dz from staged values, one workgroup per (256-wide vocabulary tile, 64 rows):
-// rows are read and written back coalesced (16 bytes per lane), and the
-// block is transposed through LDS into dz^T.
-//   DIV = false: the buffer holds e = exp(z - m_tile) (label / argmax
-//                cross-entropies only).
-//   DIV = true:  the buffer holds q and `dd` holds d = q - p; with
-//                c = [q < p] (1/2 on ties) read from the sign of d,
-//                dz = seed (A q + B d - C q (c - S) - w_lab [v = y_lab] - w_arg [v = y_arg])
-//                where A = w_lab + w_arg, B = w_kl + w_lk lam,
-//                C = w_tv + w_nla / alpha + w_lk (1 - lam), lam = exp(-3 alpha).
-//   LOG (with DIV): `dl` holds l = log q - log p, and the rkl and jsd terms
-//                are added: + seed q (w_rkl (l - rKL) + w_jsd (g - E_q[g])),
-//                g = (ln 2 - softplus(-l)) / 2 = (log q - log m) / 2.
-template <typename T, bool DIV, bool LOG>
+// dz^T rows of one (256-entry vocabulary tile, 64 chunk rows) block from
+// its LDS copy: row rr of the block holds its 16-byte chunk ch at position
+// ch ^ (rr / KC), so the KC-row column reads hit distinct banks.
+template <typename T>
+__device__ __forceinline__ void store_dzt_block(const char* tile, T* dzt, int64_t ld_dzt, int vt,
+                                                int rb) {
+  constexpr int VT = kVocabTile, RB = 64;
+  constexpr int KC = ElemTraits<T>::kPerChunk;
+  constexpr int STRIDE = VT * (int)sizeof(T);
+  constexpr int PER_ROW = RB / KC;  // 16-byte pieces per dz^T row segment
+  for (int idx = threadIdx.x; idx < VT * PER_ROW; idx += 256) {
+    const int v = idx / PER_ROW, q = idx % PER_ROW;
+    i32x4_t out;
+    const char* col = tile + (((v / KC) ^ q) << 4) + (v % KC) * (int)sizeof(T);
+    if constexpr (sizeof(T) == 2) {
+      bf16x8_t b;
+#pragma unroll
+      for (int e = 0; e < KC; ++e)
+        b[e] = *reinterpret_cast<const __bf16*>(col + (q * KC + e) * STRIDE);
+      out = __builtin_bit_cast(i32x4_t, b);
+    } else {
+#pragma unroll
+      for (int e = 0; e < KC; ++e)
+        out[e] = *reinterpret_cast<const int*>(col + (q * KC + e) * STRIDE);
+    }
+    *reinterpret_cast<i32x4_t*>(dzt + (int64_t)(vt * VT + v) * ld_dzt + rb * RB + q * KC) = out;
+  }
+}
+
+// dz of the label / argmax cross-entropies from the staged e = exp(z - m_tile),
+// one workgroup per (256-wide vocabulary tile, 64 rows): rows are read and
+// written back coalesced (16 bytes per lane), and the block is transposed
+// through LDS into dz^T.
+//   dz = seed ((w_lab + w_arg) e exp(m_tile - lse) - w_lab [v = y_lab] - w_arg [v = y_arg])
+template <typename T>
 __global__ __launch_bounds__(256) void k_dz_stage(DzStageLaunch a) {
   constexpr int VT = kVocabTile, RB = 64;
   constexpr int KC = ElemTraits<T>::kPerChunk;       // elements per 16 bytes
@@ -630,7 +671,7 @@ __global__ __launch_bounds__(256) void k_dz_stage(DzStageLaunch a) {
 
   constexpr int IT = RB * CPR / 256;  // 16-byte chunks per thread
   static_assert(RB * CPR % 256 == 0, "chunks must split evenly over the block");
-  i32x4_t raw[IT], rawd[DIV ? IT : 1], rawl[LOG ? IT : 1];
+  i32x4_t raw[IT];
   // all of this thread's loads first, so they are in flight together
 #pragma unroll
   for (int it = 0; it < IT; ++it) {
@@ -638,8 +679,6 @@ __global__ __launch_bounds__(256) void k_dz_stage(DzStageLaunch a) {
     const int rr = idx / CPR, ch = idx % CPR;
     const int64_t o = (int64_t)(rb * RB + rr) * a.ld_dz + vt * VT + ch * KC;
     raw[it] = *reinterpret_cast<const i32x4_t*>(dz + o);
-    if constexpr (DIV) rawd[it] = *reinterpret_cast<const i32x4_t*>(static_cast<const T*>(a.dd) + o);
-    if constexpr (LOG) rawl[it] = *reinterpret_cast<const i32x4_t*>(static_cast<const T*>(a.dl) + o);
   }
 #pragma unroll
   for (int it = 0; it < IT; ++it) {
@@ -648,58 +687,23 @@ __global__ __launch_bounds__(256) void k_dz_stage(DzStageLaunch a) {
     const int c = rb * RB + rr;                    // chunk row
     const int v0 = vt * VT + ch * KC;
     T* p = dz + (int64_t)c * a.ld_dz + v0;
-    float e[KC], dd[KC], ll[KC];
+    float e[KC];
     if constexpr (sizeof(T) == 2) {
       const bf16x8_t b = __builtin_bit_cast(bf16x8_t, raw[it]);
 #pragma unroll
       for (int q = 0; q < KC; ++q) e[q] = (float)b[q];
-      if constexpr (DIV) {
-        const bf16x8_t bd = __builtin_bit_cast(bf16x8_t, rawd[it]);
-#pragma unroll
-        for (int q = 0; q < KC; ++q) dd[q] = (float)bd[q];
-      }
-      if constexpr (LOG) {
-        const bf16x8_t bl = __builtin_bit_cast(bf16x8_t, rawl[LOG ? it : 0]);
-#pragma unroll
-        for (int q = 0; q < KC; ++q) ll[q] = (float)bl[q];
-      }
     } else {
 #pragma unroll
       for (int q = 0; q < KC; ++q) e[q] = __int_as_float(raw[it][q]);
-      if constexpr (DIV) {
-#pragma unroll
-        for (int q = 0; q < KC; ++q) dd[q] = __int_as_float(rawd[DIV ? it : 0][q]);
-      }
-      if constexpr (LOG) {
-#pragma unroll
-        for (int q = 0; q < KC; ++q) ll[q] = __int_as_float(rawl[LOG ? it : 0][q]);
-      }
     }
-    float sd = 0.0f, scale = 0.0f, cb = 0.0f, cc = 0.0f, S = 0.0f;
-    float cr = 0.0f, cj = 0.0f, rkl = 0.0f, eqg = 0.0f;
+    float sd = 0.0f, scale = 0.0f;
     int yl = -1, ya = -1;
     if (c < a.ncols) {
       const int64_t gr = a.r0 + c;
       sd = a.seed[gr];
       if (sd != 0.0f) {
-        if (DIV) {
-          const float alpha = a.sv.alpha[gr];
-          const float lam = __expf(-3.0f * alpha);
-          scale = sd * (a.w_lab + a.w_arg);
-          cb = sd * (a.w_kl + a.w_lk * lam);
-          cc = sd * (a.w_tv + (a.w_nla != 0.0f ? a.w_nla / alpha : 0.0f) +
-                     a.w_lk * (1.0f - lam));
-          S = a.sv.S[gr];
-          if (LOG) {
-            cr = sd * a.w_rkl;
-            cj = sd * a.w_jsd;
-            rkl = a.sv.rkl[gr];
-            eqg = a.sv.eqg[gr];
-          }
-        } else {
-          scale = sd * (a.w_lab + a.w_arg) *
-                  fast_exp2((a.pm[(int64_t)vt * a.ldp + c] - a.sv.lse_q[gr]) * kLog2e);
-        }
+        scale = sd * (a.w_lab + a.w_arg) *
+                fast_exp2((a.pm[(int64_t)vt * a.ldp + c] - a.sv.lse_q[gr]) * kLog2e);
         yl = a.sv.y_label[gr];
         ya = a.sv.y_arg[gr];
       }
@@ -709,17 +713,6 @@ __global__ __launch_bounds__(256) void k_dz_stage(DzStageLaunch a) {
     for (int q = 0; q < KC; ++q) {
       const int v = v0 + q;
       float x = e[q] * scale;
-      if (DIV) {
-        const float ci = dd[q] < 0.0f ? 1.0f : (dd[q] == 0.0f ? 0.5f : 0.0f);
-        x = fmaf(cb, dd[q], x) - cc * e[q] * (ci - S);
-      }
-      if (LOG) {
-        // softplus(-l) = max(-l, 0) + log(1 + exp(-|l|))
-        const float l = ll[q];
-        const float sp = fmaxf(-l, 0.0f) + fast_log2(1.0f + fast_exp2(-fabsf(l) * kLog2e)) * kLn2;
-        const float g = 0.5f * (kLn2 - sp);
-        x += e[q] * (cr * (l - rkl) + cj * (g - eqg));
-      }
       if (v == yl) x -= sd * a.w_lab;
       if (v == ya) x -= sd * a.w_arg;
       d[q] = (sd != 0.0f && v < a.vocab) ? x : 0.0f;
@@ -739,36 +732,15 @@ __global__ __launch_bounds__(256) void k_dz_stage(DzStageLaunch a) {
   }
   if (!dzt) return;  // bf16: the dW contraction reads dz itself
   __syncthreads();
-  // dz^T rows: vocabulary entry v of this tile, 64 chunk rows = RB elements
-  constexpr int PER_ROW = RB / KC;  // 16-byte pieces per dz^T row segment
-  for (int idx = threadIdx.x; idx < VT * PER_ROW; idx += 256) {
-    const int v = idx / PER_ROW, q = idx % PER_ROW;
-    i32x4_t out;
-    const char* col = tile + (((v / KC) ^ q) << 4) + (v % KC) * (int)sizeof(T);
-    if constexpr (sizeof(T) == 2) {
-      bf16x8_t b;
-#pragma unroll
-      for (int e = 0; e < KC; ++e)
-        b[e] = *reinterpret_cast<const __bf16*>(col + (q * KC + e) * STRIDE);
-      out = __builtin_bit_cast(i32x4_t, b);
-    } else {
-#pragma unroll
-      for (int e = 0; e < KC; ++e)
-        out[e] = *reinterpret_cast<const int*>(col + (q * KC + e) * STRIDE);
-    }
-    *reinterpret_cast<i32x4_t*>(dzt + (int64_t)(vt * VT + v) * a.ld_dzt + rb * RB + q * KC) = out;
-  }
+  store_dzt_block<T>(tile, dzt, a.ld_dzt, vt, rb);
 }
 
 // ============================================================================
 // pass 2: divergence sums with the final logsumexps
 // ============================================================================
-// STAGE: also store q and d = q - p of every (row, vocab) for the logit
-// gradient (rounded to the storage type; d keeps the sign of q - p, zero on
-// ties, so the indicator [q < p] is unchanged by the rounding).
 // NEED != 0: the set of sums as a compile-time constant (the common sets),
 // so the per-element tests of `need` disappear; NEED == 0 reads a.need.
-template <typename T, bool STAGE, int WNW, uint32_t NEED = 0>
+template <typename T, int WNW, uint32_t NEED = 0>
 __global__ __launch_bounds__(128 * WNW, 1) void k_div(DivLaunch a) {
   using Cfg = TileCfg<T, 256, 128, 1, WNW>;
   __shared__ __attribute__((aligned(16))) char smem[Cfg::LDS_BYTES];
@@ -798,21 +770,14 @@ __global__ __launch_bounds__(128 * WNW, 1) void k_div(DivLaunch a) {
     float s_alpha = 0.f, s_s = 0.f, s_kl = 0.f, s_rkl = 0.f, s_jsd = 0.f, s_eqg = 0.f;
 #pragma unroll
     for (int i = 0; i < Cfg::FM; ++i) {
-      float sq[4], sd[4], sl[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int v = v_base + i * kFrag + frag_row(r, lane);
-        sq[r] = 0.0f;
-        sd[r] = 0.0f;
-        sl[r] = 0.0f;
         if (tail && v >= a.vocab) continue;
         const float lq = az[i][j][r] - lq0;
         const float lp = au[i][j][r] - lp0;
         const float q = fast_exp2(lq * kLog2e);
         const float p = fast_exp2(lp * kLog2e);
-        sq[r] = q;
-        sd[r] = q - p;
-        sl[r] = lq - lp;
         if (need & SUM_ALPHA) s_alpha += fminf(p, q);
         if (need & SUM_S) s_s += (q < p) ? q : ((q == p) ? 0.5f * q : 0.0f);
         if (need & SUM_KL) s_kl += p * (lp - lq);
@@ -822,12 +787,6 @@ __global__ __launch_bounds__(128 * WNW, 1) void k_div(DivLaunch a) {
           if (need & SUM_JSD) s_jsd += 0.5f * (p * (lp - lm) + q * (lq - lm));
           if (need & SUM_EQG) s_eqg += 0.5f * q * (lq - lm);
         }
-      }
-      if (STAGE) {
-        const int64_t o = (int64_t)c_tile * a.ld_stage + v_base + i * kFrag + frag_row(0, lane);
-        store4<T>(static_cast<T*>(a.stage_q) + o, sq[0], sq[1], sq[2], sq[3]);
-        store4<T>(static_cast<T*>(a.stage_d) + o, sd[0], sd[1], sd[2], sd[3]);
-        if (a.stage_l) store4<T>(static_cast<T*>(a.stage_l) + o, sl[0], sl[1], sl[2], sl[3]);
       }
     }
     const float v6[kNumSums] = {s_alpha, s_s, s_kl, s_rkl, s_jsd, s_eqg};
@@ -865,9 +824,9 @@ __global__ __launch_bounds__(128 * WNW, 1) void k_div(DivLaunch a) {
 // column wn holds, for each head k, the same 32 target rows as its u
 // columns: z column wn * 32 K + k * 32 + jj pairs with u column wn * 32 + jj
 // (the map puts the matching draft row there).  Per (vocabulary row, draft
-// row) the arithmetic is that of k_div, in the same order, so the sums and
-// staged values are the same bits.
-template <typename T, bool STAGE, int K, uint32_t NEED = 0>
+// row) the arithmetic is that of k_div, in the same order, so the sums are
+// the same bits.
+template <typename T, int K, uint32_t NEED = 0>
 __global__ __launch_bounds__(kThreads, 1) void k_div_heads(DivHeadsLaunch h) {
   using CfgZ = TileCfg<T, 256, 64 * K>;
   using CfgU = TileCfg<T, 256, 64>;
@@ -908,21 +867,14 @@ __global__ __launch_bounds__(kThreads, 1) void k_div_heads(DivHeadsLaunch h) {
       float s_alpha = 0.f, s_s = 0.f, s_kl = 0.f, s_rkl = 0.f, s_jsd = 0.f, s_eqg = 0.f;
 #pragma unroll
       for (int i = 0; i < CfgU::FM; ++i) {
-        float sq[4], sd[4], sl[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int v = v_base + i * kFrag + frag_row(r, lane);
-          sq[r] = 0.0f;
-          sd[r] = 0.0f;
-          sl[r] = 0.0f;
           if (tail && v >= a.vocab) continue;
           const float lq = az[i][k * CfgU::FN + j][r] - lq0;
           const float lp = au[i][j][r] - lp0;
           const float q = fast_exp2(lq * kLog2e);
           const float p = fast_exp2(lp * kLog2e);
-          sq[r] = q;
-          sd[r] = q - p;
-          sl[r] = lq - lp;
           if (need & SUM_ALPHA) s_alpha += fminf(p, q);
           if (need & SUM_S) s_s += (q < p) ? q : ((q == p) ? 0.5f * q : 0.0f);
           if (need & SUM_KL) s_kl += p * (lp - lq);
@@ -932,12 +884,6 @@ __global__ __launch_bounds__(kThreads, 1) void k_div_heads(DivHeadsLaunch h) {
             if (need & SUM_JSD) s_jsd += 0.5f * (p * (lp - lm) + q * (lq - lm));
             if (need & SUM_EQG) s_eqg += 0.5f * q * (lq - lm);
           }
-        }
-        if (STAGE && ok) {
-          const int64_t o = lr * a.ld_stage + v_base + i * kFrag + frag_row(0, lane);
-          store4<T>(static_cast<T*>(a.stage_q) + o, sq[0], sq[1], sq[2], sq[3]);
-          store4<T>(static_cast<T*>(a.stage_d) + o, sd[0], sd[1], sd[2], sd[3]);
-          if (a.stage_l) store4<T>(static_cast<T*>(a.stage_l) + o, sl[0], sl[1], sl[2], sl[3]);
         }
       }
       const float v6[kNumSums] = {s_alpha, s_s, s_kl, s_rkl, s_jsd, s_eqg};
@@ -992,6 +938,193 @@ __global__ __launch_bounds__(256) void k_heads_map(int32_t* map, int32_t tiles_n
   if (tj - sh.v[k] < 0 || lr < 0) lr = 0;
   if (lr >= rows) lr = rows - 1;
   map[idx] = (int32_t)lr;
+}
+
+// ============================================================================
+// pass 2 and the logit gradient from raw logits (single call, divergences)
+// ============================================================================
+// Pass 1 of the single call keeps both raw fp32 logit rows of the chunk
+// (z: draft, u: target), so the second sweep and the logit gradient are
+// memory passes over them instead of two recomputed contractions.
+
+__device__ __forceinline__ int raw_urow(const RawRows& r, int c) {
+  if (!r.urow) return c;
+  const int64_t x = (int64_t)r.urow[c] - r.ushift;
+  return (int)(x < 0 ? 0 : (x >= r.n_u ? r.n_u - 1 : x));
+}
+
+// sum over the 16 lanes of a row group (lanes 16 g .. 16 g + 15): butterflies
+// with the lower lane first at each level, so every lane ends with the same,
+// repeatable value
+__device__ __forceinline__ float row16_sum(float x, int lane) {
+#pragma unroll
+  for (int m = 1; m < 16; m <<= 1) {
+    const float o = __shfl_xor(x, m);
+    x = (lane & m) ? o + x : x + o;
+  }
+  return x;
+}
+
+// One workgroup per (256-entry vocabulary tile, 64 chunk rows); a 16-lane
+// group owns a row, each lane four 16-byte pieces of it (the group reads
+// 256 contiguous bytes per load), and the per-lane sums meet in row16_sum.
+// The element terms are those of k_div (speculators "Available Losses" rows).
+template <uint32_t NEED = 0>
+__global__ __launch_bounds__(256) void k_div_raw(DivRawLaunch a) {
+  const int vt = blockIdx.x % a.tiles_m;
+  const int rb = blockIdx.x / a.tiles_m;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 4, t = lane & 15;
+  const uint32_t need = NEED ? NEED : a.need;
+  const int v0 = vt * kVocabTile + t * 4;
+  const bool tail = (vt + 1) * kVocabTile > a.vocab;
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const int c = rb * 64 + wave * 16 + it * 4 + g;  // chunk row of this group
+    const int cc = c < a.ncols ? c : a.ncols - 1;
+    const float* zr = a.r.z + (int64_t)cc * a.r.ld_z + v0;
+    const float* ur = a.r.u + (int64_t)raw_urow(a.r, cc) * a.r.ld_u + v0;
+    f32x4_t zz[4], uu[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      zz[m] = *reinterpret_cast<const f32x4_t*>(zr + m * 64);
+      uu[m] = *reinterpret_cast<const f32x4_t*>(ur + m * 64);
+    }
+    const float lq0 = a.lse_q[cc], lp0 = a.lse_p[cc];
+    float s_alpha = 0.f, s_s = 0.f, s_kl = 0.f, s_rkl = 0.f, s_jsd = 0.f, s_eqg = 0.f;
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (tail && v0 + m * 64 + e >= a.vocab) continue;
+        const float lq = zz[m][e] - lq0;
+        const float lp = uu[m][e] - lp0;
+        const float q = fast_exp2(lq * kLog2e);
+        const float p = fast_exp2(lp * kLog2e);
+        if (need & SUM_ALPHA) s_alpha += fminf(p, q);
+        if (need & SUM_S) s_s += (q < p) ? q : ((q == p) ? 0.5f * q : 0.0f);
+        if (need & SUM_KL) s_kl += p * (lp - lq);
+        if (need & SUM_RKL) s_rkl += q * (lq - lp);
+        if (need & (SUM_JSD | SUM_EQG)) {
+          const float lm = log_mixture(p, q);
+          if (need & SUM_JSD) s_jsd += 0.5f * (p * (lp - lm) + q * (lq - lm));
+          if (need & SUM_EQG) s_eqg += 0.5f * q * (lq - lm);
+        }
+      }
+    const float v6[kNumSums] = {s_alpha, s_s, s_kl, s_rkl, s_jsd, s_eqg};
+#pragma unroll
+    for (int f = 0; f < kNumSums; ++f) {
+      if (!(need & (1u << f))) continue;
+      const float x = row16_sum(v6[f], lane);
+      if (t == 0 && c < a.ncols) a.part[f * a.part_stride + (int64_t)vt * a.ldp + c] = x;
+    }
+  }
+}
+
+// dz from raw logits (the formula at DzRawLaunch), one workgroup per
+// (256-entry vocabulary tile, 64 chunk rows): q, d = q - p and l = log q -
+// log p formed in fp32 (and c = [q < p] from the sign of that d, as the S
+// sums of k_div_raw decide it).  The block is written row-major and,
+// transposed through LDS, into dz^T.
+template <typename T, bool LOG>
+__global__ __launch_bounds__(256) void k_dz_raw(DzRawLaunch a) {
+  constexpr int VT = kVocabTile, RB = 64;
+  constexpr int KC = ElemTraits<T>::kPerChunk;  // output values per 16 bytes
+  constexpr int CPR = VT / KC;
+  constexpr int NL = KC / 4;                    // 16-byte fp32 loads per chunk and side
+  constexpr int STRIDE = VT * (int)sizeof(T);
+  constexpr int IT = RB * CPR / 256;
+  static_assert(RB * CPR % 256 == 0, "chunks must split evenly over the block");
+  __shared__ __attribute__((aligned(16))) char tile[RB * STRIDE];
+  const int vt = blockIdx.x % a.tiles_m;
+  const int rb = blockIdx.x / a.tiles_m;
+  T* dz = static_cast<T*>(a.dz);
+  T* dzt = static_cast<T*>(a.dzt);
+
+  f32x4_t zz[IT][NL], uu[IT][NL];
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int idx = it * 256 + threadIdx.x;
+    const int rr = idx / CPR, ch = idx % CPR;
+    const int c = rb * RB + rr;
+    const int cc = c < a.ncols ? c : a.ncols - 1;
+    const float* zr = a.r.z + (int64_t)cc * a.r.ld_z + vt * VT + ch * KC;
+    const float* ur = a.r.u + (int64_t)raw_urow(a.r, cc) * a.r.ld_u + vt * VT + ch * KC;
+#pragma unroll
+    for (int l = 0; l < NL; ++l) {
+      zz[it][l] = *reinterpret_cast<const f32x4_t*>(zr + 4 * l);
+      uu[it][l] = *reinterpret_cast<const f32x4_t*>(ur + 4 * l);
+    }
+  }
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int idx = it * 256 + threadIdx.x;
+    const int rr = idx / CPR, ch = idx % CPR;
+    const int c = rb * RB + rr;
+    const int v0 = vt * VT + ch * KC;
+    float sd = 0.0f, scale = 0.0f, cb = 0.0f, cc = 0.0f, S = 0.0f;
+    float cr = 0.0f, cj = 0.0f, rkl = 0.0f, eqg = 0.0f, lq0 = 0.0f, lp0 = 0.0f;
+    int yl = -1, ya = -1;
+    if (c < a.ncols) {
+      const int64_t gr = a.r0 + c;
+      sd = a.seed[gr];
+      if (sd != 0.0f) {
+        const float alpha = a.sv.alpha[gr];
+        const float lam = __expf(-3.0f * alpha);
+        scale = sd * (a.w_lab + a.w_arg);
+        cb = sd * (a.w_kl + a.w_lk * lam);
+        cc = sd * (a.w_tv + (a.w_nla != 0.0f ? a.w_nla / alpha : 0.0f) + a.w_lk * (1.0f - lam));
+        S = a.sv.S[gr];
+        if (LOG) {
+          cr = sd * a.w_rkl;
+          cj = sd * a.w_jsd;
+          rkl = a.sv.rkl[gr];
+          eqg = a.sv.eqg[gr];
+        }
+        yl = a.sv.y_label[gr];
+        ya = a.sv.y_arg[gr];
+        lq0 = a.sv.lse_q[gr];
+        lp0 = a.sv.lse_p[gr];
+      }
+    }
+    float d[KC];
+#pragma unroll
+    for (int q = 0; q < KC; ++q) {
+      const int v = v0 + q;
+      const float lq = zz[it][q / 4][q % 4] - lq0;
+      const float lp = uu[it][q / 4][q % 4] - lp0;
+      const float qq = fast_exp2(lq * kLog2e);
+      const float pp = fast_exp2(lp * kLog2e);
+      const float dd = qq - pp;
+      const float ci = dd < 0.0f ? 1.0f : (dd == 0.0f ? 0.5f : 0.0f);
+      float x = fmaf(cb, dd, qq * scale) - cc * qq * (ci - S);
+      if (LOG) {
+        // softplus(-l) = max(-l, 0) + log(1 + exp(-|l|))
+        const float l = lq - lp;
+        const float sp = fmaxf(-l, 0.0f) + fast_log2(1.0f + fast_exp2(-fabsf(l) * kLog2e)) * kLn2;
+        const float g = 0.5f * (kLn2 - sp);
+        x += qq * (cr * (l - rkl) + cj * (g - eqg));
+      }
+      if (v == yl) x -= sd * a.w_lab;
+      if (v == ya) x -= sd * a.w_arg;
+      d[q] = (sd != 0.0f && v < a.vocab) ? x : 0.0f;
+    }
+    i32x4_t out;
+    if constexpr (sizeof(T) == 2) {
+      bf16x8_t b;
+#pragma unroll
+      for (int q = 0; q < KC; ++q) b[q] = (__bf16)d[q];
+      out = __builtin_bit_cast(i32x4_t, b);
+    } else {
+#pragma unroll
+      for (int q = 0; q < KC; ++q) out[q] = __float_as_int(d[q]);
+    }
+    *reinterpret_cast<i32x4_t*>(dz + (int64_t)c * a.ld_dz + v0) = out;
+    if (dzt) *reinterpret_cast<i32x4_t*>(tile + rr * STRIDE + ((ch ^ (rr / KC)) << 4)) = out;
+  }
+  if (!dzt) return;
+  __syncthreads();
+  store_dzt_block<T>(tile, dzt, a.ld_dzt, vt, rb);
 }
 
 // ============================================================================
@@ -1771,11 +1904,17 @@ constexpr int kStatsWNW = 4;
 hipError_t launch_stats(bool bf16, bool target, const StatsLaunch& a, hipStream_t s) {
   const dim3 grid(grid_for_tiles(a.tiles_m * a.tiles_n)), block(kThreads);
   constexpr int W = kStatsWNW;
+  const bool raw = a.raw != nullptr;
   if (bf16) {
-    if (target) hipLaunchKernelGGL((k_stats<bf16_bits, true, W>), grid, dim3(128 * W), 0, s, a);
-    else hipLaunchKernelGGL((k_stats<bf16_bits, false, W>), grid, dim3(128 * W), 0, s, a);
+    const dim3 b8(128 * W);
+    if (raw && target) hipLaunchKernelGGL((k_stats<bf16_bits, true, W, true>), grid, b8, 0, s, a);
+    else if (raw) hipLaunchKernelGGL((k_stats<bf16_bits, false, W, true>), grid, b8, 0, s, a);
+    else if (target) hipLaunchKernelGGL((k_stats<bf16_bits, true, W>), grid, b8, 0, s, a);
+    else hipLaunchKernelGGL((k_stats<bf16_bits, false, W>), grid, b8, 0, s, a);
   } else {
-    if (target) hipLaunchKernelGGL((k_stats<float, true>), grid, block, 0, s, a);
+    if (raw && target) hipLaunchKernelGGL((k_stats<float, true, 2, true>), grid, block, 0, s, a);
+    else if (raw) hipLaunchKernelGGL((k_stats<float, false, 2, true>), grid, block, 0, s, a);
+    else if (target) hipLaunchKernelGGL((k_stats<float, true>), grid, block, 0, s, a);
     else hipLaunchKernelGGL((k_stats<float, false>), grid, block, 0, s, a);
   }
   return hipGetLastError();
@@ -1794,15 +1933,8 @@ hipError_t launch_stats_stage(bool bf16, const StatsStageLaunch& a, hipStream_t 
 
 hipError_t launch_dz_stage(bool bf16, const DzStageLaunch& a, hipStream_t s) {
   const dim3 grid((unsigned)(a.tiles_m * a.row_blocks)), block(256);
-  if (bf16) {
-    if (a.dl) hipLaunchKernelGGL((k_dz_stage<bf16_bits, true, true>), grid, block, 0, s, a);
-    else if (a.dd) hipLaunchKernelGGL((k_dz_stage<bf16_bits, true, false>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((k_dz_stage<bf16_bits, false, false>), grid, block, 0, s, a);
-  } else {
-    if (a.dl) hipLaunchKernelGGL((k_dz_stage<float, true, true>), grid, block, 0, s, a);
-    else if (a.dd) hipLaunchKernelGGL((k_dz_stage<float, true, false>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((k_dz_stage<float, false, false>), grid, block, 0, s, a);
-  }
+  if (bf16) hipLaunchKernelGGL(k_dz_stage<bf16_bits>, grid, block, 0, s, a);
+  else hipLaunchKernelGGL(k_dz_stage<float>, grid, block, 0, s, a);
   return hipGetLastError();
 }
 
@@ -1831,16 +1963,29 @@ hipError_t launch_heads_map(int32_t* map, int32_t tiles_n, int32_t n_heads, cons
 hipError_t launch_div_heads(bool bf16, const DivHeadsLaunch& a, hipStream_t s) {
   if (!bf16 || a.n_heads < 2 || a.n_heads > 3) return hipErrorInvalidValue;
   const dim3 grid(grid_for_tiles(a.d.tiles_m * a.d.tiles_n)), block(kThreads);
-  const bool stage = a.d.stage_q != nullptr;
-  constexpr uint32_t kTv = SUM_ALPHA | SUM_S;
-  if (a.n_heads == 2) {
-    if (stage) hipLaunchKernelGGL((k_div_heads<bf16_bits, true, 2>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((k_div_heads<bf16_bits, false, 2>), grid, block, 0, s, a);
+  if (a.n_heads == 2) hipLaunchKernelGGL((k_div_heads<bf16_bits, 2>), grid, block, 0, s, a);
+  else hipLaunchKernelGGL((k_div_heads<bf16_bits, 3>), grid, block, 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_div_raw(const DivRawLaunch& a, hipStream_t s) {
+  const dim3 grid((unsigned)(a.tiles_m * ((a.ncols + 63) / 64))), block(256);
+  constexpr uint32_t kLk = SUM_ALPHA | SUM_S | SUM_KL, kTv = SUM_ALPHA | SUM_S;
+  if (a.need == kLk) hipLaunchKernelGGL((k_div_raw<kLk>), grid, block, 0, s, a);
+  else if (a.need == kTv) hipLaunchKernelGGL((k_div_raw<kTv>), grid, block, 0, s, a);
+  else hipLaunchKernelGGL((k_div_raw<0>), grid, block, 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_dz_raw(bool bf16, const DzRawLaunch& a, hipStream_t s) {
+  const dim3 grid((unsigned)(a.tiles_m * a.row_blocks)), block(256);
+  const bool log = a.w_rkl != 0.0f || a.w_jsd != 0.0f;
+  if (bf16) {
+    if (log) hipLaunchKernelGGL((k_dz_raw<bf16_bits, true>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((k_dz_raw<bf16_bits, false>), grid, block, 0, s, a);
   } else {
-    if (stage && a.d.need == kTv)
-      hipLaunchKernelGGL((k_div_heads<bf16_bits, true, 3, kTv>), grid, block, 0, s, a);
-    else if (stage) hipLaunchKernelGGL((k_div_heads<bf16_bits, true, 3>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((k_div_heads<bf16_bits, false, 3>), grid, block, 0, s, a);
+    if (log) hipLaunchKernelGGL((k_dz_raw<float, true>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((k_dz_raw<float, false>), grid, block, 0, s, a);
   }
   return hipGetLastError();
 }
@@ -1848,20 +1993,15 @@ hipError_t launch_div_heads(bool bf16, const DivHeadsLaunch& a, hipStream_t s) {
 hipError_t launch_div(bool bf16, const DivLaunch& a, hipStream_t s) {
   constexpr int W = kDivWNW;
   const dim3 grid(grid_for_tiles(a.tiles_m * a.tiles_n)), block(128 * W);
-  const bool stage = a.stage_q != nullptr;
-  // the second sweep's common sum sets (lk_hybrid; tv / nla) as constants:
-  // measured 2% faster than reading them per element
+  // the common sum sets (lk_hybrid; tv / nla) as constants: measured 2%
+  // faster than reading them per element
   constexpr uint32_t kLk = SUM_ALPHA | SUM_S | SUM_KL, kTv = SUM_ALPHA | SUM_S;
   if (bf16) {
-    if (stage && a.need == kLk)
-      hipLaunchKernelGGL((k_div<bf16_bits, true, W, kLk>), grid, block, 0, s, a);
-    else if (stage && a.need == kTv)
-      hipLaunchKernelGGL((k_div<bf16_bits, true, W, kTv>), grid, block, 0, s, a);
-    else if (stage) hipLaunchKernelGGL((k_div<bf16_bits, true, W>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((k_div<bf16_bits, false, W>), grid, block, 0, s, a);
+    if (a.need == kLk) hipLaunchKernelGGL((k_div<bf16_bits, W, kLk>), grid, block, 0, s, a);
+    else if (a.need == kTv) hipLaunchKernelGGL((k_div<bf16_bits, W, kTv>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((k_div<bf16_bits, W>), grid, block, 0, s, a);
   } else {
-    if (stage) hipLaunchKernelGGL((k_div<float, true, 2>), dim3(grid), dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((k_div<float, false, 2>), dim3(grid), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((k_div<float, 2>), dim3(grid), dim3(256), 0, s, a);
   }
   return hipGetLastError();
 }

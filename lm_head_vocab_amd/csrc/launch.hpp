@@ -59,6 +59,11 @@ struct StatsLaunch {
   float* ps;
   int32_t* pi;  // target variant only: lowest-index argmax per tile
   float* pq;    // target variant only: sum exp(2 (u - m_tile)) per tile
+  // optional: the tile's raw fp32 logits, row c (< ncols) of B at
+  // raw[c * ld_raw + v] for every v of the padded vocabulary (v >= vocab
+  // holds values of clamped weight rows, never read as logits)
+  float* raw;
+  int64_t ld_raw;
 };
 // target: the variant for the target logits u (argmax and e^2 sums as well)
 hipError_t launch_stats(bool bf16, bool target, const StatsLaunch& a, hipStream_t s);
@@ -109,32 +114,77 @@ struct StatsStageLaunch {
 };
 hipError_t launch_stats_stage(bool bf16, const StatsStageLaunch& a, hipStream_t s);
 
-// logit gradient from staged values, written over them and, transposed, into
-// dzt ([Vp][cap]).  Without dd (label / argmax cross-entropies) the buffer
-// holds e = exp(z - m_tile):
-//   dz = seed * ((w_lab + w_arg) e exp(m_tile - lse) - w_lab [v == y_lab] - w_arg [v == y_arg]);
-// with dd it holds q and dd holds q - p, and the divergence terms
-// (kl_div, tv, nla, lk_hybrid) are added from the saved alpha and S; with dl
-// (log q - log p) also rkl, q (dl - rkl), and jsd, q (g - E_q[g]) with
-// g = (ln 2 - softplus(-dl)) / 2 = (log q - log m) / 2, m = (p + q) / 2.
+// logit gradient of the label / argmax cross-entropies from the staged
+// e = exp(z - m_tile), written over it and, transposed, into dzt ([Vp][cap]):
+//   dz = seed * ((w_lab + w_arg) e exp(m_tile - lse) - w_lab [v == y_lab] - w_arg [v == y_arg])
 struct DzStageLaunch {
   int32_t tiles_m, ncols, vocab, ldp;
   int64_t r0;
-  const float* pm;     // chunk partial maxima [tiles_m][ldp] (e mode only)
+  const float* pm;     // chunk partial maxima [tiles_m][ldp]
   const float* seed;   // [N], global rows
   SavedView sv;        // global rows
   float w_lab, w_arg;
-  float w_kl, w_tv, w_nla, w_lk;  // divergence weights (dd mode only)
-  float w_rkl, w_jsd;             // (dl mode only)
-  const void* dd;      // [cap][Vp] q - p, or null
-  const void* dl;      // [cap][Vp] log q - log p (with dd, for rkl / jsd), or null
-  void* dz;            // in: e or q, out: dz; [cap][Vp]
+  void* dz;            // in: e, out: dz; [cap][Vp]
   int64_t ld_dz;
   void* dzt;           // [Vp][cap], or null (not needed by bf16 contractions)
   int64_t ld_dzt;
   int32_t row_blocks;  // 64-row blocks covered (multiple of the 256-row tiles)
 };
 hipError_t launch_dz_stage(bool bf16, const DzStageLaunch& a, hipStream_t s);
+
+// Second sweep over raw logits kept from pass 1 (single call, divergences):
+// the draft row c of the chunk is z[c * ld_z + v], its target row is
+// u[r * ld_u + v] with r = c, or with urow set r = urow[c] - ushift clamped
+// into [0, n_u) (rows that share target rows keep one copy).  q and p are
+// formed with the final logsumexps exactly as in launch_div.
+struct RawRows {
+  const float* z;
+  int64_t ld_z;
+  const float* u;
+  int64_t ld_u;
+  const int32_t* urow;  // chunk-local, or null
+  int64_t ushift;
+  int32_t n_u;
+};
+
+// The pass-2 sums from raw logits, memory-bound: per (256-entry vocabulary
+// tile, chunk row) partials in the layout of launch_div.
+struct DivRawLaunch {
+  RawRows r;
+  int32_t tiles_m, ncols, vocab, ldp;
+  const float* lse_q;  // chunk-local
+  const float* lse_p;
+  uint32_t need;
+  float* part;          // [kNumSums][tiles_m][ldp]
+  int64_t part_stride;
+};
+hipError_t launch_div_raw(const DivRawLaunch& a, hipStream_t s);
+
+// The logit gradient of the divergences (and of label / argmax
+// cross-entropies mixed with them) from raw logits, with q = exp(z - lse_q),
+// p = exp(u - lse_p), d = q - p, c = [q < p] (1/2 on ties) and
+// l = log q - log p formed in fp32:
+//   dz = seed (A q + B d - C q (c - S) + q (w_rkl (l - rKL) + w_jsd (g - E_q[g])))
+//        - seed (w_lab [v = y_lab] + w_arg [v = y_arg])
+// where A = w_lab + w_arg, B = w_kl + w_lk lam, C = w_tv + w_nla / alpha +
+// w_lk (1 - lam), lam = exp(-3 alpha), g = (ln 2 - softplus(-l)) / 2 =
+// (log q - log m) / 2, m = (p + q) / 2, and alpha, S, rKL, E_q[g] the row's
+// saved sums.  dz ([cap][ld_dz], input dtype) and, transposed, dzt
+// ([Vp][ld_dzt], or null).
+struct DzRawLaunch {
+  RawRows r;
+  int32_t tiles_m, ncols, vocab;
+  int64_t r0;
+  const float* seed;  // [N], global rows
+  SavedView sv;       // global rows
+  float w_lab, w_arg, w_kl, w_tv, w_nla, w_lk, w_rkl, w_jsd;
+  void* dz;
+  int64_t ld_dz;
+  void* dzt;
+  int64_t ld_dzt;
+  int32_t row_blocks;  // 64-row blocks covered
+};
+hipError_t launch_dz_raw(bool bf16, const DzRawLaunch& a, hipStream_t s);
 
 struct DivLaunch {
   GemmOperand Az, Bz, Au, Bu;
@@ -144,10 +194,6 @@ struct DivLaunch {
   uint32_t need;
   float* part;          // [kNumSums][tiles_m][ldp]
   int64_t part_stride;  // tiles_m * ldp
-  void* stage_q;        // null, or [cap][ld_stage]: q of every (chunk row, vocab)
-  void* stage_d;        // [cap][ld_stage]: q - p (with stage_q)
-  void* stage_l;        // [cap][ld_stage]: log q - log p (with stage_q), or null
-  int64_t ld_stage;
 };
 hipError_t launch_div(bool bf16, const DivLaunch& a, hipStream_t s);
 
@@ -157,8 +203,8 @@ hipError_t launch_div(bool bf16, const DivLaunch& a, hipStream_t s);
 // target tile computed once for the K <= 3 draft rows (j - shifts[k]) * K + k
 // it serves that lie in the chunk.  Bz rows come through `map` (filled by
 // launch_heads_map: [tiles_n][64 K] chunk-local rows, clamped into the
-// chunk); Bu starts at target row jlo.  Sums, partials and staging as for
-// launch_div, indexed by chunk row.
+// chunk); Bu starts at target row jlo.  Sums and partials as for launch_div,
+// indexed by chunk row.
 struct DivHeadsLaunch {
   DivLaunch d;     // Bz: the chunk's rows with `map`; Bu: target rows from jlo
   int32_t n_heads;

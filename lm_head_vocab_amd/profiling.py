@@ -63,11 +63,11 @@ def trace_name(kernel: str) -> str:
              "k_rowdot": "rowdot", "k_transpose": "transpose", "k_validity": "validity",
              "k_reduce": "reduce", "k_seed": "seed", "k_align": "align",
              "k_stats_dual": "stats_dual", "k_div_heads": "div_heads", "k_heads_map": "heads_map",
-             "k_sum_parts": "sum_partials"}
+             "k_sum_parts": "sum_partials", "k_div_raw": "div_raw", "k_dz_raw": "dz_raw"}
     name = names.get(base, base)
-    if "true" in targs:
-        name = {"k_stats": "stats_p", "k_div": "div_stage", "k_dz_stage": "dz_div",
-                "k_div_heads": "div_heads_stage"}.get(base, name)
+    if base == "k_stats":  # k_stats<T, TARGET, WNW, RAW>
+        args = [a.strip() for a in targs.strip("<>").split(",")]
+        return "stats_p" if len(args) > 1 and args[1] == "true" else "stats_q"
     return name
 
 

@@ -257,7 +257,8 @@ def full_parity(prob, *, max_chunk_rows=0, check_grads=True, tag="", single_call
         assert np.all(dh_np[~ref.valid] == 0.0), "masked rows must get a zero gradient"
         out.update(dh=dh_np, dW=dW_np, rdh=rdh, rdW=rdW)
     if trace is not None:
-        names = {name for name, _, _ in trace.read()}
+        out["trace"] = trace.read()
+        names = {name for name, _, _ in out["trace"]}
         run.problem.trace = None
         trace.close()
         if expect_kernels is not None:

@@ -345,8 +345,9 @@ def test_single_call_each_divergence(kind, dtype):
 
 
 def test_single_call_log_ratio_kinds_mix_and_two_calls():
-    """rkl, jsd, kl_div and tv together in one single call (staged log q - log p
-    beside q and q - p), against the oracle and against the two calls."""
+    """rkl, jsd, kl_div and tv together in one single call (log q - log p formed
+    from the raw logits beside q and q - p), against the oracle and against the
+    two calls (the same sums in another fp32 order: losses within 2e-5)."""
     w = {"rkl": 0.5, "jsd": 0.7, "kl_div": 0.2, "tv": 0.4, "ce": 0.1}
     p = synthetic.make_problem("multihead_bf16_405b", seq_len=140, hidden_dim=128, vocab=900,
                                weights=w)
@@ -359,7 +360,7 @@ def test_single_call_log_ratio_kinds_mix_and_two_calls():
     b.forward()
     dh2, dW2 = b.backward(grad_mean=gm)
     torch.cuda.synchronize()
-    assert torch.equal(a.loss, b.loss)
+    assert torch.allclose(a.loss, b.loss, rtol=2e-5, atol=1e-6)
     assert rel_frob(dh1.cpu().numpy(), dh2.cpu().numpy()) < 1e-2
     assert rel_frob(dW1.cpu().numpy(), dW2.cpu().numpy()) < 1e-2
 
@@ -383,8 +384,10 @@ def test_single_call_identical_target_ties():
 
 
 def test_single_call_divergence_matches_two_calls():
-    """Staged-divergence single call against the two calls: same losses bit for bit
-    (the forward kernels are the same), gradients within the bar of each other."""
+    """Divergence single call (second sweep over the raw logits kept by pass 1)
+    against the two calls (second sweep recomputing the tiles): the same fp32
+    logits and sums added in another order, so the losses agree within 2e-5
+    relative; gradients within the bar of each other."""
     p = synthetic.make_problem("lk_hybrid_bf16_8b", n_rows=700, hidden_dim=128, vocab=900)
     dev = to_device(p)
     gm = torch.ones(1, device="cuda")
@@ -394,8 +397,8 @@ def test_single_call_divergence_matches_two_calls():
     b.forward()
     dh2, dW2 = b.backward(grad_mean=gm)
     torch.cuda.synchronize()
-    assert torch.equal(a.loss, b.loss)
-    assert torch.equal(a.reduced, b.reduced)
+    assert torch.allclose(a.loss, b.loss, rtol=2e-5, atol=1e-6)
+    assert torch.allclose(a.reduced, b.reduced, rtol=2e-5, atol=1e-6)
     assert rel_frob(dh1.cpu().numpy(), dh2.cpu().numpy()) < 1e-2
     assert rel_frob(dW1.cpu().numpy(), dW2.cpu().numpy()) < 1e-2
 
@@ -660,12 +663,15 @@ def _heads_problem(S, shifts, batch, H, V, weights, seed):
                                   "k3_far_shifts_single", "k3_lean_single", "k3_tv_single",
                                   "k4_single_per_row", "k3_f32_two_calls_per_row"])
 def test_aligned_heads_share_target_tiles(case):
-    """Declared token-major heads: the second sweep computes each target tile once
-    for the heads it serves (k_div_heads) instead of once per row.  Against the
-    oracle (the bar), and bit for bit against the same problem without the
-    declaration (per-row second sweep): losses, terms, saved state, gradients.
-    256-row chunks split tokens between chunks (256 is no multiple of 3).
-    Four heads and fp32 inputs keep the per-row sweep (same checks)."""
+    """Declared token-major heads: each target tile is computed once for the
+    heads it serves instead of once per row -- in the two-call forward's second
+    sweep (k_div_heads), and in the single call's pass 1, which keeps one raw
+    target row per token of a chunk's span (its target contractions then do
+    about a third of the work of the per-row ones).  Against the oracle (the
+    bar), and bit for bit against the same problem without the declaration:
+    losses, terms, saved state, gradients.  256-row chunks split tokens between
+    chunks (256 is no multiple of 3).  Four heads and fp32 inputs keep the
+    per-row path (same checks)."""
     import lm_head_vocab_amd as L
     single = "single" in case
     shifts, batch = {"k3_single": ((1, 2, 3), 1), "k3_two_calls": ((1, 2, 3), 1),
@@ -684,9 +690,13 @@ def test_aligned_heads_share_target_tiles(case):
         for f in ("hidden", "W", "target_hidden", "W_t"):
             setattr(p, f, synthetic.bf16_bits_to_f32(getattr(p, f)).copy())
     flags = L.binding.FLAG_NO_COPIES if case == "k3_lean_single" else None
-    shared = "div_heads_stage" if single else "div_heads"
-    plain = "div_stage" if single else "div"
-    stage, absent = (plain, shared) if case.endswith("per_row") else (shared, plain)
+    per_row = case.endswith("per_row")
+    if single:
+        shared = plain = "div_raw"
+        stage, absent = "div_raw", "div"
+    else:
+        shared, plain = "div_heads", "div"
+        stage, absent = (plain, shared) if per_row else (shared, plain)
     out = full_parity(p, max_chunk_rows=256, tag=f"heads-{case}", single_call=single, flags=flags,
                       expect_kernels=([stage], [absent]))
     run = out["run"]
@@ -702,10 +712,17 @@ def test_aligned_heads_share_target_tiles(case):
         ref.forward()
         dh, dW = ref.backward(grad_mean=gm)
     torch.cuda.synchronize()
-    names = {n for n, _, _ in trace.read()}
+    recs = trace.read()
+    names = {n for n, _, _ in recs}
     ref.problem.trace = None
     trace.close()
-    assert plain in names and shared not in names, names
+    if single:
+        assert "div_raw" in names, names
+        target_work = lambda rs: sum(w for n, _, w in rs if n == "stats_p")
+        if not per_row:
+            assert target_work(out["trace"]) < 0.7 * target_work(recs)
+    else:
+        assert plain in names and shared not in names, names
     assert torch.equal(run.loss, ref.loss)
     assert torch.equal(run.term, ref.term)
     assert torch.equal(run.counts, ref.counts)

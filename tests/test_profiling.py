@@ -10,7 +10,11 @@ def test_trace_name_mapping():
     assert P.trace_name("void specloss::k_gemm<unsigned short, float, 0, false>(specloss::GemmLaunch)") == "gemm_dh"
     assert P.trace_name("void specloss::k_stats<unsigned short, true>(specloss::StatsLaunch)") == "stats_p"
     assert P.trace_name("void specloss::k_stats<unsigned short, false>(specloss::StatsLaunch)") == "stats_q"
-    assert P.trace_name("void specloss::k_div<unsigned short, true>(specloss::DivLaunch)") == "div_stage"
+    assert P.trace_name("void specloss::k_stats<unsigned short, false, 4, true>(specloss::StatsLaunch)") == "stats_q"
+    assert P.trace_name("void specloss::k_stats<unsigned short, true, 4, true>(specloss::StatsLaunch)") == "stats_p"
+    assert P.trace_name("void specloss::k_div_raw<7u>(specloss::DivRawLaunch)") == "div_raw"
+    assert P.trace_name("void specloss::k_dz_raw<unsigned short, true>(specloss::DzRawLaunch)") == "dz_raw"
+    assert P.trace_name("void specloss::k_div<unsigned short, 2, 7u>(specloss::DivLaunch)") == "div"
     assert P.trace_name("void specloss::k_stats_stage<unsigned short>(specloss::StatsStageLaunch)") == "stats_stage"
     assert P.trace_name("__amd_rocclr_copyBuffer") == "__amd_rocclr_copyBuffer"
 
