@@ -145,13 +145,16 @@ struct Layout {
   // target statistics are computed once per target row, then gathered
   bool shared_target;
   int64_t Nt;
-  // forward
-  size_t pz, pu, p2, zy, hmap, fwd_end;
+  // forward (fwd_raw: the two-call forward keeps both raw logit rows, zr and
+  // ur, as the single call does)
+  bool fwd_raw;
+  size_t pz, pu, p2, zy, hmap, zr, ur, fwd_end;
   // backward
   size_t wt, ht, dz, dzt, dhp, bwd_end;
   // single-call forward+backward: forward partials and backward buffers at once;
   // the divergences keep the chunk's raw fp32 logits (f_zr: Nc draft rows,
-  // f_ur: Nu target rows) and the target partials have pu_cols columns
+  // f_ur: Nu target rows; the same in the forward region with fwd_raw) and
+  // the target partials have pu_cols columns
   int64_t Nu, pu_cols;
   size_t f_pz, f_pu, f_p2, f_zy, f_wt, f_ht, f_dz, f_zr, f_ur, f_dzt, f_rs, f_dhp, fused_end;
 };
@@ -164,6 +167,10 @@ bool heads_pass2(const specloss_problem* p, const KindSet& k) {
   return k.pass2 && k.target && p->target_row && p->in_dtype == SPECLOSS_BF16 &&
          (p->n_heads == 2 || p->n_heads == 3);
 }
+
+// The kinds whose second sweep can read raw logits kept by pass 1 (all that
+// need one, except kl_div / rkl alone, which the dual pass 1 yields).
+bool raw_second_sweep(const KindSet& k) { return k.target && k.pass2 && !k.ratio_only; }
 
 void shift_range(const specloss_problem* p, int32_t& lo, int32_t& hi) {
   lo = p->head_shift[0];
@@ -217,7 +224,7 @@ int32_t dh_splits(int64_t Nc, int64_t H) {
 
 // fp32 inputs always take LAYOUT_COPIES (the transposing LDS load is bf16).
 Layout plan(const specloss_problem* p, const KindSet& k, int64_t Nc,
-            int32_t layout = LAYOUT_COPIES) {
+            int32_t layout = LAYOUT_COPIES, bool fwd_raw = false) {
   Layout L;
   L.N = p->n_rows;
   L.H = p->hidden;
@@ -243,12 +250,19 @@ Layout plan(const specloss_problem* p, const KindSet& k, int64_t Nc,
   L.tstat = take(L.shared_target ? 3 * align_up((size_t)L.Nt * 4, kAlign) : 0);
   L.head_end = o;
   const size_t tile_cols = (size_t)L.Tv * Nc * 4;
+  L.fwd_raw = fwd_raw && raw_second_sweep(k);
+  L.Nu = (k.stage_div || L.fwd_raw) ? (heads_pass2(p, k) ? heads_span_cap(p, Nc) : Nc) : 0;
+  L.pu_cols = L.Nu > Nc ? L.Nu : Nc;
+  const size_t pu_bytes = k.target ? 4 * (size_t)L.Tv * L.pu_cols * 4 : 0;
   L.pz = take(2 * tile_cols);
-  L.pu = take(k.target ? 4 * tile_cols : 0);
+  L.pu = take(pu_bytes);
   L.p2 = take(k.pass2 ? (size_t)kNumSums * tile_cols : 0);
   L.zy = take(2 * (size_t)Nc * 4);
-  const size_t hmap_bytes = heads_pass2(p, k) ? (size_t)heads_map_entries(p, Nc) * 4 : 0;
+  const size_t hmap_bytes =
+      heads_pass2(p, k) && !L.fwd_raw ? (size_t)heads_map_entries(p, Nc) * 4 : 0;
   L.hmap = take(hmap_bytes);
+  L.zr = take(L.fwd_raw ? (size_t)Nc * L.Vp * 4 : 0);
+  L.ur = take(L.fwd_raw ? (size_t)L.Nu * L.Vp * 4 : 0);
   L.fwd_end = o;
   o = L.head_end;
   L.wt = take(L.wt_copy ? (size_t)L.H * L.Vp * L.es : 0);
@@ -260,10 +274,8 @@ Layout plan(const specloss_problem* p, const KindSet& k, int64_t Nc,
   L.dhp = take(dhp_bytes);
   L.bwd_end = o;
   o = L.head_end;
-  L.Nu = k.stage_div ? (heads_pass2(p, k) ? heads_span_cap(p, Nc) : Nc) : 0;
-  L.pu_cols = L.Nu > Nc ? L.Nu : Nc;
   L.f_pz = take(2 * tile_cols);
-  L.f_pu = take(k.target ? 4 * (size_t)L.Tv * L.pu_cols * 4 : 0);
+  L.f_pu = take(pu_bytes);
   L.f_p2 = take(k.stage_div ? (size_t)kNumSums * tile_cols : 0);
   L.f_zy = take(2 * (size_t)Nc * 4);
   L.f_wt = take(L.wt_copy ? (size_t)L.H * L.Vp * L.es : 0);
@@ -292,11 +304,12 @@ size_t workspace_end(const Layout& L) {
 // Largest chunk (multiple of 256, at most `top` rows) whose region fits
 // `ws_bytes` (strictly below it when `strict`).
 int64_t largest_chunk(const specloss_problem* p, const KindSet& k, size_t ws_bytes,
-                      Region region, int32_t layout, int64_t top, bool strict = false) {
+                      Region region, int32_t layout, int64_t top, bool strict = false,
+                      bool fwd_raw = false) {
   int64_t lo = 1, hi = top / kChunkQuantum, best = 0;
   while (lo <= hi) {  // the requirement grows with the chunk
     const int64_t mid = (lo + hi) / 2;
-    const Layout L = plan(p, k, mid * kChunkQuantum, layout);
+    const Layout L = plan(p, k, mid * kChunkQuantum, layout, fwd_raw);
     const size_t need = region_end(L, region);
     if (strict ? need < ws_bytes : need <= ws_bytes) {
       best = mid;
@@ -344,6 +357,24 @@ int64_t pick_chunk(const specloss_problem* p, const KindSet& k, size_t ws_bytes,
     }
   }
   return best;
+}
+
+// Chunk of the two-call forward.  The kinds of raw_second_sweep keep both raw
+// logit rows (the second sweep is then a memory pass) when the workspace
+// holds them for a chunk of at least min(N, 1024) rows; otherwise their
+// second sweep recomputes both tiles, with the largest chunk that fits.
+int64_t pick_fwd_chunk(const specloss_problem* p, const KindSet& k, size_t ws_bytes, bool* raw) {
+  *raw = false;
+  if (raw_second_sweep(k)) {
+    const int64_t top = round_up(p->n_rows, kChunkQuantum);
+    const int64_t want = top < 1024 ? top : 1024;
+    const int64_t nc = largest_chunk(p, k, ws_bytes, REGION_FWD, LAYOUT_COPIES, top, false, true);
+    if (nc >= want) {
+      *raw = true;
+      return nc;
+    }
+  }
+  return pick_chunk(p, k, ws_bytes, REGION_FWD);
 }
 
 // The default chunk (workspace size for max_chunk_rows <= 0).  Blog, "Backward
@@ -1400,7 +1431,8 @@ int lmhead_loss_chunk(const specloss_problem* p, size_t ws_bytes, int32_t call,
   int32_t lay = LAYOUT_COPIES;
   int64_t nc;
   if (call == 0) {
-    nc = pick_chunk(p, k, ws_bytes, REGION_FWD);
+    bool raw;
+    nc = pick_fwd_chunk(p, k, ws_bytes, &raw);
   } else if (call == 1) {
     nc = pick_chunk(p, k, ws_bytes, REGION_BWD, &lay);
   } else {
@@ -1419,23 +1451,32 @@ int lmhead_loss_fwd(const specloss_problem* p, void* workspace, size_t ws_bytes,
   TRY(check_problem(p, &k));
   TRY(check_fwd_outputs(loss, term_loss, lse_q, saved, counts, reduced));
   if (!workspace || !aligned(workspace, kAlign)) return SPECLOSS_E_WORKSPACE;
-  const int64_t Nc = pick_chunk(p, k, ws_bytes, REGION_FWD);
+  bool raw = false;
+  const int64_t Nc = pick_fwd_chunk(p, k, ws_bytes, &raw);
   if (Nc <= 0) return SPECLOSS_E_WORKSPACE;
-  const Layout L = plan(p, k, Nc);
+  const Layout L = plan(p, k, Nc, LAYOUT_COPIES, raw);
   char* ws = static_cast<char*>(workspace);
   const int64_t N = L.N;
   const SavedView sv = saved_view(saved ? saved : ws + L.saved, N);
   float* terms = term_loss ? term_loss : reinterpret_cast<float*>(ws + L.terms);
   const FwdBufs b{reinterpret_cast<float*>(ws + L.pz), reinterpret_cast<float*>(ws + L.pu),
                   reinterpret_cast<float*>(ws + L.p2), reinterpret_cast<float*>(ws + L.zy), Nc,
-                  ws + L.tstat, reinterpret_cast<int32_t*>(ws + L.hmap)};
+                  ws + L.tstat, raw ? nullptr : reinterpret_cast<int32_t*>(ws + L.hmap)};
   Tracer tr{p->trace, stream};
 
   TRY(launch_validity_for(p, k, sv, counts, tr, stream));
-  if (L.shared_target) TRY(target_prepass(p, L, b, tr, stream));
+  // aligned heads with raw logits: the target statistics come per chunk
+  if (L.shared_target && !(raw && heads_pass2(p, k))) TRY(target_prepass(p, L, b, tr, stream));
+  SpanCarry carry;
   for (int64_t r0 = 0; r0 < N; r0 += Nc) {
     const int64_t rows = (N - r0) < Nc ? (N - r0) : Nc;
-    TRY(fwd_chunk(p, k, L, b, sv, loss, terms, r0, rows, nullptr, tr, stream));
+    if (raw) {
+      RawRows rr{};
+      TRY(div_chunk_raw(p, k, L, b, sv, loss, terms, r0, rows, reinterpret_cast<float*>(ws + L.zr),
+                        reinterpret_cast<float*>(ws + L.ur), rr, carry, tr, stream));
+    } else {
+      TRY(fwd_chunk(p, k, L, b, sv, loss, terms, r0, rows, nullptr, tr, stream));
+    }
   }
   if (reduced) TRY(launch_reduce_for(p, k, loss, terms, counts, reduced, tr, stream));
   if (lse_q)

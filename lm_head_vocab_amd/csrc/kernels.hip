@@ -953,52 +953,56 @@ __device__ __forceinline__ int raw_urow(const RawRows& r, int c) {
   return (int)(x < 0 ? 0 : (x >= r.n_u ? r.n_u - 1 : x));
 }
 
-// sum over the 16 lanes of a row group (lanes 16 g .. 16 g + 15): butterflies
-// with the lower lane first at each level, so every lane ends with the same,
-// repeatable value
-__device__ __forceinline__ float row16_sum(float x, int lane) {
+// Sum of the eight lanes of a row (lanes 8 k .. 8 k + 7, lane 8 k + 4 h + g):
+// (g0 + g1) + (g2 + g3) within each h, then h0 + h1, the lower lane first at
+// each level, so every lane ends with the same value.
+__device__ __forceinline__ float row8_sum(float x, int lane) {
 #pragma unroll
-  for (int m = 1; m < 16; m <<= 1) {
+  for (int m = 1; m < 8; m <<= 1) {
     const float o = __shfl_xor(x, m);
     x = (lane & m) ? o + x : x + o;
   }
   return x;
 }
 
-// One workgroup per (256-entry vocabulary tile, 64 chunk rows); a 16-lane
-// group owns a row, each lane four 16-byte pieces of it (the group reads
-// 256 contiguous bytes per load), and the per-lane sums meet in row16_sum.
-// The element terms are those of k_div (speculators "Available Losses" rows).
+// One workgroup per (256-entry vocabulary tile, 64 chunk rows), eight lanes
+// per row.  Lane (h, g) of a row sums the 32 entries h 128 + i 16 + 4 g + r
+// (i < 8, r < 4) in that order (eight 16-byte loads per side), and the eight
+// partials meet in row8_sum: the order in which k_div forms the same sums
+// from its accumulators (a wave row h, lane group g, fragments i, registers
+// r, then col_sum and the two wave rows), so both second sweeps give the same
+// bits.  The element terms are those of k_div (speculators "Available
+// Losses" rows).
 template <uint32_t NEED = 0>
 __global__ __launch_bounds__(256) void k_div_raw(DivRawLaunch a) {
   const int vt = blockIdx.x % a.tiles_m;
   const int rb = blockIdx.x / a.tiles_m;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int g = lane >> 4, t = lane & 15;
+  const int lane = threadIdx.x & 63;
+  const int sub = lane & 7, g = sub & 3, hh = sub >> 2;
   const uint32_t need = NEED ? NEED : a.need;
-  const int v0 = vt * kVocabTile + t * 4;
+  const int vb = vt * kVocabTile + hh * 128 + 4 * g;  // entry (i, r): vb + 16 i + r
   const bool tail = (vt + 1) * kVocabTile > a.vocab;
 #pragma unroll
-  for (int it = 0; it < 4; ++it) {
-    const int c = rb * 64 + wave * 16 + it * 4 + g;  // chunk row of this group
+  for (int it = 0; it < 2; ++it) {
+    const int c = rb * 64 + it * 32 + (threadIdx.x >> 3);  // chunk row of this lane's group
     const int cc = c < a.ncols ? c : a.ncols - 1;
-    const float* zr = a.r.z + (int64_t)cc * a.r.ld_z + v0;
-    const float* ur = a.r.u + (int64_t)raw_urow(a.r, cc) * a.r.ld_u + v0;
-    f32x4_t zz[4], uu[4];
+    const float* zr = a.r.z + (int64_t)cc * a.r.ld_z + vb;
+    const float* ur = a.r.u + (int64_t)raw_urow(a.r, cc) * a.r.ld_u + vb;
+    f32x4_t zz[8], uu[8];
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      zz[m] = *reinterpret_cast<const f32x4_t*>(zr + m * 64);
-      uu[m] = *reinterpret_cast<const f32x4_t*>(ur + m * 64);
+    for (int i = 0; i < 8; ++i) {
+      zz[i] = *reinterpret_cast<const f32x4_t*>(zr + 16 * i);
+      uu[i] = *reinterpret_cast<const f32x4_t*>(ur + 16 * i);
     }
     const float lq0 = a.lse_q[cc], lp0 = a.lse_p[cc];
     float s_alpha = 0.f, s_s = 0.f, s_kl = 0.f, s_rkl = 0.f, s_jsd = 0.f, s_eqg = 0.f;
 #pragma unroll
-    for (int m = 0; m < 4; ++m)
+    for (int i = 0; i < 8; ++i)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        if (tail && v0 + m * 64 + e >= a.vocab) continue;
-        const float lq = zz[m][e] - lq0;
-        const float lp = uu[m][e] - lp0;
+      for (int r = 0; r < 4; ++r) {
+        if (tail && vb + 16 * i + r >= a.vocab) continue;
+        const float lq = zz[i][r] - lq0;
+        const float lp = uu[i][r] - lp0;
         const float q = fast_exp2(lq * kLog2e);
         const float p = fast_exp2(lp * kLog2e);
         if (need & SUM_ALPHA) s_alpha += fminf(p, q);
@@ -1015,8 +1019,8 @@ __global__ __launch_bounds__(256) void k_div_raw(DivRawLaunch a) {
 #pragma unroll
     for (int f = 0; f < kNumSums; ++f) {
       if (!(need & (1u << f))) continue;
-      const float x = row16_sum(v6[f], lane);
-      if (t == 0 && c < a.ncols) a.part[f * a.part_stride + (int64_t)vt * a.ldp + c] = x;
+      const float x = row8_sum(v6[f], lane);
+      if (sub == 0 && c < a.ncols) a.part[f * a.part_stride + (int64_t)vt * a.ldp + c] = x;
     }
   }
 }

@@ -12,9 +12,11 @@ import pytest
 import torch
 
 import synthetic
+import lm_head_vocab_amd as L
 from oracle import specloss_oracle as O
 from lm_head_vocab_amd.runner import ShardedLossRun
-from tests._gpu_helpers import (GRAD_FROB, full_parity, make_run, rel_frob, say, to_device)
+from tests._gpu_helpers import (GRAD_FROB, check_tokens, full_parity, make_run, rel_frob, say,
+                                to_device)
 
 pytestmark = pytest.mark.gpu
 
@@ -347,7 +349,8 @@ def test_single_call_each_divergence(kind, dtype):
 def test_single_call_log_ratio_kinds_mix_and_two_calls():
     """rkl, jsd, kl_div and tv together in one single call (log q - log p formed
     from the raw logits beside q and q - p), against the oracle and against the
-    two calls (the same sums in another fp32 order: losses within 2e-5)."""
+    two calls: the same losses bit for bit (every second sweep adds its sums in
+    one order), gradients within the bar of each other."""
     w = {"rkl": 0.5, "jsd": 0.7, "kl_div": 0.2, "tv": 0.4, "ce": 0.1}
     p = synthetic.make_problem("multihead_bf16_405b", seq_len=140, hidden_dim=128, vocab=900,
                                weights=w)
@@ -360,7 +363,7 @@ def test_single_call_log_ratio_kinds_mix_and_two_calls():
     b.forward()
     dh2, dW2 = b.backward(grad_mean=gm)
     torch.cuda.synchronize()
-    assert torch.allclose(a.loss, b.loss, rtol=2e-5, atol=1e-6)
+    assert torch.equal(a.loss, b.loss)
     assert rel_frob(dh1.cpu().numpy(), dh2.cpu().numpy()) < 1e-2
     assert rel_frob(dW1.cpu().numpy(), dW2.cpu().numpy()) < 1e-2
 
@@ -383,11 +386,63 @@ def test_single_call_identical_target_ties():
     assert np.allclose(run.saved_field(5).cpu().numpy(), 0.5, atol=1e-5)  # S
 
 
+def _forward_trace(run):
+    import lm_head_vocab_amd as L
+    trace = L.binding.Trace(capacity=4096)
+    trace.attach(run.problem)
+    run.forward()
+    torch.cuda.synchronize()
+    names = {n for n, _, _ in trace.read()}
+    run.problem.trace = None
+    trace.close()
+    return names
+
+
+@pytest.mark.parametrize("case", ["mix_bf16", "mix_f32", "heads_bf16"])
+def test_raw_and_recomputed_second_sweeps_agree(case):
+    """The two-call forward's second sweep either reads raw logits kept by pass 1
+    (a workspace that holds them for min(N, 1024) rows) or recomputes both tiles
+    (a smaller one, e.g. the allocation-free scratch): the same losses, terms
+    and saved state bit for bit, since every sweep adds its sums in one order
+    and the contractions give the same logits.  Every divergence kind at once
+    (jsd and rkl included); aligned heads compare the shared-target-tile sweep."""
+    w = {"tv": 0.7, "ce": 0.2, "kl_div": 0.4, "rkl": 0.3, "jsd": 0.5, "nla": 0.2,
+         "lk_hybrid": 0.6, "ce_label": 0.1}
+    if case == "heads_bf16":
+        p = _heads_problem(300, (1, 2, 3), 1, 128, 900, w, seed=29)
+        raw_kernel, rec_kernel = "div_raw", "div_heads"
+    else:
+        p = synthetic.make_problem("lk_hybrid_bf16_8b", n_rows=700, hidden_dim=128, vocab=900,
+                                   weights=w)
+        p.labels = np.random.default_rng(5).integers(0, p.vocab, p.n_rows).astype(np.int32)
+        raw_kernel, rec_kernel = "div_raw", "div"
+    if case == "mix_f32":
+        p.dtype = "f32"
+        for f in ("hidden", "W", "target_hidden", "W_t"):
+            setattr(p, f, synthetic.bf16_bits_to_f32(getattr(p, f)).copy())
+    say(f"[sweeps] {case} N={p.n_rows}")
+    dev = to_device(p)
+    raw = make_run(p, dev, workspace_bytes=256 << 20, flags=None)
+    rec = make_run(p, dev, max_chunk_rows=256)  # raw rows for 1024 rows do not fit
+    names_raw, names_rec = _forward_trace(raw), _forward_trace(rec)
+    assert raw_kernel in names_raw and rec_kernel not in names_raw, names_raw
+    assert rec_kernel in names_rec and raw_kernel not in names_rec, names_rec
+    assert torch.equal(raw.counts, rec.counts)
+    assert torch.equal(raw.loss, rec.loss)
+    assert torch.equal(raw.term, rec.term)
+    valid = torch.from_numpy(O.row_validity(O.OracleProblem.of(p))[0]).cuda()
+    for f in range(L.binding.SAVED_FIELDS):
+        a_f, b_f = raw.saved_field(f, torch.int32), rec.saved_field(f, torch.int32)
+        assert torch.equal(a_f[valid], b_f[valid]), f"saved field {f}"
+    check_tokens(raw.loss.cpu().numpy(), O.forward(p).loss, "loss against the oracle")
+
+
 def test_single_call_divergence_matches_two_calls():
     """Divergence single call (second sweep over the raw logits kept by pass 1)
-    against the two calls (second sweep recomputing the tiles): the same fp32
-    logits and sums added in another order, so the losses agree within 2e-5
-    relative; gradients within the bar of each other."""
+    against the two calls, whose forward keeps the raw logits too with this
+    workspace: the same losses bit for bit, gradients within the bar of each
+    other.  The recompute sweep adds the same sums in the same order, which
+    test_raw_and_recomputed_second_sweeps_agree checks."""
     p = synthetic.make_problem("lk_hybrid_bf16_8b", n_rows=700, hidden_dim=128, vocab=900)
     dev = to_device(p)
     gm = torch.ones(1, device="cuda")
@@ -397,8 +452,8 @@ def test_single_call_divergence_matches_two_calls():
     b.forward()
     dh2, dW2 = b.backward(grad_mean=gm)
     torch.cuda.synchronize()
-    assert torch.allclose(a.loss, b.loss, rtol=2e-5, atol=1e-6)
-    assert torch.allclose(a.reduced, b.reduced, rtol=2e-5, atol=1e-6)
+    assert torch.equal(a.loss, b.loss)
+    assert torch.equal(a.reduced, b.reduced)
     assert rel_frob(dh1.cpu().numpy(), dh2.cpu().numpy()) < 1e-2
     assert rel_frob(dW1.cpu().numpy(), dW2.cpu().numpy()) < 1e-2
 
