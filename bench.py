@@ -42,7 +42,9 @@ def parse():
     ap.add_argument("--shards", type=int, default=1,
                     help="G > 1: time one vocabulary shard's calls (V/G rows of W) and the "
                          "merges, i.e. one device's step of a G-way vocabulary-parallel group")
-    ap.add_argument("--cpu-sample-rows", type=int, default=1536)
+    ap.add_argument("--cpu-sample-rows", type=int, default=0,
+                    help="rows of the oracle's timed sample (0: 1536 at H = 4096, scaled by "
+                         "4096 / H, at least 256: about 10-30 s on the host cores)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also copy a buffer of known size (for counter calibration)")
@@ -277,7 +279,8 @@ def main():
         result["blas_reference"] = blas_reference(h, W, inputs["labels"], min(chunk_rows, N), N,
                                                   kernels)
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(prob, args.cpu_sample_rows)
+        rows = args.cpu_sample_rows or max(256, 1536 * 4096 // prob.hidden_dim // 64 * 64)
+        result["cpu_baseline"] = cpu_baseline(prob, min(rows, prob.n_rows))
     print(json.dumps(result), flush=True)
     if not result["workspace_below_logits"]:
         print(f"warning: the workspace ({result['workspace_gib']} GiB) is not below the [N, V] "

@@ -63,7 +63,8 @@ def trace_name(kernel: str) -> str:
              "k_rowdot": "rowdot", "k_transpose": "transpose", "k_validity": "validity",
              "k_reduce": "reduce", "k_seed": "seed", "k_align": "align",
              "k_stats_dual": "stats_dual", "k_div_heads": "div_heads", "k_heads_map": "heads_map",
-             "k_sum_parts": "sum_partials", "k_div_raw": "div_raw", "k_dz_raw": "dz_raw"}
+             "k_sum_parts": "sum_partials", "k_div_raw": "div_raw", "k_dz_raw": "dz_raw",
+             "k_target_gather": "target_gather"}
     name = names.get(base, base)
     if base == "k_stats":  # k_stats<T, TARGET, WNW, RAW>
         args = [a.strip() for a in targs.strip("<>").split(",")]
@@ -113,6 +114,21 @@ def summarize(fetch_csv: str, write_csv: str, copy_bytes: int):
 
 TRACE_CMD = ("rocprofv3 --kernel-trace --stats --output-format csv -d <out> -o run -- "
              "python3 <repo>/bench.py --workload {w} --steps 3 --warmup 1 --no-cpu-baseline")
+TRACE_STEPS = 4  # single-call steps of TRACE_CMD (warmup + timed), run before the two calls
+
+
+def single_call_avg_ms(trace_csv: str, kernel: str, launches_per_step: float):
+    """Average duration (ms) of `kernel`'s dispatches in the single-call steps of
+    TRACE_CMD: bench.py runs those first, so they are the kernel's first
+    TRACE_STEPS x launches-per-step dispatches (None if the trace has fewer)."""
+    n = int(round(TRACE_STEPS * launches_per_step))
+    durs = []
+    for r in csv.DictReader(open(trace_csv)):
+        if trace_name(r["Kernel_Name"]) == kernel:
+            durs.append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    if n <= 0 or len(durs) < n:
+        return None
+    return sum(durs[:n]) / n / 1e6
 PMC_CMD = ("rocprofv3 --pmc {c} --output-format csv -d <{d}> -o pmc -- python3 <repo>/bench.py "
            "--workload {w} --steps 1 --warmup 0 --no-cpu-baseline --calibrate-copy")
 
@@ -173,6 +189,15 @@ def markdown(stats_csv: str, traffic: dict, workload: str, bench: dict = None,
                 f"dominant kernel `{r['kernel']}` {r['avg_launch_ms']:.4f} ms per launch (HIP events "
                 f"on the library's stream), {r['achieved']:.1f} {r['unit']}, {r['frac']:.4f} of peak.",
                 ""]
+        trace_csv = stats_csv.replace("kernel_stats", "kernel_trace")
+        per_step = bench.get("kernels", {}).get(r["kernel"], {}).get("launches_per_step")
+        if os.path.exists(trace_csv) and per_step:
+            avg = single_call_avg_ms(trace_csv, r["kernel"], per_step)
+            if avg is not None:
+                out += [f"The same kernel in the traced run's single-call steps (its first "
+                        f"{int(round(TRACE_STEPS * per_step))} dispatches in `run_kernel_trace.csv`; "
+                        f"the averages above also hold the two calls' launches): {avg:.4f} ms per "
+                        f"launch.", ""]
     out += ["## HBM bytes per launch", "", "Commands (two passes, each its own run):", "", "```",
             PMC_CMD.format(c="FETCH_SIZE", d="fetch", w=workload),
             PMC_CMD.format(c="WRITE_SIZE", d="write", w=workload),

@@ -85,3 +85,22 @@ def test_markdown_lists_kernels_traffic_and_bench(tmp_path):
     assert "| `void k_gemm<unsigned short, float, 1, false>(GemmLaunch)` | 4 | 1.0000 |" in md
     assert "| gemm_dW | 2.000 | 1.000 | 3.000 |" in md
     assert "--workload ce_bf16_8b" in md and "`gemm_dW` 1.0000 ms per launch" in md
+
+
+def test_single_call_average_takes_the_first_dispatches(tmp_path):
+    """bench.py runs the single call's steps first: the kernel's first
+    TRACE_STEPS x launches-per-step dispatches are that call's."""
+    path = tmp_path / "run_kernel_trace.csv"
+    gemm = "void specloss::k_gemm<unsigned short, float, 1, false, 4>(specloss::GemmLaunch)"
+    other = "void specloss::k_dz_raw<unsigned short, false>(specloss::DzRawLaunch)"
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Kernel_Name", "Start_Timestamp", "End_Timestamp"])
+        w.writeheader()
+        t = 0
+        for i in range(P.TRACE_STEPS * 2 + 3):  # two launches per step, then three longer ones
+            dur = 1_000_000 if i < P.TRACE_STEPS * 2 else 9_000_000
+            w.writerow({"Kernel_Name": gemm, "Start_Timestamp": t, "End_Timestamp": t + dur})
+            w.writerow({"Kernel_Name": other, "Start_Timestamp": t, "End_Timestamp": t + 5})
+            t += dur
+    assert P.single_call_avg_ms(str(path), "gemm_dW", 2.0) == 1.0
+    assert P.single_call_avg_ms(str(path), "gemm_dW", 10.0) is None
