@@ -164,9 +164,11 @@ typedef struct {
  * process the rows in chunks (blog, "Streaming Cross Entropy" and "Backward
  * pass": per chunk, its logits, loss and gradients; only per-row statistics
  * outlive a chunk).  The single call and the backward stage a logit-gradient
- * chunk of about 2 x chunk x V elements (3 x for the staged divergences) in
- * the input dtype, which is the blog's streaming bound chunk x vocab x
- * dtype x 2, plus (by default) a transposed copy of W.
+ * chunk of about 2 x chunk x V elements in the input dtype, which is the
+ * blog's streaming bound chunk x vocab x dtype x 2, plus (by default) a
+ * transposed copy of W; for the divergences the single call also keeps the
+ * chunk's two raw fp32 logit rows (draft and target), chunk x V x 4 x 2
+ * bytes, so its chunks are smaller under the same limit.
  *   max_chunk_rows <= 0: the default policy.  The token set is streamed in
  *     at least four balanced chunks of at most 8192 rows, and the whole
  *     workspace stays strictly below N x V x (input element size) bytes, the
@@ -234,7 +236,11 @@ int specloss_saved_offset(int64_t n_rows, int32_t field, size_t* offset);
  * logsumexps, except when kl_div and rkl are the only ones and every row has
  * a target row of its own (no target_row map, or n_target_rows >= n_rows):
  * then one sweep computes both sides of a row together and forms
- * KL = E[log-ratio] - lse + lse from the same tiles.
+ * KL = E[log-ratio] - lse + lse from the same tiles.  When the workspace
+ * holds the raw fp32 logit rows of both sides for min(N, 1024) rows, the
+ * first sweep keeps them and the second reads them; otherwise the second
+ * sweep recomputes both tiles.  Either way the results are the same bits
+ * (lmhead_loss_chunk with call 0 gives the chunk).
  */
 int lmhead_loss_fwd(const specloss_problem* p, void* workspace, size_t ws_bytes, float* loss,
                     float* term_loss, float* lse_q, void* saved, int64_t* counts, float* reduced,
@@ -290,9 +296,9 @@ int lmhead_loss_bwd(const specloss_problem* p, const float* grad_loss, const flo
  * accumulated over chunks), and the logits are never recomputed: for the
  * label and argmax-p cross-entropies the forward pass leaves exp(z - label
  * logit) of the chunk (in the input dtype, both layouts) in the workspace;
- * with divergences the second forward pass leaves q, q - p and, for rkl and
- * jsd, log q - log p; the logit gradient is formed from these.  `saved` may
- * be NULL.  Errors as for the two calls.
+ * with divergences the first forward pass keeps the raw fp32 logit rows of
+ * both sides, from which the second sweep's sums and then the logit gradient
+ * are formed.  `saved` may be NULL.  Errors as for the two calls.
  */
 int lmhead_loss_fwd_bwd(const specloss_problem* p, void* workspace, size_t ws_bytes, float* loss,
                         float* term_loss, float* lse_q, void* saved, int64_t* counts,
