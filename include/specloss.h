@@ -280,6 +280,10 @@ int lmhead_loss_fwd_noalloc(const specloss_problem* p, float* loss, float* term_
  *   dW      [V, H] fp32, or NULL to skip.  accumulate_dW != 0 adds to its
  *           contents, else it is overwritten.  Gradients flow to the draft
  *           side only (no gradient for target_hidden or W_t).
+ * For the divergences the recomputed logits go through raw fp32 rows of
+ * both sides when the workspace holds them for min(N, 1024) rows (as in the
+ * single call); otherwise the logit gradient is formed from the recomputed
+ * tiles directly.  The two ways agree to fp32 rounding.
  */
 int lmhead_loss_bwd(const specloss_problem* p, const float* grad_loss, const float* grad_mean,
                     const int64_t* counts, const void* saved, void* workspace, size_t ws_bytes,

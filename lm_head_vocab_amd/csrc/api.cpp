@@ -149,8 +149,10 @@ struct Layout {
   // ur, as the single call does)
   bool fwd_raw;
   size_t pz, pu, p2, zy, hmap, zr, ur, fwd_end;
-  // backward
-  size_t wt, ht, dz, dzt, dhp, bwd_end;
+  // backward (bwd_raw: the divergences' logit rows are recomputed into raw
+  // buffers, b_zr and b_ur, with partial scratch b_pz / b_pu, as in pass 1)
+  bool bwd_raw;
+  size_t wt, ht, dz, dzt, dhp, b_pz, b_pu, b_zr, b_ur, bwd_end;
   // single-call forward+backward: forward partials and backward buffers at once;
   // the divergences keep the chunk's raw fp32 logits (f_zr: Nc draft rows,
   // f_ur: Nu target rows; the same in the forward region with fwd_raw) and
@@ -224,7 +226,7 @@ int32_t dh_splits(int64_t Nc, int64_t H) {
 
 // fp32 inputs always take LAYOUT_COPIES (the transposing LDS load is bf16).
 Layout plan(const specloss_problem* p, const KindSet& k, int64_t Nc,
-            int32_t layout = LAYOUT_COPIES, bool fwd_raw = false) {
+            int32_t layout = LAYOUT_COPIES, bool fwd_raw = false, bool bwd_raw = false) {
   Layout L;
   L.N = p->n_rows;
   L.H = p->hidden;
@@ -272,6 +274,11 @@ Layout plan(const specloss_problem* p, const KindSet& k, int64_t Nc,
   L.dh_splits = dh_splits(Nc, L.H);
   const size_t dhp_bytes = L.dh_splits > 1 ? (size_t)L.dh_splits * Nc * L.H * 4 : 0;
   L.dhp = take(dhp_bytes);
+  L.bwd_raw = bwd_raw && k.stage_div;
+  L.b_pz = take(L.bwd_raw ? 2 * tile_cols : 0);
+  L.b_pu = take(L.bwd_raw ? pu_bytes : 0);
+  L.b_zr = take(L.bwd_raw ? (size_t)Nc * L.Vp * 4 : 0);
+  L.b_ur = take(L.bwd_raw ? (size_t)L.Nu * L.Vp * 4 : 0);
   L.bwd_end = o;
   o = L.head_end;
   L.f_pz = take(2 * tile_cols);
@@ -305,11 +312,12 @@ size_t workspace_end(const Layout& L) {
 // `ws_bytes` (strictly below it when `strict`).
 int64_t largest_chunk(const specloss_problem* p, const KindSet& k, size_t ws_bytes,
                       Region region, int32_t layout, int64_t top, bool strict = false,
-                      bool fwd_raw = false) {
+                      bool raw = false) {
   int64_t lo = 1, hi = top / kChunkQuantum, best = 0;
   while (lo <= hi) {  // the requirement grows with the chunk
     const int64_t mid = (lo + hi) / 2;
-    const Layout L = plan(p, k, mid * kChunkQuantum, layout, fwd_raw);
+    const Layout L = plan(p, k, mid * kChunkQuantum, layout, raw && region == REGION_FWD,
+                          raw && region == REGION_BWD);
     const size_t need = region_end(L, region);
     if (strict ? need < ws_bytes : need <= ws_bytes) {
       best = mid;
@@ -375,6 +383,36 @@ int64_t pick_fwd_chunk(const specloss_problem* p, const KindSet& k, size_t ws_by
     }
   }
   return pick_chunk(p, k, ws_bytes, REGION_FWD);
+}
+
+// Chunk and layout of the two-call backward.  The divergences recompute both
+// raw logit rows with the pass-1 contraction and form dz from them
+// (k_dz_raw) when the workspace holds them for a chunk of at least min(N,
+// 1024) rows in some layout (tried in pick_chunk's order); otherwise, and for
+// vocabulary shards, one dual recompute kernel forms dz from the tiles.
+int64_t pick_bwd_chunk(const specloss_problem* p, const KindSet& k, size_t ws_bytes,
+                       int32_t* layout, bool* raw, bool shard) {
+  *raw = false;
+  if (k.stage_div && !shard) {
+    const int64_t top = round_up(p->n_rows, kChunkQuantum);
+    const int64_t want = top < 1024 ? top : 1024;
+    const int32_t forced = forced_layout(p);
+    int32_t lays[3] = {LAYOUT_COPIES, LAYOUT_DW_COPIES, LAYOUT_NONE};
+    int n_lays = p->in_dtype == SPECLOSS_BF16 ? 3 : 1;
+    if (forced >= 0) {
+      lays[0] = forced;
+      n_lays = 1;
+    }
+    for (int i = 0; i < n_lays; ++i) {
+      const int64_t nc = largest_chunk(p, k, ws_bytes, REGION_BWD, lays[i], top, false, true);
+      if (nc >= want) {
+        *layout = lays[i];
+        *raw = true;
+        return nc;
+      }
+    }
+  }
+  return pick_chunk(p, k, ws_bytes, REGION_BWD, layout);
 }
 
 // The default chunk (workspace size for max_chunk_rows <= 0).  Blog, "Backward
@@ -875,10 +913,13 @@ struct SpanCarry {
   bool valid = false;
 };
 
-int div_chunk_raw(const specloss_problem* p, const KindSet& k, const Layout& L, const FwdBufs& b,
-                  const SavedView& sv, float* loss, float* terms, int64_t r0, int64_t rows,
-                  float* zr, float* ur, RawRows& rr, SpanCarry& carry, Tracer& tr,
-                  hipStream_t stream) {
+// The raw logit rows of chunk rows [r0, r0 + rows) into zr and ur (`rr`
+// describes them), with pass 1's contractions; `stats`: also the pass-1
+// statistics (partials in b.pz / b.pu and, for aligned heads, merged per
+// target row), else the partials are scratch.
+int raw_pass1(const specloss_problem* p, const KindSet& k, const Layout& L, const FwdBufs& b,
+              int64_t r0, int64_t rows, float* zr, float* ur, RawRows& rr, SpanCarry& carry,
+              bool stats, Tracer& tr, hipStream_t stream) {
   const bool bf16 = p->in_dtype == SPECLOSS_BF16;
   const int64_t H = L.H, Nc = b.Nc, tile_cols = L.Tv * Nc;
   rr = RawRows{zr, L.Vp, ur, L.Vp, nullptr, 0, (int32_t)Nc};
@@ -934,8 +975,8 @@ int div_chunk_raw(const specloss_problem* p, const KindSet& k, const Layout& L, 
       su.pi = reinterpret_cast<int32_t*>(b.pu + 2 * ufield);
       su.pq = b.pu + 3 * ufield;
       su.raw = ur + keep * L.Vp;
-      TRACED(tr, K_STATS_P, 2.0 * nn * H * p->vocab, launch_stats(bf16, true, su, stream));
-      if (j0 < Nt) {
+      TRACED(tr, K_STATS_P, 2.0 * nn * H * p->vocab, launch_stats(bf16, stats, su, stream));
+      if (stats && j0 < Nt) {
         // statistics per target row
         char* tb = static_cast<char*>(b.tstat);
         const size_t fs = align_up((size_t)Nt * 4, kAlign);
@@ -966,8 +1007,17 @@ int div_chunk_raw(const specloss_problem* p, const KindSet& k, const Layout& L, 
     su.pq = b.pu + 3 * tile_cols;
     // shared target rows: the statistics come from the prepass, only u is kept
     TRACED(tr, K_STATS_P, 2.0 * rows * H * p->vocab,
-           launch_stats(bf16, !L.shared_target, su, stream));
+           launch_stats(bf16, stats && !L.shared_target, su, stream));
   }
+  return SPECLOSS_OK;
+}
+
+int div_chunk_raw(const specloss_problem* p, const KindSet& k, const Layout& L, const FwdBufs& b,
+                  const SavedView& sv, float* loss, float* terms, int64_t r0, int64_t rows,
+                  float* zr, float* ur, RawRows& rr, SpanCarry& carry, Tracer& tr,
+                  hipStream_t stream) {
+  const int64_t Nc = b.Nc, tile_cols = L.Tv * Nc;
+  TRY(raw_pass1(p, k, L, b, r0, rows, zr, ur, rr, carry, true, tr, stream));
   TRY(merge_pass1(p, k, L, b, sv, r0, rows, false, tr, stream));
   TRY(gather_label_logits(p, k, L, b, sv, r0, rows, tr, stream));
 
@@ -1148,6 +1198,37 @@ int ce_chunk_staged(const specloss_problem* p, const KindSet& k, const Layout& L
   return SPECLOSS_OK;
 }
 
+// dz (and dz^T when dzt is set) of chunk rows [r0, r0 + rows) from the raw
+// logit rows `rr`, the seeds and the saved per-row sums.
+int dz_from_raw(const specloss_problem* p, const Layout& L, const RawRows& rr, int64_t r0,
+                int64_t rows, const float* seed, const SavedView& sv, void* dz, void* dzt,
+                Tracer& tr, hipStream_t stream) {
+  DzRawLaunch dr{};
+  dr.r = rr;
+  dr.tiles_m = (int32_t)L.Tv;
+  dr.ncols = (int32_t)rows;
+  dr.vocab = (int32_t)L.V;
+  dr.r0 = r0;
+  dr.seed = seed;
+  dr.sv = sv;
+  dr.w_lab = p->weights[SPECLOSS_CE_LABEL];
+  dr.w_arg = p->weights[SPECLOSS_CE_ARGMAX_P];
+  dr.w_kl = p->weights[SPECLOSS_KL];
+  dr.w_tv = p->weights[SPECLOSS_TV];
+  dr.w_nla = p->weights[SPECLOSS_NLA];
+  dr.w_lk = p->weights[SPECLOSS_LK_HYBRID];
+  dr.w_rkl = p->weights[SPECLOSS_RKL];
+  dr.w_jsd = p->weights[SPECLOSS_JSD];
+  dr.dz = dz;
+  dr.ld_dz = L.Vp;
+  dr.dzt = dzt;
+  dr.ld_dzt = L.Nc;
+  dr.row_blocks = (int32_t)(cdiv(rows, 256) * 4);
+  TRACED(tr, K_DZ_RAW, (double)dr.row_blocks * 64 * L.Vp * (8.0 + L.es * (dzt ? 2 : 1)),
+         launch_dz_raw(p->in_dtype == SPECLOSS_BF16, dr, stream));
+  return SPECLOSS_OK;
+}
+
 int launch_reduce_for(const specloss_problem* p, const KindSet& k, const float* loss,
                       const float* terms, const int64_t* counts, float* reduced, Tracer& tr,
                       hipStream_t stream) {
@@ -1298,11 +1379,12 @@ int check_bwd_inputs(const float* grad_loss, const float* grad_mean, const int64
 int bwd_recompute(const specloss_problem* p, const KindSet& k, const float* grad_loss,
                   const float* grad_mean, const int64_t* counts, const void* saved,
                   void* workspace, size_t ws_bytes, void* dhidden, int32_t dh_dtype, float* dW,
-                  int accumulate_dW, int64_t vocab_offset, hipStream_t stream) {
+                  int accumulate_dW, int64_t vocab_offset, bool shard, hipStream_t stream) {
   int32_t layout = LAYOUT_COPIES;
-  const int64_t Nc = pick_chunk(p, k, ws_bytes, REGION_BWD, &layout);
+  bool raw = false;
+  const int64_t Nc = pick_bwd_chunk(p, k, ws_bytes, &layout, &raw, shard);
   if (Nc <= 0) return SPECLOSS_E_WORKSPACE;
-  const Layout L = plan(p, k, Nc, layout);
+  const Layout L = plan(p, k, Nc, layout, false, raw);
   char* ws = static_cast<char*>(workspace);
   const bool bf16 = p->in_dtype == SPECLOSS_BF16;
   const int64_t N = L.N, H = L.H, V = L.V, Vp = L.Vp;
@@ -1313,6 +1395,10 @@ int bwd_recompute(const specloss_problem* p, const KindSet& k, const float* grad
   void* dz = ws + L.dz;
   void* dzt = L.dw_copies ? ws + L.dzt : nullptr;
   Tracer tr{p->trace, stream};
+  // raw logit rows: partials are scratch, the span carry as in the forward
+  const FwdBufs rb{reinterpret_cast<float*>(ws + L.b_pz), reinterpret_cast<float*>(ws + L.b_pu),
+                   nullptr, nullptr, Nc, nullptr, nullptr};
+  SpanCarry carry;
 
   TRY(launch_seed_for(p, sv, grad_loss, grad_mean, counts, seed, tr, stream));
   if (dhidden && L.wt_copy)
@@ -1325,6 +1411,19 @@ int bwd_recompute(const specloss_problem* p, const KindSet& k, const float* grad
     if (dW && L.dw_copies)
       TRACED(tr, K_TRANSPOSE_H, 2.0 * Nc * H * L.es, launch_transpose(bf16, hc, rows, H, ht, Nc, stream));
 
+    if (raw) {
+      RawRows rr{};
+      TRY(raw_pass1(p, k, L, rb, r0, rows, reinterpret_cast<float*>(ws + L.b_zr),
+                    reinterpret_cast<float*>(ws + L.b_ur), rr, carry, false, tr, stream));
+      TRY(dz_from_raw(p, L, rr, r0, rows, seed, sv, dz, dzt, tr, stream));
+      if (dhidden)
+        TRY(contract_dh(p, L, Nc, dz, wt, r0, rows, dhidden, dh_dtype, tr, stream, nullptr,
+                        reinterpret_cast<float*>(ws + L.dhp)));
+      if (dW)
+        TRY(contract_dW(p, L, Nc, dz, dzt, ht, Nc, r0, rows, chunk > 0 || accumulate_dW, dW, tr,
+                        stream));
+      continue;
+    }
     DzLaunch dl{};
     dl.Az = op(p->W, H, V);
     dl.Bz = op(hc, H, rows);
@@ -1434,7 +1533,8 @@ int lmhead_loss_chunk(const specloss_problem* p, size_t ws_bytes, int32_t call,
     bool raw;
     nc = pick_fwd_chunk(p, k, ws_bytes, &raw);
   } else if (call == 1) {
-    nc = pick_chunk(p, k, ws_bytes, REGION_BWD, &lay);
+    bool raw;
+    nc = pick_bwd_chunk(p, k, ws_bytes, &lay, &raw, false);
   } else {
     nc = pick_chunk(p, k, ws_bytes, REGION_FUSED, &lay);
   }
@@ -1507,7 +1607,7 @@ int lmhead_loss_bwd(const specloss_problem* p, const float* grad_loss, const flo
   TRY(check_problem(p, &k));
   TRY(check_bwd_inputs(grad_loss, grad_mean, counts, saved, dhidden, dh_dtype, dW, workspace));
   return bwd_recompute(p, k, grad_loss, grad_mean, counts, saved, workspace, ws_bytes, dhidden,
-                       dh_dtype, dW, accumulate_dW, 0, stream);
+                       dh_dtype, dW, accumulate_dW, 0, false, stream);
 }
 
 int lmhead_loss_fwd_bwd(const specloss_problem* p, void* workspace, size_t ws_bytes, float* loss,
@@ -1580,29 +1680,7 @@ int lmhead_loss_fwd_bwd(const specloss_problem* p, void* workspace, size_t ws_by
     if (k.stage_div) {
       RawRows rr{};
       TRY(div_chunk_raw(p, k, L, b, sv, loss, terms, r0, rows, zr, ur, rr, carry, tr, stream));
-      DzRawLaunch dr{};
-      dr.r = rr;
-      dr.tiles_m = (int32_t)L.Tv;
-      dr.ncols = (int32_t)rows;
-      dr.vocab = (int32_t)V;
-      dr.r0 = r0;
-      dr.seed = seed;
-      dr.sv = sv;
-      dr.w_lab = p->weights[SPECLOSS_CE_LABEL];
-      dr.w_arg = p->weights[SPECLOSS_CE_ARGMAX_P];
-      dr.w_kl = p->weights[SPECLOSS_KL];
-      dr.w_tv = p->weights[SPECLOSS_TV];
-      dr.w_nla = p->weights[SPECLOSS_NLA];
-      dr.w_lk = p->weights[SPECLOSS_LK_HYBRID];
-      dr.w_rkl = p->weights[SPECLOSS_RKL];
-      dr.w_jsd = p->weights[SPECLOSS_JSD];
-      dr.dz = dz;
-      dr.ld_dz = Vp;
-      dr.dzt = dzt;
-      dr.ld_dzt = Nc;
-      dr.row_blocks = (int32_t)(cdiv(rows, 256) * 4);
-      TRACED(tr, K_DZ_RAW, (double)dr.row_blocks * 64 * Vp * (8.0 + L.es * (dzt ? 2 : 1)),
-             launch_dz_raw(bf16, dr, stream));
+      TRY(dz_from_raw(p, L, rr, r0, rows, seed, sv, dz, dzt, tr, stream));
     } else {
       TRY(fwd_chunk(p, k, L, b, sv, loss, terms, r0, rows, dz, tr, stream));
       DzStageLaunch ds{};
@@ -1938,7 +2016,7 @@ int lmhead_shard_bwd(const specloss_problem* p, const specloss_shard* sh, const 
   TRY(check_bwd_inputs(grad_loss, grad_mean, counts, saved, dh_partial, SPECLOSS_F32, dW,
                        workspace));
   return bwd_recompute(p, k, grad_loss, grad_mean, counts, saved, workspace, ws_bytes, dh_partial,
-                       SPECLOSS_F32, dW, accumulate_dW, sh->vocab_offset, stream);
+                       SPECLOSS_F32, dW, accumulate_dW, sh->vocab_offset, true, stream);
 }
 
 int specloss_sum_partials(const float* parts, int64_t n, int32_t n_parts, void* out,

@@ -15,8 +15,7 @@ import synthetic
 import lm_head_vocab_amd as L
 from oracle import specloss_oracle as O
 from lm_head_vocab_amd.runner import ShardedLossRun
-from tests._gpu_helpers import (GRAD_FROB, check_tokens, full_parity, make_run, rel_frob, say,
-                                to_device)
+from tests._gpu_helpers import (GRAD_FROB, full_parity, make_run, rel_frob, say, to_device)
 
 pytestmark = pytest.mark.gpu
 
@@ -386,26 +385,29 @@ def test_single_call_identical_target_ties():
     assert np.allclose(run.saved_field(5).cpu().numpy(), 0.5, atol=1e-5)  # S
 
 
-def _forward_trace(run):
-    import lm_head_vocab_amd as L
+def _traced(run, call):
     trace = L.binding.Trace(capacity=4096)
     trace.attach(run.problem)
-    run.forward()
+    out = call()
     torch.cuda.synchronize()
     names = {n for n, _, _ in trace.read()}
     run.problem.trace = None
     trace.close()
-    return names
+    return names, out
 
 
 @pytest.mark.parametrize("case", ["mix_bf16", "mix_f32", "heads_bf16"])
 def test_raw_and_recomputed_second_sweeps_agree(case):
-    """The two-call forward's second sweep either reads raw logits kept by pass 1
-    (a workspace that holds them for min(N, 1024) rows) or recomputes both tiles
-    (a smaller one, e.g. the allocation-free scratch): the same losses, terms
-    and saved state bit for bit, since every sweep adds its sums in one order
-    and the contractions give the same logits.  Every divergence kind at once
-    (jsd and rkl included); aligned heads compare the shared-target-tile sweep."""
+    """The two calls either keep raw logit rows (a workspace that holds them for
+    min(N, 1024) rows: the forward's second sweep reads them, the backward
+    recomputes them with the pass-1 contraction and forms dz from them) or
+    recompute the tiles (a smaller one, e.g. the allocation-free scratch).
+    Forward: the same losses, terms and saved state bit for bit, since every
+    sweep adds its sums in one order and the contractions give the same
+    logits.  Backward: the same gradient formula in two kernels, so dh and dW
+    agree to fp32 rounding (rel. Frobenius 1e-3) and each meets the oracle's
+    bar.  Every divergence kind at once (jsd and rkl included); aligned heads
+    compare the shared-target-tile sweep."""
     w = {"tv": 0.7, "ce": 0.2, "kl_div": 0.4, "rkl": 0.3, "jsd": 0.5, "nla": 0.2,
          "lk_hybrid": 0.6, "ce_label": 0.1}
     if case == "heads_bf16":
@@ -424,7 +426,8 @@ def test_raw_and_recomputed_second_sweeps_agree(case):
     dev = to_device(p)
     raw = make_run(p, dev, workspace_bytes=256 << 20, flags=None)
     rec = make_run(p, dev, max_chunk_rows=256)  # raw rows for 1024 rows do not fit
-    names_raw, names_rec = _forward_trace(raw), _forward_trace(rec)
+    names_raw, _ = _traced(raw, raw.forward)
+    names_rec, _ = _traced(rec, rec.forward)
     assert raw_kernel in names_raw and rec_kernel not in names_raw, names_raw
     assert rec_kernel in names_rec and raw_kernel not in names_rec, names_rec
     assert torch.equal(raw.counts, rec.counts)
@@ -434,7 +437,17 @@ def test_raw_and_recomputed_second_sweeps_agree(case):
     for f in range(L.binding.SAVED_FIELDS):
         a_f, b_f = raw.saved_field(f, torch.int32), rec.saved_field(f, torch.int32)
         assert torch.equal(a_f[valid], b_f[valid]), f"saved field {f}"
-    check_tokens(raw.loss.cpu().numpy(), O.forward(p).loss, "loss against the oracle")
+
+    gm = torch.ones(1, device="cuda")
+    bnames_raw, (dh1, dW1) = _traced(raw, lambda: raw.backward(grad_mean=gm))
+    bnames_rec, (dh2, dW2) = _traced(rec, lambda: rec.backward(grad_mean=gm))
+    assert "dz_raw" in bnames_raw and "dz" not in bnames_raw, bnames_raw
+    assert "dz" in bnames_rec and "dz_raw" not in bnames_rec, bnames_rec
+    dh1, dW1, dh2, dW2 = (t.float().cpu().numpy() for t in (dh1, dW1, dh2, dW2))
+    assert rel_frob(dh1, dh2) < 1e-3 and rel_frob(dW1, dW2) < 1e-3
+    # the raw path of both calls against the oracle
+    full_parity(p, workspace_bytes=256 << 20, tag=f"sweeps-raw-{case}",
+                expect_kernels=([raw_kernel, "dz_raw"], [rec_kernel, "dz"]))
 
 
 def test_single_call_divergence_matches_two_calls():
