@@ -892,31 +892,24 @@ int fwd_chunk(const specloss_problem* p, const KindSet& k, const Layout& L, cons
                         stream);
 }
 
-// Forward of chunk rows [r0, r0 + rows) for the divergences in the single
-// call.  Pass 1 of each side keeps the raw fp32 logits (z into zr, u into
-// ur, both [.][Vp]), so the second sweep (k_div_raw) and later the logit
-// gradient read them instead of computing both contractions again (blog
-// "Backward pass": at most chunk x vocab x 2 logits-sized values are held,
-// here in fp32).  With aligned heads the target side runs once over the
-// chunk's span of target rows [jlo, jhi): its statistics are merged per
-// target row and gathered, and ur holds one row per token of the span.  Other
-// shared target rows take their statistics from the prepass, with u kept per
-// chunk row.  Fills `rr` for the logit gradient.
-//
-// Consecutive chunks' spans overlap by a few target rows (the spread of the
-// shifts): `carry` holds the previous chunk's span, whose last rows are moved
-// to the front of ur instead of being computed again, so every chunk after
-// the first contracts only its Nc / K new target rows (whole 256-row tiles
-// when Nc / K is a multiple of 256).
+// The previous chunk's span of target rows (aligned heads).  Consecutive
+// chunks' spans overlap by a few rows (the spread of the shifts plus one or
+// two): those rows move to the front of ur instead of being computed again,
+// so every chunk after the first contracts only its Nc / K new target rows
+// (whole 256-row tiles when Nc / K is a multiple of 256).
 struct SpanCarry {
   int64_t jlo = 0, jhi = 0;
   bool valid = false;
 };
 
-// The raw logit rows of chunk rows [r0, r0 + rows) into zr and ur (`rr`
-// describes them), with pass 1's contractions; `stats`: also the pass-1
-// statistics (partials in b.pz / b.pu and, for aligned heads, merged per
-// target row), else the partials are scratch.
+// The raw fp32 logit rows of chunk rows [r0, r0 + rows) with pass 1's
+// contractions: z into zr [Nc][Vp], u into ur [Nu][Vp]; `rr` describes them.
+// With aligned heads the target side runs once over the chunk's span of
+// target rows [jlo, jhi) (ur holds one row per token of the span, read
+// through target_row - jlo); otherwise u is kept per chunk row.  `stats`:
+// also the pass-1 statistics (partials in b.pz / b.pu and, for aligned
+// heads, merged per target row into b.tstat; other shared target rows take
+// theirs from the prepass), else the partials are scratch.
 int raw_pass1(const specloss_problem* p, const KindSet& k, const Layout& L, const FwdBufs& b,
               int64_t r0, int64_t rows, float* zr, float* ur, RawRows& rr, SpanCarry& carry,
               bool stats, Tracer& tr, hipStream_t stream) {
@@ -1012,6 +1005,12 @@ int raw_pass1(const specloss_problem* p, const KindSet& k, const Layout& L, cons
   return SPECLOSS_OK;
 }
 
+// Forward of chunk rows [r0, r0 + rows) for the divergences that keep raw
+// logits (the single call, and the two-call forward when its workspace holds
+// them): raw_pass1 with statistics, the merge, the label logits, the second
+// sweep's sums from the raw rows (k_div_raw) and the per-row losses (blog
+// "Backward pass": at most chunk x vocab x 2 logits-sized values are held,
+// here in fp32).  Fills `rr` for the logit gradient.
 int div_chunk_raw(const specloss_problem* p, const KindSet& k, const Layout& L, const FwdBufs& b,
                   const SavedView& sv, float* loss, float* terms, int64_t r0, int64_t rows,
                   float* zr, float* ur, RawRows& rr, SpanCarry& carry, Tracer& tr,
