@@ -7,13 +7,17 @@
 //            k_stats on (W_t, target rows) -> same plus argmax (target kinds)
 //   merge    k_combine1 -> logsumexp of q and p, argmax p
 //   gather   k_rowdot   -> label logit z_y (ce_label) and z at argmax p (ce)
-//   pass 2   k_div      -> alpha, S, KL, rKL, JSD, E_q[g] partials (divergences)
+//   pass 2   k_div      -> alpha, S, KL, rKL, JSD, E_q[g] partials (divergences),
+//            or k_div_raw over the raw logit rows pass 1 kept (k_stats RAW)
 //   losses   k_combine2 -> per-row weighted loss, unweighted terms, saved stats
 // then k_reduce -> sum / n_valid (blog "Backward pass": one denominator).
 // Backward, per chunk (blog "Backward pass": per-chunk logits, gradients for
 // the chunk's hidden states, LM-head gradient accumulated over chunks):
-//   k_dz (recompute + logit gradient) -> staged dz chunk, both layouts
+//   k_dz (recompute + logit gradient), or for the divergences raw logit rows
+//   recomputed by pass 1's contraction and k_dz_raw -> dz chunk, both layouts
 //   k_gemm dh = dz W^T^T  and  k_gemm dW (+)= dz^T h, chunks in order.
+// The single call (lmhead_loss_fwd_bwd) forms dz from what its forward kept:
+// the staged exp(z - label logit) of the cross-entropies, or the raw rows.
 #include <math.h>
 #include <string.h>
 
