@@ -313,24 +313,20 @@ size_t workspace_end(const Layout& L) {
 }
 
 // Largest chunk (multiple of 256, at most `top` rows) whose region fits
-// `ws_bytes` (strictly below it when `strict`).
+// `ws_bytes` (strictly below it when `strict`).  The requirement is not
+// monotonic in the chunk (a chunk with few row tiles adds split-K partials of
+// dh, e.g. 1792 rows at H = 16384 take more than 2048), so every candidate is
+// tried from the top; a plan costs a few arithmetic operations.
 int64_t largest_chunk(const specloss_problem* p, const KindSet& k, size_t ws_bytes,
                       Region region, int32_t layout, int64_t top, bool strict = false,
                       bool raw = false) {
-  int64_t lo = 1, hi = top / kChunkQuantum, best = 0;
-  while (lo <= hi) {  // the requirement grows with the chunk
-    const int64_t mid = (lo + hi) / 2;
-    const Layout L = plan(p, k, mid * kChunkQuantum, layout, raw && region == REGION_FWD,
+  for (int64_t m = top / kChunkQuantum; m >= 1; --m) {
+    const Layout L = plan(p, k, m * kChunkQuantum, layout, raw && region == REGION_FWD,
                           raw && region == REGION_BWD);
     const size_t need = region_end(L, region);
-    if (strict ? need < ws_bytes : need <= ws_bytes) {
-      best = mid;
-      lo = mid + 1;
-    } else {
-      hi = mid - 1;
-    }
+    if (strict ? need < ws_bytes : need <= ws_bytes) return m * kChunkQuantum;
   }
-  return best * kChunkQuantum;
+  return 0;
 }
 
 int32_t forced_layout(const specloss_problem* p) {

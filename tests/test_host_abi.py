@@ -310,6 +310,9 @@ def _shape(name):
         return _problem(N=16384, H=4096, V=128256, weights={"lk_hybrid": 1.0}, target=16384)
     p = _problem(N=3 * 4096, H=16384, V=128256, weights={"ce": 0.1, "tv": 0.9}, target=4096)
     p.target_row = 0x60000
+    p.n_heads = 3  # the workload declares its token-major heads
+    for i, sh in enumerate((1, 2, 3)):
+        p.head_shift[i] = sh
     return p
 
 
@@ -323,7 +326,7 @@ def _chunk(lib, p, ws, call):
     ("ce_bf16_1b", 2048, "copies"),
     ("ce_bf16_8b", 8192, "copies"),
     ("lk_hybrid_bf16_8b", 1792, "copies"),
-    ("multihead_bf16_405b", 1536, "no_weight_copy"),
+    ("multihead_bf16_405b", 2048, "no_weight_copy"),
 ])
 def test_default_chunk_streams_below_the_logits_size(lib, name, chunk, layout):
     """Blog, "Backward pass" / "Choosing the chunk size": the default workspace
@@ -391,3 +394,20 @@ def test_size_limits(lib):
     rows, lay = ctypes.c_int64(), ctypes.c_int32()
     assert lib.lmhead_loss_chunk(ctypes.byref(p), ws, 2, ctypes.byref(rows), ctypes.byref(lay)) == 0
     assert 0 < rows.value <= 8192
+
+
+def test_chunk_search_takes_the_largest_fitting_chunk(lib):
+    """The workspace a chunk needs is not monotonic in the chunk: at H = 16384
+    a 1792-row chunk gives the dh contraction 7 x 64 tiles and four split-K
+    slices of fp32 partials, more than a 2048-row chunk (8 x 64 tiles, no
+    split) needs.  A workspace sized for 2048 rows must give 2048 rows."""
+    p = _shape("multihead_bf16_405b")
+    p.flags = B.FLAG_NO_WEIGHT_COPY
+    sizes = {}
+    for rows in (1792, 2048):
+        out = ctypes.c_size_t()
+        assert lib.lmhead_loss_workspace_size(ctypes.byref(p), rows, ctypes.byref(out)) == 0
+        sizes[rows] = out.value
+    assert sizes[1792] > sizes[2048]
+    for call in (B.CALL_BWD, B.CALL_FWD_BWD):
+        assert _chunk(lib, p, sizes[2048], call) == (0, 2048, "no_weight_copy")
