@@ -728,7 +728,8 @@ def _heads_problem(S, shifts, batch, H, V, weights, seed):
 
 
 @pytest.mark.parametrize("case", ["k3_single", "k3_two_calls", "k2_batch_single",
-                                  "k3_far_shifts_single", "k3_lean_single", "k3_tv_single",
+                                  "k3_far_shifts_single", "k3_wide_shifts_single",
+                                  "k3_lean_single", "k3_tv_single",
                                   "k4_single_per_row", "k3_f32_two_calls_per_row"])
 def test_aligned_heads_share_target_tiles(case):
     """Declared token-major heads: each target tile is computed once for the
@@ -744,6 +745,8 @@ def test_aligned_heads_share_target_tiles(case):
     single = "single" in case
     shifts, batch = {"k3_single": ((1, 2, 3), 1), "k3_two_calls": ((1, 2, 3), 1),
                      "k2_batch_single": ((2, 0), 3), "k3_far_shifts_single": ((0, 7, 70), 2),
+                     # spans overlap by more than a chunk advances: no rows are carried
+                     "k3_wide_shifts_single": ((0, 1, 150), 1),
                      "k3_lean_single": ((1, 2, 3), 1), "k3_tv_single": ((1, 2, 3), 1),
                      "k4_single_per_row": ((1, 2, 3, 4), 1),
                      "k3_f32_two_calls_per_row": ((1, 2, 3), 1)}[case]
@@ -788,7 +791,10 @@ def test_aligned_heads_share_target_tiles(case):
         assert "div_raw" in names, names
         target_work = lambda rs: sum(w for n, _, w in rs if n == "stats_p")
         if not per_row:
-            assert target_work(out["trace"]) < 0.7 * target_work(recs)
+            # spans of about N / K rows per chunk plus the shift spread; the
+            # wide shifts overlap most of a span with the next one's
+            bound = 0.8 if case == "k3_wide_shifts_single" else 0.7
+            assert target_work(out["trace"]) < bound * target_work(recs)
     else:
         assert plain in names and shared not in names, names
     assert torch.equal(run.loss, ref.loss)
