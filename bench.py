@@ -183,7 +183,8 @@ def main():
         torch.cuda.synchronize()
         starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
         ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-        trace = L.binding.Trace(capacity=128 * steps)
+        # room for every launch: a few per call plus at most 24 per chunk
+        trace = L.binding.Trace(capacity=steps * (32 + 24 * max_chunks))
         trace.attach(run.problem)
         torch.cuda.synchronize()
         wall0 = time.time()
@@ -193,12 +194,20 @@ def main():
             ends[i].record(stream)
         torch.cuda.synchronize()
         wall = time.time() - wall0
-        kernels = summarize_trace(trace.read(), steps)
+        entries = trace.read()
+        if len(entries) >= trace.capacity:
+            raise RuntimeError("the launch trace filled up; per-kernel times would be partial")
+        kernels = summarize_trace(entries, steps)
         run.problem.trace = None
         trace.close()
         per = sorted(a.elapsed_time(b) for a, b in zip(starts, ends))
         return sum(per) / steps, per[len(per) // 2], kernels, wall
 
+    if G == 1:
+        calls = (L.binding.CALL_FWD, L.binding.CALL_BWD, L.binding.CALL_FWD_BWD)
+        max_chunks = max(-(-N // run.chunk(c)[0]) for c in calls)
+    else:
+        max_chunks = -(-N // 256) * 2
     ms_mean, ms_med, kernels, wall = timed(step_single, args.steps, args.warmup)
     if step_two is not None:
         ms_two, ms_two_med, kernels_two, _ = timed(step_two, max(2, args.steps // 2), 1)
