@@ -109,9 +109,45 @@ class _LMHeadLoss(torch.autograd.Function):
         return (None if dh is None else dh.to(h.dtype), None if dW is None else dW.to(W.dtype), None)
 
 
-def lmhead_loss(hidden: torch.Tensor, W: torch.Tensor, weights: Dict[str, float], **kw) -> torch.Tensor:
-    """Mean streaming LM-head loss with autograd; gradients flow to hidden and W."""
+class _LMHeadLossTerminal(torch.autograd.Function):
+    """The mean loss of a graph that ends in it: the single call forms the
+    gradients of the mean with the forward, and backward scales them by the
+    upstream scalar (the gradient is linear in it)."""
+
+    @staticmethod
+    def forward(ctx, hidden, W, run: LossRun):
+        want_h, want_w = ctx.needs_input_grad[0], ctx.needs_input_grad[1]
+        ctx.dtypes = (hidden.dtype, W.dtype)
+        ctx.dh = ctx.dW = None
+        if want_h or want_w:
+            one = torch.ones(1, dtype=torch.float32, device=hidden.device)
+            ctx.dh, ctx.dW = run.forward_backward(grad_mean=one, want_dh=want_h, want_dW=want_w)
+        else:
+            run.forward()
+        return run.reduced[0].clone()
+
+    @staticmethod
+    def backward(ctx, g):
+        dh, dW = ctx.dh, ctx.dW
+        ctx.dh = ctx.dW = None
+        g = g.to(torch.float32)
+        th, tw = ctx.dtypes
+        return (None if dh is None else (dh * g).to(th),
+                None if dW is None else (dW * g).to(tw), None)
+
+
+def lmhead_loss(hidden: torch.Tensor, W: torch.Tensor, weights: Dict[str, float], *,
+                terminal: bool = False, **kw) -> torch.Tensor:
+    """Mean streaming LM-head loss with autograd; gradients flow to hidden and W.
+
+    terminal: the loss is the last node of the graph and backward will be called:
+    the forward then runs the single call (lmhead_loss_fwd_bwd), which forms the
+    gradients without recomputing any logits tile, and backward only scales them.
+    Otherwise the forward keeps per-row state and backward recomputes the tiles
+    (lmhead_loss_fwd, then lmhead_loss_bwd)."""
     run = LossRun(hidden.detach(), W.detach(), weights, **kw)
+    if terminal:
+        return _LMHeadLossTerminal.apply(hidden, W, run)
     return _LMHeadLoss.apply(hidden, W, run)
 
 

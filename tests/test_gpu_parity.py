@@ -262,6 +262,36 @@ def test_autograd_wrapper():
     assert rel_frob(W.grad.float().cpu().numpy(), rdW) <= GRAD_FROB
 
 
+def test_autograd_terminal_matches_two_calls():
+    """terminal=True runs the single call in the forward: the loss is bitwise the
+    two-call one, the gradients agree with it and with the oracle, and an
+    upstream scale other than one reaches both gradients."""
+    import lm_head_vocab_amd as L
+    p = synthetic.make_problem("lk_hybrid_bf16_8b", n_rows=300, hidden_dim=128, vocab=900)
+    dev = to_device(p)
+    kw = dict(labels=dev["labels"], mask=dev["mask"], target_hidden=dev["target_hidden"],
+              W_t=dev["W_t"], target_row=dev["target_row"])
+    grads = []
+    for terminal in (False, True):
+        h = dev["hidden"].clone().requires_grad_(True)
+        W = dev["W"].clone().requires_grad_(True)
+        loss = L.lmhead_loss(h, W, p.weights, terminal=terminal, **kw)
+        (2.5 * loss).backward()
+        grads.append((loss.item(), h.grad.float().cpu().numpy(), W.grad.float().cpu().numpy()))
+    (l0, h0, w0), (l1, h1, w1) = grads
+    assert l0 == l1
+    mean, _, _ = O.mean_loss(p)
+    rdh, rdW = O.backward(p)
+    assert abs(l1 - mean) <= 1e-3 * abs(mean)
+    # the two-call backward folds the 2.5 into dz before dz is rounded to bf16 for
+    # the contractions, the terminal one scales the fp32 result; both gradients are
+    # then rounded to bf16 (unit roundoff 2^-8 each): 2^-7 plus the dz rounding
+    assert rel_frob(h1, h0) <= 1e-2 and rel_frob(w1, w0) <= 1e-2
+    assert rel_frob(h1, 2.5 * rdh) <= GRAD_FROB and rel_frob(w1, 2.5 * rdW) <= GRAD_FROB
+    with torch.no_grad():   # no gradient wanted: the forward alone
+        assert L.lmhead_loss(dev["hidden"], dev["W"], p.weights, terminal=True, **kw).item() == l0
+
+
 # ---------------------------------------------------------------- single call
 @pytest.mark.parametrize("case", ["c1_full", "ce_ragged", "ce_chunked", "argmax_ce", "mix_ce",
                                   "divergence"])
