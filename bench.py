@@ -150,8 +150,8 @@ def main():
         run.backward(grad_mean=gmean, dhidden=dh, dW=dW, stream=stream)
         p0, s0 = run.problems[0], run.shards[0]
         v_shard = run.bounds[1]
-        chunk_rows, chunk_layout = L.binding.lmhead_loss_chunk(p0, run.workspace.numel(),
-                                                               L.binding.CALL_BWD)
+        chunk_rows, chunk_layout, dw_group = L.binding.lmhead_loss_chunk(
+            p0, run.workspace.numel(), L.binding.CALL_BWD)
         dh_part = torch.empty((N, H), dtype=torch.float32, device=dev)
         terms = torch.empty(L.binding.NUM_KINDS, N, dtype=torch.float32, device=dev)
 
@@ -168,7 +168,7 @@ def main():
     else:
         run = LossRun(h, W, prob.weights, max_chunk_rows=args.chunk, want_terms=False, **inputs)
         v_shard = V
-        chunk_rows, chunk_layout = run.chunk(L.binding.CALL_FWD_BWD)
+        chunk_rows, chunk_layout, dw_group = run.chunk(L.binding.CALL_FWD_BWD)
 
         def step_single():
             run.forward_backward(grad_mean=gmean, dhidden=dh, dW=dW, stream=stream)
@@ -257,6 +257,7 @@ def main():
         "data": f"synthetic (seeded; {prob.recipe})",
         "config": {"workload": args.workload, "tokens": N, "hidden": H, "vocab": V,
                    "loss": prob.weights, "chunk_rows": chunk_rows, "bwd_layout": chunk_layout,
+                   "dw_group": dw_group,
                    "call": "lmhead_loss_fwd_bwd" if G == 1 else
                    "lmhead_shard_pass1/merge1/pass2/merge2/bwd of shard 0",
                    "parallelism": "none (1 GPU)" if G == 1 else

@@ -110,7 +110,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     P = ctypes.POINTER(Problem)
     lib.lmhead_loss_workspace_size.argtypes = [P, i64, ctypes.POINTER(sz)]
     lib.lmhead_loss_workspace_size.restype = ctypes.c_int
-    lib.lmhead_loss_chunk.argtypes = [P, sz, i32, ctypes.POINTER(i64), ctypes.POINTER(i32)]
+    lib.lmhead_loss_chunk.argtypes = [P, sz, i32, ctypes.POINTER(i64), ctypes.POINTER(i32),
+                                      ctypes.POINTER(i32)]
     lib.lmhead_loss_chunk.restype = ctypes.c_int
     lib.specloss_saved_bytes.argtypes = [i64]
     lib.specloss_saved_bytes.restype = sz
@@ -240,12 +241,14 @@ LAYOUTS = ("copies", "no_weight_copy", "no_copies")
 
 
 def lmhead_loss_chunk(problem: Problem, ws_bytes: int, call: int = CALL_FWD_BWD):
-    """(rows per chunk, backward layout name) the call uses with ws_bytes of workspace."""
-    rows, lay = ctypes.c_int64(0), ctypes.c_int32(0)
+    """(rows per chunk, backward layout name, chunks per dW contraction) the
+    call uses with ws_bytes of workspace."""
+    rows, lay, group = ctypes.c_int64(0), ctypes.c_int32(0), ctypes.c_int32(0)
     _check(load_library().lmhead_loss_chunk(ctypes.byref(problem), ws_bytes, call,
-                                            ctypes.byref(rows), ctypes.byref(lay)),
+                                            ctypes.byref(rows), ctypes.byref(lay),
+                                            ctypes.byref(group)),
            "lmhead_loss_chunk")
-    return rows.value, LAYOUTS[lay.value]
+    return rows.value, LAYOUTS[lay.value], group.value
 
 
 def specloss_saved_bytes(n_rows: int) -> int:

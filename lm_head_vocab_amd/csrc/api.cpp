@@ -142,7 +142,11 @@ struct Layout {
   int32_t layout;   // BwdLayout
   int32_t dh_splits;  // split-K slices of the dh contraction (1: none)
   bool wt_copy;     // dh reads the copy W^T [H][Vp]
-  bool dw_copies;   // dW reads the copies h^T [H][Nc] and dz^T [Vp][Nc]
+  bool dw_copies;   // dW reads the copies h^T [H][ld_t] and dz^T [Vp][ld_t]
+  // chunks one dW contraction takes (copies only): chunk c writes its copies'
+  // columns [(c mod dw_group) Nc, + Nc); ld_t = dw_group Nc
+  int32_t dw_group;
+  int64_t ld_t;
   // head
   size_t terms, saved, seed, tstat, head_end;
   // rows share target rows (a row map onto fewer target rows than rows): the
@@ -230,7 +234,8 @@ int32_t dh_splits(int64_t Nc, int64_t H) {
 
 // fp32 inputs always take LAYOUT_COPIES (the transposing LDS load is bf16).
 Layout plan(const specloss_problem* p, const KindSet& k, int64_t Nc,
-            int32_t layout = LAYOUT_COPIES, bool fwd_raw = false, bool bwd_raw = false) {
+            int32_t layout = LAYOUT_COPIES, bool fwd_raw = false, bool bwd_raw = false,
+            int32_t dw_group = 1) {
   Layout L;
   L.N = p->n_rows;
   L.H = p->hidden;
@@ -242,6 +247,8 @@ Layout plan(const specloss_problem* p, const KindSet& k, int64_t Nc,
   L.layout = L.es == 4 ? LAYOUT_COPIES : layout;
   L.wt_copy = L.layout == LAYOUT_COPIES;
   L.dw_copies = L.layout != LAYOUT_NONE;
+  L.dw_group = L.dw_copies ? dw_group : 1;
+  L.ld_t = L.dw_group * Nc;
   size_t o = 0;
   auto take = [&](size_t bytes) {
     const size_t at = o;
@@ -272,9 +279,9 @@ Layout plan(const specloss_problem* p, const KindSet& k, int64_t Nc,
   L.fwd_end = o;
   o = L.head_end;
   L.wt = take(L.wt_copy ? (size_t)L.H * L.Vp * L.es : 0);
-  L.ht = take(L.dw_copies ? (size_t)L.H * Nc * L.es : 0);
+  L.ht = take(L.dw_copies ? (size_t)L.H * L.ld_t * L.es : 0);
   L.dz = take((size_t)Nc * L.Vp * L.es);
-  L.dzt = take(L.dw_copies ? (size_t)L.Vp * Nc * L.es : 0);
+  L.dzt = take(L.dw_copies ? (size_t)L.Vp * L.ld_t * L.es : 0);
   L.dh_splits = dh_splits(Nc, L.H);
   const size_t dhp_bytes = L.dh_splits > 1 ? (size_t)L.dh_splits * Nc * L.H * 4 : 0;
   L.dhp = take(dhp_bytes);
@@ -290,11 +297,11 @@ Layout plan(const specloss_problem* p, const KindSet& k, int64_t Nc,
   L.f_p2 = take(k.stage_div ? (size_t)kNumSums * tile_cols : 0);
   L.f_zy = take(2 * (size_t)Nc * 4);
   L.f_wt = take(L.wt_copy ? (size_t)L.H * L.Vp * L.es : 0);
-  L.f_ht = take(L.dw_copies ? (size_t)L.H * Nc * L.es : 0);
+  L.f_ht = take(L.dw_copies ? (size_t)L.H * L.ld_t * L.es : 0);
   L.f_dz = take((size_t)Nc * L.Vp * L.es);
   L.f_zr = take(k.stage_div ? (size_t)Nc * L.Vp * 4 : 0);
   L.f_ur = take(k.stage_div ? (size_t)L.Nu * L.Vp * 4 : 0);
-  L.f_dzt = take(L.dw_copies ? (size_t)L.Vp * Nc * L.es : 0);
+  L.f_dzt = take(L.dw_copies ? (size_t)L.Vp * L.ld_t * L.es : 0);
   L.f_rs = take(4 * (size_t)Nc * 4);
   L.f_dhp = take(dhp_bytes);
   L.fused_end = o;
@@ -319,10 +326,10 @@ size_t workspace_end(const Layout& L) {
 // tried from the top; a plan costs a few arithmetic operations.
 int64_t largest_chunk(const specloss_problem* p, const KindSet& k, size_t ws_bytes,
                       Region region, int32_t layout, int64_t top, bool strict = false,
-                      bool raw = false) {
+                      bool raw = false, int32_t dw_group = 1) {
   for (int64_t m = top / kChunkQuantum; m >= 1; --m) {
     const Layout L = plan(p, k, m * kChunkQuantum, layout, raw && region == REGION_FWD,
-                          raw && region == REGION_BWD);
+                          raw && region == REGION_BWD, dw_group);
     const size_t need = region_end(L, region);
     if (strict ? need < ws_bytes : need <= ws_bytes) return m * kChunkQuantum;
   }
@@ -344,26 +351,75 @@ int32_t forced_layout(const specloss_problem* p) {
 // larger chunk.  (The in-place operands run the contractions slower; below
 // about 1000 rows per chunk the fp32 read-modify-write of dW per chunk costs
 // more than that at the large shapes.)  flags force the layout.
+// Smallest chunk a layout is taken with (pick_chunk) and smallest chunk of a
+// dW group: min(N, 1024) rows.
+int64_t wanted_chunk(const specloss_problem* p) {
+  const int64_t top = round_up(p->n_rows, kChunkQuantum);
+  return top < 1024 ? top : 1024;
+}
+
+// Largest chunk of one layout and its dW group.  Each dW contraction reads and
+// writes the whole fp32 dW (2 V H 4 bytes) beside its 2 rows H V flops, so at
+// small chunks it is bound by that traffic.  With the copies, two chunks can
+// share one contraction (dw_group 2: their dz^T and h^T columns side by side,
+// K = 2 Nc).  The copies of two chunks take a smaller chunk, which costs the
+// other kernels some efficiency, so pairs are taken when
+//   - their chunk still has min(N, 1024) rows,
+//   - a pair is at most kDwGroupDepth rows deep (on MI355X the contraction ran
+//     at 1.32 PFLOP/s with K = 8192 and 1.26 with K = 16384 at H = 4096,
+//     V = 128256), and
+//   - they save at least two of dW's read-modify-writes per call (measured
+//     whole-call changes: one saved at N = 8192, H = 2048 lost 2.6 %; two at
+//     the three-head H = 16384 shape gained 3.4 %, four at N = 16384,
+//     H = 4096 with a target gained 4.6 %).
+constexpr int64_t kDwGroupDepth = 8192;
+
+bool take_dw_group(const specloss_problem* p, int64_t n1, int64_t n2) {
+  const int64_t N = p->n_rows;
+  if (n1 <= 0 || n1 >= N || n2 < wanted_chunk(p) || 2 * n2 > kDwGroupDepth) return false;
+  return cdiv(N, n1) - cdiv(cdiv(N, n2), 2) >= 2;
+}
+
+int64_t fit_chunk(const specloss_problem* p, const KindSet& k, size_t ws_bytes, Region region,
+                  int32_t layout, int64_t top, bool strict, bool raw, int32_t* dw_group) {
+  *dw_group = 1;
+  const int64_t n1 = largest_chunk(p, k, ws_bytes, region, layout, top, strict, raw, 1);
+  if (region == REGION_FWD || n1 <= 0 || n1 >= p->n_rows || !plan(p, k, n1, layout).dw_copies)
+    return n1;
+  const int64_t n2 = largest_chunk(p, k, ws_bytes, region, layout, top, strict, raw, 2);
+  if (take_dw_group(p, n1, n2)) {
+    *dw_group = 2;
+    return n2;
+  }
+  return n1;
+}
+
 int64_t pick_chunk(const specloss_problem* p, const KindSet& k, size_t ws_bytes, Region region,
-                   int32_t* layout = nullptr) {
+                   int32_t* layout = nullptr, int32_t* dw_group = nullptr) {
   const int64_t top = round_up(p->n_rows, kChunkQuantum);
   const int32_t forced = forced_layout(p);
+  int32_t g = 1;
+  int64_t best;
   if (forced >= 0) {
     if (layout) *layout = forced;
-    return largest_chunk(p, k, ws_bytes, region, forced, top);
-  }
-  int64_t best = largest_chunk(p, k, ws_bytes, region, LAYOUT_COPIES, top);
-  if (layout) *layout = LAYOUT_COPIES;
-  if (!layout || p->in_dtype != SPECLOSS_BF16) return best;
-  const int64_t want = top < 1024 ? top : 1024;
-  for (int32_t lay : {LAYOUT_DW_COPIES, LAYOUT_NONE}) {
-    if (best >= want) break;
-    const int64_t nc = largest_chunk(p, k, ws_bytes, region, lay, top);
-    if (nc > best) {
-      best = nc;
-      *layout = lay;
+    best = fit_chunk(p, k, ws_bytes, region, forced, top, false, false, &g);
+  } else {
+    best = fit_chunk(p, k, ws_bytes, region, LAYOUT_COPIES, top, false, false, &g);
+    if (layout) *layout = LAYOUT_COPIES;
+    if (layout && p->in_dtype == SPECLOSS_BF16) {
+      for (int32_t lay : {LAYOUT_DW_COPIES, LAYOUT_NONE}) {
+        if (best >= wanted_chunk(p)) break;
+        int32_t gl = 1;
+        const int64_t nc = fit_chunk(p, k, ws_bytes, region, lay, top, false, false, &gl);
+        if (nc > best) {
+          best = nc;
+          *layout = lay;
+          g = gl;
+        }
+      }
     }
   }
+  if (dw_group) *dw_group = g;
   return best;
 }
 
@@ -391,11 +447,11 @@ int64_t pick_fwd_chunk(const specloss_problem* p, const KindSet& k, size_t ws_by
 // 1024) rows in some layout (tried in pick_chunk's order); otherwise, and for
 // vocabulary shards, one dual recompute kernel forms dz from the tiles.
 int64_t pick_bwd_chunk(const specloss_problem* p, const KindSet& k, size_t ws_bytes,
-                       int32_t* layout, bool* raw, bool shard) {
+                       int32_t* layout, bool* raw, bool shard, int32_t* dw_group) {
   *raw = false;
   if (k.stage_div && !shard) {
     const int64_t top = round_up(p->n_rows, kChunkQuantum);
-    const int64_t want = top < 1024 ? top : 1024;
+    const int64_t want = wanted_chunk(p);
     const int32_t forced = forced_layout(p);
     int32_t lays[3] = {LAYOUT_COPIES, LAYOUT_DW_COPIES, LAYOUT_NONE};
     int n_lays = p->in_dtype == SPECLOSS_BF16 ? 3 : 1;
@@ -404,7 +460,7 @@ int64_t pick_bwd_chunk(const specloss_problem* p, const KindSet& k, size_t ws_by
       n_lays = 1;
     }
     for (int i = 0; i < n_lays; ++i) {
-      const int64_t nc = largest_chunk(p, k, ws_bytes, REGION_BWD, lays[i], top, false, true);
+      const int64_t nc = fit_chunk(p, k, ws_bytes, REGION_BWD, lays[i], top, false, true, dw_group);
       if (nc >= want) {
         *layout = lays[i];
         *raw = true;
@@ -412,7 +468,7 @@ int64_t pick_bwd_chunk(const specloss_problem* p, const KindSet& k, size_t ws_by
       }
     }
   }
-  return pick_chunk(p, k, ws_bytes, REGION_BWD, layout);
+  return pick_chunk(p, k, ws_bytes, REGION_BWD, layout, dw_group);
 }
 
 // The default chunk (workspace size for max_chunk_rows <= 0).  Blog, "Backward
@@ -424,7 +480,8 @@ int64_t pick_bwd_chunk(const specloss_problem* p, const KindSet& k, size_t ws_by
 // N x V x (input dtype size) bytes, the size of the full logits; layouts are
 // tried in the order of pick_chunk.  Problems too small for any chunk to fit
 // below that size (the W^T copy alone exceeds it) take 256-row chunks.
-int64_t default_chunk(const specloss_problem* p, const KindSet& k, int32_t* layout) {
+int64_t default_chunk(const specloss_problem* p, const KindSet& k, int32_t* layout,
+                      int32_t* dw_group) {
   const int64_t N = p->n_rows;
   const int64_t top = round_up(N, kChunkQuantum);
   int64_t cap = round_up(cdiv(N, 4), kChunkQuantum);
@@ -438,13 +495,26 @@ int64_t default_chunk(const specloss_problem* p, const KindSet& k, int32_t* layo
     lays[0] = forced;
     n_lays = 1;
   }
-  for (int i = 0; i < n_lays; ++i) {
-    int64_t nc = largest_chunk(p, k, limit, REGION_FWD, lays[i], cap, true);
-    const int64_t nb = largest_chunk(p, k, limit, REGION_BWD, lays[i], cap, true);
-    const int64_t nf = largest_chunk(p, k, limit, REGION_FUSED, lays[i], cap, true);
+  // the chunk every region fits with the copies of dw_group chunks
+  auto fits = [&](int32_t lay, int32_t g) {
+    int64_t nc = largest_chunk(p, k, limit, REGION_FWD, lay, cap, true);
+    const int64_t nb = largest_chunk(p, k, limit, REGION_BWD, lay, cap, true, false, g);
+    const int64_t nf = largest_chunk(p, k, limit, REGION_FUSED, lay, cap, true, false, g);
     nc = nb < nc ? nb : nc;
-    nc = nf < nc ? nf : nc;
+    return nf < nc ? nf : nc;
+  };
+  *dw_group = 1;
+  for (int i = 0; i < n_lays; ++i) {
+    int64_t nc = fits(lays[i], 1);
     if (nc <= 0 || (nc < want && i + 1 < n_lays)) continue;
+    // a dW group as in fit_chunk
+    if (nc < N && plan(p, k, nc, lays[i]).dw_copies) {
+      const int64_t n2 = fits(lays[i], 2);
+      if (take_dw_group(p, nc, n2)) {
+        nc = n2;
+        *dw_group = 2;
+      }
+    }
     // balance: the fewest chunks of that size, then equal chunks
     const int64_t nch = cdiv(N, nc);
     *layout = lays[i];
@@ -1128,7 +1198,7 @@ int ce_chunk_staged(const specloss_problem* p, const KindSet& k, const Layout& L
   ss.stage = e;
   ss.ld_stage = L.Vp;
   ss.stage_t = et;
-  ss.ld_stage_t = Nc;
+  ss.ld_stage_t = L.ld_t;
   ss.ref = ce_lab ? b.zy : b.zy + Nc;
   ss.seed = seed + r0;
   ss.y1 = ce_lab ? sv.y_label + r0 : nullptr;
@@ -1191,7 +1261,7 @@ int ce_chunk_staged(const specloss_problem* p, const KindSet& k, const Layout& L
   sf.stage = e;
   sf.ld_stage = L.Vp;
   sf.stage_t = et;
-  sf.ld_stage_t = Nc;
+  sf.ld_stage_t = L.ld_t;
   sf.rscale = rscale;
   TRACED(tr, K_STAGE_FIX, (double)rows * 32, launch_stage_fix(bf16, sf, stream));
   return SPECLOSS_OK;
@@ -1221,7 +1291,7 @@ int dz_from_raw(const specloss_problem* p, const Layout& L, const RawRows& rr, i
   dr.dz = dz;
   dr.ld_dz = L.Vp;
   dr.dzt = dzt;
-  dr.ld_dzt = L.Nc;
+  dr.ld_dzt = L.ld_t;
   dr.row_blocks = (int32_t)(cdiv(rows, 256) * 4);
   TRACED(tr, K_DZ_RAW, (double)dr.row_blocks * 64 * L.Vp * (8.0 + L.es * (dzt ? 2 : 1)),
          launch_dz_raw(p->in_dtype == SPECLOSS_BF16, dr, stream));
@@ -1342,6 +1412,26 @@ int contract_dW(const specloss_problem* p, const Layout& L, int64_t Nc, const vo
   return SPECLOSS_OK;
 }
 
+// The dW contraction after chunk `chunk` (rows [r0, r0 + rows)): once the
+// last chunk of its dW group, or of the problem, has written its copies'
+// columns; K spans the group's rows.  Groups accumulate in order, the first
+// overwrites dW unless accumulate_dW.
+int dw_after_chunk(const specloss_problem* p, const Layout& L, int chunk, int64_t r0,
+                   int64_t rows, const void* dz, const void* dzt, const void* ht,
+                   int accumulate_dW, float* dW, Tracer& tr, hipStream_t stream) {
+  const int32_t G = L.dw_group;
+  const int64_t slot = chunk % G;
+  if (slot != G - 1 && r0 + rows < L.N) return SPECLOSS_OK;
+  const int64_t g0 = r0 - slot * L.Nc;
+  return contract_dW(p, L, L.Nc, dz, dzt, ht, L.ld_t, g0, r0 + rows - g0,
+                     chunk >= G || accumulate_dW, dW, tr, stream);
+}
+
+// The copies' columns of chunk `chunk` (dw_group slots of Nc columns).
+void* slot_cols(void* base, const Layout& L, int chunk) {
+  return base ? static_cast<char*>(base) + (size_t)(chunk % L.dw_group) * L.Nc * L.es : nullptr;
+}
+
 int check_fwd_outputs(const float* loss, const float* term_loss, const float* lse_q,
                       const void* saved, const int64_t* counts, const float* reduced) {
   if (!loss || !counts) return SPECLOSS_E_INVAL;
@@ -1379,11 +1469,11 @@ int bwd_recompute(const specloss_problem* p, const KindSet& k, const float* grad
                   const float* grad_mean, const int64_t* counts, const void* saved,
                   void* workspace, size_t ws_bytes, void* dhidden, int32_t dh_dtype, float* dW,
                   int accumulate_dW, int64_t vocab_offset, bool shard, hipStream_t stream) {
-  int32_t layout = LAYOUT_COPIES;
+  int32_t layout = LAYOUT_COPIES, group = 1;
   bool raw = false;
-  const int64_t Nc = pick_bwd_chunk(p, k, ws_bytes, &layout, &raw, shard);
+  const int64_t Nc = pick_bwd_chunk(p, k, ws_bytes, &layout, &raw, shard, &group);
   if (Nc <= 0) return SPECLOSS_E_WORKSPACE;
-  const Layout L = plan(p, k, Nc, layout, false, raw);
+  const Layout L = plan(p, k, Nc, layout, false, raw, group);
   char* ws = static_cast<char*>(workspace);
   const bool bf16 = p->in_dtype == SPECLOSS_BF16;
   const int64_t N = L.N, H = L.H, V = L.V, Vp = L.Vp;
@@ -1401,26 +1491,28 @@ int bwd_recompute(const specloss_problem* p, const KindSet& k, const float* grad
 
   TRY(launch_seed_for(p, sv, grad_loss, grad_mean, counts, seed, tr, stream));
   if (dhidden && L.wt_copy)
-    TRACED(tr, K_TRANSPOSE_W, 2.0 * Vp * H * L.es, launch_transpose(bf16, p->W, V, H, wt, Vp, stream));
+    TRACED(tr, K_TRANSPOSE_W, 2.0 * Vp * H * L.es, launch_transpose(bf16, p->W, V, H, wt, Vp, Vp, stream));
 
   int chunk = 0;
   for (int64_t r0 = 0; r0 < N; r0 += Nc, ++chunk) {
     const int64_t rows = (N - r0) < Nc ? (N - r0) : Nc;
     const void* hc = offset_rows(p->hidden_states, r0, H, L.es);
+    void* htc = slot_cols(ht, L, chunk);
+    void* dztc = slot_cols(dzt, L, chunk);
     if (dW && L.dw_copies)
-      TRACED(tr, K_TRANSPOSE_H, 2.0 * Nc * H * L.es, launch_transpose(bf16, hc, rows, H, ht, Nc, stream));
+      TRACED(tr, K_TRANSPOSE_H, 2.0 * Nc * H * L.es,
+             launch_transpose(bf16, hc, rows, H, htc, Nc, L.ld_t, stream));
 
     if (raw) {
       RawRows rr{};
       TRY(raw_pass1(p, k, L, rb, r0, rows, reinterpret_cast<float*>(ws + L.b_zr),
                     reinterpret_cast<float*>(ws + L.b_ur), rr, carry, false, tr, stream));
-      TRY(dz_from_raw(p, L, rr, r0, rows, seed, sv, dz, dzt, tr, stream));
+      TRY(dz_from_raw(p, L, rr, r0, rows, seed, sv, dz, dztc, tr, stream));
       if (dhidden)
         TRY(contract_dh(p, L, Nc, dz, wt, r0, rows, dhidden, dh_dtype, tr, stream, nullptr,
                         reinterpret_cast<float*>(ws + L.dhp)));
       if (dW)
-        TRY(contract_dW(p, L, Nc, dz, dzt, ht, Nc, r0, rows, chunk > 0 || accumulate_dW, dW, tr,
-                        stream));
+        TRY(dw_after_chunk(p, L, chunk, r0, rows, dz, dzt, ht, accumulate_dW, dW, tr, stream));
       continue;
     }
     DzLaunch dl{};
@@ -1444,16 +1536,15 @@ int bwd_recompute(const specloss_problem* p, const KindSet& k, const float* grad
     memcpy(dl.w, p->weights, sizeof(dl.w));
     dl.dz = dz;
     dl.ld_dz = Vp;
-    dl.dzt = dzt;
-    dl.ld_dzt = Nc;
+    dl.dzt = dztc;
+    dl.ld_dzt = L.ld_t;
     dl.vocab_offset = (int32_t)vocab_offset;
     TRACED(tr, K_DZ, (k.dual_bwd ? 4.0 : 2.0) * rows * H * V, launch_dz(bf16, k.dual_bwd, dl, stream));
     if (dhidden)
       TRY(contract_dh(p, L, Nc, dz, wt, r0, rows, dhidden, dh_dtype, tr, stream, nullptr,
                       reinterpret_cast<float*>(ws + L.dhp)));
     if (dW)
-      TRY(contract_dW(p, L, Nc, dz, dzt, ht, Nc, r0, rows, chunk > 0 || accumulate_dW, dW, tr,
-                      stream));
+      TRY(dw_after_chunk(p, L, chunk, r0, rows, dz, dzt, ht, accumulate_dW, dW, tr, stream));
   }
   return SPECLOSS_OK;
 }
@@ -1507,39 +1598,41 @@ int lmhead_loss_workspace_size(const specloss_problem* p, int64_t max_chunk_rows
   const int rc = check_problem(p, &k);
   if (rc) return rc;
   if (!bytes) return SPECLOSS_E_INVAL;
-  int32_t layout = LAYOUT_COPIES;
+  int32_t layout = LAYOUT_COPIES, group = 1;
   int64_t nc;
   if (max_chunk_rows <= 0) {
-    nc = default_chunk(p, k, &layout);
+    nc = default_chunk(p, k, &layout, &group);
   } else {
     const int32_t forced = forced_layout(p);
     layout = forced >= 0 ? forced : LAYOUT_COPIES;
     nc = round_up(max_chunk_rows, kChunkQuantum);
     nc = nc < round_up(p->n_rows, kChunkQuantum) ? nc : round_up(p->n_rows, kChunkQuantum);
   }
-  *bytes = workspace_end(plan(p, k, nc, layout));
+  *bytes = workspace_end(plan(p, k, nc, layout, false, false, group));
   return SPECLOSS_OK;
 }
 
 int lmhead_loss_chunk(const specloss_problem* p, size_t ws_bytes, int32_t call,
-                      int64_t* chunk_rows, int32_t* layout) {
+                      int64_t* chunk_rows, int32_t* layout, int32_t* dw_group) {
   KindSet k;
   TRY(check_problem(p, &k));
   if (!chunk_rows || !layout || call < 0 || call > 2) return SPECLOSS_E_INVAL;
-  int32_t lay = LAYOUT_COPIES;
+  int32_t lay = LAYOUT_COPIES, group = 1;
   int64_t nc;
   if (call == 0) {
     bool raw;
     nc = pick_fwd_chunk(p, k, ws_bytes, &raw);
   } else if (call == 1) {
     bool raw;
-    nc = pick_bwd_chunk(p, k, ws_bytes, &lay, &raw, false);
+    nc = pick_bwd_chunk(p, k, ws_bytes, &lay, &raw, false, &group);
   } else {
-    nc = pick_chunk(p, k, ws_bytes, REGION_FUSED, &lay);
+    nc = pick_chunk(p, k, ws_bytes, REGION_FUSED, &lay, &group);
   }
   if (nc <= 0) return SPECLOSS_E_WORKSPACE;
+  const Layout L = plan(p, k, nc, lay, false, false, group);
   *chunk_rows = nc;
-  *layout = plan(p, k, nc, lay).layout;
+  *layout = L.layout;
+  if (dw_group) *dw_group = L.dw_group;
   return SPECLOSS_OK;
 }
 
@@ -1623,10 +1716,10 @@ int lmhead_loss_fwd_bwd(const specloss_problem* p, void* workspace, size_t ws_by
   // (ce_chunk_staged); with divergences, pass 1 keeps both raw logit rows
   // (div_chunk_raw), from which the sums and then the logit gradient are
   // formed.  No logits tile is computed twice.
-  int32_t layout = LAYOUT_COPIES;
-  const int64_t Nc = pick_chunk(p, k, ws_bytes, REGION_FUSED, &layout);
+  int32_t layout = LAYOUT_COPIES, group = 1;
+  const int64_t Nc = pick_chunk(p, k, ws_bytes, REGION_FUSED, &layout, &group);
   if (Nc <= 0) return SPECLOSS_E_WORKSPACE;
-  const Layout L = plan(p, k, Nc, layout);
+  const Layout L = plan(p, k, Nc, layout, false, false, group);
   char* ws = static_cast<char*>(workspace);
   const bool bf16 = p->in_dtype == SPECLOSS_BF16;
   const int64_t N = L.N, H = L.H, V = L.V, Vp = L.Vp;
@@ -1650,7 +1743,7 @@ int lmhead_loss_fwd_bwd(const specloss_problem* p, void* workspace, size_t ws_by
   if (L.shared_target && !(k.stage_div && heads_pass2(p, k)))
     TRY(target_prepass(p, L, b, tr, stream));
   if (dhidden && L.wt_copy)
-    TRACED(tr, K_TRANSPOSE_W, 2.0 * Vp * H * L.es, launch_transpose(bf16, p->W, V, H, wt, Vp, stream));
+    TRACED(tr, K_TRANSPOSE_W, 2.0 * Vp * H * L.es, launch_transpose(bf16, p->W, V, H, wt, Vp, Vp, stream));
   // label / argmax cross-entropies with the dW copies: pass 1 stages the
   // logit gradient in both layouts up to a per-row factor (ce_chunk_staged)
   // (not when w_lab + w_arg = 0: the row factor would vanish)
@@ -1661,25 +1754,26 @@ int lmhead_loss_fwd_bwd(const specloss_problem* p, void* workspace, size_t ws_by
   int chunk = 0;
   for (int64_t r0 = 0; r0 < N; r0 += Nc, ++chunk) {
     const int64_t rows = (N - r0) < Nc ? (N - r0) : Nc;
+    void* htc = slot_cols(ht, L, chunk);
+    void* dztc = slot_cols(dzt, L, chunk);
     if (staged_ce) {
-      TRY(ce_chunk_staged(p, k, L, b, sv, loss, terms, seed, r0, rows, dz, dW ? dzt : nullptr,
+      TRY(ce_chunk_staged(p, k, L, b, sv, loss, terms, seed, r0, rows, dz, dW ? dztc : nullptr,
                           rscale, tr, stream));
       const void* hc = offset_rows(p->hidden_states, r0, H, L.es);
       if (dW)
         TRACED(tr, K_TRANSPOSE_H, 2.0 * Nc * H * L.es,
-               launch_transpose(bf16, hc, rows, H, ht, Nc, stream, rscale));
+               launch_transpose(bf16, hc, rows, H, htc, Nc, L.ld_t, stream, rscale));
       if (dhidden)
         TRY(contract_dh(p, L, Nc, dz, wt, r0, rows, dhidden, dh_dtype, tr, stream, rscale,
                         reinterpret_cast<float*>(ws + L.f_dhp)));
       if (dW)
-        TRY(contract_dW(p, L, Nc, dz, dzt, ht, Nc, r0, rows, chunk > 0 || accumulate_dW, dW, tr,
-                        stream));
+        TRY(dw_after_chunk(p, L, chunk, r0, rows, dz, dzt, ht, accumulate_dW, dW, tr, stream));
       continue;
     }
     if (k.stage_div) {
       RawRows rr{};
       TRY(div_chunk_raw(p, k, L, b, sv, loss, terms, r0, rows, zr, ur, rr, carry, tr, stream));
-      TRY(dz_from_raw(p, L, rr, r0, rows, seed, sv, dz, dzt, tr, stream));
+      TRY(dz_from_raw(p, L, rr, r0, rows, seed, sv, dz, dztc, tr, stream));
     } else {
       TRY(fwd_chunk(p, k, L, b, sv, loss, terms, r0, rows, dz, tr, stream));
       DzStageLaunch ds{};
@@ -1695,21 +1789,21 @@ int lmhead_loss_fwd_bwd(const specloss_problem* p, void* workspace, size_t ws_by
       ds.w_arg = p->weights[SPECLOSS_CE_ARGMAX_P];
       ds.dz = dz;
       ds.ld_dz = Vp;
-      ds.dzt = dzt;
-      ds.ld_dzt = Nc;
+      ds.dzt = dztc;
+      ds.ld_dzt = L.ld_t;
       ds.row_blocks = (int32_t)(cdiv(rows, 256) * 4);
       TRACED(tr, K_DZ_STAGE, (double)ds.row_blocks * 64 * Vp * L.es * (2 + (dzt ? 1 : 0)),
              launch_dz_stage(bf16, ds, stream));
     }
     const void* hc = offset_rows(p->hidden_states, r0, H, L.es);
     if (dW && L.dw_copies)
-      TRACED(tr, K_TRANSPOSE_H, 2.0 * Nc * H * L.es, launch_transpose(bf16, hc, rows, H, ht, Nc, stream));
+      TRACED(tr, K_TRANSPOSE_H, 2.0 * Nc * H * L.es,
+             launch_transpose(bf16, hc, rows, H, htc, Nc, L.ld_t, stream));
     if (dhidden)
       TRY(contract_dh(p, L, Nc, dz, wt, r0, rows, dhidden, dh_dtype, tr, stream, nullptr,
                       reinterpret_cast<float*>(ws + L.f_dhp)));
     if (dW)
-      TRY(contract_dW(p, L, Nc, dz, dzt, ht, Nc, r0, rows, chunk > 0 || accumulate_dW, dW, tr,
-                      stream));
+      TRY(dw_after_chunk(p, L, chunk, r0, rows, dz, dzt, ht, accumulate_dW, dW, tr, stream));
   }
   if (reduced) TRY(launch_reduce_for(p, k, loss, terms, counts, reduced, tr, stream));
   if (lse_q)

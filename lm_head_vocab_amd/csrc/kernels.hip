@@ -2118,10 +2118,11 @@ hipError_t launch_seed(const SeedLaunch& a, hipStream_t s) {
 }
 
 hipError_t launch_transpose(bool bf16, const void* in, int64_t rows, int64_t cols, void* out,
-                            int64_t ld_out, hipStream_t s, const float* rscale) {
-  // whole 64 x 64 tiles on the column side and 16-byte aligned rows
-  if (cols % 64 != 0 || ld_out % 64 != 0 || rows > ld_out) return hipErrorInvalidValue;
-  const dim3 grid((unsigned)(ld_out / 64), (unsigned)(cols / 64)), block(256);
+                            int64_t width, int64_t ld_out, hipStream_t s, const float* rscale) {
+  // whole 64 x 64 tiles on both sides and 16-byte aligned rows
+  if (cols % 64 != 0 || width % 64 != 0 || ld_out % 64 != 0 || rows > width || width > ld_out)
+    return hipErrorInvalidValue;
+  const dim3 grid((unsigned)(width / 64), (unsigned)(cols / 64)), block(256);
   if (bf16)
     hipLaunchKernelGGL(k_transpose<bf16_bits>, grid, block, 0, s,
                        static_cast<const bf16_bits*>(in), rows, cols, static_cast<bf16_bits*>(out),

@@ -419,10 +419,11 @@ struct SeedLaunch {
 };
 hipError_t launch_seed(const SeedLaunch& a, hipStream_t s);
 
-// out[j][c] = c < rows ? in[c][j] : 0 for j < cols, c < ld_out
+// out[j][c] = c < rows ? in[c][j] : 0 for j < cols, c < width (row stride ld_out)
 // rscale (optional, per source row): out = rscale[row] * in, rounded to the type
 hipError_t launch_transpose(bool bf16, const void* in, int64_t rows, int64_t cols, void* out,
-                            int64_t ld_out, hipStream_t s, const float* rscale = nullptr);
+                            int64_t width, int64_t ld_out, hipStream_t s,
+                            const float* rscale = nullptr);
 
 struct AlignLaunch {
   int64_t seq_len, batch;

@@ -78,7 +78,8 @@ class LossRun:
         return self.workspace.numel()
 
     def chunk(self, call: int = B.CALL_FWD_BWD):
-        """(rows per chunk, backward layout) the given call uses with this workspace."""
+        """(rows per chunk, backward layout, chunks per dW contraction) the given
+        call uses with this workspace."""
         return B.lmhead_loss_chunk(self.problem, self.workspace_bytes, call)
 
     def saved_field(self, i: int, dtype=torch.float32) -> torch.Tensor:

@@ -682,7 +682,7 @@ def test_backward_without_transposed_copies(case):
             hi = mid
         else:
             lo = mid + 1
-    assert L.binding.lmhead_loss_chunk(probe.problem, lo, call) == (256, "no_copies")
+    assert L.binding.lmhead_loss_chunk(probe.problem, lo, call) == (256, "no_copies", 1)
     if not single:
         assert L.binding.lmhead_loss_chunk(probe.problem, lo, L.binding.CALL_FWD)[0] >= 256
     del probe
@@ -859,3 +859,50 @@ def test_jsd_with_underflowing_probabilities(single):
     out = full_parity(p, max_chunk_rows=256, tag=f"jsd-underflow-{single}", single_call=single)
     assert np.all(np.isfinite(out["loss"])) and np.all(np.isfinite(out["dh"]))
     assert np.all(np.isfinite(out["dW"]))
+
+
+# ---------------------------------------------------------------- dW groups
+def _dw_group_workspace(prob, call, flags):
+    """A workspace with which `call` contracts two chunks per dW launch over an
+    odd number (at least three) of chunks: the last group is one ragged chunk."""
+    dev = to_device(prob)
+    probe = make_run(prob, dev, max_chunk_rows=256, flags=flags)
+    for rows in range(1024, prob.n_rows + 256, 256):
+        ws = L.binding.lmhead_loss_workspace_size(probe.problem, rows)
+        nc, _, group = L.binding.lmhead_loss_chunk(probe.problem, ws, call)
+        chunks = -(-prob.n_rows // nc)
+        if group == 2 and chunks >= 3 and chunks % 2 == 1 and prob.n_rows % nc:
+            return ws, nc
+    raise AssertionError("no workspace gives a dW group")
+
+
+@pytest.mark.parametrize("case", ["ce_single", "ce_two", "ce32_two", "lk_single", "lk_two",
+                                  "kl_two", "heads_single"])
+def test_dw_group_matches_oracle(case):
+    """Two chunks per dW contraction (each writes its half of dz^T and h^T
+    copies two chunks wide): parity with the oracle, and one dW launch per
+    group in the trace.  The pairs must save two contractions, hence seven
+    or more chunks (eleven in fp32, whose copies take more of the space)."""
+    kind, calls = case.split("_")
+    single = calls == "single"
+    flags = 0
+    if kind in ("ce", "ce32"):
+        p = synthetic.make_problem("ce_bf16_1b", n_rows=11000 if kind == "ce32" else 7000,
+                                   hidden_dim=128, vocab=700)
+        if kind == "ce32":
+            p.dtype = "f32"
+            for f in ("hidden", "W"):
+                setattr(p, f, synthetic.bf16_bits_to_f32(getattr(p, f)).copy())
+    elif kind == "heads":
+        p = synthetic.make_problem("multihead_bf16_405b", seq_len=2334, hidden_dim=128, vocab=700)
+        flags = L.binding.FLAG_NO_WEIGHT_COPY
+    else:
+        w = {"lk": {"lk_hybrid": 1.0}, "kl": {"kl_div": 1.0}}[kind]
+        p = synthetic.make_problem("lk_hybrid_bf16_8b", n_rows=7000, hidden_dim=128, vocab=700,
+                                   weights=w)
+    call = L.binding.CALL_FWD_BWD if single else L.binding.CALL_BWD
+    ws, nc = _dw_group_workspace(p, call, flags)
+    out = full_parity(p, workspace_bytes=ws, single_call=single, flags=flags,
+                      tag=f"dw-group-{case}", expect_kernels=(("gemm_dW",), ()))
+    n_dw = sum(1 for name, _, _ in out["trace"] if name == "gemm_dW")
+    assert n_dw == -(-(-(-p.n_rows // nc)) // 2), (n_dw, nc)

@@ -316,19 +316,20 @@ def _shape(name):
     return p
 
 
-def _chunk(lib, p, ws, call):
-    rows, lay = ctypes.c_int64(), ctypes.c_int32()
-    rc = lib.lmhead_loss_chunk(ctypes.byref(p), ws, call, ctypes.byref(rows), ctypes.byref(lay))
-    return rc, rows.value, B.LAYOUTS[lay.value]
+def _chunk(lib, p, ws, call, group=False):
+    rows, lay, g = ctypes.c_int64(), ctypes.c_int32(), ctypes.c_int32()
+    rc = lib.lmhead_loss_chunk(ctypes.byref(p), ws, call, ctypes.byref(rows), ctypes.byref(lay),
+                               ctypes.byref(g))
+    return (rc, rows.value, B.LAYOUTS[lay.value]) + ((g.value,) if group else ())
 
 
-@pytest.mark.parametrize("name,chunk,layout", [
-    ("ce_bf16_1b", 2048, "copies"),
-    ("ce_bf16_8b", 8192, "copies"),
-    ("lk_hybrid_bf16_8b", 1792, "copies"),
-    ("multihead_bf16_405b", 2048, "no_weight_copy"),
+@pytest.mark.parametrize("name,chunk,layout,group", [
+    ("ce_bf16_1b", 2048, "copies", 1),
+    ("ce_bf16_8b", 8192, "copies", 1),
+    ("lk_hybrid_bf16_8b", 1536, "copies", 2),
+    ("multihead_bf16_405b", 1536, "no_weight_copy", 2),
 ])
-def test_default_chunk_streams_below_the_logits_size(lib, name, chunk, layout):
+def test_default_chunk_streams_below_the_logits_size(lib, name, chunk, layout, group):
     """Blog, "Backward pass" / "Choosing the chunk size": the default workspace
     streams the token set in chunks well below the token count, and the whole
     workspace stays below the size of the [N, V] logits in the input dtype."""
@@ -337,7 +338,7 @@ def test_default_chunk_streams_below_the_logits_size(lib, name, chunk, layout):
     assert rc == 0
     limit = M.logits_sized_limit_bytes(p.n_rows, p.vocab)
     assert ws < limit, (ws / 2**30, limit / 2**30)
-    assert _chunk(lib, p, ws, B.CALL_FWD_BWD) == (0, chunk, layout)
+    assert _chunk(lib, p, ws, B.CALL_FWD_BWD, group=True) == (0, chunk, layout, group)
     assert chunk <= -(-p.n_rows // 4 // 256) * 256
     rc, rows_bwd, _ = _chunk(lib, p, ws, B.CALL_BWD)
     assert rc == 0 and 0 < rows_bwd < p.n_rows
@@ -356,8 +357,9 @@ def test_chunk_query_validation(lib):
     p = _shape("ce_bf16_8b")
     rows, lay = ctypes.c_int64(), ctypes.c_int32()
     assert lib.lmhead_loss_chunk(ctypes.byref(p), 1 << 40, 3, ctypes.byref(rows),
-                                 ctypes.byref(lay)) == E_INVAL
-    assert lib.lmhead_loss_chunk(ctypes.byref(p), 1 << 40, 0, None, ctypes.byref(lay)) == E_INVAL
+                                 ctypes.byref(lay), None) == E_INVAL
+    assert lib.lmhead_loss_chunk(ctypes.byref(p), 1 << 40, 0, None, ctypes.byref(lay),
+                                 None) == E_INVAL
     assert _chunk(lib, p, 1000, B.CALL_BWD)[0] == E_WS
     # flags force the layout
     p.flags = B.FLAG_NO_COPIES
@@ -392,7 +394,8 @@ def test_size_limits(lib):
     p = _problem(N=big, V=128256, H=4096)
     rc, ws = _ws(lib, p)
     rows, lay = ctypes.c_int64(), ctypes.c_int32()
-    assert lib.lmhead_loss_chunk(ctypes.byref(p), ws, 2, ctypes.byref(rows), ctypes.byref(lay)) == 0
+    assert lib.lmhead_loss_chunk(ctypes.byref(p), ws, 2, ctypes.byref(rows), ctypes.byref(lay),
+                                 None) == 0
     assert 0 < rows.value <= 8192
 
 
@@ -400,9 +403,10 @@ def test_chunk_search_takes_the_largest_fitting_chunk(lib):
     """The workspace a chunk needs is not monotonic in the chunk: at H = 16384
     a 1792-row chunk gives the dh contraction 7 x 64 tiles and four split-K
     slices of fp32 partials, more than a 2048-row chunk (8 x 64 tiles, no
-    split) needs.  A workspace sized for 2048 rows must give 2048 rows."""
+    split) needs.  A workspace sized for 2048 rows must give 2048 rows (without
+    copies, so that no dW group is an option)."""
     p = _shape("multihead_bf16_405b")
-    p.flags = B.FLAG_NO_WEIGHT_COPY
+    p.flags = B.FLAG_NO_COPIES
     sizes = {}
     for rows in (1792, 2048):
         out = ctypes.c_size_t()
@@ -410,4 +414,4 @@ def test_chunk_search_takes_the_largest_fitting_chunk(lib):
         sizes[rows] = out.value
     assert sizes[1792] > sizes[2048]
     for call in (B.CALL_BWD, B.CALL_FWD_BWD):
-        assert _chunk(lib, p, sizes[2048], call) == (0, 2048, "no_weight_copy")
+        assert _chunk(lib, p, sizes[2048], call, group=True) == (0, 2048, "no_copies", 1)
