@@ -906,3 +906,11 @@ def test_dw_group_matches_oracle(case):
                       tag=f"dw-group-{case}", expect_kernels=(("gemm_dW",), ()))
     n_dw = sum(1 for name, _, _ in out["trace"] if name == "gemm_dW")
     assert n_dw == -(-(-(-p.n_rows // nc)) // 2), (n_dw, nc)
+    # accumulate_dW adds every group onto the caller's dW
+    run = out["run"]
+    gm = torch.ones(1, dtype=torch.float32, device="cuda")
+    dW = torch.from_numpy(out["dW"]).cuda()
+    call = run.forward_backward if single else run.backward
+    call(grad_mean=gm, dW=dW, accumulate_dW=True, want_dh=False)
+    torch.cuda.synchronize()
+    assert rel_frob(dW.cpu().numpy(), 2.0 * out["dW"]) <= 1e-5

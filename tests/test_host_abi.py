@@ -340,8 +340,9 @@ def test_default_chunk_streams_below_the_logits_size(lib, name, chunk, layout, g
     assert ws < limit, (ws / 2**30, limit / 2**30)
     assert _chunk(lib, p, ws, B.CALL_FWD_BWD, group=True) == (0, chunk, layout, group)
     assert chunk <= -(-p.n_rows // 4 // 256) * 256
-    rc, rows_bwd, _ = _chunk(lib, p, ws, B.CALL_BWD)
-    assert rc == 0 and 0 < rows_bwd < p.n_rows
+    rc, rows_bwd, _, group_bwd = _chunk(lib, p, ws, B.CALL_BWD, group=True)
+    assert rc == 0 and 0 < rows_bwd < p.n_rows and group_bwd == group
+    assert _chunk(lib, p, ws, B.CALL_FWD, group=True)[3] == 1  # no dW in the forward
 
 
 def test_default_chunk_of_a_tiny_problem(lib):
