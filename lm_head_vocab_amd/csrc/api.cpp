@@ -345,12 +345,6 @@ int32_t forced_layout(const specloss_problem* p) {
   }
 }
 
-// Chunk for a region and the backward layout.  With every copy when the
-// workspace holds them at a chunk of at least min(N, 1024) rows; otherwise
-// (bf16) without the W^T copy, then without any copy, whichever allows a
-// larger chunk.  (The in-place operands run the contractions slower; below
-// about 1000 rows per chunk the fp32 read-modify-write of dW per chunk costs
-// more than that at the large shapes.)  flags force the layout.
 // Smallest chunk a layout is taken with (pick_chunk) and smallest chunk of a
 // dW group: min(N, 1024) rows.
 int64_t wanted_chunk(const specloss_problem* p) {
@@ -394,6 +388,13 @@ int64_t fit_chunk(const specloss_problem* p, const KindSet& k, size_t ws_bytes, 
   return n1;
 }
 
+// Chunk for a region and the backward layout.  With every copy when the
+// workspace holds them at a chunk of at least min(N, 1024) rows; otherwise
+// (bf16) without the W^T copy, then without any copy, whichever allows a
+// larger chunk.  (The in-place operands run the contractions slower; below
+// about 1000 rows per chunk the fp32 read-modify-write of dW per chunk costs
+// more than that at the large shapes.)  flags force the layout.  Each layout's chunk comes with
+// its dW group (fit_chunk).
 int64_t pick_chunk(const specloss_problem* p, const KindSet& k, size_t ws_bytes, Region region,
                    int32_t* layout = nullptr, int32_t* dw_group = nullptr) {
   const int64_t top = round_up(p->n_rows, kChunkQuantum);
