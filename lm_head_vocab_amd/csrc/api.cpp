@@ -18,6 +18,8 @@
 //   k_gemm dh = dz W^T^T  and  k_gemm dW (+)= dz^T h, chunks in order.
 // The single call (lmhead_loss_fwd_bwd) forms dz from what its forward kept:
 // the staged exp(z - label logit) of the cross-entropies, or the raw rows.
+// With both gradients the cross-entropies' pass 1 stages dz only, and the dh
+// contraction writes dz^T from the dz slabs it streams through LDS.
 #include <math.h>
 #include <string.h>
 
@@ -1335,7 +1337,7 @@ int launch_seed_for(const specloss_problem* p, const SavedView& sv, const float*
 int contract_dh(const specloss_problem* p, const Layout& L, int64_t Nc, const void* dz,
                 const void* wt, int64_t r0, int64_t rows, void* dhidden, int32_t dh_dtype,
                 Tracer& tr, hipStream_t stream, const float* rscale = nullptr,
-                float* dhp = nullptr) {
+                float* dhp = nullptr, void* dzt = nullptr, int64_t ld_dzt = 0) {
   const bool bf16 = p->in_dtype == SPECLOSS_BF16;
   const int64_t H = L.H, V = L.V, Vp = L.Vp;
   const size_t dh_es = dh_dtype == SPECLOSS_BF16 ? 2 : 4;
@@ -1361,6 +1363,8 @@ int contract_dh(const specloss_problem* p, const Layout& L, int64_t Nc, const vo
   g.out_bf16 = dh_dtype == SPECLOSS_BF16;
   g.role = 0;
   g.rscale = rscale;
+  g.at_out = dzt;
+  g.ld_at = ld_dzt;
   g.splits = 1;
   if (L.dh_splits > 1 && dhp) {
     // slices of K, fp32 partials in the workspace, added in slice order
@@ -1758,15 +1762,19 @@ int lmhead_loss_fwd_bwd(const specloss_problem* p, void* workspace, size_t ws_by
     void* htc = slot_cols(ht, L, chunk);
     void* dztc = slot_cols(dzt, L, chunk);
     if (staged_ce) {
-      TRY(ce_chunk_staged(p, k, L, b, sv, loss, terms, seed, r0, rows, dz, dW ? dztc : nullptr,
-                          rscale, tr, stream));
+      // with both gradients (bf16) the dh contraction writes dz^T from its
+      // slabs of dz; otherwise pass 1 stores it
+      const bool dzt_from_dh = dW && dhidden && bf16;
+      TRY(ce_chunk_staged(p, k, L, b, sv, loss, terms, seed, r0, rows, dz,
+                          dW && !dzt_from_dh ? dztc : nullptr, rscale, tr, stream));
       const void* hc = offset_rows(p->hidden_states, r0, H, L.es);
       if (dW)
         TRACED(tr, K_TRANSPOSE_H, 2.0 * Nc * H * L.es,
                launch_transpose(bf16, hc, rows, H, htc, Nc, L.ld_t, stream, rscale));
       if (dhidden)
         TRY(contract_dh(p, L, Nc, dz, wt, r0, rows, dhidden, dh_dtype, tr, stream, rscale,
-                        reinterpret_cast<float*>(ws + L.f_dhp)));
+                        reinterpret_cast<float*>(ws + L.f_dhp), dzt_from_dh ? dztc : nullptr,
+                        L.ld_t));
       if (dW)
         TRY(dw_after_chunk(p, L, chunk, r0, rows, dz, dzt, ht, accumulate_dW, dW, tr, stream));
       continue;

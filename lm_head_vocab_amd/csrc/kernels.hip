@@ -1253,6 +1253,11 @@ __global__ __launch_bounds__(128 * WNW, 1) void k_dz(DzLaunch a) {
 // as an MN-major B (its rows are k), dW reads dz and the hidden chunk as
 // MN-major A and B.
 //
+// DUMP (dh, bf16): the contraction also writes A's transpose (dz^T, from dz)
+// as it streams A's slabs through LDS; each workgroup writes the slabs whose
+// index equals its tile column modulo the tile columns, so every slab of
+// every row tile goes out once (tile_gemm.hpp, SlabDump).
+//
 // Epilogue: the tile goes out in two halves of 128 rows.  The two waves that
 // own a half write their accumulators into LDS (rows padded to 1040 bytes so
 // the four row groups of a store land in different banks); then all threads
@@ -1264,7 +1269,7 @@ __global__ __launch_bounds__(128 * WNW, 1) void k_dz(DzLaunch a) {
 constexpr int kHalfRows = 128;
 constexpr int kEpiStride = 256 * 4 + 16;  // bytes per staged row
 
-template <typename T, typename OutT, int ROLE, bool LEAN, int WNW>
+template <typename T, typename OutT, int ROLE, bool LEAN, int WNW, bool DUMP = false>
 __global__ __launch_bounds__(128 * WNW, 1) void k_gemm(GemmLaunch a) {
   using Cfg = TileCfg<T, 256, 256, 1, WNW>;
   constexpr bool kA_MN = LEAN && ROLE == 1;
@@ -1300,7 +1305,21 @@ __global__ __launch_bounds__(128 * WNW, 1) void k_gemm(GemmLaunch a) {
   if (a.splits > 1 && k_len > a.k_split) k_len = a.k_split;
   f32x4_t acc[Cfg::FM][Cfg::FN];
   zero_acc<Cfg>(acc);
-  tile_mainloop<T, Cfg, kA_MN, kB_MN>(acc, opA, tm * Cfg::BM, opB, tn * Cfg::BN, k_len, smem);
+  if constexpr (DUMP) {
+    static_assert(ROLE == 0 && !kA_MN && sizeof(T) == 2, "A's transpose: dh, bf16, K-major A");
+    SlabDump D;
+    D.out = static_cast<bf16_bits*>(a.at_out);
+    D.ld = a.ld_at;
+    D.col0 = tm * Cfg::BM;
+    D.n_valid = a.m_valid - tm * Cfg::BM;
+    D.every = a.tiles_n;
+    D.phase = tn;
+    D.slab0 = split * (a.k_split / Cfg::BK);
+    tile_mainloop<T, Cfg, kA_MN, kB_MN, true>(acc, opA, tm * Cfg::BM, opB, tn * Cfg::BN, k_len,
+                                              smem, &D);
+  } else {
+    tile_mainloop<T, Cfg, kA_MN, kB_MN>(acc, opA, tm * Cfg::BM, opB, tn * Cfg::BN, k_len, smem);
+  }
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / Cfg::WNW, wn = wave % Cfg::WNW;
   constexpr int kPieces = kHalfRows * 64;              // 16-byte pieces (4 values) per half
@@ -2039,6 +2058,19 @@ template <int ROLE>
 static void launch_gemm_role(bool bf16, const GemmLaunch& a, hipStream_t s) {
   constexpr int W = kGemmWNW;
   const dim3 grid(grid_for_tiles(a.tiles_m * a.splits * a.tiles_n)), block(128 * W);
+  if constexpr (ROLE == 0) {
+    if (bf16 && a.at_out) {
+      static_assert(kGemmWNW == 4 && kLeanWNW == 4, "A's transpose needs eight waves");
+      if (a.lean) {
+        if (a.out_bf16) hipLaunchKernelGGL((k_gemm<bf16_bits, bf16_bits, 0, true, 4, true>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((k_gemm<bf16_bits, float, 0, true, 4, true>), grid, block, 0, s, a);
+      } else {
+        if (a.out_bf16) hipLaunchKernelGGL((k_gemm<bf16_bits, bf16_bits, 0, false, 4, true>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((k_gemm<bf16_bits, float, 0, false, 4, true>), grid, block, 0, s, a);
+      }
+      return;
+    }
+  }
   if (bf16 && a.lean) {
     constexpr int LW = kLeanWNW;
     if (a.out_bf16) hipLaunchKernelGGL((k_gemm<bf16_bits, bf16_bits, ROLE, true, LW>), grid, dim3(128 * LW), 0, s, a);
@@ -2055,6 +2087,10 @@ static void launch_gemm_role(bool bf16, const GemmLaunch& a, hipStream_t s) {
 hipError_t launch_gemm(bool bf16, const GemmLaunch& a, hipStream_t s) {
   if (a.splits < 1 || (a.splits > 1 && (a.k_split <= 0 || a.k_split % 64 != 0 ||
                                         (int64_t)(a.splits - 1) * a.k_split >= a.k_len)))
+    return hipErrorInvalidValue;
+  if (a.at_out && (a.role != 0 || !bf16 || a.ld_at % 8 != 0 ||
+                   reinterpret_cast<uintptr_t>(a.at_out) % 16 != 0 ||
+                   (int64_t)a.tiles_m * 256 > a.ld_at || a.k_len % 64 != 0))
     return hipErrorInvalidValue;
   if (a.role == 0) launch_gemm_role<0>(bf16, a, s);
   else launch_gemm_role<1>(bf16, a, s);

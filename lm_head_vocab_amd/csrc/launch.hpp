@@ -249,6 +249,11 @@ struct GemmLaunch {
   // The grid covers tiles_m * splits tile rows.
   int32_t splits, k_split;
   int64_t part_stride;
+  // dh only (bf16), or null: A's transpose, at_out[k * ld_at + m] for every
+  // k < k_len and m of the row tiles (0 at m >= m_valid), written from A's
+  // LDS slabs as the contraction streams them
+  void* at_out;
+  int64_t ld_at;
 };
 hipError_t launch_gemm(bool bf16, const GemmLaunch& a, hipStream_t s);
 

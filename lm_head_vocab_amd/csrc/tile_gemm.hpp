@@ -286,19 +286,83 @@ __device__ __forceinline__ void read_frags(const char* sa, const char* sb, int s
   else read_frags_k<Cfg::FN>(sb, s, lane, wn * Cfg::WN, bf);
 }
 
+// Transposed copy of the A operand, taken from its LDS slabs (the dh
+// contraction: A = dz [rows][V], K-major).  Each (slab, tile row) pair is
+// written by exactly one workgroup, the one whose tile column equals the
+// slab's global index modulo `every`, so across a launch every 64-column slab
+// of every 256-row tile goes out once as 64 rows of `out` (row = k, 256
+// values = the tile's A rows), with values of rows at or past n_valid as 0.
+struct SlabDump {
+  bf16_bits* out;  // out[k * ld + col0 + n]
+  int64_t ld;
+  int32_t col0;     // first A row of the tile
+  int32_t n_valid;  // A rows of the tile that hold data (may exceed 256)
+  int32_t every;    // tile columns of the launch
+  int32_t phase;    // this workgroup's tile column
+  int32_t slab0;    // global index of the workgroup's first slab (split K)
+};
+
+// Eight waves: wave w writes k-rows 16 (w % 4) .. + 15 of the slab for tile
+// rows 128 (w / 4) .. + 127.  A transposing LDS read in a 16-lane group gives
+// lane L four consecutive tile rows of k-row kb + L (source lane 4 j + q reads
+// tile row n0 + j at k kb + 4 q .. + 3, and lane L receives element L % 4 of
+// lanes 4 j + L / 4); two such reads make 8 rows, stored as one 16-byte piece.
+template <typename Cfg>
+__device__ __forceinline__ void dump_slab_t(const char* sa, const SlabDump& D, int slab, int lane,
+                                            int wave) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  static_assert(Cfg::WAVES == 8 && Cfg::BM == 256 && sizeof(bf16_bits) == 2, "8 waves, 256 rows");
+  const int g = lane >> 4, L = lane & 15, j = L >> 2, q = L & 3;
+  const int kb = 16 * (wave & 3), nh = 128 * (wave >> 2);
+  const int kbyte = (kb + 4 * q) * 2;
+  const int kch = kbyte >> 4, koff = kbyte & 15;
+  bf16_bits* orow = D.out + (int64_t)(slab * 64 + kb + L) * D.ld + D.col0;
+  typedef __attribute__((address_space(3))) bf16x4_tr_t lds_bf16x4;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int n0 = nh + 32 * i + 8 * g;
+    const int ra = n0 + j, rb = ra + 4;
+    const char* pa = sa + ra * kRowBytes + ((kch ^ (ra & 7)) << 4) + koff;
+    const char* pb = sa + rb * kRowBytes + ((kch ^ (rb & 7)) << 4) + koff;
+    const bf16x4_tr_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+        (lds_bf16x4*)((__attribute__((address_space(3))) char*)(pa)));
+    const bf16x4_tr_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+        (lds_bf16x4*)((__attribute__((address_space(3))) char*)(pb)));
+    const i32x2_t l2 = __builtin_bit_cast(i32x2_t, lo), h2 = __builtin_bit_cast(i32x2_t, hi);
+    i32x4_t w = i32x4_t{l2[0], l2[1], h2[0], h2[1]};
+    if (n0 + 8 > D.n_valid) {
+      // keep only the bf16 halves of rows below n_valid (element e: word e / 2,
+      // low half when e is even)
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (n0 + e >= D.n_valid) w[e >> 1] &= (e & 1) ? 0x0000ffff : (int)0xffff0000;
+    }
+    *reinterpret_cast<i32x4_t*>(orow + n0) = w;
+  }
+#else
+  (void)sa, (void)D, (void)slab, (void)lane, (void)wave;
+#endif
+}
+
 // One slab = two k-steps of MFMAs.  Step 0 issues the second half of slab
 // k+1's loads (unless FIRST: the prologue loaded all of it) and reads step
 // 1's fragments; step 1 (unless LAST) waits for slab k+1, meets the other
 // waves at the barrier (all of them now hold step 1's fragments, so this
 // stage is free), issues the first half of slab k+2 into it and reads slab
 // k+1's step-0 fragments.  Inside a step, loads and fragment reads are
-// interleaved with the MFMAs so they land while the rest run.
-template <typename T, typename Cfg, int PER_WAVE, bool FIRST, bool LAST, bool A_MN, bool B_MN>
+// interleaved with the MFMAs so they land while the rest run.  With DUMP and
+// dump_slab >= 0 the wave also writes its share of slab k+1's transposed A
+// right after that barrier (slab k+1 stays in its stage for a whole slab, so
+// the stores have a slab's time before the next barrier waits for them;
+// measured 0.1 ms per step better than writing a slab during its own step 0).
+template <typename T, typename Cfg, int PER_WAVE, bool FIRST, bool LAST, bool A_MN, bool B_MN,
+          bool DUMP = false>
 __device__ __forceinline__ void slab_steps(f32x4_t (&acc)[Cfg::FM][Cfg::FN],
                                            i32x4_t (&fa)[2][Cfg::FM], i32x4_t (&fb)[2][Cfg::FN],
                                            char* smem, int stage, int lane, int wm, int wn,
                                            const SlabLoads<PER_WAVE>& L, int next_slab,
-                                           int pend_slab) {
+                                           int pend_slab, const SlabDump* D = nullptr,
+                                           int dump_slab = -1) {
   // LDS read instructions per step: one per K-major fragment, two per MN-major one
   constexpr int kR = Cfg::FM * (A_MN ? 2 : 1) + Cfg::FN * (B_MN ? 2 : 1);
   constexpr int kH = PER_WAVE / 2;
@@ -327,6 +391,11 @@ __device__ __forceinline__ void slab_steps(f32x4_t (&acc)[Cfg::FM][Cfg::FN],
       __syncthreads();
       issue_groups<PER_WAVE, 0, kH, Cfg>(L, stage, next_slab);
       const char* na = smem + (stage ^ 1) * Cfg::STAGE;
+      if constexpr (DUMP) {
+        // the next slab, complete in the other stage since this barrier and
+        // kept there until the next one: a slab's time for the stores
+        if (dump_slab >= 0) dump_slab_t<Cfg>(na, *D, dump_slab, lane, wm * Cfg::WNW + wn);
+      }
       read_frags<Cfg, A_MN, B_MN>(na, na + Cfg::BM * kRowBytes, 0, lane, wm, wn, fa[0], fb[0]);
     }
 #pragma unroll
@@ -366,11 +435,11 @@ __device__ __forceinline__ void slab_steps(f32x4_t (&acc)[Cfg::FM][Cfg::FN],
 // (global_load_lds_dwordx4): one wave instruction fills 1 KB = 8 slab rows,
 // lane i landing at byte 16 i; lane i therefore fetches logical chunk
 // (i % 8) ^ (row % 8) of row i / 8, which realises the XOR swizzle.
-template <typename T, typename Cfg, bool A_MN = false, bool B_MN = false>
+template <typename T, typename Cfg, bool A_MN = false, bool B_MN = false, bool DUMP = false>
 __device__ __forceinline__ void tile_mainloop(f32x4_t (&acc)[Cfg::FM][Cfg::FN],
                                               const Operand<T>& A, int32_t a_row0,
                                               const Operand<T>& B, int32_t b_row0, int32_t k_len,
-                                              char* smem) {
+                                              char* smem, const SlabDump* D = nullptr) {
   constexpr int ROWS = Cfg::BM + Cfg::BN;
   constexpr int GROUPS = ROWS / 8;               // 1 KB load instructions per slab
   constexpr int PER_WAVE = GROUPS / Cfg::WAVES;  // per wave
@@ -421,17 +490,41 @@ __device__ __forceinline__ void tile_mainloop(f32x4_t (&acc)[Cfg::FM][Cfg::FN],
   // slab k+2's loads (clamped to the last slab: a reload into a stage that is
   // never read again) start at slab k's last step and finish at slab k+1's step 0
   auto clampk = [&](int k) { return k < nslab ? k : nslab - 1; };
+  // DUMP: slabs whose global index is phase modulo every go out transposed;
+  // `until` counts the slabs left before the next one (uniform)
+  int until = 0;
+  if constexpr (DUMP) {
+    until = (D->phase - D->slab0) % D->every;
+    if (until < 0) until += D->every;
+  }
+  auto dump_at = [&](int ks) {
+    if constexpr (!DUMP) return -1;
+    if (until != 0) {
+      --until;
+      return -1;
+    }
+    until = D->every - 1;
+    return D->slab0 + ks;
+  };
+  if constexpr (DUMP) {
+    // slab 0 from stage 0 (visible since the prologue barrier, kept until
+    // the barrier of its step 1); slab k + 1 after slab k's barrier
+    const int d0 = dump_at(0);
+    if (d0 >= 0) dump_slab_t<Cfg>(smem, *D, d0, lane, wave);
+    __builtin_amdgcn_sched_barrier(0);
+  }
   if (nslab > 1) {
-    slab_steps<T, Cfg, PER_WAVE, true, false, A_MN, B_MN>(acc, fa, fb, smem, 0, lane, wm, wn, L,
-                                                          clampk(2), 0);
+    slab_steps<T, Cfg, PER_WAVE, true, false, A_MN, B_MN, DUMP>(acc, fa, fb, smem, 0, lane, wm, wn,
+                                                                L, clampk(2), 0, D, dump_at(1));
     for (int ks = 1; ks + 1 < nslab; ++ks)
-      slab_steps<T, Cfg, PER_WAVE, false, false, A_MN, B_MN>(acc, fa, fb, smem, ks & 1, lane, wm,
-                                                             wn, L, clampk(ks + 2), clampk(ks + 1));
-    slab_steps<T, Cfg, PER_WAVE, false, true, A_MN, B_MN>(acc, fa, fb, smem, (nslab - 1) & 1, lane,
-                                                          wm, wn, L, 0, clampk(nslab));
+      slab_steps<T, Cfg, PER_WAVE, false, false, A_MN, B_MN, DUMP>(
+          acc, fa, fb, smem, ks & 1, lane, wm, wn, L, clampk(ks + 2), clampk(ks + 1), D,
+          dump_at(ks + 1));
+    slab_steps<T, Cfg, PER_WAVE, false, true, A_MN, B_MN, DUMP>(acc, fa, fb, smem, (nslab - 1) & 1,
+                                                                lane, wm, wn, L, 0, clampk(nslab));
   } else {
-    slab_steps<T, Cfg, PER_WAVE, true, true, A_MN, B_MN>(acc, fa, fb, smem, 0, lane, wm, wn, L, 0,
-                                                         0);
+    slab_steps<T, Cfg, PER_WAVE, true, true, A_MN, B_MN, DUMP>(acc, fa, fb, smem, 0, lane, wm, wn,
+                                                               L, 0, 0);
   }
   wait_vmem();      // reloads must land before LDS is reused
   __syncthreads();  // LDS is handed to the epilogue

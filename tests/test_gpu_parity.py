@@ -320,6 +320,25 @@ def test_single_call_forward_backward(case):
     full_parity(p, max_chunk_rows=ch, tag=f"single-{case}", single_call=True)
 
 
+@pytest.mark.parametrize("hidden,chunk", [(192, 256), (640, 256), (640, 0)])
+def test_single_call_dzt_from_dh(hidden, chunk):
+    """With both gradients the cross-entropy single call takes dz^T from the dh
+    contraction (each workgroup copies the dz slabs whose index equals its
+    tile column modulo the tile columns; rows past a chunk's end go out as
+    zeros); asked for dW alone, pass 1 stores dz^T itself.  The two must give
+    the same dW bits.  H = 640: three tile columns over 1280 / 64 = 20 slabs
+    (an uneven share); 256-row chunks of 600 rows: a ragged last chunk and
+    split-K dh.  dh and dW also match the oracle."""
+    p = synthetic.make_problem("ce_bf16_1b", n_rows=600, hidden_dim=hidden, vocab=1100)
+    say(f"[dzt-from-dh] H={hidden} chunk={chunk}")
+    out = full_parity(p, max_chunk_rows=chunk, tag=f"dzt-{hidden}-{chunk}", single_call=True)
+    run = out["run"]
+    gm = torch.ones(1, dtype=torch.float32, device="cuda")
+    _, dW_only = run.forward_backward(grad_mean=gm, want_dh=False)
+    torch.cuda.synchronize()
+    assert np.array_equal(dW_only.cpu().numpy(), out["dW"])
+
+
 @pytest.mark.parametrize("case", ["far", "far_f32", "near", "zero_sum"])
 def test_single_call_staged_ce_references(case):
     """The single call stages exp(z - label logit) per row.  far: logits spread
