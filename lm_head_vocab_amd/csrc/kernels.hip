@@ -65,6 +65,23 @@ __device__ __forceinline__ float col_max(float x) {
   return fmaxf(x, __shfl_xor(x, 32));
 }
 
+// Tile entries past the vocabulary's end (the last vocabulary tile) become
+// -inf, so that the max and exp loops need no per-entry test: exp2(-inf) = 0
+// adds nothing to a sum.  The loops then take the maximum with the IEEE
+// maximum (v_maximum3_f32 on gfx950, NaN-propagating), which needs no
+// canonicalising of the accumulators that fmaxf would add.
+template <typename Cfg>
+__device__ __forceinline__ void mask_vocab_tail(f32x4_t (&acc)[Cfg::FM][Cfg::FN], int v_base,
+                                                int lane, int vocab) {
+#pragma unroll
+  for (int i = 0; i < Cfg::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < Cfg::FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (v_base + i * kFrag + frag_row(r, lane) >= vocab) acc[i][j][r] = -INFINITY;
+}
+
 // Merge two (max, sum of exp(x - max)) pairs; `a` is the lower-index side.
 __device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2) {
   const float mn = fmaxf(m, m2);
@@ -254,6 +271,7 @@ __global__ __launch_bounds__(128 * WNW, 1) void k_stats(StatsLaunch a) {
     }
   }
 
+  if (tail) mask_vocab_tail<Cfg>(acc, v_base, lane, a.vocab);
   float mj[Cfg::FN], sj[Cfg::FN], qj[Cfg::FN];
   int ij[Cfg::FN];
 #pragma unroll
@@ -264,13 +282,12 @@ __global__ __launch_bounds__(128 * WNW, 1) void k_stats(StatsLaunch a) {
     for (int i = 0; i < Cfg::FM; ++i)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int v = v_base + i * kFrag + frag_row(r, lane);
-        float x = acc[i][j][r];
-        if (tail && v >= a.vocab) x = -INFINITY;
+        const float x = acc[i][j][r];
         if (ARGMAX) {
-          if (x > mx) { mx = x; idx = v; }  // strict: keeps the lowest index
+          // strict: keeps the lowest index
+          if (x > mx) { mx = x; idx = v_base + i * kFrag + frag_row(r, lane); }
         } else {
-          mx = fmaxf(mx, x);
+          mx = __builtin_elementwise_maximum(mx, x);
         }
       }
     const float m = col_max(mx);
@@ -281,12 +298,9 @@ __global__ __launch_bounds__(128 * WNW, 1) void k_stats(StatsLaunch a) {
       for (int i = 0; i < Cfg::FM; ++i)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int v = v_base + i * kFrag + frag_row(r, lane);
-          if (!tail || v < a.vocab) {
-            const float e = fast_exp2(fmaf(acc[i][j][r], kLog2e, -mb));
-            s += e;
-            if (TARGET) q = fmaf(e, e, q);
-          }
+          const float e = fast_exp2(fmaf(acc[i][j][r], kLog2e, -mb));
+          s += e;
+          if (TARGET) q = fmaf(e, e, q);
         }
     }
     mj[j] = m;
@@ -500,6 +514,7 @@ __global__ __launch_bounds__(128 * WNW, 1) void k_stats_stage(StatsStageLaunch a
   const bool tail = tm * Cfg::BM + Cfg::BM > st.vocab;
   float* red = reinterpret_cast<float*>(smem);  // [2 wave rows][BN]
 
+  if (tail) mask_vocab_tail<Cfg>(acc, v_base, lane, st.vocab);
   float mj[Cfg::FN];
 #pragma unroll
   for (int j = 0; j < Cfg::FN; ++j) {
@@ -507,10 +522,7 @@ __global__ __launch_bounds__(128 * WNW, 1) void k_stats_stage(StatsStageLaunch a
 #pragma unroll
     for (int i = 0; i < Cfg::FM; ++i)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int v = v_base + i * kFrag + frag_row(r, lane);
-        if (!tail || v < st.vocab) mx = fmaxf(mx, acc[i][j][r]);
-      }
+      for (int r = 0; r < 4; ++r) mx = __builtin_elementwise_maximum(mx, acc[i][j][r]);
     mj[j] = col_max(mx);
     if (lane < kFrag) red[wm * Cfg::BN + wn * Cfg::WN + j * kFrag + lane] = mj[j];
   }
@@ -579,10 +591,8 @@ __global__ __launch_bounds__(128 * WNW, 1) void k_stats_stage(StatsStageLaunch a
       float e[4], f[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int v = v_base + i * kFrag + frag_row(r, lane);
-        const bool in = !tail || v < st.vocab;
-        e[r] = in ? fast_exp2(fmaf(acc[i][j][r], kLog2e, -mb0)) : 0.0f;
-        f[r] = in ? fast_exp2(fmaf(acc[i][j + 1][r], kLog2e, -mb1)) : 0.0f;
+        e[r] = fast_exp2(fmaf(acc[i][j][r], kLog2e, -mb0));
+        f[r] = fast_exp2(fmaf(acc[i][j + 1][r], kLog2e, -mb1));
         s0 += e[r];
         s1 += f[r];
         e[r] *= f0;
