@@ -332,7 +332,7 @@ def blas_reference(h, W, labels, nc, N, kernels):
         return round(flops / (sorted(ts)[2] * 1e-3) / 1e12, 1)
 
     ours = {k: round(kernels[k]["work_per_launch"] / (kernels[k]["ms_avg"] * 1e-3) / 1e12, 1)
-            for k in ("stats_stage", "gemm_dh", "gemm_dW") if k in kernels}
+            for k in ("stats_stage", "gemm_dh", "gemm_dh_dzt", "gemm_dW") if k in kernels}
     return {"library": "hipBLASLt via torch.matmul (bf16 in, fp32 accumulate, bf16 out)",
             "shapes": {"pass1": [nc, W.shape[0], h.shape[1]], "dh": [nc, h.shape[1], W.shape[0]],
                        "dW": [W.shape[0], h.shape[1], nc]},
@@ -343,7 +343,7 @@ def blas_reference(h, W, labels, nc, N, kernels):
 
 
 FLOP_KERNELS = ("stats_q", "stats_p", "stats_stage", "stats_dual", "div", "div_heads", "dz",
-                "gemm_dh", "gemm_dW")
+                "gemm_dh", "gemm_dh_dzt", "gemm_dW")
 
 
 def summarize_trace(entries, steps):

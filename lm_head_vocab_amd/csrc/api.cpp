@@ -580,13 +580,14 @@ enum KernelId : int32_t {
   K_VALIDITY, K_STATS_Q, K_STATS_P, K_COMBINE1, K_ROWDOT, K_DIV, K_COMBINE2, K_REDUCE, K_COPY,
   K_SEED, K_TRANSPOSE_W, K_TRANSPOSE_H, K_DZ, K_GEMM_DH, K_GEMM_DW, K_STATS_STAGE, K_DZ_STAGE,
   K_TILE_SUM, K_SUM_PARTS, K_TARGET_GATHER, K_STAGE_FIX, K_STATS_DUAL, K_DIV_HEADS, K_HEADS_MAP,
-  K_DIV_RAW, K_DZ_RAW, K_SPAN_CARRY, K_NUM_IDS
+  K_DIV_RAW, K_DZ_RAW, K_SPAN_CARRY, K_GEMM_DH_DZT, K_NUM_IDS
 };
 const char* const kKernelNames[K_NUM_IDS] = {
     "validity", "stats_q", "stats_p", "combine1", "rowdot", "div", "combine2", "reduce",
     "copy_lse", "seed", "transpose_W", "transpose_h", "dz", "gemm_dh", "gemm_dW",
     "stats_stage", "dz_stage", "tile_sum", "sum_partials", "target_gather", "stage_fix",
-    "stats_dual", "div_heads", "heads_map", "div_raw", "dz_raw", "span_carry"};
+    "stats_dual", "div_heads", "heads_map", "div_raw", "dz_raw", "span_carry",
+    "gemm_dh_dzt"};
 
 // Brackets launches with the trace's events when the problem carries one.
 struct Tracer {
@@ -1375,7 +1376,9 @@ int contract_dh(const specloss_problem* p, const Layout& L, int64_t Nc, const vo
     g.out_bf16 = 0;
     g.part_stride = (int64_t)rows * H;
   }
-  TRACED(tr, K_GEMM_DH, 2.0 * rows * H * V, launch_gemm(bf16, g, stream));
+  // the dh contraction that also writes dz^T has a trace name of its own
+  TRACED(tr, g.at_out ? K_GEMM_DH_DZT : K_GEMM_DH, 2.0 * rows * H * V,
+         launch_gemm(bf16, g, stream));
   if (g.splits > 1)
     TRACED(tr, K_SUM_PARTS, 4.0 * rows * H * (g.splits + 1),
            launch_sum_parts(dhp, rows * H, g.splits, out, dh_dtype == SPECLOSS_BF16, stream));

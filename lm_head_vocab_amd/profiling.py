@@ -55,9 +55,11 @@ def trace_name(kernel: str) -> str:
     if not m:
         return kernel
     base, targs = m.group(1), m.group(2) or ""
-    if base == "k_gemm":  # k_gemm<T, OutT, ROLE, LEAN>
+    if base == "k_gemm":  # k_gemm<T, OutT, ROLE, LEAN, WNW, DUMP>
         args = [a.strip() for a in targs.strip("<>").split(",")]
-        return "gemm_dW" if len(args) > 2 and args[2] == "1" else "gemm_dh"
+        if len(args) > 2 and args[2] == "1":
+            return "gemm_dW"
+        return "gemm_dh_dzt" if len(args) > 5 and args[5] == "true" else "gemm_dh"
     names = {"k_stats": "stats_q", "k_stats_stage": "stats_stage", "k_dz_stage": "dz_stage",
              "k_dz": "dz", "k_div": "div", "k_combine1": "combine1", "k_combine2": "combine2", "k_stage_fix": "stage_fix",
              "k_rowdot": "rowdot", "k_transpose": "transpose", "k_validity": "validity",
@@ -181,7 +183,8 @@ def markdown(stats_csv: str, traffic: dict, workload: str, bench: dict = None,
         out.append(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e6:.4f} | "
                    f"{float(r['TotalDurationNs']) / 1e6:.3f} | {float(r['Percentage']):.2f} |")
     out += ["", "`k_gemm<T, OutT, 1, ...>` is the dW contraction, `k_gemm<T, OutT, 0, ...>` the dh "
-            "contraction (the last template argument selects the copy-free variant).", ""]
+            "contraction (the fourth template argument selects the copy-free variant; the sixth, "
+            "traced as `gemm_dh_dzt`, the dh contraction that also writes dz^T).", ""]
     if bench:
         r = bench["roofline"]
         out += [f"`python3 bench.py --workload {workload}` on the same box, just before: "

@@ -268,7 +268,7 @@ def full_parity(prob, *, max_chunk_rows=0, check_grads=True, tag="", single_call
             lay = {True: "copies", False: "no_copies"}.get(expect_copies, expect_copies)
             want_wt, want_ht = {"copies": (True, True), "no_weight_copy": (False, True),
                                 "no_copies": (False, False)}[lay]
-            assert "gemm_dh" in names, names
+            assert "gemm_dh" in names or "gemm_dh_dzt" in names, names
             assert (("transpose_W" in names) == want_wt
                     and ("transpose_h" in names) == want_ht), names
     return out

@@ -8,6 +8,9 @@ from lm_head_vocab_amd import profiling as P
 def test_trace_name_mapping():
     assert P.trace_name("void specloss::k_gemm<unsigned short, float, 1, false>(specloss::GemmLaunch)") == "gemm_dW"
     assert P.trace_name("void specloss::k_gemm<unsigned short, float, 0, false>(specloss::GemmLaunch)") == "gemm_dh"
+    assert P.trace_name("void specloss::k_gemm<unsigned short, float, 0, false, 4, false>(specloss::GemmLaunch)") == "gemm_dh"
+    assert P.trace_name("void specloss::k_gemm<unsigned short, float, 0, false, 4, true>(specloss::GemmLaunch)") == "gemm_dh_dzt"
+    assert P.trace_name("void specloss::k_gemm<unsigned short, float, 1, false, 4, false>(specloss::GemmLaunch)") == "gemm_dW"
     assert P.trace_name("void specloss::k_stats<unsigned short, true>(specloss::StatsLaunch)") == "stats_p"
     assert P.trace_name("void specloss::k_stats<unsigned short, false>(specloss::StatsLaunch)") == "stats_q"
     assert P.trace_name("void specloss::k_stats<unsigned short, false, 4, true>(specloss::StatsLaunch)") == "stats_q"
