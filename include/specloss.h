@@ -308,7 +308,9 @@ int lmhead_loss_bwd(const specloss_problem* p, const float* grad_loss, const flo
  * section (logits, loss and gradients of one token chunk, LM-head gradient
  * accumulated over chunks), and the logits are never recomputed: for the
  * label and argmax-p cross-entropies the forward pass leaves exp(z - label
- * logit) of the chunk (in the input dtype, both layouts) in the workspace;
+ * logit) of the chunk in the workspace (in the input dtype; its transposed
+ * copy for the dW contraction is written by the dh contraction, or by the
+ * forward pass when dhidden is NULL or the inputs are fp32);
  * with divergences the first forward pass keeps the raw fp32 logit rows of
  * both sides, from which the second sweep's sums and then the logit gradient
  * are formed.  `saved` may be NULL.  Errors as for the two calls.
