@@ -320,18 +320,23 @@ def test_single_call_forward_backward(case):
     full_parity(p, max_chunk_rows=ch, tag=f"single-{case}", single_call=True)
 
 
-@pytest.mark.parametrize("hidden,chunk", [(192, 256), (640, 256), (640, 0)])
-def test_single_call_dzt_from_dh(hidden, chunk):
+@pytest.mark.parametrize("hidden,chunk,w_in_place", [(192, 256, False), (640, 256, False),
+                                                     (640, 0, False), (640, 256, True)])
+def test_single_call_dzt_from_dh(hidden, chunk, w_in_place):
     """With both gradients the cross-entropy single call takes dz^T from the dh
     contraction (each workgroup copies the dz slabs whose index equals its
     tile column modulo the tile columns; rows past a chunk's end go out as
     zeros); asked for dW alone, pass 1 stores dz^T itself.  The two must give
     the same dW bits.  H = 640: three tile columns over 1280 / 64 = 20 slabs
     (an uneven share); 256-row chunks of 600 rows: a ragged last chunk and
-    split-K dh.  dh and dW also match the oracle."""
+    split-K dh; w_in_place: the dh contraction reading W in place (no W^T
+    copy) writes the copy too.  dh and dW also match the oracle."""
     p = synthetic.make_problem("ce_bf16_1b", n_rows=600, hidden_dim=hidden, vocab=1100)
-    say(f"[dzt-from-dh] H={hidden} chunk={chunk}")
-    out = full_parity(p, max_chunk_rows=chunk, tag=f"dzt-{hidden}-{chunk}", single_call=True)
+    say(f"[dzt-from-dh] H={hidden} chunk={chunk} w_in_place={w_in_place}")
+    flags = L.binding.FLAG_NO_WEIGHT_COPY if w_in_place else None
+    out = full_parity(p, max_chunk_rows=chunk, tag=f"dzt-{hidden}-{chunk}", single_call=True,
+                      flags=flags, expect_copies="no_weight_copy" if w_in_place else None,
+                      expect_kernels=(("gemm_dh_dzt",), ("gemm_dh",)))
     run = out["run"]
     gm = torch.ones(1, dtype=torch.float32, device="cuda")
     _, dW_only = run.forward_backward(grad_mean=gm, want_dh=False)
