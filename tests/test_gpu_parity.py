@@ -233,6 +233,20 @@ def test_bf16_dhidden_output():
     assert rel_frob(dh.float().cpu().numpy(), rdh) <= GRAD_FROB
 
 
+def test_bf16_dhidden_single_call():
+    """bf16 dhidden from the single call, whose dh contraction also writes
+    dz^T (the bf16-output variant of that kernel); dW from that copy."""
+    p = synthetic.make_problem("ce_bf16_1b", n_rows=600, hidden_dim=384, vocab=700)
+    dev = to_device(p)
+    run = make_run(p, dev, max_chunk_rows=256)
+    dh = torch.empty(dev["hidden"].shape, dtype=torch.bfloat16, device="cuda")
+    dh, dW = run.forward_backward(grad_mean=torch.ones(1, device="cuda"), dhidden=dh)
+    torch.cuda.synchronize()
+    rdh, rdW = O.backward(p)
+    assert rel_frob(dh.float().cpu().numpy(), rdh) <= GRAD_FROB
+    assert rel_frob(dW.cpu().numpy(), rdW) <= GRAD_FROB
+
+
 def test_align_heads_kernel():
     import lm_head_vocab_amd as L
     S, B, shifts = 37, 3, (1, 2, 5)
