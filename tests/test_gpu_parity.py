@@ -185,13 +185,19 @@ def test_bad_labels_counted_and_masked():
     assert counts[1] == 2
 
 
-def test_all_rows_masked():
+@pytest.mark.parametrize("single", [False, True])
+def test_all_rows_masked(single):
+    """No valid row: mean 0 and every gradient exactly 0, by the two calls
+    and by the single call (whose staged values and dz^T copy are zeros)."""
     p = synthetic.make_problem("ce_bf16_1b", n_rows=100, hidden_dim=64, vocab=300)
     p.mask = np.zeros(100, np.uint8)
     dev = to_device(p)
     run = make_run(p, dev)
-    run.forward()
-    dh, dW = run.backward(grad_mean=torch.ones(1, device="cuda"))
+    if single:
+        dh, dW = run.forward_backward(grad_mean=torch.ones(1, device="cuda"))
+    else:
+        run.forward()
+        dh, dW = run.backward(grad_mean=torch.ones(1, device="cuda"))
     torch.cuda.synchronize()
     assert run.counts.cpu().tolist() == [0, 0]
     assert float(run.reduced[0]) == 0.0
