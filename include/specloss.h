@@ -185,13 +185,13 @@ typedef struct {
  * with every copy when that chunk reaches min(N, 1024) rows, otherwise
  * (bf16) without the W^T copy or without any copy if that allows a larger
  * chunk; lmhead_loss_chunk reports the choice.
- * dW groups: with the transposed copies (every copy, or no W^T copy), two
- * consecutive chunks may share one dW contraction, each writing its half of
- * a dz^T and h^T copy two chunks wide (dW is then read and written once per
- * two chunks).  The default policy and the calls take that when it fits
- * with a chunk of at least min(N, 1024) rows, two chunks together are at
- * most 8192 rows, and it saves at least two dW contractions over the largest
- * single chunk that would fit.
+ * dW groups: with the transposed copies (every copy, or no W^T copy), G = 2
+ * to 4 consecutive chunks may share one dW contraction, each writing its
+ * columns of a dz^T and h^T copy G chunks wide (dW is then read and written
+ * once per G chunks).  The default policy and the calls take the group with
+ * the fewest dW read-modify-writes among those that fit with a chunk of at
+ * least min(N, 1024) rows, are at most 8192 rows deep and save at least two
+ * dW contractions over the largest single chunk that would fit.
  * SPECLOSS_E_INVAL for a NULL `bytes` and as for the calls.
  */
 int lmhead_loss_workspace_size(const specloss_problem* p, int64_t max_chunk_rows, size_t* bytes);
@@ -199,7 +199,7 @@ int lmhead_loss_workspace_size(const specloss_problem* p, int64_t max_chunk_rows
 /*
  * The chunk the calls use with a workspace of ws_bytes: rows per chunk, the
  * backward layout (0 every copy, 1 no W^T copy, 2 no copy) and, when
- * dw_group is not NULL, the chunks per dW contraction (1 or 2; 1 for call 0),
+ * dw_group is not NULL, the chunks per dW contraction (1 to 4; 1 for call 0),
  * for `call` 0 = lmhead_loss_fwd, 1 = lmhead_loss_bwd, 2 =
  * lmhead_loss_fwd_bwd.  Host only.  SPECLOSS_E_WORKSPACE when no chunk fits,
  * SPECLOSS_E_INVAL for a NULL chunk_rows or layout or an unknown call, and as

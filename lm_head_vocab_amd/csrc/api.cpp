@@ -356,24 +356,45 @@ int64_t wanted_chunk(const specloss_problem* p) {
 
 // Largest chunk of one layout and its dW group.  Each dW contraction reads and
 // writes the whole fp32 dW (2 V H 4 bytes) beside its 2 rows H V flops, so at
-// small chunks it is bound by that traffic.  With the copies, two chunks can
-// share one contraction (dw_group 2: their dz^T and h^T columns side by side,
-// K = 2 Nc).  The copies of two chunks take a smaller chunk, which costs the
-// other kernels some efficiency, so pairs are taken when
-//   - their chunk still has min(N, 1024) rows,
-//   - a pair is at most kDwGroupDepth rows deep (on MI355X the contraction ran
+// small chunks it is bound by that traffic.  With the copies, G consecutive
+// chunks can share one contraction (dw_group G: their dz^T and h^T columns
+// side by side, K = G Nc).  The copies of G chunks take a smaller chunk, which
+// costs the other kernels some efficiency, so a group is taken when
+//   - its chunk still has min(N, 1024) rows,
+//   - it is at most kDwGroupDepth rows deep (on MI355X the contraction ran
 //     at 1.32 PFLOP/s with K = 8192 and 1.26 with K = 16384 at H = 4096,
 //     V = 128256), and
-//   - they save at least two of dW's read-modify-writes per call (measured
-//     whole-call changes: one saved at N = 8192, H = 2048 lost 2.6 %; two at
-//     the three-head H = 16384 shape gained 3.4 %, four at N = 16384,
-//     H = 4096 with a target gained 4.6 %).
+//   - it saves at least two of dW's read-modify-writes per call over single
+//     chunks (measured whole-call changes: one saved at N = 8192, H = 2048
+//     lost 2.6 %; two at the three-head H = 16384 shape gained 3.4 %, four at
+//     N = 16384, H = 4096 with a target gained 4.6 %);
+// among those, the group with the fewest read-modify-writes (the smaller
+// group on a tie).
 constexpr int64_t kDwGroupDepth = 8192;
+constexpr int32_t kMaxDwGroup = 4;
 
-bool take_dw_group(const specloss_problem* p, int64_t n1, int64_t n2) {
+// Read-modify-writes of dW per call with chunks of n rows in groups of g.
+int64_t dw_passes(const specloss_problem* p, int64_t n, int32_t g) {
+  return cdiv(cdiv(p->n_rows, n), g);
+}
+
+// The dW group (1 if none) for single chunks of n1 rows, given the largest
+// chunk ng[g] that fits with groups of g (g = 2 .. kMaxDwGroup; <= 0: none).
+int32_t choose_dw_group(const specloss_problem* p, int64_t n1, const int64_t* ng) {
   const int64_t N = p->n_rows;
-  if (n1 <= 0 || n1 >= N || n2 < wanted_chunk(p) || 2 * n2 > kDwGroupDepth) return false;
-  return cdiv(N, n1) - cdiv(cdiv(N, n2), 2) >= 2;
+  if (n1 <= 0 || n1 >= N) return 1;
+  int32_t best = 1;
+  int64_t best_passes = dw_passes(p, n1, 1) - 1;  // a group must save at least two
+  for (int32_t g = 2; g <= kMaxDwGroup; ++g) {
+    const int64_t n = ng[g];
+    if (n < wanted_chunk(p) || g * n > kDwGroupDepth) continue;
+    const int64_t passes = dw_passes(p, n, g);
+    if (passes < best_passes) {
+      best = g;
+      best_passes = passes;
+    }
+  }
+  return best;
 }
 
 int64_t fit_chunk(const specloss_problem* p, const KindSet& k, size_t ws_bytes, Region region,
@@ -382,12 +403,11 @@ int64_t fit_chunk(const specloss_problem* p, const KindSet& k, size_t ws_bytes, 
   const int64_t n1 = largest_chunk(p, k, ws_bytes, region, layout, top, strict, raw, 1);
   if (region == REGION_FWD || n1 <= 0 || n1 >= p->n_rows || !plan(p, k, n1, layout).dw_copies)
     return n1;
-  const int64_t n2 = largest_chunk(p, k, ws_bytes, region, layout, top, strict, raw, 2);
-  if (take_dw_group(p, n1, n2)) {
-    *dw_group = 2;
-    return n2;
-  }
-  return n1;
+  int64_t ng[kMaxDwGroup + 1] = {};
+  for (int32_t g = 2; g <= kMaxDwGroup; ++g)
+    ng[g] = largest_chunk(p, k, ws_bytes, region, layout, top, strict, raw, g);
+  *dw_group = choose_dw_group(p, n1, ng);
+  return *dw_group > 1 ? ng[*dw_group] : n1;
 }
 
 // Chunk for a region and the backward layout.  With every copy when the
@@ -512,11 +532,10 @@ int64_t default_chunk(const specloss_problem* p, const KindSet& k, int32_t* layo
     if (nc <= 0 || (nc < want && i + 1 < n_lays)) continue;
     // a dW group as in fit_chunk
     if (nc < N && plan(p, k, nc, lays[i]).dw_copies) {
-      const int64_t n2 = fits(lays[i], 2);
-      if (take_dw_group(p, nc, n2)) {
-        nc = n2;
-        *dw_group = 2;
-      }
+      int64_t ng[kMaxDwGroup + 1] = {};
+      for (int32_t g = 2; g <= kMaxDwGroup; ++g) ng[g] = fits(lays[i], g);
+      *dw_group = choose_dw_group(p, nc, ng);
+      if (*dw_group > 1) nc = ng[*dw_group];
     }
     // balance: the fewest chunks of that size, then equal chunks
     const int64_t nch = cdiv(N, nc);

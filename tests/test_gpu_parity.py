@@ -906,28 +906,31 @@ def test_jsd_with_underflowing_probabilities(single):
 
 
 # ---------------------------------------------------------------- dW groups
-def _dw_group_workspace(prob, call, flags):
-    """A workspace with which `call` contracts two chunks per dW launch over an
-    odd number (at least three) of chunks: the last group is one ragged chunk."""
+def _dw_group_workspace(prob, call, flags, group):
+    """A workspace with which `call` contracts `group` chunks per dW launch
+    over a number of chunks that leaves a shorter last group, whose last
+    chunk is ragged."""
     dev = to_device(prob)
     probe = make_run(prob, dev, max_chunk_rows=256, flags=flags)
     for rows in range(1024, prob.n_rows + 256, 256):
         ws = L.binding.lmhead_loss_workspace_size(probe.problem, rows)
-        nc, _, group = L.binding.lmhead_loss_chunk(probe.problem, ws, call)
+        nc, _, g = L.binding.lmhead_loss_chunk(probe.problem, ws, call)
         chunks = -(-prob.n_rows // nc)
-        if group == 2 and chunks >= 3 and chunks % 2 == 1 and prob.n_rows % nc:
+        if g == group and chunks > group and chunks % group and prob.n_rows % nc:
             return ws, nc
-    raise AssertionError("no workspace gives a dW group")
+    raise AssertionError(f"no workspace gives a dW group of {group}")
 
 
-@pytest.mark.parametrize("case", ["ce_single", "ce_two", "ce32_two", "lk_single", "lk_two",
-                                  "kl_two", "heads_single"])
+@pytest.mark.parametrize("case", ["ce_single_2", "ce_two_2", "ce32_two_2", "lk_single_2",
+                                  "lk_two_2", "kl_two_2", "heads_single_2", "ce_single_3",
+                                  "ce_single_4", "ce32_two_3", "lk_single_4", "lk_two_4"])
 def test_dw_group_matches_oracle(case):
-    """Two chunks per dW contraction (each writes its half of dz^T and h^T
-    copies two chunks wide): parity with the oracle, and one dW launch per
-    group in the trace.  The pairs must save two contractions, hence seven
-    or more chunks (eleven in fp32, whose copies take more of the space)."""
-    kind, calls = case.split("_")
+    """G chunks per dW contraction (each writes its columns of dz^T and h^T
+    copies G chunks wide): parity with the oracle, and one dW launch per
+    group in the trace.  A group must save two contractions, hence seven or
+    more chunks here (eleven in fp32, whose copies take more of the space)."""
+    kind, calls, group = case.split("_")
+    group = int(group)
     single = calls == "single"
     flags = 0
     if kind in ("ce", "ce32"):
@@ -945,11 +948,11 @@ def test_dw_group_matches_oracle(case):
         p = synthetic.make_problem("lk_hybrid_bf16_8b", n_rows=7000, hidden_dim=128, vocab=700,
                                    weights=w)
     call = L.binding.CALL_FWD_BWD if single else L.binding.CALL_BWD
-    ws, nc = _dw_group_workspace(p, call, flags)
+    ws, nc = _dw_group_workspace(p, call, flags, group)
     out = full_parity(p, workspace_bytes=ws, single_call=single, flags=flags,
                       tag=f"dw-group-{case}", expect_kernels=(("gemm_dW",), ()))
     n_dw = sum(1 for name, _, _ in out["trace"] if name == "gemm_dW")
-    assert n_dw == -(-(-(-p.n_rows // nc)) // 2), (n_dw, nc)
+    assert n_dw == -(-(-(-p.n_rows // nc)) // group), (n_dw, nc, group)
     # accumulate_dW adds every group onto the caller's dW
     run = out["run"]
     gm = torch.ones(1, dtype=torch.float32, device="cuda")

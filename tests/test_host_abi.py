@@ -324,10 +324,10 @@ def _chunk(lib, p, ws, call, group=False):
 
 
 @pytest.mark.parametrize("name,chunk,layout,group", [
-    ("ce_bf16_1b", 2048, "copies", 1),
+    ("ce_bf16_1b", 1024, "copies", 4),
     ("ce_bf16_8b", 8192, "copies", 1),
-    ("lk_hybrid_bf16_8b", 1536, "copies", 2),
-    ("multihead_bf16_405b", 1536, "no_weight_copy", 2),
+    ("lk_hybrid_bf16_8b", 1280, "copies", 4),
+    ("multihead_bf16_405b", 1536, "no_weight_copy", 3),
 ])
 def test_default_chunk_streams_below_the_logits_size(lib, name, chunk, layout, group):
     """Blog, "Backward pass" / "Choosing the chunk size": the default workspace
